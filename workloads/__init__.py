@@ -1,0 +1,302 @@
+"""Seeded synthetic inputs for the paged-KV attention path.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and
+benchmark. It holds no attention, softmax, allocator, block-table or cache-write
+arithmetic: only random draws, the rounding of those draws to the storage dtype,
+and the shape recipes (lengths, pool sizes, initial free-list orders, and the
+list of alloc/free *requests* that fragments a pool). Block ids are never chosen
+here; an allocator replays the request list.
+
+Every stream is a NumPy PCG64 generator keyed by a SeedSequence of integers, so
+any one sequence's values can be regenerated without drawing the others.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+# dtype names used throughout: "f32", "bf16", "fp8" (OCP E4M3 cache only)
+
+_STREAM_LENGTHS = 11
+_STREAM_POOL = 12
+_STREAM_HISTORY = 13
+_STREAM_Q = 20
+_STREAM_K = 21
+_STREAM_V = 22
+_STREAM_TRACE = 30
+
+
+def rng_for(*key: int) -> np.random.Generator:
+    """A PCG64 generator for the integer key (seed, stream, index...)."""
+    return np.random.default_rng(np.random.SeedSequence([int(k) for k in key]))
+
+
+# ----------------------------------------------------------------------------
+# storage rounding of draws (input preparation, not part of the method)
+# ----------------------------------------------------------------------------
+
+def bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bfloat16 bit patterns, nearest-even; NaN kept quiet."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if np.any(nan):
+        r = np.where(nan, ((u >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16), r)
+    return r
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def as_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Float32 draws -> storage array: float32 for "f32", uint16 bits for "bf16"."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits(x32)
+    raise ValueError(f"unsupported storage dtype {dtype!r}")
+
+
+def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 view of an f32 array or bf16 bit array."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_to_f32(a).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# workload recipes
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Workload:
+    """One attention step over a paged KV cache, described by shapes and seeds.
+
+    seq_lens[s] counts the tokens of sequence s in the cache *after* this step's
+    new tokens are written; q_lens[s] is the number of new (query) tokens, which
+    occupy positions seq_lens[s]-q_lens[s] .. seq_lens[s]-1.
+    """
+
+    name: str
+    seed: int
+    dtype: str                 # query / new K,V / output dtype: "f32" or "bf16"
+    cache_dtype: str           # "f32", "bf16" or "fp8"
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    seq_lens: np.ndarray       # int32 [B]
+    q_lens: np.ndarray         # int32 [B]
+    num_blocks: int
+    free_order: np.ndarray     # int32 [num_blocks], initial free list (popped from the end)
+    history: List[Tuple] = dataclasses.field(default_factory=list)
+    partition_size: int = 0    # split-context partition length in tokens (0 = none)
+    sigma: float = 1.0
+    scale: Optional[float] = None  # softmax scale; None = 1/sqrt(head_dim)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.seq_lens))
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(self.scale) if self.scale is not None else 1.0 / float(np.sqrt(self.head_dim))
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def is_decode(self) -> bool:
+        return bool(np.all(self.q_lens == 1))
+
+    def blocks_needed(self) -> np.ndarray:
+        """ceil(seq_len / block_size) per sequence (used to size pools)."""
+        return (self.seq_lens.astype(np.int64) + self.block_size - 1) // self.block_size
+
+    def max_blocks_per_seq(self) -> int:
+        return int(self.blocks_needed().max()) if self.num_seqs else 0
+
+    # -- values -----------------------------------------------------------
+    def _draw(self, stream: int, s: int, rows: int, heads: int) -> np.ndarray:
+        g = rng_for(self.seed, stream, s)
+        x = g.standard_normal((rows, heads, self.head_dim), dtype=np.float32)
+        if self.sigma != 1.0:
+            x = x * np.float32(self.sigma)
+        return x
+
+    def kv_f32(self, s: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Float32 draws of K and V for positions 0..seq_lens[s]-1 of sequence s."""
+        L = int(self.seq_lens[s])
+        return (self._draw(_STREAM_K, s, L, self.num_kv_heads),
+                self._draw(_STREAM_V, s, L, self.num_kv_heads))
+
+    def kv(self, s: int) -> Tuple[np.ndarray, np.ndarray]:
+        """K and V of sequence s in the step's input dtype (float32 or bf16 bits)."""
+        k, v = self.kv_f32(s)
+        return as_storage(k, self.dtype), as_storage(v, self.dtype)
+
+    def q(self, s: int) -> np.ndarray:
+        """Queries of sequence s, [q_lens[s], Hq, d], in the input dtype."""
+        x = self._draw(_STREAM_Q, s, int(self.q_lens[s]), self.num_q_heads)
+        return as_storage(x, self.dtype)
+
+    def q_all(self) -> np.ndarray:
+        parts = [self.q(s) for s in range(self.num_seqs)]
+        if not parts:
+            shape = (0, self.num_q_heads, self.head_dim)
+            return np.zeros(shape, np.float32 if self.dtype == "f32" else np.uint16)
+        return np.concatenate(parts, axis=0)
+
+    def cu_q(self) -> np.ndarray:
+        cu = np.zeros(self.num_seqs + 1, np.int32)
+        np.cumsum(self.q_lens, out=cu[1:])
+        return cu
+
+
+def _permutation(seed: int, n: int) -> np.ndarray:
+    return rng_for(seed, _STREAM_POOL).permutation(n).astype(np.int32)
+
+
+def _pool_1p2(need_blocks: np.ndarray) -> int:
+    return int(np.ceil(1.2 * float(need_blocks.sum())))
+
+
+def config1() -> Workload:
+    """Tiny fp32 decode: 4 sequences of context 17/14/13/14 (the four prompt lengths
+    of the tiny-vllm queue), 32 query / 8 KV heads, head_dim 64, blocks of 16,
+    a 64-block pool whose free list is a seeded permutation."""
+    seed = 1
+    L = np.array([17, 14, 13, 14], np.int32)
+    return Workload("cfg1_tiny_decode_f32", seed, "f32", "f32", 32, 8, 64, 16,
+                    L, np.ones(4, np.int32), 64, _permutation(seed, 64))
+
+
+def config2() -> Workload:
+    """Mixed continuous-batching step, bf16: 48 decode rows (context U{16..2048})
+    and 4 prefill chunks of 512 new tokens after 0/512/1024/1536 cached tokens
+    (the four chunks of a 2048-token prompt); 32/8 heads, d=128, blocks of 16.
+    The pool is 1.5x the need and is fragmented by 2000 seeded alloc/free
+    requests from dummy owners that stay live."""
+    seed = 2
+    g = rng_for(seed, _STREAM_LENGTHS)
+    dec = g.integers(16, 2048, size=48, endpoint=True).astype(np.int32)
+    c0 = np.array([0, 512, 1024, 1536], np.int32)
+    L = np.concatenate([dec, c0 + 512]).astype(np.int32)
+    q = np.concatenate([np.ones(48, np.int32), np.full(4, 512, np.int32)])
+    w = Workload("cfg2_mixed_step_bf16", seed, "bf16", "bf16", 32, 8, 128, 16,
+                 L, q, 0, np.zeros(0, np.int32))
+    need = int(w.blocks_needed().sum())
+    w.num_blocks = int(np.ceil(1.5 * need))
+    w.free_order = np.arange(w.num_blocks, dtype=np.int32)
+    w.history = alloc_free_history(seed, w.num_blocks, w.num_blocks - need, 2000)
+    return w
+
+
+def config3() -> Workload:
+    """Large bf16 decode batch: 256 sequences, context lognormal with median 1024
+    (sigma 1.0 in natural log), capped at 8192; 32/8 heads, d=128, blocks of 16;
+    pool 1.2x the total blocks with a shuffled free list."""
+    seed = 3
+    g = rng_for(seed, _STREAM_LENGTHS)
+    L = np.clip(np.rint(g.lognormal(np.log(1024.0), 1.0, size=256)), 1, 8192).astype(np.int32)
+    w = Workload("cfg3_large_decode_bf16", seed, "bf16", "bf16", 32, 8, 128, 16,
+                 L, np.ones(256, np.int32), 0, np.zeros(0, np.int32), partition_size=256)
+    w.num_blocks = _pool_1p2(w.blocks_needed())
+    w.free_order = _permutation(seed, w.num_blocks)
+    return w
+
+
+def config4() -> Workload:
+    """Long-context bf16 decode with split context: 16 sequences of U{32k..128k}
+    tokens, 64/8 heads, d=128, blocks of 32, 512-token partitions; values N(0, 0.5)."""
+    seed = 4
+    g = rng_for(seed, _STREAM_LENGTHS)
+    L = g.integers(32768, 131072, size=16, endpoint=True).astype(np.int32)
+    w = Workload("cfg4_long_context_bf16", seed, "bf16", "bf16", 64, 8, 128, 32,
+                 L, np.ones(16, np.int32), 0, np.zeros(0, np.int32),
+                 partition_size=512, sigma=0.5)
+    w.num_blocks = _pool_1p2(w.blocks_needed())
+    w.free_order = _permutation(seed, w.num_blocks)
+    return w
+
+
+def alloc_free_history(seed: int, pool_blocks: int, final_budget: int, n_ops: int) -> List[Tuple]:
+    """A seeded list of pool requests from dummy owners: ("alloc", owner, n) with
+    n in 1..64, or ("free", owner). Only counts are tracked here (never block ids).
+    During the first n_ops requests the dummies may hold the whole pool, which
+    churns the free list; then random dummies are freed until they hold at most
+    `final_budget` blocks, and the rest stay live as holes."""
+    g = rng_for(seed, _STREAM_HISTORY)
+    ops: List[Tuple] = []
+    live: List[Tuple[int, int]] = []   # (owner, n)
+    held = 0
+    next_owner = 0
+    for _ in range(n_ops):
+        want_alloc = (not live) or g.random() < 0.55
+        if want_alloc:
+            n = int(g.integers(1, 64, endpoint=True))
+            if held + n <= pool_blocks:
+                ops.append(("alloc", next_owner, n))
+                live.append((next_owner, n))
+                held += n
+                next_owner += 1
+                continue
+            if not live:
+                continue
+        i = int(g.integers(0, len(live)))
+        owner, n = live.pop(i)
+        ops.append(("free", owner))
+        held -= n
+    while held > final_budget:
+        i = int(g.integers(0, len(live)))
+        owner, n = live.pop(i)
+        ops.append(("free", owner))
+        held -= n
+    return ops
+
+
+def small_decode(seed: int, seq_lens, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                 block_size=16, dtype="f32", cache_dtype=None, pool_extra=7,
+                 sigma=1.0, partition_size=0) -> Workload:
+    """A small decode step with a seeded permuted pool (test helper)."""
+    L = np.asarray(seq_lens, np.int32)
+    w = Workload(f"small_decode_{seed}", seed, dtype, cache_dtype or dtype, num_q_heads,
+                 num_kv_heads, head_dim, block_size, L, np.ones(len(L), np.int32), 0,
+                 np.zeros(0, np.int32), sigma=sigma, partition_size=partition_size)
+    w.num_blocks = int(w.blocks_needed().sum()) + pool_extra
+    w.free_order = _permutation(seed, w.num_blocks)
+    return w
+
+
+def small_varlen(seed: int, seq_lens, q_lens, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                 block_size=16, dtype="bf16", cache_dtype=None, pool_extra=5) -> Workload:
+    """A small mixed step (decode rows and prefill chunks) with a permuted pool."""
+    L = np.asarray(seq_lens, np.int32)
+    q = np.asarray(q_lens, np.int32)
+    w = Workload(f"small_varlen_{seed}", seed, dtype, cache_dtype or dtype, num_q_heads,
+                 num_kv_heads, head_dim, block_size, L, q, 0, np.zeros(0, np.int32))
+    w.num_blocks = int(w.blocks_needed().sum()) + pool_extra
+    w.free_order = _permutation(seed, w.num_blocks)
+    return w
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}
+
+
+def config(n: int) -> Workload:
+    return CONFIGS[n]()
