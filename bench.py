@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark: one continuous-batching decode step of attention over a paged KV cache
+on one MI355X, through libpkv's C ABI.
+
+A step is the whole hot path for that batch: the cache write of the step's new K/V
+(one token per sequence) followed by paged decode attention (partition pass plus the
+log-sum-exp merge). Inputs (cache contents, queries, tables) are resident in HBM
+before the timed region; block tables come from libpkv's host pool.
+
+Default workload: the large decode batch -- 256 sequences with lognormal contexts
+(median 1024, sigma 1, capped at 8192), 32 query / 8 KV heads, head_dim 128, blocks
+of 16 tokens, bf16, a pool 1.2x the need with shuffled block ids.
+
+Prints one JSON line. `value` is decode HBM GB/s: algorithmic bytes of the decode
+launch (K/V of every context token, queries, outputs, block-table entries, lengths)
+divided by the decode time (partition pass + merge), timed with HIP events on the
+launch stream. `roofline` reports the partition pass alone against the 8 TB/s HBM
+peak. `cpu_baseline` times the CPU oracle on a bounded prefix of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "paged-attn decode HBM GB/s (% of peak) + attention tokens/s per step"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg3", choices=["cfg3", "cfg4"])
+    ap.add_argument("--partition", type=int, default=None, help="split-context partition (tokens); 0 = none")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one decode launch (each byte the math must touch, once)."""
+    import numpy as np
+    e_kv = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    e_q = {"f32": 4, "bf16": 2}[w.dtype]
+    L = w.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_dim * e_kv
+    qo = w.num_seqs * w.num_q_heads * w.head_dim * 2 * e_q
+    tables = int(((L + w.block_size - 1) // w.block_size).sum()) * 4
+    return kv + qo + tables + w.num_seqs * 4
+
+
+def write_bytes(w) -> int:
+    e_in = {"f32": 4, "bf16": 2}[w.dtype]
+    e_kv = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    T = int(w.q_lens.sum())
+    return T * 2 * w.num_kv_heads * w.head_dim * (e_in + e_kv) + T * 8
+
+
+def setup_device(w, partition):
+    """Pool + tables (libpkv host), K/V generated on the GPU, context written by the
+    cache-write kernel; returns the tensors of one decode step."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_42_amd as pkv
+    import workloads.gpu as wgen
+
+    pool = pkv.Pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.cache_dtype, free_order=w.free_order)
+    for s, L in enumerate(w.seq_lens):
+        pool.seq_reserve(s, int(L))
+    W = w.max_blocks_per_seq()
+    ids = np.arange(w.num_seqs)
+    prior = (w.seq_lens - w.q_lens).astype(np.int32)
+    _, _, ctx_slots = pool.build_block_table(ids, prior, prior, W)
+    bt, cu, slots = pool.build_block_table(ids, w.q_lens, w.seq_lens, W)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    k_cache = torch.empty(shape, dtype=dt, device="cuda")
+    v_cache = torch.empty(shape, dtype=dt, device="cuda")
+    Hkv, Hq, d = w.num_kv_heads, w.num_q_heads, w.head_dim
+    n_new = int(w.q_lens.sum())
+    new_k = torch.empty((n_new, Hkv, d), dtype=dt, device="cuda")
+    new_v = torch.empty_like(new_k)
+    q = torch.empty((n_new, Hq, d), dtype=dt, device="cuda")
+    # the context is written in chunks of sequences to bound the staging buffers
+    on = 0
+    chunk_tokens = 1 << 20
+    s0 = 0
+    slot_off = 0
+    while s0 < w.num_seqs:
+        s1, tok = s0, 0
+        while s1 < w.num_seqs and (tok == 0 or tok + int(prior[s1]) <= chunk_tokens):
+            tok += int(prior[s1])
+            s1 += 1
+        ck = torch.empty((tok, Hkv, d), dtype=dt, device="cuda")
+        cv = torch.empty_like(ck)
+        o = 0
+        for s in range(s0, s1):
+            p = int(prior[s])
+            if p:
+                wgen.fill(ck[o:o + p], w.value_key("k", s), 0, w.sigma)
+                wgen.fill(cv[o:o + p], w.value_key("v", s), 0, w.sigma)
+            o += p
+        if tok:
+            sl = torch.from_numpy(ctx_slots[slot_off:slot_off + tok].copy()).cuda()
+            pkv.kv_cache_write(ck, cv, k_cache, v_cache, sl, w.block_size)
+        slot_off += tok
+        s0 = s1
+        del ck, cv
+    for s in range(w.num_seqs):
+        p, L = int(prior[s]), int(w.seq_lens[s])
+        wgen.fill(new_k[on:on + L - p], w.value_key("k", s), p * Hkv * d, w.sigma)
+        wgen.fill(new_v[on:on + L - p], w.value_key("v", s), p * Hkv * d, w.sigma)
+        wgen.fill(q[on:on + L - p], w.value_key("q", s), p * Hq * d, w.sigma)
+        on += L - p
+    msl = int(w.seq_lens.max())
+    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, Hq, d, msl, partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    return dict(pool=pool, k_cache=k_cache, v_cache=v_cache, new_k=new_k, new_v=new_v, q=q,
+                out=torch.empty_like(q), slots=torch.from_numpy(slots).cuda(), bt=torch.from_numpy(bt).cuda(),
+                lens=torch.from_numpy(w.seq_lens.astype(np.int32)).cuda(), ws=ws, max_seq_len=msl)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (float64 NumPy, as it stands) on a prefix of the batch, sequence by
+    sequence, until `budget_s` seconds of oracle time; inputs prepared untimed."""
+    import numpy as np
+    import workloads
+    from oracle import attention as oatt
+    from oracle import cache as ocache
+    from oracle.allocator import BlockPool, SeqTables
+    from oracle.metadata import build_block_table
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+
+    tabs = SeqTables(BlockPool(w.num_blocks, w.free_order), w.block_size)
+    for s, L in enumerate(w.seq_lens):
+        tabs.reserve(s, int(L))
+    kp = np.zeros((w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim), np.uint16)
+    vp = np.zeros_like(kp)
+    spent, done, tokens = 0.0, 0, 0
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        t = [tabs.tables[s]]
+        _, _, slots = build_block_table(t, [L], [L], w.block_size, len(t[0]))
+        k, v = w.kv(s)
+        ocache.write(kp, k, w.dtype, w.cache_dtype, slots)
+        ocache.write(vp, v, w.dtype, w.cache_dtype, slots)
+        bt, cu, _ = build_block_table(t, [1], [L], w.block_size, len(t[0]))
+        q = workloads.storage_to_f64(w.q(s), w.dtype)
+        t0 = time.perf_counter()
+        oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, [L], cu, w.softmax_scale, w.group)
+        spent += time.perf_counter() - t0
+        done += 1
+        tokens += L
+        if spent >= budget_s:
+            break
+    e_kv = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    nbytes = tokens * 2 * w.num_kv_heads * w.head_dim * e_kv
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {w.num_seqs} sequences ({tokens} context tokens, {nbytes / 1e9:.3f} GB of "
+                      f"K/V), float64 NumPy oracle, {spent:.1f} s; cores = BLAS threads"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import paged_kv_cache_42_amd as pkv
+    import workloads
+
+    w = workloads.config3() if args.workload == "cfg3" else workloads.config4()
+    P = w.partition_size if args.partition is None else args.partition
+    print(f"[bench] {w.name}: B={w.num_seqs} sumL={int(w.seq_lens.sum())} P={P}; setting up", file=sys.stderr,
+          flush=True)
+    dev = setup_device(w, P)
+    stream = torch.cuda.current_stream()
+    scale = w.softmax_scale
+
+    def step(mid_event=None):
+        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size)
+        if mid_event is not None:
+            mid_event[0].record(stream)
+        pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
+                                   w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, 1.0, 1.0, P, dev["ws"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for e in ev:        # materialise the event handles before use by the library hook
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e0, e1, e2, e3 = ev[i]
+        e0.record(stream)
+        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size)
+        e1.record(stream)
+        pkv.decode_set_profile_event(e2)
+        pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
+                                   w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, 1.0, 1.0, P, dev["ws"])
+        pkv.decode_set_profile_event(None)
+        e3.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_part = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e-3
+
+    dbytes = decode_bytes(w)
+    t_dec = float((t_part + t_merge).mean())
+    gbs = dbytes / t_dec / 1e9
+    part_gbs = dbytes / float(t_part.mean()) / 1e9
+    ms_step = wall / K * 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.cache_dtype,
+        "data": "synthetic (seeded counter-hash values, Irwin-Hall(3) approximation of N(0,1), exact in bf16)",
+        "config": {"workload": f"{w.name}: {w.num_seqs} decode rows, context lognormal median 1024 sigma 1 cap 8192"
+                               if args.workload == "cfg3" else
+                               f"{w.name}: {w.num_seqs} decode rows, context U[32k,128k]",
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "context_tokens": int(w.seq_lens.sum()),
+                   "partition_size": P, "num_blocks": w.num_blocks},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "context_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
+        "kernel_us": {"kv_cache_write": round(float(t_write.mean()) * 1e6, 2),
+                      "decode_partition_pass": round(float(t_part.mean()) * 1e6, 2),
+                      "decode_merge": round(float(t_merge.mean()) * 1e6, 2),
+                      "step_events": round(float(t_step.mean()) * 1e6, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(part_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(part_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode partition pass", "algorithmic_bytes": dbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

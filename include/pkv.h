@@ -1,0 +1,174 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged KV cache on MI355X (gfx950).
+ *
+ * The method (PagedAttention with continuous batching) is described on these pages:
+ *   [P17] "Project 17: Production Serving: Continuous Batching and PagedAttention"
+ *         (llm-under-the-hood), sections "The Concept", "Step 4: Implement the paged
+ *         KV cache", "Step 6: Implement attention over paged storage".
+ *   [CB]  "Continuous Batching" (infra.pidoku inference-engineering notes), sections
+ *         "4. Tiny example", "5. Technical explanation", "6. Under the hood".
+ *   [PY]  "Build a pure-Python continuous batching LLM serving engine from scratch",
+ *         "Step 2: Implement the PagedAttention KV Cache Manager".
+ *   [TV]  tiny-vllm code reading, part 7 (jaehun.me), "Uploading the active arrays to
+ *         the GPU", "Termination and returning blocks".
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (PKV_OK) or a negative status; nothing is thrown across the ABI.
+ *     On an error return no host state has changed and no kernel was launched;
+ *     pkv_last_error() gives a message (per thread).
+ *   - "host" pointers are CPU memory owned by the caller; "device" pointers are GPU
+ *     memory owned by the caller (the library never allocates device memory).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Device work is
+ *     asynchronous on that stream; PKV_ERR_HIP reports a failed launch.
+ *   - KV cache layout, per layer: two planes, K and V, each row-major
+ *     [num_blocks][block_size][num_kv_heads][head_dim] (the [P17] Step 6 pool axes with
+ *     the K/V axis hoisted into separate planes). Flat slot = block * block_size + offset.
+ *   - Dtype codes: PKV_F32, PKV_BF16 (raw bfloat16), PKV_FP8_E4M3 (OCP E4M3, cache only;
+ *     value = code * per-tensor scale).
+ *   - Query head h uses KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_ERR_INVALID (-1)
+#define PKV_ERR_OUT_OF_BLOCKS (-2)
+#define PKV_ERR_HIP (-3)
+#define PKV_ERR_UNSUPPORTED (-4)
+
+#define PKV_F32 0
+#define PKV_BF16 1
+#define PKV_FP8_E4M3 2
+
+typedef struct pkv_pool pkv_pool;
+
+/* Library version string (static storage). */
+const char* pkv_version(void);
+/* Message of the last error returned on this thread (static per-thread storage). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------------------
+ * Host block pool and per-sequence block tables.
+ * [P17] "Step 4": one pool of fixed-size pages and a free list; a page is taken from
+ * the END of the free list and a freed page is appended; a finished sequence returns
+ * its pages in page-table order. [PY] "Step 2": a multi-block request is
+ * all-or-nothing and fails when fewer blocks are free. The pool is host state only
+ * (no device memory); it is not thread-safe.
+ * ---------------------------------------------------------------------------- */
+
+/* Create a pool of num_blocks ids. initial_free_order (host, num_blocks ids, a
+ * permutation of 0..num_blocks-1) is the initial free list, popped from its end;
+ * NULL means 0..num_blocks-1. plane_bytes (nullable) receives the byte size of one
+ * K or V plane of one layer for this geometry. Errors: INVALID on bad sizes,
+ * dtype or a non-permutation. */
+int pkv_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t cache_dtype, const int32_t* initial_free_order,
+                   pkv_pool** out, int64_t* plane_bytes);
+void pkv_destroy_pool(pkv_pool* pool);
+
+/* Pop n ids from the end of the free list into out_ids (host, n entries), in pop
+ * order. OUT_OF_BLOCKS (nothing taken) if fewer than n are free. */
+int pkv_pool_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids);
+/* Append ids (host, n entries) to the free list in the given order. INVALID (nothing
+ * freed) if an id is out of range, not allocated, repeated, or held by a sequence. */
+int pkv_pool_free(pkv_pool* pool, const int32_t* ids, int32_t n);
+/* Counters: free blocks, sequences holding a table (either pointer nullable). */
+int pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* live_seqs);
+/* Copy the free list, bottom to top (the next pop is the last entry), into out
+ * (host, capacity entries); *count = its length. INVALID if capacity is too small. */
+int pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t capacity, int32_t* count);
+
+/* Grow sequence seq_id's table to ceil(total_tokens / block_size) blocks (never
+ * shrinks; creates the sequence if new). New ids are popped as by pkv_pool_alloc
+ * and appended to the table. OUT_OF_BLOCKS: nothing changes. */
+int pkv_seq_reserve(pkv_pool* pool, int64_t seq_id, int32_t total_tokens);
+/* Free seq_id's whole table in table order and forget the sequence. INVALID if unknown. */
+int pkv_seq_release(pkv_pool* pool, int64_t seq_id);
+/* Copy seq_id's table (host, capacity entries); *count = its length. */
+int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* out, int32_t capacity,
+                  int32_t* count);
+
+/* Per-step metadata ([CB] "6. Under the hood": cu_seqlens, block_tables
+ * (num_seqs, max_blocks), seq_lens; [P17] "Step 4": position p lives in page p/bs at
+ * slot p%bs). For sequence s (host arrays of num_seqs entries): seq_lens[s] counts its
+ * tokens after this step's q_lens[s] new tokens are written ([TV]: the current token's
+ * K/V is stored before attention), the new tokens being positions
+ * seq_lens[s]-q_lens[s] .. seq_lens[s]-1. Outputs (host):
+ *   block_tables [num_seqs][table_width] int32: table[s][j] for j < ceil(seq_lens[s]/bs),
+ *                 -1 elsewhere;
+ *   cu_seqlens_q [num_seqs+1] int32: exclusive prefix sum of q_lens;
+ *   slot_mapping [sum q_lens] int64: table[s][p/bs]*bs + p%bs for each new token.
+ * INVALID if a sequence is unknown, q_len > seq_len, its table is shorter than
+ * ceil(seq_len/bs), or table_width is too small. */
+int pkv_build_block_table(const pkv_pool* pool, int32_t num_seqs, const int64_t* seq_ids,
+                          const int32_t* q_lens, const int32_t* seq_lens, int32_t table_width,
+                          int32_t* block_tables, int32_t* cu_seqlens_q, int64_t* slot_mapping);
+
+/* ------------------------------------------------------------------------------
+ * Device kernels.
+ * ---------------------------------------------------------------------------- */
+
+/* Cache write ([P17] "Step 4", append): for each new token i < num_tokens and KV head
+ * h, k_cache[slot_i][h][:] = enc(k[i][h][:]) and the same for v, slot_i =
+ * slot_mapping[i]. k, v: device [num_tokens][num_kv_heads][head_dim] in in_dtype.
+ * k_cache, v_cache: device planes (layout above, num_blocks blocks) in cache_dtype.
+ * slot_mapping: device int64 [num_tokens]; a slot < 0 or >= num_blocks*block_size
+ * skips the token. enc: bit copy when in_dtype == cache_dtype (f32, bf16); for an
+ * E4M3 cache, y = fl32(x * fl32(1/scale)) rounded to nearest-even E4M3, |y| >= 448
+ * saturating to 448 with y's sign, NaN -> 0x7F with y's sign. Supported
+ * (in, cache): (f32,f32), (bf16,bf16), (bf16,fp8), (f32,fp8); else UNSUPPORTED.
+ * Two tokens mapped to one slot race (the result is one of them). */
+int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
+                       int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
+                       const int64_t* slot_mapping, float k_scale, float v_scale, void* stream);
+
+/* Bytes of device workspace that pkv_paged_attention_decode needs for this shape
+ * (0 when partition_size is 0 or no sequence can span two partitions). */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t partition_size);
+
+/* Decode attention, one query token per sequence ([P17] "Step 6": walk the page table,
+ * score each key against the query scaled by `scale`, softmax, sum the values).
+ * q: device [num_seqs][num_q_heads][head_dim] (q_dtype f32 or bf16); out: device,
+ * same shape and dtype. The query of sequence s sits at position seq_lens[s]-1 and
+ * sees keys 0..seq_lens[s]-1. block_tables: device int32 [num_seqs][table_width];
+ * seq_lens: device int32 [num_seqs], each in 0..min(max_seq_len, table_width*bs)
+ * (a sequence with seq_len 0 gets zeros and log-sum-exp -inf; larger values are
+ * clamped to that bound); table entries outside 0..num_blocks-1 are skipped.
+ * Keys are decoded as code * k_scale (values * v_scale) for an E4M3 cache; pass 1.0
+ * otherwise. Supported: (q, cache) in {(f32,f32), (bf16,bf16), (bf16,fp8)};
+ * head_dim 64 or 128; block_size 16 or 32; num_q_heads/num_kv_heads in {1,2,4,8}.
+ * partition_size 0 processes each sequence in one pass; otherwise (a multiple of
+ * block_size) the context is split into partitions of that many tokens whose partial
+ * results are merged by log-sum-exp in a second kernel, using `workspace` (device,
+ * >= pkv_decode_workspace_bytes). lse_out (device float [num_seqs][num_q_heads],
+ * nullable) receives the natural-log log-sum-exp of the scaled scores. */
+int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                               const void* v_cache, int32_t cache_dtype,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t table_width, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_seq_len, float scale,
+                               float k_scale, float v_scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, float* lse_out,
+                               void* stream);
+
+/* Profiling hook (for timing the partition pass alone): while `hip_event` (a
+ * hipEvent_t) is not NULL, every pkv_paged_attention_decode call made on this thread
+ * records it on its stream right after the partition pass, before the merge kernel
+ * (if any). NULL turns the hook off. The caller owns the event. */
+void pkv_decode_set_profile_event(void* hip_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

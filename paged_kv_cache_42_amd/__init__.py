@@ -1,0 +1,10 @@
+"""MI355X-native attention over a paged KV cache (libpkv, HIP for gfx950).
+
+The compute lives in libpkv.so (C++ host code + HIP kernels, C ABI in include/pkv.h);
+this package is its thin Python binding. Build with
+`python -m paged_kv_cache_42_amd.build`.
+"""
+from ._lib import (  # noqa: F401
+    BF16, F32, FP8, OutOfBlocks, PkvError, Pool, decode_set_profile_event, decode_workspace_bytes, header_functions, kv_cache_write, lib,
+    paged_attention_decode,
+)

@@ -1,0 +1,274 @@
+"""ctypes binding of libpkv (argument marshalling only).
+
+Every compute step runs in libpkv's HIP kernels or its C++ host code; this module
+only converts torch tensors / numpy arrays to pointers and sizes, and raises on a
+non-zero status. It fails loudly when libpkv.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pkv.h")
+
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_HIP, PKV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+F32, BF16, FP8 = 0, 1, 2
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libpkv status {status}: {msg}")
+        self.status = status
+
+
+class OutOfBlocks(PkvError):
+    pass
+
+
+_lib = None
+
+i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+P_i32 = C.POINTER(C.c_int32)
+P_i64 = C.POINTER(C.c_int64)
+
+_SIGS = {
+    "pkv_version": (C.c_char_p, []),
+    "pkv_last_error": (C.c_char_p, []),
+    "pkv_alloc_pool": (C.c_int, [i32, i32, i32, i32, i32, vp, C.POINTER(vp), P_i64]),
+    "pkv_destroy_pool": (None, [vp]),
+    "pkv_pool_alloc": (C.c_int, [vp, i32, vp]),
+    "pkv_pool_free": (C.c_int, [vp, vp, i32]),
+    "pkv_pool_stats": (C.c_int, [vp, P_i32, P_i32]),
+    "pkv_pool_free_list": (C.c_int, [vp, vp, i32, P_i32]),
+    "pkv_seq_reserve": (C.c_int, [vp, i64, i32]),
+    "pkv_seq_release": (C.c_int, [vp, i64]),
+    "pkv_seq_table": (C.c_int, [vp, i64, vp, i32, P_i32]),
+    "pkv_build_block_table": (C.c_int, [vp, i32, vp, vp, vp, i32, vp, vp, vp]),
+    "pkv_kv_cache_write": (C.c_int, [vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, f32, f32, vp]),
+    "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+    "pkv_decode_set_profile_event": (None, [vp]),
+    "pkv_paged_attention_decode": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, f32, f32, f32, i32, vp, sz, vp, vp]),
+}
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/pkv.h."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", txt)))
+
+
+def lib():
+    """Load libpkv.so (once); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_42_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().pkv_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != PKV_OK:
+        msg = last_error()
+        if status == PKV_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(status, msg)
+        raise PkvError(status, msg)
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(vp)
+
+
+# ----------------------------------------------------------------------------
+# host pool
+# ----------------------------------------------------------------------------
+
+class Pool:
+    """pkv_pool handle: block pool + per-sequence tables (host state)."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 cache_dtype: str = "bf16", free_order: Optional[Sequence[int]] = None):
+        self.block_size = int(block_size)
+        self.num_blocks = int(num_blocks)
+        h = vp()
+        pb = i64()
+        order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        check(lib().pkv_alloc_pool(num_blocks, block_size, num_kv_heads, head_dim,
+                                   DTYPE_CODES[cache_dtype], _np_ptr(order), C.byref(h), C.byref(pb)))
+        self._h = h
+        self.plane_bytes = int(pb.value)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pkv_destroy_pool(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def alloc(self, n: int) -> list:
+        out = np.zeros(max(n, 1), np.int32)
+        check(lib().pkv_pool_alloc(self._h, n, _np_ptr(out)))
+        return out[:n].tolist()
+
+    def free(self, ids: Sequence[int]) -> None:
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        check(lib().pkv_pool_free(self._h, _np_ptr(a), len(a)))
+
+    def stats(self):
+        f, s = i32(), i32()
+        check(lib().pkv_pool_stats(self._h, C.byref(f), C.byref(s)))
+        return int(f.value), int(s.value)
+
+    def free_list(self) -> list:
+        n = i32()
+        out = np.zeros(max(self.num_blocks, 1), np.int32)
+        check(lib().pkv_pool_free_list(self._h, _np_ptr(out), len(out), C.byref(n)))
+        return out[: n.value].tolist()
+
+    def seq_reserve(self, seq_id: int, total_tokens: int) -> None:
+        check(lib().pkv_seq_reserve(self._h, int(seq_id), int(total_tokens)))
+
+    def seq_release(self, seq_id: int) -> None:
+        check(lib().pkv_seq_release(self._h, int(seq_id)))
+
+    def seq_table(self, seq_id: int) -> list:
+        n = i32()
+        out = np.zeros(max(self.num_blocks, 1), np.int32)
+        check(lib().pkv_seq_table(self._h, int(seq_id), _np_ptr(out), len(out), C.byref(n)))
+        return out[: n.value].tolist()
+
+    def build_block_table(self, seq_ids, q_lens, seq_lens, table_width: int):
+        """Returns numpy (block_tables [B][W] int32, cu_seqlens_q [B+1] int32, slot_mapping int64)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        q = np.ascontiguousarray(q_lens, dtype=np.int32)
+        L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B = len(ids)
+        bt = np.zeros((B, table_width), np.int32)
+        cu = np.zeros(B + 1, np.int32)
+        slots = np.zeros(max(int(q.sum()) if B else 0, 1), np.int64)
+        check(lib().pkv_build_block_table(self._h, B, _np_ptr(ids), _np_ptr(q), _np_ptr(L), table_width,
+                                          _np_ptr(bt), _np_ptr(cu), _np_ptr(slots)))
+        return bt, cu, slots[: int(cu[-1])]
+
+
+# ----------------------------------------------------------------------------
+# device entry points (torch tensors supply memory and the stream)
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return vp(stream.cuda_stream)
+
+
+def tensor_dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+        return FP8
+    raise ValueError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _require_cuda_contig(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("device tensor expected (libpkv computes on the GPU only)")
+        if not t.is_contiguous():
+            raise ValueError("contiguous tensor expected")
+
+
+def _check_plane(k_cache, v_cache, block_size, Hkv, d):
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (block_size, Hkv, d):
+        raise ValueError(f"cache plane must be [num_blocks][{block_size}][{Hkv}][{d}], got {tuple(k_cache.shape)}")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("K and V planes must have the same shape and dtype")
+
+
+def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scale: float = 1.0,
+                   v_scale: float = 1.0, stream=None) -> None:
+    """k, v: [T][Hkv][d]; caches: [num_blocks][block_size][Hkv][d]; slot_mapping int64 [T]."""
+    torch = _torch()
+    _require_cuda_contig(k, v, k_cache, v_cache, slot_mapping)
+    if k.dim() != 3 or v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must both be [T][Hkv][d] of one dtype")
+    T, Hkv, d = k.shape
+    _check_plane(k_cache, v_cache, block_size, Hkv, d)
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    check(lib().pkv_kv_cache_write(_dptr(k), _dptr(v), tensor_dtype_code(k), T, Hkv, d, _dptr(k_cache),
+                                   _dptr(v_cache), tensor_dtype_code(k_cache), k_cache.shape[0], block_size,
+                                   _dptr(slot_mapping), k_scale, v_scale, _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                           partition_size: int) -> int:
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int,
+                           block_size: int, max_seq_len: int, scale: float, k_scale: float = 1.0,
+                           v_scale: float = 1.0, partition_size: int = 0, workspace=None, lse=None,
+                           stream=None) -> None:
+    """q/out: [B][Hq][d]; block_tables int32 [B][W]; seq_lens int32 [B]."""
+    torch = _torch()
+    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, workspace, lse)
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [B][Hq][d] of one dtype")
+    B, Hq, d = q.shape
+    _check_plane(k_cache, v_cache, block_size, num_kv_heads, d)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][W]")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be float32 [B][Hq]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().pkv_paged_attention_decode(
+        _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+        _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
+        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, partition_size, _dptr(workspace), ws_bytes,
+        _dptr(lse), _stream(stream)))
+
+
+def decode_set_profile_event(event) -> None:
+    """Record torch.cuda.Event `event` after the decode partition pass (None: off)."""
+    if event is None:
+        lib().pkv_decode_set_profile_event(None)
+        return
+    lib().pkv_decode_set_profile_event(vp(event.cuda_event))

@@ -1,0 +1,571 @@
+// paged_attention_decode: one query token per sequence over a paged KV cache.
+//
+// What is computed follows "Project 17: Production Serving: Continuous Batching and
+// PagedAttention", "Step 6: Implement attention over paged storage": walk the
+// sequence's page table, score every cached key against the query (scaled), softmax
+// over the scores, and sum the cached values with those weights -- per query head,
+// with query head h reading KV head h / G.
+//
+// How it is computed on gfx950 (the page's two-pass loop is replaced):
+//  * Work item = (sequence s, KV head g, context partition p). A workgroup of NW
+//    wave64s owns one item; its blocks are dealt round-robin to the waves.
+//  * GQA packing: the G query heads of KV head g are held in registers together, so
+//    each K/V element loaded from HBM serves all G heads.
+//  * Gather: a block id comes from the block table (wave-uniform, scalar load); each
+//    lane then loads 16 bytes (8 bytes for E4M3) of one token's [head_dim] row. A
+//    token row is LPT lanes wide, so one load instruction covers TPL = 64/LPT tokens.
+//  * Scores: per-lane partial dot products, summed over the LPT lanes of a token with
+//    DPP row operations (no LDS).
+//  * Online softmax per row group (the lanes sharing a token slot): running max m,
+//    running sum l and a [G][EPL] accumulator, rescaled once per 16-token tile. Row
+//    groups, then waves, are merged by log-sum-exp at the end (shuffles, then LDS).
+//  * Split context: with partition_size > 0 a sequence longer than one partition
+//    writes per-partition (normalised output, log-sum-exp) partials and a second
+//    kernel merges them; a sequence that fits in one partition writes its output
+//    directly.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxPartitions = 8192;   // merge keeps one float per partition in LDS
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// Cache element traits: bytes per lane per load, elements per lane per load.
+template <int CDT>
+struct Cache;
+template <>
+struct Cache<PKV_F32> {
+  static constexpr int EPL = 4;
+  using Vec = uint4;
+};
+template <>
+struct Cache<PKV_BF16> {
+  static constexpr int EPL = 8;
+  using Vec = uint4;
+};
+template <>
+struct Cache<PKV_FP8_E4M3> {
+  static constexpr int EPL = 8;
+  using Vec = uint2;
+};
+
+template <int CDT>
+__device__ __forceinline__ void unpack(const typename Cache<CDT>::Vec& x, float (&f)[Cache<CDT>::EPL]) {
+  if constexpr (CDT == PKV_F32) {
+    f[0] = __uint_as_float(x.x);
+    f[1] = __uint_as_float(x.y);
+    f[2] = __uint_as_float(x.z);
+    f[3] = __uint_as_float(x.w);
+  } else if constexpr (CDT == PKV_BF16) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = pkv::bf16_lo(w[j]);
+      f[2 * j + 1] = pkv::bf16_hi(w[j]);
+    }
+  } else {
+    const uint32_t w[2] = {x.x, x.y};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = pkv::fp8_to_f32(w[j >> 2] >> (8 * (j & 3)));
+  }
+}
+
+template <int CDT>
+__device__ __forceinline__ typename Cache<CDT>::Vec zero_vec() {
+  if constexpr (CDT == PKV_FP8_E4M3)
+    return make_uint2(0, 0);
+  else
+    return make_uint4(0, 0, 0, 0);
+}
+
+struct DecodeArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws_o;       // [B][Hq][pmax][D]
+  float* ws_lse;     // [B][Hq][pmax] (log2 domain)
+  float* lse_out;    // [B][Hq] natural log, nullable
+  int table_width;
+  int num_kv_heads;
+  int num_blocks;
+  int len_clamp;     // min(max_seq_len, table_width * block_size)
+  int part_tokens;   // 0 = whole context in one item
+  int pmax;
+  float zscale;      // softmax scale * k_scale * log2(e)
+  float v_scale;
+};
+
+template <int QDT, int CDT, int D, int G, int BS, int NW>
+__global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
+  using Vec = typename Cache<CDT>::Vec;
+  constexpr int EPL = Cache<CDT>::EPL;
+  constexpr int LPT = D / EPL;                 // lanes per token row
+  constexpr int TPL = 64 / LPT;                // tokens per load instruction
+  constexpr int TILE = BS < 16 ? BS : 16;      // tokens per softmax update
+  constexpr int NLT = TILE / TPL;              // loads per tile (each of K and V)
+  constexpr int SUB = BS / TILE;               // tiles per block
+  constexpr bool DOT2 = (QDT == PKV_BF16 && CDT == PKV_BF16);
+  static_assert(NLT >= 1 && TILE % TPL == 0, "tile too small for this row width");
+
+  const int g = blockIdx.x;
+  const int p = blockIdx.y;
+  const int s = blockIdx.z;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * G;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r = lane / LPT;
+  const int c = lane % LPT;
+
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+  int tok_begin = 0, tok_end = L, nparts = 1;
+  if (a.part_tokens > 0) {
+    nparts = (L + a.part_tokens - 1) / a.part_tokens;
+    if (nparts < 1) nparts = 1;
+    if (p >= nparts) return;
+    tok_begin = p * a.part_tokens;
+    tok_end = min(L, tok_begin + a.part_tokens);
+  }
+  const int blk_begin = tok_begin / BS;
+  const int blk_end = (tok_end + BS - 1) / BS;
+
+  // ---- queries of the G packed heads, this lane's EPL-wide slice of head_dim
+  constexpr int QW = DOT2 ? EPL / 2 : EPL;     // words (bf16 pairs) or floats per head
+  float qf[DOT2 ? 1 : G][DOT2 ? 1 : EPL];
+  uint32_t qp[DOT2 ? G : 1][DOT2 ? QW : 1];
+  {
+    const int64_t qbase = (int64_t(s) * Hq + int64_t(g) * G) * D + c * EPL;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if constexpr (QDT == PKV_F32) {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qbase + h * D);
+        qf[h][0] = v.x;
+        qf[h][1] = v.y;
+        qf[h][2] = v.z;
+        qf[h][3] = v.w;
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qbase + h * D);
+        if constexpr (DOT2) {
+          qp[h][0] = v.x;
+          qp[h][1] = v.y;
+          qp[h][2] = v.z;
+          qp[h][3] = v.w;
+        } else {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            qf[h][2 * j] = pkv::bf16_lo(wv[j]);
+            qf[h][2 * j + 1] = pkv::bf16_hi(wv[j]);
+          }
+        }
+      }
+    }
+  }
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const Vec* kc = static_cast<const Vec*>(a.k_cache);
+  const Vec* vc = static_cast<const Vec*>(a.v_cache);
+  const int64_t row_vecs = int64_t(Hkv) * LPT;          // Vec units per token row
+  const int64_t lane_off = int64_t(g) * LPT + c;        // this lane's Vec within the row
+  const int32_t* bt_row = a.block_tables + int64_t(s) * a.table_width;
+
+  // tiles owned by this wave: block j = blk_begin + w + NW*(n / SUB), sub-tile n % SUB
+  const int my_blocks = blk_end - blk_begin > w ? (blk_end - blk_begin - w + NW - 1) / NW : 0;
+  const int ntiles = my_blocks * SUB;
+
+  Vec kb[2][NLT], vb[2][NLT];
+  int tok0[2];
+  bool okb[2];
+
+  auto issue = [&](int n, Vec (&kr)[NLT], Vec (&vr)[NLT], int& t0, bool& ok) {
+    const int j = blk_begin + w + NW * (n / SUB);
+    const int sub = n % SUB;
+    const int blk = __builtin_amdgcn_readfirstlane(bt_row[j]);
+    ok = blk >= 0 && blk < a.num_blocks;
+    t0 = j * BS + sub * TILE;
+    const int64_t base = (int64_t(ok ? blk : 0) * BS + sub * TILE + r) * row_vecs + lane_off;
+#pragma unroll
+    for (int i = 0; i < NLT; ++i) {
+      if (ok) {
+        kr[i] = kc[base + int64_t(i) * TPL * row_vecs];
+        vr[i] = vc[base + int64_t(i) * TPL * row_vecs];
+      } else {
+        kr[i] = zero_vec<CDT>();
+        vr[i] = zero_vec<CDT>();
+      }
+    }
+  };
+
+  auto consume = [&](const Vec (&kr)[NLT], const Vec (&vr)[NLT], int t0, bool ok) {
+    float z[NLT][G];
+    bool valid[NLT];
+#pragma unroll
+    for (int i = 0; i < NLT; ++i) {
+      const int t = t0 + i * TPL + r;
+      valid[i] = ok && t < tok_end;
+      float part[G];
+      if constexpr (DOT2) {
+        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float sacc = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sacc = dot2_bf16(qp[h][j], kw[j], sacc);
+          part[h] = sacc;
+        }
+      } else {
+        float kf[EPL];
+        unpack<CDT>(kr[i], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float sacc = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) sacc = fmaf(qf[h][e], kf[e], sacc);
+          part[h] = sacc;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float zz = pkv::group_sum<LPT>(part[h]) * a.zscale;
+        z[i][h] = valid[i] ? zz : -INFINITY;
+      }
+    }
+    // online softmax update, once per tile
+    float pw[NLT][G];
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mt = z[0][h];
+#pragma unroll
+      for (int i = 1; i < NLT; ++i) mt = fmaxf(mt, z[i][h]);
+      const float mn = fmaxf(m[h], mt);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      alpha[h] = pkv::fast_exp2(m[h] - mref);
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < NLT; ++i) {
+        pw[i][h] = pkv::fast_exp2(z[i][h] - mref);
+        ls += pw[i][h];
+      }
+      l[h] = l[h] * alpha[h] + ls;
+      m[h] = mn;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+#pragma unroll
+    for (int i = 0; i < NLT; ++i) {
+      float vf[EPL];
+      unpack<CDT>(vr[i], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vf[e] = valid[i] ? vf[e] : 0.f;   // masked slots may hold NaN
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw[i][h], vf[e], acc[h][e]);
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(0, kb[0], vb[0], tok0[0], okb[0]);
+    int n = 0;
+    for (; n + 1 < ntiles; n += 2) {
+      issue(n + 1, kb[1], vb[1], tok0[1], okb[1]);
+      consume(kb[0], vb[0], tok0[0], okb[0]);
+      if (n + 2 < ntiles) issue(n + 2, kb[0], vb[0], tok0[0], okb[0]);
+      consume(kb[1], vb[1], tok0[1], okb[1]);
+    }
+    if (n < ntiles) consume(kb[0], vb[0], tok0[0], okb[0]);
+  }
+
+  // ---- merge the TPL row groups of the wave (lanes with equal c)
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float mn = fmaxf(m[h], mo);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float wa = pkv::fast_exp2(m[h] - mref);
+      const float wb = pkv::fast_exp2(mo - mref);
+      l[h] = l[h] * wa + lo * wb;
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * wa + ao * wb;
+      }
+    }
+  }
+
+  // ---- merge the NW waves through LDS
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
+  if (lane < LPT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (lane == 0) {
+        sm_m[w][h] = m[h];
+        sm_l[w][h] = l[h];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_acc[w][h][c * EPL + e] = acc[h][e];
+    }
+  }
+  __syncthreads();
+
+  const bool single = nparts == 1;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int e = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) M = fmaxf(M, sm_m[x][h]);
+    const float mref = M == -INFINITY ? 0.f : M;
+    float S = 0.f, A = 0.f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      const float wx = pkv::fast_exp2(sm_m[x][h] - mref);
+      S += sm_l[x][h] * wx;
+      A += sm_acc[x][h][e] * wx;
+    }
+    const float o = S > 0.f ? A / S * a.v_scale : 0.f;
+    const float lse2 = S > 0.f ? M + log2f(S) : -INFINITY;
+    const int hq = g * G + h;
+    if (single) {
+      const int64_t oi = (int64_t(s) * Hq + hq) * D + e;
+      if constexpr (QDT == PKV_F32)
+        static_cast<float*>(a.out)[oi] = o;
+      else
+        static_cast<uint16_t*>(a.out)[oi] = uint16_t(pkv::f32_to_bf16(o));
+      if (a.lse_out && e == 0) a.lse_out[int64_t(s) * Hq + hq] = lse2 * kLn2;
+    } else {
+      const int64_t pi = (int64_t(s) * Hq + hq) * a.pmax + p;
+      a.ws_o[pi * D + e] = o;
+      if (e == 0) a.ws_lse[pi] = lse2;
+    }
+  }
+}
+
+// Log-sum-exp merge of the partition partials of one (sequence, query head).
+template <int QDT, int D>
+__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_heads) {
+  extern __shared__ float sm_w[];
+  __shared__ float red[256 / 64];
+  const int hq = blockIdx.x;
+  const int s = blockIdx.y;
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  if (nparts <= 1) return;                     // written directly by the partition pass
+  const int64_t base = (int64_t(s) * num_q_heads + hq) * a.pmax;
+  const int tid = threadIdx.x;
+  // max over partitions
+  float M = -INFINITY;
+  for (int k = tid; k < nparts; k += blockDim.x) {
+    const float v = a.ws_lse[base + k];
+    sm_w[k] = v;
+    M = fmaxf(M, v);
+  }
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = red[0];
+  for (int x = 1; x < int(blockDim.x) / 64; ++x) M = fmaxf(M, red[x]);
+  __syncthreads();
+  const float mref = M == -INFINITY ? 0.f : M;
+  float S = 0.f;
+  for (int k = tid; k < nparts; k += blockDim.x) {
+    const float wk = pkv::fast_exp2(sm_w[k] - mref);
+    sm_w[k] = wk;
+    S += wk;
+  }
+  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+  if ((tid & 63) == 0) red[tid >> 6] = S;
+  __syncthreads();
+  S = 0.f;
+  for (int x = 0; x < int(blockDim.x) / 64; ++x) S += red[x];
+  // each thread owns one element of head_dim (threads >= D idle)
+  if (tid < D) {
+    float A = 0.f;
+    const float* o = a.ws_o + base * D + tid;
+    for (int k = 0; k < nparts; ++k) A = fmaf(sm_w[k], o[int64_t(k) * D], A);
+    const float res = S > 0.f ? A / S : 0.f;
+    const int64_t oi = (int64_t(s) * num_q_heads + hq) * D + tid;
+    if constexpr (QDT == PKV_F32)
+      static_cast<float*>(a.out)[oi] = res;
+    else
+      static_cast<uint16_t*>(a.out)[oi] = uint16_t(pkv::f32_to_bf16(res));
+    if (a.lse_out && tid == 0) a.lse_out[int64_t(s) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
+  }
+}
+
+constexpr int kWaves = 4;
+
+thread_local hipEvent_t g_profile_event = nullptr;
+
+using DecodeFn = void (*)(DecodeArgs);
+using MergeFn = void (*)(DecodeArgs, int);
+
+template <int QDT, int CDT, int D, int BS>
+DecodeFn pick_g(int G) {
+  switch (G) {
+    case 1: return decode_kernel<QDT, CDT, D, 1, BS, kWaves>;
+    case 2: return decode_kernel<QDT, CDT, D, 2, BS, kWaves>;
+    case 4: return decode_kernel<QDT, CDT, D, 4, BS, kWaves>;
+    case 8: return decode_kernel<QDT, CDT, D, 8, BS, kWaves>;
+    default: return nullptr;
+  }
+}
+
+template <int QDT, int CDT, int D>
+DecodeFn pick_bs(int G, int BS) {
+  switch (BS) {
+    case 16: return pick_g<QDT, CDT, D, 16>(G);
+    case 32: return pick_g<QDT, CDT, D, 32>(G);
+    default: return nullptr;
+  }
+}
+
+template <int QDT, int CDT>
+DecodeFn pick_d(int D, int G, int BS) {
+  switch (D) {
+    case 64: return pick_bs<QDT, CDT, 64>(G, BS);
+    case 128: return pick_bs<QDT, CDT, 128>(G, BS);
+    default: return nullptr;
+  }
+}
+
+DecodeFn pick_decode(int qdt, int cdt, int D, int G, int BS) {
+  if (qdt == PKV_F32 && cdt == PKV_F32) return pick_d<PKV_F32, PKV_F32>(D, G, BS);
+  if (qdt == PKV_BF16 && cdt == PKV_BF16) return pick_d<PKV_BF16, PKV_BF16>(D, G, BS);
+  if (qdt == PKV_BF16 && cdt == PKV_FP8_E4M3) return pick_d<PKV_BF16, PKV_FP8_E4M3>(D, G, BS);
+  return nullptr;
+}
+
+MergeFn pick_merge(int qdt, int D) {
+  if (qdt == PKV_F32) return D == 64 ? merge_kernel<PKV_F32, 64> : merge_kernel<PKV_F32, 128>;
+  return D == 64 ? merge_kernel<PKV_BF16, 64> : merge_kernel<PKV_BF16, 128>;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int64_t partitions_for(int32_t max_seq_len, int32_t partition_size) {
+  if (partition_size <= 0 || max_seq_len <= 0) return 1;
+  return (int64_t(max_seq_len) + partition_size - 1) / partition_size;
+}
+
+}  // namespace
+
+extern "C" void pkv_decode_set_profile_event(void* hip_event) {
+  g_profile_event = static_cast<hipEvent_t>(hip_event);
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                             int32_t max_seq_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size <= 0) return 0;
+  const int64_t pmax = partitions_for(max_seq_len, partition_size);
+  if (pmax <= 1) return 0;
+  return size_t(num_seqs) * num_q_heads * pmax * (head_dim + 1) * sizeof(float);
+}
+
+extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                          const void* v_cache, int32_t cache_dtype, const int32_t* block_tables,
+                                          const int32_t* seq_lens, int32_t table_width, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                                          float scale, float k_scale, float v_scale, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes, float* lse_out,
+                                          void* stream) {
+  using pkv::fail;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
+      max_seq_len < 0 || partition_size < 0)
+    return fail(PKV_ERR_INVALID, "decode: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "decode: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (num_seqs > 65535) return fail(PKV_ERR_INVALID, "decode: at most 65535 sequences per launch");
+  const int G = num_q_heads / num_kv_heads;
+  DecodeFn fn = pick_decode(q_dtype, cache_dtype, head_dim, G, block_size);
+  if (!fn)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "decode: unsupported (q dtype %d, cache dtype %d, head_dim %d, group %d, block_size %d)", q_dtype,
+                cache_dtype, head_dim, G, block_size);
+  if (partition_size > 0 && partition_size % block_size != 0)
+    return fail(PKV_ERR_INVALID, "decode: partition_size %d not a multiple of block_size %d", partition_size,
+                block_size);
+  if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(PKV_ERR_INVALID, "decode: scales must be > 0");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return fail(PKV_ERR_INVALID, "decode: NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID, "decode: q, out and cache planes must be 16-byte aligned");
+  int64_t pmax = partitions_for(max_seq_len, partition_size);
+  if (pmax > kMaxPartitions)
+    return fail(PKV_ERR_INVALID, "decode: %lld partitions exceed %d", (long long)pmax, kMaxPartitions);
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_INVALID, "decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+
+  DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.lse_out = lse_out;
+  a.table_width = table_width;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  const int64_t tcap = int64_t(table_width) * block_size;
+  a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
+  a.part_tokens = need > 0 ? partition_size : 0;
+  a.pmax = need > 0 ? int(pmax) : 1;
+  if (need > 0) {
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = a.ws_o + size_t(num_seqs) * num_q_heads * pmax * head_dim;
+  }
+  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
+  a.v_scale = v_scale;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(fn, dim3(num_kv_heads, a.pmax, num_seqs), dim3(kWaves * 64), 0, st, a);
+  if (g_profile_event) (void)hipEventRecord(g_profile_event, st);
+  if (need > 0) {
+    MergeFn mf = pick_merge(q_dtype, head_dim);
+    hipLaunchKernelGGL(mf, dim3(num_q_heads, num_seqs), dim3(256), size_t(a.pmax) * sizeof(float), st, a,
+                       num_q_heads);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}

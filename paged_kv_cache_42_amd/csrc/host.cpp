@@ -1,0 +1,236 @@
+// Host side of libpkv: the block pool, per-sequence block tables and the per-step
+// metadata build. Pure C++17, no device calls.
+//
+// Pool semantics follow "Project 17: Production Serving: Continuous Batching and
+// PagedAttention", "Step 4: Implement the paged KV cache" (take from the end of the
+// free list, append on free, return a finished sequence's pages in table order) and
+// "Build a pure-Python continuous batching LLM serving engine from scratch", "Step 2"
+// (a multi-block request is all-or-nothing and fails when too few blocks are free).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int dtype_bytes(int32_t dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+}  // namespace pkv
+
+using pkv::fail;
+
+enum : uint8_t { kFree = 0, kRaw = 1, kInSeq = 2 };
+
+struct pkv_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_list;        // next pop = back()
+  std::vector<uint8_t> state;            // per id: kFree / kRaw / kInSeq
+  std::unordered_map<int64_t, std::vector<int32_t>> tables;
+};
+
+extern "C" {
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+const char* pkv_last_error(void) { return pkv::g_last_error.c_str(); }
+
+int pkv_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t cache_dtype, const int32_t* initial_free_order,
+                   pkv_pool** out, int64_t* plane_bytes) {
+  if (!out) return fail(PKV_ERR_INVALID, "alloc_pool: out is NULL");
+  if (num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID, "alloc_pool: bad sizes (blocks %d, block_size %d, kv heads %d, head_dim %d)",
+                num_blocks, block_size, num_kv_heads, head_dim);
+  const int eb = pkv::dtype_bytes(cache_dtype);
+  if (eb == 0) return fail(PKV_ERR_INVALID, "alloc_pool: unknown cache dtype %d", cache_dtype);
+  auto* p = new pkv_pool();
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->state.assign(num_blocks, kFree);
+  p->free_list.resize(num_blocks);
+  if (initial_free_order) {
+    std::vector<uint8_t> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return fail(PKV_ERR_INVALID, "alloc_pool: initial order is not a permutation (entry %d = %d)", i, b);
+      }
+      seen[b] = 1;
+      p->free_list[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->free_list[i] = i;
+  }
+  if (plane_bytes)
+    *plane_bytes = int64_t(num_blocks) * block_size * num_kv_heads * head_dim * eb;
+  *out = p;
+  return PKV_OK;
+}
+
+void pkv_destroy_pool(pkv_pool* pool) { delete pool; }
+
+int pkv_pool_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids) {
+  if (!pool || n < 0 || (n > 0 && !out_ids)) return fail(PKV_ERR_INVALID, "pool_alloc: bad arguments");
+  if (int64_t(pool->free_list.size()) < n)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "pool_alloc: need %d, %zu free", n, pool->free_list.size());
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = pool->free_list.back();
+    pool->free_list.pop_back();
+    pool->state[b] = kRaw;
+    out_ids[i] = b;
+  }
+  return PKV_OK;
+}
+
+int pkv_pool_free(pkv_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !ids)) return fail(PKV_ERR_INVALID, "pool_free: bad arguments");
+  std::vector<int32_t> seen;
+  seen.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = ids[i];
+    if (b < 0 || b >= pool->num_blocks || pool->state[b] != kRaw)
+      return fail(PKV_ERR_INVALID, "pool_free: id %d is not a block taken by pool_alloc", b);
+    for (int32_t x : seen)
+      if (x == b) return fail(PKV_ERR_INVALID, "pool_free: id %d repeated", b);
+    seen.push_back(b);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    pool->state[ids[i]] = kFree;
+    pool->free_list.push_back(ids[i]);
+  }
+  return PKV_OK;
+}
+
+int pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* live_seqs) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool_stats: pool is NULL");
+  if (free_blocks) *free_blocks = int32_t(pool->free_list.size());
+  if (live_seqs) *live_seqs = int32_t(pool->tables.size());
+  return PKV_OK;
+}
+
+int pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t capacity, int32_t* count) {
+  if (!pool || !count) return fail(PKV_ERR_INVALID, "pool_free_list: bad arguments");
+  const int32_t n = int32_t(pool->free_list.size());
+  *count = n;
+  if (capacity < n || (n > 0 && !out))
+    return fail(PKV_ERR_INVALID, "pool_free_list: capacity %d < %d", capacity, n);
+  if (n) std::memcpy(out, pool->free_list.data(), sizeof(int32_t) * n);
+  return PKV_OK;
+}
+
+int pkv_seq_reserve(pkv_pool* pool, int64_t seq_id, int32_t total_tokens) {
+  if (!pool || total_tokens < 0) return fail(PKV_ERR_INVALID, "seq_reserve: bad arguments");
+  const int64_t want = (int64_t(total_tokens) + pool->block_size - 1) / pool->block_size;
+  auto it = pool->tables.find(seq_id);
+  const int64_t have = it == pool->tables.end() ? 0 : int64_t(it->second.size());
+  const int64_t need = want - have;
+  if (need > int64_t(pool->free_list.size()))
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "seq_reserve: sequence %lld needs %lld more blocks, %zu free",
+                (long long)seq_id, (long long)need, pool->free_list.size());
+  std::vector<int32_t>& t = pool->tables[seq_id];
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = pool->free_list.back();
+    pool->free_list.pop_back();
+    pool->state[b] = kInSeq;
+    t.push_back(b);
+  }
+  return PKV_OK;
+}
+
+int pkv_seq_release(pkv_pool* pool, int64_t seq_id) {
+  if (!pool) return fail(PKV_ERR_INVALID, "seq_release: pool is NULL");
+  auto it = pool->tables.find(seq_id);
+  if (it == pool->tables.end())
+    return fail(PKV_ERR_INVALID, "seq_release: unknown sequence %lld", (long long)seq_id);
+  for (int32_t b : it->second) {
+    pool->state[b] = kFree;
+    pool->free_list.push_back(b);
+  }
+  pool->tables.erase(it);
+  return PKV_OK;
+}
+
+int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* out, int32_t capacity,
+                  int32_t* count) {
+  if (!pool || !count) return fail(PKV_ERR_INVALID, "seq_table: bad arguments");
+  auto it = pool->tables.find(seq_id);
+  if (it == pool->tables.end())
+    return fail(PKV_ERR_INVALID, "seq_table: unknown sequence %lld", (long long)seq_id);
+  const int32_t n = int32_t(it->second.size());
+  *count = n;
+  if (capacity < n || (n > 0 && !out))
+    return fail(PKV_ERR_INVALID, "seq_table: capacity %d < %d", capacity, n);
+  if (n) std::memcpy(out, it->second.data(), sizeof(int32_t) * n);
+  return PKV_OK;
+}
+
+int pkv_build_block_table(const pkv_pool* pool, int32_t num_seqs, const int64_t* seq_ids,
+                          const int32_t* q_lens, const int32_t* seq_lens, int32_t table_width,
+                          int32_t* block_tables, int32_t* cu_seqlens_q, int64_t* slot_mapping) {
+  if (!pool || num_seqs < 0 || table_width < 0 || !cu_seqlens_q ||
+      (num_seqs > 0 && (!seq_ids || !q_lens || !seq_lens || (table_width > 0 && !block_tables))))
+    return fail(PKV_ERR_INVALID, "build_block_table: bad arguments");
+  const int64_t bs = pool->block_size;
+  // validate everything before writing anything
+  std::vector<const std::vector<int32_t>*> tabs(num_seqs);
+  int64_t total_q = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    auto it = pool->tables.find(seq_ids[s]);
+    if (it == pool->tables.end())
+      return fail(PKV_ERR_INVALID, "build_block_table: unknown sequence %lld", (long long)seq_ids[s]);
+    const int64_t L = seq_lens[s], q = q_lens[s];
+    if (q < 0 || L < 0 || q > L)
+      return fail(PKV_ERR_INVALID, "build_block_table: sequence %d q_len %lld outside 0..seq_len %lld", s,
+                  (long long)q, (long long)L);
+    const int64_t nblk = (L + bs - 1) / bs;
+    if (nblk > int64_t(it->second.size()))
+      return fail(PKV_ERR_INVALID, "build_block_table: sequence %d holds %zu blocks, needs %lld", s,
+                  it->second.size(), (long long)nblk);
+    if (nblk > table_width)
+      return fail(PKV_ERR_INVALID, "build_block_table: sequence %d needs %lld blocks > width %d", s,
+                  (long long)nblk, table_width);
+    tabs[s] = &it->second;
+    total_q += q;
+  }
+  if (total_q > 0 && !slot_mapping) return fail(PKV_ERR_INVALID, "build_block_table: slot_mapping is NULL");
+  int64_t r = 0;
+  cu_seqlens_q[0] = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const std::vector<int32_t>& t = *tabs[s];
+    const int64_t L = seq_lens[s], q = q_lens[s];
+    const int64_t nblk = (L + bs - 1) / bs;
+    int32_t* row = block_tables + int64_t(s) * table_width;
+    for (int64_t j = 0; j < table_width; ++j) row[j] = j < nblk ? t[j] : -1;
+    for (int64_t p = L - q; p < L; ++p) slot_mapping[r++] = int64_t(t[p / bs]) * bs + p % bs;
+    cu_seqlens_q[s + 1] = int32_t(r);
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal helpers shared by libpkv's host code and HIP kernels (not part of the ABI).
+#pragma once
+
+#include <stdint.h>
+
+namespace pkv {
+
+// Record a message for pkv_last_error() and return `code`.
+int fail(int code, const char* fmt, ...);
+// Bytes per element of a PKV_* dtype code (0 if unknown).
+int dtype_bytes(int32_t dt);
+
+}  // namespace pkv
+
+#ifdef __HIPCC__
+#include <hip/hip_runtime.h>
+
+namespace pkv {
+
+// ---- scalar conversions --------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN, quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// OCP E4M3 code (low 8 bits of c) -> float, exact. Relies on fp32 denormals being
+// preserved (gfx950 default mode): the 7 magnitude bits placed at bit 20 form a
+// float equal to the E4M3 magnitude times 2^-120 (subnormal codes included).
+__device__ __forceinline__ float fp8_to_f32(uint32_t c) {
+  const uint32_t em = c & 0x7fu;
+  float mag = __uint_as_float(em << 20) * 0x1p120f;
+  mag = (em == 0x7fu) ? __builtin_nanf("") : mag;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// float y -> OCP E4M3 code: nearest-even, |y| >= 448 (inf included) saturates to
+// 448, NaN -> 0x7F; the sign of y is always kept.
+__device__ __forceinline__ uint32_t f32_to_fp8(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;           // 448.0f
+  if (a >= 0x3c800000u) {                              // >= 2^-6: normal E4M3 range
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // round 23 -> 3 mantissa bits
+    return sign | ((r >> 20) - (120u << 3));
+  }
+  // subnormal range: multiple of 2^-9, m in 0..8 (8 is the smallest normal, 0x08)
+  const float t = __uint_as_float(a) * 512.0f;         // exact scaling
+  return sign | uint32_t(__builtin_rintf(t));          // rint = round half to even
+}
+
+// ---- cross-lane reductions -----------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over aligned groups of N lanes (N in 1,2,4,8,16,32); every lane of a group gets
+// the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x);  // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv
+#endif  // __HIPCC__

@@ -1,0 +1,89 @@
+"""kv_cache_write on the GPU vs the oracle: cache bytes must match bit-exactly."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_42_amd as pkv
+import workloads
+from oracle import cache as ocache
+from oracle import fp8 as ofp8
+
+from gpu_setup import build_step, oracle_planes, plane_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("make", [
+    lambda: workloads.config1(),
+    lambda: workloads.small_decode(21, [1, 16, 17, 33, 100], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                   block_size=16, dtype="bf16"),
+    lambda: workloads.small_varlen(22, [40, 64, 7], [40, 10, 1], num_q_heads=8, num_kv_heads=4, head_dim=64,
+                                   block_size=32, dtype="bf16", cache_dtype="fp8"),
+    lambda: workloads.small_decode(23, [5, 70], num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                                   dtype="f32", cache_dtype="fp8"),
+], ids=["cfg1_f32", "bf16_d128", "bf16_to_fp8_bs32", "f32_to_fp8"])
+def test_cache_bytes_and_tables_bit_exact(make):
+    w = make()
+    if w.cache_dtype == "fp8":
+        w.k_scale, w.v_scale = 0.5, 0.125
+    st = build_step(w)
+    tabs, bt, cu, slots, kp, vp = oracle_planes(st)
+    assert (st.bt == bt).all() and (st.cu == cu).all() and (st.slots == slots).all()
+    assert (plane_bits(st.k_cache) == kp).all()
+    assert (plane_bits(st.v_cache) == vp).all()
+
+
+def test_config2_cache_write_bit_exact():
+    w = workloads.config2()
+    st = build_step(w)
+    tabs, bt, cu, slots, kp, vp = oracle_planes(st)
+    assert (st.bt == bt).all() and (st.slots == slots).all()
+    assert (plane_bits(st.k_cache) == kp).all() and (plane_bits(st.v_cache) == vp).all()
+
+
+def _encode_on_gpu(x_storage: np.ndarray, in_dtype: str, scale: float):
+    """Write rows [T][1][64] to an fp8 plane with identity slots; return the codes."""
+    T = x_storage.shape[0]
+    kc = torch.zeros((T, 1, 1, 64), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    x = to_device(x_storage, in_dtype)
+    pkv.kv_cache_write(x, x, kc, vc, torch.arange(T, dtype=torch.int64, device="cuda"), 1, scale, scale)
+    torch.cuda.synchronize()
+    return kc.cpu().numpy().reshape(T, 64), vc.cpu().numpy().reshape(T, 64)
+
+
+def test_fp8_encoder_exhaustive_over_bf16_inputs():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1024, 1, 64)
+    for scale in (1.0, 0.5, 3.0):
+        k, v = _encode_on_gpu(bits, "bf16", scale)
+        ref = ofp8.encode(workloads.bf16_to_f32(bits).reshape(1024, 64), scale)
+        assert (k == ref).all() and (v == ref).all(), f"scale {scale}: {(k != ref).sum()} codes differ"
+
+
+def test_fp8_encoder_float32_edges_and_random():
+    rng = np.random.default_rng(0)
+    edges = np.array([0.0, -0.0, 448.0, 447.99, 448.01, 463.9, 464.0, 464.1, 480.0, 1e30, np.inf, -np.inf,
+                      np.nan, 2 ** -6, np.nextafter(2 ** -6, 0), 2 ** -9, 2 ** -10, 3 * 2 ** -10,
+                      np.nextafter(2 ** -10, 1), 1.0625, 1.1875, 1e-45, -1e-45, 15.5, 240.0, 232.0],
+                     dtype=np.float32)
+    rnd = (rng.standard_normal(64 * 64 * 8) * np.exp(rng.uniform(-14, 7, 64 * 64 * 8))).astype(np.float32)
+    raw = rng.integers(0, 2 ** 32, 64 * 64, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    x = np.concatenate([edges, rnd, raw])
+    x = np.concatenate([x, np.zeros((-len(x)) % 64, np.float32)]).reshape(-1, 1, 64)
+    k, _ = _encode_on_gpu(x, "f32", 1.0)
+    ref = ofp8.encode(x.reshape(-1, 64))
+    bad = k != ref
+    assert not bad.any(), f"{bad.sum()} codes differ, e.g. x={x.reshape(-1, 64)[bad][:5]}"
+
+
+def test_padding_and_out_of_range_slots_are_skipped():
+    T = 8
+    kc = torch.zeros((4, 2, 1, 64), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    k = torch.ones((T, 1, 64), dtype=torch.bfloat16, device="cuda")
+    slots = torch.tensor([0, -1, 3, 8, 100, -5, 7, 1], dtype=torch.int64, device="cuda")
+    pkv.kv_cache_write(k, k * 2, kc, vc, slots, 2)
+    torch.cuda.synchronize()
+    written = (kc.view(8, 64) != 0).any(1).cpu().numpy()
+    assert written.tolist() == [True, True, False, True, False, False, False, True]
+    assert (vc.view(8, 64)[written] == 2).all()

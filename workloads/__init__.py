@@ -7,8 +7,20 @@ and the shape recipes (lengths, pool sizes, initial free-list orders, and the
 list of alloc/free *requests* that fragments a pool). Block ids are never chosen
 here; an allocator replays the request list.
 
-Every stream is a NumPy PCG64 generator keyed by a SeedSequence of integers, so
-any one sequence's values can be regenerated without drawing the others.
+Shapes and orders come from NumPy PCG64 generators keyed by integer SeedSequences.
+Q/K/V values come from a counter-based hash so that any element can be produced
+independently, on the CPU (here) or on the GPU (workloads/gen.hip), bit for bit:
+
+  key(seed, stream, seq) = mix(seed * 2^32 + stream * 2^24 + seq)
+  h_n = mix(key + (n + 1) * 0x9E3779B97F4A7C15)          (SplitMix64: Steele, Lea
+                                                         and Flood, OOPSLA 2014)
+  element e of a (seq, stream) lives in h_{e//3}, bits 18*(e%3) .. +17, as three
+  6-bit fields a, b, c; value = sigma * (2(a+b+c) - 189) / 64.
+
+mix is the SplitMix64 finaliser. The value is the Irwin-Hall(3) approximation of
+N(0, sigma^2): mean 0, variance (4095/4096) sigma^2, support |x| <= 2.953 sigma, and
+every value (an odd multiple of sigma/64 below 189 sigma/64) is exact in bfloat16.
+Element index e = (position * heads + head) * head_dim + dim.
 """
 from __future__ import annotations
 
@@ -25,12 +37,112 @@ _STREAM_HISTORY = 13
 _STREAM_Q = 20
 _STREAM_K = 21
 _STREAM_V = 22
+STREAMS = {"q": _STREAM_Q, "k": _STREAM_K, "v": _STREAM_V}
 _STREAM_TRACE = 30
 
 
 def rng_for(*key: int) -> np.random.Generator:
     """A PCG64 generator for the integer key (seed, stream, index...)."""
     return np.random.default_rng(np.random.SeedSequence([int(k) for k in key]))
+
+
+_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_MIX1 = np.uint64(0xBF58476D1CE4E5B9)
+_MIX2 = np.uint64(0x94D049BB133111EB)
+_MASK64 = (1 << 64) - 1
+_CHUNK = 1 << 16
+
+
+def _mix_int(z: int) -> int:
+    """SplitMix64 finaliser on a Python int (mod 2^64)."""
+    z &= _MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def hash_key(seed: int, stream: int, seq: int) -> int:
+    """64-bit key of one (seed, stream, sequence) value stream."""
+    if not (0 <= seq < (1 << 24) and 0 <= stream < 256 and 0 <= seed < (1 << 31)):
+        raise ValueError("key field out of range")
+    return _mix_int((seed << 32) + (stream << 24) + seq)
+
+
+def _hash_at(key: int, e: np.ndarray, sigma: float) -> np.ndarray:
+    """Values of the elements with flat indices e (uint64 array) of stream `key`."""
+    k = np.uint64(key)
+    n = e // np.uint64(3)
+    j = (e - n * np.uint64(3)) * np.uint64(18)
+    z = (n + np.uint64(1)) * _GAMMA
+    z += k
+    z ^= z >> np.uint64(30)
+    z *= _MIX1
+    z ^= z >> np.uint64(27)
+    z *= _MIX2
+    z ^= z >> np.uint64(31)
+    f = ((z >> j) & np.uint64(0x3FFFF)).astype(np.uint32)
+    tot = (f & np.uint32(63)) + ((f >> np.uint32(6)) & np.uint32(63)) + (f >> np.uint32(12))
+    v = tot.astype(np.float32) * np.float32(2.0 / 64.0) - np.float32(189.0 / 64.0)
+    if np.float32(sigma) != np.float32(1.0):
+        v *= np.float32(sigma)
+    return v
+
+
+def hash_values_strided(key: int, starts: np.ndarray, width: int, sigma: float = 1.0) -> np.ndarray:
+    """Values of the runs [starts[i], starts[i]+width) of stream `key`, as [len(starts)][width]."""
+    starts = np.asarray(starts, dtype=np.uint64)
+    out = np.empty((len(starts), width), np.float32)
+    rows = max(1, _CHUNK // max(width, 1))
+    cols = np.arange(width, dtype=np.uint64)[None, :]
+    for i in range(0, len(starts), rows):
+        e = starts[i:i + rows, None] + cols
+        out[i:i + rows] = _hash_at(key, e, sigma)
+    return out
+
+
+def hash_values(key: int, e0: int, e1: int, sigma: float = 1.0) -> np.ndarray:
+    """float32 values of elements e0 .. e1-1 of the stream `key` (see module doc)."""
+    if e1 <= e0:
+        return np.zeros(0, np.float32)
+    n0, n1 = e0 // 3, (e1 - 1) // 3 + 1
+    res = np.empty(3 * (n1 - n0), np.float32)
+    z = np.empty(_CHUNK, np.uint64)
+    t = np.empty(_CHUNK, np.uint64)
+    f = np.empty((_CHUNK, 3), np.uint32)
+    acc = np.empty((_CHUNK, 3), np.uint32)
+    k = np.uint64(key)
+    sig = np.float32(sigma)
+    for c0 in range(n0, n1, _CHUNK):
+        m = min(_CHUNK, n1 - c0)
+        zz, tt = z[:m], t[:m]
+        zz[:] = np.arange(c0 + 1, c0 + 1 + m, dtype=np.uint64)
+        np.multiply(zz, _GAMMA, out=zz)
+        np.add(zz, k, out=zz)
+        np.right_shift(zz, np.uint64(30), out=tt)
+        np.bitwise_xor(zz, tt, out=zz)
+        np.multiply(zz, _MIX1, out=zz)
+        np.right_shift(zz, np.uint64(27), out=tt)
+        np.bitwise_xor(zz, tt, out=zz)
+        np.multiply(zz, _MIX2, out=zz)
+        np.right_shift(zz, np.uint64(31), out=tt)
+        np.bitwise_xor(zz, tt, out=zz)
+        ff, aa = f[:m], acc[:m]
+        for j in range(3):
+            np.right_shift(zz, np.uint64(18 * j), out=tt)
+            np.bitwise_and(tt, np.uint64(0x3FFFF), out=tt)
+            ff[:, j] = tt
+        np.bitwise_and(ff, np.uint32(63), out=aa)
+        np.right_shift(ff, np.uint32(6), out=ff)
+        aa += ff & np.uint32(63)
+        np.right_shift(ff, np.uint32(6), out=ff)
+        aa += ff
+        o = res[3 * (c0 - n0): 3 * (c0 - n0 + m)].reshape(m, 3)
+        o[:] = aa
+        o *= np.float32(2.0 / 64.0)
+        o -= np.float32(189.0 / 64.0)
+        if sig != np.float32(1.0):
+            o *= sig
+    return res[e0 - 3 * n0: e1 - 3 * n0]
 
 
 # ----------------------------------------------------------------------------
@@ -99,7 +211,7 @@ class Workload:
     free_order: np.ndarray     # int32 [num_blocks], initial free list (popped from the end)
     history: List[Tuple] = dataclasses.field(default_factory=list)
     partition_size: int = 0    # split-context partition length in tokens (0 = none)
-    sigma: float = 1.0
+    sigma: float = 1.0         # value scale: 1.0 or 0.5 keep every value exact in bf16
     scale: Optional[float] = None  # softmax scale; None = 1/sqrt(head_dim)
     k_scale: float = 1.0
     v_scale: float = 1.0
@@ -132,18 +244,29 @@ class Workload:
         return int(self.blocks_needed().max()) if self.num_seqs else 0
 
     # -- values -----------------------------------------------------------
-    def _draw(self, stream: int, s: int, rows: int, heads: int) -> np.ndarray:
-        g = rng_for(self.seed, stream, s)
-        x = g.standard_normal((rows, heads, self.head_dim), dtype=np.float32)
-        if self.sigma != 1.0:
-            x = x * np.float32(self.sigma)
-        return x
+    def _draw(self, stream: int, s: int, pos0: int, pos1: int, heads: int) -> np.ndarray:
+        key = hash_key(self.seed, stream, s)
+        e0 = pos0 * heads * self.head_dim
+        e1 = pos1 * heads * self.head_dim
+        x = hash_values(key, e0, e1, self.sigma)
+        return x.reshape(pos1 - pos0, heads, self.head_dim)
 
     def kv_f32(self, s: int) -> Tuple[np.ndarray, np.ndarray]:
         """Float32 draws of K and V for positions 0..seq_lens[s]-1 of sequence s."""
         L = int(self.seq_lens[s])
-        return (self._draw(_STREAM_K, s, L, self.num_kv_heads),
-                self._draw(_STREAM_V, s, L, self.num_kv_heads))
+        return (self._draw(_STREAM_K, s, 0, L, self.num_kv_heads),
+                self._draw(_STREAM_V, s, 0, L, self.num_kv_heads))
+
+    def value_key(self, which: str, s: int) -> int:
+        """Hash key of sequence s's "q", "k" or "v" value stream."""
+        return hash_key(self.seed, STREAMS[which], s)
+
+    def kv_head_f32(self, s: int, g: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Float32 K and V of KV head g of sequence s, [seq_len][head_dim] each."""
+        L = int(self.seq_lens[s])
+        starts = (np.arange(L, dtype=np.int64) * self.num_kv_heads + g) * self.head_dim
+        return (hash_values_strided(hash_key(self.seed, _STREAM_K, s), starts, self.head_dim, self.sigma),
+                hash_values_strided(hash_key(self.seed, _STREAM_V, s), starts, self.head_dim, self.sigma))
 
     def kv(self, s: int) -> Tuple[np.ndarray, np.ndarray]:
         """K and V of sequence s in the step's input dtype (float32 or bf16 bits)."""
@@ -152,7 +275,8 @@ class Workload:
 
     def q(self, s: int) -> np.ndarray:
         """Queries of sequence s, [q_lens[s], Hq, d], in the input dtype."""
-        x = self._draw(_STREAM_Q, s, int(self.q_lens[s]), self.num_q_heads)
+        L, q = int(self.seq_lens[s]), int(self.q_lens[s])
+        x = self._draw(_STREAM_Q, s, L - q, L, self.num_q_heads)
         return as_storage(x, self.dtype)
 
     def q_all(self) -> np.ndarray:

@@ -1,0 +1,48 @@
+// GPU twin of the counter-based value generator in workloads/__init__.py.
+// Input generation only (test and benchmark infrastructure): element e of stream
+// `key` is field e%3 of SplitMix64(key + (e/3 + 1) * golden gamma), three 6-bit
+// uniforms summed (Irwin-Hall(3)), value = sigma * (2 * sum - 189) / 64, stored as
+// float32 or bfloat16 (exact). Bit-identical to the NumPy implementation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__device__ __forceinline__ uint64_t finalize(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ void __launch_bounds__(256) fill_values(void* out, int as_bf16, uint64_t key, int64_t e0,
+                                                   int64_t count, float sigma) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const uint64_t e = uint64_t(e0 + i);
+    const uint64_t n = e / 3;
+    const uint32_t j = uint32_t(e - n * 3);
+    const uint64_t h = finalize(key + (n + 1) * 0x9E3779B97F4A7C15ull);
+    const uint32_t f = uint32_t((h >> (18 * j)) & 0x3FFFFull);
+    const uint32_t s = (f & 63u) + ((f >> 6) & 63u) + (f >> 12);
+    float v = float(s) * 0.03125f - 2.953125f;
+    if (sigma != 1.0f) v *= sigma;
+    if (as_bf16)
+      static_cast<uint16_t*>(out)[i] = uint16_t(__float_as_uint(v) >> 16);
+    else
+      static_cast<float*>(out)[i] = v;
+  }
+}
+
+}  // namespace
+
+// out: device buffer of `count` float32 (as_bf16 = 0) or bfloat16 (1) values.
+extern "C" int pkvgen_fill(void* out, int as_bf16, uint64_t key, int64_t e0, int64_t count, float sigma,
+                           void* stream) {
+  if (count <= 0) return 0;
+  if (!out || e0 < 0) return -1;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_values, dim3(unsigned(blocks)), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), out,
+                     as_bf16, key, e0, count, sigma);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}

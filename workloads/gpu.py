@@ -1,0 +1,59 @@
+"""GPU side of the counter-based value generator (libpkvgen.so, built from gen.hip).
+
+Test and benchmark infrastructure: fills device buffers with the same values as
+`workloads.hash_values`, bit for bit, so large workloads need no host generation."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import shutil
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gen.hip")
+LIB = os.path.join(HERE, "libpkvgen.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+    arch = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
+    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={arch}", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", SRC, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"libpkvgen build failed\n{r.stdout}\n{r.stderr}")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built: run `python -m workloads.gpu`")
+        L = C.CDLL(LIB)
+        L.pkvgen_fill.restype = C.c_int
+        L.pkvgen_fill.argtypes = [C.c_void_p, C.c_int, C.c_uint64, C.c_int64, C.c_int64, C.c_float, C.c_void_p]
+        _lib = L
+    return _lib
+
+
+def fill(t, key: int, e0: int, sigma: float = 1.0) -> None:
+    """Fill contiguous device tensor t (float32 or bfloat16) with elements e0.. of stream key."""
+    import torch
+    if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("contiguous float32/bfloat16 device tensor expected")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib().pkvgen_fill(C.c_void_p(t.data_ptr()), int(t.dtype == torch.bfloat16), C.c_uint64(key),
+                           int(e0), t.numel(), float(sigma), C.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError(f"pkvgen_fill failed ({rc})")
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
