@@ -130,6 +130,17 @@ int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype, int32_t n
                        int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
                        const int64_t* slot_mapping, float k_scale, float v_scale, void* stream);
 
+/* Decode work list (host): one item per non-empty (sequence, context partition), so the
+ * decode launch has no idle workgroups. seq_lens: host int32 [num_seqs] (the values the
+ * device copy holds). partition_size: as for pkv_paged_attention_decode (0 = one item per
+ * sequence). items: host int32 [capacity][4] receiving (seq, partition, partitions of
+ * that sequence, end token of the partition); a sequence of length 0 still gets one item
+ * (it writes zeros). Order: longest item first (full partitions in sequence order, then
+ * the shorter last partitions by decreasing length). *count = number of items. INVALID
+ * if capacity is too small (nothing written) or partition_size < 0. */
+int pkv_build_decode_work(int32_t num_seqs, const int32_t* seq_lens, int32_t partition_size,
+                          int32_t* items, int32_t capacity, int32_t* count);
+
 /* Bytes of device workspace that pkv_paged_attention_decode needs for this shape
  * (0 when partition_size is 0 or no sequence can span two partitions). */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -150,7 +161,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * block_size) the context is split into partitions of that many tokens whose partial
  * results are merged by log-sum-exp in a second kernel, using `workspace` (device,
  * >= pkv_decode_workspace_bytes). lse_out (device float [num_seqs][num_q_heads],
- * nullable) receives the natural-log log-sum-exp of the scaled scores. */
+ * nullable) receives the natural-log log-sum-exp of the scaled scores.
+ * work_items (device int32 [num_work][4], nullable): the list pkv_build_decode_work
+ * returns for these seq_lens and partition_size; with it the launch covers exactly the
+ * listed items (a sequence missing from the list is not computed), without it every
+ * (sequence, possible partition) gets a workgroup that exits when empty. */
 int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
                                const void* v_cache, int32_t cache_dtype,
                                const int32_t* block_tables, const int32_t* seq_lens,
@@ -159,7 +174,7 @@ int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const 
                                int32_t num_blocks, int32_t max_seq_len, float scale,
                                float k_scale, float v_scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, float* lse_out,
-                               void* stream);
+                               const int32_t* work_items, int32_t num_work, void* stream);
 
 /* Profiling hook (for timing the partition pass alone): while `hip_event` (a
  * hipEvent_t) is not NULL, every pkv_paged_attention_decode call made on this thread

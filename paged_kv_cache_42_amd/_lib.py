@@ -55,7 +55,8 @@ _SIGS = {
     "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
     "pkv_decode_set_profile_event": (None, [vp]),
     "pkv_paged_attention_decode": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
-                                             i32, i32, f32, f32, f32, i32, vp, sz, vp, vp]),
+                                             i32, i32, f32, f32, f32, i32, vp, sz, vp, vp, i32, vp]),
+    "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
 }
 
 
@@ -241,10 +242,20 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_s
     return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size))
 
 
+def build_decode_work(seq_lens, partition_size: int) -> np.ndarray:
+    """Host decode work list: int32 [n][4] (seq, partition, partitions, end token)."""
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    cap = int(sum(max(1, -(-int(x) // partition_size)) if partition_size > 0 else 1 for x in L)) or 1
+    out = np.zeros((cap, 4), np.int32)
+    n = i32()
+    check(lib().pkv_build_decode_work(len(L), _np_ptr(L), partition_size, _np_ptr(out), cap, C.byref(n)))
+    return out[: n.value]
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int,
                            block_size: int, max_seq_len: int, scale: float, k_scale: float = 1.0,
                            v_scale: float = 1.0, partition_size: int = 0, workspace=None, lse=None,
-                           stream=None) -> None:
+                           work=None, stream=None) -> None:
     """q/out: [B][Hq][d]; block_tables int32 [B][W]; seq_lens int32 [B]."""
     torch = _torch()
     _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, workspace, lse)
@@ -258,12 +269,16 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num
         raise ValueError("seq_lens must be int32 [B]")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
         raise ValueError("lse must be float32 [B][Hq]")
+    if work is not None:
+        _require_cuda_contig(work)
+        if work.dtype != torch.int32 or work.dim() != 2 or work.shape[1] != 4:
+            raise ValueError("work must be int32 [n][4] (from build_decode_work)")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().pkv_paged_attention_decode(
         _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
         _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
         k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, partition_size, _dptr(workspace), ws_bytes,
-        _dptr(lse), _stream(stream)))
+        _dptr(lse), _dptr(work), 0 if work is None else work.shape[0], _stream(stream)))
 
 
 def decode_set_profile_event(event) -> None:

@@ -109,7 +109,41 @@ struct DecodeArgs {
   int pmax;
   float zscale;      // softmax scale * k_scale * log2(e)
   float v_scale;
+  int group;         // query heads per KV head
+  int num_seqs;
+  const int4* work;  // (seq, partition, partitions, end token) per item, or null: grid over all
 };
+
+// The (sequence, partition) of this workgroup and its token range; false = nothing to do.
+__device__ __forceinline__ bool locate_item(const DecodeArgs& a, int& s, int& p, int& nparts, int& tok_begin,
+                                            int& tok_end) {
+  if (a.work) {
+    const int4 it = a.work[blockIdx.y];
+    s = it.x;
+    p = it.y;
+    nparts = it.z;
+    if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.pmax) return false;   // malformed item: skip
+    tok_end = it.w < 0 ? 0 : (it.w > a.len_clamp ? a.len_clamp : it.w);
+    tok_begin = a.part_tokens > 0 ? p * a.part_tokens : 0;
+    if (tok_begin > tok_end) tok_begin = tok_end;
+    return true;
+  }
+  s = blockIdx.z;
+  p = blockIdx.y;
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+  tok_begin = 0;
+  tok_end = L;
+  nparts = 1;
+  if (a.part_tokens > 0) {
+    nparts = (L + a.part_tokens - 1) / a.part_tokens;
+    if (nparts < 1) nparts = 1;
+    if (p >= nparts) return false;
+    tok_begin = p * a.part_tokens;
+    tok_end = min(L, tok_begin + a.part_tokens);
+  }
+  return true;
+}
 
 template <int QDT, int CDT, int D, int G, int BS, int NW>
 __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
@@ -124,25 +158,14 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
   static_assert(NLT >= 1 && TILE % TPL == 0, "tile too small for this row width");
 
   const int g = blockIdx.x;
-  const int p = blockIdx.y;
-  const int s = blockIdx.z;
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * G;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int r = lane / LPT;
   const int c = lane % LPT;
-
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
-  int tok_begin = 0, tok_end = L, nparts = 1;
-  if (a.part_tokens > 0) {
-    nparts = (L + a.part_tokens - 1) / a.part_tokens;
-    if (nparts < 1) nparts = 1;
-    if (p >= nparts) return;
-    tok_begin = p * a.part_tokens;
-    tok_end = min(L, tok_begin + a.part_tokens);
-  }
+  int s, p, nparts, tok_begin, tok_end;
+  if (!locate_item(a, s, p, nparts, tok_begin, tok_end)) return;
   const int blk_begin = tok_begin / BS;
   const int blk_end = (tok_end + BS - 1) / BS;
 
@@ -428,6 +451,257 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   }
 }
 
+
+// ---------------------------------------------------------------------------------
+// MFMA decode (bf16 queries; bf16 or E4M3 cache).
+//
+// One wave owns 16-token tiles. Lane l works for query head slot hl = l % 16 (slots
+// >= G are zero padding) and lane group grp = l / 16.
+//  * K tile -> registers: in load i, lane l reads 16 bytes of token hl's head row at
+//    byte 64*i + 16*grp, so each load instruction covers 64 contiguous bytes of each of
+//    16 token rows. Those registers are directly the A operand of
+//    v_mfma_f32_16x16x32_bf16 (A[token][k]); the packed queries are the B operand with
+//    the same head_dim permutation. Result: lane l holds the scores of head hl for
+//    tokens 4*grp .. 4*grp+3.
+//  * Online softmax is lane-local per head (tile max over the 4 lane groups by two
+//    shuffles). exp2 of the scores, rounded to bf16, is already the B operand of
+//    v_mfma_f32_16x16x16_bf16 for P^T (tokens 4*grp+j, head hl).
+//  * V tile -> LDS ([token][head_dim], padded rows), read back with ds_read_b64_tr_b16
+//    as V^T fragments (d = 16*mt + hl, tokens 4*grp+j): the A operand. The output
+//    O^T accumulates in lane l for head hl, d = 16*mt + 4*grp + r: per-head rescaling
+//    stays lane-local.
+// ---------------------------------------------------------------------------------
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// 8 E4M3 codes (two words) -> 8 bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t src = j < 2 ? lo : hi;
+    const uint32_t sh = 16 * (j & 1);
+    const uint32_t a = __float_as_uint(pkv::fp8_to_f32(src >> sh)) >> 16;
+    const uint32_t b = __float_as_uint(pkv::fp8_to_f32(src >> (sh + 8))) >> 16;
+    w[j] = a | (b << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  return pkv::f32_to_bf16(a) | (pkv::f32_to_bf16(b) << 16);
+}
+
+template <int CDT, int D, int BS, int HPW>
+__global__ void __launch_bounds__(HPW * 64) decode_mfma_kernel(DecodeArgs a) {
+  constexpr int CH = D / 4;                     // head_dim elements per lane group
+  constexpr int KS = D / 32;                    // QK k-steps (16x16x32)
+  constexpr int MT = D / 16;                    // PV d-tiles (16x16x16)
+  constexpr int EB = CDT == PKV_BF16 ? 2 : 1;   // cache bytes per element
+  constexpr int NV = CH * EB / 16;              // 16-byte loads per lane per tile (each of K, V)
+  constexpr int SUB = BS / 16;                  // 16-token tiles per block
+  constexpr int RS = D * 2 + 32;                // LDS row stride (bytes) of the bf16 V tile
+  static_assert(NV >= 1 && CH % 8 == 0, "unsupported head_dim");
+
+  // the HPW waves of a workgroup take HPW consecutive KV heads of the same work item,
+  // so together they stream whole token rows of every block
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = blockIdx.x * HPW + w;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * G;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  int s, p, nparts, tok_begin, tok_end;
+  if (!locate_item(a, s, p, nparts, tok_begin, tok_end)) return;
+  const int blk_begin = tok_begin / BS;
+  const int blk_end = (tok_end + BS - 1) / BS;
+
+  // queries: B operand of the QK MFMA, with the head_dim permutation of the K registers.
+  // K load i of a lane reads bytes 64*i + 16*grp of its token's head row, so k-step kk of
+  // lane group grp holds elements 32*kk + 8*grp .. +7 (bf16 cache) or, as half of a
+  // 16-element E4M3 load, 64*(kk/2) + 16*grp + 8*(kk%2) .. +7.
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(s) * Hq + int64_t(g) * G + hl) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int d0 = EB == 2 ? 32 * kk + 8 * grp : 64 * (kk / 2) + 16 * grp + 8 * (kk % 2);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (hl < G) v = *reinterpret_cast<const uint4*>(qrow + d0);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4_t o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[HPW][16 * RS];
+  uint8_t* my_vt = vt_lds[w];
+
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache);
+  const int64_t row_bytes = int64_t(Hkv) * D * EB;                  // one token, all KV heads
+  const int64_t lane_off = int64_t(g) * D * EB + 16 * grp;
+  const int32_t* bt_row = a.block_tables + int64_t(s) * a.table_width;
+  const int nblk = blk_end - blk_begin;
+  const int ntiles = nblk * SUB;
+
+  // block ids of the item, 64 at a time, one per lane (read back with readlane)
+  int bt_base = -64, bt_lane = 0;
+  auto block_id = [&](int j) -> int {   // j: block index relative to blk_begin (wave-uniform)
+    const int base = j & ~63;
+    if (base != bt_base) {
+      bt_base = base;
+      const int jj = blk_begin + base + lane;
+      bt_lane = jj < blk_end ? bt_row[jj] : -1;
+    }
+    return __builtin_amdgcn_readlane(bt_lane, j & 63);
+  };
+
+  uint4 kb[2][NV], vb[2][NV];
+  int tok0[2];
+  bool okb[2];
+
+  auto issue = [&](int n, uint4 (&kr)[NV], uint4 (&vr)[NV], int& t0, bool& ok) {
+    const int j = n / SUB;
+    const int sub = n % SUB;
+    const int blk = block_id(j);
+    ok = blk >= 0 && blk < a.num_blocks;
+    t0 = (blk_begin + j) * BS + sub * 16;
+    const int64_t off = (int64_t(ok ? blk : 0) * BS + sub * 16 + hl) * row_bytes + lane_off;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (ok) {
+        kr[i] = *reinterpret_cast<const uint4*>(kc + off + 64 * i);
+        vr[i] = *reinterpret_cast<const uint4*>(vc + off + 64 * i);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto consume = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int t0, bool ok) {
+    // ---- scores S^T[token][head] = K . Q^T
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (CDT == PKV_BF16) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[kk]), qf[kk], sc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const uint4 lo = fp8x8_to_bf16x8(kr[i].x, kr[i].y);
+        const uint4 hi = fp8x8_to_bf16x8(kr[i].z, kr[i].w);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qf[2 * i], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qf[2 * i + 1], sc, 0, 0, 0);
+      }
+    }
+    // ---- V tile -> LDS as bf16 rows; rows of tokens past the context are zeroed
+    {
+      // load i holds head_dim elements 32*i + 8*grp .. +7 (bf16) or 64*i + 16*grp .. +15 (E4M3)
+      const bool row_ok = ok && (t0 + hl < tok_end);
+      uint8_t* dst = my_vt + hl * RS;
+      if constexpr (CDT == PKV_BF16) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          *reinterpret_cast<uint4*>(dst + 2 * (32 * i + 8 * grp)) = row_ok ? vr[i] : make_uint4(0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const uint4 lo = row_ok ? fp8x8_to_bf16x8(vr[i].x, vr[i].y) : make_uint4(0, 0, 0, 0);
+          const uint4 hi = row_ok ? fp8x8_to_bf16x8(vr[i].z, vr[i].w) : make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp)) = lo;
+          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp) + 16) = hi;
+        }
+      }
+    }
+    // ---- online softmax for head hl over tokens t0 + 4*grp + r
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * grp + r;
+      z[r] = (ok && t < tok_end) ? sc[r] * a.zscale : -INFINITY;
+    }
+    float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
+    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
+    const float mn = fmaxf(m, mt_);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = pkv::fast_exp2(m - mref);
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = pkv::fast_exp2(z[r] - mref);
+    // the weights are used in bf16 by the PV product; sum the same rounded values
+    const uint32_t p01 = pack_bf16x2_rne(pr[0], pr[1]);
+    const uint32_t p23 = pack_bf16x2_rne(pr[2], pr[3]);
+    lsum = lsum * alpha + (pkv::bf16_lo(p01) + pkv::bf16_hi(p01)) + (pkv::bf16_lo(p23) + pkv::bf16_hi(p23));
+    m = mn;
+    const s16x4_t pf = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+    __builtin_amdgcn_wave_barrier();
+    // ---- O^T[d][head] += V^T[d][token] . P^T[token][head]
+    const uint8_t* src = my_vt + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const s16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 32 * mt));
+      f32x4_t acc = o[mt];
+      acc[0] *= alpha;
+      acc[1] *= alpha;
+      acc[2] *= alpha;
+      acc[3] *= alpha;
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  if (ntiles > 0) {
+    issue(0, kb[0], vb[0], tok0[0], okb[0]);
+    int n = 0;
+    for (; n + 1 < ntiles; n += 2) {
+      issue(n + 1, kb[1], vb[1], tok0[1], okb[1]);
+      consume(kb[0], vb[0], tok0[0], okb[0]);
+      if (n + 2 < ntiles) issue(n + 2, kb[0], vb[0], tok0[0], okb[0]);
+      consume(kb[1], vb[1], tok0[1], okb[1]);
+    }
+    if (n < ntiles) consume(kb[0], vb[0], tok0[0], okb[0]);
+  }
+
+  // lane-partial sums over the 4 lane groups (m is uniform per head across them)
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  if (hl < G) {
+    const int hq = g * G + hl;
+    const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+    const float lse2 = lsum > 0.f ? m + log2f(lsum) : -INFINITY;
+    if (nparts == 1) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(s) * Hq + hq) * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
+        const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 16 * mt) = make_uint2(lo, hi);
+      }
+      if (a.lse_out && grp == 0) a.lse_out[int64_t(s) * Hq + hq] = lse2 * kLn2;
+    } else {
+      const int64_t pi = (int64_t(s) * Hq + hq) * a.pmax + p;
+      float* orow = a.ws_o + pi * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<float4*>(orow + 16 * mt) =
+            make_float4(o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv, o[mt][3] * inv);
+      if (grp == 0) a.ws_lse[pi] = lse2;
+    }
+  }
+}
+
 constexpr int kWaves = 4;
 
 thread_local hipEvent_t g_profile_event = nullptr;
@@ -464,11 +738,54 @@ DecodeFn pick_d(int D, int G, int BS) {
   }
 }
 
-DecodeFn pick_decode(int qdt, int cdt, int D, int G, int BS) {
-  if (qdt == PKV_F32 && cdt == PKV_F32) return pick_d<PKV_F32, PKV_F32>(D, G, BS);
-  if (qdt == PKV_BF16 && cdt == PKV_BF16) return pick_d<PKV_BF16, PKV_BF16>(D, G, BS);
-  if (qdt == PKV_BF16 && cdt == PKV_FP8_E4M3) return pick_d<PKV_BF16, PKV_FP8_E4M3>(D, G, BS);
-  return nullptr;
+template <int CDT, int D, int HPW>
+DecodeFn pick_mfma_bs(int BS) {
+  switch (BS) {
+    case 16: return decode_mfma_kernel<CDT, D, 16, HPW>;
+    case 32: return decode_mfma_kernel<CDT, D, 32, HPW>;
+    default: return nullptr;
+  }
+}
+
+template <int CDT, int HPW>
+DecodeFn pick_mfma(int D, int BS) {
+  switch (D) {
+    case 64: return pick_mfma_bs<CDT, 64, HPW>(BS);
+    case 128: return pick_mfma_bs<CDT, 128, HPW>(BS);
+    default: return nullptr;
+  }
+}
+
+template <int CDT>
+DecodeFn pick_mfma_hpw(int D, int BS, int hpw) {
+  switch (hpw) {
+    case 1: return pick_mfma<CDT, 1>(D, BS);
+    case 2: return pick_mfma<CDT, 2>(D, BS);
+    case 4: return pick_mfma<CDT, 4>(D, BS);
+    case 8: return pick_mfma<CDT, 8>(D, BS);
+    default: return nullptr;
+  }
+}
+
+// KV heads per workgroup for the MFMA kernel: the largest of 8, 4, 2, 1 dividing Hkv
+// (measured on the 256-sequence batch: 8 heads 5.23 TB/s, 4 heads 5.20, 2 heads 4.13,
+// 1 head 3.73 with the earlier load layout; whole token rows per workgroup stream best).
+int mfma_heads_per_wg(int Hkv) {
+  for (int h : {8, 4, 2})
+    if (Hkv % h == 0) return h;
+  return 1;
+}
+
+// fp32 -> the VALU kernel (fp32 products, four waves per work item); bf16 queries ->
+// the MFMA kernel (one wave per KV head, *waves heads per workgroup).
+DecodeFn pick_decode(int qdt, int cdt, int D, int G, int BS, int Hkv, int* waves) {
+  if (qdt == PKV_F32 && cdt == PKV_F32) {
+    *waves = kWaves;
+    return pick_d<PKV_F32, PKV_F32>(D, G, BS);
+  }
+  if (qdt != PKV_BF16 || (cdt != PKV_BF16 && cdt != PKV_FP8_E4M3) || G < 1 || G > 16) return nullptr;
+  *waves = mfma_heads_per_wg(Hkv);
+  return cdt == PKV_BF16 ? pick_mfma_hpw<PKV_BF16>(D, BS, *waves) : pick_mfma_hpw<PKV_FP8_E4M3>(D, BS, *waves);
 }
 
 MergeFn pick_merge(int qdt, int D) {
@@ -504,7 +821,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
                                           int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
                                           float scale, float k_scale, float v_scale, int32_t partition_size,
                                           void* workspace, size_t workspace_bytes, float* lse_out,
-                                          void* stream) {
+                                          const int32_t* work_items, int32_t num_work, void* stream) {
   using pkv::fail;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
       max_seq_len < 0 || partition_size < 0)
@@ -514,7 +831,8 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
                 num_kv_heads);
   if (num_seqs > 65535) return fail(PKV_ERR_INVALID, "decode: at most 65535 sequences per launch");
   const int G = num_q_heads / num_kv_heads;
-  DecodeFn fn = pick_decode(q_dtype, cache_dtype, head_dim, G, block_size);
+  int waves = kWaves;
+  DecodeFn fn = pick_decode(q_dtype, cache_dtype, head_dim, G, block_size, num_kv_heads, &waves);
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED,
                 "decode: unsupported (q dtype %d, cache dtype %d, head_dim %d, group %d, block_size %d)", q_dtype,
@@ -557,8 +875,22 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
   }
   a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
   a.v_scale = v_scale;
+  a.group = G;
+  a.num_seqs = num_seqs;
+  const bool mfma = q_dtype == PKV_BF16;
+  const int head_groups = mfma ? num_kv_heads / waves : num_kv_heads;
+  dim3 grid(head_groups, a.pmax, num_seqs);
+  if (work_items) {
+    if (num_work <= 0 || num_work > 2147483647 / 4)
+      return fail(PKV_ERR_INVALID, "decode: num_work %d out of range", num_work);
+    if ((reinterpret_cast<uintptr_t>(work_items) & 15) != 0)
+      return fail(PKV_ERR_INVALID, "decode: work_items must be 16-byte aligned");
+    a.work = reinterpret_cast<const int4*>(work_items);
+    grid = dim3(head_groups, num_work, 1);
+    if (num_work > 65535 * 32) return fail(PKV_ERR_INVALID, "decode: too many work items");
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3(num_kv_heads, a.pmax, num_seqs), dim3(kWaves * 64), 0, st, a);
+  hipLaunchKernelGGL(fn, grid, dim3(waves * 64), 0, st, a);
   if (g_profile_event) (void)hipEventRecord(g_profile_event, st);
   if (need > 0) {
     MergeFn mf = pick_merge(q_dtype, head_dim);

@@ -6,6 +6,7 @@
 // free list, append on free, return a finished sequence's pages in table order) and
 // "Build a pure-Python continuous batching LLM serving engine from scratch", "Step 2"
 // (a multi-block request is all-or-nothing and fails when too few blocks are free).
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -230,6 +231,44 @@ int pkv_build_block_table(const pkv_pool* pool, int32_t num_seqs, const int64_t*
     for (int64_t p = L - q; p < L; ++p) slot_mapping[r++] = int64_t(t[p / bs]) * bs + p % bs;
     cu_seqlens_q[s + 1] = int32_t(r);
   }
+  return PKV_OK;
+}
+
+int pkv_build_decode_work(int32_t num_seqs, const int32_t* seq_lens, int32_t partition_size,
+                          int32_t* items, int32_t capacity, int32_t* count) {
+  if (num_seqs < 0 || partition_size < 0 || !count || (num_seqs > 0 && !seq_lens))
+    return fail(PKV_ERR_INVALID, "build_decode_work: bad arguments");
+  struct Item {
+    int32_t s, p, n, end, len;
+  };
+  std::vector<Item> full, tail;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = seq_lens[s] < 0 ? 0 : seq_lens[s];
+    if (partition_size == 0 || L <= partition_size) {
+      tail.push_back({s, 0, 1, L, L});
+      continue;
+    }
+    const int32_t n = int32_t((int64_t(L) + partition_size - 1) / partition_size);
+    for (int32_t p = 0; p < n; ++p) {
+      const int32_t b = p * partition_size;
+      const int32_t e = std::min(L, b + partition_size);
+      (e - b == partition_size ? full : tail).push_back({s, p, n, e, e - b});
+    }
+  }
+  std::stable_sort(tail.begin(), tail.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
+  const int64_t total = int64_t(full.size()) + int64_t(tail.size());
+  *count = int32_t(total);
+  if (total > capacity || (total > 0 && !items))
+    return fail(PKV_ERR_INVALID, "build_decode_work: %lld items, capacity %d", (long long)total, capacity);
+  int32_t* o = items;
+  for (const auto* v : {&full, &tail})
+    for (const Item& it : *v) {
+      o[0] = it.s;
+      o[1] = it.p;
+      o[2] = it.n;
+      o[3] = it.end;
+      o += 4;
+    }
   return PKV_OK;
 }
 

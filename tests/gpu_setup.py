@@ -186,7 +186,8 @@ def oracle_decode_sampled(w: workloads.Workload, pairs):
     return outs
 
 
-def run_decode(st: Step, partition_size: Optional[int] = None, lse: bool = True, max_seq_len=None):
+def run_decode(st: Step, partition_size: Optional[int] = None, lse: bool = True, max_seq_len=None,
+               use_work: bool = True):
     w = st.w
     P = w.partition_size if partition_size is None else partition_size
     B, Hq, d = w.num_seqs, w.num_q_heads, w.head_dim
@@ -195,8 +196,9 @@ def run_decode(st: Step, partition_size: Optional[int] = None, lse: bool = True,
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, d, msl, P)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
     lse_t = torch.empty((B, Hq), dtype=torch.float32, device="cuda") if lse else None
+    work = torch.from_numpy(pkv.build_decode_work(w.seq_lens, P)).cuda() if use_work else None
     pkv.paged_attention_decode(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, w.num_kv_heads,
-                               w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, P, ws, lse_t)
+                               w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, P, ws, lse_t, work=work)
     torch.cuda.synchronize()
     return out, lse_t
 

@@ -141,3 +141,28 @@ def test_block_tables_and_slots_bit_exact_on_configs(cfg):
                                  w.block_size, W)
     assert (slots2 == rslots2).all()
     assert len(np.unique(slots2)) == len(slots2)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.integers(0, 5000), max_size=40), st.sampled_from([0, 16, 64, 256, 512]))
+def test_decode_work_list_covers_every_partition_once(lens, P):
+    items = pkv.build_decode_work(lens, P)
+    want = set()
+    for s, L in enumerate(lens):
+        n = 1 if P == 0 or L <= P else -(-L // P)
+        for p in range(n):
+            want.add((s, p, n, min(L, (p + 1) * P) if n > 1 else L))
+    got = [tuple(int(x) for x in it) for it in items]
+    assert len(got) == len(set(got)) == len(want) and set(got) == want
+    work = [e - (p * P if P else 0) for _, p, _, e in got]
+    assert work == sorted(work, reverse=True)          # longest item first
+    with pytest.raises(pkv.PkvError):
+        if len(lens) > 0:
+            out = np.zeros((max(len(got) - 1, 0), 4), np.int32)
+            n = ctypes.c_int32()
+            L = np.asarray(lens, np.int32)
+            _lib.check(pkv.lib().pkv_build_decode_work(len(L), L.ctypes.data_as(ctypes.c_void_p), P,
+                                                       out.ctypes.data_as(ctypes.c_void_p), len(got) - 1,
+                                                       ctypes.byref(n)))
+        else:
+            raise pkv.PkvError(-1, "empty")

@@ -339,7 +339,7 @@ def config3() -> Workload:
     g = rng_for(seed, _STREAM_LENGTHS)
     L = np.clip(np.rint(g.lognormal(np.log(1024.0), 1.0, size=256)), 1, 8192).astype(np.int32)
     w = Workload("cfg3_large_decode_bf16", seed, "bf16", "bf16", 32, 8, 128, 16,
-                 L, np.ones(256, np.int32), 0, np.zeros(0, np.int32), partition_size=256)
+                 L, np.ones(256, np.int32), 0, np.zeros(0, np.int32), partition_size=512)
     w.num_blocks = _pool_1p2(w.blocks_needed())
     w.free_order = _permutation(seed, w.num_blocks)
     return w

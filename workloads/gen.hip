@@ -46,3 +46,45 @@ extern "C" int pkvgen_fill(void* out, int as_bf16, uint64_t key, int64_t e0, int
                      as_bf16, key, e0, count, sigma);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+
+// ---------------------------------------------------------------------------------
+// HBM stream-read probe (measurement only): every lane reads 16-byte chunks of `buf`
+// with UNROLL independent loads in flight per iteration, folds them with xor, and
+// writes one word per thread (so the loads cannot be dropped).
+// ---------------------------------------------------------------------------------
+namespace {
+template <int UNROLL>
+__global__ void __launch_bounds__(256) read_probe(const uint4* __restrict__ buf, int64_t n16, uint32_t* out) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = buf[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = buf[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
+}
+}  // namespace
+
+// buf: device, n16 chunks of 16 bytes; out: device uint32 [blocks * 256].
+extern "C" int pkvgen_read_probe(const void* buf, int64_t n16, int blocks, int unroll, void* out, void* stream) {
+  if (!buf || !out || n16 <= 0 || blocks <= 0) return -1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint4* b = static_cast<const uint4*>(buf);
+  uint32_t* o = static_cast<uint32_t*>(out);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(read_probe<1>, dim3(blocks), dim3(256), 0, st, b, n16, o); break;
+    case 2: hipLaunchKernelGGL(read_probe<2>, dim3(blocks), dim3(256), 0, st, b, n16, o); break;
+    case 4: hipLaunchKernelGGL(read_probe<4>, dim3(blocks), dim3(256), 0, st, b, n16, o); break;
+    case 8: hipLaunchKernelGGL(read_probe<8>, dim3(blocks), dim3(256), 0, st, b, n16, o); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}

@@ -39,6 +39,8 @@ def lib():
         L = C.CDLL(LIB)
         L.pkvgen_fill.restype = C.c_int
         L.pkvgen_fill.argtypes = [C.c_void_p, C.c_int, C.c_uint64, C.c_int64, C.c_int64, C.c_float, C.c_void_p]
+        L.pkvgen_read_probe.restype = C.c_int
+        L.pkvgen_read_probe.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib
 
@@ -53,6 +55,19 @@ def fill(t, key: int, e0: int, sigma: float = 1.0) -> None:
                            int(e0), t.numel(), float(sigma), C.c_void_p(st))
     if rc != 0:
         raise RuntimeError(f"pkvgen_fill failed ({rc})")
+
+
+def read_probe(buf, blocks: int, unroll: int, out) -> None:
+    """Stream-read the whole of device tensor `buf` (out: int32 tensor of blocks*256)."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    if out.numel() < blocks * 256 or nbytes % 16:
+        raise ValueError("probe buffers mis-sized")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib().pkvgen_read_probe(C.c_void_p(buf.data_ptr()), nbytes // 16, blocks, unroll,
+                                 C.c_void_p(out.data_ptr()), C.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError(f"pkvgen_read_probe failed ({rc})")
 
 
 if __name__ == "__main__":
