@@ -176,6 +176,40 @@ int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const 
                                void* workspace, size_t workspace_bytes, float* lse_out,
                                const int32_t* work_items, int32_t num_work, void* stream);
 
+/* Varlen work list (host) for pkv_paged_attention_prefill_varlen. For each sequence s
+ * with q = q_lens[s] new tokens and seq_len L = seq_lens[s] (host int32 arrays):
+ * q == 1 gives one decode item per group of 4 KV heads; q > 1 gives one prefill item
+ * per KV head and per block of 128/G new tokens (G = group = num_q_heads/num_kv_heads),
+ * whose keys end at the block's last position + 1; q == 0 gives none. items: host int32
+ * [capacity][4] = (seq, kind << 24 | KV head or head group, first new token of the
+ * block, keys to visit); longest first. *count = number of items. INVALID if
+ * q > L or capacity is too small; UNSUPPORTED unless G is 1, 2, 4, 8 or 16. */
+int pkv_build_varlen_work(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
+                          int32_t num_kv_heads, int32_t group, int32_t* items, int32_t capacity,
+                          int32_t* count);
+
+/* Attention for a mixed step of prefill chunks and decode rows in one launch ([CB]
+ * "5. Technical explanation", mixed batching: varlen kernels over cu_seqlens; [P17]
+ * "Step 6" per row). Sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+ * (device int32 [num_seqs+1], total_q rows in all); its new row i sits at position
+ * seq_lens[s] - q_s + i and sees keys 0 .. that position (bottom-right causal; the step's
+ * K/V are already in the cache). q, out: device bf16 [total_q][num_q_heads][head_dim].
+ * Cache, block_tables, seq_lens, scales, num_blocks, max_seq_len: as for decode.
+ * work_items: device int32 [num_work][4] from pkv_build_varlen_work for the same q_lens
+ * and seq_lens (rows not covered by an item are not written). lse_out: device float
+ * [total_q][num_q_heads], nullable (natural log). Supported: bf16 queries with a bf16
+ * or E4M3 cache, head_dim 64/128, block_size 16/32, group 1/2/4/8/16. */
+int pkv_paged_attention_prefill_varlen(void* out, const void* q, int32_t q_dtype,
+                                       const void* k_cache, const void* v_cache,
+                                       int32_t cache_dtype, const int32_t* block_tables,
+                                       const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                       int32_t table_width, int32_t num_seqs, int32_t total_q,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                                       float scale, float k_scale, float v_scale,
+                                       const int32_t* work_items, int32_t num_work, float* lse_out,
+                                       void* stream);
+
 /* Profiling hook (for timing the partition pass alone): while `hip_event` (a
  * hipEvent_t) is not NULL, every pkv_paged_attention_decode call made on this thread
  * records it on its stream right after the partition pass, before the merge kernel

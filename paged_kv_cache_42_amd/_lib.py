@@ -57,6 +57,9 @@ _SIGS = {
     "pkv_paged_attention_decode": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                              i32, i32, f32, f32, f32, i32, vp, sz, vp, vp, i32, vp]),
     "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
+    "pkv_build_varlen_work": (C.c_int, [i32, vp, vp, i32, i32, vp, i32, P_i32]),
+    "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                     i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, vp]),
 }
 
 
@@ -287,3 +290,43 @@ def decode_set_profile_event(event) -> None:
         lib().pkv_decode_set_profile_event(None)
         return
     lib().pkv_decode_set_profile_event(vp(event.cuda_event))
+
+
+def build_varlen_work(q_lens, seq_lens, num_kv_heads: int, group: int) -> np.ndarray:
+    """Host varlen work list: int32 [n][4] (seq, kind<<24 | head or group, first token, keys)."""
+    q = np.ascontiguousarray(q_lens, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qb = max(1, 128 // max(group, 1))
+    cap = int(sum((-(-int(x) // qb)) * num_kv_heads if x > 1 else (-(-num_kv_heads // 4) if x == 1 else 0)
+                  for x in q)) or 1
+    out = np.zeros((cap, 4), np.int32)
+    n = i32()
+    check(lib().pkv_build_varlen_work(len(q), _np_ptr(q), _np_ptr(L), num_kv_heads, group, _np_ptr(out), cap,
+                                      C.byref(n)))
+    return out[: n.value]
+
+
+def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,
+                                   num_kv_heads: int, block_size: int, max_seq_len: int, scale: float,
+                                   k_scale: float = 1.0, v_scale: float = 1.0, lse=None, stream=None) -> None:
+    """q/out: [total_q][Hq][d] bf16; cu_seqlens_q int32 [B+1]; work int32 [n][4] (device)."""
+    torch = _torch()
+    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work, lse)
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [total_q][Hq][d] of one dtype")
+    T, Hq, d = q.shape
+    _check_plane(k_cache, v_cache, block_size, num_kv_heads, d)
+    B = seq_lens.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][W]")
+    if seq_lens.dtype != torch.int32 or cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (B + 1,):
+        raise ValueError("seq_lens int32 [B] and cu_seqlens_q int32 [B+1] expected")
+    if work.dtype != torch.int32 or work.dim() != 2 or work.shape[1] != 4:
+        raise ValueError("work must be int32 [n][4] (from build_varlen_work)")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise ValueError("lse must be float32 [total_q][Hq]")
+    check(lib().pkv_paged_attention_prefill_varlen(
+        _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+        _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads, d,
+        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(work), work.shape[0], _dptr(lse),
+        _stream(stream)))

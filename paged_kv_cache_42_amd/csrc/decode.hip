@@ -29,6 +29,7 @@
 
 #include "pkv.h"
 #include "pkv_internal.h"
+#include "mfma_common.h"
 
 namespace {
 
@@ -472,40 +473,15 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
 //    stays lane-local.
 // ---------------------------------------------------------------------------------
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// 8 E4M3 codes (two words) -> 8 bf16 (exact: every E4M3 value is a bf16 value).
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t src = j < 2 ? lo : hi;
-    const uint32_t sh = 16 * (j & 1);
-    const uint32_t a = __float_as_uint(pkv::fp8_to_f32(src >> sh)) >> 16;
-    const uint32_t b = __float_as_uint(pkv::fp8_to_f32(src >> (sh + 8))) >> 16;
-    w[j] = a | (b << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
-  return pkv::f32_to_bf16(a) | (pkv::f32_to_bf16(b) << 16);
-}
+using pkv::bf16x8_t;
+using pkv::f32x4_t;
+using pkv::pack_bf16x2_rne;
 
 template <int CDT, int D, int BS, int HPW>
 __global__ void __launch_bounds__(HPW * 64) decode_mfma_kernel(DecodeArgs a) {
-  constexpr int CH = D / 4;                     // head_dim elements per lane group
-  constexpr int KS = D / 32;                    // QK k-steps (16x16x32)
-  constexpr int MT = D / 16;                    // PV d-tiles (16x16x16)
-  constexpr int EB = CDT == PKV_BF16 ? 2 : 1;   // cache bytes per element
-  constexpr int NV = CH * EB / 16;              // 16-byte loads per lane per tile (each of K, V)
-  constexpr int SUB = BS / 16;                  // 16-token tiles per block
-  constexpr int RS = D * 2 + 32;                // LDS row stride (bytes) of the bf16 V tile
-  static_assert(NV >= 1 && CH % 8 == 0, "unsupported head_dim");
-
+  constexpr int MT = D / 16;
+  constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
+  constexpr int RS = D * 2 + 32;
   // the HPW waves of a workgroup take HPW consecutive KV heads of the same work item,
   // so together they stream whole token rows of every block
   const int lane = threadIdx.x & 63;
@@ -518,164 +494,24 @@ __global__ void __launch_bounds__(HPW * 64) decode_mfma_kernel(DecodeArgs a) {
   const int grp = lane >> 4;
   int s, p, nparts, tok_begin, tok_end;
   if (!locate_item(a, s, p, nparts, tok_begin, tok_end)) return;
-  const int blk_begin = tok_begin / BS;
-  const int blk_end = (tok_end + BS - 1) / BS;
-
-  // queries: B operand of the QK MFMA, with the head_dim permutation of the K registers.
-  // K load i of a lane reads bytes 64*i + 16*grp of its token's head row, so k-step kk of
-  // lane group grp holds elements 32*kk + 8*grp .. +7 (bf16 cache) or, as half of a
-  // 16-element E4M3 load, 64*(kk/2) + 16*grp + 8*(kk%2) .. +7.
-  bf16x8_t qf[KS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(s) * Hq + int64_t(g) * G + hl) * D;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int d0 = EB == 2 ? 32 * kk + 8 * grp : 64 * (kk / 2) + 16 * grp + 8 * (kk % 2);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (hl < G) v = *reinterpret_cast<const uint4*>(qrow + d0);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-
-  float m = -INFINITY, lsum = 0.f;
-  f32x4_t o[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[HPW][16 * RS];
-  uint8_t* my_vt = vt_lds[w];
+  pkv::DecodeWaveIn in;
+  in.q = static_cast<const uint16_t*>(a.q) + (int64_t(s) * Hq + int64_t(g) * G) * D;
+  in.G = G;
+  in.kc = static_cast<const uint8_t*>(a.k_cache);
+  in.vc = static_cast<const uint8_t*>(a.v_cache);
+  in.row_bytes = int64_t(Hkv) * D * EB;
+  in.head_off = int64_t(g) * D * EB;
+  in.bt_row = a.block_tables + int64_t(s) * a.table_width;
+  in.num_blocks = a.num_blocks;
+  in.tok_begin = tok_begin;
+  in.tok_end = tok_end;
+  in.zscale = a.zscale;
+  float m, lsum;
+  f32x4_t o[MT];
+  pkv::decode_wave<CDT, D, BS>(in, vt_lds[w], m, lsum, o);
 
-  const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache);
-  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache);
-  const int64_t row_bytes = int64_t(Hkv) * D * EB;                  // one token, all KV heads
-  const int64_t lane_off = int64_t(g) * D * EB + 16 * grp;
-  const int32_t* bt_row = a.block_tables + int64_t(s) * a.table_width;
-  const int nblk = blk_end - blk_begin;
-  const int ntiles = nblk * SUB;
-
-  // block ids of the item, 64 at a time, one per lane (read back with readlane)
-  int bt_base = -64, bt_lane = 0;
-  auto block_id = [&](int j) -> int {   // j: block index relative to blk_begin (wave-uniform)
-    const int base = j & ~63;
-    if (base != bt_base) {
-      bt_base = base;
-      const int jj = blk_begin + base + lane;
-      bt_lane = jj < blk_end ? bt_row[jj] : -1;
-    }
-    return __builtin_amdgcn_readlane(bt_lane, j & 63);
-  };
-
-  uint4 kb[2][NV], vb[2][NV];
-  int tok0[2];
-  bool okb[2];
-
-  auto issue = [&](int n, uint4 (&kr)[NV], uint4 (&vr)[NV], int& t0, bool& ok) {
-    const int j = n / SUB;
-    const int sub = n % SUB;
-    const int blk = block_id(j);
-    ok = blk >= 0 && blk < a.num_blocks;
-    t0 = (blk_begin + j) * BS + sub * 16;
-    const int64_t off = (int64_t(ok ? blk : 0) * BS + sub * 16 + hl) * row_bytes + lane_off;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if (ok) {
-        kr[i] = *reinterpret_cast<const uint4*>(kc + off + 64 * i);
-        vr[i] = *reinterpret_cast<const uint4*>(vc + off + 64 * i);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  auto consume = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int t0, bool ok) {
-    // ---- scores S^T[token][head] = K . Q^T
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (CDT == PKV_BF16) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[kk]), qf[kk], sc, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const uint4 lo = fp8x8_to_bf16x8(kr[i].x, kr[i].y);
-        const uint4 hi = fp8x8_to_bf16x8(kr[i].z, kr[i].w);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qf[2 * i], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qf[2 * i + 1], sc, 0, 0, 0);
-      }
-    }
-    // ---- V tile -> LDS as bf16 rows; rows of tokens past the context are zeroed
-    {
-      // load i holds head_dim elements 32*i + 8*grp .. +7 (bf16) or 64*i + 16*grp .. +15 (E4M3)
-      const bool row_ok = ok && (t0 + hl < tok_end);
-      uint8_t* dst = my_vt + hl * RS;
-      if constexpr (CDT == PKV_BF16) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-          *reinterpret_cast<uint4*>(dst + 2 * (32 * i + 8 * grp)) = row_ok ? vr[i] : make_uint4(0, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const uint4 lo = row_ok ? fp8x8_to_bf16x8(vr[i].x, vr[i].y) : make_uint4(0, 0, 0, 0);
-          const uint4 hi = row_ok ? fp8x8_to_bf16x8(vr[i].z, vr[i].w) : make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp)) = lo;
-          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp) + 16) = hi;
-        }
-      }
-    }
-    // ---- online softmax for head hl over tokens t0 + 4*grp + r
-    float z[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 4 * grp + r;
-      z[r] = (ok && t < tok_end) ? sc[r] * a.zscale : -INFINITY;
-    }
-    float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
-    const float mn = fmaxf(m, mt_);
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = pkv::fast_exp2(m - mref);
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = pkv::fast_exp2(z[r] - mref);
-    // the weights are used in bf16 by the PV product; sum the same rounded values
-    const uint32_t p01 = pack_bf16x2_rne(pr[0], pr[1]);
-    const uint32_t p23 = pack_bf16x2_rne(pr[2], pr[3]);
-    lsum = lsum * alpha + (pkv::bf16_lo(p01) + pkv::bf16_hi(p01)) + (pkv::bf16_lo(p23) + pkv::bf16_hi(p23));
-    m = mn;
-    const s16x4_t pf = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-    __builtin_amdgcn_wave_barrier();
-    // ---- O^T[d][head] += V^T[d][token] . P^T[token][head]
-    const uint8_t* src = my_vt + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const s16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 32 * mt));
-      f32x4_t acc = o[mt];
-      acc[0] *= alpha;
-      acc[1] *= alpha;
-      acc[2] *= alpha;
-      acc[3] *= alpha;
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, acc, 0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
-
-  if (ntiles > 0) {
-    issue(0, kb[0], vb[0], tok0[0], okb[0]);
-    int n = 0;
-    for (; n + 1 < ntiles; n += 2) {
-      issue(n + 1, kb[1], vb[1], tok0[1], okb[1]);
-      consume(kb[0], vb[0], tok0[0], okb[0]);
-      if (n + 2 < ntiles) issue(n + 2, kb[0], vb[0], tok0[0], okb[0]);
-      consume(kb[1], vb[1], tok0[1], okb[1]);
-    }
-    if (n < ntiles) consume(kb[0], vb[0], tok0[0], okb[0]);
-  }
-
-  // lane-partial sums over the 4 lane groups (m is uniform per head across them)
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
 
   if (hl < G) {
     const int hq = g * G + hl;

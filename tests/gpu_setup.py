@@ -213,3 +213,18 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what=""):
         tol = TOL[dtype]
         err = np.abs(got - ref)
         assert np.all(err <= tol), f"{what}: max abs err {np.nanmax(err):.3e} > {tol}"
+
+
+def run_varlen(st: Step, lse: bool = True, max_seq_len=None):
+    """The mixed-step launch (prefill chunks + decode rows) over the step's rows."""
+    w = st.w
+    T, Hq, d = w.total_q, w.num_q_heads, w.head_dim
+    msl = int(w.seq_lens.max()) if max_seq_len is None else max_seq_len
+    out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_t = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    work = torch.from_numpy(pkv.build_varlen_work(w.q_lens, w.seq_lens, w.num_kv_heads, w.group)).cuda()
+    pkv.paged_attention_prefill_varlen(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d, work,
+                                       w.num_kv_heads, w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale,
+                                       lse=lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t
