@@ -35,6 +35,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg3", choices=["cfg3", "cfg4"])
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="skip the mixed prefill+decode step (48 decode rows + 4 chunks of 512) sub-measurement")
     ap.add_argument("--partition", type=int, default=None, help="split-context partition (tokens); 0 = none")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -109,6 +111,109 @@ def write_bytes(w) -> int:
     e_kv = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
     T = int(w.q_lens.sum())
     return T * 2 * w.num_kv_heads * w.head_dim * (e_in + e_kv) + T * 8
+
+
+def mixed_bytes_flops(w):
+    """Algorithmic bytes and flops of one varlen launch over a mixed step."""
+    import numpy as np
+    e = 2
+    L = w.seq_lens.astype(np.int64)
+    q = w.q_lens.astype(np.int64)
+    nbytes = int(L.sum()) * 2 * w.num_kv_heads * w.head_dim * e + int(q.sum()) * w.num_q_heads * w.head_dim * 2 * e
+    nbytes += int(((L + w.block_size - 1) // w.block_size).sum()) * 4 + (2 * w.num_seqs + 1) * 4
+    keys = 0
+    for Ls, qs in zip(L, q):
+        keys += int(qs * (Ls - qs) + qs * (qs + 1) // 2)      # row i sees L - q + i + 1 keys
+    flops = keys * w.num_q_heads * w.head_dim * 4
+    return nbytes, flops
+
+
+def mixed_step(steps: int, warmup: int):
+    """Config-2 mixed continuous-batching step: cache write of the 2096 new tokens, then
+    one varlen launch over 48 decode rows and 4 prefill chunks of 512 (causal)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_42_amd as pkv
+    import workloads
+    import workloads.gpu as wgen
+
+    w = workloads.config2()
+    pool = pkv.Pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.cache_dtype, free_order=w.free_order)
+    for op in w.history:                       # fragment the pool with the dummy owners
+        if op[0] == "alloc":
+            pool.seq_reserve((1 << 40) + op[1], op[2] * w.block_size)
+        else:
+            pool.seq_release((1 << 40) + op[1])
+    for s, L in enumerate(w.seq_lens):
+        pool.seq_reserve(s, int(L))
+    W = w.max_blocks_per_seq()
+    ids = np.arange(w.num_seqs)
+    prior = (w.seq_lens - w.q_lens).astype(np.int32)
+    _, _, ctx_slots = pool.build_block_table(ids, prior, prior, W)
+    bt, cu, slots = pool.build_block_table(ids, w.q_lens, w.seq_lens, W)
+    Hkv, Hq, d = w.num_kv_heads, w.num_q_heads, w.head_dim
+    shape = (w.num_blocks, w.block_size, Hkv, d)
+    kc = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    n_ctx, n_new = int(prior.sum()), int(w.q_lens.sum())
+    ck = torch.empty((n_ctx, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    cv = torch.empty_like(ck)
+    nk = torch.empty((n_new, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    nv = torch.empty_like(nk)
+    q = torch.empty((n_new, Hq, d), dtype=torch.bfloat16, device="cuda")
+    oc = on = 0
+    for s in range(w.num_seqs):
+        p, L = int(prior[s]), int(w.seq_lens[s])
+        if p:
+            wgen.fill(ck[oc:oc + p], w.value_key("k", s), 0, w.sigma)
+            wgen.fill(cv[oc:oc + p], w.value_key("v", s), 0, w.sigma)
+        wgen.fill(nk[on:on + L - p], w.value_key("k", s), p * Hkv * d, w.sigma)
+        wgen.fill(nv[on:on + L - p], w.value_key("v", s), p * Hkv * d, w.sigma)
+        wgen.fill(q[on:on + L - p], w.value_key("q", s), p * Hq * d, w.sigma)
+        oc += p
+        on += L - p
+    pkv.kv_cache_write(ck, cv, kc, vc, torch.from_numpy(ctx_slots).cuda(), w.block_size)
+    del ck, cv
+    slots_d = torch.from_numpy(slots).cuda()
+    bt_d = torch.from_numpy(bt).cuda()
+    lens_d = torch.from_numpy(w.seq_lens.astype(np.int32)).cuda()
+    cu_d = torch.from_numpy(cu).cuda()
+    work = torch.from_numpy(pkv.build_varlen_work(w.q_lens, w.seq_lens, Hkv, w.group)).cuda()
+    out = torch.empty_like(q)
+    msl = int(w.seq_lens.max())
+    stream = torch.cuda.current_stream()
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        pkv.kv_cache_write(nk, nv, kc, vc, slots_d, w.block_size)
+        if e is not None:
+            e[1].record(stream)
+        pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, work, Hkv, w.block_size, msl,
+                                           w.softmax_scale)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    t_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    nbytes, flops = mixed_bytes_flops(w)
+    return {"workload": f"{w.name}: 48 decode rows (context U[16,2048]) + 4 causal chunks of 512 new tokens "
+                        f"after 0/512/1024/1536 cached, 32/8 heads, d 128, bs 16, bf16, fragmented pool",
+            "query_tokens": n_new, "context_tokens": int(w.seq_lens.sum()), "ms_per_step": round(wall * 1e3, 4),
+            "kernel_us": {"kv_cache_write": round(t_w * 1e6, 2), "varlen_attention": round(t_a * 1e6, 2)},
+            "tokens_per_s": round(n_new / wall, 1),
+            "attention_bytes": nbytes, "attention_flops": flops,
+            "hbm_GBps": round(nbytes / t_a / 1e9, 1), "hbm_frac": round(nbytes / t_a / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_TFLOPs": round(flops / t_a / 1e12, 1), "mfma_frac": round(flops / t_a / 1e12 / 2500.0, 4)}
 
 
 def measured_traffic(partition: int, workload: str):
@@ -343,6 +448,9 @@ def main():
                      "kernel": "decode partition pass", "algorithmic_bytes": dbytes},
         "cpu_baseline": None,
     }
+    if not args.no_mixed:
+        print("[bench] mixed prefill+decode step", file=sys.stderr, flush=True)
+        res["mixed_step"] = mixed_step(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

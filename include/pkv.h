@@ -178,11 +178,11 @@ int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const 
 
 /* Varlen work list (host) for pkv_paged_attention_prefill_varlen. For each sequence s
  * with q = q_lens[s] new tokens and seq_len L = seq_lens[s] (host int32 arrays):
- * q == 1 gives one decode item per group of 4 KV heads; q > 1 gives one prefill item
+ * q == 1 gives one decode item per KV head; q > 1 gives one prefill item
  * per KV head and per block of 128/G new tokens (G = group = num_q_heads/num_kv_heads),
  * whose keys end at the block's last position + 1; q == 0 gives none. items: host int32
  * [capacity][4] = (seq, kind << 24 | KV head or head group, first new token of the
- * block, keys to visit); longest first. *count = number of items. INVALID if
+ * block, keys to visit); longest first (by keys to visit). *count = number of items. INVALID if
  * q > L or capacity is too small; UNSUPPORTED unless G is 1, 2, 4, 8 or 16. */
 int pkv_build_varlen_work(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
                           int32_t num_kv_heads, int32_t group, int32_t* items, int32_t capacity,

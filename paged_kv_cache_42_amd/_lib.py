@@ -297,7 +297,7 @@ def build_varlen_work(q_lens, seq_lens, num_kv_heads: int, group: int) -> np.nda
     q = np.ascontiguousarray(q_lens, dtype=np.int32)
     L = np.ascontiguousarray(seq_lens, dtype=np.int32)
     qb = max(1, 128 // max(group, 1))
-    cap = int(sum((-(-int(x) // qb)) * num_kv_heads if x > 1 else (-(-num_kv_heads // 4) if x == 1 else 0)
+    cap = int(sum((-(-int(x) // qb)) * num_kv_heads if x > 1 else (num_kv_heads if x == 1 else 0)
                   for x in q)) or 1
     out = np.zeros((cap, 4), np.int32)
     n = i32()

@@ -98,38 +98,28 @@ __device__ __forceinline__ void decode_wave(const DecodeWaveIn& in, uint8_t* my_
   const int nblk = blk_end - blk_begin;
   const int ntiles = nblk * SUB;
 
-  // block ids of the item, 64 at a time, one per lane (read back with readlane)
-  int bt_base = -64, bt_lane = 0;
-  auto block_id = [&](int j) -> int {   // j: block index relative to blk_begin (wave-uniform)
-    const int base = j & ~63;
-    if (base != bt_base) {
-      bt_base = base;
-      const int jj = blk_begin + base + lane;
-      bt_lane = jj < blk_end ? bt_row[jj] : -1;
-    }
-    return __builtin_amdgcn_readlane(bt_lane, j & 63);
-  };
+  // block ids are wave-uniform: read them through the constant address space so they
+  // become scalar loads (counted apart from the vector K/V loads, never draining them)
+  const __attribute__((address_space(4))) int32_t* btc =
+      (const __attribute__((address_space(4))) int32_t*)(uintptr_t)(bt_row);
 
   uint4 kb[2][NV], vb[2][NV];
   int tok0[2];
   bool okb[2];
 
+  // K/V loads are unconditional (a skipped block reads block 0 and is zeroed after), so
+  // the number of loads in flight is static and waits stay partial
   auto issue = [&](int n, uint4 (&kr)[NV], uint4 (&vr)[NV], int& t0, bool& ok) {
     const int j = n / SUB;
     const int sub = n % SUB;
-    const int blk = block_id(j);
+    const int blk = btc[blk_begin + j];
     ok = blk >= 0 && blk < in.num_blocks;
     t0 = (blk_begin + j) * BS + sub * 16;
     const int64_t off = (int64_t(ok ? blk : 0) * BS + sub * 16 + hl) * row_bytes + lane_off;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      if (ok) {
-        kr[i] = *reinterpret_cast<const uint4*>(kc + off + 64 * i);
-        vr[i] = *reinterpret_cast<const uint4*>(vc + off + 64 * i);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
+      kr[i] = *reinterpret_cast<const uint4*>(kc + off + 64 * i);
+      vr[i] = *reinterpret_cast<const uint4*>(vc + off + 64 * i);
     }
   };
 

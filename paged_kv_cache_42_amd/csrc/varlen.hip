@@ -10,17 +10,19 @@
 // sequence with q new tokens and seq_len L sits at position L - q + i and attends keys
 // 0 .. L - q + i (bottom-right causal alignment, the K/V of the step already written).
 //
-// gfx950 design (one kernel, 4-wave workgroups, a host work list, longest item first):
+// gfx950 design (one kernel, 8-wave workgroups, a host work list, longest item first):
 //  * prefill item = (sequence, KV head g, block of 128/G new tokens): the 128 query rows
 //    (token, head) -- GQA packed, all G heads of g share each K/V tile -- are split over
-//    the 4 waves, 32 rows (two 16-column MFMA blocks) each. K/V tiles of 32 keys are
+//    the 8 waves, 16 rows (one 16-column MFMA block) each. K/V tiles of 32 keys are
 //    staged in LDS by the whole workgroup with coalesced 16-byte loads (each 16 lanes
 //    read one head row), double buffered; K fragments are read with ds_read_b128 as
-//    the A operand of v_mfma_f32_16x16x32_bf16, V^T fragments with ds_read_b64_tr_b16
-//    for v_mfma_f32_16x16x16_bf16. Tiles past the block's last position are never
-//    loaded; on the diagonal, scores are masked per row.
-//  * decode item = (sequence with one new token, 4 KV heads): each wave streams one KV
-//    head's context with the decode kernel's per-wave loop (mfma_common.h).
+//    the A operand of v_mfma_f32_16x16x32_bf16; the softmax runs over the whole tile and
+//    P.V uses the same instruction, its V^T operand assembled from two
+//    ds_read_b64_tr_b16. Tiles past the block's last position are never loaded; on the
+//    diagonal, scores are masked per row.
+//  * decode item = (sequence with one new token, KV head): the 8 waves stream contiguous
+//    block ranges of the context with the decode kernel's per-wave loop (mfma_common.h)
+//    and merge their partial softmax states by log-sum-exp through LDS.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,6 +46,9 @@ constexpr int kKindPrefill = 0;
 constexpr int kKindDecode = 1;
 constexpr int kRowsPerItem = 128;   // query rows (token, head) of a prefill item
 constexpr int kTileKeys = 32;       // keys per LDS tile
+constexpr int kWaves = 8;           // waves per workgroup: 16 rows each / one KV head each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = 4;           // K/V tiles in flight per workgroup (register ring)
 
 struct VarlenArgs {
   const uint16_t* q;      // [total_q][Hq][D] bf16
@@ -71,25 +76,32 @@ struct Smem {
   static constexpr int RS = D * 2 + 32;                       // bytes per bf16 key row (padded)
   static constexpr int kTile = kTileKeys * RS;                // one K or V tile
   static constexpr int kPrefill = 4 * kTile;                  // K, V x double buffer
-  static constexpr int kDecode = 4 * 16 * RS;                 // 4 waves' V tiles
+  static constexpr int kDecodeTiles = kWaves * 16 * RS;       // the waves' V tiles
+  static constexpr int kDecodeMerge = (kWaves / 2) * (D / 4 + 2) * 64 * 4;   // merge states
+  static constexpr int kDecode = kDecodeTiles > kDecodeMerge ? kDecodeTiles : kDecodeMerge;
   static constexpr int kBytes = kPrefill > kDecode ? kPrefill : kDecode;
 };
 
+// Decode item (one new token of sequence s, KV head g): the 8 waves take contiguous
+// ranges of the context's blocks, stream them with the decode kernel's per-wave loop,
+// then merge their (m, l, o) states in three LDS rounds (8 -> 4 -> 2 -> 1 waves).
 template <int CDT, int D, int BS>
-__device__ __forceinline__ void run_decode_item(const VarlenArgs& a, uint8_t* smem, int s, int hg, int key_end) {
+__device__ __forceinline__ void run_decode_item(const VarlenArgs& a, uint8_t* smem, int s, int g, int key_end) {
   constexpr int MT = D / 16;
   constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
   constexpr int RS = D * 2 + 32;
+  constexpr int NS = MT * 4 + 2;                 // floats of one lane's state
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int g = hg * 4 + w;
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * G;
-  if (g >= Hkv) return;                      // no workgroup barrier on this path
   const int hl = lane & 15;
   const int grp = lane >> 4;
-  const int row = a.cu_q[s + 1] - 1;         // the sequence's one new token
+  const int row = a.cu_q[s + 1] - 1;             // the sequence's one new token
+  const int nblk = (key_end + BS - 1) / BS;
+  const int per = (nblk + kWaves - 1) / kWaves;  // blocks per wave
+  const int b0 = min(nblk, w * per), b1 = min(nblk, (w + 1) * per);
   pkv::DecodeWaveIn in;
   in.q = a.q + (int64_t(row) * Hq + int64_t(g) * G) * D;
   in.G = G;
@@ -99,25 +111,57 @@ __device__ __forceinline__ void run_decode_item(const VarlenArgs& a, uint8_t* sm
   in.head_off = int64_t(g) * D * EB;
   in.bt_row = a.block_tables + int64_t(s) * a.table_width;
   in.num_blocks = a.num_blocks;
-  in.tok_begin = 0;
-  in.tok_end = key_end;
+  in.tok_begin = b0 * BS;
+  in.tok_end = min(key_end, b1 * BS);
   in.zscale = a.zscale;
   float m, lsum;
   f32x4_t o[MT];
   pkv::decode_wave<CDT, D, BS>(in, smem + w * 16 * RS, m, lsum, o);
-  if (hl < G) {
-    const int hq = g * G + hl;
-    const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
-    uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+
+  // tree merge; the state of wave x lives at st + x*NS*64, one float per (field, lane)
+  __syncthreads();                               // the V tiles are no longer needed
+  float* st = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
-      const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * mt) = make_uint2(lo, hi);
+  for (int half = kWaves / 2; half >= 1; half /= 2) {
+    if (w >= half && w < 2 * half) {
+      float* dst = st + (w - half) * NS * 64 + lane;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * mt + r) * 64] = o[mt][r];
+      dst[(4 * MT) * 64] = m;
+      dst[(4 * MT + 1) * 64] = lsum;
     }
-    if (a.lse_out && grp == 0)
-      a.lse_out[int64_t(row) * Hq + hq] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+    __syncthreads();
+    if (w < half) {
+      const float* src = st + w * NS * 64 + lane;
+      const float mo = src[(4 * MT) * 64];
+      const float lo = src[(4 * MT + 1) * 64];
+      const float mn = fmaxf(m, mo);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float ca = pkv::fast_exp2(m - mref);
+      const float cb = pkv::fast_exp2(mo - mref);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[mt][r] = o[mt][r] * ca + src[(4 * mt + r) * 64] * cb;
+      lsum = lsum * ca + lo * cb;
+      m = mn;
+    }
+    __syncthreads();
   }
+  if (w != 0 || hl >= G) return;
+  const int hq = g * G + hl;
+  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+  uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
+    const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
+    *reinterpret_cast<uint2*>(orow + 16 * mt) = make_uint2(lo, hi);
+  }
+  if (a.lse_out && grp == 0)
+    a.lse_out[int64_t(row) * Hq + hq] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
 template <int CDT, int D, int BS>
@@ -130,8 +174,7 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
   constexpr int TILE = Smem<CDT, D>::kTile;
   constexpr int CPK = D * EB / 16;                      // 16-byte chunks per key head row
   constexpr int CHUNKS = kTileKeys * CPK;               // per plane per tile
-  constexpr int LPT = (CHUNKS + 255) / 256;             // chunk loads per thread per plane
-  constexpr int NB = 2;                                 // 16-row MFMA blocks per wave
+  constexpr int LPT = (CHUNKS + kThreads - 1) / kThreads;   // chunk loads per thread per plane
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -149,71 +192,67 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
   const int QB = kRowsPerItem / G;                      // new tokens of this item
   const int ntok = min(QB, qs - q0);
 
-  // rows of this wave: r = 32*w + 16*nb + hl -> token r / G, head r % G
-  int tok_of[NB];
-  bool row_ok[NB];
-  bf16x8_t qf[NB][KS];
-  int wave_last_pos = -1;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int r = 32 * w + 16 * nb + hl;
-    tok_of[nb] = r / G;
-    row_ok[nb] = tok_of[nb] < ntok;
-    const uint16_t* qrow =
-        a.q + (int64_t(row0 + q0 + tok_of[nb]) * Hq + int64_t(g) * G + r % G) * D + 8 * grp;
+  // this wave's 16 rows: r = 16*w + hl -> token r / G, head r % G
+  const int r_row = 16 * w + hl;
+  const int tok = r_row / G;
+  const bool row_ok = tok < ntok;
+  const int pos = pos0 + q0 + tok;
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = a.q + (int64_t(row0 + q0 + tok) * Hq + int64_t(g) * G + r_row % G) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_ok[nb]) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-      qf[nb][kk] = __builtin_bit_cast(bf16x8_t, v);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  {
-    // last position among this wave's valid rows (wave-uniform)
-    const int last_tok = min(ntok - 1, (32 * w + 31) / G);
-    wave_last_pos = last_tok >= (32 * w) / G ? pos0 + q0 + last_tok : -1;
-  }
+  // last position among this wave's valid rows (wave-uniform)
+  const int last_tok = min(ntok - 1, (16 * w + 15) / G);
+  const int wave_last_pos = last_tok >= (16 * w) / G ? pos0 + q0 + last_tok : -1;
 
-  float m[NB], lsum[NB];
-  f32x4_t o[NB][MT];
+  float m = -INFINITY, lsum = 0.f;
+  f32x4_t o[MT];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m[nb] = -INFINITY;
-    lsum[nb] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[nb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt_row = a.block_tables + int64_t(s) * a.table_width;
   const int64_t row_bytes = int64_t(Hkv) * D * EB;
   const int64_t head_off = int64_t(g) * D * EB;
   const int ntiles = (key_end + kTileKeys - 1) / kTileKeys;
 
-  uint4 kst[LPT], vst[LPT];
-  auto stage = [&](int t) {
+  // tile t is staged in registers kst[t % kDepth] (kDepth tiles in flight), then
+  // committed to the LDS buffer t % 2 one iteration before it is consumed
+  uint4 kst[kDepth][LPT], vst[kDepth][LPT];
+  // block ids of a tile are wave-uniform scalar loads (constant address space); K/V loads
+  // are unconditional (clamped to block 0, zeroed after) so the ring's waits stay partial
+  const __attribute__((address_space(4))) int32_t* btc =
+      (const __attribute__((address_space(4))) int32_t*)(uintptr_t)(bt_row);
+  auto stage = [&](int t, uint4 (&ks)[LPT], uint4 (&vs)[LPT]) {
+    const int key0 = t * kTileKeys;
+    const int blk0 = btc[key0 / BS];
+    const int blk1 = BS >= kTileKeys ? blk0 : (key0 + 16 < key_end ? btc[(key0 + 16) / BS] : -1);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i;
-      const int key = t * kTileKeys + c / CPK;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (c < CHUNKS && key < key_end) {
-        const int blk = bt_row[key / BS];
-        if (blk >= 0 && blk < a.num_blocks) {
-          const int64_t off = (int64_t(blk) * BS + key % BS) * row_bytes + head_off + 16 * (c % CPK);
-          kv = *reinterpret_cast<const uint4*>(a.kc + off);
-          vv = *reinterpret_cast<const uint4*>(a.vc + off);
-        }
-      }
-      kst[i] = kv;
-      vst[i] = vv;
+      const int c = min(tid + kThreads * i, CHUNKS - 1);
+      const int kt = c / CPK;                              // key within the tile
+      const int key = key0 + kt;
+      const int blk = (BS >= kTileKeys || kt < 16) ? blk0 : blk1;
+      const bool ok = tid + kThreads * i < CHUNKS && key < key_end && blk >= 0 && blk < a.num_blocks;
+      int64_t off = ok ? (int64_t(blk) * BS + key % BS) * row_bytes + head_off + 16 * (c % CPK) : 0;
+      asm volatile("" : "+v"(off));                        // keep the load unconditional
+      const uint4 kv = *reinterpret_cast<const uint4*>(a.kc + off);
+      const uint4 vv = *reinterpret_cast<const uint4*>(a.vc + off);
+      ks[i] = ok ? kv : make_uint4(0, 0, 0, 0);
+      vs[i] = ok ? vv : make_uint4(0, 0, 0, 0);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, const uint4 (&kst)[LPT], const uint4 (&vst)[LPT]) {
     uint8_t* kt = smem + buf * 2 * TILE;
     uint8_t* vt = kt + TILE;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + kThreads * i;
       if (c >= CHUNKS) continue;
       const int key = c / CPK;
       const int ci = c % CPK;
@@ -228,96 +267,102 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
       }
     }
   };
+  // One 32-key tile: scores for keys key0 + 16*sb + 4*grp + r (sb = 0, 1), softmax over
+  // the tile, then P.V on v_mfma_f32_16x16x32_bf16 whose k index 8*grp + j runs over keys
+  // 4*grp + j (j < 4) and 16 + 4*grp + (j - 4) (j >= 4): the lane's own 8 weights.
   auto compute = [&](int t, int buf) {
+    const int key0 = t * kTileKeys;
+    if (key0 > wave_last_pos) return;                        // wave-uniform: all masked
     const uint8_t* kt = smem + buf * 2 * TILE;
     const uint8_t* vt = kt + TILE;
+    float z[8];
 #pragma unroll
-    for (int sb = 0; sb < kTileKeys / 16; ++sb) {
-      const int key0 = t * kTileKeys + 16 * sb;
-      if (key0 > wave_last_pos || key0 >= key_end) continue;     // wave-uniform: all masked
-      bf16x8_t kf[KS];
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        kf[kk] = *reinterpret_cast<const bf16x8_t*>(kt + (16 * sb + hl) * RS + 2 * (32 * kk + 8 * grp));
-      s16x4_t vf[MT];
-      const uint8_t* vsrc = vt + (16 * sb + 4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) vf[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 32 * mt));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[nb][kk], sc, 0, 0, 0);
-        const int pos = pos0 + q0 + tok_of[nb];
-        float z[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 4 * grp + r;
-          z[r] = (row_ok[nb] && key <= pos && key < key_end) ? sc[r] * a.zscale : -INFINITY;
-        }
-        float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
-        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
-        const float mn = fmaxf(m[nb], mt_);
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = pkv::fast_exp2(m[nb] - mref);
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = pkv::fast_exp2(z[r] - mref);
-        const uint32_t p01 = pack_bf16x2_rne(pr[0], pr[1]);
-        const uint32_t p23 = pack_bf16x2_rne(pr[2], pr[3]);
-        lsum[nb] = lsum[nb] * alpha + (pkv::bf16_lo(p01) + pkv::bf16_hi(p01)) + (pkv::bf16_lo(p23) + pkv::bf16_hi(p23));
-        m[nb] = mn;
-        const s16x4_t pf = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          f32x4_t acc = o[nb][mt];
-          acc[0] *= alpha;
-          acc[1] *= alpha;
-          acc[2] *= alpha;
-          acc[3] *= alpha;
-          o[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[mt], pf, acc, 0, 0, 0);
-        }
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + (16 * sb + hl) * RS + 2 * (32 * kk + 8 * grp));
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], sc, 0, 0, 0);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 16 * sb + 4 * grp + r;
+        z[4 * sb + r] = (row_ok && key <= pos && key < key_end) ? sc[r] * a.zscale : -INFINITY;
+      }
+    }
+    float mt_ = z[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mt_ = fmaxf(mt_, z[j]);
+    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
+    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
+    const float mn = fmaxf(m, mt_);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = pkv::fast_exp2(m - mref);
+    uint32_t pw[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pw[j] = pack_bf16x2_rne(pkv::fast_exp2(z[2 * j] - mref), pkv::fast_exp2(z[2 * j + 1] - mref));
+      ps += pkv::bf16_lo(pw[j]) + pkv::bf16_hi(pw[j]);
+    }
+    lsum = lsum * alpha + ps;
+    m = mn;
+    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    const uint8_t* vsrc = vt + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 32 * mt));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 16 * RS + 32 * mt));
+      const bf16x8_t vf = __builtin_bit_cast(
+          bf16x8_t, make_uint4(__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
+                               __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y));
+      f32x4_t acc = o[mt];
+      acc[0] *= alpha;
+      acc[1] *= alpha;
+      acc[2] *= alpha;
+      acc[3] *= alpha;
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc, 0, 0, 0);
     }
   };
 
   if (ntiles > 0) {
-    stage(0);
-    commit(0);
+    // the ring is static: tile t + kDepth is always staged (tiles past the end read
+    // clamped addresses and are zeroed), so every wait is a known partial count
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) stage(u, kst[u], vst[u]);
+    commit(0, kst[0], vst[0]);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      if (t + 1 < ntiles) stage(t + 1);
-      compute(t, t & 1);
-      if (t + 1 < ntiles) commit((t + 1) & 1);
-      __syncthreads();
+    for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int t = t0 + u;
+        stage(t + kDepth, kst[u], vst[u]);                 // slot of tile t, already committed
+        if (t < ntiles) compute(t, t & 1);
+        commit((t + 1) & 1, kst[(u + 1) % kDepth], vst[(u + 1) % kDepth]);
+        __syncthreads();
+      }
     }
   }
 
+  float l = lsum;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const int row = row0 + q0 + tok;
+  const int hq = g * G + r_row % G;
+  const float inv = l > 0.f ? a.v_scale / l : 0.f;
+  uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float l = lsum[nb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (!row_ok[nb]) continue;
-    const int r = 32 * w + 16 * nb + hl;
-    const int row = row0 + q0 + tok_of[nb];
-    const int hq = g * G + r % G;
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
-    uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t lo = pack_bf16x2_rne(o[nb][mt][0] * inv, o[nb][mt][1] * inv);
-      const uint32_t hi = pack_bf16x2_rne(o[nb][mt][2] * inv, o[nb][mt][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * mt) = make_uint2(lo, hi);
-    }
-    if (a.lse_out && grp == 0)
-      a.lse_out[int64_t(row) * Hq + hq] = l > 0.f ? (m[nb] + log2f(l)) * kLn2 : -INFINITY;
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
+    const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
+    *reinterpret_cast<uint2*>(orow + 16 * mt) = make_uint2(lo, hi);
   }
+  if (a.lse_out && grp == 0) a.lse_out[int64_t(row) * Hq + hq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <int CDT, int D, int BS>
-__global__ void __launch_bounds__(256) varlen_kernel(VarlenArgs a) {
+__global__ void __launch_bounds__(kThreads) varlen_kernel(VarlenArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<CDT, D>::kBytes];
   const int4 it = a.work[blockIdx.x];
   const int s = it.x;
@@ -328,7 +373,7 @@ __global__ void __launch_bounds__(256) varlen_kernel(VarlenArgs a) {
   const int qs = a.cu_q[s + 1] - row0;
   if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q) return;   // malformed offsets: skip
   if (kind == kKindDecode) {
-    if (h * 4 >= a.num_kv_heads) return;
+    if (h >= a.num_kv_heads) return;
     run_decode_item<CDT, D, BS>(a, smem, s, h, max(0, min(it.w, a.len_clamp)));
   } else {
     if (h >= a.num_kv_heads || it.z < 0 || it.z >= qs) return;
@@ -378,7 +423,7 @@ extern "C" int pkv_build_varlen_work(int32_t num_seqs, const int32_t* q_lens, co
     if (q < 0 || L < 0 || q > L) return fail(PKV_ERR_INVALID, "build_varlen_work: sequence %d q_len %d seq_len %d", s, q, L);
     if (q == 0) continue;
     if (q == 1) {
-      for (int32_t hg = 0; hg * 4 < num_kv_heads; ++hg) v.push_back({s, (kKindDecode << 24) | hg, 0, L, 0});
+      for (int32_t g = 0; g < num_kv_heads; ++g) v.push_back({s, (kKindDecode << 24) | g, 0, L, 0});
       continue;
     }
     for (int32_t q0 = 0; q0 < q; q0 += QB) {
@@ -433,6 +478,7 @@ extern "C" int pkv_paged_attention_prefill_varlen(void* out, const void* q, int3
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return fail(PKV_ERR_INVALID, "prefill_varlen: scales must be > 0");
   if (num_work == 0 || num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "prefill_varlen: the cache has no blocks");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seqlens_q || !work_items)
     return fail(PKV_ERR_INVALID, "prefill_varlen: NULL pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(work_items))
@@ -457,7 +503,7 @@ extern "C" int pkv_paged_attention_prefill_varlen(void* out, const void* q, int3
   a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
   a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
   a.v_scale = v_scale;
-  hipLaunchKernelGGL(fn, dim3(num_work), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(fn, dim3(num_work), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_varlen: launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
