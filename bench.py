@@ -37,7 +37,11 @@ def parse_args():
     ap.add_argument("--workload", default="cfg3", choices=["cfg3", "cfg4"])
     ap.add_argument("--no-mixed", action="store_true",
                     help="skip the mixed prefill+decode step (48 decode rows + 4 chunks of 512) sub-measurement")
-    ap.add_argument("--partition", type=int, default=None, help="split-context partition (tokens); 0 = none")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-context partition (tokens; 0 = none) of the fixed-partition decode; the smallest "
+                         "piece of the balanced split")
+    ap.add_argument("--decode", default="split", choices=["split", "partition"],
+                    help="balanced split over resident workgroup slots (default) or fixed context partitions")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
@@ -216,7 +220,7 @@ def mixed_step(steps: int, warmup: int):
             "mfma_TFLOPs": round(flops / t_a / 1e12, 1), "mfma_frac": round(flops / t_a / 1e12 / 2500.0, 4)}
 
 
-def measured_traffic(partition: int, workload: str):
+def measured_traffic(partition: int, workload: str, decode: str):
     """HBM bytes per partition-pass launch from the committed rocprofv3 counter record,
     valid only while the profiled kernel source is unchanged (else None)."""
     import hashlib
@@ -228,7 +232,7 @@ def measured_traffic(partition: int, workload: str):
     src = os.path.join(here, r["source"])
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != r["source_sha256"]:
         return None
-    if r.get("partition_size", 512) != partition:
+    if r.get("partition_size", 512) != partition or r.get("decode", "partition") != decode:
         return None
     return int(r["traffic_bytes"])
 
@@ -292,11 +296,16 @@ def setup_device(w, partition):
     msl = int(w.seq_lens.max())
     work = torch.from_numpy(pkv.build_decode_work(w.seq_lens, partition)).cuda()
     ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, Hq, d, msl, partition)
+    # balanced split: the plan for the slots that fill this device
+    cdt = pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16
+    split = pkv.build_decode_split(w.seq_lens, pkv.decode_split_slots(cdt, Hkv, d, w.block_size), partition)
+    ws_bytes = max(ws_bytes, pkv.decode_split_workspace_bytes(w.num_seqs, Hq, d, split.max_pieces))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     return dict(pool=pool, k_cache=k_cache, v_cache=v_cache, new_k=new_k, new_v=new_v, q=q,
                 out=torch.empty_like(q), slots=torch.from_numpy(slots).cuda(), bt=torch.from_numpy(bt).cuda(),
-                lens=torch.from_numpy(w.seq_lens.astype(np.int32)).cuda(), ws=ws, max_seq_len=msl, work=work)
+                lens=torch.from_numpy(w.seq_lens.astype(np.int32)).cuda(), ws=ws, max_seq_len=msl, work=work,
+                split=split, plan=torch.from_numpy(split.plan).cuda())
 
 
 def cpu_baseline(w, budget_s: float):
@@ -375,16 +384,19 @@ def main():
     stream = torch.cuda.current_stream()
     scale = w.softmax_scale
 
-    def step(mid_event=None):
-        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size)
-        if mid_event is not None:
-            mid_event[0].record(stream)
-        pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
-                                   w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, 1.0, 1.0, P, dev["ws"],
-                                   work=dev["work"])
+    def decode():
+        if args.decode == "split":
+            pkv.paged_attention_decode_split(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"],
+                                             dev["lens"], dev["plan"], dev["split"], w.num_kv_heads, w.block_size,
+                                             dev["max_seq_len"], scale, 1.0, 1.0, dev["ws"])
+        else:
+            pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
+                                       w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, 1.0, 1.0, P,
+                                       dev["ws"], work=dev["work"])
 
     for _ in range(args.warmup):
-        step()
+        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size)
+        decode()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -400,9 +412,7 @@ def main():
         pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size)
         e1.record(stream)
         pkv.decode_set_profile_event(e2)
-        pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
-                                   w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, 1.0, 1.0, P, dev["ws"],
-                                   work=dev["work"])
+        decode()
         pkv.decode_set_profile_event(None)
         e3.record(stream)
     torch.cuda.synchronize()
@@ -435,7 +445,9 @@ def main():
                                f"{w.name}: {w.num_seqs} decode rows, context U[32k,128k]",
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_tokens": int(w.seq_lens.sum()),
-                   "partition_size": P, "num_blocks": w.num_blocks},
+                   "partition_size": P, "num_blocks": w.num_blocks, "decode": args.decode,
+                   **({"split_slots": dev["split"].num_slots, "split_tiles_per_slot": dev["split"].tiles_per_slot}
+                      if args.decode == "split" else {})},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
@@ -444,7 +456,7 @@ def main():
                       "decode_merge": round(float(t_merge.mean()) * 1e6, 2),
                       "step_events": round(float(t_step.mean()) * 1e6, 2)},
         "roofline": {"bound": "hbm", "achieved": round(part_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(part_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(P, args.workload),
+                     "frac": round(part_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(P, args.workload, args.decode),
                      "kernel": "decode partition pass", "algorithmic_bytes": dbytes},
         "cpu_baseline": None,
     }

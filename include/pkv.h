@@ -176,6 +176,57 @@ int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const 
                                void* workspace, size_t workspace_bytes, float* lse_out,
                                const int32_t* work_items, int32_t num_work, void* stream);
 
+/* Balanced split plan (host) for pkv_paged_attention_decode_split. The context of each
+ * sequence is cut into 16-token tiles (the last one partial) and the tiles of all
+ * sequences are laid end to end; slot j of the launch streams tiles [j*C, (j+1)*C) with
+ * C = max(ceil(total tiles / num_slots), ceil(min_piece_tokens / 16), 1), so every slot
+ * moves the same bytes whatever the length mix. seq_lens: host int32 [num_seqs] (the
+ * values the device copy holds). plan: host int32 [capacity], capacity >=
+ * num_seqs + 1 + num_slots, receiving the tile offsets [num_seqs + 1] (offset of sequence
+ * s = tiles of sequences 0..s-1) followed by the first sequence with a tile in each slot's
+ * range [num_slots]. *tiles_per_slot = C; *max_pieces = the most slots one sequence
+ * spans (<= ceil(max_seq_len / (16 C)) + 1). INVALID on a bad argument, a short
+ * capacity or more than 2^31 - 2 tiles (nothing useful written). */
+int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t min_piece_tokens,
+                           int32_t num_slots, int32_t* plan, int32_t capacity,
+                           int32_t* tiles_per_slot, int32_t* max_pieces);
+
+/* Slots that fill the current device with resident workgroups of the balanced-split
+ * decode kernel for this cache dtype and shape (any value >= 1 is correct; this one
+ * keeps every compute unit busy for one wave of workgroups). UNSUPPORTED for shapes
+ * pkv_paged_attention_decode_split does not take; PKV_ERR_HIP if the query fails. */
+int pkv_decode_split_slots(int32_t cache_dtype, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t* slots);
+
+/* Bytes of device workspace pkv_paged_attention_decode_split needs: partial outputs and
+ * log-sum-exps of num_seqs * num_q_heads * max_pieces pieces (0 when max_pieces <= 1). */
+size_t pkv_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_pieces);
+
+/* Decode attention with a balanced split of the context over a fixed number of slots
+ * (the attention of [P17] "Step 6", as for pkv_paged_attention_decode; the split and
+ * its log-sum-exp merge are this library's scheduling, not the pages'). Arguments from
+ * `out` to `v_scale` and `lse_out`: as for pkv_paged_attention_decode, with bf16 queries
+ * and a bf16 or E4M3 cache, head_dim 64/128, block_size 16/32, at most 16 query heads per
+ * KV head. plan: device int32, the array pkv_build_decode_split returned for the same
+ * seq_lens and num_slots (tiles_per_slot and max_pieces likewise); the launch has
+ * num_slots workgroups per group of KV heads. A sequence inside one slot's range is
+ * written directly; the pieces of one spanning several slots are merged by log-sum-exp
+ * in a second kernel, which also writes zeros (log-sum-exp -inf) for sequences without
+ * context. workspace: device, >= pkv_decode_split_workspace_bytes(num_seqs,
+ * num_q_heads, head_dim, max_pieces). A plan that does not match seq_lens reads no
+ * memory out of bounds: a piece that does not fit is masked and not written. */
+int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,
+                                     const void* k_cache, const void* v_cache,
+                                     int32_t cache_dtype, const int32_t* block_tables,
+                                     const int32_t* seq_lens, int32_t table_width,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_seq_len, float scale, float k_scale,
+                                     float v_scale, const int32_t* plan, int32_t num_slots,
+                                     int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
+                                     size_t workspace_bytes, float* lse_out, void* stream);
+
 /* Varlen work list (host) for pkv_paged_attention_prefill_varlen. For each sequence s
  * with q = q_lens[s] new tokens and seq_len L = seq_lens[s] (host int32 arrays):
  * q == 1 gives one decode item per KV head; q > 1 gives one prefill item
@@ -211,9 +262,9 @@ int pkv_paged_attention_prefill_varlen(void* out, const void* q, int32_t q_dtype
                                        void* stream);
 
 /* Profiling hook (for timing the partition pass alone): while `hip_event` (a
- * hipEvent_t) is not NULL, every pkv_paged_attention_decode call made on this thread
- * records it on its stream right after the partition pass, before the merge kernel
- * (if any). NULL turns the hook off. The caller owns the event. */
+ * hipEvent_t) is not NULL, every pkv_paged_attention_decode and
+ * pkv_paged_attention_decode_split call made on this thread records it on its stream
+ * right after the partition pass, before the merge kernel (if any). NULL turns the hook off. The caller owns the event. */
 void pkv_decode_set_profile_event(void* hip_event);
 
 #ifdef __cplusplus

@@ -58,6 +58,11 @@ _SIGS = {
                                              i32, i32, f32, f32, f32, i32, vp, sz, vp, vp, i32, vp]),
     "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
     "pkv_build_varlen_work": (C.c_int, [i32, vp, vp, i32, i32, vp, i32, P_i32]),
+    "pkv_build_decode_split": (C.c_int, [i32, vp, i32, i32, vp, i32, P_i32, P_i32]),
+    "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
+    "pkv_decode_split_workspace_bytes": (sz, [i32, i32, i32, i32]),
+    "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                   i32, i32, f32, f32, f32, vp, i32, i32, i32, vp, sz, vp, vp]),
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, vp]),
 }
@@ -282,6 +287,62 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num
         _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
         k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, partition_size, _dptr(workspace), ws_bytes,
         _dptr(lse), _dptr(work), 0 if work is None else work.shape[0], _stream(stream)))
+
+
+class SplitPlan:
+    """Host result of build_decode_split: plan (int32 numpy), slots, tiles per slot, max pieces."""
+
+    def __init__(self, plan: np.ndarray, num_slots: int, tiles_per_slot: int, max_pieces: int):
+        self.plan, self.num_slots, self.tiles_per_slot, self.max_pieces = plan, num_slots, tiles_per_slot, max_pieces
+
+
+def build_decode_split(seq_lens, num_slots: int, min_piece_tokens: int = 0) -> SplitPlan:
+    """Balanced split of the 16-token tiles of all sequences over num_slots workgroup slots."""
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    cap = len(L) + 1 + int(num_slots)
+    plan = np.zeros(cap, np.int32)
+    c, mp = i32(), i32()
+    check(lib().pkv_build_decode_split(len(L), _np_ptr(L), min_piece_tokens, num_slots, _np_ptr(plan), cap,
+                                       C.byref(c), C.byref(mp)))
+    return SplitPlan(plan, int(num_slots), c.value, mp.value)
+
+
+def decode_split_slots(cache_dtype: int, num_kv_heads: int, head_dim: int, block_size: int) -> int:
+    """Workgroup slots that fill the current device for the balanced-split decode kernel."""
+    n = i32()
+    check(lib().pkv_decode_split_slots(cache_dtype, num_kv_heads, head_dim, block_size, C.byref(n)))
+    return n.value
+
+
+def decode_split_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_pieces: int) -> int:
+    return int(lib().pkv_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim, max_pieces))
+
+
+def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split: SplitPlan,
+                                 num_kv_heads: int, block_size: int, max_seq_len: int, scale: float,
+                                 k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, lse=None,
+                                 stream=None) -> None:
+    """q/out: [B][Hq][d] bf16; plan_dev: device int32 copy of split.plan."""
+    torch = _torch()
+    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, workspace, lse)
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [B][Hq][d] of one dtype")
+    B, Hq, d = q.shape
+    _check_plane(k_cache, v_cache, block_size, num_kv_heads, d)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][W]")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if plan_dev.dtype != torch.int32 or tuple(plan_dev.shape) != (B + 1 + split.num_slots,):
+        raise ValueError("plan must be int32 [B + 1 + num_slots] (from build_decode_split)")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be float32 [B][Hq]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().pkv_paged_attention_decode_split(
+        _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+        _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
+        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(plan_dev), split.num_slots,
+        split.tiles_per_slot, split.max_pieces, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
 
 
 def decode_set_profile_event(event) -> None:

@@ -25,6 +25,7 @@
 //    directly.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "pkv.h"
@@ -112,7 +113,10 @@ struct DecodeArgs {
   float v_scale;
   int group;         // query heads per KV head
   int num_seqs;
+  int num_work;      // items in `work`
   const int4* work;  // (seq, partition, partitions, end token) per item, or null: grid over all
+  const int32_t* plan;   // balanced split: tile offsets [B + 1], then first sequence per slot
+  int tiles_per_slot;    // balanced split: 16-token tiles per workgroup slot
 };
 
 // The (sequence, partition) of this workgroup and its token range; false = nothing to do.
@@ -123,7 +127,10 @@ __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int& s, int& p,
     s = it.x;
     p = it.y;
     nparts = it.z;
-    if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.pmax) return false;   // malformed item: skip
+    // malformed item (bad index, or split without a workspace): skip
+    if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.pmax || nparts < 1 || p >= nparts ||
+        (nparts > 1 && !a.ws_o))
+      return false;
     tok_end = it.w < 0 ? 0 : (it.w > a.len_clamp ? a.len_clamp : it.w);
     tok_begin = a.part_tokens > 0 ? p * a.part_tokens : 0;
     if (tok_begin > tok_end) tok_begin = tok_end;
@@ -410,9 +417,27 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   const int hq = blockIdx.x * HW + threadIdx.x / LPH;
   const int e = 4 * (threadIdx.x % LPH);
   if (hq >= num_q_heads) return;
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  int nparts;
+  if (a.plan) {
+    // balanced split: pieces = slots that the sequence's tiles touch
+    const int c0 = a.plan[s], c1 = a.plan[s + 1];
+    nparts = c1 > c0 && c0 >= 0 ? (c1 - 1) / a.tiles_per_slot - c0 / a.tiles_per_slot + 1 : 0;
+    if (nparts == 0) {                        // no context: zero output (no piece wrote it)
+      const int64_t oi = (int64_t(s) * num_q_heads + hq) * D + e;
+      if constexpr (QDT == PKV_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(0u, 0u);
+      }
+      if (a.lse_out && e == 0) a.lse_out[int64_t(s) * num_q_heads + hq] = -INFINITY;
+      return;
+    }
+    nparts = nparts < a.pmax ? nparts : a.pmax;
+  } else {
+    int L = a.seq_lens[s];
+    L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+    nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  }
   if (nparts <= 1) return;                    // written directly by the partition pass
   const int64_t base = (int64_t(s) * num_q_heads + hq) * a.pmax;
   // pass 1: the maximum log-sum-exp; pass 2: independent weighted loads (unrolled)
@@ -532,6 +557,289 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Balanced split decode (bf16 queries; bf16 or E4M3 cache). The context of every
+// sequence is cut into 16-token tiles and the tiles of all sequences are laid end to
+// end; workgroup slot j streams global tiles [j*C, (j+1)*C), so every slot moves the
+// same number of bytes and all finish together, whatever the length mix. The part of
+// one sequence inside a slot's range is a piece: a sequence held by one slot is written
+// directly, the pieces of a longer one go to the workspace (piece index = slot - first
+// slot of the sequence) for the log-sum-exp merge. One wave per KV head (8 heads per
+// workgroup stream whole token rows together); the load pipeline runs across piece
+// boundaries (the next piece's queries and first tile are in flight while the last
+// tile of the current one is consumed). Per-tile work is that of decode_wave.
+// ---------------------------------------------------------------------------------
+template <int CDT, int D, int BS, int HPW>
+__global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
+  constexpr int NV = (D / 4) * EB / 16;
+  constexpr int SUB = BS / 16;
+  constexpr int RS = D * 2 + 32;
+  typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = blockIdx.x * HPW + w;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * G;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int hl_q = hl < G ? hl : hl % G;
+  const int slot = blockIdx.y;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache);
+  const int64_t row_bytes = int64_t(Hkv) * D * EB;
+  const int64_t lane_off = int64_t(g) * D * EB + 16 * grp;
+
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[HPW][16 * RS];
+  uint8_t* my_vt = vt_lds[w];
+
+  // ---- issue cursor: the piece whose tiles are being loaded. Slot j owns global tiles
+  // [j*C, (j+1)*C) of the sequences' tiles laid end to end; a piece is the part of
+  // one sequence inside that range.
+  const int B = a.num_seqs;
+  const cptr_i32 plan = (cptr_i32)(uintptr_t)(a.plan);
+  const int C = a.tiles_per_slot;
+  const int total = plan[B];
+  const int64_t lo64 = int64_t(slot) * C;
+  int t = lo64 < total ? int(lo64) : total;                      // global tile cursor
+  const int hi = lo64 + C < total ? int(lo64 + C) : total;
+  int cs = plan[B + 1 + slot];                                   // current sequence
+  cs = cs < 0 ? 0 : (cs > B ? B : cs);
+  int cu_cur = plan[cs];
+  int cu_next = cs < B ? plan[cs + 1] : 0x7fffffff;
+  int iord = 0;                              // ordinal of the piece being issued
+  int i_s = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
+  bool i_valid = false;
+  cptr_i32 i_bt = nullptr;
+  // Queries: a piece's rows are loaded into qtmp when the piece is entered and moved
+  // into stage (ordinal & 1) at the start of the next issue, by which time only the
+  // loads issued after them (one tile) are still in flight. Two stages suffice: the
+  // piece two ordinals back has been fully consumed by then.
+  // (two named arrays, not one indexed array: a runtime index would put them in scratch)
+  uint4 qtmp[KS];
+  bf16x8_t qs0[KS], qs1[KS];
+  bool q_pending = false;
+
+  // enters the piece that starts at tile t and loads its queries; false when none is left
+  auto enter = [&]() -> bool {
+    if (t >= hi) return false;
+    while (cs < B && cu_next <= t) {          // skip finished and empty sequences
+      ++cs;
+      cu_cur = cu_next;
+      cu_next = cs < B ? plan[cs + 1] : 0x7fffffff;
+    }
+    if (cs >= B) return false;
+    const int pe = hi < cu_next ? hi : cu_next;
+    const int tb = t - cu_cur;               // first tile of the piece within the sequence
+    const int nt = pe - t;
+    t = pe;
+    int L = a.seq_lens[cs];
+    L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+    const int first = cu_cur / C;
+    const int np = (cu_next - 1) / C - first + 1;
+    const int p = slot - first;
+    // a piece of an inconsistent plan is streamed masked and not written
+    const bool valid = tb >= 0 && cu_cur >= 0 && p >= 0 && p < np && (np == 1 || (a.ws_o != nullptr && p < a.pmax));
+    i_s = cs;
+    i_p = p;
+    i_np = np;
+    i_valid = valid;
+    i_t0 = valid ? tb : 0;
+    i_te = valid ? min(16 * (tb + nt), L) : 0;
+    i_nt = nt;
+    i_n = 0;
+    i_bt = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(cs) * a.table_width);
+    // lanes past the group read a duplicate head of it: their columns are never written
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(cs) * Hq + int64_t(g) * G + hl_q) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int d0 = EB == 2 ? 32 * kk + 8 * grp : 64 * (kk / 2) + 16 * grp + 8 * (kk % 2);
+      qtmp[kk] = *reinterpret_cast<const uint4*>(qrow + d0);
+    }
+    q_pending = true;
+    return true;
+  };
+
+  // per-slot tile state (two slots: the tile being consumed and the one in flight)
+  uint4 kb[2][NV], vb[2][NV];
+  int sl_t0[2], sl_s[2], sl_p[2], sl_np[2], sl_te[2];
+  bool sl_ok[2], sl_first[2], sl_last[2], sl_par[2], sl_valid[2];
+
+  bool more = enter();
+  // issue the next tile of the stream into slot k; false when the stream is exhausted
+  auto issue = [&](int k, uint4 (&kr)[NV], uint4 (&vr)[NV]) -> bool {
+    if (q_pending) {
+      q_pending = false;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (iord & 1) qs1[kk] = __builtin_bit_cast(bf16x8_t, qtmp[kk]);
+        else qs0[kk] = __builtin_bit_cast(bf16x8_t, qtmp[kk]);
+      }
+    }
+    // Every call issues the same loads (row 0 of block 0 once the stream is exhausted),
+    // so each consume waits on a fixed count and never drains the tile behind it.
+    const bool live = more;
+    const int ti = i_t0 + i_n;               // tile within the sequence
+    const int tok_lo = 16 * ti;
+    const bool any = live && tok_lo < i_te;
+    const int blk = any ? i_bt[ti / SUB] : -1;
+    const bool ok = any && blk >= 0 && blk < a.num_blocks;
+    const int64_t off = (int64_t(ok ? blk : 0) * BS + (ti % SUB) * 16 + hl) * row_bytes + lane_off;
+    sl_t0[k] = tok_lo;
+    sl_ok[k] = ok;
+    sl_s[k] = i_s;
+    sl_p[k] = i_p;
+    sl_np[k] = i_np;
+    sl_te[k] = i_te;
+    sl_valid[k] = live && i_valid;
+    sl_first[k] = live && i_n == 0;
+    sl_last[k] = live && i_n == i_nt - 1;
+    sl_par[k] = iord & 1;
+    // the next piece's queries go out before this tile's rows
+    if (live && ++i_n == i_nt) {
+      ++iord;
+      more = enter();
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      kr[i] = *reinterpret_cast<const uint4*>(kc + off + 64 * i);
+      vr[i] = *reinterpret_cast<const uint4*>(vc + off + 64 * i);
+    }
+    return live;
+  };
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4_t o[MT];
+
+  auto consume = [&](int k, const uint4 (&kr)[NV], const uint4 (&vr)[NV]) {
+    bf16x8_t qf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = sl_par[k] ? qs1[kk] : qs0[kk];
+    if (sl_first[k]) {
+      m = -INFINITY;
+      lsum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int t0 = sl_t0[k];
+    const int tok_end = sl_te[k];
+    const bool ok = sl_ok[k];
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (CDT == PKV_BF16) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[kk]), qf[kk], sc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const uint4 lo = pkv::fp8x8_to_bf16x8(kr[i].x, kr[i].y);
+        const uint4 hi = pkv::fp8x8_to_bf16x8(kr[i].z, kr[i].w);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qf[2 * i], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qf[2 * i + 1], sc, 0, 0, 0);
+      }
+    }
+    {
+      // Rows past the end are zeroed by masking, not by a branch: every lane waits for
+      // its rows on the main path, so no later wait is made conservative by a skipped one.
+      const uint32_t keep = (ok && (t0 + hl < tok_end)) ? 0xffffffffu : 0u;
+      uint8_t* dst = my_vt + hl * RS;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        uint4 v = vr[i];
+        asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+        v.x &= keep;
+        v.y &= keep;
+        v.z &= keep;
+        v.w &= keep;
+        if constexpr (CDT == PKV_BF16) {
+          *reinterpret_cast<uint4*>(dst + 2 * (32 * i + 8 * grp)) = v;
+        } else {
+          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp)) = pkv::fp8x8_to_bf16x8(v.x, v.y);
+          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp) + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+        }
+      }
+    }
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * grp + r;
+      z[r] = (ok && t < tok_end) ? sc[r] * a.zscale : -INFINITY;
+    }
+    float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
+    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
+    const float mn = fmaxf(m, mt_);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = pkv::fast_exp2(m - mref);
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = pkv::fast_exp2(z[r] - mref);
+    const uint32_t p01 = pack_bf16x2_rne(pr[0], pr[1]);
+    const uint32_t p23 = pack_bf16x2_rne(pr[2], pr[3]);
+    lsum = lsum * alpha + (pkv::bf16_lo(p01) + pkv::bf16_hi(p01)) + (pkv::bf16_lo(p23) + pkv::bf16_hi(p23));
+    m = mn;
+    const pkv::s16x4_t pf = __builtin_bit_cast(pkv::s16x4_t, make_uint2(p01, p23));
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* src = my_vt + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const pkv::s16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pkv::lds_s16x4_t*)(src + 32 * mt));
+      f32x4_t acc = o[mt];
+      acc[0] *= alpha;
+      acc[1] *= alpha;
+      acc[2] *= alpha;
+      acc[3] *= alpha;
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (!sl_last[k]) return;
+    // ---- the item's last tile: write its output (or partition partial)
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!sl_valid[k] || hl >= G) return;
+    const int s = sl_s[k];
+    const int hq = g * G + hl;
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
+    if (sl_np[k] == 1) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(s) * Hq + hq) * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
+        const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
+        pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
+      }
+      if (a.lse_out && grp == 0)
+        pkv::store_b32_untracked(a.lse_out + int64_t(s) * Hq + hq, __float_as_uint(lse2 * kLn2));
+    } else {
+      const int64_t pi = (int64_t(s) * Hq + hq) * a.pmax + sl_p[k];
+      float* orow = a.ws_o + pi * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        pkv::store_b128_untracked(orow + 16 * mt, o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv, o[mt][3] * inv);
+      if (grp == 0) pkv::store_b32_untracked(a.ws_lse + pi, __float_as_uint(lse2));
+    }
+  };
+
+  if (!more) return;
+  // One exit, at the bottom: a tile issued after the stream ran out is masked to nothing
+  // (no row is valid, so it changes neither the running sums nor the outputs). An exit
+  // between the two halves would join the loop's back edge in the control-flow graph
+  // with a slot still in flight, and every wait at the top would become a full drain.
+  bool live = issue(0, kb[0], vb[0]);
+  do {
+    issue(1, kb[1], vb[1]);
+    consume(0, kb[0], vb[0]);
+    live = issue(0, kb[0], vb[0]);
+    consume(1, kb[1], vb[1]);
+  } while (live);
+}
+
 constexpr int kWaves = 4;
 
 thread_local hipEvent_t g_profile_event = nullptr;
@@ -584,6 +892,47 @@ DecodeFn pick_mfma(int D, int BS) {
     case 128: return pick_mfma_bs<CDT, 128, HPW>(BS);
     default: return nullptr;
   }
+}
+
+template <int CDT, int D, int HPW>
+DecodeFn pick_split_bs(int BS) {
+  switch (BS) {
+    case 16: return decode_split_kernel<CDT, D, 16, HPW>;
+    case 32: return decode_split_kernel<CDT, D, 32, HPW>;
+    default: return nullptr;
+  }
+}
+
+template <int CDT, int HPW>
+DecodeFn pick_split(int D, int BS) {
+  switch (D) {
+    case 64: return pick_split_bs<CDT, 64, HPW>(BS);
+    case 128: return pick_split_bs<CDT, 128, HPW>(BS);
+    default: return nullptr;
+  }
+}
+
+template <int CDT>
+DecodeFn pick_split_hpw(int D, int BS, int hpw) {
+  switch (hpw) {
+    case 1: return pick_split<CDT, 1>(D, BS);
+    case 2: return pick_split<CDT, 2>(D, BS);
+    case 4: return pick_split<CDT, 4>(D, BS);
+    case 8: return pick_split<CDT, 8>(D, BS);
+    default: return nullptr;
+  }
+}
+
+// Resident workgroups of `fn` per CU times the CU count (cached per device and kernel).
+int resident_slots(DecodeFn fn, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0) !=
+      hipSuccess)
+    return 0;
+  return cus * (per_cu > 0 ? per_cu : 1);
 }
 
 template <int CDT>
@@ -717,6 +1066,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
     if ((reinterpret_cast<uintptr_t>(work_items) & 15) != 0)
       return fail(PKV_ERR_INVALID, "decode: work_items must be 16-byte aligned");
     a.work = reinterpret_cast<const int4*>(work_items);
+    a.num_work = num_work;
     grid = dim3(head_groups, num_work, 1);
     if (num_work > 65535 * 32) return fail(PKV_ERR_INVALID, "decode: too many work items");
   }
@@ -731,5 +1081,107 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int pkv_decode_split_slots(int32_t cache_dtype, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t* slots) {
+  using pkv::fail;
+  if (!slots || num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "decode_split_slots: bad arguments");
+  const int hpw = mfma_heads_per_wg(num_kv_heads);
+  DecodeFn fn = cache_dtype == PKV_BF16       ? pick_split_hpw<PKV_BF16>(head_dim, block_size, hpw)
+                : cache_dtype == PKV_FP8_E4M3 ? pick_split_hpw<PKV_FP8_E4M3>(head_dim, block_size, hpw)
+                                              : nullptr;
+  if (!fn)
+    return fail(PKV_ERR_UNSUPPORTED, "decode_split_slots: unsupported (cache dtype %d, head_dim %d, block_size %d)",
+                cache_dtype, head_dim, block_size);
+  const int resident = resident_slots(fn, hpw * 64);
+  if (resident <= 0) return fail(PKV_ERR_HIP, "decode_split_slots: occupancy query failed");
+  *slots = std::max(1, resident / (num_kv_heads / hpw));
+  return PKV_OK;
+}
+
+extern "C" size_t pkv_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                                   int32_t max_pieces) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_pieces <= 1) return 0;
+  return size_t(num_seqs) * num_q_heads * max_pieces * (head_dim + 1) * sizeof(float);
+}
+
+extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                                const void* v_cache, int32_t cache_dtype,
+                                                const int32_t* block_tables, const int32_t* seq_lens,
+                                                int32_t table_width, int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale,
+                                                float v_scale, const int32_t* plan, int32_t num_slots,
+                                                int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
+                                                size_t workspace_bytes, float* lse_out, void* stream) {
+  using pkv::fail;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
+      max_seq_len < 0)
+    return fail(PKV_ERR_INVALID, "decode_split: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "decode_split: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (num_seqs > 65535) return fail(PKV_ERR_INVALID, "decode_split: at most 65535 sequences per launch");
+  const int G = num_q_heads / num_kv_heads;
+  if (q_dtype != PKV_BF16 || G > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "decode_split: needs bf16 queries and at most 16 query heads per KV head");
+  const int hpw = mfma_heads_per_wg(num_kv_heads);
+  DecodeFn fn = cache_dtype == PKV_BF16       ? pick_split_hpw<PKV_BF16>(head_dim, block_size, hpw)
+                : cache_dtype == PKV_FP8_E4M3 ? pick_split_hpw<PKV_FP8_E4M3>(head_dim, block_size, hpw)
+                                              : nullptr;
+  if (!fn)
+    return fail(PKV_ERR_UNSUPPORTED, "decode_split: unsupported (cache dtype %d, head_dim %d, block_size %d)",
+                cache_dtype, head_dim, block_size);
+  if (num_slots < 1 || num_slots > 65535 || tiles_per_slot < 1 || max_pieces < 0 || max_pieces > kMaxPartitions)
+    return fail(PKV_ERR_INVALID, "decode_split: bad plan sizes (slots %d, tiles per slot %d, pieces %d)", num_slots,
+                tiles_per_slot, max_pieces);
+  if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(PKV_ERR_INVALID, "decode_split: scales must be > 0");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !plan)
+    return fail(PKV_ERR_INVALID, "decode_split: NULL pointer");
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "decode_split: the cache has no blocks");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID, "decode_split: q, out and cache planes must be 16-byte aligned");
+  const size_t need = pkv_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim, max_pieces);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_INVALID, "decode_split: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+
+  DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.lse_out = lse_out;
+  a.table_width = table_width;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  const int64_t tcap = int64_t(table_width) * block_size;
+  a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
+  a.pmax = need > 0 ? max_pieces : 1;
+  if (need > 0) {
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = a.ws_o + size_t(num_seqs) * num_q_heads * max_pieces * head_dim;
+  }
+  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
+  a.v_scale = v_scale;
+  a.group = G;
+  a.num_seqs = num_seqs;
+  a.plan = plan;
+  a.tiles_per_slot = tiles_per_slot;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(fn, dim3(num_kv_heads / hpw, num_slots), dim3(hpw * 64), 0, st, a);
+  if (g_profile_event) (void)hipEventRecord(g_profile_event, st);
+  // the merge also writes the zero output of sequences without context
+  MergeFn mf = pick_merge(q_dtype, head_dim);
+  const int heads_per_wg = 256 / (head_dim / 4);
+  hipLaunchKernelGGL(mf, dim3((num_q_heads + heads_per_wg - 1) / heads_per_wg, num_seqs), dim3(256), 0, st, a,
+                     num_q_heads);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_split: launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }

@@ -7,6 +7,7 @@
 // "Build a pure-Python continuous batching LLM serving engine from scratch", "Step 2"
 // (a multi-block request is all-or-nothing and fails when too few blocks are free).
 #include <algorithm>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -269,6 +270,48 @@ int pkv_build_decode_work(int32_t num_seqs, const int32_t* seq_lens, int32_t par
       o[3] = it.end;
       o += 4;
     }
+  return PKV_OK;
+}
+
+int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t min_piece_tokens, int32_t num_slots,
+                           int32_t* plan, int32_t capacity, int32_t* tiles_per_slot, int32_t* max_pieces) {
+  if (num_seqs < 0 || min_piece_tokens < 0 || num_slots < 1 || !tiles_per_slot || !max_pieces ||
+      (num_seqs > 0 && !seq_lens))
+    return fail(PKV_ERR_INVALID, "build_decode_split: bad arguments");
+  const int64_t need = int64_t(num_seqs) + 1 + num_slots;
+  if (need > capacity || !plan)
+    return fail(PKV_ERR_INVALID, "build_decode_split: plan needs %lld entries, capacity %d", (long long)need,
+                capacity);
+  // tile offsets of the sequences laid end to end (16-token tiles, the last one partial)
+  int64_t total = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t L = seq_lens[s] < 0 ? 0 : seq_lens[s];
+    total += (L + 15) / 16;
+    if (total > INT32_MAX - 1) return fail(PKV_ERR_INVALID, "build_decode_split: context too long");
+  }
+  int64_t C = (total + num_slots - 1) / num_slots;
+  C = std::max<int64_t>(C, (int64_t(min_piece_tokens) + 15) / 16);
+  C = std::max<int64_t>(C, 1);
+  int32_t* cu = plan;
+  int32_t* first_seq = plan + num_seqs + 1;
+  int64_t acc = 0;
+  int32_t pieces_max = 0;
+  int32_t s = 0;
+  cu[0] = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t L = seq_lens[i] < 0 ? 0 : seq_lens[i];
+    const int64_t nt = (L + 15) / 16;
+    if (nt > 0) pieces_max = std::max<int32_t>(pieces_max, int32_t((acc + nt - 1) / C - acc / C + 1));
+    acc += nt;
+    cu[i + 1] = int32_t(acc);
+  }
+  for (int32_t j = 0; j < num_slots; ++j) {
+    const int64_t lo = int64_t(j) * C;
+    while (s < num_seqs && cu[s + 1] <= lo) ++s;     // first sequence with a tile at or past lo
+    first_seq[j] = s;
+  }
+  *tiles_per_slot = int32_t(C);
+  *max_pieces = pieces_max;
   return PKV_OK;
 }
 

@@ -27,10 +27,36 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
-  return pkv::f32_to_bf16(a) | (pkv::f32_to_bf16(b) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Global stores issued as inline assembly, which the compiler's wait-count pass does not
+// see. In a loop that keeps loads in flight across iterations, a store the pass can see
+// leaves loads and stores outstanding together; it then cannot order them and turns the
+// next wait for a load into a full drain. Hidden stores only ever add to the hardware
+// count, so every wait the pass computes for its loads stays sufficient. Store data
+// registers may be reused right after issue on this target (the pass itself inserts no
+// wait for that), and the end of the kernel makes the writes visible.
+__device__ __forceinline__ void store_b32_untracked(void* p, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_b64_untracked(void* p, uint32_t lo, uint32_t hi) {
+  const u32x2_t v = {lo, hi};
+  asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_b128_untracked(void* p, float x, float y, float z, float w) {
+  const u32x4_t v = {__float_as_uint(x), __float_as_uint(y), __float_as_uint(z), __float_as_uint(w)};
+  asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
 
 // Input of one wave's streaming pass over the context of one (sequence, KV head).
 struct DecodeWaveIn {

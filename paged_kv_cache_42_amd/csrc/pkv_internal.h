@@ -24,9 +24,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN, quiet).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN (quieted)
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // OCP E4M3 code (low 8 bits of c) -> float, exact. Relies on fp32 denormals being

@@ -203,6 +203,29 @@ def run_decode(st: Step, partition_size: Optional[int] = None, lse: bool = True,
     return out, lse_t
 
 
+def run_decode_split(st: Step, num_slots: Optional[int] = None, min_piece_tokens: int = 0, lse: bool = True,
+                     max_seq_len=None, plan_lens=None, q=None):
+    """The balanced-split decode launch; outputs start as NaN so an unwritten row shows.
+    q: decode queries [B][Hq][d] (default: the step's rows, one per sequence)."""
+    w = st.w
+    B, Hq, d = w.num_seqs, w.num_q_heads, w.head_dim
+    msl = int(w.seq_lens.max()) if max_seq_len is None else max_seq_len
+    if num_slots is None:
+        num_slots = pkv.decode_split_slots(pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16, w.num_kv_heads, d,
+                                           w.block_size)
+    split = pkv.build_decode_split(w.seq_lens if plan_lens is None else plan_lens, num_slots, min_piece_tokens)
+    plan_d = torch.from_numpy(split.plan).cuda()
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch_dtype(w.dtype), device="cuda")
+    nb = pkv.decode_split_workspace_bytes(B, Hq, d, split.max_pieces)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+    lse_t = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    pkv.paged_attention_decode_split(out, st.q if q is None else q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, plan_d, split,
+                                     w.num_kv_heads, w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale,
+                                     ws, lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t, split
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what=""):
     if dtype == "f32":
         err = np.abs(got - ref)

@@ -166,3 +166,50 @@ def test_decode_work_list_covers_every_partition_once(lens, P):
                                                        ctypes.byref(n)))
         else:
             raise pkv.PkvError(-1, "empty")
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.lists(st.integers(0, 3000), max_size=30), st.integers(1, 300), st.sampled_from([0, 16, 100, 512]))
+def test_balanced_split_plan_covers_every_tile_once(lens, slots, min_piece):
+    sp = pkv.build_decode_split(lens, slots, min_piece)
+    B = len(lens)
+    cu, first = sp.plan[:B + 1], sp.plan[B + 1:]
+    tiles = [-(-L // 16) for L in lens]
+    assert cu.tolist() == np.concatenate([[0], np.cumsum(tiles, dtype=np.int64)]).astype(np.int64).tolist()
+    total = int(cu[-1])
+    C = sp.tiles_per_slot
+    assert C >= max(1, -(-min_piece // 16)) and C >= -(-total // slots)
+    assert C == max(1, -(-min_piece // 16), -(-total // slots))
+    # walk the slots as the kernel does; every tile of every sequence lands in exactly one piece
+    seen = [np.zeros(t, np.int32) for t in tiles]
+    pieces = [0] * B
+    for j in range(slots):
+        lo, hi = min(j * C, total), min((j + 1) * C, total)
+        s = int(first[j])
+        assert all(cu[i + 1] <= lo for i in range(s)) and (s == B or cu[s + 1] > lo or lo >= total)
+        t = lo
+        while t < hi:
+            while s < B and cu[s + 1] <= t:
+                s += 1
+            pe = min(hi, int(cu[s + 1]))
+            seen[s][t - cu[s]:pe - cu[s]] += 1
+            pieces[s] += 1
+            assert j - int(cu[s]) // C == pieces[s] - 1            # piece index = slot - first slot
+            t = pe
+    assert all((x == 1).all() for x in seen)
+    assert sp.max_pieces == max([p for p in pieces] + [0])
+    for s, p in enumerate(pieces):
+        if tiles[s]:
+            assert p == (int(cu[s + 1]) - 1) // C - int(cu[s]) // C + 1
+
+
+def test_balanced_split_plan_errors():
+    with pytest.raises(pkv.PkvError):
+        pkv.build_decode_split([10, 20], 0)
+    out = np.zeros(3, np.int32)
+    c, m = ctypes.c_int32(), ctypes.c_int32()
+    L = np.array([10, 20], np.int32)
+    with pytest.raises(pkv.PkvError):     # capacity below num_seqs + 1 + num_slots
+        _lib.check(pkv.lib().pkv_build_decode_split(2, L.ctypes.data_as(ctypes.c_void_p), 0, 4,
+                                                    out.ctypes.data_as(ctypes.c_void_p), 3, ctypes.byref(c),
+                                                    ctypes.byref(m)))

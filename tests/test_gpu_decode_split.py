@@ -1,0 +1,134 @@
+"""Balanced-split decode on the GPU vs the oracle (element by element): every slot count
+from one workgroup to more slots than tiles, empty sequences, the full-size decode
+batches (sampled), and a plan built for longer contexts than the device lengths."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_42_amd as pkv
+import workloads
+
+from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_decode_sampled, oracle_planes,
+                       out_f64, run_decode, run_decode_split)
+
+pytestmark = pytest.mark.gpu
+
+# log-sum-exp tolerance of the bf16 paths: the P.V weights are rounded to bf16 (relative
+# error <= 2^-9 each) and the same rounded weights are summed, so ln(sum) may move by
+# up to 2^-9; allow 2^-8 (as for the partitioned decode).
+LSE_ATOL = 2.0 ** -8
+
+
+def _tol(w):
+    return "fp8" if w.cache_dtype == "fp8" else "bf16"
+
+
+def _decode_batch(w, st, ref, ref_lse):
+    """Decode queries and oracle rows for a batch where sequences of length 0 have no
+    new row: their query is zeros, their expected output zeros and log-sum-exp -inf."""
+    B, Hq, d = w.num_seqs, w.num_q_heads, w.head_dim
+    live = np.asarray(w.seq_lens) > 0
+    q = torch.zeros((B, Hq, d), dtype=st.q.dtype, device="cuda")
+    q[torch.from_numpy(live).cuda()] = st.q
+    r = np.zeros((B, Hq, d))
+    rl = np.full((B, Hq), -np.inf)
+    r[live] = ref
+    rl[live] = ref_lse
+    return q, r, rl
+
+
+def _check(w, st, q, ref, ref_lse, slots, min_piece=0):
+    out, lse, split = run_decode_split(st, num_slots=slots, min_piece_tokens=min_piece, q=q)
+    what = f"{w.name} slots={slots} min_piece={min_piece} C={split.tiles_per_slot}"
+    got = out_f64(out)
+    assert not np.isnan(got).any(), f"{what}: unwritten output"
+    assert_close(got, ref, _tol(w), what)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert (np.isneginf(got_lse) == ~fin).all(), what
+    np.testing.assert_allclose(got_lse[fin], ref_lse[fin], rtol=1e-6, atol=LSE_ATOL, err_msg=what)
+
+
+CASES = []
+for cdt in ("bf16", "fp8"):
+    for d in (64, 128):
+        for G in (1, 3, 4, 8, 16):
+            for bs in (16, 32):
+                CASES.append((cdt, d, G, bs))
+
+
+@pytest.mark.parametrize("cdt,d,G,bs", CASES, ids=[f"{a}-d{b}-g{c}-bs{e}" for a, b, c, e in CASES])
+def test_small_split_all_variants_and_slot_counts(cdt, d, G, bs):
+    seed = zlib.crc32(f"split{cdt}{d}{G}{bs}".encode()) % 10_000
+    lens = [1, bs - 1, 0, bs, bs + 1, 3 * bs + 5, 200, 0, 77, 1000]
+    Hkv = 2 if G != 3 else 4
+    w = workloads.small_varlen(seed, lens, [min(1, x) for x in lens], num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                               head_dim=d, block_size=bs, dtype="bf16", cache_dtype=cdt)
+    if cdt == "fp8":
+        w.k_scale, w.v_scale = 0.25, 0.5
+    st = build_step(w)
+    tabs, bt, cu, slots, kp, vp = oracle_planes(st)
+    q, ref, ref_lse = _decode_batch(w, st, *oracle_attention_full(st, kp, vp, bt, cu))
+    for n in (1, 2, 3, 7, 64, None, 5000):
+        _check(w, st, q, ref, ref_lse, n)
+    _check(w, st, q, ref, ref_lse, 7, min_piece=64)
+
+
+def test_all_sequences_empty():
+    w = workloads.small_varlen(3, [0, 0, 0], [0, 0, 0], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                               block_size=16, dtype="bf16")
+    st = build_step(w)
+    q = torch.zeros((3, 8, 64), dtype=torch.bfloat16, device="cuda")
+    out, lse, split = run_decode_split(st, num_slots=4, max_seq_len=16, q=q)
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_plan_for_longer_contexts_still_covers_every_token():
+    # the plan only has to cover the device lengths: tiles past them are masked
+    w = workloads.small_decode(11, [40, 300, 17, 5], num_q_heads=16, num_kv_heads=4, head_dim=128,
+                               block_size=16, dtype="bf16")
+    st = build_step(w, width=w.max_blocks_per_seq() + 8)
+    tabs, bt, cu, slots, kp, vp = oracle_planes(st)
+    ref, ref_lse = oracle_attention_full(st, kp, vp, bt, cu)
+    longer = np.asarray(w.seq_lens) + np.array([100, 20, 0, 64])
+    out, lse, split = run_decode_split(st, num_slots=5, plan_lens=longer,
+                                       max_seq_len=int(w.seq_lens.max()))
+    assert_close(out_f64(out), ref, "bf16", "longer plan")
+
+
+def test_split_close_to_unsplit_partitioned_decode():
+    w = workloads.small_decode(10, [3000, 129, 4097, 1, 700], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                               block_size=16, dtype="bf16")
+    st = build_step(w)
+    o0, l0 = run_decode(st, partition_size=0)
+    for n in (1, 5, 40, None):
+        o, l, _ = run_decode_split(st, num_slots=n)
+        assert np.abs(out_f64(o) - out_f64(o0)).max() <= 2 ** -8
+        np.testing.assert_allclose(l.cpu().numpy(), l0.cpu().numpy(), rtol=0, atol=2 * LSE_ATOL)
+
+
+def _sampled(w, n_samples):
+    st = build_step(w, fill_nan=False)
+    rng = np.random.default_rng(w.seed)
+    order = np.argsort(w.seq_lens)
+    seqs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    seqs += rng.choice(w.num_seqs, size=min(n_samples, w.num_seqs), replace=False).tolist()
+    pairs = sorted(set((int(s), int(rng.integers(w.num_kv_heads))) for s in seqs))
+    out, lse, split = run_decode_split(st)
+    o = out_f64(out)
+    assert np.isfinite(o).all()
+    l = lse.cpu().numpy()
+    G = w.group
+    for (s, g), (ro, rl) in oracle_decode_sampled(w, pairs).items():
+        assert_close(o[s, g * G:(g + 1) * G], ro, w.dtype, f"{w.name} seq {s} head {g} (L={w.seq_lens[s]})")
+        np.testing.assert_allclose(l[s, g * G:(g + 1) * G], rl, rtol=0, atol=LSE_ATOL)
+
+
+def test_config3_full_size_sampled_split():
+    _sampled(workloads.config3(), 24)
+
+
+def test_config4_full_size_sampled_split():
+    _sampled(workloads.config4(), 5)
