@@ -558,6 +558,10 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
 }
 
 // ---------------------------------------------------------------------------------
+// Tiles in each wave's load ring of the balanced-split kernel: while one is consumed,
+// NS - 1 are in flight.
+constexpr int kSplitRing = 2;
+
 // Balanced split decode (bf16 queries; bf16 or E4M3 cache). The context of every
 // sequence is cut into 16-token tiles and the tiles of all sequences are laid end to
 // end; workgroup slot j streams global tiles [j*C, (j+1)*C), so every slot moves the
@@ -569,7 +573,7 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
 // boundaries (the next piece's queries and first tile are in flight while the last
 // tile of the current one is consumed). Per-tile work is that of decode_wave.
 // ---------------------------------------------------------------------------------
-template <int CDT, int D, int BS, int HPW>
+template <int CDT, int D, int BS, int HPW, int NS = kSplitRing>
 __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
@@ -602,6 +606,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   // one sequence inside that range.
   const int B = a.num_seqs;
   const cptr_i32 plan = (cptr_i32)(uintptr_t)(a.plan);
+  const cptr_i32 lens = (cptr_i32)(uintptr_t)(a.seq_lens);
   const int C = a.tiles_per_slot;
   const int total = plan[B];
   const int64_t lo64 = int64_t(slot) * C;
@@ -611,17 +616,18 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   cs = cs < 0 ? 0 : (cs > B ? B : cs);
   int cu_cur = plan[cs];
   int cu_next = cs < B ? plan[cs + 1] : 0x7fffffff;
-  int iord = 0;                              // ordinal of the piece being issued
   int i_s = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
   bool i_valid = false;
   cptr_i32 i_bt = nullptr;
   // Queries: a piece's rows are loaded into qtmp when the piece is entered and moved
-  // into stage (ordinal & 1) at the start of the next issue, by which time only the
-  // loads issued after them (one tile) are still in flight. Two stages suffice: the
-  // piece two ordinals back has been fully consumed by then.
-  // (two named arrays, not one indexed array: a runtime index would put them in scratch)
+  // into stage (ordinal mod NS) at the start of the next issue, by which time only the
+  // loads issued after them (one tile) are still in flight. NS stages suffice: the piece
+  // NS ordinals back has been fully consumed by then (at most NS - 1 tiles are issued
+  // and not consumed). Named register arrays, selected by bit tests: an indexed array
+  // would be placed in scratch memory.
   uint4 qtmp[KS];
-  bf16x8_t qs0[KS], qs1[KS];
+  bf16x8_t qs0[KS], qs1[KS], qs2[NS > 2 ? KS : 1];
+  int q_stage = 0;                           // stage of the piece being issued
   bool q_pending = false;
 
   // enters the piece that starts at tile t and loads its queries; false when none is left
@@ -637,7 +643,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const int tb = t - cu_cur;               // first tile of the piece within the sequence
     const int nt = pe - t;
     t = pe;
-    int L = a.seq_lens[cs];
+    int L = lens[cs];                         // scalar load: no vector wait at piece entry
     L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
     const int first = cu_cur / C;
     const int np = (cu_next - 1) / C - first + 1;
@@ -664,10 +670,11 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     return true;
   };
 
-  // per-slot tile state (two slots: the tile being consumed and the one in flight)
-  uint4 kb[2][NV], vb[2][NV];
-  int sl_t0[2], sl_s[2], sl_p[2], sl_np[2], sl_te[2];
-  bool sl_ok[2], sl_first[2], sl_last[2], sl_par[2], sl_valid[2];
+  // per-slot tile state (NS slots: the tile being consumed and those in flight)
+  static_assert(NS == 2 || NS == 3, "ring of 2 or 3 tiles");
+  uint4 kb[NS][NV], vb[NS][NV];
+  int sl_t0[NS], sl_s[NS], sl_p[NS], sl_np[NS], sl_te[NS], sl_par[NS];
+  bool sl_ok[NS], sl_first[NS], sl_last[NS], sl_valid[NS];
 
   bool more = enter();
   // issue the next tile of the stream into slot k; false when the stream is exhausted
@@ -676,8 +683,15 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
       q_pending = false;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        if (iord & 1) qs1[kk] = __builtin_bit_cast(bf16x8_t, qtmp[kk]);
-        else qs0[kk] = __builtin_bit_cast(bf16x8_t, qtmp[kk]);
+        const bf16x8_t v = __builtin_bit_cast(bf16x8_t, qtmp[kk]);
+        if constexpr (NS > 2) {
+          if (q_stage & 2) qs2[kk] = v;
+          else if (q_stage & 1) qs1[kk] = v;
+          else qs0[kk] = v;
+        } else {
+          if (q_stage & 1) qs1[kk] = v;
+          else qs0[kk] = v;
+        }
       }
     }
     // Every call issues the same loads (row 0 of block 0 once the stream is exhausted),
@@ -698,10 +712,10 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     sl_valid[k] = live && i_valid;
     sl_first[k] = live && i_n == 0;
     sl_last[k] = live && i_n == i_nt - 1;
-    sl_par[k] = iord & 1;
+    sl_par[k] = q_stage;
     // the next piece's queries go out before this tile's rows
     if (live && ++i_n == i_nt) {
-      ++iord;
+      q_stage = q_stage + 1 == NS ? 0 : q_stage + 1;
       more = enter();
     }
 #pragma unroll
@@ -718,7 +732,11 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   auto consume = [&](int k, const uint4 (&kr)[NV], const uint4 (&vr)[NV]) {
     bf16x8_t qf[KS];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = sl_par[k] ? qs1[kk] : qs0[kk];
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8_t lo = (sl_par[k] & 1) ? qs1[kk] : qs0[kk];
+      if constexpr (NS > 2) qf[kk] = (sl_par[k] & 2) ? qs2[kk] : lo;
+      else qf[kk] = lo;
+    }
     if (sl_first[k]) {
       m = -INFINITY;
       lsum = 0.f;
@@ -831,12 +849,19 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   // (no row is valid, so it changes neither the running sums nor the outputs). An exit
   // between the two halves would join the loop's back edge in the control-flow graph
   // with a slot still in flight, and every wait at the top would become a full drain.
-  bool live = issue(0, kb[0], vb[0]);
+#pragma unroll
+  for (int k = 0; k + 1 < NS; ++k) issue(k, kb[k], vb[k]);
+  bool live = true;
   do {
-    issue(1, kb[1], vb[1]);
-    consume(0, kb[0], vb[0]);
-    live = issue(0, kb[0], vb[0]);
-    consume(1, kb[1], vb[1]);
+    // issue into the slot consumed last, then consume the oldest; after the sweep the
+    // slots issued at k >= 1 are outstanding, and the first of them decides whether any is live
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int ik = (k + NS - 1) % NS;
+      const bool l = issue(ik, kb[ik], vb[ik]);
+      if (k == 1) live = l;
+      consume(k, kb[k], vb[k]);
+    }
   } while (live);
 }
 
