@@ -132,3 +132,30 @@ def test_config3_full_size_sampled_split():
 
 def test_config4_full_size_sampled_split():
     _sampled(workloads.config4(), 5)
+
+
+def test_repeated_calls_on_one_workspace_agree():
+    w = workloads.small_decode(21, [3000, 129, 4097, 1, 700, 16], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                               block_size=16, dtype="bf16")
+    st = build_step(w)
+    tabs, bt, cu, slots, kp, vp = oracle_planes(st)
+    ref, ref_lse = oracle_attention_full(st, kp, vp, bt, cu)
+    B, Hq, d = w.num_seqs, w.num_q_heads, w.head_dim
+    split = pkv.build_decode_split(w.seq_lens, 9)
+    assert split.max_pieces > 1
+    plan_d = torch.from_numpy(split.plan).cuda()
+    nb = pkv.decode_split_workspace_bytes(B, Hq, d, split.max_pieces)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    first = None
+    for i in range(4):
+        out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_decode_split(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, plan_d, split,
+                                         w.num_kv_heads, w.block_size, int(w.seq_lens.max()), w.softmax_scale,
+                                         1.0, 1.0, ws, lse)
+        torch.cuda.synchronize()
+        o = out_f64(out)
+        assert_close(o, ref, "bf16", f"call {i}")
+        if first is None:
+            first = o
+        assert (o == first).all(), f"call {i} differs from call 0"
