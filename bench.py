@@ -229,7 +229,7 @@ def measured_traffic(partition: int, workload: str, decode: str):
     valid only while the profiled kernel source is unchanged (else None)."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    rec = os.path.join(here, "profiles", "decode_partition_pass__cfg3_large_decode_bf16.counters.json")
+    rec = os.path.join(here, "profiles", f"decode_{decode}_pass__cfg3_large_decode_bf16.counters.json")
     if workload != "cfg3" or not os.path.exists(rec):
         return None
     r = json.load(open(rec))
