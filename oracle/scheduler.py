@@ -1,0 +1,160 @@
+"""Oracle of one continuous-batching scheduler step (test infrastructure only: tests,
+the smoke check and the benchmark's CPU baseline may use it; the product never does).
+
+The policy is the engine loop of "Continuous Batching" (infra.pidoku inference
+notes), section "2. Why does it exist?" (the Go `Engine.Step` with `preempt`), with
+the lifecycle of its section "1. What is it?" and the recompute preemption of
+"5. Technical explanation":
+
+  1. admit from the head of the waiting queue while fewer than max_running run and
+     the head's blocks can be allocated; stop at the first that does not fit;
+  2. one forward pass over every running request (prefill rows for the newly
+     admitted, one decode row for the others);
+  3. in running order: append one output token; a request that reached its output
+     count frees its blocks at once; one that needs a new block for its next token
+     allocates one, and if that fails it is preempted: its blocks are freed and it
+     goes to the FRONT of the waiting queue, to be re-prefilled later.
+
+Readings taken where the page leaves a step open (each listed with the others):
+  * blocks needed at admission = ceil((prompt + outputs so far) / block_size): a
+    preempted request re-prefills its prompt and the outputs it already has;
+  * the prefill row of a request holds prompt + outputs-so-far new tokens at
+    positions 0.. ; a decode row is the last output token at position
+    prompt + outputs - 1 (its K/V is written by that step), seeing all positions up to
+    it;
+  * a request finishes when its output count reaches max_tokens (no EOS: no model);
+  * arrivals: the requests whose arrival step is <= the current step join the back of
+    the waiting queue in (arrival, id) order at the start of the step;
+  * a step with nothing running emits no rows (the loop returns before the forward).
+
+Parity unpinned beyond invariants and hand-worked traces: the pages print no trace of
+this loop, so the tests pin it with small traces worked out by hand from the page's
+loop and with invariants (conservation of blocks, strict first-come-first-served
+admission, exact output counts, no leak) on random and full-size traces.
+"""
+from __future__ import annotations
+
+import collections
+import dataclasses
+from typing import Dict, List
+
+import numpy as np
+
+from . import allocator as oa
+from .metadata import build_block_table
+
+PREFILL, DECODE = 0, 1
+
+
+@dataclasses.dataclass
+class Req:
+    rid: int
+    arrival: int
+    prompt: int
+    max_tokens: int
+    n_out: int = 0
+    stage: int = PREFILL
+    preempted: int = 0
+    finished_step: int = -1
+
+
+@dataclasses.dataclass
+class StepPlan:
+    """What one step hands to the device: rows in running order and their metadata."""
+    step: int
+    ids: np.ndarray          # int64 [n] request ids
+    stages: np.ndarray       # int32 [n] PREFILL / DECODE
+    q_lens: np.ndarray       # int32 [n] new tokens of each row
+    seq_lens: np.ndarray     # int32 [n] context including the new tokens
+    block_tables: np.ndarray  # int32 [n][width], -1 padded
+    cu_seqlens_q: np.ndarray  # int32 [n + 1]
+    slot_mapping: np.ndarray  # int64 [sum q]
+    counters: Dict[str, int]
+
+
+class Scheduler:
+    def __init__(self, arrival, prompt, max_tokens, num_blocks: int, free_order, block_size: int,
+                 max_running: int):
+        self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
+        self.arrival_order = sorted(range(len(self.reqs)), key=lambda i: (self.reqs[i].arrival, i))
+        self.next_arrival = 0
+        self.pool = oa.BlockPool(num_blocks, free_order)
+        self.tables = oa.SeqTables(self.pool, block_size)
+        self.bs = block_size
+        self.max_running = max_running
+        self.waiting: collections.deque = collections.deque()
+        self.running: List[Req] = []
+        self.step_no = 0
+        self.preemptions = 0
+        self.finished = 0
+
+    # -- counters -------------------------------------------------------------------
+    def counters(self) -> Dict[str, int]:
+        return {"free": self.pool.num_free, "running": len(self.running), "waiting": len(self.waiting),
+                "preempted": self.preemptions, "finished": self.finished}
+
+    def done(self) -> bool:
+        return self.finished == len(self.reqs)
+
+    # -- one step, first half: arrivals, admission, the rows of the forward pass -------
+    def schedule(self, width: int) -> StepPlan:
+        s = self.step_no
+        while self.next_arrival < len(self.arrival_order):
+            r = self.reqs[self.arrival_order[self.next_arrival]]
+            if r.arrival > s:
+                break
+            self.waiting.append(r)
+            self.next_arrival += 1
+        while self.waiting and len(self.running) < self.max_running:
+            r = self.waiting[0]
+            try:
+                self.tables.reserve(r.rid, r.prompt + r.n_out)      # all-or-nothing
+            except oa.OutOfBlocks:
+                break                                               # strict FCFS: stop here
+            self.waiting.popleft()
+            r.stage = PREFILL
+            self.running.append(r)
+        ids, stages, q, L = [], [], [], []
+        for r in self.running:
+            ctx = r.prompt + r.n_out
+            ids.append(r.rid)
+            stages.append(r.stage)
+            q.append(ctx if r.stage == PREFILL else 1)
+            L.append(ctx)
+        tabs = [self.tables.tables[i] for i in ids]
+        bt, cu, slots = build_block_table(tabs, q, L, self.bs, width)
+        return StepPlan(s, np.asarray(ids, np.int64), np.asarray(stages, np.int32), np.asarray(q, np.int32),
+                        np.asarray(L, np.int32), bt, cu, slots, self.counters())
+
+    # -- second half: one output token per row, retire, grow or preempt --------------
+    def update(self) -> None:
+        still = []
+        for r in self.running:
+            r.n_out += 1
+            r.stage = DECODE
+            if r.n_out >= r.max_tokens:
+                self.tables.release(r.rid)                          # freed at once
+                r.finished_step = self.step_no
+                self.finished += 1
+                continue
+            need = r.prompt + r.n_out                               # tokens its next row writes up to
+            if need > len(self.tables.tables[r.rid]) * self.bs:
+                try:
+                    self.tables.reserve(r.rid, need)                # one more block
+                except oa.OutOfBlocks:
+                    self.tables.release(r.rid)                      # preempt by recompute
+                    r.preempted += 1
+                    self.preemptions += 1
+                    self.waiting.appendleft(r)
+                    continue
+            still.append(r)
+        self.running = still
+        self.step_no += 1
+
+
+def run(sched: Scheduler, width: int, max_steps: int = 1 << 30):
+    """Yield (plan, counters after the update) for every step until all requests finish."""
+    while not sched.done() and sched.step_no < max_steps:
+        plan = sched.schedule(width)
+        sched.update()
+        yield plan, sched.counters()

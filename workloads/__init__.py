@@ -39,6 +39,10 @@ _STREAM_K = 21
 _STREAM_V = 22
 STREAMS = {"q": _STREAM_Q, "k": _STREAM_K, "v": _STREAM_V}
 _STREAM_TRACE = 30
+_STREAM_ARRIVALS = 31
+_STREAM_PROMPTS = 32
+_STREAM_OUTPUTS = 33
+_STREAM_LAYER_BASE = 40     # per-layer q/k/v streams: 40 + 3 * layer + (0, 1, 2)
 
 
 def rng_for(*key: int) -> np.random.Generator:
@@ -417,6 +421,80 @@ def small_varlen(seed: int, seq_lens, q_lens, num_q_heads=8, num_kv_heads=2, hea
     w.num_blocks = int(w.blocks_needed().sum()) + pool_extra
     w.free_order = _permutation(seed, w.num_blocks)
     return w
+
+
+@dataclasses.dataclass
+class Trace:
+    """A request trace for the continuous-batching replay: request r arrives at step
+    arrival[r] with a prompt of prompt[r] tokens and stops after max_tokens[r] outputs.
+    Q/K/V of (request, layer, position) are counter-hash values, so a recompute after a
+    preemption writes the same bytes."""
+    name: str
+    seed: int
+    arrival: np.ndarray
+    prompt: np.ndarray
+    max_tokens: np.ndarray
+    num_blocks: int
+    free_order: np.ndarray
+    block_size: int = 16
+    max_running: int = 128
+    num_layers: int = 16
+    num_q_heads: int = 32
+    num_kv_heads: int = 8
+    head_dim: int = 64
+    dtype: str = "bf16"
+    cache_dtype: str = "bf16"
+    sigma: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def num_requests(self) -> int:
+        return len(self.arrival)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    def value_key(self, which: str, layer: int, req: int) -> int:
+        return hash_key(self.seed, _STREAM_LAYER_BASE + 3 * layer + "qkv".index(which), req)
+
+    def rows_f32(self, which: str, layer: int, req: int, pos0: int, pos1: int) -> np.ndarray:
+        """Values of positions pos0..pos1-1 of a request in one layer: [n][heads][d] float32."""
+        heads = self.num_q_heads if which == "q" else self.num_kv_heads
+        per = heads * self.head_dim
+        v = hash_values(self.value_key(which, layer, req), pos0 * per, pos1 * per, self.sigma)
+        return v.reshape(pos1 - pos0, heads, self.head_dim)
+
+
+def config5(cache_dtype: str = "bf16") -> Trace:
+    """Continuous-batching trace: 2000 requests, Poisson arrivals of one per step on
+    average (arrival step = floor of the summed Exp(1) gaps), prompts lognormal with
+    median 512 (sigma 1) capped at 4096, outputs Geometric(1/256) capped at 4096; at most
+    128 running; blocks of 16 in a 4096-block pool (shuffled ids) that forces
+    preemption; 16 layers, 32/8 heads, d=64; bf16 values, bf16 or E4M3 cache."""
+    seed, n = 5, 2000
+    arrival = np.floor(np.cumsum(rng_for(seed, _STREAM_ARRIVALS).exponential(1.0, size=n))).astype(np.int32)
+    prompt = np.clip(np.rint(rng_for(seed, _STREAM_PROMPTS).lognormal(np.log(512.0), 1.0, size=n)),
+                     1, 4096).astype(np.int32)
+    max_tokens = np.minimum(rng_for(seed, _STREAM_OUTPUTS).geometric(1.0 / 256.0, size=n), 4096).astype(np.int32)
+    return Trace(f"cfg5_trace_{cache_dtype}", seed, arrival, prompt, max_tokens, 4096, _permutation(seed, 4096),
+                 cache_dtype=cache_dtype)
+
+
+def small_trace(seed: int, n: int, num_blocks: int, block_size: int = 4, max_running: int = 8,
+                prompt_max: int = 40, out_max: int = 30, rate: float = 1.0) -> Trace:
+    """A small seeded trace for tests (same generation rules, small sizes)."""
+    arrival = np.floor(np.cumsum(rng_for(seed, _STREAM_ARRIVALS).exponential(1.0 / rate, size=n))).astype(np.int32)
+    prompt = rng_for(seed, _STREAM_PROMPTS).integers(1, prompt_max, size=n, endpoint=True).astype(np.int32)
+    max_tokens = rng_for(seed, _STREAM_OUTPUTS).integers(1, out_max, size=n, endpoint=True).astype(np.int32)
+    return Trace(f"small_trace_{seed}", seed, arrival, prompt, max_tokens, num_blocks,
+                 _permutation(seed, num_blocks), block_size=block_size, max_running=max_running,
+                 num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=64)
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}
