@@ -261,6 +261,43 @@ int pkv_paged_attention_prefill_varlen(void* out, const void* q, int32_t q_dtype
                                        const int32_t* work_items, int32_t num_work, float* lse_out,
                                        void* stream);
 
+/* Continuous-batching scheduler step (host) over a pool ([CB] "2. Why does it exist?",
+ * the engine loop: admit, one mixed forward pass, update; [CB] "5. Technical
+ * explanation", preemption by recompute). Each request's id is its sequence id in the
+ * pool (the scheduler reserves and releases its table). One step is:
+ *   pkv_sched_schedule: requests whose arrival step <= the current step join the back of
+ *     the waiting queue in (arrival, id) order; then, while fewer than max_running run,
+ *     the head of the queue is admitted if ceil((prompt + outputs so far) / block_size)
+ *     blocks can be reserved for it, else admission stops (strict first come, first
+ *     served). Reports the step's rows, new tokens and widest table.
+ *   pkv_sched_plan (any number of times): the rows in running order -- id, stage (0
+ *     prefill: prompt + outputs so far new tokens at positions 0..; 1 decode: one new
+ *     token, the last output, at position prompt + outputs - 1), q_len, seq_len -- and
+ *     their block_tables / cu_seqlens_q / slot_mapping as pkv_build_block_table makes
+ *     them (host arrays; block_tables [rows][table_width], slot_mapping [total q]).
+ *   pkv_sched_update: in running order, one output token per row; a request with
+ *     max_tokens outputs finishes and frees its table at once; one whose next token needs
+ *     a new block reserves one, or, if none is free, is preempted: its table is freed and
+ *     it goes to the front of the waiting queue (several preempted in one step end up in
+ *     reverse order), to be re-prefilled with its outputs. The step number advances.
+ * Calls out of this order are INVALID. pkv_sched_add_requests: host arrays [n]; ids unique
+ * and without a table in the pool, prompt >= 1, max_tokens >= 1, arrival >= the current
+ * step, and prompt + max_tokens - 1 tokens must fit the pool (else the queue could stall);
+ * INVALID otherwise (nothing added). pkv_sched_counters: out int64 [7] = step, free
+ * blocks, running, waiting, preemptions so far, finished so far, requests added. The
+ * scheduler does not own the pool, which must outlive it; not thread-safe. */
+typedef struct pkv_sched pkv_sched;
+int pkv_sched_create(pkv_pool* pool, int32_t max_running, pkv_sched** out);
+void pkv_sched_destroy(pkv_sched* sched);
+int pkv_sched_add_requests(pkv_sched* sched, int32_t n, const int64_t* ids, const int32_t* arrival,
+                           const int32_t* prompt, const int32_t* max_tokens);
+int pkv_sched_schedule(pkv_sched* sched, int32_t* num_rows, int32_t* total_q, int32_t* max_blocks);
+int pkv_sched_plan(const pkv_sched* sched, int32_t table_width, int64_t* ids, int32_t* stages,
+                   int32_t* q_lens, int32_t* seq_lens, int32_t* block_tables, int32_t* cu_seqlens_q,
+                   int64_t* slot_mapping);
+int pkv_sched_update(pkv_sched* sched);
+int pkv_sched_counters(const pkv_sched* sched, int64_t* out);
+
 /* Profiling hook (for timing the partition pass alone): while `hip_event` (a
  * hipEvent_t) is not NULL, every pkv_paged_attention_decode and
  * pkv_paged_attention_decode_split call made on this thread records it on its stream

@@ -59,6 +59,13 @@ _SIGS = {
     "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
     "pkv_build_varlen_work": (C.c_int, [i32, vp, vp, i32, i32, vp, i32, P_i32]),
     "pkv_build_decode_split": (C.c_int, [i32, vp, i32, i32, vp, i32, P_i32, P_i32]),
+    "pkv_sched_create": (C.c_int, [vp, i32, C.POINTER(vp)]),
+    "pkv_sched_destroy": (None, [vp]),
+    "pkv_sched_add_requests": (C.c_int, [vp, i32, vp, vp, vp, vp]),
+    "pkv_sched_schedule": (C.c_int, [vp, P_i32, P_i32, P_i32]),
+    "pkv_sched_plan": (C.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+    "pkv_sched_update": (C.c_int, [vp]),
+    "pkv_sched_counters": (C.c_int, [vp, vp]),
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
     "pkv_decode_split_workspace_bytes": (sz, [i32, i32, i32, i32]),
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -66,6 +73,62 @@ _SIGS = {
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, vp]),
 }
+
+
+class StepPlan:
+    """Host arrays of one scheduled step (rows in running order)."""
+
+    def __init__(self, step, ids, stages, q_lens, seq_lens, block_tables, cu_seqlens_q, slot_mapping):
+        self.step, self.ids, self.stages, self.q_lens, self.seq_lens = step, ids, stages, q_lens, seq_lens
+        self.block_tables, self.cu_seqlens_q, self.slot_mapping = block_tables, cu_seqlens_q, slot_mapping
+
+
+class Scheduler:
+    """pkv_sched handle: the continuous-batching step over a Pool (which it must not outlive)."""
+
+    COUNTERS = ("step", "free", "running", "waiting", "preempted", "finished", "requests")
+
+    def __init__(self, pool: Pool, max_running: int):
+        self.pool = pool                        # keeps the pool alive
+        h = vp()
+        check(lib().pkv_sched_create(pool.handle, max_running, C.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pkv_sched_destroy(h)
+            self._h = None
+
+    def add_requests(self, ids, arrival, prompt, max_tokens) -> None:
+        a = [np.ascontiguousarray(x, dtype=t) for x, t in
+             ((ids, np.int64), (arrival, np.int32), (prompt, np.int32), (max_tokens, np.int32))]
+        check(lib().pkv_sched_add_requests(self._h, len(a[0]), *[_np_ptr(x) for x in a]))
+
+    def schedule(self):
+        n, q, mb = i32(), i32(), i32()
+        check(lib().pkv_sched_schedule(self._h, C.byref(n), C.byref(q), C.byref(mb)))
+        return int(n.value), int(q.value), int(mb.value)
+
+    def plan(self, num_rows: int, total_q: int, table_width: int) -> StepPlan:
+        ids = np.zeros(num_rows, np.int64)
+        st = np.zeros(num_rows, np.int32)
+        ql = np.zeros(num_rows, np.int32)
+        sl = np.zeros(num_rows, np.int32)
+        bt = np.zeros((num_rows, table_width), np.int32)
+        cu = np.zeros(num_rows + 1, np.int32)
+        slots = np.zeros(total_q, np.int64)
+        check(lib().pkv_sched_plan(self._h, table_width, _np_ptr(ids), _np_ptr(st), _np_ptr(ql), _np_ptr(sl),
+                                   _np_ptr(bt), _np_ptr(cu), _np_ptr(slots)))
+        return StepPlan(self.counters()["step"], ids, st, ql, sl, bt, cu, slots)
+
+    def update(self) -> None:
+        check(lib().pkv_sched_update(self._h))
+
+    def counters(self) -> dict:
+        out = np.zeros(7, np.int64)
+        check(lib().pkv_sched_counters(self._h, _np_ptr(out)))
+        return dict(zip(self.COUNTERS, (int(x) for x in out)))
 
 
 def header_functions() -> list:

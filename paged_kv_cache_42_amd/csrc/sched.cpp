@@ -1,0 +1,223 @@
+// Host scheduler step of continuous batching, on top of the block pool.
+//
+// The loop is the engine step of "Continuous Batching" (infra.pidoku inference notes),
+// section "2. Why does it exist?" (admit from the head of the waiting queue while a slot
+// and the blocks are free, stopping at the first request that does not fit; run one
+// mixed forward pass over every running request; then, in running order, append one
+// output token, free a finished request's blocks at once, give a request that needs one
+// a new block, and preempt it to the front of the queue when none is left), with the
+// recompute preemption of "5. Technical explanation". Readings where the page leaves a
+// step open: blocks at admission cover prompt + outputs so far (a preempted request
+// re-prefills both); a prefill row holds those tokens at positions 0..; a decode row is
+// the last output token; a request finishes at its output count; arrivals join the
+// back of the queue at the start of their step in (arrival, id) order.
+#include <algorithm>
+#include <cstdint>
+#include <deque>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+#include "pool_internal.h"
+
+using pkv::fail;
+
+namespace {
+
+enum : int32_t { kPrefill = 0, kDecode = 1 };
+
+struct Req {
+  int64_t id;
+  int32_t arrival, prompt, max_tokens;
+  int32_t n_out = 0;
+  int32_t stage = kPrefill;
+};
+
+// Grow the table of `id` to cover `tokens` tokens, all-or-nothing; false when the pool
+// has too few free blocks (nothing changed).
+bool reserve(pkv_pool* p, int64_t id, int64_t tokens) {
+  const int64_t want = (tokens + p->block_size - 1) / p->block_size;
+  auto it = p->tables.find(id);
+  const int64_t have = it == p->tables.end() ? 0 : int64_t(it->second.size());
+  const int64_t need = want - have;
+  if (need > int64_t(p->free_list.size())) return false;
+  std::vector<int32_t>& t = p->tables[id];
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = p->free_list.back();
+    p->free_list.pop_back();
+    p->state[b] = kInSeq;
+    t.push_back(b);
+  }
+  return true;
+}
+
+// Free the table of `id` in table order.
+void release(pkv_pool* p, int64_t id) {
+  auto it = p->tables.find(id);
+  if (it == p->tables.end()) return;
+  for (int32_t b : it->second) {
+    p->state[b] = kFree;
+    p->free_list.push_back(b);
+  }
+  p->tables.erase(it);
+}
+
+}  // namespace
+
+struct pkv_sched {
+  pkv_pool* pool = nullptr;
+  int32_t max_running = 0;
+  std::vector<Req> reqs;
+  std::vector<int32_t> arrival_order;   // indices into reqs, by (arrival, id)
+  size_t next_arrival = 0;
+  std::deque<int32_t> waiting;
+  std::vector<int32_t> running;
+  int64_t step = 0;
+  int64_t preempted = 0;
+  int64_t finished = 0;
+  bool scheduled = false;               // schedule() done, update() pending
+};
+
+extern "C" {
+
+int pkv_sched_create(pkv_pool* pool, int32_t max_running, pkv_sched** out) {
+  if (!pool || !out || max_running < 1) return fail(PKV_ERR_INVALID, "sched_create: bad arguments");
+  auto* s = new pkv_sched();
+  s->pool = pool;
+  s->max_running = max_running;
+  *out = s;
+  return PKV_OK;
+}
+
+void pkv_sched_destroy(pkv_sched* s) { delete s; }
+
+int pkv_sched_add_requests(pkv_sched* s, int32_t n, const int64_t* ids, const int32_t* arrival,
+                           const int32_t* prompt, const int32_t* max_tokens) {
+  if (!s || n < 0 || (n > 0 && (!ids || !arrival || !prompt || !max_tokens)))
+    return fail(PKV_ERR_INVALID, "sched_add_requests: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    if (prompt[i] < 1 || max_tokens[i] < 1 || arrival[i] < 0)
+      return fail(PKV_ERR_INVALID, "sched_add_requests: request %lld needs prompt >= 1, max_tokens >= 1, "
+                  "arrival >= 0", (long long)ids[i]);
+    if (arrival[i] < s->step)
+      return fail(PKV_ERR_INVALID, "sched_add_requests: request %lld arrives at step %d, before the current "
+                  "step %lld", (long long)ids[i], arrival[i], (long long)s->step);
+    const int64_t blocks = (int64_t(prompt[i]) + max_tokens[i] - 1 + s->pool->block_size - 1) / s->pool->block_size;
+    if (blocks > s->pool->num_blocks)
+      return fail(PKV_ERR_INVALID, "sched_add_requests: request %lld can need %lld blocks, the pool has %d",
+                  (long long)ids[i], (long long)blocks, s->pool->num_blocks);
+    if (s->pool->tables.count(ids[i]))
+      return fail(PKV_ERR_INVALID, "sched_add_requests: id %lld already holds a table", (long long)ids[i]);
+  }
+  for (const Req& r : s->reqs)
+    for (int32_t i = 0; i < n; ++i)
+      if (r.id == ids[i]) return fail(PKV_ERR_INVALID, "sched_add_requests: id %lld repeated", (long long)ids[i]);
+  for (int32_t i = 0; i < n; ++i) {
+    for (int32_t j = 0; j < i; ++j)
+      if (ids[j] == ids[i]) return fail(PKV_ERR_INVALID, "sched_add_requests: id %lld repeated", (long long)ids[i]);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    s->reqs.push_back(Req{ids[i], arrival[i], prompt[i], max_tokens[i]});
+    s->arrival_order.push_back(int32_t(s->reqs.size() - 1));
+  }
+  // requests not yet arrived are kept sorted by (arrival, id)
+  std::sort(s->arrival_order.begin() + s->next_arrival, s->arrival_order.end(), [&](int32_t a, int32_t b) {
+    const Req &x = s->reqs[a], &y = s->reqs[b];
+    return x.arrival != y.arrival ? x.arrival < y.arrival : x.id < y.id;
+  });
+  return PKV_OK;
+}
+
+int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_t* max_blocks) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_schedule: scheduler is NULL");
+  if (s->scheduled) return fail(PKV_ERR_INVALID, "sched_schedule: the previous step was not updated");
+  // arrivals
+  while (s->next_arrival < s->arrival_order.size()) {
+    const int32_t i = s->arrival_order[s->next_arrival];
+    if (s->reqs[i].arrival > s->step) break;
+    s->waiting.push_back(i);
+    ++s->next_arrival;
+  }
+  // strict first-come-first-served admission
+  while (!s->waiting.empty() && int32_t(s->running.size()) < s->max_running) {
+    Req& r = s->reqs[s->waiting.front()];
+    if (!reserve(s->pool, r.id, int64_t(r.prompt) + r.n_out)) break;
+    r.stage = kPrefill;
+    s->running.push_back(s->waiting.front());
+    s->waiting.pop_front();
+  }
+  int64_t q = 0, mb = 0;
+  for (int32_t i : s->running) {
+    const Req& r = s->reqs[i];
+    const int64_t ctx = int64_t(r.prompt) + r.n_out;
+    q += r.stage == kPrefill ? ctx : 1;
+    mb = std::max<int64_t>(mb, (ctx + s->pool->block_size - 1) / s->pool->block_size);
+  }
+  s->scheduled = true;
+  if (num_rows) *num_rows = int32_t(s->running.size());
+  if (total_q) *total_q = int32_t(q);
+  if (max_blocks) *max_blocks = int32_t(mb);
+  return PKV_OK;
+}
+
+int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_t* stages, int32_t* q_lens,
+                   int32_t* seq_lens, int32_t* block_tables, int32_t* cu_seqlens_q, int64_t* slot_mapping) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_plan: scheduler is NULL");
+  if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_plan: no step scheduled");
+  const int32_t n = int32_t(s->running.size());
+  if (n > 0 && (!ids || !stages || !q_lens || !seq_lens))
+    return fail(PKV_ERR_INVALID, "sched_plan: NULL row array");
+  for (int32_t k = 0; k < n; ++k) {
+    const Req& r = s->reqs[s->running[k]];
+    const int32_t ctx = r.prompt + r.n_out;
+    ids[k] = r.id;
+    stages[k] = r.stage;
+    q_lens[k] = r.stage == kPrefill ? ctx : 1;
+    seq_lens[k] = ctx;
+  }
+  return pkv_build_block_table(s->pool, n, ids, q_lens, seq_lens, table_width, block_tables, cu_seqlens_q,
+                               slot_mapping);
+}
+
+int pkv_sched_update(pkv_sched* s) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_update: scheduler is NULL");
+  if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_update: no step scheduled");
+  std::vector<int32_t> still;
+  still.reserve(s->running.size());
+  for (int32_t i : s->running) {
+    Req& r = s->reqs[i];
+    r.n_out += 1;
+    r.stage = kDecode;
+    if (r.n_out >= r.max_tokens) {            // finished: blocks freed at once
+      release(s->pool, r.id);
+      ++s->finished;
+      continue;
+    }
+    const int64_t need = int64_t(r.prompt) + r.n_out;   // tokens the next row writes up to
+    if (!reserve(s->pool, r.id, need)) {      // no block for the next token: preempt
+      release(s->pool, r.id);
+      ++s->preempted;
+      s->waiting.push_front(i);
+      continue;
+    }
+    still.push_back(i);
+  }
+  s->running.swap(still);
+  s->scheduled = false;
+  ++s->step;
+  return PKV_OK;
+}
+
+int pkv_sched_counters(const pkv_sched* s, int64_t* out) {
+  if (!s || !out) return fail(PKV_ERR_INVALID, "sched_counters: bad arguments");
+  out[0] = s->step;
+  out[1] = int64_t(s->pool->free_list.size());
+  out[2] = int64_t(s->running.size());
+  out[3] = int64_t(s->waiting.size());
+  out[4] = s->preempted;
+  out[5] = s->finished;
+  out[6] = int64_t(s->reqs.size());
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+"""libpkv's scheduler step (C++ through the C ABI) against the scheduler oracle, bit-exact
+at every step: rows, block tables, cu_seqlens, slot mapping and counters. Host only."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import paged_kv_cache_42_amd as pkv
+import workloads
+from oracle import scheduler as osch
+
+
+def _pair(tr):
+    pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
+                    free_order=tr.free_order)
+    ours = pkv.Scheduler(pool, tr.max_running)
+    ours.add_requests(np.arange(tr.num_requests), tr.arrival, tr.prompt, tr.max_tokens)
+    ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
+                         tr.max_running)
+    return pool, ours, ref
+
+
+def _replay_both(tr, width):
+    pool, ours, ref = _pair(tr)
+    steps = 0
+    for rp, rafter in osch.run(ref, width):
+        n, q, mb = ours.schedule()
+        assert (n, q) == (len(rp.ids), int(rp.q_lens.sum())), f"step {rp.step}"
+        assert mb <= width
+        c = ours.counters()
+        assert {k: c[k] for k in rp.counters} == rp.counters, f"step {rp.step} after admission"
+        p = ours.plan(n, q, width)
+        for name in ("ids", "stages", "q_lens", "seq_lens", "block_tables", "cu_seqlens_q", "slot_mapping"):
+            a, b = getattr(p, name), getattr(rp, name)
+            assert a.dtype == b.dtype and a.shape == b.shape and (a == b).all(), f"step {rp.step}: {name}"
+        ours.update()
+        c = ours.counters()
+        assert {k: c[k] for k in rafter} == rafter, f"step {rp.step} after update"
+        steps += 1
+    assert ours.counters()["finished"] == tr.num_requests
+    assert pool.stats() == (tr.num_blocks, 0)
+    return steps, ref
+
+
+def test_config5_full_trace_bit_exact_every_step():
+    tr = workloads.config5()
+    steps, ref = _replay_both(tr, 512)
+    assert ref.preemptions > 0 and steps == ref.step_no
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(0, 10_000), st.integers(18, 60), st.integers(1, 8))
+def test_random_small_traces_bit_exact(seed, pool, max_running):
+    tr = workloads.small_trace(seed, 30, pool, block_size=4, max_running=max_running, prompt_max=40,
+                               out_max=30, rate=2.0)
+    _replay_both(tr, 20)
+
+
+def test_call_order_and_request_errors():
+    pool = pkv.Pool(8, 4, 1, 64, "bf16")
+    s = pkv.Scheduler(pool, 2)
+    with pytest.raises(pkv.PkvError):
+        s.update()                                   # nothing scheduled
+    with pytest.raises(pkv.PkvError):
+        s.add_requests([1], [0], [0], [1])           # empty prompt
+    with pytest.raises(pkv.PkvError):
+        s.add_requests([1], [0], [30], [4])          # 33 tokens cannot fit 8 blocks of 4
+    with pytest.raises(pkv.PkvError):
+        s.add_requests([1, 1], [0, 0], [3, 3], [2, 2])   # repeated id
+    s.add_requests([1, 2], [0, 1], [3, 3], [2, 2])
+    assert s.counters()["requests"] == 2
+    s.schedule()
+    with pytest.raises(pkv.PkvError):
+        s.schedule()                                 # previous step not updated
+    with pytest.raises(pkv.PkvError):
+        s.plan(1, 3, 0)                              # table too narrow
+    s.update()
+    with pytest.raises(pkv.PkvError):
+        s.add_requests([3], [0], [3], [2])           # arrives before the current step
+    pool.seq_reserve(9, 4)
+    with pytest.raises(pkv.PkvError):
+        s.add_requests([9], [5], [3], [2])           # id already holds a table
