@@ -46,6 +46,10 @@ def parse_args():
                          "piece of the balanced split")
     ap.add_argument("--decode", default="split", choices=["split", "partition"],
                     help="balanced split over resident workgroup slots (default) or fixed context partitions")
+    ap.add_argument("--no-replay", action="store_true",
+                    help="skip the continuous-batching trace replay (2000 requests, scheduler step + 16 layers of "
+                         "cache write and mixed attention per step, bf16 and E4M3 caches)")
+    ap.add_argument("--replay-steps", type=int, default=None, help="replay only the first N scheduler steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
@@ -222,6 +226,23 @@ def mixed_step(steps: int, warmup: int):
             "attention_bytes": nbytes, "attention_flops": flops,
             "hbm_GBps": round(nbytes / t_a / 1e9, 1), "hbm_frac": round(nbytes / t_a / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_TFLOPs": round(flops / t_a / 1e12, 1), "mfma_frac": round(flops / t_a / 1e12 / 2500.0, 4)}
+
+
+def sched_replay(max_steps):
+    """Continuous-batching trace replay (the 2000-request trace): per step the host
+    scheduler admits/plans/updates and 16 layers run the cache write and the mixed
+    attention launch; per-step attention time from HIP events (inputs generated on the
+    device before each step's timed region)."""
+    import workloads
+    from workloads import replay
+    out = {}
+    for cdt in ("bf16", "fp8"):
+        tr = workloads.config5(cdt)
+        print(f"[bench] replay {tr.name}", file=sys.stderr, flush=True)
+        _, summ = replay.run(tr, max_steps=max_steps,
+                             progress=lambda n: print(f"[bench] replay {cdt}: {n} steps", file=sys.stderr, flush=True))
+        out[cdt] = summ
+    return out
 
 
 def measured_traffic(partition: int, workload: str, decode: str):
@@ -477,6 +498,8 @@ def main():
     if not args.no_mixed:
         print("[bench] mixed prefill+decode step", file=sys.stderr, flush=True)
         res["mixed_step"] = mixed_step(args.steps, args.warmup)
+    if not args.no_replay:
+        res["sched_replay"] = sched_replay(args.replay_steps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -1,0 +1,73 @@
+"""Config 5 trace replay on the GPU: libpkv's scheduler step drives the cache write and
+the mixed attention launch of 16 layers; sampled rows (prefill, recompute after a
+preemption, decode) are compared with the oracle's attention over the dense K/V of the
+request, element by element. The scheduler itself is bit-exact vs its oracle on the CPU
+(test_sched_host.py); here the device path is checked end to end."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as oatt
+from oracle import fp8 as ofp8
+from workloads import replay
+
+from gpu_setup import TOL, out_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dense(tr, which, layer, req, L):
+    x = tr.rows_f32(which, layer, req, 0, L).astype(np.float64)
+    if tr.cache_dtype == "fp8":
+        scale = tr.k_scale if which == "k" else tr.v_scale
+        x = ofp8.decode(ofp8.encode(x.astype(np.float32), scale), scale)
+    return x
+
+
+def _check_step(tr, rec, rng, max_rows=8, tokens_per_row=3):
+    plan = rec.plan
+    cu = plan.cu_seqlens_q
+    rows = list(range(len(plan.ids)))
+    pre = [r for r in rows if plan.stages[r] == 0]
+    dec = [r for r in rows if plan.stages[r] == 1]
+    pick = pre[:max_rows // 2] + list(rng.choice(dec, size=min(len(dec), max_rows - min(len(pre), max_rows // 2)),
+                                                 replace=False))
+    checked = 0
+    for layer, out in rec.kept.items():
+        o = out_f64(out)
+        assert np.isfinite(o).all()
+        for r in pick:
+            req, q, L = int(plan.ids[r]), int(plan.q_lens[r]), int(plan.seq_lens[r])
+            K = _dense(tr, "k", layer, req, L)
+            V = _dense(tr, "v", layer, req, L)
+            toks = sorted(set([0, q - 1] + rng.integers(0, q, size=tokens_per_row).tolist()))
+            qs = tr.rows_f32("q", layer, req, L - q, L)[toks].astype(np.float64)
+            ref, _ = oatt.attend(qs, K, V, [L - q + t for t in toks], tr.softmax_scale, tr.group)
+            got = o[cu[r] + np.array(toks)]
+            tol = TOL["fp8" if tr.cache_dtype == "fp8" else "bf16"]
+            err = np.abs(got - ref).max()
+            assert err <= tol, f"step {rec.step} layer {layer} request {req} (q {q}, L {L}): err {err:.3e}"
+            checked += 1
+    return checked
+
+
+@pytest.mark.parametrize("cache_dtype,steps,keep_steps", [
+    ("bf16", 160, (0, 1, 112, 115, 145, 159)),
+    ("fp8", 120, (0, 112, 115, 119)),
+])
+def test_config5_replay_sampled_parity(cache_dtype, steps, keep_steps):
+    tr = workloads.config5(cache_dtype)
+    keep = {s: (0, tr.num_layers - 1) for s in keep_steps}
+    recs, summary = replay.run(tr, max_steps=steps, keep=keep)
+    assert summary["steps"] == steps
+    by_step = {r.step: r for r in recs}
+    rng = np.random.default_rng(5)
+    checked = 0
+    for s in keep_steps:
+        checked += _check_step(tr, by_step[s], rng)
+    assert checked >= 20
+    if steps > 112:
+        assert summary["preemptions"] > 0
+        # the step after the first preemption re-prefills a request with its outputs
+        p = by_step[112].plan
+        assert any(st_ == 0 and q > tr.prompt[i] for i, st_, q in zip(p.ids, p.stages, p.q_lens))

@@ -47,6 +47,51 @@ extern "C" int pkvgen_fill(void* out, int as_bf16, uint64_t key, int64_t e0, int
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// Many segments in one launch: segment r writes elements e0[r] .. e0[r] + n_r - 1 of
+// stream keys[r] to out[off[r] .. off[r+1]) (off: int64 prefix of the segment sizes,
+// off[0] = 0). Each thread finds its segment by binary search over off.
+namespace {
+__global__ void __launch_bounds__(256) fill_segments(void* out, int as_bf16, int nseg, const uint64_t* keys,
+                                                     const int64_t* e0, const int64_t* off, float sigma) {
+  const int64_t total = off[nseg];
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    int lo = 0, hi = nseg - 1;                 // last r with off[r] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const uint64_t e = uint64_t(e0[lo] + (i - off[lo]));
+    const uint64_t n = e / 3;
+    const uint32_t j = uint32_t(e - n * 3);
+    const uint64_t h = finalize(keys[lo] + (n + 1) * 0x9E3779B97F4A7C15ull);
+    const uint32_t f = uint32_t((h >> (18 * j)) & 0x3FFFFull);
+    const uint32_t s = (f & 63u) + ((f >> 6) & 63u) + (f >> 12);
+    float v = float(s) * 0.03125f - 2.953125f;
+    if (sigma != 1.0f) v *= sigma;
+    if (as_bf16)
+      static_cast<uint16_t*>(out)[i] = uint16_t(__float_as_uint(v) >> 16);
+    else
+      static_cast<float*>(out)[i] = v;
+  }
+}
+}  // namespace
+
+// keys, e0: device [nseg]; off: device int64 [nseg + 1] (non-decreasing, off[0] = 0);
+// out: device buffer of off[nseg] elements; total: off[nseg] (host copy, sizes the grid).
+extern "C" int pkvgen_fill_segments(void* out, int as_bf16, int nseg, const void* keys, const void* e0,
+                                    const void* off, int64_t total, float sigma, void* stream) {
+  if (nseg <= 0 || total <= 0) return 0;
+  if (!out || !keys || !e0 || !off) return -1;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_segments, dim3(unsigned(blocks)), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     out, as_bf16, nseg, static_cast<const uint64_t*>(keys), static_cast<const int64_t*>(e0),
+                     static_cast<const int64_t*>(off), sigma);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 // ---------------------------------------------------------------------------------
 // HBM stream-read probe (measurement only): every lane reads 16-byte chunks of `buf`
 // with UNROLL independent loads in flight per iteration, folds them with xor, and

@@ -39,6 +39,9 @@ def lib():
         L = C.CDLL(LIB)
         L.pkvgen_fill.restype = C.c_int
         L.pkvgen_fill.argtypes = [C.c_void_p, C.c_int, C.c_uint64, C.c_int64, C.c_int64, C.c_float, C.c_void_p]
+        L.pkvgen_fill_segments.restype = C.c_int
+        L.pkvgen_fill_segments.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_int64, C.c_float, C.c_void_p]
         L.pkvgen_read_probe.restype = C.c_int
         L.pkvgen_read_probe.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         _lib = L
@@ -55,6 +58,24 @@ def fill(t, key: int, e0: int, sigma: float = 1.0) -> None:
                            int(e0), t.numel(), float(sigma), C.c_void_p(st))
     if rc != 0:
         raise RuntimeError(f"pkvgen_fill failed ({rc})")
+
+
+def fill_segments(t, seg_dev, nseg: int, total: int, sigma: float = 1.0) -> None:
+    """Fill the first `total` elements of device tensor t from nseg segments described by
+    seg_dev, a device int64 tensor [3 * nseg + 1]: keys (as int64 bits) [nseg], first
+    element index [nseg], then the output offsets [nseg + 1] (starting at 0)."""
+    import torch
+    if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("contiguous float32/bfloat16 device tensor expected")
+    if seg_dev.dtype != torch.int64 or seg_dev.numel() != 3 * nseg + 1 or t.numel() < total:
+        raise ValueError("segment table mis-sized")
+    st = torch.cuda.current_stream().cuda_stream
+    base = seg_dev.data_ptr()
+    rc = lib().pkvgen_fill_segments(C.c_void_p(t.data_ptr()), int(t.dtype == torch.bfloat16), int(nseg),
+                                    C.c_void_p(base), C.c_void_p(base + 8 * nseg), C.c_void_p(base + 16 * nseg),
+                                    int(total), float(sigma), C.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError(f"pkvgen_fill_segments failed ({rc})")
 
 
 def read_probe(buf, blocks: int, unroll: int, out) -> None:
