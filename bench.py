@@ -194,38 +194,58 @@ def mixed_step(steps: int, warmup: int):
     out = torch.empty_like(q)
     msl = int(w.seq_lens.max())
     stream = torch.cuda.current_stream()
+    # the same attention as two launches: split decode rows + prefill-only varlen
+    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, Hkv, w.group, pkv.decode_split_slots(pkv.BF16, Hkv, d, w.block_size))
+    rows_d = torch.from_numpy(mp.decode_rows).cuda()
+    plan_d = torch.from_numpy(mp.split.plan).cuda()
+    pwork = torch.from_numpy(mp.prefill_work).cuda()
+    ws = torch.empty(max(1, pkv.decode_split_workspace_bytes(len(mp.decode_rows), Hq, d, mp.split.max_pieces)),
+                     dtype=torch.uint8, device="cuda")
 
-    def step(e=None):
+    def attention(two_launch):
+        if not two_launch:
+            pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, work, Hkv, w.block_size, msl,
+                                               w.softmax_scale)
+            return
+        pkv.paged_attention_decode_split(out, q, kc, vc, bt_d, lens_d, plan_d, mp.split, Hkv, w.block_size, msl,
+                                         w.softmax_scale, 1.0, 1.0, ws, rows=rows_d, cu_seqlens_q=cu_d)
+        pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, pwork, Hkv, w.block_size, msl,
+                                           w.softmax_scale)
+
+    def step(two_launch, e=None):
         if e is not None:
             e[0].record(stream)
         pkv.kv_cache_write(nk, nv, kc, vc, slots_d, w.block_size)
         if e is not None:
             e[1].record(stream)
-        pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, work, Hkv, w.block_size, msl,
-                                           w.softmax_scale)
+        attention(two_launch)
         if e is not None:
             e[2].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    t_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
     nbytes, flops = mixed_bytes_flops(w)
-    return {"workload": f"{w.name}: 48 decode rows (context U[16,2048]) + 4 causal chunks of 512 new tokens "
-                        f"after 0/512/1024/1536 cached, 32/8 heads, d 128, bs 16, bf16, fragmented pool",
-            "query_tokens": n_new, "context_tokens": int(w.seq_lens.sum()), "ms_per_step": round(wall * 1e3, 4),
-            "kernel_us": {"kv_cache_write": round(t_w * 1e6, 2), "varlen_attention": round(t_a * 1e6, 2)},
+    res = {"workload": f"{w.name}: 48 decode rows (context U[16,2048]) + 4 causal chunks of 512 new tokens "
+                       f"after 0/512/1024/1536 cached, 32/8 heads, d 128, bs 16, bf16, fragmented pool",
+           "query_tokens": n_new, "context_tokens": int(w.seq_lens.sum()),
+           "attention_bytes": nbytes, "attention_flops": flops}
+    for two in (False, True):
+        for _ in range(warmup):
+            step(two)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(two, ev[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        t_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+        t_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+        res["split_decode_plus_prefill" if two else "one_launch"] = {
+            "ms_per_step": round(wall * 1e3, 4),
+            "kernel_us": {"kv_cache_write": round(t_w * 1e6, 2), "attention": round(t_a * 1e6, 2)},
             "tokens_per_s": round(n_new / wall, 1),
-            "attention_bytes": nbytes, "attention_flops": flops,
             "hbm_GBps": round(nbytes / t_a / 1e9, 1), "hbm_frac": round(nbytes / t_a / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_TFLOPs": round(flops / t_a / 1e12, 1), "mfma_frac": round(flops / t_a / 1e12 / 2500.0, 4)}
+    return res
 
 
 def sched_replay(max_steps):

@@ -206,16 +206,25 @@ size_t pkv_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
 /* Decode attention with a balanced split of the context over a fixed number of slots
  * (the attention of [P17] "Step 6", as for pkv_paged_attention_decode; the split and
  * its log-sum-exp merge are this library's scheduling, not the pages'). Arguments from
- * `out` to `v_scale` and `lse_out`: as for pkv_paged_attention_decode, with bf16 queries
- * and a bf16 or E4M3 cache, head_dim 64/128, block_size 16/32, at most 16 query heads per
- * KV head. plan: device int32, the array pkv_build_decode_split returned for the same
- * seq_lens and num_slots (tiles_per_slot and max_pieces likewise); the launch has
- * num_slots workgroups per group of KV heads. A sequence inside one slot's range is
+ * `out` to `v_scale` and `lse_out`: as for pkv_paged_attention_decode (num_seqs = the
+ * batch's sequences, the rows of block_tables and seq_lens), with bf16 queries and a
+ * bf16 or E4M3 cache, head_dim 64/128, block_size 16/32, at most 16 query heads per KV
+ * head. Which rows are decoded: rows (device int32 [num_rows], nullable) gives the batch
+ * sequence of each plan row, e.g. the decode rows of a mixed step; NULL means every
+ * sequence in order (num_rows must equal num_seqs). Where queries and outputs live:
+ * with cu_seqlens_q (device int32 [num_seqs + 1], nullable) q and out are
+ * [total_q][num_q_heads][head_dim] and sequence b's row is its last new token,
+ * cu_seqlens_q[b + 1] - 1 (for a decode row, its only one); with NULL they are
+ * [num_seqs][...] and total_q must equal num_seqs. lse_out follows the same rows. plan:
+ * device int32, the array pkv_build_decode_split returned for the plan rows' seq_lens
+ * (in plan-row order) and num_slots (tiles_per_slot and max_pieces likewise); the launch
+ * has num_slots workgroups per group of KV heads. A plan row inside one slot's range is
  * written directly; the pieces of one spanning several slots are merged by log-sum-exp
- * in a second kernel, which also writes zeros (log-sum-exp -inf) for sequences without
- * context. workspace: device, >= pkv_decode_split_workspace_bytes(num_seqs,
- * num_q_heads, head_dim, max_pieces). A plan that does not match seq_lens reads no
- * memory out of bounds: a piece that does not fit is masked and not written. */
+ * in a second kernel, which also writes zeros (log-sum-exp -inf) for rows without
+ * context. workspace: device, >= pkv_decode_split_workspace_bytes(num_rows,
+ * num_q_heads, head_dim, max_pieces). A plan or row map that does not match the batch
+ * reads no memory out of bounds: a piece whose row falls outside the batch or that does
+ * not fit is masked and not written. */
 int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,
                                      const void* k_cache, const void* v_cache,
                                      int32_t cache_dtype, const int32_t* block_tables,
@@ -223,7 +232,9 @@ int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,
                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                      int32_t max_seq_len, float scale, float k_scale,
-                                     float v_scale, const int32_t* plan, int32_t num_slots,
+                                     float v_scale, const int32_t* rows, int32_t num_rows,
+                                     const int32_t* cu_seqlens_q, int32_t total_q,
+                                     const int32_t* plan, int32_t num_slots,
                                      int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
                                      size_t workspace_bytes, float* lse_out, void* stream);
 

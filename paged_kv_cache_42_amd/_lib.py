@@ -69,7 +69,8 @@ _SIGS = {
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
     "pkv_decode_split_workspace_bytes": (sz, [i32, i32, i32, i32]),
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                   i32, i32, f32, f32, f32, vp, i32, i32, i32, vp, sz, vp, vp]),
+                                                   i32, i32, f32, f32, f32, vp, i32, vp, i32, vp, i32, i32, i32, vp,
+                                                   sz, vp, vp]),
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, vp]),
 }
@@ -384,29 +385,41 @@ def decode_split_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
 def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split: SplitPlan,
                                  num_kv_heads: int, block_size: int, max_seq_len: int, scale: float,
                                  k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, lse=None,
-                                 stream=None) -> None:
-    """q/out: [B][Hq][d] bf16; plan_dev: device int32 copy of split.plan."""
+                                 rows=None, cu_seqlens_q=None, stream=None) -> None:
+    """Balanced-split decode. Without rows / cu_seqlens_q: q/out [B][Hq][d], one plan row per
+    sequence. rows (device int32 [n]): the batch sequences the plan covers; cu_seqlens_q
+    (device int32 [B + 1]): q/out are [total_q][Hq][d] and a sequence's row is its last
+    new token. plan_dev: device int32 copy of split.plan."""
     torch = _torch()
-    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, workspace, lse)
+    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, workspace, lse, rows,
+                         cu_seqlens_q)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q and out must both be [B][Hq][d] of one dtype")
-    B, Hq, d = q.shape
+        raise ValueError("q and out must both be [rows][Hq][d] of one dtype")
+    T, Hq, d = q.shape
+    B = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
     _check_plane(k_cache, v_cache, block_size, num_kv_heads, d)
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be int32 [B][W]")
-    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+    if seq_lens.dtype != torch.int32 or B < 0:
         raise ValueError("seq_lens must be int32 [B]")
-    if plan_dev.dtype != torch.int32 or tuple(plan_dev.shape) != (B + 1 + split.num_slots,):
-        raise ValueError("plan must be int32 [B + 1 + num_slots] (from build_decode_split)")
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq)):
-        raise ValueError("lse must be float32 [B][Hq]")
+    n = B if rows is None else rows.shape[0]
+    if rows is not None and (rows.dtype != torch.int32 or rows.dim() != 1):
+        raise ValueError("rows must be int32 [n]")
+    if cu_seqlens_q is None and T != B:
+        raise ValueError("q must be [B][Hq][d] without cu_seqlens_q")
+    if cu_seqlens_q is not None and (cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (B + 1,)):
+        raise ValueError("cu_seqlens_q must be int32 [B + 1]")
+    if plan_dev.dtype != torch.int32 or tuple(plan_dev.shape) != (n + 1 + split.num_slots,):
+        raise ValueError("plan must be int32 [rows + 1 + num_slots] (from build_decode_split)")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise ValueError("lse must be float32 [rows][Hq]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().pkv_paged_attention_decode_split(
         _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
         _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
-        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(plan_dev), split.num_slots,
-        split.tiles_per_slot, split.max_pieces, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
-
+        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(rows), n, _dptr(cu_seqlens_q), T,
+        _dptr(plan_dev), split.num_slots, split.tiles_per_slot, split.max_pieces, _dptr(workspace), ws_bytes,
+        _dptr(lse), _stream(stream)))
 
 def decode_set_profile_event(event) -> None:
     """Record torch.cuda.Event `event` after the decode partition pass (None: off)."""
@@ -428,6 +441,27 @@ def build_varlen_work(q_lens, seq_lens, num_kv_heads: int, group: int) -> np.nda
     check(lib().pkv_build_varlen_work(len(q), _np_ptr(q), _np_ptr(L), num_kv_heads, group, _np_ptr(out), cap,
                                       C.byref(n)))
     return out[: n.value]
+
+
+class MixedPlan:
+    """Host plan of a mixed step run as two launches: the decode rows (one new token) by
+    the balanced-split decode, the prefill chunks by the varlen launch."""
+
+    def __init__(self, decode_rows, split, prefill_work):
+        self.decode_rows, self.split, self.prefill_work = decode_rows, split, prefill_work
+
+
+def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots: int,
+                     min_piece_tokens: int = 0) -> MixedPlan:
+    """Split a mixed step's rows: sequences with exactly one new token go to a balanced
+    split plan (rows in batch order), the others to a prefill-only varlen work list."""
+    q = np.ascontiguousarray(q_lens, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    dec = np.nonzero(q == 1)[0].astype(np.int32)
+    split = build_decode_split(L[dec], num_slots, min_piece_tokens) if len(dec) else None
+    qp = np.where(q == 1, 0, q).astype(np.int32)
+    work = build_varlen_work(qp, L, num_kv_heads, group) if (qp > 0).any() else np.zeros((0, 4), np.int32)
+    return MixedPlan(dec, split, work)
 
 
 def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,

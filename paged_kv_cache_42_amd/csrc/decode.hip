@@ -117,7 +117,22 @@ struct DecodeArgs {
   const int4* work;  // (seq, partition, partitions, end token) per item, or null: grid over all
   const int32_t* plan;   // balanced split: tile offsets [B + 1], then first sequence per slot
   int tiles_per_slot;    // balanced split: 16-token tiles per workgroup slot
+  const int32_t* rows;   // balanced split: batch sequence of each plan row (null: row = sequence)
+  const int32_t* cu_q;   // balanced split: the batch's cu_seqlens_q (null: one query row per sequence)
+  int num_batch;         // batch sequences (rows of block_tables / seq_lens)
+  int total_q;           // query / output rows
 };
+
+// Batch sequence and query/output row of plan row s of a balanced split (the decode row
+// of a sequence is its last new token); -1 in *row for an index outside the batch.
+__device__ __forceinline__ void split_row(const DecodeArgs& a, int s, int& b, int& row) {
+  typedef __attribute__((address_space(4))) const int32_t* cptr;
+  b = a.rows ? ((cptr)(uintptr_t)(a.rows))[s] : s;
+  row = -1;
+  if (b < 0 || b >= a.num_batch) return;
+  const int r = a.cu_q ? ((cptr)(uintptr_t)(a.cu_q))[b + 1] - 1 : b;
+  if (r >= 0 && r < a.total_q) row = r;
+}
 
 // The (sequence, partition) of this workgroup and its token range; false = nothing to do.
 __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int& s, int& p, int& nparts, int& tok_begin,
@@ -418,18 +433,22 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   const int e = 4 * (threadIdx.x % LPH);
   if (hq >= num_q_heads) return;
   int nparts;
+  int orow_idx = s;
   if (a.plan) {
     // balanced split: pieces = slots that the sequence's tiles touch
+    int b;
+    split_row(a, s, b, orow_idx);
+    if (orow_idx < 0) return;
     const int c0 = a.plan[s], c1 = a.plan[s + 1];
     nparts = c1 > c0 && c0 >= 0 ? (c1 - 1) / a.tiles_per_slot - c0 / a.tiles_per_slot + 1 : 0;
     if (nparts == 0) {                        // no context: zero output (no piece wrote it)
-      const int64_t oi = (int64_t(s) * num_q_heads + hq) * D + e;
+      const int64_t oi = (int64_t(orow_idx) * num_q_heads + hq) * D + e;
       if constexpr (QDT == PKV_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(0.f, 0.f, 0.f, 0.f);
       } else {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(0u, 0u);
       }
-      if (a.lse_out && e == 0) a.lse_out[int64_t(s) * num_q_heads + hq] = -INFINITY;
+      if (a.lse_out && e == 0) a.lse_out[int64_t(orow_idx) * num_q_heads + hq] = -INFINITY;
       return;
     }
     nparts = nparts < a.pmax ? nparts : a.pmax;
@@ -459,7 +478,7 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const float r[4] = {A.x * inv, A.y * inv, A.z * inv, A.w * inv};
-  const int64_t oi = (int64_t(s) * num_q_heads + hq) * D + e;
+  const int64_t oi = (int64_t(orow_idx) * num_q_heads + hq) * D + e;
   if constexpr (QDT == PKV_F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(r[0], r[1], r[2], r[3]);
   } else {
@@ -467,7 +486,8 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
     const uint32_t hi = pkv::f32_to_bf16(r[2]) | (pkv::f32_to_bf16(r[3]) << 16);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(lo, hi);
   }
-  if (a.lse_out && e == 0) a.lse_out[int64_t(s) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
+  if (a.lse_out && e == 0)
+    a.lse_out[int64_t(orow_idx) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
 }
 
 // ---------------------------------------------------------------------------------
@@ -616,7 +636,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   cs = cs < 0 ? 0 : (cs > B ? B : cs);
   int cu_cur = plan[cs];
   int cu_next = cs < B ? plan[cs + 1] : 0x7fffffff;
-  int i_s = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
+  int i_s = 0, i_row = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
   bool i_valid = false;
   cptr_i32 i_bt = nullptr;
   // Queries: a piece's rows are loaded into qtmp when the piece is entered and moved
@@ -643,14 +663,19 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const int tb = t - cu_cur;               // first tile of the piece within the sequence
     const int nt = pe - t;
     t = pe;
-    int L = lens[cs];                         // scalar load: no vector wait at piece entry
+    int b, row;
+    split_row(a, cs, b, row);                 // scalar loads: no vector wait at piece entry
+    if (row < 0) b = 0;
+    int L = lens[b];
     L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
     const int first = cu_cur / C;
     const int np = (cu_next - 1) / C - first + 1;
     const int p = slot - first;
     // a piece of an inconsistent plan is streamed masked and not written
-    const bool valid = tb >= 0 && cu_cur >= 0 && p >= 0 && p < np && (np == 1 || (a.ws_o != nullptr && p < a.pmax));
+    const bool valid = row >= 0 && tb >= 0 && cu_cur >= 0 && p >= 0 && p < np &&
+                       (np == 1 || (a.ws_o != nullptr && p < a.pmax));
     i_s = cs;
+    i_row = row;
     i_p = p;
     i_np = np;
     i_valid = valid;
@@ -658,9 +683,10 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     i_te = valid ? min(16 * (tb + nt), L) : 0;
     i_nt = nt;
     i_n = 0;
-    i_bt = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(cs) * a.table_width);
+    i_bt = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(b) * a.table_width);
     // lanes past the group read a duplicate head of it: their columns are never written
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(cs) * Hq + int64_t(g) * G + hl_q) * D;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (int64_t(row < 0 ? 0 : row) * Hq + int64_t(g) * G + hl_q) * D;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int d0 = EB == 2 ? 32 * kk + 8 * grp : 64 * (kk / 2) + 16 * grp + 8 * (kk % 2);
@@ -673,7 +699,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   // per-slot tile state (NS slots: the tile being consumed and those in flight)
   static_assert(NS == 2 || NS == 3, "ring of 2 or 3 tiles");
   uint4 kb[NS][NV], vb[NS][NV];
-  int sl_t0[NS], sl_s[NS], sl_p[NS], sl_np[NS], sl_te[NS], sl_par[NS];
+  int sl_t0[NS], sl_s[NS], sl_row[NS], sl_p[NS], sl_np[NS], sl_te[NS], sl_par[NS];
   bool sl_ok[NS], sl_first[NS], sl_last[NS], sl_valid[NS];
 
   bool more = enter();
@@ -706,6 +732,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     sl_t0[k] = tok_lo;
     sl_ok[k] = ok;
     sl_s[k] = i_s;
+    sl_row[k] = i_row;
     sl_p[k] = i_p;
     sl_np[k] = i_np;
     sl_te[k] = i_te;
@@ -825,7 +852,8 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
     if (sl_np[k] == 1) {
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(s) * Hq + hq) * D + 4 * grp;
+      const int row = sl_row[k];
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(row) * Hq + hq) * D + 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
@@ -833,7 +861,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
         pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
       }
       if (a.lse_out && grp == 0)
-        pkv::store_b32_untracked(a.lse_out + int64_t(s) * Hq + hq, __float_as_uint(lse2 * kLn2));
+        pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + hq, __float_as_uint(lse2 * kLn2));
     } else {
       const int64_t pi = (int64_t(s) * Hq + hq) * a.pmax + sl_p[k];
       float* orow = a.ws_o + pi * D + 4 * grp;
@@ -1138,7 +1166,9 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
                                                 int32_t table_width, int32_t num_seqs, int32_t num_q_heads,
                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                                 int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale,
-                                                float v_scale, const int32_t* plan, int32_t num_slots,
+                                                float v_scale, const int32_t* rows, int32_t num_rows,
+                                                const int32_t* cu_seqlens_q, int32_t total_q,
+                                                const int32_t* plan, int32_t num_slots,
                                                 int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
                                                 size_t workspace_bytes, float* lse_out, void* stream) {
   using pkv::fail;
@@ -1164,13 +1194,19 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
                 tiles_per_slot, max_pieces);
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return fail(PKV_ERR_INVALID, "decode_split: scales must be > 0");
-  if (num_seqs == 0) return PKV_OK;
+  if (rows ? num_rows < 0 : num_rows != num_seqs)
+    return fail(PKV_ERR_INVALID, "decode_split: num_rows %d (rows %s) with %d sequences", num_rows,
+                rows ? "given" : "NULL", num_seqs);
+  if (cu_seqlens_q ? total_q < 0 : total_q != num_seqs)
+    return fail(PKV_ERR_INVALID, "decode_split: total_q %d (cu_seqlens_q %s) with %d sequences", total_q,
+                cu_seqlens_q ? "given" : "NULL", num_seqs);
+  if (num_rows == 0 || num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !plan)
     return fail(PKV_ERR_INVALID, "decode_split: NULL pointer");
   if (num_blocks < 1) return fail(PKV_ERR_INVALID, "decode_split: the cache has no blocks");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID, "decode_split: q, out and cache planes must be 16-byte aligned");
-  const size_t need = pkv_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim, max_pieces);
+  const size_t need = pkv_decode_split_workspace_bytes(num_rows, num_q_heads, head_dim, max_pieces);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_INVALID, "decode_split: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
 
@@ -1190,21 +1226,25 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
   a.pmax = need > 0 ? max_pieces : 1;
   if (need > 0) {
     a.ws_o = static_cast<float*>(workspace);
-    a.ws_lse = a.ws_o + size_t(num_seqs) * num_q_heads * max_pieces * head_dim;
+    a.ws_lse = a.ws_o + size_t(num_rows) * num_q_heads * max_pieces * head_dim;
   }
   a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
   a.v_scale = v_scale;
   a.group = G;
-  a.num_seqs = num_seqs;
+  a.num_seqs = num_rows;                      // the plan's rows
   a.plan = plan;
   a.tiles_per_slot = tiles_per_slot;
+  a.rows = rows;
+  a.cu_q = cu_seqlens_q;
+  a.num_batch = num_seqs;
+  a.total_q = total_q;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(fn, dim3(num_kv_heads / hpw, num_slots), dim3(hpw * 64), 0, st, a);
   if (g_profile_event) (void)hipEventRecord(g_profile_event, st);
   // the merge also writes the zero output of sequences without context
   MergeFn mf = pick_merge(q_dtype, head_dim);
   const int heads_per_wg = 256 / (head_dim / 4);
-  hipLaunchKernelGGL(mf, dim3((num_q_heads + heads_per_wg - 1) / heads_per_wg, num_seqs), dim3(256), 0, st, a,
+  hipLaunchKernelGGL(mf, dim3((num_q_heads + heads_per_wg - 1) / heads_per_wg, num_rows), dim3(256), 0, st, a,
                      num_q_heads);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_split: launch failed: %s", hipGetErrorString(e));

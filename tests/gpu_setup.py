@@ -251,3 +251,30 @@ def run_varlen(st: Step, lse: bool = True, max_seq_len=None):
                                        lse=lse_t)
     torch.cuda.synchronize()
     return out, lse_t
+
+
+def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_tokens: int = 0, lse: bool = True):
+    """A mixed step as two launches: decode rows (one new token) by the balanced-split decode
+    with the batch's row map, prefill chunks by the varlen launch over prefill items only."""
+    w = st.w
+    T, Hq, d = w.total_q, w.num_q_heads, w.head_dim
+    msl = int(w.seq_lens.max())
+    if num_slots is None:
+        num_slots = pkv.decode_split_slots(pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16, w.num_kv_heads, d,
+                                           w.block_size)
+    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, w.num_kv_heads, w.group, num_slots, min_piece_tokens)
+    out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_t = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    if len(mp.decode_rows):
+        nb = pkv.decode_split_workspace_bytes(len(mp.decode_rows), Hq, d, mp.split.max_pieces)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+        pkv.paged_attention_decode_split(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d,
+                                         torch.from_numpy(mp.split.plan).cuda(), mp.split, w.num_kv_heads,
+                                         w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, ws, lse_t,
+                                         rows=torch.from_numpy(mp.decode_rows).cuda(), cu_seqlens_q=st.cu_d)
+    if len(mp.prefill_work):
+        pkv.paged_attention_prefill_varlen(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d,
+                                           torch.from_numpy(mp.prefill_work).cuda(), w.num_kv_heads, w.block_size,
+                                           msl, w.softmax_scale, w.k_scale, w.v_scale, lse=lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t

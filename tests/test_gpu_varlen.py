@@ -9,23 +9,30 @@ import torch
 import paged_kv_cache_42_amd as pkv
 import workloads
 
-from gpu_setup import assert_close, build_step, oracle_attention_full, oracle_planes, out_f64, run_varlen
+from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_planes, out_f64, run_mixed_two_launch,
+                       run_varlen)
 
 pytestmark = pytest.mark.gpu
 
 LSE_ATOL = 2.0 ** -8   # weights enter P.V rounded to bf16 (see the decode tests)
 
 
-def _check(w):
+def _check(w, two_launch_slots=(None, 3)):
     st = build_step(w)
     tabs, bt, cu, slots, kp, vp = oracle_planes(st)
     assert (st.bt == bt).all() and (st.cu == cu).all() and (st.slots == slots).all()
     ref, ref_lse = oracle_attention_full(st, kp, vp, bt, cu)
-    out, lse = run_varlen(st)
     dt = "fp8" if w.cache_dtype == "fp8" else "bf16"
+    out, lse = run_varlen(st)
     assert_close(out_f64(out), ref, dt, w.name)
-    got = lse.cpu().numpy()
-    np.testing.assert_allclose(got, ref_lse, rtol=0, atol=LSE_ATOL)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
+    # the same step as two launches (split decode rows + prefill-only varlen)
+    for n in two_launch_slots:
+        o2, l2 = run_mixed_two_launch(st, num_slots=n)
+        got = out_f64(o2)
+        assert not np.isnan(got).any(), f"{w.name} two launches ({n} slots): unwritten rows"
+        assert_close(got, ref, dt, f"{w.name} two launches ({n} slots)")
+        np.testing.assert_allclose(l2.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
     return st, out, lse
 
 

@@ -4,8 +4,9 @@ mixed (prefill + decode) attention launch of every layer, step after step.
 Benchmark and test infrastructure. Per step: the host scheduler admits, plans and
 updates (C ABI); the step's metadata goes to the device once for all layers; the Q/K/V
 of every new token of every layer are generated on the device by the counter-hash
-generator (outside the timed region), then each layer runs pkv_kv_cache_write followed
-by pkv_paged_attention_prefill_varlen, bracketed by HIP events per step."""
+generator (outside the timed region), then each layer runs pkv_kv_cache_write, the
+balanced-split decode over the step's decode rows and the varlen launch over its prefill
+chunks, bracketed by HIP events per step."""
 from __future__ import annotations
 
 import dataclasses
@@ -56,6 +57,9 @@ class Replay:
         self.heads = np.array([tr.num_q_heads, tr.num_kv_heads, tr.num_kv_heads], np.int64)
         self.buf = None
         self.e_kv = 1 if tr.cache_dtype == "fp8" else 2
+        self.slots = pkv.decode_split_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.num_kv_heads,
+                                            tr.head_dim, tr.block_size)
+        self.min_piece = 256
 
     def _values(self, ids, q_lens, seq_lens):
         """Generate Q/K/V of the step's new tokens for every layer into one buffer; return
@@ -100,7 +104,15 @@ class Replay:
         lens = torch.from_numpy(seq_lens).cuda()
         cu = torch.from_numpy(plan.cu_seqlens_q).cuda()
         slots = torch.from_numpy(plan.slot_mapping).cuda()
-        work = torch.from_numpy(pkv.build_varlen_work(q_lens, seq_lens, tr.num_kv_heads, tr.group)).cuda()
+        # decode rows by the balanced-split decode, prefill chunks by the varlen launch
+        mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, self.slots, self.min_piece)
+        work = torch.from_numpy(mp.prefill_work).cuda() if len(mp.prefill_work) else None
+        if len(mp.decode_rows):
+            rows = torch.from_numpy(mp.decode_rows).cuda()
+            plan_d = torch.from_numpy(mp.split.plan).cuda()
+            nb = pkv.decode_split_workspace_bytes(len(mp.decode_rows), tr.num_q_heads, tr.head_dim,
+                                                  mp.split.max_pieces)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
         msl = int(seq_lens.max())
         out = torch.empty((T, tr.num_q_heads, tr.head_dim), dtype=torch.bfloat16, device="cuda")
         kept = {}
@@ -110,9 +122,14 @@ class Replay:
         for l in range(tr.num_layers):
             q, k, v = vals[l]
             pkv.kv_cache_write(k, v, self.k_cache[l], self.v_cache[l], slots, tr.block_size, tr.k_scale, tr.v_scale)
-            pkv.paged_attention_prefill_varlen(out, q, self.k_cache[l], self.v_cache[l], bt, lens, cu, work,
-                                               tr.num_kv_heads, tr.block_size, msl, tr.softmax_scale, tr.k_scale,
-                                               tr.v_scale)
+            if len(mp.decode_rows):
+                pkv.paged_attention_decode_split(out, q, self.k_cache[l], self.v_cache[l], bt, lens, plan_d, mp.split,
+                                                 tr.num_kv_heads, tr.block_size, msl, tr.softmax_scale, tr.k_scale,
+                                                 tr.v_scale, ws, rows=rows, cu_seqlens_q=cu)
+            if work is not None:
+                pkv.paged_attention_prefill_varlen(out, q, self.k_cache[l], self.v_cache[l], bt, lens, cu, work,
+                                                   tr.num_kv_heads, tr.block_size, msl, tr.softmax_scale,
+                                                   tr.k_scale, tr.v_scale)
             if l in keep_layers:
                 kept[l] = out.clone()
         e1.record()
