@@ -194,31 +194,37 @@ def mixed_step(steps: int, warmup: int):
     out = torch.empty_like(q)
     msl = int(w.seq_lens.max())
     stream = torch.cuda.current_stream()
-    # the same attention as two launches: split decode rows + prefill-only varlen
-    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, Hkv, w.group, pkv.decode_split_slots(pkv.BF16, Hkv, d, w.block_size))
+    # the same attention as two launches: split decode rows + the chunk kernel, with the
+    # chunk blocks uncut ("uncut") or cut along the keys over the resident workgroups
+    dslots = pkv.decode_split_slots(pkv.BF16, Hkv, d, w.block_size)
+    plans = {}
+    for mode, cslots in (("uncut", 0), ("cut", pkv.chunk_slots(pkv.BF16, d, w.block_size))):
+        mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, Hkv, w.group, dslots, 0, cslots)
+        plans[mode] = (mp, mp.chunks.to_device(d))
+    mp = plans["cut"][0]
     rows_d = torch.from_numpy(mp.decode_rows).cuda()
     plan_d = torch.from_numpy(mp.split.plan).cuda()
-    pwork = torch.from_numpy(mp.prefill_work).cuda()
     ws = torch.empty(max(1, pkv.decode_split_workspace_bytes(len(mp.decode_rows), Hq, d, mp.split.max_pieces)),
                      dtype=torch.uint8, device="cuda")
 
-    def attention(two_launch):
-        if not two_launch:
+    def attention(mode):
+        if mode == "one_launch":
             pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, work, Hkv, w.block_size, msl,
                                                w.softmax_scale)
             return
         pkv.paged_attention_decode_split(out, q, kc, vc, bt_d, lens_d, plan_d, mp.split, Hkv, w.block_size, msl,
                                          w.softmax_scale, 1.0, 1.0, ws, rows=rows_d, cu_seqlens_q=cu_d)
-        pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, pwork, Hkv, w.block_size, msl,
-                                           w.softmax_scale)
+        cp, (cwork, cmerges, cws) = plans[mode]
+        pkv.paged_attention_prefill_chunks(out, q, kc, vc, bt_d, lens_d, cu_d, cwork, cmerges, cp.chunks.num_partials,
+                                           cws, Hkv, w.block_size, msl, w.softmax_scale)
 
-    def step(two_launch, e=None):
+    def step(mode, e=None):
         if e is not None:
             e[0].record(stream)
         pkv.kv_cache_write(nk, nv, kc, vc, slots_d, w.block_size)
         if e is not None:
             e[1].record(stream)
-        attention(two_launch)
+        attention(mode)
         if e is not None:
             e[2].record(stream)
 
@@ -227,7 +233,9 @@ def mixed_step(steps: int, warmup: int):
                        f"after 0/512/1024/1536 cached, 32/8 heads, d 128, bs 16, bf16, fragmented pool",
            "query_tokens": n_new, "context_tokens": int(w.seq_lens.sum()),
            "attention_bytes": nbytes, "attention_flops": flops}
-    for two in (False, True):
+    names = {"one_launch": "one_launch", "uncut": "split_decode_plus_chunks_uncut",
+             "cut": "split_decode_plus_chunks"}
+    for two in names:
         for _ in range(warmup):
             step(two)
         torch.cuda.synchronize()
@@ -239,7 +247,7 @@ def mixed_step(steps: int, warmup: int):
         wall = (time.perf_counter() - t0) / steps
         t_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
         t_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
-        res["split_decode_plus_prefill" if two else "one_launch"] = {
+        res[names[two]] = {
             "ms_per_step": round(wall * 1e3, 4),
             "kernel_us": {"kv_cache_write": round(t_w * 1e6, 2), "attention": round(t_a * 1e6, 2)},
             "tokens_per_s": round(n_new / wall, 1),

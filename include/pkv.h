@@ -272,6 +272,63 @@ int pkv_paged_attention_prefill_varlen(void* out, const void* q, int32_t q_dtype
                                        const int32_t* work_items, int32_t num_work, float* lse_out,
                                        void* stream);
 
+/* Chunk work list (host) for pkv_paged_attention_prefill_chunks. For each sequence s with
+ * q = q_lens[s] >= 2 new tokens and seq_len L = seq_lens[s] (host int32 arrays; q < 2 gives
+ * nothing: decode rows go to the split decode), one row block per KV head g and per 128/G
+ * new tokens q0.. (G = group), whose keys end at the block's last position + 1 ([P17]
+ * "Step 6", causal). With T the 64-key tiles of all blocks and num_slots > 0 (the
+ * workgroups resident at once, pkv_chunk_slots), a block of more than
+ * max_tiles = max(1, min_piece_tiles, ceil(T / num_slots)) tiles is cut into
+ * np = ceil(tiles / max_tiles) pieces of whole tiles whose sizes differ by at most one
+ * tile (num_slots <= 0: nothing is cut); each piece writes a partial into its own workspace slot and one merge
+ * record combines the block's pieces by log-sum-exp (the decomposition of [P17] "Step 6"
+ * over disjoint key ranges). items: host int32 [capacity][8] = (seq, KV head, first new
+ * token of the block, first key, key end, slot or -1, 0, 0), most tiles first;
+ * merges: host int32 [merge_capacity][4] = (seq, KV head, first new token, first slot |
+ * np << 20); *count, *merge_count, *num_partials = items, merge records and workspace
+ * slots (also set when a capacity is too small). INVALID if q > L, a capacity is too small
+ * or the slots reach 2^20; UNSUPPORTED unless G is 1, 2, 4, 8 or 16. */
+int pkv_build_chunk_work(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
+                         int32_t num_kv_heads, int32_t group, int32_t num_slots,
+                         int32_t min_piece_tiles, int32_t* items,
+                         int32_t capacity, int32_t* count, int32_t* merges, int32_t merge_capacity,
+                         int32_t* merge_count, int32_t* num_partials);
+
+/* Chunk-kernel workgroups resident on the current device at once (compute units x
+ * workgroups per unit for this cache dtype / head_dim / block_size): the num_slots of
+ * pkv_build_chunk_work. UNSUPPORTED for a shape the kernel does not cover, HIP if the
+ * occupancy query fails. */
+int pkv_chunk_slots(int32_t cache_dtype, int32_t head_dim, int32_t block_size, int32_t* slots);
+
+/* Device workspace bytes for num_partials slots of pkv_build_chunk_work's split pieces
+ * (128 rows of fp32 head_dim outputs plus one log-sum-exp each); 0 when none. */
+int64_t pkv_chunk_workspace_bytes(int32_t num_partials, int32_t head_dim);
+
+/* Prefill chunks of a mixed step: new row i of sequence s sits at position
+ * seq_lens[s] - q_s + i and attends keys 0 .. that position ([P17] "Step 6", [CB]
+ * "5. Technical explanation"; rows delimited by cu_seqlens_q as for
+ * pkv_paged_attention_prefill_varlen, whose cache, table, scale and lse_out arguments
+ * this shares). work_items: device int32 [num_work][8], merges: device int32
+ * [num_merges][4], both from pkv_build_chunk_work for the same q_lens and seq_lens, with
+ * num_partials its slot count; workspace: device, at least pkv_chunk_workspace_bytes
+ * bytes, 16-byte aligned (not needed when num_partials is 0). The chunk kernel runs one
+ * workgroup per item (4 waves of 32 GQA-packed query rows, 64-key tiles on MFMA), then a
+ * merge kernel writes the rows of split blocks. Rows of sequences with q < 2 are not
+ * written. Supported: bf16 queries with a bf16 or E4M3 cache, head_dim 64/128,
+ * block_size 16/32, group 1/2/4/8/16. Calls sharing a workspace must not overlap. */
+int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype,
+                                       const void* k_cache, const void* v_cache,
+                                       int32_t cache_dtype, const int32_t* block_tables,
+                                       const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                       int32_t table_width, int32_t num_seqs, int32_t total_q,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                                       float scale, float k_scale, float v_scale,
+                                       const int32_t* work_items, int32_t num_work,
+                                       const int32_t* merges, int32_t num_merges, int32_t num_partials,
+                                       void* workspace, int64_t workspace_bytes, float* lse_out,
+                                       void* stream);
+
 /* Continuous-batching scheduler step (host) over a pool ([CB] "2. Why does it exist?",
  * the engine loop: admit, one mixed forward pass, update; [CB] "5. Technical
  * explanation", preemption by recompute). Each request's id is its sequence id in the

@@ -8,5 +8,6 @@ from ._lib import (  # noqa: F401
     BF16, F32, FP8, OutOfBlocks, PkvError, Pool, build_decode_work, decode_set_profile_event, decode_workspace_bytes, header_functions, kv_cache_write, lib,
     paged_attention_decode, build_varlen_work, paged_attention_prefill_varlen, SplitPlan, build_decode_split,
     decode_split_slots, decode_split_workspace_bytes, paged_attention_decode_split, Scheduler, StepPlan,
-    MixedPlan, build_mixed_step,
+    MixedPlan, build_mixed_step, paged_attention_prefill_chunks, ChunkPlan, build_chunk_work, chunk_slots,
+    chunk_workspace_bytes,
 )

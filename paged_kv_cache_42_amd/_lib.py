@@ -59,6 +59,12 @@ _SIGS = {
     "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
     "pkv_build_varlen_work": (C.c_int, [i32, vp, vp, i32, i32, vp, i32, P_i32]),
     "pkv_build_decode_split": (C.c_int, [i32, vp, i32, i32, vp, i32, P_i32, P_i32]),
+    "pkv_paged_attention_prefill_chunks": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                     i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, i32, i32, vp,
+                                                     i64, vp, vp]),
+    "pkv_build_chunk_work": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, vp, i32, P_i32, vp, i32, P_i32, P_i32]),
+    "pkv_chunk_slots": (C.c_int, [i32, i32, i32, P_i32]),
+    "pkv_chunk_workspace_bytes": (i64, [i32, i32]),
     "pkv_sched_create": (C.c_int, [vp, i32, C.POINTER(vp)]),
     "pkv_sched_destroy": (None, [vp]),
     "pkv_sched_add_requests": (C.c_int, [vp, i32, vp, vp, vp, vp]),
@@ -443,25 +449,76 @@ def build_varlen_work(q_lens, seq_lens, num_kv_heads: int, group: int) -> np.nda
     return out[: n.value]
 
 
-class MixedPlan:
-    """Host plan of a mixed step run as two launches: the decode rows (one new token) by
-    the balanced-split decode, the prefill chunks by the varlen launch."""
+class ChunkPlan:
+    """Host result of build_chunk_work: items int32 [n][8], merges int32 [m][4], workspace slots."""
 
-    def __init__(self, decode_rows, split, prefill_work):
-        self.decode_rows, self.split, self.prefill_work = decode_rows, split, prefill_work
+    def __init__(self, items: np.ndarray, merges: np.ndarray, num_partials: int):
+        self.items, self.merges, self.num_partials = items, merges, num_partials
+
+    def to_device(self, head_dim: int, device="cuda"):
+        """(work, merges or None, workspace or None) as device tensors for
+        paged_attention_prefill_chunks; None when there are no items."""
+        torch = _torch()
+        if len(self.items) == 0:
+            return None
+        work = torch.from_numpy(self.items).to(device)
+        merges = torch.from_numpy(self.merges).to(device) if len(self.merges) else None
+        nb = chunk_workspace_bytes(self.num_partials, head_dim)
+        ws = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+        return work, merges, ws
+
+
+def build_chunk_work(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots: int = 0,
+                     min_piece_tiles: int = 0) -> ChunkPlan:
+    """Row blocks of the sequences with two or more new tokens; blocks longer than the
+    even share of num_slots are cut along the keys (num_slots <= 0: never)."""
+    q = np.ascontiguousarray(q_lens, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    n, m, p = i32(), i32(), i32()
+    cap, mcap = 64, 16
+    while True:
+        items = np.zeros((cap, 8), np.int32)
+        merges = np.zeros((mcap, 4), np.int32)
+        st = lib().pkv_build_chunk_work(len(q), _np_ptr(q), _np_ptr(L), num_kv_heads, group, num_slots,
+                                        min_piece_tiles, _np_ptr(items), cap, C.byref(n), _np_ptr(merges), mcap,
+                                        C.byref(m), C.byref(p))
+        if st == PKV_OK:
+            return ChunkPlan(items[:n.value].copy(), merges[:m.value].copy(), p.value)
+        if st != PKV_ERR_INVALID or (n.value <= cap and m.value <= mcap):
+            check(st)
+        cap, mcap = max(cap, n.value), max(mcap, m.value)
+
+
+def chunk_slots(cache_dtype: int, head_dim: int, block_size: int) -> int:
+    """Chunk-kernel workgroups resident on the current device at once."""
+    out = i32()
+    check(lib().pkv_chunk_slots(cache_dtype, head_dim, block_size, C.byref(out)))
+    return out.value
+
+
+def chunk_workspace_bytes(num_partials: int, head_dim: int) -> int:
+    return int(lib().pkv_chunk_workspace_bytes(num_partials, head_dim))
+
+
+class MixedPlan:
+    """Host plan of a mixed step: decode rows (batch indices) with their balanced split
+    plan, and the chunk work of the other rows."""
+
+    def __init__(self, decode_rows, split, chunks):
+        self.decode_rows, self.split, self.chunks = decode_rows, split, chunks
 
 
 def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots: int,
-                     min_piece_tokens: int = 0) -> MixedPlan:
+                     min_piece_tokens: int = 0, chunk_slots: int = 0, min_piece_tiles: int = 0) -> MixedPlan:
     """Split a mixed step's rows: sequences with exactly one new token go to a balanced
-    split plan (rows in batch order), the others to a prefill-only varlen work list."""
+    split plan over num_slots (rows in batch order), those with more to the chunk work list
+    (cut along the keys over chunk_slots resident workgroups, 0: uncut)."""
     q = np.ascontiguousarray(q_lens, dtype=np.int32)
     L = np.ascontiguousarray(seq_lens, dtype=np.int32)
     dec = np.nonzero(q == 1)[0].astype(np.int32)
     split = build_decode_split(L[dec], num_slots, min_piece_tokens) if len(dec) else None
-    qp = np.where(q == 1, 0, q).astype(np.int32)
-    work = build_varlen_work(qp, L, num_kv_heads, group) if (qp > 0).any() else np.zeros((0, 4), np.int32)
-    return MixedPlan(dec, split, work)
+    chunks = build_chunk_work(q, L, num_kv_heads, group, chunk_slots, min_piece_tiles)
+    return MixedPlan(dec, split, chunks)
 
 
 def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,
@@ -488,3 +545,39 @@ def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_l
         _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads, d,
         block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(work), work.shape[0], _dptr(lse),
         _stream(stream)))
+
+
+def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,
+                                   merges, num_partials: int, workspace, num_kv_heads: int, block_size: int,
+                                   max_seq_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                                   lse=None, stream=None) -> None:
+    """Rows of the sequences with two or more new tokens. work: device int32 [n][8] and
+    merges: device int32 [m][4] (or None) from build_chunk_work, num_partials its slots,
+    workspace: device tensor of at least chunk_workspace_bytes (None when no slots); the
+    rest as for paged_attention_prefill_varlen."""
+    torch = _torch()
+    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work, merges, workspace, lse)
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [total_q][Hq][d] of one dtype")
+    T, Hq, d = q.shape
+    _check_plane(k_cache, v_cache, block_size, num_kv_heads, d)
+    B = seq_lens.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][W]")
+    if seq_lens.dtype != torch.int32 or cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (B + 1,):
+        raise ValueError("seq_lens int32 [B] and cu_seqlens_q int32 [B+1] expected")
+    if work.dtype != torch.int32 or work.dim() != 2 or work.shape[1] != 8:
+        raise ValueError("work must be int32 [n][8] (from build_chunk_work)")
+    nm = 0
+    if merges is not None:
+        if merges.dtype != torch.int32 or merges.dim() != 2 or merges.shape[1] != 4:
+            raise ValueError("merges must be int32 [m][4] (from build_chunk_work)")
+        nm = merges.shape[0]
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise ValueError("lse must be float32 [total_q][Hq]")
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().pkv_paged_attention_prefill_chunks(
+        _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+        _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads, d,
+        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(work), work.shape[0],
+        _dptr(merges), nm, num_partials, _dptr(workspace), wsb, _dptr(lse), _stream(stream)))

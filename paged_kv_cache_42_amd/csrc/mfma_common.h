@@ -45,7 +45,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // next wait for a load into a full drain. Hidden stores only ever add to the hardware
 // count, so every wait the pass computes for its loads stays sufficient. Store data
 // registers may be reused right after issue on this target (the pass itself inserts no
-// wait for that), and the end of the kernel makes the writes visible.
+// wait for that), and the end of the kernel makes the writes visible. One exception: a
+// store of more than 8 bytes reads its data registers late, so a vector ALU write to them
+// must wait two cycles; the hazard pass cannot see into inline assembly, so the 16-byte
+// store carries its own s_nop (without it the next instruction overwrote the data).
 __device__ __forceinline__ void store_b32_untracked(void* p, uint32_t v) {
   asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
@@ -55,7 +58,7 @@ __device__ __forceinline__ void store_b64_untracked(void* p, uint32_t lo, uint32
 }
 __device__ __forceinline__ void store_b128_untracked(void* p, float x, float y, float z, float w) {
   const u32x4_t v = {__float_as_uint(x), __float_as_uint(y), __float_as_uint(z), __float_as_uint(w)};
-  asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 
 // Input of one wave's streaming pass over the context of one (sequence, KV head).

@@ -1,0 +1,634 @@
+// paged_attention_prefill_chunks: the prefill chunks of a continuous-batching step (a
+// sequence's new tokens, with or without a cached prefix) over the paged KV cache.
+//
+// What a query row computes is the page-walk attention of "Project 17: Production
+// Serving: Continuous Batching and PagedAttention", "Step 6": new row i of a sequence
+// with q new tokens and seq_len L sits at position L - q + i and attends keys
+// 0 .. L - q + i (bottom-right causal alignment; the step's K/V already written). The
+// rows are those of the mixed batch of "Continuous Batching", "5. Technical
+// explanation", delimited by cu_seqlens ("6. Under the hood").
+//
+// gfx950 design (the MFMA-bound part of a mixed step; decode rows go to the split decode):
+//  * item = (sequence, KV head g, block of 128/G new tokens): 128 GQA-packed query rows
+//    (token, head), all G heads of g sharing each K/V tile. A workgroup of 4 waves takes
+//    an item, 32 rows per wave as two 16-row MFMA blocks, so every K and V fragment read
+//    from LDS feeds two MFMAs; two workgroups share a compute unit.
+//  * K/V tiles of 64 keys are staged in LDS (rows padded by 32 bytes) by the workgroup
+//    with coalesced 16-byte loads held two tiles ahead in registers; E4M3 rows are
+//    widened to bf16 on the way in. Block ids of a tile are scalar loads.
+//  * S^T = K.Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the packed
+//    queries as B): lane l holds row l%16 of its block for keys 4(l/16)+r of each
+//    16-key group. Online softmax per row (two shuffles for the tile maximum); masks only
+//    on tiles that reach a row's diagonal or the end of the keys.
+//  * O^T += V^T.P^T on v_mfma_f32_16x16x16_bf16 per 16 keys: the lane's own 4 rounded
+//    weights are its B fragment, V^T comes straight from one ds_read_b64_tr_b16.
+//    Accumulators are rescaled only when a row's maximum grows.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "mfma_common.h"
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using pkv::bf16x8_t;
+using pkv::f32x4_t;
+using pkv::lds_s16x4_t;
+using pkv::pack_bf16x2_rne;
+using pkv::s16x4_t;
+
+using pkv::bf16x2_t;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr bf16x2_t kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+constexpr int kRows = 128;         // query rows (token, head) of an item
+constexpr int kKeys = 64;          // keys per LDS tile
+constexpr int kWaves = 4;          // 32 rows each
+constexpr int kThreads = 64 * kWaves;
+
+struct ChunkArgs {
+  const uint16_t* q;      // [total_q][Hq][D] bf16
+  uint16_t* out;          // [total_q][Hq][D] bf16
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;
+  float* lse_out;         // [total_q][Hq], nullable
+  const int4* work;       // [n][2] int4: (seq, KV head, first new token, first key) (key end, slot, 0, 0)
+  float* ws_o;            // partials [slot][kRows][D] (normalised), then
+  float* ws_lse;          //   their log2-sum-exps [slot][kRows]
+  int num_slots;          // partials the workspace holds
+  int table_width;
+  int num_seqs;
+  int total_q;
+  int num_kv_heads;
+  int group;
+  int num_blocks;
+  int len_clamp;
+  float zscale;           // softmax scale * k_scale * log2(e)
+  float v_scale;
+};
+
+template <int D>
+struct Lds {
+  static constexpr int RS = D * 2 + 32;          // bytes per bf16 key row (padded)
+  static constexpr int kTile = kKeys * RS;       // one K or V tile
+  static constexpr int kBytes = 4 * kTile;       // K, V x double buffer
+};
+
+template <int CDT, int D, int BS>
+__global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
+  constexpr int RS = Lds<D>::RS;
+  constexpr int TILE = Lds<D>::kTile;
+  constexpr int CPK = D * EB / 16;                       // 16-byte chunks per key head row
+  constexpr int LPT = kKeys * CPK / kThreads;            // chunk loads per thread per plane
+  constexpr int NB = kKeys / BS;                         // blocks per tile
+  static_assert(kKeys * CPK % kThreads == 0 && LPT >= 1, "tile / workgroup shape");
+  static_assert(LPT <= 32, "mask word");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D>::kBytes];
+  typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
+
+  // ---- item (uniform): rows of (seq, KV head, block of new tokens) over keys
+  // [key_lo, key_end); slot >= 0: write a partial for the merge. A malformed item exits
+  // before any barrier.
+  const int4 it = a.work[2 * blockIdx.x];
+  const int4 it2 = a.work[2 * blockIdx.x + 1];
+  const int s = it.x;
+  const int g = it.y;
+  const int q0 = it.z;
+  const int slot = it2.y;
+  if (s < 0 || s >= a.num_seqs || g < 0 || g >= a.num_kv_heads || slot >= a.num_slots) return;
+  const int row0 = a.cu_q[s];
+  const int qs = a.cu_q[s + 1] - row0;
+  if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q || q0 < 0 || q0 >= qs) return;
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+  if (qs > L) return;
+  const int key_end = max(0, min(it2.x, L));
+  const int key_lo = it.w;
+  if (key_lo < 0 || key_lo % kKeys != 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * G;
+  const int pos0 = L - qs;                               // position of new token 0
+  const int ntok = min(kRows / G, qs - q0);
+
+  // ---- this wave's rows: block rb holds rows 32w + 16rb + hl -> token r / G, head r % G
+  int pos[2];
+  bool row_ok[2];
+  bf16x8_t qf[2][KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 32 * w + 16 * rb + hl;
+    const int tok = r / G;
+    row_ok[rb] = tok < ntok;
+    pos[rb] = pos0 + q0 + tok;
+    const uint16_t* qrow = a.q + (int64_t(row0 + q0 + min(tok, ntok - 1)) * Hq + int64_t(g) * G + r % G) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      if (!row_ok[rb]) v = make_uint4(0, 0, 0, 0);
+      qf[rb][kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // positions of the wave's first and last valid rows (uniform); -1: no valid row
+  const int tok_first = (32 * w) / G;
+  const int tok_last = min(ntok - 1, (32 * w + 31) / G);
+  const int wave_first = pos0 + q0 + tok_first;
+  const int wave_last = tok_first < ntok ? pos0 + q0 + tok_last : -1;
+
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4_t o[2][MT];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[rb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const cptr_i32 btc = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(s) * a.table_width);
+  const int64_t row_bytes = int64_t(Hkv) * D * EB;
+  const int64_t head_off = int64_t(g) * D * EB;
+  const int t_lo = key_lo / kKeys;                      // tiles [t_lo, t_hi)
+  const int t_hi = (key_end + kKeys - 1) / kKeys;
+
+  // Per-thread parts of the chunk addresses (the same in every tile): chunk i of this
+  // thread is 16 bytes of key kt[i] of the tile, which lies in the tile's block jb[i].
+  int kti[LPT], jb[LPT];
+  int64_t cpart[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + kThreads * i;
+    kti[i] = c / CPK;
+    jb[i] = kti[i] / BS;
+    cpart[i] = int64_t(kti[i] % BS) * row_bytes + head_off + 16 * (c % CPK);
+  }
+  const int64_t block_bytes = int64_t(BS) * row_bytes;
+
+  // Stage tile t into registers: every load is issued (clamped to byte 0 of the plane
+  // when out of range) so the waits of the ring stay partial. `keep` marks the real rows;
+  // all-ones (uniform) when every row of the tile is in the context and its blocks valid.
+  auto stage = [&](int t, uint4 (&ks)[LPT], uint4 (&vs)[LPT], uint32_t& keep) {
+    const int key0 = t * kKeys;
+    int blk[NB];
+    bool all_ok = key0 + kKeys <= key_end;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      blk[j] = key0 + j * BS < key_end ? btc[(key0 + j * BS) / BS] : -1;
+      all_ok = all_ok && blk[j] >= 0 && blk[j] < a.num_blocks;
+    }
+    keep = all_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      int b = blk[0];
+#pragma unroll
+      for (int j = 1; j < NB; ++j) b = jb[i] >= j ? blk[j] : b;
+      int64_t off = int64_t(b) * block_bytes + cpart[i];
+      if (!all_ok) {                                      // uniform: the tail tile, or a bad block id
+        const bool ok = (key0 + kti[i] < key_end) & (b >= 0) & (b < a.num_blocks);
+        off &= -int64_t(ok);                               // masked to byte 0 (a select became a branch)
+        keep |= ok ? (1u << i) : 0u;
+      }
+      asm volatile("" : "+v"(off));                        // keep the load unconditional
+      ks[i] = *reinterpret_cast<const uint4*>(a.kc + off);
+      vs[i] = *reinterpret_cast<const uint4*>(a.vc + off);
+    }
+  };
+  auto commit = [&](int buf, const uint4 (&ks)[LPT], const uint4 (&vs)[LPT], uint32_t keep) {
+    uint8_t* kt = smem + buf * 2 * TILE;
+    uint8_t* vt = kt + TILE;
+    const bool plain = keep == 0xffffffffu;                // uniform
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      uint4 k = ks[i], v = vs[i];
+      if (!plain) {
+        const uint32_t mk = (keep >> i) & 1u ? 0xffffffffu : 0u;
+        k = make_uint4(k.x & mk, k.y & mk, k.z & mk, k.w & mk);
+        v = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
+      }
+      const int ci = (tid + kThreads * i) % CPK;
+      if constexpr (CDT == PKV_BF16) {
+        *reinterpret_cast<uint4*>(kt + kti[i] * RS + 16 * ci) = k;
+        *reinterpret_cast<uint4*>(vt + kti[i] * RS + 16 * ci) = v;
+      } else {
+        *reinterpret_cast<uint4*>(kt + kti[i] * RS + 32 * ci) = pkv::fp8x8_to_bf16x8(k.x, k.y);
+        *reinterpret_cast<uint4*>(kt + kti[i] * RS + 32 * ci + 16) = pkv::fp8x8_to_bf16x8(k.z, k.w);
+        *reinterpret_cast<uint4*>(vt + kti[i] * RS + 32 * ci) = pkv::fp8x8_to_bf16x8(v.x, v.y);
+        *reinterpret_cast<uint4*>(vt + kti[i] * RS + 32 * ci + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+      }
+    }
+  };
+
+  // One 64-key tile from LDS buffer `buf`.
+  auto compute = [&](int t, int buf) {
+    const int key0 = t * kKeys;
+    if (key0 > wave_last) return;                          // uniform: every key is past every row
+    const uint8_t* kt = smem + buf * 2 * TILE;
+    const uint8_t* vt = kt + TILE;
+    // S^T blocks: sc[rb][kb] -> keys key0 + 16kb + 4grp + r of row block rb
+    f32x4_t sc[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sc[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + (16 * kb + hl) * RS + 2 * (32 * kk + 8 * grp));
+        sc[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], sc[0][kb], 0, 0, 0);
+        sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], sc[1][kb], 0, 0, 0);
+      }
+    }
+    // masks only where the tile reaches a row's diagonal or the end of the keys (uniform
+    // branch); inside it the mask is added to the raw score (0 or -inf), since a select
+    // around the scaled score was compiled into per-lane branches
+    const bool full = key0 + kKeys - 1 <= wave_first && key0 + kKeys <= key_end;
+    if (!full) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = key0 + 16 * kb + 4 * grp + r;
+            sc[rb][kb][r] += ((key <= pos[rb]) & (key < key_end)) ? 0.f : -INFINITY;
+          }
+    }
+    s16x4_t pf[2][4];                                      // [rb][kb]: B fragments of P^T
+    bool grow = false;
+    float alpha[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      // the scale is positive: the maximum of the raw scores, scaled once
+      float mx = fmaxf(fmaxf(sc[rb][0][0], sc[rb][0][1]), fmaxf(sc[rb][0][2], sc[rb][0][3]));
+#pragma unroll
+      for (int kb = 1; kb < 4; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[rb][kb][0], sc[rb][kb][1]), fmaxf(sc[rb][kb][2], sc[rb][kb][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[rb], mx * a.zscale);
+      grow |= mn > m[rb];
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      alpha[rb] = pkv::fast_exp2(m[rb] - mref);
+      m[rb] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t p01 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][0], a.zscale, -mref)),
+                                             pkv::fast_exp2(fmaf(sc[rb][kb][1], a.zscale, -mref)));
+        const uint32_t p23 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][2], a.zscale, -mref)),
+                                             pkv::fast_exp2(fmaf(sc[rb][kb][3], a.zscale, -mref)));
+        // the sum uses the same bf16-rounded weights that enter P.V (two per dot2)
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), kOnes, ps, false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), kOnes, ps, false);
+        // B operand of the 16-key product: lane l holds keys 4(l/16) + j, its own weights
+        pf[rb][kb] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+      }
+      lsum[rb] = lsum[rb] * alpha[rb] + ps;
+    }
+    // rescale the accumulators only when some row's maximum grew (alpha is 1 otherwise)
+    if (__any(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          o[rb][mt][0] *= alpha[rb];
+          o[rb][mt][1] *= alpha[rb];
+          o[rb][mt][2] *= alpha[rb];
+          o[rb][mt][3] *= alpha[rb];
+        }
+    }
+    // O^T[d][row] += V^T[d][key] . P^T[key][row] per 16-key group: V^T fragments straight
+    // from ds_read_b64_tr_b16 (rows 16kb + 4(l/16) + (l%16)/4), each feeding both row blocks
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint8_t* vsrc = vt + (16 * kb + 4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const s16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 32 * mt));
+        o[0][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[0][kb], o[0][mt], 0, 0, 0);
+        o[1][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[1][kb], o[1][mt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (t_lo < t_hi) {
+    // register ring of two tiles: tile t + 2 is issued before tile t is consumed; tiles
+    // past the end are staged clamped and masked, so every wait is a known partial count
+    uint4 k0[LPT], v0[LPT], k1[LPT], v1[LPT];
+    uint32_t keep0, keep1;
+    stage(t_lo, k0, v0, keep0);
+    stage(t_lo + 1, k1, v1, keep1);
+    commit(0, k0, v0, keep0);
+    __syncthreads();
+    for (int t = t_lo; t < t_hi; t += 2) {
+      stage(t + 2, k0, v0, keep0);
+      compute(t, 0);
+      commit(1, k1, v1, keep1);
+      __syncthreads();
+      stage(t + 3, k1, v1, keep1);
+      if (t + 1 < t_hi) compute(t + 1, 1);
+      commit(0, k0, v0, keep0);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float l = lsum[rb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!row_ok[rb]) continue;
+    const int r = 32 * w + 16 * rb + hl;
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    if (slot >= 0) {                                       // partial of a split item
+      float* prow = a.ws_o + (int64_t(slot) * kRows + r) * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        pkv::store_b128_untracked(prow + 16 * mt, o[rb][mt][0] * inv, o[rb][mt][1] * inv, o[rb][mt][2] * inv,
+                                  o[rb][mt][3] * inv);
+      if (grp == 0)
+        pkv::store_b32_untracked(a.ws_lse + int64_t(slot) * kRows + r,
+                                 __float_as_uint(l > 0.f ? m[rb] + log2f(l) : -INFINITY));
+      continue;
+    }
+    const int row = row0 + q0 + r / G;
+    const int hq = g * G + r % G;
+    uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t lo = pack_bf16x2_rne(o[rb][mt][0] * inv, o[rb][mt][1] * inv);
+      const uint32_t hi = pack_bf16x2_rne(o[rb][mt][2] * inv, o[rb][mt][3] * inv);
+      pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
+    }
+    if (a.lse_out && grp == 0)
+      pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + hq,
+                               __float_as_uint(l > 0.f ? (m[rb] + log2f(l)) * kLn2 : -INFINITY));
+  }
+}
+
+// Log-sum-exp merge of the partials of split items. Merge record: (seq, KV head,
+// first new token, first slot | pieces << 20). Thread task = (row of the 128, four
+// head_dim elements): M = max_k lse_k, out = sum_k 2^(lse_k - M) o_k / sum_k 2^(lse_k - M).
+template <int D>
+__global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int4* merges) {
+  const int4 mg = merges[blockIdx.x];
+  const int s = mg.x, g = mg.y, q0 = mg.z;
+  const int first = mg.w & 0xfffff, np = mg.w >> 20;
+  if (s < 0 || s >= a.num_seqs || g < 0 || g >= a.num_kv_heads || np < 1 || first < 0 || first + np > a.num_slots)
+    return;
+  const int row0 = a.cu_q[s];
+  const int qs = a.cu_q[s + 1] - row0;
+  if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q || q0 < 0 || q0 >= qs) return;
+  const int G = a.group;
+  const int Hq = a.num_kv_heads * G;
+  const int ntok = min(kRows / G, qs - q0);
+  constexpr int LPR = D / 4;                               // tasks per row
+  for (int task = threadIdx.x; task < kRows * LPR; task += 256) {
+    const int r = task / LPR;
+    const int e = 4 * (task % LPR);
+    if (r / G >= ntok) break;                              // rows are in token order
+    float M = -INFINITY;
+    for (int k = 0; k < np; ++k) M = fmaxf(M, a.ws_lse[int64_t(first + k) * kRows + r]);
+    const float mref = M == -INFINITY ? 0.f : M;
+    float S = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < np; ++k) {
+      const float wk = pkv::fast_exp2(a.ws_lse[int64_t(first + k) * kRows + r] - mref);
+      const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + (int64_t(first + k) * kRows + r) * D + e);
+      S += wk;
+      A.x = fmaf(wk, ok.x, A.x);
+      A.y = fmaf(wk, ok.y, A.y);
+      A.z = fmaf(wk, ok.z, A.z);
+      A.w = fmaf(wk, ok.w, A.w);
+    }
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    const int row = row0 + q0 + r / G;
+    const int hq = g * G + r % G;
+    uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + e;
+    *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2_rne(A.x * inv, A.y * inv), pack_bf16x2_rne(A.z * inv, A.w * inv));
+    if (a.lse_out && e == 0) a.lse_out[int64_t(row) * Hq + hq] = S > 0.f ? (M + log2f(S)) * kLn2 : -INFINITY;
+  }
+}
+
+using ChunkFn = void (*)(ChunkArgs);
+
+template <int CDT, int D>
+ChunkFn pick_bs(int BS) {
+  switch (BS) {
+    case 16: return chunk_kernel<CDT, D, 16>;
+    case 32: return chunk_kernel<CDT, D, 32>;
+    default: return nullptr;
+  }
+}
+
+template <int CDT>
+ChunkFn pick_d(int D, int BS) {
+  switch (D) {
+    case 64: return pick_bs<CDT, 64>(BS);
+    case 128: return pick_bs<CDT, 128>(BS);
+    default: return nullptr;
+  }
+}
+
+using MergeFn = void (*)(ChunkArgs, const int4*);
+
+MergeFn pick_merge(int D) {
+  switch (D) {
+    case 64: return chunk_merge_kernel<64>;
+    case 128: return chunk_merge_kernel<128>;
+    default: return nullptr;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+constexpr int kSlotBits = 20;                              // merge record: first slot | pieces << 20
+
+}  // namespace
+
+extern "C" int pkv_build_chunk_work(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
+                                    int32_t num_kv_heads, int32_t group, int32_t num_slots,
+                                    int32_t min_piece_tiles, int32_t* items,
+                                    int32_t capacity, int32_t* count, int32_t* merges, int32_t merge_capacity,
+                                    int32_t* merge_count, int32_t* num_partials) {
+  using pkv::fail;
+  if (num_seqs < 0 || num_kv_heads <= 0 || group <= 0 || !count || !merge_count || !num_partials ||
+      (num_seqs > 0 && (!q_lens || !seq_lens)))
+    return fail(PKV_ERR_INVALID, "build_chunk_work: bad arguments");
+  if (group > 16 || kRows % group != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "build_chunk_work: group %d not in {1,2,4,8,16}", group);
+  struct Item {
+    int32_t s, g, q0, key_lo, key_hi, slot, tiles;
+  };
+  std::vector<Item> v;
+  std::vector<int32_t> m;
+  const int32_t QB = kRows / group;
+  // cap on a piece: the tiles of all blocks spread evenly over the slots, at least
+  // min_piece_tiles (a smaller piece does not repay its partial and merge)
+  int64_t total = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t q = q_lens[s], L = seq_lens[s];
+    if (q < 0 || L < 0 || q > L) return fail(PKV_ERR_INVALID, "build_chunk_work: sequence %d q_len %d seq_len %d", s, q, L);
+    if (q < 2) continue;                                   // decode rows and idle sequences: not here
+    for (int32_t q0 = 0; q0 < q; q0 += QB)
+      total += (int64_t(std::min(L, L - q + std::min(q, q0 + QB))) + kKeys - 1) / kKeys * num_kv_heads;
+  }
+  const int64_t max_tiles = num_slots > 0 ? std::max<int64_t>({1, min_piece_tiles, (total + num_slots - 1) / num_slots})
+                                          : int64_t(1) << 40;
+  int64_t partials = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t q = q_lens[s], L = seq_lens[s];
+    if (q < 2) continue;
+    for (int32_t q0 = 0; q0 < q; q0 += QB) {
+      const int32_t keys = std::min(L, L - q + std::min(q, q0 + QB));   // through the block's last position
+      const int32_t tiles = (keys + kKeys - 1) / kKeys;
+      const int32_t np = tiles > max_tiles ? int32_t((tiles + max_tiles - 1) / max_tiles) : 1;
+      for (int32_t g = 0; g < num_kv_heads; ++g) {
+        if (np == 1) {
+          v.push_back({s, g, q0, 0, keys, -1, tiles});
+          continue;
+        }
+        if (partials + np >= (int64_t(1) << kSlotBits) || np >= (1 << (31 - kSlotBits)))
+          return fail(PKV_ERR_INVALID, "build_chunk_work: too many partials (%lld)", (long long)(partials + np));
+        m.insert(m.end(), {s, g, q0, int32_t(partials) | (np << kSlotBits)});
+        for (int32_t k = 0; k < np; ++k) {                // balanced pieces of whole tiles
+          const int32_t t0 = int32_t(int64_t(tiles) * k / np), t1 = int32_t(int64_t(tiles) * (k + 1) / np);
+          v.push_back({s, g, q0, t0 * kKeys, std::min(keys, t1 * kKeys), int32_t(partials + k), t1 - t0});
+        }
+        partials += np;
+      }
+    }
+  }
+  // longest first: an item costs about its tiles x 128 rows of MFMA work
+  std::stable_sort(v.begin(), v.end(), [](const Item& x, const Item& y) { return x.tiles > y.tiles; });
+  *count = int32_t(v.size());
+  *merge_count = int32_t(m.size() / 4);
+  *num_partials = int32_t(partials);
+  if (int64_t(v.size()) > capacity || (!v.empty() && !items))
+    return fail(PKV_ERR_INVALID, "build_chunk_work: %zu items, capacity %d", v.size(), capacity);
+  if (int64_t(m.size() / 4) > merge_capacity || (!m.empty() && !merges))
+    return fail(PKV_ERR_INVALID, "build_chunk_work: %zu merges, capacity %d", m.size() / 4, merge_capacity);
+  for (size_t i = 0; i < v.size(); ++i) {
+    const int32_t rec[8] = {v[i].s, v[i].g, v[i].q0, v[i].key_lo, v[i].key_hi, v[i].slot, 0, 0};
+    std::copy(rec, rec + 8, items + 8 * i);
+  }
+  std::copy(m.begin(), m.end(), merges);
+  return PKV_OK;
+}
+
+extern "C" int pkv_chunk_slots(int32_t cache_dtype, int32_t head_dim, int32_t block_size, int32_t* slots) {
+  using pkv::fail;
+  if (!slots) return fail(PKV_ERR_INVALID, "chunk_slots: slots is NULL");
+  ChunkFn fn = cache_dtype == PKV_BF16       ? pick_d<PKV_BF16>(head_dim, block_size)
+               : cache_dtype == PKV_FP8_E4M3 ? pick_d<PKV_FP8_E4M3>(head_dim, block_size)
+                                             : nullptr;
+  if (!fn)
+    return fail(PKV_ERR_UNSUPPORTED, "chunk_slots: unsupported (cache dtype %d, head_dim %d, block_size %d)",
+                cache_dtype, head_dim, block_size);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0) !=
+          hipSuccess)
+    return fail(PKV_ERR_HIP, "chunk_slots: occupancy query failed");
+  *slots = std::max(1, cus * std::max(per_cu, 1));
+  return PKV_OK;
+}
+
+extern "C" int64_t pkv_chunk_workspace_bytes(int32_t num_partials, int32_t head_dim) {
+  if (num_partials <= 0 || head_dim <= 0) return 0;
+  return int64_t(num_partials) * kRows * (head_dim + 1) * 4;
+}
+
+extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                                  const void* v_cache, int32_t cache_dtype,
+                                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                                  const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs,
+                                                  int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                                  int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                                  const int32_t* work_items, int32_t num_work,
+                                                  const int32_t* merges, int32_t num_merges, int32_t num_partials,
+                                                  void* workspace, int64_t workspace_bytes, float* lse_out,
+                                                  void* stream) {
+  using pkv::fail;
+  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
+      max_seq_len < 0 || num_work < 0 || num_merges < 0 || num_partials < 0 || num_partials >= (1 << kSlotBits))
+    return fail(PKV_ERR_INVALID, "prefill_chunks: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "prefill_chunks: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (q_dtype != PKV_BF16 || (cache_dtype != PKV_BF16 && cache_dtype != PKV_FP8_E4M3) || G > 16 || kRows % G != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill_chunks: unsupported (q dtype %d, cache dtype %d, group %d)", q_dtype,
+                cache_dtype, G);
+  ChunkFn fn = cache_dtype == PKV_BF16 ? pick_d<PKV_BF16>(head_dim, block_size)
+                                       : pick_d<PKV_FP8_E4M3>(head_dim, block_size);
+  if (!fn)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill_chunks: head_dim %d / block_size %d not supported", head_dim,
+                block_size);
+  if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(PKV_ERR_INVALID, "prefill_chunks: scales must be > 0");
+  if (num_work == 0 || num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "prefill_chunks: the cache has no blocks");
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seqlens_q || !work_items)
+    return fail(PKV_ERR_INVALID, "prefill_chunks: NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(work_items))
+    return fail(PKV_ERR_INVALID, "prefill_chunks: q, out, cache planes and work list must be 16-byte aligned");
+  if (num_merges > 0 && num_partials == 0) return fail(PKV_ERR_INVALID, "prefill_chunks: merges without partials");
+  if (num_partials > 0) {
+    if (!merges || !workspace || !aligned16(merges) || !aligned16(workspace))
+      return fail(PKV_ERR_INVALID, "prefill_chunks: split items need 16-byte aligned merges and workspace");
+    const int64_t need = pkv_chunk_workspace_bytes(num_partials, head_dim);
+    if (workspace_bytes < need)
+      return fail(PKV_ERR_INVALID, "prefill_chunks: workspace %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)need);
+  }
+  ChunkArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.vc = static_cast<const uint8_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_seqlens_q;
+  a.lse_out = lse_out;
+  a.work = reinterpret_cast<const int4*>(work_items);
+  a.num_slots = num_partials;
+  if (num_partials > 0) {
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = a.ws_o + int64_t(num_partials) * kRows * head_dim;
+  }
+  a.table_width = table_width;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_kv_heads = num_kv_heads;
+  a.group = G;
+  a.num_blocks = num_blocks;
+  const int64_t tcap = int64_t(table_width) * block_size;
+  a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
+  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
+  a.v_scale = v_scale;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(fn, dim3(num_work), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: launch failed: %s", hipGetErrorString(e));
+  if (num_merges > 0) {
+    hipLaunchKernelGGL(pick_merge(head_dim), dim3(num_merges), dim3(256), 0, st, a,
+                       reinterpret_cast<const int4*>(merges));
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: merge launch failed: %s", hipGetErrorString(e));
+  }
+  return PKV_OK;
+}

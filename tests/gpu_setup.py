@@ -253,16 +253,21 @@ def run_varlen(st: Step, lse: bool = True, max_seq_len=None):
     return out, lse_t
 
 
-def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_tokens: int = 0, lse: bool = True):
+def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_tokens: int = 0, lse: bool = True,
+                         chunk_slots: Optional[int] = None, min_piece_tiles: int = 0):
     """A mixed step as two launches: decode rows (one new token) by the balanced-split decode
-    with the batch's row map, prefill chunks by the varlen launch over prefill items only."""
+    with the batch's row map, the other rows by the chunk kernel (blocks cut along the keys
+    over chunk_slots resident workgroups, the device's count when None, 0: uncut)."""
     w = st.w
     T, Hq, d = w.total_q, w.num_q_heads, w.head_dim
     msl = int(w.seq_lens.max())
+    cdt = pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16
     if num_slots is None:
-        num_slots = pkv.decode_split_slots(pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16, w.num_kv_heads, d,
-                                           w.block_size)
-    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, w.num_kv_heads, w.group, num_slots, min_piece_tokens)
+        num_slots = pkv.decode_split_slots(cdt, w.num_kv_heads, d, w.block_size)
+    if chunk_slots is None:
+        chunk_slots = pkv.chunk_slots(cdt, d, w.block_size)
+    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, w.num_kv_heads, w.group, num_slots, min_piece_tokens,
+                              chunk_slots, min_piece_tiles)
     out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse_t = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
     if len(mp.decode_rows):
@@ -272,9 +277,11 @@ def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_to
                                          torch.from_numpy(mp.split.plan).cuda(), mp.split, w.num_kv_heads,
                                          w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, ws, lse_t,
                                          rows=torch.from_numpy(mp.decode_rows).cuda(), cu_seqlens_q=st.cu_d)
-    if len(mp.prefill_work):
-        pkv.paged_attention_prefill_varlen(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d,
-                                           torch.from_numpy(mp.prefill_work).cuda(), w.num_kv_heads, w.block_size,
-                                           msl, w.softmax_scale, w.k_scale, w.v_scale, lse=lse_t)
+    dev = mp.chunks.to_device(d)
+    if dev is not None:
+        work, merges, cws = dev
+        pkv.paged_attention_prefill_chunks(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d, work,
+                                           merges, mp.chunks.num_partials, cws, w.num_kv_heads, w.block_size, msl,
+                                           w.softmax_scale, w.k_scale, w.v_scale, lse=lse_t)
     torch.cuda.synchronize()
     return out, lse_t

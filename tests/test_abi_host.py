@@ -213,3 +213,63 @@ def test_balanced_split_plan_errors():
         _lib.check(pkv.lib().pkv_build_decode_split(2, L.ctypes.data_as(ctypes.c_void_p), 0, 4,
                                                     out.ctypes.data_as(ctypes.c_void_p), 3, ctypes.byref(c),
                                                     ctypes.byref(m)))
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 700), st.integers(0, 2500)), max_size=12), st.sampled_from([1, 2, 4, 8, 16]),
+       st.integers(1, 3), st.sampled_from([0, 1, 5, 64, 5000]), st.sampled_from([0, 1, 3]))
+def test_chunk_work_covers_every_row_block_and_key_once(pairs, G, Hkv, slots, min_tiles):
+    q = [min(a, b) for a, b in pairs]
+    L = [max(a, b) for a, b in pairs]
+    cp = pkv.build_chunk_work(q, L, Hkv, G, slots, min_tiles)
+    QB = 128 // G
+    # expected row blocks: (s, g, q0) -> keys through the block's last position
+    want = {}
+    for s, (qq, LL) in enumerate(zip(q, L)):
+        if qq < 2:
+            continue
+        for q0 in range(0, qq, QB):
+            for g in range(Hkv):
+                want[(s, g, q0)] = min(LL, LL - qq + min(qq, q0 + QB))
+    total = sum(-(-k // 64) for k in want.values())
+    cap = max(1, min_tiles, -(-total // slots)) if slots > 0 else None
+    it, mg = cp.items, cp.merges
+    assert it.shape[1] == 8 and mg.shape[1] == 4 and (it[:, 6:] == 0).all()
+    tiles = -(-(it[:, 4] - it[:, 3]) // 64)
+    assert (np.diff(tiles) <= 0).all()                       # most tiles first
+    got = {}
+    for s, g, q0, lo, hi, slot, _, _ in it.tolist():
+        assert lo % 64 == 0 and lo < hi or (lo == 0 and hi == 0)
+        got.setdefault((s, g, q0), []).append((lo, hi, slot))
+    assert set(got) == set(want)
+    merges = {(s, g, q0): (w & 0xfffff, w >> 20) for s, g, q0, w in mg.tolist()}
+    used = []
+    for key, pieces in got.items():
+        pieces.sort()
+        keys = want[key]
+        ntiles = -(-keys // 64)
+        assert pieces[0][0] == 0 and pieces[-1][1] == keys
+        assert all(a[1] == b[0] for a, b in zip(pieces, pieces[1:]))    # contiguous, disjoint
+        sizes = [-(-(hi - lo) // 64) for lo, hi, _ in pieces]
+        assert max(sizes) - min(sizes) <= 1
+        if len(pieces) == 1:
+            assert pieces[0][2] == -1 and key not in merges
+            assert cap is None or ntiles <= cap
+        else:
+            assert cap is not None and len(pieces) == -(-ntiles // cap) and max(sizes) <= cap
+            first, np_ = merges[key]
+            assert np_ == len(pieces) and [p[2] for p in pieces] == list(range(first, first + np_))
+            used += [p[2] for p in pieces]
+    assert len(merges) == sum(len(p) > 1 for p in got.values())
+    assert sorted(used) == list(range(cp.num_partials))
+    assert pkv.chunk_workspace_bytes(cp.num_partials, 128) == cp.num_partials * 128 * 129 * 4
+
+
+def test_chunk_work_errors():
+    with pytest.raises(pkv.PkvError):
+        pkv.build_chunk_work([5], [4], 1, 4)               # more new tokens than the sequence holds
+    with pytest.raises(pkv.PkvError):
+        pkv.build_chunk_work([5], [9], 1, 3)               # group 3 does not divide 128 rows
+    cp = pkv.build_chunk_work([0, 1, 1], [0, 7, 300], 2, 4, 64)
+    assert len(cp.items) == 0 and len(cp.merges) == 0 and cp.num_partials == 0
+    assert pkv.chunk_workspace_bytes(0, 128) == 0

@@ -17,7 +17,12 @@ pytestmark = pytest.mark.gpu
 LSE_ATOL = 2.0 ** -8   # weights enter P.V rounded to bf16 (see the decode tests)
 
 
-def _check(w, two_launch_slots=(None, 3)):
+# two-launch variants: (decode split slots, chunk slots, min piece tiles); None = the
+# device's resident count; 5000 chunk slots cut every block into single tiles
+TWO_LAUNCH = ((None, None, 0), (3, 5000, 0), (None, 7, 2), (None, 0, 0))
+
+
+def _check(w, two_launch=TWO_LAUNCH):
     st = build_step(w)
     tabs, bt, cu, slots, kp, vp = oracle_planes(st)
     assert (st.bt == bt).all() and (st.cu == cu).all() and (st.slots == slots).all()
@@ -27,11 +32,12 @@ def _check(w, two_launch_slots=(None, 3)):
     assert_close(out_f64(out), ref, dt, w.name)
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
     # the same step as two launches (split decode rows + prefill-only varlen)
-    for n in two_launch_slots:
-        o2, l2 = run_mixed_two_launch(st, num_slots=n)
+    for n, cs, mpt in two_launch:
+        o2, l2 = run_mixed_two_launch(st, num_slots=n, chunk_slots=cs, min_piece_tiles=mpt)
         got = out_f64(o2)
-        assert not np.isnan(got).any(), f"{w.name} two launches ({n} slots): unwritten rows"
-        assert_close(got, ref, dt, f"{w.name} two launches ({n} slots)")
+        tag = f"{w.name} two launches ({n} / {cs} / {mpt})"
+        assert not np.isnan(got).any(), f"{tag}: unwritten rows"
+        assert_close(got, ref, dt, tag)
         np.testing.assert_allclose(l2.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
     return st, out, lse
 

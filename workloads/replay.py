@@ -5,7 +5,7 @@ Benchmark and test infrastructure. Per step: the host scheduler admits, plans an
 updates (C ABI); the step's metadata goes to the device once for all layers; the Q/K/V
 of every new token of every layer are generated on the device by the counter-hash
 generator (outside the timed region), then each layer runs pkv_kv_cache_write, the
-balanced-split decode over the step's decode rows and the varlen launch over its prefill
+balanced-split decode over the step's decode rows and the chunk kernel over its prefill
 chunks, bracketed by HIP events per step."""
 from __future__ import annotations
 
@@ -60,6 +60,8 @@ class Replay:
         self.slots = pkv.decode_split_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.num_kv_heads,
                                             tr.head_dim, tr.block_size)
         self.min_piece = 256
+        self.chunk_slots = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim,
+                                           tr.block_size)
 
     def _values(self, ids, q_lens, seq_lens):
         """Generate Q/K/V of the step's new tokens for every layer into one buffer; return
@@ -104,9 +106,10 @@ class Replay:
         lens = torch.from_numpy(seq_lens).cuda()
         cu = torch.from_numpy(plan.cu_seqlens_q).cuda()
         slots = torch.from_numpy(plan.slot_mapping).cuda()
-        # decode rows by the balanced-split decode, prefill chunks by the varlen launch
-        mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, self.slots, self.min_piece)
-        work = torch.from_numpy(mp.prefill_work).cuda() if len(mp.prefill_work) else None
+        # decode rows by the balanced-split decode, prefill rows by the chunk kernel
+        mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, self.slots, self.min_piece,
+                                  self.chunk_slots)
+        chunk_dev = mp.chunks.to_device(tr.head_dim)
         if len(mp.decode_rows):
             rows = torch.from_numpy(mp.decode_rows).cuda()
             plan_d = torch.from_numpy(mp.split.plan).cuda()
@@ -126,10 +129,11 @@ class Replay:
                 pkv.paged_attention_decode_split(out, q, self.k_cache[l], self.v_cache[l], bt, lens, plan_d, mp.split,
                                                  tr.num_kv_heads, tr.block_size, msl, tr.softmax_scale, tr.k_scale,
                                                  tr.v_scale, ws, rows=rows, cu_seqlens_q=cu)
-            if work is not None:
-                pkv.paged_attention_prefill_varlen(out, q, self.k_cache[l], self.v_cache[l], bt, lens, cu, work,
-                                                   tr.num_kv_heads, tr.block_size, msl, tr.softmax_scale,
-                                                   tr.k_scale, tr.v_scale)
+            if chunk_dev is not None:
+                work, merges, cws = chunk_dev
+                pkv.paged_attention_prefill_chunks(out, q, self.k_cache[l], self.v_cache[l], bt, lens, cu, work,
+                                                   merges, mp.chunks.num_partials, cws, tr.num_kv_heads,
+                                                   tr.block_size, msl, tr.softmax_scale, tr.k_scale, tr.v_scale)
             if l in keep_layers:
                 kept[l] = out.clone()
         e1.record()
