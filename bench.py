@@ -207,13 +207,15 @@ def mixed_step(steps: int, warmup: int):
     ws = torch.empty(max(1, pkv.decode_split_workspace_bytes(len(mp.decode_rows), Hq, d, mp.split.max_pieces)),
                      dtype=torch.uint8, device="cuda")
 
-    def attention(mode):
+    def attention(mode, emid=None):
         if mode == "one_launch":
             pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, work, Hkv, w.block_size, msl,
                                                w.softmax_scale)
             return
         pkv.paged_attention_decode_split(out, q, kc, vc, bt_d, lens_d, plan_d, mp.split, Hkv, w.block_size, msl,
                                          w.softmax_scale, 1.0, 1.0, ws, rows=rows_d, cu_seqlens_q=cu_d)
+        if emid is not None:
+            emid.record(stream)
         cp, (cwork, cmerges, cws) = plans[mode]
         pkv.paged_attention_prefill_chunks(out, q, kc, vc, bt_d, lens_d, cu_d, cwork, cmerges, cp.chunks.num_partials,
                                            cws, Hkv, w.block_size, msl, w.softmax_scale)
@@ -224,7 +226,7 @@ def mixed_step(steps: int, warmup: int):
         pkv.kv_cache_write(nk, nv, kc, vc, slots_d, w.block_size)
         if e is not None:
             e[1].record(stream)
-        attention(mode)
+        attention(mode, None if e is None else e[3])
         if e is not None:
             e[2].record(stream)
 
@@ -239,7 +241,7 @@ def mixed_step(steps: int, warmup: int):
         for _ in range(warmup):
             step(two)
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
             step(two, ev[i])
@@ -247,9 +249,13 @@ def mixed_step(steps: int, warmup: int):
         wall = (time.perf_counter() - t0) / steps
         t_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
         t_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+        parts = {}
+        if two in ("uncut", "cut"):
+            parts = {"decode_rows": round(float(np.mean([e[1].elapsed_time(e[3]) for e in ev])) * 1e3, 2),
+                     "chunks": round(float(np.mean([e[3].elapsed_time(e[2]) for e in ev])) * 1e3, 2)}
         res[names[two]] = {
             "ms_per_step": round(wall * 1e3, 4),
-            "kernel_us": {"kv_cache_write": round(t_w * 1e6, 2), "attention": round(t_a * 1e6, 2)},
+            "kernel_us": {"kv_cache_write": round(t_w * 1e6, 2), "attention": round(t_a * 1e6, 2), **parts},
             "tokens_per_s": round(n_new / wall, 1),
             "hbm_GBps": round(nbytes / t_a / 1e9, 1), "hbm_frac": round(nbytes / t_a / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_TFLOPs": round(flops / t_a / 1e12, 1), "mfma_frac": round(flops / t_a / 1e12 / 2500.0, 4)}

@@ -276,8 +276,8 @@ int pkv_paged_attention_prefill_varlen(void* out, const void* q, int32_t q_dtype
  * q = q_lens[s] >= 2 new tokens and seq_len L = seq_lens[s] (host int32 arrays; q < 2 gives
  * nothing: decode rows go to the split decode), one row block per KV head g and per 128/G
  * new tokens q0.. (G = group), whose keys end at the block's last position + 1 ([P17]
- * "Step 6", causal). With T the 64-key tiles of all blocks and num_slots > 0 (the
- * workgroups resident at once, pkv_chunk_slots), a block of more than
+ * "Step 6", causal). With T the 64-key tiles of all blocks and num_slots > 0 (for
+ * instance pkv_chunk_slots), a block of more than
  * max_tiles = max(1, min_piece_tiles, ceil(T / num_slots)) tiles is cut into
  * np = ceil(tiles / max_tiles) pieces of whole tiles whose sizes differ by at most one
  * tile (num_slots <= 0: nothing is cut); each piece writes a partial into its own workspace slot and one merge
@@ -294,10 +294,10 @@ int pkv_build_chunk_work(int32_t num_seqs, const int32_t* q_lens, const int32_t*
                          int32_t capacity, int32_t* count, int32_t* merges, int32_t merge_capacity,
                          int32_t* merge_count, int32_t* num_partials);
 
-/* Chunk-kernel workgroups resident on the current device at once (compute units x
- * workgroups per unit for this cache dtype / head_dim / block_size): the num_slots of
- * pkv_build_chunk_work. UNSUPPORTED for a shape the kernel does not cover, HIP if the
- * occupancy query fails. */
+/* Slots to balance chunk work over on the current device (its compute units: a second
+ * resident workgroup shares a unit's issue slots, so it adds little throughput): the
+ * num_slots of pkv_build_chunk_work. UNSUPPORTED for a cache dtype / head_dim /
+ * block_size the kernel does not cover, HIP if the device query fails. */
 int pkv_chunk_slots(int32_t cache_dtype, int32_t head_dim, int32_t block_size, int32_t* slots);
 
 /* Device workspace bytes for num_partials slots of pkv_build_chunk_work's split pieces

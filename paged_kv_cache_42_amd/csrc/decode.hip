@@ -421,6 +421,8 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
   }
 }
 
+constexpr int kMergeFast = 4;      // pieces merged with all loads in flight at once
+
 // Log-sum-exp merge of the partition partials. A workgroup of 4 waves takes HW query
 // heads of one sequence; D/4 lanes own one head, 4 consecutive head_dim elements each
 // (16-byte loads): M = max_k lse_k, out = sum_k 2^(lse_k - M) o_k / sum_k 2^(lse_k - M).
@@ -459,22 +461,46 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   }
   if (nparts <= 1) return;                    // written directly by the partition pass
   const int64_t base = (int64_t(s) * num_q_heads + hq) * a.pmax;
-  // pass 1: the maximum log-sum-exp; pass 2: independent weighted loads (unrolled)
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_lse[base + k]);
-  const float mref = M == -INFINITY ? 0.f : M;
-  float S = 0.f;
+  float M = -INFINITY, S = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (nparts <= kMergeFast) {
+    // few pieces (the usual case): every load issued at once, one memory round trip;
+    // slots past nparts re-read piece 0 and are dropped
+    float lse[kMergeFast];
+    float4 ov[kMergeFast];
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k) {
+      const int64_t pi = base + (k < nparts ? k : 0);
+      lse[k] = a.ws_lse[pi];
+      ov[k] = *reinterpret_cast<const float4*>(a.ws_o + pi * D + e);
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k) M = k < nparts ? fmaxf(M, lse[k]) : M;
+    const float mref = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k) {
+      const float wk = k < nparts ? pkv::fast_exp2(lse[k] - mref) : 0.f;   // 0 for an empty piece
+      S += wk;
+      A.x = fmaf(wk, ov[k].x, A.x);
+      A.y = fmaf(wk, ov[k].y, A.y);
+      A.z = fmaf(wk, ov[k].z, A.z);
+      A.w = fmaf(wk, ov[k].w, A.w);
+    }
+  } else {
+    // pass 1: the maximum log-sum-exp; pass 2: independent weighted loads (unrolled)
+#pragma unroll 8
+    for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_lse[base + k]);
+    const float mref = M == -INFINITY ? 0.f : M;
 #pragma unroll 4
-  for (int k = 0; k < nparts; ++k) {
-    const float wk = pkv::fast_exp2(a.ws_lse[base + k] - mref);   // 0 for an empty partition
-    const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + (base + k) * D + e);
-    S += wk;
-    A.x = fmaf(wk, ok.x, A.x);
-    A.y = fmaf(wk, ok.y, A.y);
-    A.z = fmaf(wk, ok.z, A.z);
-    A.w = fmaf(wk, ok.w, A.w);
+    for (int k = 0; k < nparts; ++k) {
+      const float wk = pkv::fast_exp2(a.ws_lse[base + k] - mref);   // 0 for an empty partition
+      const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + (base + k) * D + e);
+      S += wk;
+      A.x = fmaf(wk, ok.x, A.x);
+      A.y = fmaf(wk, ok.y, A.y);
+      A.z = fmaf(wk, ok.z, A.z);
+      A.w = fmaf(wk, ok.w, A.w);
+    }
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const float r[4] = {A.x * inv, A.y * inv, A.z * inv, A.w * inv};

@@ -13,16 +13,18 @@
 //    (token, head), all G heads of g sharing each K/V tile. A workgroup of 4 waves takes
 //    an item, 32 rows per wave as two 16-row MFMA blocks, so every K and V fragment read
 //    from LDS feeds two MFMAs; two workgroups share a compute unit.
-//  * K/V tiles of 64 keys are staged in LDS (rows padded by 32 bytes) by the workgroup
-//    with coalesced 16-byte loads held two tiles ahead in registers; E4M3 rows are
-//    widened to bf16 on the way in. Block ids of a tile are scalar loads.
+//  * K/V tiles of 64 keys are staged in two LDS buffers (rows padded by 32 bytes) by the
+//    workgroup with coalesced 16-byte loads, the next tile held in registers while the
+//    current one is computed; E4M3 rows are widened to bf16 on the way in. Block ids of a
+//    tile are scalar loads.
 //  * S^T = K.Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the packed
 //    queries as B): lane l holds row l%16 of its block for keys 4(l/16)+r of each
 //    16-key group. Online softmax per row (two shuffles for the tile maximum); masks only
 //    on tiles that reach a row's diagonal or the end of the keys.
-//  * O^T += V^T.P^T on v_mfma_f32_16x16x16_bf16 per 16 keys: the lane's own 4 rounded
-//    weights are its B fragment, V^T comes straight from one ds_read_b64_tr_b16.
-//    Accumulators are rescaled only when a row's maximum grows.
+//  * O^T += V^T.P^T on v_mfma_f32_16x16x32_bf16 per 32 keys: the lane's own 8 rounded
+//    weights (two 16-key groups) are its B fragment, V^T comes straight from two
+//    ds_read_b64_tr_b16 at the same keys. The softmax reference maximum is lazy: it moves
+//    (and the accumulators are rescaled) only when a row's maximum grows by more than 2^8.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,6 +46,7 @@ using pkv::s16x4_t;
 using pkv::bf16x2_t;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr bf16x2_t kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+constexpr float kLazy = 8.f;       // log2 headroom of the lazy softmax maximum
 constexpr int kRows = 128;         // query rows (token, head) of an item
 constexpr int kKeys = 64;          // keys per LDS tile
 constexpr int kWaves = 4;          // 32 rows each
@@ -237,17 +240,35 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
     const uint8_t* kt = smem + buf * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     // S^T blocks: sc[rb][kb] -> keys key0 + 16kb + 4grp + r of row block rb
+    // the K fragments of 16-key group kb + 1 are read while group kb is on the MFMAs
     f32x4_t sc[2][4];
+    bf16x8_t kf[2][KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      kf[0][kk] = *reinterpret_cast<const bf16x8_t*>(kt + hl * RS + 2 * (32 * kk + 8 * grp));
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      if (kb + 1 < 4) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          kf[(kb + 1) & 1][kk] =
+              *reinterpret_cast<const bf16x8_t*>(kt + (16 * (kb + 1) + hl) * RS + 2 * (32 * kk + 8 * grp));
+      }
       sc[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       sc[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + (16 * kb + hl) * RS + 2 * (32 * kk + 8 * grp));
-        sc[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], sc[0][kb], 0, 0, 0);
-        sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], sc[1][kb], 0, 0, 0);
+        sc[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb & 1][kk], qf[0][kk], sc[0][kb], 0, 0, 0);
+        sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb & 1][kk], qf[1][kk], sc[1][kb], 0, 0, 0);
       }
+    }
+    // keep that order through the scheduler (left alone, it pulls every read down to
+    // just before its MFMA and the wave waits out the LDS latency each time)
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);          // LDS reads, group 0
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // reads of group kb + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // MFMAs of group kb
     }
     // masks only where the tile reaches a row's diagonal or the end of the keys (uniform
     // branch); inside it the mask is added to the raw score (0 or -inf), since a select
@@ -264,9 +285,12 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
             sc[rb][kb][r] += ((key <= pos[rb]) & (key < key_end)) ? 0.f : -INFINITY;
           }
     }
-    s16x4_t pf[2][4];                                      // [rb][kb]: B fragments of P^T
-    bool grow = false;
-    float alpha[2];
+    // Lazy maximum: a row's reference moves only when the tile holds a score above it by
+    // more than kLazy (log2 units), so weights stay below 2^kLazy; the sum and the output
+    // share the reference, so the result is the same. Each lane first checks its own 16
+    // scores per row block; only when some lane of the wave sees such a score (the first
+    // tile, then rarely) is the row maximum reduced across lanes and the state rescaled.
+    float lm[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       // the scale is positive: the maximum of the raw scores, scaled once
@@ -274,13 +298,32 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int kb = 1; kb < 4; ++kb)
         mx = fmaxf(mx, fmaxf(fmaxf(sc[rb][kb][0], sc[rb][kb][1]), fmaxf(sc[rb][kb][2], sc[rb][kb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[rb], mx * a.zscale);
-      grow |= mn > m[rb];
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      alpha[rb] = pkv::fast_exp2(m[rb] - mref);
-      m[rb] = mn;
+      lm[rb] = mx * a.zscale;
+    }
+    if (__any((lm[0] > m[0] + kLazy) | (lm[1] > m[1] + kLazy))) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float mx = lm[rb];
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool up = mx > m[rb] + kLazy;                // false while the row has no key
+        const float mn = up ? mx : m[rb];
+        const float alpha = up ? pkv::fast_exp2(m[rb] - mn) : 1.f;
+        m[rb] = mn;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          o[rb][mt][0] *= alpha;
+          o[rb][mt][1] *= alpha;
+          o[rb][mt][2] *= alpha;
+          o[rb][mt][3] *= alpha;
+        }
+      }
+    }
+    uint32_t pw[2][4][2];                                  // [rb][kb]: rounded weights, 2 per word
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -291,54 +334,60 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
         // the sum uses the same bf16-rounded weights that enter P.V (two per dot2)
         ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), kOnes, ps, false);
         ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), kOnes, ps, false);
-        // B operand of the 16-key product: lane l holds keys 4(l/16) + j, its own weights
-        pf[rb][kb] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+        pw[rb][kb][0] = p01;
+        pw[rb][kb][1] = p23;
       }
-      lsum[rb] = lsum[rb] * alpha[rb] + ps;
+      lsum[rb] += ps;
     }
-    // rescale the accumulators only when some row's maximum grew (alpha is 1 otherwise)
-    if (__any(grow)) {
+    // O^T[d][row] += V^T[d][key] . P^T[key][row] per 32 keys on the 16x16x32 MFMA. The
+    // contraction slots of lane l are 8(l/16) .. +7; they take keys 32j + 4(l/16) + r and
+    // 32j + 16 + 4(l/16) + r (r < 4) - the lane's own weights of 16-key groups 2j and 2j+1 -
+    // and the A operand takes V^T at the same keys: two ds_read_b64_tr_b16 (rows
+    // 16kb + 4(l/16) + (l%16)/4) per fragment, each fragment feeding both row blocks.
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          o[rb][mt][0] *= alpha[rb];
-          o[rb][mt][1] *= alpha[rb];
-          o[rb][mt][2] *= alpha[rb];
-          o[rb][mt][3] *= alpha[rb];
-        }
-    }
-    // O^T[d][row] += V^T[d][key] . P^T[key][row] per 16-key group: V^T fragments straight
-    // from ds_read_b64_tr_b16 (rows 16kb + 4(l/16) + (l%16)/4), each feeding both row blocks
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const uint8_t* vsrc = vt + (16 * kb + 4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* vsrc = vt + (32 * j + 4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+      const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0][2 * j][0], pw[0][2 * j][1],
+                                                                     pw[0][2 * j + 1][0], pw[0][2 * j + 1][1]));
+      const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[1][2 * j][0], pw[1][2 * j][1],
+                                                                     pw[1][2 * j + 1][0], pw[1][2 * j + 1][1]));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const s16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 32 * mt));
-        o[0][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[0][kb], o[0][mt], 0, 0, 0);
-        o[1][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[1][kb], o[1][mt], 0, 0, 0);
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 32 * mt));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vsrc + 16 * RS + 32 * mt));
+        const uint2 u0 = __builtin_bit_cast(uint2, v0), u1 = __builtin_bit_cast(uint2, v1);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+        o[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb0, o[0][mt], 0, 0, 0);
+        o[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb1, o[1][mt], 0, 0, 0);
       }
+    }
+    // V reads run four fragments ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int f = 0; f < 2 * MT; ++f) {
+      if (f + 4 < 2 * MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
     }
   };
 
   if (t_lo < t_hi) {
-    // register ring of two tiles: tile t + 2 is issued before tile t is consumed; tiles
-    // past the end are staged clamped and masked, so every wait is a known partial count
-    uint4 k0[LPT], v0[LPT], k1[LPT], v1[LPT];
-    uint32_t keep0, keep1;
-    stage(t_lo, k0, v0, keep0);
-    stage(t_lo + 1, k1, v1, keep1);
-    commit(0, k0, v0, keep0);
+    // Two LDS buffers, one register stage: tile t + 1 is loaded into registers while tile
+    // t is computed, then written to the buffer tile t - 1 used (free once every wave has
+    // passed the barrier after t - 1). Tiles past the end are staged clamped and masked.
+    uint4 kr[LPT], vr[LPT];
+    uint32_t keep;
+    stage(t_lo, kr, vr, keep);
+    commit(0, kr, vr, keep);
+    stage(t_lo + 1, kr, vr, keep);
     __syncthreads();
     for (int t = t_lo; t < t_hi; t += 2) {
-      stage(t + 2, k0, v0, keep0);
       compute(t, 0);
-      commit(1, k1, v1, keep1);
+      commit(1, kr, vr, keep);
+      stage(t + 2, kr, vr, keep);
       __syncthreads();
-      stage(t + 3, k1, v1, keep1);
       if (t + 1 < t_hi) compute(t + 1, 1);
-      commit(0, k0, v0, keep0);
+      commit(0, kr, vr, keep);
+      stage(t + 3, kr, vr, keep);
       __syncthreads();
     }
   }
@@ -536,13 +585,15 @@ extern "C" int pkv_chunk_slots(int32_t cache_dtype, int32_t head_dim, int32_t bl
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED, "chunk_slots: unsupported (cache dtype %d, head_dim %d, block_size %d)",
                 cache_dtype, head_dim, block_size);
-  int dev = 0, cus = 0, per_cu = 0;
+  // One item per compute unit: a second workgroup on the unit shares its issue slots and
+  // roughly halves the speed of both, so balancing over more slots than units only adds
+  // pieces (measured on the 4 x 512-token chunk step: pieces of 17 tiles over 512 slots
+  // ran slower than uncut items of up to 32 tiles).
+  int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0) !=
-          hipSuccess)
-    return fail(PKV_ERR_HIP, "chunk_slots: occupancy query failed");
-  *slots = std::max(1, cus * std::max(per_cu, 1));
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(PKV_ERR_HIP, "chunk_slots: device query failed");
+  *slots = std::max(1, cus);
   return PKV_OK;
 }
 
