@@ -13,21 +13,21 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// 8 E4M3 codes (two words) -> 8 bf16 (exact: every E4M3 value is a bf16 value).
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t src = j < 2 ? lo : hi;
-    const uint32_t sh = 16 * (j & 1);
-    const uint32_t a = __float_as_uint(pkv::fp8_to_f32(src >> sh)) >> 16;
-    const uint32_t b = __float_as_uint(pkv::fp8_to_f32(src >> (sh + 8))) >> 16;
-    w[j] = a | (b << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes (two words) -> 8 bf16, code j of the 8 bytes -> element j. Exact: every
+// E4M3 value is a bf16 value. v_cvt_scalef32_pk_bf16_fp8 with scale 1 widens the two
+// codes of one 16-bit half per instruction (OCP E4M3 on this target; it agrees with the
+// bit-level decode pkv::fp8_to_f32 on all 256 codes, NaN codes giving NaN).
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool high_half) {
+  const bf16x2_t v = high_half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                               : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  return make_uint4(fp8x2_to_bf16x2(lo, false), fp8x2_to_bf16x2(lo, true), fp8x2_to_bf16x2(hi, false),
+                    fp8x2_to_bf16x2(hi, true));
+}
 
 // Two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
