@@ -288,8 +288,13 @@ def measured_traffic(partition: int, workload: str, decode: str):
     if workload != "cfg3" or not os.path.exists(rec):
         return None
     r = json.load(open(rec))
-    src = os.path.join(here, r["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != r["source_sha256"]:
+    h = hashlib.sha256()
+    for f in r.get("sources", [r.get("source", "")]):          # the kernel's file and its headers
+        src = os.path.join(here, f)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != r.get("sources_sha256", r.get("source_sha256")):
         return None
     if r.get("partition_size", 512) != partition or r.get("decode", "partition") != decode:
         return None

@@ -437,13 +437,18 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   int nparts;
   int orow_idx = s;
   if (a.plan) {
-    // balanced split: pieces = slots that the sequence's tiles touch
-    int b;
-    split_row(a, s, b, orow_idx);
-    if (orow_idx < 0) return;
-    const int c0 = a.plan[s], c1 = a.plan[s + 1];
+    // balanced split: pieces = slots that the sequence's tiles touch. The output row
+    // (a row map lookup) is resolved after the partials' loads are issued, so the two
+    // memory round trips overlap.
+    typedef __attribute__((address_space(4))) const int32_t* cptr;
+    const cptr plan = (cptr)(uintptr_t)(a.plan);
+    const int c0 = plan[s], c1 = plan[s + 1];
     nparts = c1 > c0 && c0 >= 0 ? (c1 - 1) / a.tiles_per_slot - c0 / a.tiles_per_slot + 1 : 0;
+    if (nparts == 1) return;                  // written directly by the split pass
     if (nparts == 0) {                        // no context: zero output (no piece wrote it)
+      int b;
+      split_row(a, s, b, orow_idx);
+      if (orow_idx < 0) return;
       const int64_t oi = (int64_t(orow_idx) * num_q_heads + hq) * D + e;
       if constexpr (QDT == PKV_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -501,6 +506,11 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
       A.z = fmaf(wk, ok.z, A.z);
       A.w = fmaf(wk, ok.w, A.w);
     }
+  }
+  if (a.plan) {
+    int b;
+    split_row(a, s, b, orow_idx);
+    if (orow_idx < 0) return;
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const float r[4] = {A.x * inv, A.y * inv, A.z * inv, A.w * inv};

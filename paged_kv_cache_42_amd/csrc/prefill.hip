@@ -427,8 +427,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
 }
 
 // Log-sum-exp merge of the partials of split items. Merge record: (seq, KV head,
-// first new token, first slot | pieces << 20). Thread task = (row of the 128, four
-// head_dim elements): M = max_k lse_k, out = sum_k 2^(lse_k - M) o_k / sum_k 2^(lse_k - M).
+// first new token, first slot | pieces << 20). One thread per (row of the 128, four
+// head_dim elements), blockIdx.y picking 256 of them, so every load of a thread is issued
+// at once: M = max_k lse_k, out = sum_k 2^(lse_k - M) o_k / sum_k 2^(lse_k - M).
+constexpr int kChunkMergeFast = 4;   // pieces merged with all loads in flight at once
+
 template <int D>
 __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int4* merges) {
   const int4 mg = merges[blockIdx.x];
@@ -436,22 +439,37 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
   const int first = mg.w & 0xfffff, np = mg.w >> 20;
   if (s < 0 || s >= a.num_seqs || g < 0 || g >= a.num_kv_heads || np < 1 || first < 0 || first + np > a.num_slots)
     return;
-  const int row0 = a.cu_q[s];
-  const int qs = a.cu_q[s + 1] - row0;
-  if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q || q0 < 0 || q0 >= qs) return;
-  const int G = a.group;
-  const int Hq = a.num_kv_heads * G;
-  const int ntok = min(kRows / G, qs - q0);
-  constexpr int LPR = D / 4;                               // tasks per row
-  for (int task = threadIdx.x; task < kRows * LPR; task += 256) {
-    const int r = task / LPR;
-    const int e = 4 * (task % LPR);
-    if (r / G >= ntok) break;                              // rows are in token order
-    float M = -INFINITY;
+  constexpr int LPR = D / 4;                               // threads per row
+  const int task = blockIdx.y * 256 + threadIdx.x;
+  const int r = task / LPR;
+  const int e = 4 * (task % LPR);
+  if (r >= kRows) return;
+  float M = -INFINITY, S = 0.f;
+  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (np <= kChunkMergeFast) {
+    float lse[kChunkMergeFast];
+    float4 ov[kChunkMergeFast];
+#pragma unroll
+    for (int k = 0; k < kChunkMergeFast; ++k) {             // slots past np re-read piece 0
+      const int64_t sl = first + (k < np ? k : 0);
+      lse[k] = a.ws_lse[sl * kRows + r];
+      ov[k] = *reinterpret_cast<const float4*>(a.ws_o + (sl * kRows + r) * D + e);
+    }
+#pragma unroll
+    for (int k = 0; k < kChunkMergeFast; ++k) M = k < np ? fmaxf(M, lse[k]) : M;
+    const float mref = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int k = 0; k < kChunkMergeFast; ++k) {
+      const float wk = k < np ? pkv::fast_exp2(lse[k] - mref) : 0.f;
+      S += wk;
+      A.x = fmaf(wk, ov[k].x, A.x);
+      A.y = fmaf(wk, ov[k].y, A.y);
+      A.z = fmaf(wk, ov[k].z, A.z);
+      A.w = fmaf(wk, ov[k].w, A.w);
+    }
+  } else {
     for (int k = 0; k < np; ++k) M = fmaxf(M, a.ws_lse[int64_t(first + k) * kRows + r]);
     const float mref = M == -INFINITY ? 0.f : M;
-    float S = 0.f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < np; ++k) {
       const float wk = pkv::fast_exp2(a.ws_lse[int64_t(first + k) * kRows + r] - mref);
       const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + (int64_t(first + k) * kRows + r) * D + e);
@@ -461,13 +479,20 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
       A.z = fmaf(wk, ok.z, A.z);
       A.w = fmaf(wk, ok.w, A.w);
     }
-    const float inv = S > 0.f ? 1.f / S : 0.f;
-    const int row = row0 + q0 + r / G;
-    const int hq = g * G + r % G;
-    uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + e;
-    *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2_rne(A.x * inv, A.y * inv), pack_bf16x2_rne(A.z * inv, A.w * inv));
-    if (a.lse_out && e == 0) a.lse_out[int64_t(row) * Hq + hq] = S > 0.f ? (M + log2f(S)) * kLn2 : -INFINITY;
   }
+  // the row's place in the batch (rows of a block are in token order)
+  const int row0 = a.cu_q[s];
+  const int qs = a.cu_q[s + 1] - row0;
+  if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q || q0 < 0 || q0 >= qs) return;
+  const int G = a.group;
+  if (r / G >= min(kRows / G, qs - q0)) return;
+  const int Hq = a.num_kv_heads * G;
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  const int row = row0 + q0 + r / G;
+  const int hq = g * G + r % G;
+  uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + e;
+  *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2_rne(A.x * inv, A.y * inv), pack_bf16x2_rne(A.z * inv, A.w * inv));
+  if (a.lse_out && e == 0) a.lse_out[int64_t(row) * Hq + hq] = S > 0.f ? (M + log2f(S)) * kLn2 : -INFINITY;
 }
 
 using ChunkFn = void (*)(ChunkArgs);
@@ -676,7 +701,7 @@ extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int3
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: launch failed: %s", hipGetErrorString(e));
   if (num_merges > 0) {
-    hipLaunchKernelGGL(pick_merge(head_dim), dim3(num_merges), dim3(256), 0, st, a,
+    hipLaunchKernelGGL(pick_merge(head_dim), dim3(num_merges, kRows * (head_dim / 4) / 256), dim3(256), 0, st, a,
                        reinterpret_cast<const int4*>(merges));
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: merge launch failed: %s", hipGetErrorString(e));

@@ -34,7 +34,7 @@ class StepRecord:
 
 
 class Replay:
-    def __init__(self, tr: workloads.Trace):
+    def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0):
         import torch
         self.torch = torch
         self.tr = tr
@@ -61,7 +61,8 @@ class Replay:
                                             tr.head_dim, tr.block_size)
         self.min_piece = 256
         self.chunk_slots = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim,
-                                           tr.block_size)
+                                           tr.block_size) if chunk_cut else 0
+        self.min_piece_tiles = min_piece_tiles
 
     def _values(self, ids, q_lens, seq_lens):
         """Generate Q/K/V of the step's new tokens for every layer into one buffer; return
@@ -108,7 +109,7 @@ class Replay:
         slots = torch.from_numpy(plan.slot_mapping).cuda()
         # decode rows by the balanced-split decode, prefill rows by the chunk kernel
         mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, self.slots, self.min_piece,
-                                  self.chunk_slots)
+                                  self.chunk_slots, self.min_piece_tiles)
         chunk_dev = mp.chunks.to_device(tr.head_dim)
         if len(mp.decode_rows):
             rows = torch.from_numpy(mp.decode_rows).cuda()
@@ -147,11 +148,11 @@ class Replay:
                           (e0, e1), kept, plan if keep_plan else None)
 
 
-def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progress=None):
+def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progress=None, **replay_args):
     """Replay the trace (or its first max_steps steps). keep: {step: layers} whose outputs
-    (and plans) are kept. Returns (records, summary)."""
+    (and plans) are kept; replay_args go to Replay. Returns (records, summary)."""
     import torch
-    rp = Replay(tr)
+    rp = Replay(tr, **replay_args)
     recs: List[StepRecord] = []
     keep = keep or {}
     t0 = time.perf_counter()
