@@ -87,6 +87,29 @@ def probe_read(mib: int, steps: int) -> None:
                       "unroll": best[2]}), flush=True)
 
 
+def measured_read_peak() -> float:
+    """Best stream-read rate of a 1 GiB buffer over a few launch shapes (GB/s): the
+    achievable read bandwidth the decode rate is also compared with."""
+    import torch
+    import workloads.gpu as wgen
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    best = 0.0
+    for blocks, unroll in [(b, u) for b in (256, 512, 1024, 2048, 4096, 8192) for u in (1, 2, 4, 8)]:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        wgen.read_probe(buf, blocks, unroll, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            wgen.read_probe(buf, blocks, unroll, out)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, buf.numel() / (e0.elapsed_time(e1) * 1e-3 / 10) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
 def probe_copy(mib: int, steps: int, warmup: int) -> None:
     import torch
     n = mib * (1 << 20)
@@ -141,8 +164,10 @@ def mixed_bytes_flops(w):
 
 
 def mixed_step(steps: int, warmup: int):
-    """Config-2 mixed continuous-batching step: cache write of the 2096 new tokens, then
-    one varlen launch over 48 decode rows and 4 prefill chunks of 512 (causal)."""
+    """Config-2 mixed continuous-batching step: cache write of the 2096 new tokens, then the
+    attention of 48 decode rows and 4 prefill chunks of 512 (causal), as one varlen launch
+    or as split decode rows + the chunk kernel. Each timed step follows a 512 MiB cache
+    flush; times are HIP events (write + attention), tokens/s = query tokens / that time."""
     import numpy as np
     import torch
     import paged_kv_cache_42_amd as pkv
@@ -237,16 +262,22 @@ def mixed_step(steps: int, warmup: int):
            "attention_bytes": nbytes, "attention_flops": flops}
     names = {"one_launch": "one_launch", "uncut": "split_decode_plus_chunks_uncut",
              "cut": "split_decode_plus_chunks"}
+    # the step's working set (~250 MB) fits in the last-level cache: evict it before every
+    # timed step (outside the events) by streaming a 512 MiB buffer through the caches. A
+    # read, not a write: a written flush leaves dirty lines whose write-back the next step
+    # would pay for.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    flush_out = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
     for two in names:
         for _ in range(warmup):
             step(two)
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        t0 = time.perf_counter()
         for i in range(steps):
+            wgen.read_probe(flush, 4096, 4, flush_out)
             step(two, ev[i])
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / steps
+        wall = float(np.mean([e[0].elapsed_time(e[2]) for e in ev])) * 1e-3     # write + attention
         t_w = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
         t_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
         parts = {}
@@ -522,10 +553,13 @@ def main():
                    **({"split_slots": dev["split"].num_slots, "split_tiles_per_slot": dev["split"].tiles_per_slot}
                       if args.decode == "split" else {})},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "pct_of_measured_read_peak": None,
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "kernel_us": {"kv_cache_write": round(float(t_write.mean()) * 1e6, 2),
                       "decode": round(t_dec * 1e6, 2),
+                      "decode_median": round(float(np.median(t_decode)) * 1e6, 2),
+                      "decode_min": round(float(t_decode.min()) * 1e6, 2),
                       "step_events": round(float(t_step.mean()) * 1e6, 2),
                       "profiled_partition_pass": round(float(t_part.mean()) * 1e6, 2),
                       "profiled_merge": round(float(t_merge.mean()) * 1e6, 2)},
@@ -534,6 +568,9 @@ def main():
                      "kernel": "decode partition pass", "algorithmic_bytes": dbytes},
         "cpu_baseline": None,
     }
+    rp = measured_read_peak()
+    res["measured_read_peak_GBps"] = round(rp, 1)
+    res["pct_of_measured_read_peak"] = round(100 * gbs / rp, 2)
     if not args.no_mixed:
         print("[bench] mixed prefill+decode step", file=sys.stderr, flush=True)
         res["mixed_step"] = mixed_step(args.steps, args.warmup)
