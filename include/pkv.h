@@ -366,6 +366,13 @@ int pkv_sched_plan(const pkv_sched* sched, int32_t table_width, int64_t* ids, in
 int pkv_sched_update(pkv_sched* sched);
 int pkv_sched_counters(const pkv_sched* sched, int64_t* out);
 
+/* Admission without the memory check (enabled = 0), the sabotage of the "Break It"
+ * experiment of [P17]: pkv_sched_schedule takes the head of the waiting queue off it and
+ * allocates its blocks unchecked; when they do not fit it returns PKV_ERR_OUT_OF_BLOCKS
+ * (the pool unchanged, that request out of every queue, the step not scheduled) and the
+ * scheduler is not meant to be used further. enabled != 0 restores the check (default). */
+int pkv_sched_set_admission_check(pkv_sched* sched, int32_t enabled);
+
 /* Profiling hook (for timing the partition pass alone): while `hip_event` (a
  * hipEvent_t) is not NULL, every pkv_paged_attention_decode and
  * pkv_paged_attention_decode_split call made on this thread records it on its stream

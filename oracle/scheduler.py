@@ -74,7 +74,7 @@ class StepPlan:
 
 class Scheduler:
     def __init__(self, arrival, prompt, max_tokens, num_blocks: int, free_order, block_size: int,
-                 max_running: int):
+                 max_running: int, admission_check: bool = True):
         self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
         self.arrival_order = sorted(range(len(self.reqs)), key=lambda i: (self.reqs[i].arrival, i))
         self.next_arrival = 0
@@ -82,6 +82,10 @@ class Scheduler:
         self.tables = oa.SeqTables(self.pool, block_size)
         self.bs = block_size
         self.max_running = max_running
+        # admission_check=False is the sabotage of the "Break It" experiment of "Project 17"
+        # (its admission loop pops the head and prefills it with no memory check): the head
+        # is taken off the queue and its allocation may raise OutOfBlocks out of the step
+        self.admission_check = admission_check
         self.waiting: collections.deque = collections.deque()
         self.running: List[Req] = []
         self.step_no = 0
@@ -107,6 +111,12 @@ class Scheduler:
             self.next_arrival += 1
         while self.waiting and len(self.running) < self.max_running:
             r = self.waiting[0]
+            if not self.admission_check:
+                self.waiting.popleft()
+                self.tables.reserve(r.rid, r.prompt + r.n_out)      # OutOfBlocks leaves the step
+                r.stage = PREFILL
+                self.running.append(r)
+                continue
             try:
                 self.tables.reserve(r.rid, r.prompt + r.n_out)      # all-or-nothing
             except oa.OutOfBlocks:

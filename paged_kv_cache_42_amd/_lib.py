@@ -72,6 +72,7 @@ _SIGS = {
     "pkv_sched_plan": (C.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
     "pkv_sched_update": (C.c_int, [vp]),
     "pkv_sched_counters": (C.c_int, [vp, vp]),
+    "pkv_sched_set_admission_check": (C.c_int, [vp, i32]),
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
     "pkv_decode_split_workspace_bytes": (sz, [i32, i32, i32, i32]),
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -131,6 +132,11 @@ class Scheduler:
 
     def update(self) -> None:
         check(lib().pkv_sched_update(self._h))
+
+    def set_admission_check(self, enabled: bool) -> None:
+        """False: admit without checking for free blocks (the Break-It sabotage); schedule()
+        then raises OutOfBlocks at the step whose admission does not fit."""
+        check(lib().pkv_sched_set_admission_check(self._h, int(bool(enabled))))
 
     def counters(self) -> dict:
         out = np.zeros(7, np.int64)

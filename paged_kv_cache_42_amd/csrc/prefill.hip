@@ -167,21 +167,27 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   const int t_hi = (key_end + kKeys - 1) / kKeys;
 
   // Per-thread parts of the chunk addresses (the same in every tile): chunk i of this
-  // thread is 16 bytes of key kt[i] of the tile, which lies in the tile's block jb[i].
-  int kti[LPT], jb[LPT];
-  int64_t cpart[LPT];
+  // thread is 16 bytes of key kti[i] of the tile. The 64 chunks of one wave's load i cover
+  // 64 / CPK consecutive keys, aligned, so they never straddle a block: the block (jw[i])
+  // is wave-uniform, and the address is a scalar block base plus a fixed 32-bit lane
+  // offset (no per-lane 64-bit address arithmetic per tile).
+  static_assert(BS % (64 / CPK) == 0, "a wave's chunks of one load stay in one block");
+  int kti[LPT], jw[LPT];
+  uint32_t voff[LPT], loff[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + kThreads * i;
     kti[i] = c / CPK;
-    jb[i] = kti[i] / BS;
-    cpart[i] = int64_t(kti[i] % BS) * row_bytes + head_off + 16 * (c % CPK);
+    jw[i] = __builtin_amdgcn_readfirstlane(kti[i] / BS);
+    voff[i] = uint32_t((kti[i] % BS) * row_bytes + head_off + 16 * (c % CPK));
+    loff[i] = uint32_t(kti[i] * RS + (CDT == PKV_BF16 ? 16 : 32) * (c % CPK));
   }
   const int64_t block_bytes = int64_t(BS) * row_bytes;
 
-  // Stage tile t into registers: every load is issued (clamped to byte 0 of the plane
-  // when out of range) so the waits of the ring stay partial. `keep` marks the real rows;
-  // all-ones (uniform) when every row of the tile is in the context and its blocks valid.
+  // Stage tile t into registers: every load is issued (from block 0 when the tile's block
+  // is past the end or invalid), so the loads stay unconditional. `keep` marks the real
+  // rows; all-ones (uniform) when every row of the tile is in the context and its blocks
+  // are valid.
   auto stage = [&](int t, uint4 (&ks)[LPT], uint4 (&vs)[LPT], uint32_t& keep) {
     const int key0 = t * kKeys;
     int blk[NB];
@@ -196,16 +202,17 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
     for (int i = 0; i < LPT; ++i) {
       int b = blk[0];
 #pragma unroll
-      for (int j = 1; j < NB; ++j) b = jb[i] >= j ? blk[j] : b;
-      int64_t off = int64_t(b) * block_bytes + cpart[i];
+      for (int j = 1; j < NB; ++j) b = jw[i] == j ? blk[j] : b;      // wave-uniform
+      const bool bok = b >= 0 && b < a.num_blocks;
+      const int64_t base = int64_t(bok ? b : 0) * block_bytes;
       if (!all_ok) {                                      // uniform: the tail tile, or a bad block id
-        const bool ok = (key0 + kti[i] < key_end) & (b >= 0) & (b < a.num_blocks);
-        off &= -int64_t(ok);                               // masked to byte 0 (a select became a branch)
+        const bool ok = (key0 + kti[i] < key_end) & bok;
         keep |= ok ? (1u << i) : 0u;
       }
-      asm volatile("" : "+v"(off));                        // keep the load unconditional
-      ks[i] = *reinterpret_cast<const uint4*>(a.kc + off);
-      vs[i] = *reinterpret_cast<const uint4*>(a.vc + off);
+      const uint8_t* kb = a.kc + base;                     // scalar block bases
+      const uint8_t* vb = a.vc + base;
+      ks[i] = *reinterpret_cast<const uint4*>(kb + voff[i]);
+      vs[i] = *reinterpret_cast<const uint4*>(vb + voff[i]);
     }
   };
   auto commit = [&](int buf, const uint4 (&ks)[LPT], const uint4 (&vs)[LPT], uint32_t keep) {
@@ -220,15 +227,14 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
         k = make_uint4(k.x & mk, k.y & mk, k.z & mk, k.w & mk);
         v = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
       }
-      const int ci = (tid + kThreads * i) % CPK;
       if constexpr (CDT == PKV_BF16) {
-        *reinterpret_cast<uint4*>(kt + kti[i] * RS + 16 * ci) = k;
-        *reinterpret_cast<uint4*>(vt + kti[i] * RS + 16 * ci) = v;
+        *reinterpret_cast<uint4*>(kt + loff[i]) = k;
+        *reinterpret_cast<uint4*>(vt + loff[i]) = v;
       } else {
-        *reinterpret_cast<uint4*>(kt + kti[i] * RS + 32 * ci) = pkv::fp8x8_to_bf16x8(k.x, k.y);
-        *reinterpret_cast<uint4*>(kt + kti[i] * RS + 32 * ci + 16) = pkv::fp8x8_to_bf16x8(k.z, k.w);
-        *reinterpret_cast<uint4*>(vt + kti[i] * RS + 32 * ci) = pkv::fp8x8_to_bf16x8(v.x, v.y);
-        *reinterpret_cast<uint4*>(vt + kti[i] * RS + 32 * ci + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+        *reinterpret_cast<uint4*>(kt + loff[i]) = pkv::fp8x8_to_bf16x8(k.x, k.y);
+        *reinterpret_cast<uint4*>(kt + loff[i] + 16) = pkv::fp8x8_to_bf16x8(k.z, k.w);
+        *reinterpret_cast<uint4*>(vt + loff[i]) = pkv::fp8x8_to_bf16x8(v.x, v.y);
+        *reinterpret_cast<uint4*>(vt + loff[i] + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
       }
     }
   };
@@ -293,11 +299,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
     float lm[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      // the scale is positive: the maximum of the raw scores, scaled once
-      float mx = fmaxf(fmaxf(sc[rb][0][0], sc[rb][0][1]), fmaxf(sc[rb][0][2], sc[rb][0][3]));
+      // the scale is positive: the maximum of the raw scores, scaled once; a linear chain,
+      // so pairs fold into three-operand v_max3 (a tree did not)
+      float mx = sc[rb][0][0];
 #pragma unroll
-      for (int kb = 1; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[rb][kb][0], sc[rb][kb][1]), fmaxf(sc[rb][kb][2], sc[rb][kb][3])));
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[rb][e / 4][e % 4]);
       lm[rb] = mx * a.zscale;
     }
     if (__any((lm[0] > m[0] + kLazy) | (lm[1] > m[1] + kLazy))) {

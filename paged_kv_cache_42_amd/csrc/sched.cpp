@@ -76,6 +76,7 @@ struct pkv_sched {
   int64_t preempted = 0;
   int64_t finished = 0;
   bool scheduled = false;               // schedule() done, update() pending
+  bool admission_check = true;          // false: admit without checking for free blocks
 };
 
 extern "C" {
@@ -140,7 +141,17 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
   }
   // strict first-come-first-served admission
   while (!s->waiting.empty() && int32_t(s->running.size()) < s->max_running) {
-    Req& r = s->reqs[s->waiting.front()];
+    const int32_t head = s->waiting.front();
+    Req& r = s->reqs[head];
+    if (!s->admission_check) {          // the head leaves the queue before its allocation
+      s->waiting.pop_front();
+      if (!reserve(s->pool, r.id, int64_t(r.prompt) + r.n_out))
+        return fail(PKV_ERR_OUT_OF_BLOCKS, "sched_schedule: step %lld, request %lld does not fit and admission "
+                    "does not check", (long long)s->step, (long long)r.id);
+      r.stage = kPrefill;
+      s->running.push_back(head);
+      continue;
+    }
     if (!reserve(s->pool, r.id, int64_t(r.prompt) + r.n_out)) break;
     r.stage = kPrefill;
     s->running.push_back(s->waiting.front());
@@ -205,6 +216,12 @@ int pkv_sched_update(pkv_sched* s) {
   s->running.swap(still);
   s->scheduled = false;
   ++s->step;
+  return PKV_OK;
+}
+
+int pkv_sched_set_admission_check(pkv_sched* s, int32_t enabled) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_set_admission_check: scheduler is NULL");
+  s->admission_check = enabled != 0;
   return PKV_OK;
 }
 

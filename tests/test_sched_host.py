@@ -79,3 +79,41 @@ def test_call_order_and_request_errors():
     pool.seq_reserve(9, 4)
     with pytest.raises(pkv.PkvError):
         s.add_requests([9], [5], [3], [2])           # id already holds a table
+
+
+@pytest.mark.parametrize("seed,pool_blocks,max_running", [(1, 24, 6), (2, 40, 12), (3, 18, 3)])
+def test_admission_without_memory_check_fails_at_the_same_step(seed, pool_blocks, max_running):
+    # "Break It" of Project 17: the admission loop with its memory check removed. Both
+    # schedulers take the queue head and allocate unchecked; the first admission that does
+    # not fit must fail at the same step, with the same pool state, in both.
+    tr = workloads.small_trace(seed, 40, pool_blocks, block_size=4, max_running=max_running, prompt_max=30,
+                               out_max=20, rate=3.0)
+    pool, ours, ref = _pair(tr)
+    ours.set_admission_check(False)
+    ref.admission_check = False
+    from oracle import allocator as oa
+    failed_ref = None
+    for _ in range(400):
+        if ref.done():
+            break
+        try:
+            ref.schedule(20)
+        except oa.OutOfBlocks:
+            failed_ref = ref.step_no
+            break
+        ref.update()
+    assert failed_ref is not None, "the sabotaged oracle never ran out of blocks"
+    failed_ours = None
+    for _ in range(400):
+        try:
+            ours.schedule()
+        except pkv.OutOfBlocks:
+            failed_ours = ours.counters()["step"]
+            break
+        ours.update()
+    assert failed_ours == failed_ref
+    c = ours.counters()
+    assert (c["free"], c["running"], c["waiting"]) == (ref.pool.num_free, len(ref.running), len(ref.waiting))
+    # with the check in place the same trace completes
+    steps, _ = _replay_both(tr, 20)
+    assert steps > failed_ref
