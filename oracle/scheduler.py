@@ -36,11 +36,12 @@ from __future__ import annotations
 
 import collections
 import dataclasses
-from typing import Dict, List
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 from . import allocator as oa
+from . import prefix as opx
 from .metadata import build_block_table
 
 PREFILL, DECODE = 0, 1
@@ -56,6 +57,8 @@ class Req:
     stage: int = PREFILL
     preempted: int = 0
     finished_step: int = -1
+    tokens: Optional[Tuple[int, ...]] = None   # prompt token ids (prefix caching)
+    cached: int = 0                            # prompt tokens of this prefill found in the cache
 
 
 @dataclasses.dataclass
@@ -74,12 +77,23 @@ class StepPlan:
 
 class Scheduler:
     def __init__(self, arrival, prompt, max_tokens, num_blocks: int, free_order, block_size: int,
-                 max_running: int, admission_check: bool = True):
+                 max_running: int, admission_check: bool = True,
+                 prompt_tokens: Optional[Sequence[Sequence[int]]] = None):
         self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
+        # prompt_tokens given: prefix caching over shared blocks (oracle/prefix.py)
+        self.pcache = None
         self.arrival_order = sorted(range(len(self.reqs)), key=lambda i: (self.reqs[i].arrival, i))
         self.next_arrival = 0
         self.pool = oa.BlockPool(num_blocks, free_order)
         self.tables = oa.SeqTables(self.pool, block_size)
+        if prompt_tokens is not None:
+            self.tables = opx.SharedTables(self.pool, block_size)
+            self.pcache = opx.PrefixCache(self.tables)
+            for r, tok in zip(self.reqs, prompt_tokens):
+                if len(tok) != r.prompt:
+                    raise ValueError(f"request {r.rid}: {len(tok)} tokens for a prompt of {r.prompt}")
+                r.tokens = tuple(int(x) for x in tok)
+        self.cached_tokens = 0
         self.bs = block_size
         self.max_running = max_running
         # admission_check=False is the sabotage of the "Break It" experiment of "Project 17"
@@ -94,8 +108,11 @@ class Scheduler:
 
     # -- counters -------------------------------------------------------------------
     def counters(self) -> Dict[str, int]:
-        return {"free": self.pool.num_free, "running": len(self.running), "waiting": len(self.waiting),
-                "preempted": self.preemptions, "finished": self.finished}
+        c = {"free": self.pool.num_free, "running": len(self.running), "waiting": len(self.waiting),
+             "preempted": self.preemptions, "finished": self.finished}
+        if self.pcache is not None:
+            c["cached_tokens"] = self.cached_tokens
+        return c
 
     def done(self) -> bool:
         return self.finished == len(self.reqs)
@@ -111,25 +128,29 @@ class Scheduler:
             self.next_arrival += 1
         while self.waiting and len(self.running) < self.max_running:
             r = self.waiting[0]
+            ctx = r.prompt + r.n_out
+            n_hit, pages = 0, []
+            if self.pcache is not None:                             # longest cached prefix
+                n_hit, pages = self.pcache.lookup(r.tokens, min(r.prompt, ctx - 1))
             if not self.admission_check:
                 self.waiting.popleft()
-                self.tables.reserve(r.rid, r.prompt + r.n_out)      # OutOfBlocks leaves the step
-                r.stage = PREFILL
-                self.running.append(r)
-                continue
-            try:
-                self.tables.reserve(r.rid, r.prompt + r.n_out)      # all-or-nothing
-            except oa.OutOfBlocks:
+            elif self.tables.blocks_for(ctx) - len(pages) > self.pool.num_free:
                 break                                               # strict FCFS: stop here
-            self.waiting.popleft()
+            else:
+                self.waiting.popleft()
+            if pages:
+                self.tables.share(r.rid, pages)
+            self.tables.reserve(r.rid, ctx)                         # all-or-nothing; unchecked: may raise
             r.stage = PREFILL
+            r.cached = n_hit
+            self.cached_tokens += n_hit
             self.running.append(r)
         ids, stages, q, L = [], [], [], []
         for r in self.running:
             ctx = r.prompt + r.n_out
             ids.append(r.rid)
             stages.append(r.stage)
-            q.append(ctx if r.stage == PREFILL else 1)
+            q.append(ctx - r.cached if r.stage == PREFILL else 1)
             L.append(ctx)
         tabs = [self.tables.tables[i] for i in ids]
         bt, cu, slots = build_block_table(tabs, q, L, self.bs, width)
@@ -138,8 +159,13 @@ class Scheduler:
 
     # -- second half: one output token per row, retire, grow or preempt --------------
     def update(self) -> None:
+        if self.pcache is not None:                                 # this step wrote these pages
+            for r in self.running:
+                if r.stage == PREFILL:
+                    self.pcache.insert(r.tokens, self.tables.tables[r.rid], r.prompt)
         still = []
         for r in self.running:
+            r.cached = 0
             r.n_out += 1
             r.stage = DECODE
             if r.n_out >= r.max_tokens:

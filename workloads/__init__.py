@@ -43,6 +43,11 @@ _STREAM_ARRIVALS = 31
 _STREAM_PROMPTS = 32
 _STREAM_OUTPUTS = 33
 _STREAM_LAYER_BASE = 40     # per-layer q/k/v streams: 40 + 3 * layer + (0, 1, 2)
+_STREAM_GROUPS = 34         # prefix traces: group of each request
+_STREAM_SHARED = 35         #   lengths of the groups' shared prompts
+_STREAM_UNIQUE = 36         #   lengths of the requests' own prompt parts
+_STREAM_TOKENS = 37         #   token ids
+GROUP_OWNER = 1 << 23       # value/token streams of group g are owned by GROUP_OWNER + g
 
 
 def rng_for(*key: int) -> np.random.Generator:
@@ -447,10 +452,37 @@ class Trace:
     sigma: float = 1.0
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # prefix traces: request r's first prefix_len[r] prompt tokens are the system prompt of
+    # group prefix_group[r] (-1: none), identical across the group, so their K/V are too
+    prefix_group: Optional[np.ndarray] = None
+    prefix_len: Optional[np.ndarray] = None
 
     @property
     def num_requests(self) -> int:
         return len(self.arrival)
+
+    def owner_segments(self, req: int, pos0: int, pos1: int):
+        """[(owner, lo, hi)] covering positions pos0..pos1-1 of request req: positions in its
+        group's shared prompt belong to the group's streams, the rest to the request's."""
+        S, g = 0, -1
+        if self.prefix_group is not None and self.prefix_group[req] >= 0:
+            S, g = int(self.prefix_len[req]), int(self.prefix_group[req])
+        segs = []
+        if pos0 < min(S, pos1):
+            segs.append((GROUP_OWNER + g, pos0, min(S, pos1)))
+        if max(pos0, S) < pos1:
+            segs.append((req, max(pos0, S), pos1))
+        return segs
+
+    def prompt_tokens(self, req: int) -> np.ndarray:
+        """Token ids of request req's prompt (int32 [prompt]): hashed from (owner, position)."""
+        out = np.empty(int(self.prompt[req]), np.int32)
+        for owner, lo, hi in self.owner_segments(req, 0, int(self.prompt[req])):
+            z = (np.arange(lo, hi, dtype=np.uint64) + np.uint64(1)) * _GAMMA + np.uint64(hash_key(self.seed, _STREAM_TOKENS, owner))
+            z = (z ^ (z >> np.uint64(30))) * _MIX1
+            z = (z ^ (z >> np.uint64(27))) * _MIX2
+            out[lo:hi] = ((z ^ (z >> np.uint64(31))) >> np.uint64(33)).astype(np.int32)
+        return out
 
     @property
     def group(self) -> int:
@@ -467,7 +499,9 @@ class Trace:
         """Values of positions pos0..pos1-1 of a request in one layer: [n][heads][d] float32."""
         heads = self.num_q_heads if which == "q" else self.num_kv_heads
         per = heads * self.head_dim
-        v = hash_values(self.value_key(which, layer, req), pos0 * per, pos1 * per, self.sigma)
+        parts = [hash_values(self.value_key(which, layer, owner), lo * per, hi * per, self.sigma)
+                 for owner, lo, hi in self.owner_segments(req, pos0, pos1)]
+        v = np.concatenate(parts) if parts else np.zeros(0, np.float32)
         return v.reshape(pos1 - pos0, heads, self.head_dim)
 
 
@@ -486,15 +520,41 @@ def config5(cache_dtype: str = "bf16") -> Trace:
                  cache_dtype=cache_dtype)
 
 
+def config5_prefix(cache_dtype: str = "bf16") -> Trace:
+    """Config 5 with shared system prompts (prefix caching): the same arrivals and output
+    lengths; each request belongs to one of 16 groups (uniform), and its prompt is the
+    group's system prompt (lognormal, median 512, sigma 0.5, 64..2048 tokens) followed by
+    its own part (lognormal, median 128, sigma 1, 1..2048 tokens), capped at 4096."""
+    seed, n, G = 5, 2000, 16
+    base = config5(cache_dtype)
+    group = rng_for(seed, _STREAM_GROUPS).integers(0, G, size=n).astype(np.int32)
+    shared = np.clip(np.rint(rng_for(seed, _STREAM_SHARED).lognormal(np.log(512.0), 0.5, size=G)), 64, 2048)
+    own = np.clip(np.rint(rng_for(seed, _STREAM_UNIQUE).lognormal(np.log(128.0), 1.0, size=n)), 1, 2048)
+    plen = shared.astype(np.int32)[group]
+    prompt = np.minimum(plen + own.astype(np.int32), 4096).astype(np.int32)
+    return dataclasses.replace(base, name=f"cfg5p_prefix_trace_{cache_dtype}", prompt=prompt, prefix_group=group,
+                               prefix_len=np.minimum(plen, prompt - 1).astype(np.int32))
+
+
 def small_trace(seed: int, n: int, num_blocks: int, block_size: int = 4, max_running: int = 8,
-                prompt_max: int = 40, out_max: int = 30, rate: float = 1.0) -> Trace:
-    """A small seeded trace for tests (same generation rules, small sizes)."""
+                prompt_max: int = 40, out_max: int = 30, rate: float = 1.0, groups: int = 0) -> Trace:
+    """A small seeded trace for tests (same generation rules, small sizes); groups > 0
+    gives every request a shared prompt of one of that many groups (prefix traces)."""
     arrival = np.floor(np.cumsum(rng_for(seed, _STREAM_ARRIVALS).exponential(1.0 / rate, size=n))).astype(np.int32)
     prompt = rng_for(seed, _STREAM_PROMPTS).integers(1, prompt_max, size=n, endpoint=True).astype(np.int32)
     max_tokens = rng_for(seed, _STREAM_OUTPUTS).integers(1, out_max, size=n, endpoint=True).astype(np.int32)
-    return Trace(f"small_trace_{seed}", seed, arrival, prompt, max_tokens, num_blocks,
-                 _permutation(seed, num_blocks), block_size=block_size, max_running=max_running,
-                 num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=64)
+    tr = Trace(f"small_trace_{seed}", seed, arrival, prompt, max_tokens, num_blocks,
+               _permutation(seed, num_blocks), block_size=block_size, max_running=max_running,
+               num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=64)
+    if groups > 0:
+        group = rng_for(seed, _STREAM_GROUPS).integers(0, groups, size=n).astype(np.int32)
+        shared = rng_for(seed, _STREAM_SHARED).integers(1, prompt_max, size=groups, endpoint=True).astype(np.int32)
+        own = rng_for(seed, _STREAM_UNIQUE).integers(1, max(2, prompt_max // 2), size=n, endpoint=True).astype(np.int32)
+        plen = shared[group]
+        tr.prompt = (plen + own).astype(np.int32)
+        tr.prefix_group, tr.prefix_len = group, plen.astype(np.int32)
+        tr.name = f"small_prefix_trace_{seed}"
+    return tr
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}
