@@ -301,12 +301,15 @@ def sched_replay(max_steps):
     import workloads
     from workloads import replay
     out = {}
-    for cdt in ("bf16", "fp8"):
-        tr = workloads.config5(cdt)
-        print(f"[bench] replay {tr.name}", file=sys.stderr, flush=True)
-        _, summ = replay.run(tr, max_steps=max_steps,
-                             progress=lambda n: print(f"[bench] replay {cdt}: {n} steps", file=sys.stderr, flush=True))
-        out[cdt] = summ
+    runs = [("bf16", workloads.config5("bf16"), True), ("fp8", workloads.config5("fp8"), True),
+            # shared system prompts (16 groups), with and without the prefix cache
+            ("bf16_prefix_cache", workloads.config5_prefix("bf16"), True),
+            ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), False)]
+    for name, tr, cache in runs:
+        print(f"[bench] replay {tr.name} (prefix cache {'on' if cache else 'off'})", file=sys.stderr, flush=True)
+        _, summ = replay.run(tr, max_steps=max_steps, prefix_cache=cache,
+                             progress=lambda n: print(f"[bench] replay {name}: {n} steps", file=sys.stderr, flush=True))
+        out[name] = summ
     return out
 
 

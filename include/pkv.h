@@ -86,11 +86,22 @@ int pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* live_seq
 int pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t capacity, int32_t* count);
 
 /* Grow sequence seq_id's table to ceil(total_tokens / block_size) blocks (never
- * shrinks; creates the sequence if new). New ids are popped as by pkv_pool_alloc
- * and appended to the table. OUT_OF_BLOCKS: nothing changes. */
+ * shrinks; creates the sequence if new). New ids are popped as by pkv_pool_alloc,
+ * appended to the table and held once. OUT_OF_BLOCKS: nothing changes. */
 int pkv_seq_reserve(pkv_pool* pool, int64_t seq_id, int32_t total_tokens);
-/* Free seq_id's whole table in table order and forget the sequence. INVALID if unknown. */
+/* Forget seq_id's table: each of its blocks loses one reference, and those no other
+ * table holds go back to the free list in table order (a table nobody shares frees its
+ * whole table in table order). INVALID if unknown. */
 int pkv_seq_release(pkv_pool* pool, int64_t seq_id);
+/* Prefix sharing ([P17] "Step 8: Prefix caching"; reference counts as in [PY] "Step 2"):
+ * start seq_id's table (new or empty) with n blocks (host array) that other tables hold,
+ * each gaining a reference; later pkv_seq_reserve calls append own blocks after them.
+ * INVALID (nothing changed) if seq_id already holds blocks or a block is not held by a
+ * sequence or repeated. The caller must never write into a shared block. */
+int pkv_seq_share(pkv_pool* pool, int64_t seq_id, const int32_t* blocks, int32_t n);
+/* Copy the reference count of every block (host, capacity >= num_blocks entries): the
+ * number of tables holding it (0 for free and pkv_pool_alloc blocks). */
+int pkv_block_refs(const pkv_pool* pool, int32_t* refs, int32_t capacity);
 /* Copy seq_id's table (host, capacity entries); *count = its length. */
 int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* out, int32_t capacity,
                   int32_t* count);
@@ -351,9 +362,19 @@ int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype
  * Calls out of this order are INVALID. pkv_sched_add_requests: host arrays [n]; ids unique
  * and without a table in the pool, prompt >= 1, max_tokens >= 1, arrival >= the current
  * step, and prompt + max_tokens - 1 tokens must fit the pool (else the queue could stall);
- * INVALID otherwise (nothing added). pkv_sched_counters: out int64 [7] = step, free
- * blocks, running, waiting, preemptions so far, finished so far, requests added. The
- * scheduler does not own the pool, which must outlive it; not thread-safe. */
+ * INVALID otherwise (nothing added). pkv_sched_counters: out int64 [8] = step, free
+ * blocks, running, waiting, preemptions so far, finished so far, requests added, prompt
+ * tokens served from the prefix cache so far. The scheduler does not own the pool, which
+ * must outlive it; not thread-safe.
+ * Prefix caching ([P17] "Step 8: Prefix caching"), off unless enabled before the first
+ * step: at admission, the longest whole-page prefix of a request's prompt tokens (at
+ * most prompt - 1 tokens for a fresh request, which must compute its last prompt token;
+ * at most the prompt for a recompute) that the cache maps to still-held pages is shared
+ * (pkv_seq_share), the rest reserved, and the request admitted if that rest fits; its
+ * prefill row then holds only the uncached tokens (q = context - cached, positions from
+ * the cached length). At each update, the whole prompt pages of the step's prefill rows
+ * are registered (an existing usable entry stays). An entry dies with its pages: a block
+ * freed since it was registered makes it unusable. */
 typedef struct pkv_sched pkv_sched;
 int pkv_sched_create(pkv_pool* pool, int32_t max_running, pkv_sched** out);
 void pkv_sched_destroy(pkv_sched* sched);
@@ -365,6 +386,11 @@ int pkv_sched_plan(const pkv_sched* sched, int32_t table_width, int64_t* ids, in
                    int64_t* slot_mapping);
 int pkv_sched_update(pkv_sched* sched);
 int pkv_sched_counters(const pkv_sched* sched, int64_t* out);
+/* Turn prefix caching on (before the first step; see above). */
+int pkv_sched_enable_prefix_cache(pkv_sched* sched);
+/* Prompt token ids of request id (host int32 [n], n = its prompt length), before the first
+ * step; requests without tokens neither hit nor fill the prefix cache. */
+int pkv_sched_set_prompt_tokens(pkv_sched* sched, int64_t id, const int32_t* tokens, int32_t n);
 
 /* Admission without the memory check (enabled = 0), the sabotage of the "Break It"
  * experiment of [P17]: pkv_sched_schedule takes the head of the waiting queue off it and

@@ -73,6 +73,10 @@ _SIGS = {
     "pkv_sched_update": (C.c_int, [vp]),
     "pkv_sched_counters": (C.c_int, [vp, vp]),
     "pkv_sched_set_admission_check": (C.c_int, [vp, i32]),
+    "pkv_sched_enable_prefix_cache": (C.c_int, [vp]),
+    "pkv_sched_set_prompt_tokens": (C.c_int, [vp, i64, vp, i32]),
+    "pkv_seq_share": (C.c_int, [vp, i64, vp, i32]),
+    "pkv_block_refs": (C.c_int, [vp, vp, i32]),
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
     "pkv_decode_split_workspace_bytes": (sz, [i32, i32, i32, i32]),
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -94,7 +98,7 @@ class StepPlan:
 class Scheduler:
     """pkv_sched handle: the continuous-batching step over a Pool (which it must not outlive)."""
 
-    COUNTERS = ("step", "free", "running", "waiting", "preempted", "finished", "requests")
+    COUNTERS = ("step", "free", "running", "waiting", "preempted", "finished", "requests", "cached_tokens")
 
     def __init__(self, pool: Pool, max_running: int):
         self.pool = pool                        # keeps the pool alive
@@ -138,8 +142,17 @@ class Scheduler:
         then raises OutOfBlocks at the step whose admission does not fit."""
         check(lib().pkv_sched_set_admission_check(self._h, int(bool(enabled))))
 
+    def enable_prefix_cache(self, prompt_tokens=None) -> None:
+        """Prefix caching on (before the first step); prompt_tokens: {id: token ids} or a
+        sequence indexed like the ids added so far."""
+        check(lib().pkv_sched_enable_prefix_cache(self._h))
+        items = prompt_tokens.items() if isinstance(prompt_tokens, dict) else enumerate(prompt_tokens or [])
+        for rid, tok in items:
+            t = np.ascontiguousarray(tok, dtype=np.int32)
+            check(lib().pkv_sched_set_prompt_tokens(self._h, int(rid), _np_ptr(t), len(t)))
+
     def counters(self) -> dict:
-        out = np.zeros(7, np.int64)
+        out = np.zeros(8, np.int64)
         check(lib().pkv_sched_counters(self._h, _np_ptr(out)))
         return dict(zip(self.COUNTERS, (int(x) for x in out)))
 
@@ -236,6 +249,15 @@ class Pool:
 
     def seq_release(self, seq_id: int) -> None:
         check(lib().pkv_seq_release(self._h, int(seq_id)))
+
+    def seq_share(self, seq_id: int, blocks) -> None:
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        check(lib().pkv_seq_share(self._h, int(seq_id), _np_ptr(b), len(b)))
+
+    def block_refs(self) -> np.ndarray:
+        out = np.zeros(max(self.num_blocks, 1), np.int32)
+        check(lib().pkv_block_refs(self._h, _np_ptr(out), len(out)))
+        return out[:self.num_blocks]
 
     def seq_table(self, seq_id: int) -> list:
         n = i32()

@@ -47,6 +47,47 @@ using pkv::fail;
 
 #include "pool_internal.h"
 
+namespace pkv {
+
+bool pool_reserve(pkv_pool* p, int64_t id, int64_t tokens) {
+  const int64_t want = (tokens + p->block_size - 1) / p->block_size;
+  auto it = p->tables.find(id);
+  const int64_t have = it == p->tables.end() ? 0 : int64_t(it->second.size());
+  const int64_t need = want - have;
+  if (need > int64_t(p->free_list.size())) return false;
+  std::vector<int32_t>& t = p->tables[id];
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = p->free_list.back();
+    p->free_list.pop_back();
+    p->state[b] = kInSeq;
+    p->ref[b] = 1;
+    t.push_back(b);
+  }
+  return true;
+}
+
+void pool_release(pkv_pool* p, int64_t id) {
+  auto it = p->tables.find(id);
+  if (it == p->tables.end()) return;
+  for (int32_t b : it->second) {                 // table order
+    if (--p->ref[b] > 0) continue;               // still held by another table
+    p->state[b] = kFree;
+    ++p->gen[b];
+    p->free_list.push_back(b);
+  }
+  p->tables.erase(it);
+}
+
+void pool_share(pkv_pool* p, int64_t id, const int32_t* blocks, int32_t n) {
+  std::vector<int32_t>& t = p->tables[id];
+  for (int32_t i = 0; i < n; ++i) {
+    ++p->ref[blocks[i]];
+    t.push_back(blocks[i]);
+  }
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
@@ -66,6 +107,8 @@ int pkv_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   p->state.assign(num_blocks, kFree);
+  p->ref.assign(num_blocks, 0);
+  p->gen.assign(num_blocks, 0);
   p->free_list.resize(num_blocks);
   if (initial_free_order) {
     std::vector<uint8_t> seen(num_blocks, 0);
@@ -140,33 +183,44 @@ int pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t capacity, int
 
 int pkv_seq_reserve(pkv_pool* pool, int64_t seq_id, int32_t total_tokens) {
   if (!pool || total_tokens < 0) return fail(PKV_ERR_INVALID, "seq_reserve: bad arguments");
-  const int64_t want = (int64_t(total_tokens) + pool->block_size - 1) / pool->block_size;
-  auto it = pool->tables.find(seq_id);
-  const int64_t have = it == pool->tables.end() ? 0 : int64_t(it->second.size());
-  const int64_t need = want - have;
-  if (need > int64_t(pool->free_list.size()))
+  if (!pkv::pool_reserve(pool, seq_id, total_tokens)) {
+    const int64_t want = (int64_t(total_tokens) + pool->block_size - 1) / pool->block_size;
+    auto it = pool->tables.find(seq_id);
+    const int64_t have = it == pool->tables.end() ? 0 : int64_t(it->second.size());
     return fail(PKV_ERR_OUT_OF_BLOCKS, "seq_reserve: sequence %lld needs %lld more blocks, %zu free",
-                (long long)seq_id, (long long)need, pool->free_list.size());
-  std::vector<int32_t>& t = pool->tables[seq_id];
-  for (int64_t i = 0; i < need; ++i) {
-    const int32_t b = pool->free_list.back();
-    pool->free_list.pop_back();
-    pool->state[b] = kInSeq;
-    t.push_back(b);
+                (long long)seq_id, (long long)(want - have), pool->free_list.size());
   }
   return PKV_OK;
 }
 
 int pkv_seq_release(pkv_pool* pool, int64_t seq_id) {
   if (!pool) return fail(PKV_ERR_INVALID, "seq_release: pool is NULL");
-  auto it = pool->tables.find(seq_id);
-  if (it == pool->tables.end())
+  if (!pool->tables.count(seq_id))
     return fail(PKV_ERR_INVALID, "seq_release: unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second) {
-    pool->state[b] = kFree;
-    pool->free_list.push_back(b);
+  pkv::pool_release(pool, seq_id);
+  return PKV_OK;
+}
+
+int pkv_seq_share(pkv_pool* pool, int64_t seq_id, const int32_t* blocks, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !blocks)) return fail(PKV_ERR_INVALID, "seq_share: bad arguments");
+  auto it = pool->tables.find(seq_id);
+  if (it != pool->tables.end() && !it->second.empty())
+    return fail(PKV_ERR_INVALID, "seq_share: sequence %lld already holds blocks", (long long)seq_id);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= pool->num_blocks || pool->state[b] != kInSeq || pool->ref[b] < 1)
+      return fail(PKV_ERR_INVALID, "seq_share: block %d is not held by a sequence", b);
+    for (int32_t j = 0; j < i; ++j)
+      if (blocks[j] == b) return fail(PKV_ERR_INVALID, "seq_share: block %d repeated", b);
   }
-  pool->tables.erase(it);
+  pkv::pool_share(pool, seq_id, blocks, n);
+  return PKV_OK;
+}
+
+int pkv_block_refs(const pkv_pool* pool, int32_t* refs, int32_t capacity) {
+  if (!pool || (pool->num_blocks > 0 && !refs) || capacity < pool->num_blocks)
+    return fail(PKV_ERR_INVALID, "block_refs: bad arguments");
+  if (pool->num_blocks) std::memcpy(refs, pool->ref.data(), sizeof(int32_t) * pool->num_blocks);
   return PKV_OK;
 }
 

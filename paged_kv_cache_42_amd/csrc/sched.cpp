@@ -31,38 +31,32 @@ struct Req {
   int32_t arrival, prompt, max_tokens;
   int32_t n_out = 0;
   int32_t stage = kPrefill;
+  int32_t cached = 0;                  // prompt tokens of this prefill found in the cache
+  std::vector<int32_t> tokens;         // prompt token ids (prefix caching), else empty
 };
 
-// Grow the table of `id` to cover `tokens` tokens, all-or-nothing; false when the pool
-// has too few free blocks (nothing changed).
-bool reserve(pkv_pool* p, int64_t id, int64_t tokens) {
-  const int64_t want = (tokens + p->block_size - 1) / p->block_size;
-  auto it = p->tables.find(id);
-  const int64_t have = it == p->tables.end() ? 0 : int64_t(it->second.size());
-  const int64_t need = want - have;
-  if (need > int64_t(p->free_list.size())) return false;
-  std::vector<int32_t>& t = p->tables[id];
-  for (int64_t i = 0; i < need; ++i) {
-    const int32_t b = p->free_list.back();
-    p->free_list.pop_back();
-    p->state[b] = kInSeq;
-    t.push_back(b);
-  }
-  return true;
+using pkv::pool_release;
+using pkv::pool_reserve;
+
+// 64-bit mix (SplitMix64 finaliser) for the prefix keys.
+uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
 }
 
-// Free the table of `id` in table order.
-void release(pkv_pool* p, int64_t id) {
-  auto it = p->tables.find(id);
-  if (it == p->tables.end()) return;
-  for (int32_t b : it->second) {
-    p->state[b] = kFree;
-    p->free_list.push_back(b);
-  }
-  p->tables.erase(it);
-}
+// Prefix cache ([P17] "Step 8: Prefix caching"): page-aligned prompt prefix -> the pages
+// holding it. Keys chain a hash over whole pages; a hit is confirmed token by token
+// against the request that registered the entry. An entry is usable while each of its
+// blocks is still held and has not been freed since (generation unchanged).
+struct PrefixEntry {
+  int32_t owner;                       // request (index) whose tokens the key covers
+  int32_t n_tokens;
+  std::vector<std::pair<int32_t, uint32_t>> pages;   // (block, generation)
+};
 
 }  // namespace
+
 
 struct pkv_sched {
   pkv_pool* pool = nullptr;
@@ -77,6 +71,58 @@ struct pkv_sched {
   int64_t finished = 0;
   bool scheduled = false;               // schedule() done, update() pending
   bool admission_check = true;          // false: admit without checking for free blocks
+  bool prefix_cache = false;
+  std::unordered_map<uint64_t, PrefixEntry> cache;
+  std::unordered_map<int64_t, int32_t> index;   // request id -> index in reqs
+  int64_t cached_tokens = 0;
+
+  // page-chained keys of tokens[0 : k * bs] for k = 1..pages
+  std::vector<uint64_t> page_keys(const std::vector<int32_t>& tok, int64_t pages) const {
+    std::vector<uint64_t> keys(size_t(std::max<int64_t>(pages, 0)));
+    uint64_t h = 0x9E3779B97F4A7C15ull;
+    const int64_t bs = pool->block_size;
+    for (int64_t k = 0; k < pages; ++k) {
+      for (int64_t i = k * bs; i < (k + 1) * bs; ++i) h = mix64(h ^ (uint64_t(uint32_t(tok[size_t(i)])) + 0x632BE59BD9B4E019ull));
+      keys[size_t(k)] = h;
+    }
+    return keys;
+  }
+  bool valid(const PrefixEntry& e) const {
+    for (const auto& pg : e.pages)
+      if (pool->ref[pg.first] < 1 || pool->gen[pg.first] != pg.second) return false;
+    return true;
+  }
+  // longest cached whole-page prefix of r's prompt within `limit` tokens
+  int32_t lookup(const Req& r, int64_t limit, std::vector<int32_t>& pages) const {
+    pages.clear();
+    const int64_t bs = pool->block_size;
+    const int64_t kmax = std::min<int64_t>(limit, int64_t(r.tokens.size())) / bs;
+    const std::vector<uint64_t> keys = page_keys(r.tokens, kmax);
+    for (int64_t k = kmax; k >= 1; --k) {
+      auto it = cache.find(keys[size_t(k - 1)]);
+      if (it == cache.end() || it->second.n_tokens != k * bs || !valid(it->second)) continue;
+      const std::vector<int32_t>& ot = reqs[size_t(it->second.owner)].tokens;
+      if (!std::equal(r.tokens.begin(), r.tokens.begin() + k * bs, ot.begin())) continue;   // hash collision
+      for (const auto& pg : it->second.pages) pages.push_back(pg.first);
+      return int32_t(k * bs);
+    }
+    return 0;
+  }
+  // register the whole pages of r's prompt (held by its table) that have no usable entry
+  void insert(int32_t ri) {
+    const Req& r = reqs[size_t(ri)];
+    const int64_t bs = pool->block_size;
+    const int64_t pages = int64_t(r.tokens.size()) / bs;
+    const std::vector<uint64_t> keys = page_keys(r.tokens, pages);
+    const std::vector<int32_t>& t = pool->tables.at(r.id);
+    for (int64_t k = 1; k <= pages; ++k) {
+      auto it = cache.find(keys[size_t(k - 1)]);
+      if (it != cache.end() && valid(it->second)) continue;
+      PrefixEntry e{ri, int32_t(k * bs), {}};
+      for (int64_t j = 0; j < k; ++j) e.pages.emplace_back(t[size_t(j)], pool->gen[t[size_t(j)]]);
+      cache[keys[size_t(k - 1)]] = std::move(e);
+    }
+  }
 };
 
 extern "C" {
@@ -120,6 +166,7 @@ int pkv_sched_add_requests(pkv_sched* s, int32_t n, const int64_t* ids, const in
   for (int32_t i = 0; i < n; ++i) {
     s->reqs.push_back(Req{ids[i], arrival[i], prompt[i], max_tokens[i]});
     s->arrival_order.push_back(int32_t(s->reqs.size() - 1));
+    s->index[ids[i]] = int32_t(s->reqs.size() - 1);
   }
   // requests not yet arrived are kept sorted by (arrival, id)
   std::sort(s->arrival_order.begin() + s->next_arrival, s->arrival_order.end(), [&](int32_t a, int32_t b) {
@@ -140,28 +187,32 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
     ++s->next_arrival;
   }
   // strict first-come-first-served admission
+  std::vector<int32_t> pages;
   while (!s->waiting.empty() && int32_t(s->running.size()) < s->max_running) {
     const int32_t head = s->waiting.front();
     Req& r = s->reqs[head];
-    if (!s->admission_check) {          // the head leaves the queue before its allocation
-      s->waiting.pop_front();
-      if (!reserve(s->pool, r.id, int64_t(r.prompt) + r.n_out))
-        return fail(PKV_ERR_OUT_OF_BLOCKS, "sched_schedule: step %lld, request %lld does not fit and admission "
-                    "does not check", (long long)s->step, (long long)r.id);
-      r.stage = kPrefill;
-      s->running.push_back(head);
-      continue;
-    }
-    if (!reserve(s->pool, r.id, int64_t(r.prompt) + r.n_out)) break;
-    r.stage = kPrefill;
-    s->running.push_back(s->waiting.front());
+    const int64_t ctx = int64_t(r.prompt) + r.n_out;
+    // longest cached prefix; a fresh request computes at least its last prompt token
+    const int32_t hit = s->prefix_cache && !r.tokens.empty()
+                            ? s->lookup(r, std::min<int64_t>(r.prompt, ctx - 1), pages)
+                            : (pages.clear(), 0);
+    const int64_t need = (ctx + s->pool->block_size - 1) / s->pool->block_size - int64_t(pages.size());
+    if (s->admission_check && need > int64_t(s->pool->free_list.size())) break;   // strict FCFS
     s->waiting.pop_front();
+    if (!pages.empty()) pkv::pool_share(s->pool, r.id, pages.data(), int32_t(pages.size()));
+    if (!pool_reserve(s->pool, r.id, ctx))    // only without the admission check
+      return fail(PKV_ERR_OUT_OF_BLOCKS, "sched_schedule: step %lld, request %lld does not fit and admission "
+                  "does not check", (long long)s->step, (long long)r.id);
+    r.stage = kPrefill;
+    r.cached = hit;
+    s->cached_tokens += hit;
+    s->running.push_back(head);
   }
   int64_t q = 0, mb = 0;
   for (int32_t i : s->running) {
     const Req& r = s->reqs[i];
     const int64_t ctx = int64_t(r.prompt) + r.n_out;
-    q += r.stage == kPrefill ? ctx : 1;
+    q += r.stage == kPrefill ? ctx - r.cached : 1;
     mb = std::max<int64_t>(mb, (ctx + s->pool->block_size - 1) / s->pool->block_size);
   }
   s->scheduled = true;
@@ -183,7 +234,7 @@ int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_
     const int32_t ctx = r.prompt + r.n_out;
     ids[k] = r.id;
     stages[k] = r.stage;
-    q_lens[k] = r.stage == kPrefill ? ctx : 1;
+    q_lens[k] = r.stage == kPrefill ? ctx - r.cached : 1;
     seq_lens[k] = ctx;
   }
   return pkv_build_block_table(s->pool, n, ids, q_lens, seq_lens, table_width, block_tables, cu_seqlens_q,
@@ -193,20 +244,24 @@ int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_
 int pkv_sched_update(pkv_sched* s) {
   if (!s) return fail(PKV_ERR_INVALID, "sched_update: scheduler is NULL");
   if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_update: no step scheduled");
+  if (s->prefix_cache)                  // this step wrote the prefill rows' pages
+    for (int32_t i : s->running)
+      if (s->reqs[i].stage == kPrefill && !s->reqs[i].tokens.empty()) s->insert(i);
   std::vector<int32_t> still;
   still.reserve(s->running.size());
   for (int32_t i : s->running) {
     Req& r = s->reqs[i];
+    r.cached = 0;
     r.n_out += 1;
     r.stage = kDecode;
     if (r.n_out >= r.max_tokens) {            // finished: blocks freed at once
-      release(s->pool, r.id);
+      pool_release(s->pool, r.id);
       ++s->finished;
       continue;
     }
     const int64_t need = int64_t(r.prompt) + r.n_out;   // tokens the next row writes up to
-    if (!reserve(s->pool, r.id, need)) {      // no block for the next token: preempt
-      release(s->pool, r.id);
+    if (!pool_reserve(s->pool, r.id, need)) {  // no block for the next token: preempt
+      pool_release(s->pool, r.id);
       ++s->preempted;
       s->waiting.push_front(i);
       continue;
@@ -234,6 +289,30 @@ int pkv_sched_counters(const pkv_sched* s, int64_t* out) {
   out[4] = s->preempted;
   out[5] = s->finished;
   out[6] = int64_t(s->reqs.size());
+  out[7] = s->cached_tokens;
+  return PKV_OK;
+}
+
+int pkv_sched_enable_prefix_cache(pkv_sched* s) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_enable_prefix_cache: scheduler is NULL");
+  if (s->step > 0 || s->scheduled)
+    return fail(PKV_ERR_INVALID, "sched_enable_prefix_cache: call before the first step");
+  s->prefix_cache = true;
+  return PKV_OK;
+}
+
+int pkv_sched_set_prompt_tokens(pkv_sched* s, int64_t id, const int32_t* tokens, int32_t n) {
+  if (!s || n < 0 || (n > 0 && !tokens)) return fail(PKV_ERR_INVALID, "sched_set_prompt_tokens: bad arguments");
+  auto it = s->index.find(id);
+  if (it == s->index.end())
+    return fail(PKV_ERR_INVALID, "sched_set_prompt_tokens: unknown request %lld", (long long)id);
+  Req& r = s->reqs[size_t(it->second)];
+  if (n != r.prompt)
+    return fail(PKV_ERR_INVALID, "sched_set_prompt_tokens: request %lld has a %d-token prompt, %d tokens given",
+                (long long)id, r.prompt, n);
+  if (s->step > 0 || s->scheduled)
+    return fail(PKV_ERR_INVALID, "sched_set_prompt_tokens: call before the first step");
+  r.tokens.assign(tokens, tokens + n);
   return PKV_OK;
 }
 

@@ -273,3 +273,25 @@ def test_chunk_work_errors():
     cp = pkv.build_chunk_work([0, 1, 1], [0, 7, 300], 2, 4, 64)
     assert len(cp.items) == 0 and len(cp.merges) == 0 and cp.num_partials == 0
     assert pkv.chunk_workspace_bytes(0, 128) == 0
+
+
+def test_pool_share_reference_counts():
+    pool = pkv.Pool(6, 4, 1, 64, "bf16")
+    pool.seq_reserve(1, 12)                     # 3 blocks from the end of 0..5
+    t1 = pool.seq_table(1)
+    assert t1 == [5, 4, 3]
+    pool.seq_share(2, t1[:2])
+    pool.seq_reserve(2, 12)                     # shares 5, 4, takes 2
+    assert pool.seq_table(2) == [5, 4, 2]
+    refs = pool.block_refs()
+    assert refs.tolist() == [0, 0, 1, 1, 2, 2]
+    with pytest.raises(pkv.PkvError):
+        pool.seq_share(2, [3])                  # 2 already holds blocks
+    with pytest.raises(pkv.PkvError):
+        pool.seq_share(3, [0])                  # block 0 is free
+    with pytest.raises(pkv.PkvError):
+        pool.seq_share(3, [5, 5])               # repeated
+    pool.seq_release(1)                         # 5, 4 still held by 2; 3 freed
+    assert pool.block_refs().tolist() == [0, 0, 1, 0, 1, 1] and pool.stats() == (3, 1)
+    pool.seq_release(2)                         # 5, 4, 2 freed in table order
+    assert pool.free_list() == [0, 1, 3, 5, 4, 2]

@@ -71,3 +71,28 @@ def test_config5_replay_sampled_parity(cache_dtype, steps, keep_steps):
         # the step after the first preemption re-prefills a request with its outputs
         p = by_step[112].plan
         assert any(st_ == 0 and q > tr.prompt[i] for i, st_, q in zip(p.ids, p.stages, p.q_lens))
+
+
+def test_prefix_trace_replay_sampled_parity():
+    # shared system prompts: prefill rows start after a cached prefix whose K/V another
+    # request wrote; the oracle attends over the request's own dense K/V
+    from oracle import scheduler as osch
+    tr = workloads.config5_prefix("bf16")
+    toks = [tr.prompt_tokens(r) for r in range(tr.num_requests)]
+    ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
+                         tr.max_running, prompt_tokens=toks)
+    hit_steps = []
+    for plan, _ in osch.run(ref, 512, 140):
+        if ((plan.stages == 0) & (plan.q_lens < plan.seq_lens)).any():
+            hit_steps.append(plan.step)
+    assert len(hit_steps) >= 3
+    keep_steps = hit_steps[:2] + hit_steps[-2:]
+    keep = {s: (0, tr.num_layers - 1) for s in keep_steps}
+    recs, summary = replay.run(tr, max_steps=140, keep=keep)
+    assert summary["cached_prompt_tokens"] > 0
+    by_step = {r.step: r for r in recs}
+    rng = np.random.default_rng(7)
+    checked = 0
+    for s in keep_steps:
+        checked += _check_step(tr, by_step[s], rng)
+    assert checked >= 12

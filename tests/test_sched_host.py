@@ -9,18 +9,22 @@ import workloads
 from oracle import scheduler as osch
 
 
-def _pair(tr):
+def _pair(tr, prefix=False):
     pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
                     free_order=tr.free_order)
     ours = pkv.Scheduler(pool, tr.max_running)
     ours.add_requests(np.arange(tr.num_requests), tr.arrival, tr.prompt, tr.max_tokens)
+    toks = None
+    if prefix:
+        toks = [tr.prompt_tokens(r) for r in range(tr.num_requests)]
+        ours.enable_prefix_cache(toks)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
-                         tr.max_running)
+                         tr.max_running, prompt_tokens=toks)
     return pool, ours, ref
 
 
-def _replay_both(tr, width):
-    pool, ours, ref = _pair(tr)
+def _replay_both(tr, width, prefix=False):
+    pool, ours, ref = _pair(tr, prefix)
     steps = 0
     for rp, rafter in osch.run(ref, width):
         n, q, mb = ours.schedule()
@@ -33,6 +37,8 @@ def _replay_both(tr, width):
             a, b = getattr(p, name), getattr(rp, name)
             assert a.dtype == b.dtype and a.shape == b.shape and (a == b).all(), f"step {rp.step}: {name}"
         ours.update()
+        if prefix:                             # shared blocks: the same reference counts
+            assert (pool.block_refs() == np.asarray(ref.tables.ref)).all(), f"step {rp.step}: refs"
         c = ours.counters()
         assert {k: c[k] for k in rafter} == rafter, f"step {rp.step} after update"
         steps += 1
@@ -117,3 +123,32 @@ def test_admission_without_memory_check_fails_at_the_same_step(seed, pool_blocks
     # with the check in place the same trace completes
     steps, _ = _replay_both(tr, 20)
     assert steps > failed_ref
+
+
+def test_prefix_config5_full_trace_bit_exact_every_step():
+    tr = workloads.config5_prefix()
+    steps, ref = _replay_both(tr, 512, prefix=True)
+    assert ref.cached_tokens > 0 and ref.preemptions > 0
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(0, 10_000), st.integers(24, 80), st.integers(1, 8), st.integers(1, 4))
+def test_prefix_random_small_traces_bit_exact(seed, pool, max_running, groups):
+    tr = workloads.small_trace(seed, 30, pool, block_size=4, max_running=max_running, prompt_max=24, out_max=16,
+                               rate=2.0, groups=groups)
+    _replay_both(tr, 20, prefix=True)
+
+
+def test_prefix_cache_api_errors():
+    pool = pkv.Pool(16, 4, 1, 64, "bf16")
+    s = pkv.Scheduler(pool, 2)
+    s.add_requests([1, 2], [0, 0], [5, 6], [2, 2])
+    with pytest.raises(pkv.PkvError):
+        s.enable_prefix_cache({1: [1, 2, 3]})              # 3 tokens for a 5-token prompt
+    with pytest.raises(pkv.PkvError):
+        s.enable_prefix_cache({7: [1, 2, 3, 4, 5]})        # unknown request
+    s.enable_prefix_cache({1: [1, 2, 3, 4, 5]})
+    s.schedule()
+    s.update()
+    with pytest.raises(pkv.PkvError):
+        s.enable_prefix_cache()                            # after the first step

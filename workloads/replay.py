@@ -34,7 +34,8 @@ class StepRecord:
 
 
 class Replay:
-    def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0):
+    def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
+                 prefix_cache: bool = True):
         import torch
         self.torch = torch
         self.tr = tr
@@ -49,11 +50,15 @@ class Replay:
         else:
             self.k_cache = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
         self.v_cache = torch.zeros_like(self.k_cache)
-        # stream keys of (layer, kind, request), kind = q, k, v
-        self.keys = np.zeros((tr.num_layers, 3, tr.num_requests), np.uint64)
+        # stream keys of (layer, kind, owner), kind = q, k, v; owners = requests, then groups
+        groups = 0 if tr.prefix_group is None else int(tr.prefix_group.max()) + 1
+        self.keys = np.zeros((tr.num_layers, 3, tr.num_requests + groups), np.uint64)
         for l in range(tr.num_layers):
             for k, which in enumerate("qkv"):
-                self.keys[l, k] = [tr.value_key(which, l, r) for r in range(tr.num_requests)]
+                self.keys[l, k] = [tr.value_key(which, l, o) for o in
+                                   list(range(tr.num_requests)) + [workloads.GROUP_OWNER + g for g in range(groups)]]
+        if prefix_cache and tr.prefix_group is not None:     # shared system prompts
+            self.sched.enable_prefix_cache([tr.prompt_tokens(r) for r in range(tr.num_requests)])
         self.heads = np.array([tr.num_q_heads, tr.num_kv_heads, tr.num_kv_heads], np.int64)
         self.buf = None
         self.e_kv = 1 if tr.cache_dtype == "fp8" else 2
@@ -66,22 +71,33 @@ class Replay:
 
     def _values(self, ids, q_lens, seq_lens):
         """Generate Q/K/V of the step's new tokens for every layer into one buffer; return
-        per-layer views (q [T][Hq][d], k [T][Hkv][d], v [T][Hkv][d])."""
+        per-layer views (q [T][Hq][d], k [T][Hkv][d], v [T][Hkv][d]). A row's positions may
+        come from two streams (a group's shared prompt, then the request's own tokens)."""
         torch, tr = self.torch, self.tr
-        T, d, n, NL = int(q_lens.sum()), tr.head_dim, len(ids), tr.num_layers
+        T, d, NL = int(q_lens.sum()), tr.head_dim, tr.num_layers
         per_layer = T * d * int(self.heads.sum())
         if self.buf is None or self.buf.numel() < NL * per_layer:
             self.buf = torch.empty(max(NL * per_layer, 1 << 20), dtype=torch.bfloat16, device="cuda")
-        first = (seq_lens - q_lens).astype(np.int64)
-        # segment order: layer, kind, row -> each (layer, kind) region is [T][heads][d]
-        keys = self.keys[:, :, ids].reshape(-1).view(np.int64)
-        heads = np.broadcast_to(self.heads[None, :, None], (NL, 3, n)).reshape(-1)
-        q64 = np.broadcast_to(q_lens.astype(np.int64)[None, None, :], (NL, 3, n)).reshape(-1)
-        e0 = np.broadcast_to(first[None, None, :], (NL, 3, n)).reshape(-1) * heads * d
-        off = np.zeros(3 * NL * n + 1, np.int64)
-        np.cumsum(q64 * heads * d, out=off[1:])
+        # owner segments of the rows, in row order: (owner, first position, length)
+        segs = [(owner, lo, hi - lo) for r, q, L in zip(ids, q_lens, seq_lens)
+                for owner, lo, hi in tr.owner_segments(int(r), int(L - q), int(L))]
+        owners = np.array([o for o, _, _ in segs], np.int64)
+        pos0 = np.array([p for _, p, _ in segs], np.int64)
+        lens = np.array([n for _, _, n in segs], np.int64)
+        keys, e0s, sizes = [], [], []
+        # segment order: layer, kind, row segment -> each (layer, kind) region is [T][heads][d]
+        for l in range(NL):
+            for k, which in enumerate("qkv"):
+                h = int(self.heads[k])
+                keys.append(self._keys(l, which, owners))
+                e0s.append(pos0 * h * d)
+                sizes.append(lens * h * d)
+        keys = np.concatenate(keys).view(np.int64)
+        e0 = np.concatenate(e0s)
+        off = np.zeros(len(e0) + 1, np.int64)
+        np.cumsum(np.concatenate(sizes), out=off[1:])
         seg = torch.from_numpy(np.concatenate([keys, e0, off])).cuda()
-        wgen.fill_segments(self.buf, seg, 3 * NL * n, int(off[-1]), tr.sigma)
+        wgen.fill_segments(self.buf, seg, len(e0), int(off[-1]), tr.sigma)
         views = []
         o = 0
         for l in range(NL):
@@ -92,6 +108,12 @@ class Replay:
                 o += m
             views.append(parts)
         return views
+
+    def _keys(self, layer, which, owners):
+        """Value-stream keys (uint64) of the owners (requests, then groups) for one layer/kind."""
+        R = self.tr.num_requests
+        idx = np.where(owners >= workloads.GROUP_OWNER, R + (owners - workloads.GROUP_OWNER), owners)
+        return self.keys[layer, "qkv".index(which)][idx]
 
     def step(self, keep_layers: Sequence[int] = (), keep_plan: bool = False) -> Optional[StepRecord]:
         torch, tr = self.torch, self.tr
@@ -180,12 +202,14 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
         "trace": tr.name, "cache_dtype": tr.cache_dtype, "steps": int(c["step"]), "requests": tr.num_requests,
         "finished": int(c["finished"]), "preemptions": int(c["preempted"]),
         "preemption_rate_per_step": round(c["preempted"] / max(c["step"], 1), 4),
+        "cached_prompt_tokens": int(c["cached_tokens"]),
         "avg_running_batch": round(float(rows.mean()), 2), "query_tokens": int(qtok.sum()),
         "context_tokens_per_layer": int(sum(r.context_tokens for r in recs)),
         "attention_s_total": round(float(t.sum()), 4),
         "tokens_per_s_per_step": {"mean": round(float(tps.mean()), 1), "p50": round(float(np.percentile(tps, 50)), 1),
                                   "p99": round(float(np.percentile(tps, 99)), 1)},
         "tokens_per_s_overall": round(float(qtok.sum() / t.sum()), 1),
+        "requests_per_s": round(float(c["finished"] / t.sum()), 2),      # per second of attention
         "hbm_GBps_per_step": {"mean": round(float((byts / t).mean() / 1e9), 1),
                               "p50": round(float(np.percentile(byts / t, 50) / 1e9), 1)},
         "hbm_GBps_overall": round(float(byts.sum() / t.sum() / 1e9), 1),
