@@ -25,7 +25,16 @@ Readings taken where the page leaves a step open (each listed with the others):
   * a request finishes when its output count reaches max_tokens (no EOS: no model);
   * arrivals: the requests whose arrival step is <= the current step join the back of
     the waiting queue in (arrival, id) order at the start of the step;
-  * a step with nothing running emits no rows (the loop returns before the forward).
+  * a step with nothing running emits no rows (the loop returns before the forward);
+  * chunked prefill (the mixed batching of "5. Technical explanation", off unless a
+    budget or a chunk size is given): a step carries at most max_batched_tokens new
+    tokens. Decode rows are never cut (one token each, even past the budget); what the
+    budget leaves goes to prefill rows in running order, each taking the least of its
+    uncomputed context, chunk_tokens and the budget left, so a request can get no row
+    in a step. A chunk holds positions done..done+q-1 and sees every position below
+    done+q; the request's first output comes at the step of its last chunk; its blocks
+    are still all reserved at admission, and its prompt pages enter the prefix cache
+    only once the prefill is complete.
 
 Parity unpinned beyond invariants and hand-worked traces: the pages print no trace of
 this loop, so the tests pin it with small traces worked out by hand from the page's
@@ -59,6 +68,8 @@ class Req:
     finished_step: int = -1
     tokens: Optional[Tuple[int, ...]] = None   # prompt token ids (prefix caching)
     cached: int = 0                            # prompt tokens of this prefill found in the cache
+    done: int = 0                              # context tokens of the current prefill computed so far
+    q_step: int = 0                            # new tokens of this request's row in the current step
 
 
 @dataclasses.dataclass
@@ -78,7 +89,8 @@ class StepPlan:
 class Scheduler:
     def __init__(self, arrival, prompt, max_tokens, num_blocks: int, free_order, block_size: int,
                  max_running: int, admission_check: bool = True,
-                 prompt_tokens: Optional[Sequence[Sequence[int]]] = None):
+                 prompt_tokens: Optional[Sequence[Sequence[int]]] = None, max_batched_tokens: int = 0,
+                 chunk_tokens: int = 0):
         self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
         # prompt_tokens given: prefix caching over shared blocks (oracle/prefix.py)
         self.pcache = None
@@ -100,6 +112,13 @@ class Scheduler:
         # (its admission loop pops the head and prefills it with no memory check): the head
         # is taken off the queue and its allocation may raise OutOfBlocks out of the step
         self.admission_check = admission_check
+        # chunked prefill ([CB] "5. Technical explanation", mixed batching): at most
+        # max_batched_tokens new tokens per step (0: no limit), decode rows first, then
+        # prefill chunks of at most chunk_tokens (0: no limit) in running order
+        self.max_batched_tokens = int(max_batched_tokens)
+        self.chunk_tokens = int(chunk_tokens)
+        if self.max_batched_tokens < 0 or self.chunk_tokens < 0:
+            raise ValueError("token budget and chunk size must be >= 0")
         self.waiting: collections.deque = collections.deque()
         self.running: List[Req] = []
         self.step_no = 0
@@ -143,15 +162,33 @@ class Scheduler:
             self.tables.reserve(r.rid, ctx)                         # all-or-nothing; unchecked: may raise
             r.stage = PREFILL
             r.cached = n_hit
+            r.done = n_hit
             self.cached_tokens += n_hit
             self.running.append(r)
+        # this step's new tokens per running request: decode rows first, then prefill
+        # chunks in running order within what the budget leaves
+        budget = None
+        if self.max_batched_tokens > 0:
+            budget = max(0, self.max_batched_tokens - sum(r.stage == DECODE for r in self.running))
+        for r in self.running:
+            if r.stage == DECODE:
+                r.q_step = 1
+                continue
+            q = r.prompt + r.n_out - r.done
+            if self.chunk_tokens > 0:
+                q = min(q, self.chunk_tokens)
+            if budget is not None:
+                q = min(q, budget)
+                budget -= q
+            r.q_step = q
         ids, stages, q, L = [], [], [], []
         for r in self.running:
-            ctx = r.prompt + r.n_out
+            if r.q_step == 0:
+                continue                                            # no row this step
             ids.append(r.rid)
             stages.append(r.stage)
-            q.append(ctx - r.cached if r.stage == PREFILL else 1)
-            L.append(ctx)
+            q.append(r.q_step)
+            L.append(r.done + r.q_step if r.stage == PREFILL else r.prompt + r.n_out)
         tabs = [self.tables.tables[i] for i in ids]
         bt, cu, slots = build_block_table(tabs, q, L, self.bs, width)
         return StepPlan(s, np.asarray(ids, np.int64), np.asarray(stages, np.int32), np.asarray(q, np.int32),
@@ -159,12 +196,20 @@ class Scheduler:
 
     # -- second half: one output token per row, retire, grow or preempt --------------
     def update(self) -> None:
-        if self.pcache is not None:                                 # this step wrote these pages
+        for r in self.running:
+            if r.stage == PREFILL:
+                r.done += r.q_step
+        if self.pcache is not None:                                 # prefills completed: their pages
             for r in self.running:
-                if r.stage == PREFILL:
+                if r.stage == PREFILL and r.done == r.prompt + r.n_out:
                     self.pcache.insert(r.tokens, self.tables.tables[r.rid], r.prompt)
         still = []
         for r in self.running:
+            had_row = r.q_step > 0
+            r.q_step = 0
+            if not had_row or (r.stage == PREFILL and r.done < r.prompt + r.n_out):
+                still.append(r)                                     # no output this step
+                continue
             r.cached = 0
             r.n_out += 1
             r.stage = DECODE
