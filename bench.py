@@ -301,14 +301,17 @@ def sched_replay(max_steps):
     import workloads
     from workloads import replay
     out = {}
-    runs = [("bf16", workloads.config5("bf16"), True), ("fp8", workloads.config5("fp8"), True),
+    runs = [("bf16", workloads.config5("bf16"), {}), ("fp8", workloads.config5("fp8"), {}),
+            # chunked prefill: at most 2048 new tokens per step, prefills in chunks of 512
+            ("bf16_chunked_2048_512", workloads.config5("bf16"), {"token_budget": 2048, "chunk_tokens": 512}),
             # shared system prompts (16 groups), with and without the prefix cache
-            ("bf16_prefix_cache", workloads.config5_prefix("bf16"), True),
-            ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), False)]
-    for name, tr, cache in runs:
-        print(f"[bench] replay {tr.name} (prefix cache {'on' if cache else 'off'})", file=sys.stderr, flush=True)
-        _, summ = replay.run(tr, max_steps=max_steps, prefix_cache=cache,
+            ("bf16_prefix_cache", workloads.config5_prefix("bf16"), {}),
+            ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), {"prefix_cache": False})]
+    for name, tr, kw in runs:
+        print(f"[bench] replay {name}: {tr.name} {kw}", file=sys.stderr, flush=True)
+        _, summ = replay.run(tr, max_steps=max_steps, **kw,
                              progress=lambda n: print(f"[bench] replay {name}: {n} steps", file=sys.stderr, flush=True))
+        summ.update({k: v for k, v in kw.items() if k != "prefix_cache"})
         out[name] = summ
     return out
 

@@ -354,7 +354,8 @@ int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype
  *     token, the last output, at position prompt + outputs - 1), q_len, seq_len -- and
  *     their block_tables / cu_seqlens_q / slot_mapping as pkv_build_block_table makes
  *     them (host arrays; block_tables [rows][table_width], slot_mapping [total q]).
- *   pkv_sched_update: in running order, one output token per row; a request with
+ *   pkv_sched_update: in running order, one output token per decode row and per prefill
+ *     row that completes its context (see chunked prefill below); a request with
  *     max_tokens outputs finishes and frees its table at once; one whose next token needs
  *     a new block reserves one, or, if none is free, is preempted: its table is freed and
  *     it goes to the front of the waiting queue (several preempted in one step end up in
@@ -374,7 +375,18 @@ int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype
  * prefill row then holds only the uncached tokens (q = context - cached, positions from
  * the cached length). At each update, the whole prompt pages of the step's prefill rows
  * are registered (an existing usable entry stays). An entry dies with its pages: a block
- * freed since it was registered makes it unusable. */
+ * freed since it was registered makes it unusable.
+ * Chunked prefill under a token budget ([CB] "5. Technical explanation", mixed batching),
+ * off unless set before the first step: the rows of a step then carry at most
+ * max_batched_tokens new tokens. Every decode row is kept (one token each, even beyond
+ * the budget); what is left goes to the prefill rows in running order, each taking the
+ * least of its uncomputed context, chunk_tokens and the budget left. A running request
+ * that gets 0 tokens has no row in that step (rows are the running requests with tokens,
+ * in running order). A prefill row holds positions done..done+q-1 of the context (done:
+ * tokens computed by its earlier chunks or found in the prefix cache) with seq_len =
+ * done + q; the request gets its first output, and its prompt pages enter the prefix
+ * cache, only at the update of the step that computes its last chunk. Blocks for the
+ * whole context are still reserved at admission. */
 typedef struct pkv_sched pkv_sched;
 int pkv_sched_create(pkv_pool* pool, int32_t max_running, pkv_sched** out);
 void pkv_sched_destroy(pkv_sched* sched);
@@ -391,6 +403,10 @@ int pkv_sched_enable_prefix_cache(pkv_sched* sched);
 /* Prompt token ids of request id (host int32 [n], n = its prompt length), before the first
  * step; requests without tokens neither hit nor fill the prefix cache. */
 int pkv_sched_set_prompt_tokens(pkv_sched* sched, int64_t id, const int32_t* tokens, int32_t n);
+/* Token budget per step and prefill chunk size (before the first step; see above); 0 for
+ * either means no limit (the default, which gives every prefill its whole context in one
+ * row). Negative values are INVALID. */
+int pkv_sched_set_token_budget(pkv_sched* sched, int32_t max_batched_tokens, int32_t chunk_tokens);
 
 /* Admission without the memory check (enabled = 0), the sabotage of the "Break It"
  * experiment of [P17]: pkv_sched_schedule takes the head of the waiting queue off it and

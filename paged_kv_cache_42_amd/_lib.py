@@ -75,6 +75,7 @@ _SIGS = {
     "pkv_sched_set_admission_check": (C.c_int, [vp, i32]),
     "pkv_sched_enable_prefix_cache": (C.c_int, [vp]),
     "pkv_sched_set_prompt_tokens": (C.c_int, [vp, i64, vp, i32]),
+    "pkv_sched_set_token_budget": (C.c_int, [vp, i32, i32]),
     "pkv_seq_share": (C.c_int, [vp, i64, vp, i32]),
     "pkv_block_refs": (C.c_int, [vp, vp, i32]),
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
@@ -150,6 +151,11 @@ class Scheduler:
         for rid, tok in items:
             t = np.ascontiguousarray(tok, dtype=np.int32)
             check(lib().pkv_sched_set_prompt_tokens(self._h, int(rid), _np_ptr(t), len(t)))
+
+    def set_token_budget(self, max_batched_tokens: int, chunk_tokens: int = 0) -> None:
+        """Chunked prefill: at most max_batched_tokens new tokens per step, prefills cut into
+        chunks of at most chunk_tokens (0: no limit); before the first step."""
+        check(lib().pkv_sched_set_token_budget(self._h, int(max_batched_tokens), int(chunk_tokens)))
 
     def counters(self) -> dict:
         out = np.zeros(8, np.int64)

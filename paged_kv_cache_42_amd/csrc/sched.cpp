@@ -11,6 +11,12 @@
 // re-prefills both); a prefill row holds those tokens at positions 0..; a decode row is
 // the last output token; a request finishes at its output count; arrivals join the
 // back of the queue at the start of their step in (arrival, id) order.
+//
+// Chunked prefill (the mixed batching of "5. Technical explanation", off by default): a
+// step carries at most max_batched_tokens new tokens. Decode rows are never cut; the rest
+// of the budget goes to prefill rows in running order, each taking the least of its
+// uncomputed context, chunk_tokens and what is left, so a request may get no row. A
+// request produces its first output at the step of its last chunk.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
@@ -32,6 +38,8 @@ struct Req {
   int32_t n_out = 0;
   int32_t stage = kPrefill;
   int32_t cached = 0;                  // prompt tokens of this prefill found in the cache
+  int32_t done = 0;                    // context tokens of the current prefill computed so far
+  int32_t q_step = 0;                  // new tokens of its row in the scheduled step (0: no row)
   std::vector<int32_t> tokens;         // prompt token ids (prefix caching), else empty
 };
 
@@ -75,6 +83,9 @@ struct pkv_sched {
   std::unordered_map<uint64_t, PrefixEntry> cache;
   std::unordered_map<int64_t, int32_t> index;   // request id -> index in reqs
   int64_t cached_tokens = 0;
+  int32_t max_batched_tokens = 0;       // 0: no per-step token budget
+  int32_t chunk_tokens = 0;             // 0: prefills are not cut into chunks
+  std::vector<int32_t> rows;            // running requests with a row this step, in running order
 
   // page-chained keys of tokens[0 : k * bs] for k = 1..pages
   std::vector<uint64_t> page_keys(const std::vector<int32_t>& tok, int64_t pages) const {
@@ -205,18 +216,39 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
                   "does not check", (long long)s->step, (long long)r.id);
     r.stage = kPrefill;
     r.cached = hit;
+    r.done = hit;
     s->cached_tokens += hit;
     s->running.push_back(head);
   }
+  // new tokens per running request: decode rows first, then prefill chunks in running
+  // order within what the budget leaves
+  int64_t left = INT64_MAX;
+  if (s->max_batched_tokens > 0) {
+    int64_t decodes = 0;
+    for (int32_t i : s->running) decodes += s->reqs[i].stage == kDecode;
+    left = std::max<int64_t>(0, s->max_batched_tokens - decodes);
+  }
+  s->rows.clear();
   int64_t q = 0, mb = 0;
   for (int32_t i : s->running) {
-    const Req& r = s->reqs[i];
+    Req& r = s->reqs[i];
     const int64_t ctx = int64_t(r.prompt) + r.n_out;
-    q += r.stage == kPrefill ? ctx - r.cached : 1;
-    mb = std::max<int64_t>(mb, (ctx + s->pool->block_size - 1) / s->pool->block_size);
+    int64_t qi = 1, len = ctx;
+    if (r.stage == kPrefill) {
+      qi = ctx - r.done;
+      if (s->chunk_tokens > 0) qi = std::min<int64_t>(qi, s->chunk_tokens);
+      qi = std::min(qi, left);
+      left -= qi;
+      len = r.done + qi;
+    }
+    r.q_step = int32_t(qi);
+    if (qi == 0) continue;                // no row this step
+    s->rows.push_back(i);
+    q += qi;
+    mb = std::max<int64_t>(mb, (len + s->pool->block_size - 1) / s->pool->block_size);
   }
   s->scheduled = true;
-  if (num_rows) *num_rows = int32_t(s->running.size());
+  if (num_rows) *num_rows = int32_t(s->rows.size());
   if (total_q) *total_q = int32_t(q);
   if (max_blocks) *max_blocks = int32_t(mb);
   return PKV_OK;
@@ -226,16 +258,15 @@ int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_
                    int32_t* seq_lens, int32_t* block_tables, int32_t* cu_seqlens_q, int64_t* slot_mapping) {
   if (!s) return fail(PKV_ERR_INVALID, "sched_plan: scheduler is NULL");
   if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_plan: no step scheduled");
-  const int32_t n = int32_t(s->running.size());
+  const int32_t n = int32_t(s->rows.size());
   if (n > 0 && (!ids || !stages || !q_lens || !seq_lens))
     return fail(PKV_ERR_INVALID, "sched_plan: NULL row array");
   for (int32_t k = 0; k < n; ++k) {
-    const Req& r = s->reqs[s->running[k]];
-    const int32_t ctx = r.prompt + r.n_out;
+    const Req& r = s->reqs[s->rows[k]];
     ids[k] = r.id;
     stages[k] = r.stage;
-    q_lens[k] = r.stage == kPrefill ? ctx - r.cached : 1;
-    seq_lens[k] = ctx;
+    q_lens[k] = r.q_step;
+    seq_lens[k] = r.stage == kPrefill ? r.done + r.q_step : r.prompt + r.n_out;
   }
   return pkv_build_block_table(s->pool, n, ids, q_lens, seq_lens, table_width, block_tables, cu_seqlens_q,
                                slot_mapping);
@@ -244,13 +275,25 @@ int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_
 int pkv_sched_update(pkv_sched* s) {
   if (!s) return fail(PKV_ERR_INVALID, "sched_update: scheduler is NULL");
   if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_update: no step scheduled");
-  if (s->prefix_cache)                  // this step wrote the prefill rows' pages
-    for (int32_t i : s->running)
-      if (s->reqs[i].stage == kPrefill && !s->reqs[i].tokens.empty()) s->insert(i);
+  for (int32_t i : s->running) {
+    Req& r = s->reqs[i];
+    if (r.stage == kPrefill) r.done += r.q_step;
+  }
+  if (s->prefix_cache)                  // prefills completed this step: their prompt pages
+    for (int32_t i : s->running) {
+      const Req& r = s->reqs[i];
+      if (r.stage == kPrefill && r.done == r.prompt + r.n_out && !r.tokens.empty()) s->insert(i);
+    }
   std::vector<int32_t> still;
   still.reserve(s->running.size());
   for (int32_t i : s->running) {
     Req& r = s->reqs[i];
+    const bool had_row = r.q_step > 0;
+    r.q_step = 0;
+    if (!had_row || (r.stage == kPrefill && r.done < r.prompt + r.n_out)) {
+      still.push_back(i);                 // no output this step
+      continue;
+    }
     r.cached = 0;
     r.n_out += 1;
     r.stage = kDecode;
@@ -269,6 +312,7 @@ int pkv_sched_update(pkv_sched* s) {
     still.push_back(i);
   }
   s->running.swap(still);
+  s->rows.clear();
   s->scheduled = false;
   ++s->step;
   return PKV_OK;
@@ -277,6 +321,16 @@ int pkv_sched_update(pkv_sched* s) {
 int pkv_sched_set_admission_check(pkv_sched* s, int32_t enabled) {
   if (!s) return fail(PKV_ERR_INVALID, "sched_set_admission_check: scheduler is NULL");
   s->admission_check = enabled != 0;
+  return PKV_OK;
+}
+
+int pkv_sched_set_token_budget(pkv_sched* s, int32_t max_batched_tokens, int32_t chunk_tokens) {
+  if (!s || max_batched_tokens < 0 || chunk_tokens < 0)
+    return fail(PKV_ERR_INVALID, "sched_set_token_budget: bad arguments");
+  if (s->step > 0 || s->scheduled)
+    return fail(PKV_ERR_INVALID, "sched_set_token_budget: call before the first step");
+  s->max_batched_tokens = max_batched_tokens;
+  s->chunk_tokens = chunk_tokens;
   return PKV_OK;
 }
 

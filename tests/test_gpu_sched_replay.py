@@ -28,7 +28,8 @@ def _check_step(tr, rec, rng, max_rows=8, tokens_per_row=3):
     plan = rec.plan
     cu = plan.cu_seqlens_q
     rows = list(range(len(plan.ids)))
-    pre = [r for r in rows if plan.stages[r] == 0]
+    # prefill rows, later chunks of a cut prefill (or rows after a cached prefix) first
+    pre = sorted((r for r in rows if plan.stages[r] == 0), key=lambda r: plan.q_lens[r] == plan.seq_lens[r])
     dec = [r for r in rows if plan.stages[r] == 1]
     pick = pre[:max_rows // 2] + list(rng.choice(dec, size=min(len(dec), max_rows - min(len(pre), max_rows // 2)),
                                                  replace=False))
@@ -92,6 +93,33 @@ def test_prefix_trace_replay_sampled_parity():
     assert summary["cached_prompt_tokens"] > 0
     by_step = {r.step: r for r in recs}
     rng = np.random.default_rng(7)
+    checked = 0
+    for s in keep_steps:
+        checked += _check_step(tr, by_step[s], rng)
+    assert checked >= 12
+
+
+def test_chunked_prefill_replay_sampled_parity():
+    # token budget 2048, chunks of 512: long prompts are computed over several steps; a
+    # later chunk attends over the K/V its request's earlier chunks wrote in earlier steps
+    from oracle import scheduler as osch
+    tr = workloads.config5("bf16")
+    ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
+                         tr.max_running, max_batched_tokens=2048, chunk_tokens=512)
+    chunk_steps = []
+    for plan, _ in osch.run(ref, 512, 140):
+        later = (plan.stages == 0) & (plan.q_lens < plan.seq_lens)
+        if later.any() and (plan.q_lens[later] > 1).any():
+            chunk_steps.append(plan.step)
+    assert len(chunk_steps) >= 4
+    keep_steps = chunk_steps[:2] + chunk_steps[-2:]
+    keep = {s: (0, tr.num_layers - 1) for s in keep_steps}
+    recs, summary = replay.run(tr, max_steps=140, keep=keep, token_budget=2048, chunk_tokens=512)
+    assert summary["steps"] == 140
+    by_step = {r.step: r for r in recs}
+    for s in keep_steps:                       # the device replay took the oracle's schedule
+        assert int(by_step[s].q_tokens) <= 2048 + int((by_step[s].plan.stages == 1).sum())
+    rng = np.random.default_rng(11)
     checked = 0
     for s in keep_steps:
         checked += _check_step(tr, by_step[s], rng)

@@ -9,7 +9,7 @@ import workloads
 from oracle import scheduler as osch
 
 
-def _pair(tr, prefix=False):
+def _pair(tr, prefix=False, budget=0, chunk=0):
     pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
                     free_order=tr.free_order)
     ours = pkv.Scheduler(pool, tr.max_running)
@@ -18,13 +18,15 @@ def _pair(tr, prefix=False):
     if prefix:
         toks = [tr.prompt_tokens(r) for r in range(tr.num_requests)]
         ours.enable_prefix_cache(toks)
+    if budget or chunk:
+        ours.set_token_budget(budget, chunk)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
-                         tr.max_running, prompt_tokens=toks)
+                         tr.max_running, prompt_tokens=toks, max_batched_tokens=budget, chunk_tokens=chunk)
     return pool, ours, ref
 
 
-def _replay_both(tr, width, prefix=False):
-    pool, ours, ref = _pair(tr, prefix)
+def _replay_both(tr, width, prefix=False, budget=0, chunk=0):
+    pool, ours, ref = _pair(tr, prefix, budget, chunk)
     steps = 0
     for rp, rafter in osch.run(ref, width):
         n, q, mb = ours.schedule()
@@ -152,3 +154,40 @@ def test_prefix_cache_api_errors():
     s.update()
     with pytest.raises(pkv.PkvError):
         s.enable_prefix_cache()                            # after the first step
+
+
+def test_chunked_config5_full_trace_bit_exact_every_step():
+    tr = workloads.config5()
+    steps, ref = _replay_both(tr, 512, budget=2048, chunk=512)
+    assert ref.preemptions > 0 and steps == ref.step_no
+
+
+def test_chunked_prefix_config5_full_trace_bit_exact_every_step():
+    tr = workloads.config5_prefix()
+    steps, ref = _replay_both(tr, 512, prefix=True, budget=1024, chunk=256)
+    assert ref.cached_tokens > 0
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(0, 10_000), st.integers(18, 60), st.integers(1, 8), st.sampled_from([0, 1, 3, 8, 24]),
+       st.sampled_from([0, 1, 4, 16]), st.booleans())
+def test_chunked_random_small_traces_bit_exact(seed, pool, max_running, budget, chunk, prefix):
+    tr = workloads.small_trace(seed, 30, max(pool, 24 if prefix else 18), block_size=4, max_running=max_running,
+                               prompt_max=24 if prefix else 40, out_max=16 if prefix else 30, rate=2.0,
+                               groups=3 if prefix else 0)
+    _replay_both(tr, 20, prefix=prefix, budget=budget, chunk=chunk)
+
+
+def test_token_budget_api_errors():
+    pool = pkv.Pool(16, 4, 1, 64, "bf16")
+    s = pkv.Scheduler(pool, 2)
+    s.add_requests([1, 2], [0, 0], [5, 6], [2, 2])
+    for bad in ((-1, 0), (0, -4)):
+        with pytest.raises(pkv.PkvError):
+            s.set_token_budget(*bad)
+    s.set_token_budget(4, 2)
+    n, q, mb = s.schedule()
+    assert (n, q, mb) == (2, 4, 1)                         # 2 + 2 tokens, chunks of at most 2
+    s.update()
+    with pytest.raises(pkv.PkvError):
+        s.set_token_budget(8, 0)                           # after the first step

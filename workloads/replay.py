@@ -31,11 +31,12 @@ class StepRecord:
     ev: tuple                    # (start, end) events around the layers' write + attention
     kept: Dict[int, object]      # layer -> output tensor [T][Hq][d] (only for kept layers)
     plan: Optional[object] = None
+    first_outputs: Sequence[int] = ()   # requests whose first output token this step made
 
 
 class Replay:
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
-                 prefix_cache: bool = True):
+                 prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0):
         import torch
         self.torch = torch
         self.tr = tr
@@ -59,6 +60,9 @@ class Replay:
                                    list(range(tr.num_requests)) + [workloads.GROUP_OWNER + g for g in range(groups)]]
         if prefix_cache and tr.prefix_group is not None:     # shared system prompts
             self.sched.enable_prefix_cache([tr.prompt_tokens(r) for r in range(tr.num_requests)])
+        if token_budget or chunk_tokens:                       # chunked prefill
+            self.sched.set_token_budget(token_budget, chunk_tokens)
+        self.n_out = np.zeros(tr.num_requests, np.int64)        # outputs per request so far
         self.heads = np.array([tr.num_q_heads, tr.num_kv_heads, tr.num_kv_heads], np.int64)
         self.buf = None
         self.e_kv = 1 if tr.cache_dtype == "fp8" else 2
@@ -161,13 +165,18 @@ class Replay:
                 kept[l] = out.clone()
         e1.record()
         self.sched.update()
+        # a row makes an output token when it decodes or completes its context
+        ids = plan.ids
+        made = (plan.stages == 1) | (seq_lens == self.tr.prompt[ids] + self.n_out[ids])
+        first = ids[made & (self.n_out[ids] == 0)]
+        self.n_out[ids[made]] += 1
         ctx = int(seq_lens.sum())
         row_bytes = 2 * tr.num_kv_heads * tr.head_dim
         per_layer = (ctx * row_bytes * self.e_kv                              # K/V read by attention
                      + T * row_bytes * (2 + self.e_kv)                        # write: bf16 in, cache out
                      + T * tr.num_q_heads * tr.head_dim * 2 * 2)              # queries in, outputs out
         return StepRecord(step_no, n, T, ctx, int((plan.stages == 0).sum()), per_layer * tr.num_layers,
-                          (e0, e1), kept, plan if keep_plan else None)
+                          (e0, e1), kept, plan if keep_plan else None, first.tolist())
 
 
 def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progress=None, **replay_args):
@@ -198,6 +207,24 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
     byts = np.array([r.attention_bytes for r in recs], np.float64)
     rows = np.array([r.rows for r in recs], np.float64)
     tps = qtok / t
+    # latencies in attention time (the GPU time of the steps' layers; host time excluded):
+    # time to first token from the start of the arrival step to the end of the step that
+    # made the first output; time between tokens = the time of each decode row's step
+    nsteps = int(c["step"])
+    t_step = np.zeros(nsteps + 1)
+    first_step = np.full(tr.num_requests, -1, np.int64)
+    for r, ti in zip(recs, t):
+        t_step[r.step] = ti
+        first_step[list(r.first_outputs)] = r.step
+    t_end = np.cumsum(t_step)
+    got = first_step >= 0
+    ttft = t_end[first_step[got]] - (t_end[tr.arrival[got]] - t_step[tr.arrival[got]])
+    dec = np.array([r.rows - r.prefill_rows for r in recs], np.int64)
+    tbt = np.repeat(t, dec)
+
+    def pct(x, qs=(50, 99)):
+        return {f"p{q}": round(float(np.percentile(x, q)) * 1e3, 3) for q in qs} if len(x) else {}
+
     summary = {
         "trace": tr.name, "cache_dtype": tr.cache_dtype, "steps": int(c["step"]), "requests": tr.num_requests,
         "finished": int(c["finished"]), "preemptions": int(c["preempted"]),
@@ -213,6 +240,8 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
         "hbm_GBps_per_step": {"mean": round(float((byts / t).mean() / 1e9), 1),
                               "p50": round(float(np.percentile(byts / t, 50) / 1e9), 1)},
         "hbm_GBps_overall": round(float(byts.sum() / t.sum() / 1e9), 1),
+        "step_ms": {**pct(t, (50, 90, 99)), "max": round(float(t.max()) * 1e3, 3) if len(t) else 0.0},
+        "ttft_ms": pct(ttft), "tbt_ms": pct(tbt),
         "wall_s": round(wall, 2),
     }
     return recs, summary
