@@ -50,6 +50,8 @@ def parse_args():
                     help="skip the continuous-batching trace replay (2000 requests, scheduler step + 16 layers of "
                          "cache write and mixed attention per step, bf16 and E4M3 caches)")
     ap.add_argument("--replay-steps", type=int, default=None, help="replay only the first N scheduler steps")
+    ap.add_argument("--replay-budget-sweep", action="store_true",
+                    help="also replay the bf16 trace under several token budgets / chunk sizes (chunked prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
@@ -293,6 +295,24 @@ def mixed_step(steps: int, warmup: int):
     return res
 
 
+BUDGET_SWEEP = ((1024, 512), (2048, 512), (4096, 1024), (8192, 2048))
+
+
+def replay_budget_sweep(max_steps):
+    """The bf16 trace under per-step token budgets with chunked prefill (key-cut chunk
+    work): the prefill-throughput / decode-latency trade of the budget."""
+    import workloads
+    from workloads import replay
+    out = {}
+    for budget, chunk in BUDGET_SWEEP:
+        name = f"budget_{budget}_chunk_{chunk}"
+        print(f"[bench] replay sweep {name}", file=sys.stderr, flush=True)
+        _, summ = replay.run(workloads.config5("bf16"), max_steps=max_steps, token_budget=budget,
+                             chunk_tokens=chunk, chunk_cut=True)
+        out[name] = summ
+    return out
+
+
 def sched_replay(max_steps):
     """Continuous-batching trace replay (the 2000-request trace): per step the host
     scheduler admits/plans/updates and 16 layers run the cache write and the mixed
@@ -303,7 +323,8 @@ def sched_replay(max_steps):
     out = {}
     runs = [("bf16", workloads.config5("bf16"), {}), ("fp8", workloads.config5("fp8"), {}),
             # chunked prefill: at most 2048 new tokens per step, prefills in chunks of 512
-            ("bf16_chunked_2048_512", workloads.config5("bf16"), {"token_budget": 2048, "chunk_tokens": 512}),
+            ("bf16_chunked_2048_512", workloads.config5("bf16"),
+             {"token_budget": 2048, "chunk_tokens": 512, "chunk_cut": True}),
             # shared system prompts (16 groups), with and without the prefix cache
             ("bf16_prefix_cache", workloads.config5_prefix("bf16"), {}),
             ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), {"prefix_cache": False})]
@@ -582,6 +603,8 @@ def main():
         res["mixed_step"] = mixed_step(args.steps, args.warmup)
     if not args.no_replay:
         res["sched_replay"] = sched_replay(args.replay_steps)
+    if args.replay_budget_sweep:
+        res["replay_budget_sweep"] = replay_budget_sweep(args.replay_steps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

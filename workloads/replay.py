@@ -32,6 +32,7 @@ class StepRecord:
     kept: Dict[int, object]      # layer -> output tensor [T][Hq][d] (only for kept layers)
     plan: Optional[object] = None
     first_outputs: Sequence[int] = ()   # requests whose first output token this step made
+    host_s: float = 0.0          # host time to enqueue the step's layers (between the events)
 
 
 class Replay:
@@ -149,6 +150,7 @@ class Replay:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
+        h0 = time.perf_counter()
         for l in range(tr.num_layers):
             q, k, v = vals[l]
             pkv.kv_cache_write(k, v, self.k_cache[l], self.v_cache[l], slots, tr.block_size, tr.k_scale, tr.v_scale)
@@ -164,6 +166,7 @@ class Replay:
             if l in keep_layers:
                 kept[l] = out.clone()
         e1.record()
+        host_s = time.perf_counter() - h0
         self.sched.update()
         # a row makes an output token when it decodes or completes its context
         ids = plan.ids
@@ -176,30 +179,40 @@ class Replay:
                      + T * row_bytes * (2 + self.e_kv)                        # write: bf16 in, cache out
                      + T * tr.num_q_heads * tr.head_dim * 2 * 2)              # queries in, outputs out
         return StepRecord(step_no, n, T, ctx, int((plan.stages == 0).sum()), per_layer * tr.num_layers,
-                          (e0, e1), kept, plan if keep_plan else None, first.tolist())
+                          (e0, e1), kept, plan if keep_plan else None, first.tolist(), host_s)
 
 
 def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progress=None, **replay_args):
     """Replay the trace (or its first max_steps steps). keep: {step: layers} whose outputs
     (and plans) are kept; replay_args go to Replay. Returns (records, summary)."""
+    import gc
     import torch
     rp = Replay(tr, **replay_args)
     recs: List[StepRecord] = []
     keep = keep or {}
+    # no cyclic garbage collection inside the loop: a full collection over the records
+    # kept so far can stall the host for tens of ms while a step's layers are enqueued
+    gc_on = gc.isenabled()
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     steps = 0
-    while True:
-        c = rp.sched.counters()
-        if c["finished"] == tr.num_requests or (max_steps is not None and steps >= max_steps):
-            break
-        s = c["step"]
-        r = rp.step(keep_layers=keep.get(s, ()), keep_plan=s in keep)
-        steps += 1
-        if r is not None:
-            recs.append(r)
-        if progress and steps % 1000 == 0:
-            progress(steps)
-    torch.cuda.synchronize()
+    try:
+        while True:
+            c = rp.sched.counters()
+            if c["finished"] == tr.num_requests or (max_steps is not None and steps >= max_steps):
+                break
+            s = c["step"]
+            r = rp.step(keep_layers=keep.get(s, ()), keep_plan=s in keep)
+            steps += 1
+            if r is not None:
+                recs.append(r)
+            if progress and steps % 1000 == 0:
+                progress(steps)
+        torch.cuda.synchronize()
+    finally:
+        if gc_on:
+            gc.enable()
     wall = time.perf_counter() - t0
     c = rp.sched.counters()
     t = np.array([r.ev[0].elapsed_time(r.ev[1]) * 1e-3 for r in recs])
@@ -240,7 +253,8 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
         "hbm_GBps_per_step": {"mean": round(float((byts / t).mean() / 1e9), 1),
                               "p50": round(float(np.percentile(byts / t, 50) / 1e9), 1)},
         "hbm_GBps_overall": round(float(byts.sum() / t.sum() / 1e9), 1),
-        "step_ms": {**pct(t, (50, 90, 99)), "max": round(float(t.max()) * 1e3, 3) if len(t) else 0.0},
+        "step_ms": {**pct(t, (50, 90, 99, 99.9)), "max": round(float(t.max()) * 1e3, 3) if len(t) else 0.0},
+        "host_enqueue_ms": pct(np.array([r.host_s for r in recs]), (50, 99)),
         "ttft_ms": pct(ttft), "tbt_ms": pct(tbt),
         "wall_s": round(wall, 2),
     }
