@@ -34,7 +34,18 @@ Readings taken where the page leaves a step open (each listed with the others):
     in a step. A chunk holds positions done..done+q-1 and sees every position below
     done+q; the request's first output comes at the step of its last chunk; its blocks
     are still all reserved at admission, and its prompt pages enter the prefix cache
-    only once the prefill is complete.
+    only once the prefill is complete;
+  * preemption by swap (the SWAP strategy of "5. Technical explanation", off unless a
+    host swap space is given): the victim's blocks are copied, in table order, into
+    host blocks taken from a host free list (LIFO, like the device pool) and its device
+    blocks are freed; it goes to the front of the queue as with recompute. When the host
+    space lacks blocks for the whole table the request is preempted by recompute instead.
+    A swapped request is admitted like any other (blocks for prompt + outputs, strict
+    FCFS, no prefix lookup); its host blocks are copied back into the first blocks of
+    its new table and returned to the host free list in table order, and it resumes with
+    a decode row (no prefill). The copies are listed per step: swap-outs by the update
+    (to run before the next step's kernels), swap-ins by the schedule (before the step's
+    attention).
 
 Parity unpinned beyond invariants and hand-worked traces: the pages print no trace of
 this loop, so the tests pin it with small traces worked out by hand from the page's
@@ -66,6 +77,7 @@ class Req:
     stage: int = PREFILL
     preempted: int = 0
     finished_step: int = -1
+    host: Optional[List[int]] = None           # host blocks holding its swapped-out K/V
     tokens: Optional[Tuple[int, ...]] = None   # prompt token ids (prefix caching)
     cached: int = 0                            # prompt tokens of this prefill found in the cache
     done: int = 0                              # context tokens of the current prefill computed so far
@@ -84,13 +96,14 @@ class StepPlan:
     cu_seqlens_q: np.ndarray  # int32 [n + 1]
     slot_mapping: np.ndarray  # int64 [sum q]
     counters: Dict[str, int]
+    swap_in: List[Tuple[int, int]] = dataclasses.field(default_factory=list)   # (host block, device block)
 
 
 class Scheduler:
     def __init__(self, arrival, prompt, max_tokens, num_blocks: int, free_order, block_size: int,
                  max_running: int, admission_check: bool = True,
                  prompt_tokens: Optional[Sequence[Sequence[int]]] = None, max_batched_tokens: int = 0,
-                 chunk_tokens: int = 0):
+                 chunk_tokens: int = 0, swap_blocks: int = 0):
         self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
         # prompt_tokens given: prefix caching over shared blocks (oracle/prefix.py)
         self.pcache = None
@@ -119,6 +132,12 @@ class Scheduler:
         self.chunk_tokens = int(chunk_tokens)
         if self.max_batched_tokens < 0 or self.chunk_tokens < 0:
             raise ValueError("token budget and chunk size must be >= 0")
+        # preemption by swap into a host space of swap_blocks blocks (0: recompute only)
+        if swap_blocks < 0:
+            raise ValueError("swap_blocks must be >= 0")
+        self.host = oa.BlockPool(swap_blocks) if swap_blocks > 0 else None
+        self.swap_out: List[Tuple[int, int]] = []   # (device block, host block) of the last update
+        self.swapped_out = self.blocks_out = self.blocks_in = 0
         self.waiting: collections.deque = collections.deque()
         self.running: List[Req] = []
         self.step_no = 0
@@ -131,6 +150,8 @@ class Scheduler:
              "preempted": self.preemptions, "finished": self.finished}
         if self.pcache is not None:
             c["cached_tokens"] = self.cached_tokens
+        if self.host is not None:
+            c.update(swapped_out=self.swapped_out, blocks_out=self.blocks_out, blocks_in=self.blocks_in)
         return c
 
     def done(self) -> bool:
@@ -145,9 +166,22 @@ class Scheduler:
                 break
             self.waiting.append(r)
             self.next_arrival += 1
+        swap_in = []
         while self.waiting and len(self.running) < self.max_running:
             r = self.waiting[0]
             ctx = r.prompt + r.n_out
+            if r.host is not None:                                  # swapped out: copy back
+                if self.admission_check and self.tables.blocks_for(ctx) > self.pool.num_free:
+                    break
+                self.waiting.popleft()
+                self.tables.reserve(r.rid, ctx)
+                swap_in += list(zip(r.host, self.tables.tables[r.rid]))
+                self.blocks_in += len(r.host)
+                self.host.release(r.host)
+                r.host = None
+                r.stage = DECODE
+                self.running.append(r)
+                continue
             n_hit, pages = 0, []
             if self.pcache is not None:                             # longest cached prefix
                 n_hit, pages = self.pcache.lookup(r.tokens, min(r.prompt, ctx - 1))
@@ -192,10 +226,11 @@ class Scheduler:
         tabs = [self.tables.tables[i] for i in ids]
         bt, cu, slots = build_block_table(tabs, q, L, self.bs, width)
         return StepPlan(s, np.asarray(ids, np.int64), np.asarray(stages, np.int32), np.asarray(q, np.int32),
-                        np.asarray(L, np.int32), bt, cu, slots, self.counters())
+                        np.asarray(L, np.int32), bt, cu, slots, self.counters(), swap_in)
 
     # -- second half: one output token per row, retire, grow or preempt --------------
     def update(self) -> None:
+        self.swap_out = []
         for r in self.running:
             if r.stage == PREFILL:
                 r.done += r.q_step
@@ -223,7 +258,13 @@ class Scheduler:
                 try:
                     self.tables.reserve(r.rid, need)                # one more block
                 except oa.OutOfBlocks:
-                    self.tables.release(r.rid)                      # preempt by recompute
+                    table = self.tables.tables[r.rid]
+                    if self.host is not None and self.host.num_free >= len(table):
+                        r.host = self.host.alloc(len(table))        # preempt by swap
+                        self.swap_out += list(zip(table, r.host))
+                        self.swapped_out += 1
+                        self.blocks_out += len(table)
+                    self.tables.release(r.rid)                      # (else by recompute)
                     r.preempted += 1
                     self.preemptions += 1
                     self.waiting.appendleft(r)
