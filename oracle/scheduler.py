@@ -120,6 +120,9 @@ class Scheduler:
                 r.tokens = tuple(int(x) for x in tok)
         self.cached_tokens = 0
         self.bs = block_size
+        for r in self.reqs:                     # a request that cannot fit alone would stall the queue
+            if -(-(r.prompt + r.max_tokens - 1) // block_size) > num_blocks:
+                raise ValueError(f"request {r.rid} needs more than the pool's {num_blocks} blocks")
         self.max_running = max_running
         # admission_check=False is the sabotage of the "Break It" experiment of "Project 17"
         # (its admission loop pops the head and prefills it with no memory check): the head

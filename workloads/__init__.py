@@ -539,7 +539,8 @@ def config5_prefix(cache_dtype: str = "bf16") -> Trace:
 def small_trace(seed: int, n: int, num_blocks: int, block_size: int = 4, max_running: int = 8,
                 prompt_max: int = 40, out_max: int = 30, rate: float = 1.0, groups: int = 0) -> Trace:
     """A small seeded trace for tests (same generation rules, small sizes); groups > 0
-    gives every request a shared prompt of one of that many groups (prefix traces)."""
+    gives every request a shared prompt of one of that many groups (prefix traces).
+    Output counts are cut so that every request fits the pool on its own."""
     arrival = np.floor(np.cumsum(rng_for(seed, _STREAM_ARRIVALS).exponential(1.0 / rate, size=n))).astype(np.int32)
     prompt = rng_for(seed, _STREAM_PROMPTS).integers(1, prompt_max, size=n, endpoint=True).astype(np.int32)
     max_tokens = rng_for(seed, _STREAM_OUTPUTS).integers(1, out_max, size=n, endpoint=True).astype(np.int32)
@@ -554,6 +555,11 @@ def small_trace(seed: int, n: int, num_blocks: int, block_size: int = 4, max_run
         tr.prompt = (plen + own).astype(np.int32)
         tr.prefix_group, tr.prefix_len = group, plen.astype(np.int32)
         tr.name = f"small_prefix_trace_{seed}"
+    # every request must fit the pool on its own (prompt + max_tokens - 1 tokens)
+    tr.max_tokens = np.clip(num_blocks * block_size + 1 - tr.prompt, 1, tr.max_tokens).astype(np.int32)
+    tr.prompt = np.minimum(tr.prompt, num_blocks * block_size).astype(np.int32)
+    if tr.prefix_len is not None:
+        tr.prefix_len = np.minimum(tr.prefix_len, tr.prompt).astype(np.int32)
     return tr
 
 
