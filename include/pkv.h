@@ -408,6 +408,54 @@ int pkv_sched_set_prompt_tokens(pkv_sched* sched, int64_t id, const int32_t* tok
  * row). Negative values are INVALID. */
 int pkv_sched_set_token_budget(pkv_sched* sched, int32_t max_batched_tokens, int32_t chunk_tokens);
 
+/* Preemption by swap ([CB] "5. Technical explanation", Preemption: the SWAP strategy),
+ * off unless enabled before the first step with a host space of host_blocks >= 1 blocks
+ * (host block ids 0..host_blocks-1, handed out from the end of a free list that starts
+ * 0, 1, ..., like the device pool). In pkv_sched_update, a request that cannot grow is
+ * swapped out when the host space has as many free blocks as its table: each of its
+ * blocks, in table order, is paired with a host block popped from the list; its device
+ * blocks are freed and it goes to the front of the queue. Otherwise it is preempted by
+ * recompute, as without swap. In pkv_sched_schedule, a swapped request at the head of
+ * the queue is admitted when ceil((prompt + outputs) / block_size) blocks are free: its
+ * table is reserved, host block j is paired with the table's block j, its host blocks
+ * return to the free list in table order, and its row in that step is a decode row (no
+ * prefill, no prefix lookup). pkv_sched_swap_pairs reports the pairs of the last update
+ * (swap-outs, (device block, host block) as int32 [num_out][2]) and of the last schedule
+ * (swap-ins, (host block, device block) [num_in][2]); any of the pointers may be NULL.
+ * The caller copies the swap-outs (pkv_swap_out) after the update and before the next
+ * step's kernels, and the swap-ins (pkv_swap_in) before the step's attention.
+ * pkv_sched_swap_counters: out int64 [4] = requests swapped out so far, blocks swapped
+ * out, blocks swapped in, free host blocks. */
+int pkv_sched_enable_swap(pkv_sched* sched, int32_t host_blocks);
+/* The copies of preemption by swap ([CB] "5. Technical explanation", Preemption: SWAP):
+ * a pair moves every layer's K and V block, as the cache's bytes. Layouts: k_cache and
+ * v_cache are device planes [num_layers][num_blocks][block_bytes] (block_bytes =
+ * block_size * num_kv_heads * head_dim * element size, a positive multiple of 16, both
+ * 16-byte aligned); host_space is host memory [host_capacity][num_layers][2 (K, V)]
+ * [block_bytes] and should be pinned (hipHostMalloc; pageable memory makes the copies
+ * synchronous); workspace is device memory, 16-byte aligned, of at least
+ * pkv_swap_workspace_bytes(n, num_layers, block_bytes) bytes (the pairs are staged
+ * there). dev_blocks / host_blocks: host int32 [n], every device block in
+ * 0..num_blocks-1 and every host block in 0..host_capacity-1, neither repeated
+ * (INVALID otherwise, nothing enqueued). pkv_swap_out: a copy kernel gathers the device
+ * blocks into the workspace, then DMA copies move them to their host blocks;
+ * pkv_swap_in: DMA copies bring the host blocks into the workspace, then a copy kernel
+ * scatters them into the device blocks. Both are asynchronous on `stream` (hipStream_t,
+ * NULL = default): the host space must not be read (after a swap-out) or rewritten
+ * (before a swap-in completes) until the stream has reached that point; n = 0 is a
+ * no-op. Errors: INVALID (sizes, pointers, ids), HIP (launch or copy failure). */
+int64_t pkv_swap_workspace_bytes(int32_t n, int32_t num_layers, int64_t block_bytes);
+int pkv_swap_out(const void* k_cache, const void* v_cache, int32_t num_layers, int32_t num_blocks,
+                 int64_t block_bytes, const int32_t* dev_blocks, const int32_t* host_blocks, int32_t n,
+                 void* host_space, int32_t host_capacity, void* workspace, int64_t workspace_bytes,
+                 void* stream);
+int pkv_swap_in(void* k_cache, void* v_cache, int32_t num_layers, int32_t num_blocks, int64_t block_bytes,
+                const int32_t* host_blocks, const int32_t* dev_blocks, int32_t n, const void* host_space,
+                int32_t host_capacity, void* workspace, int64_t workspace_bytes, void* stream);
+int pkv_sched_swap_pairs(const pkv_sched* sched, int32_t* num_out, int32_t* num_in, int32_t* out_pairs,
+                         int32_t* in_pairs);
+int pkv_sched_swap_counters(const pkv_sched* sched, int64_t* out);
+
 /* Admission without the memory check (enabled = 0), the sabotage of the "Break It"
  * experiment of [P17]: pkv_sched_schedule takes the head of the waiting queue off it and
  * allocates its blocks unchecked; when they do not fit it returns PKV_ERR_OUT_OF_BLOCKS

@@ -65,6 +65,9 @@ _SIGS = {
     "pkv_build_chunk_work": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, vp, i32, P_i32, vp, i32, P_i32, P_i32]),
     "pkv_chunk_slots": (C.c_int, [i32, i32, i32, P_i32]),
     "pkv_chunk_workspace_bytes": (i64, [i32, i32]),
+    "pkv_swap_workspace_bytes": (i64, [i32, i32, i64]),
+    "pkv_swap_out": (C.c_int, [vp, vp, i32, i32, i64, vp, vp, i32, vp, i32, vp, i64, vp]),
+    "pkv_swap_in": (C.c_int, [vp, vp, i32, i32, i64, vp, vp, i32, vp, i32, vp, i64, vp]),
     "pkv_sched_create": (C.c_int, [vp, i32, C.POINTER(vp)]),
     "pkv_sched_destroy": (None, [vp]),
     "pkv_sched_add_requests": (C.c_int, [vp, i32, vp, vp, vp, vp]),
@@ -76,6 +79,9 @@ _SIGS = {
     "pkv_sched_enable_prefix_cache": (C.c_int, [vp]),
     "pkv_sched_set_prompt_tokens": (C.c_int, [vp, i64, vp, i32]),
     "pkv_sched_set_token_budget": (C.c_int, [vp, i32, i32]),
+    "pkv_sched_enable_swap": (C.c_int, [vp, i32]),
+    "pkv_sched_swap_pairs": (C.c_int, [vp, P_i32, P_i32, vp, vp]),
+    "pkv_sched_swap_counters": (C.c_int, [vp, vp]),
     "pkv_seq_share": (C.c_int, [vp, i64, vp, i32]),
     "pkv_block_refs": (C.c_int, [vp, vp, i32]),
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
@@ -156,6 +162,25 @@ class Scheduler:
         """Chunked prefill: at most max_batched_tokens new tokens per step, prefills cut into
         chunks of at most chunk_tokens (0: no limit); before the first step."""
         check(lib().pkv_sched_set_token_budget(self._h, int(max_batched_tokens), int(chunk_tokens)))
+
+    def enable_swap(self, host_blocks: int) -> None:
+        """Preemption by swap into a host space of host_blocks blocks (before the first step)."""
+        check(lib().pkv_sched_enable_swap(self._h, int(host_blocks)))
+
+    def swap_pairs(self):
+        """(swap-outs of the last update [n][2] (device, host), swap-ins of the last schedule
+        [m][2] (host, device)) as int32 arrays."""
+        n, m = i32(), i32()
+        check(lib().pkv_sched_swap_pairs(self._h, C.byref(n), C.byref(m), None, None))
+        out = np.zeros((n.value, 2), np.int32)
+        inn = np.zeros((m.value, 2), np.int32)
+        check(lib().pkv_sched_swap_pairs(self._h, C.byref(n), C.byref(m), _np_ptr(out), _np_ptr(inn)))
+        return out, inn
+
+    def swap_counters(self) -> dict:
+        out = np.zeros(4, np.int64)
+        check(lib().pkv_sched_swap_counters(self._h, _np_ptr(out)))
+        return dict(zip(("swapped_out", "blocks_out", "blocks_in", "host_free"), (int(x) for x in out)))
 
     def counters(self) -> dict:
         out = np.zeros(8, np.int64)
@@ -331,6 +356,44 @@ def _check_plane(k_cache, v_cache, block_size, Hkv, d):
         raise ValueError(f"cache plane must be [num_blocks][{block_size}][{Hkv}][{d}], got {tuple(k_cache.shape)}")
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("K and V planes must have the same shape and dtype")
+
+
+def swap_workspace_bytes(n: int, num_layers: int, block_bytes: int) -> int:
+    return int(lib().pkv_swap_workspace_bytes(int(n), int(num_layers), int(block_bytes)))
+
+
+def _swap_args(k_cache, v_cache, pairs, host_space, workspace):
+    torch = _torch()
+    _require_cuda_contig(k_cache, v_cache, workspace)
+    if k_cache.dim() != 5 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must both be [layers][num_blocks][block_size][Hkv][d] of one dtype")
+    if host_space.is_cuda or not host_space.is_contiguous() or not host_space.is_pinned():
+        raise ValueError("host_space must be a contiguous pinned host tensor")
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    L, nb = int(k_cache.shape[0]), int(k_cache.shape[1])
+    block_bytes = k_cache[0, 0].numel() * k_cache.element_size()
+    cap = host_space.numel() * host_space.element_size() // (L * 2 * block_bytes)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return pairs, L, nb, block_bytes, cap, ws, torch
+
+
+def swap_out(k_cache, v_cache, pairs, host_space, workspace, stream=None) -> None:
+    """Copy device blocks to host blocks: pairs int32 [n][2] = (device block, host block);
+    caches [layers][num_blocks][bs][Hkv][d]; host_space pinned, [host_blocks][layers][2][block]
+    bytes; workspace device, >= swap_workspace_bytes(n, layers, block bytes)."""
+    pairs, L, nb, bb, cap, ws, _ = _swap_args(k_cache, v_cache, pairs, host_space, workspace)
+    dev, host = np.ascontiguousarray(pairs[:, 0]), np.ascontiguousarray(pairs[:, 1])
+    check(lib().pkv_swap_out(_dptr(k_cache), _dptr(v_cache), L, nb, bb, _np_ptr(dev), _np_ptr(host), len(pairs),
+                             vp(host_space.data_ptr()), cap, _dptr(workspace), ws, _stream(stream)))
+
+
+def swap_in(k_cache, v_cache, pairs, host_space, workspace, stream=None) -> None:
+    """Copy host blocks back: pairs int32 [n][2] = (host block, device block); layouts as
+    swap_out."""
+    pairs, L, nb, bb, cap, ws, _ = _swap_args(k_cache, v_cache, pairs, host_space, workspace)
+    host, dev = np.ascontiguousarray(pairs[:, 0]), np.ascontiguousarray(pairs[:, 1])
+    check(lib().pkv_swap_in(_dptr(k_cache), _dptr(v_cache), L, nb, bb, _np_ptr(host), _np_ptr(dev), len(pairs),
+                            vp(host_space.data_ptr()), cap, _dptr(workspace), ws, _stream(stream)))
 
 
 def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scale: float = 1.0,

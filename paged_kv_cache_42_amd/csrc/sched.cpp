@@ -17,6 +17,14 @@
 // of the budget goes to prefill rows in running order, each taking the least of its
 // uncomputed context, chunk_tokens and what is left, so a request may get no row. A
 // request produces its first output at the step of its last chunk.
+//
+// Preemption by swap (the SWAP strategy of "5. Technical explanation", off by default):
+// a victim's blocks go, in table order, to host blocks popped from a host free list, its
+// device blocks are freed, and it waits at the front of the queue; when the host space
+// is short it is preempted by recompute. Re-admitted, it gets blocks for prompt +
+// outputs, its host blocks are copied back into the first of them and freed in table
+// order, and it resumes with a decode row. The copies are listed per call: swap-outs by
+// the update, swap-ins by the schedule.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
@@ -40,6 +48,8 @@ struct Req {
   int32_t cached = 0;                  // prompt tokens of this prefill found in the cache
   int32_t done = 0;                    // context tokens of the current prefill computed so far
   int32_t q_step = 0;                  // new tokens of its row in the scheduled step (0: no row)
+  bool swapped = false;                // its K/V waits in `host`
+  std::vector<int32_t> host;           // host blocks holding its swapped-out K/V, in table order
   std::vector<int32_t> tokens;         // prompt token ids (prefix caching), else empty
 };
 
@@ -86,6 +96,12 @@ struct pkv_sched {
   int32_t max_batched_tokens = 0;       // 0: no per-step token budget
   int32_t chunk_tokens = 0;             // 0: prefills are not cut into chunks
   std::vector<int32_t> rows;            // running requests with a row this step, in running order
+  bool swap = false;                    // preemption by swap into the host space
+  int32_t host_blocks = 0;
+  std::vector<int32_t> host_free;       // LIFO free list of host blocks
+  std::vector<int32_t> swap_out;        // (device, host) pairs of the last update
+  std::vector<int32_t> swap_in;         // (host, device) pairs of the last schedule
+  int64_t swapped_out = 0, blocks_out = 0, blocks_in = 0;
 
   // page-chained keys of tokens[0 : k * bs] for k = 1..pages
   std::vector<uint64_t> page_keys(const std::vector<int32_t>& tok, int64_t pages) const {
@@ -199,10 +215,31 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
   }
   // strict first-come-first-served admission
   std::vector<int32_t> pages;
+  s->swap_in.clear();
   while (!s->waiting.empty() && int32_t(s->running.size()) < s->max_running) {
     const int32_t head = s->waiting.front();
     Req& r = s->reqs[head];
     const int64_t ctx = int64_t(r.prompt) + r.n_out;
+    if (r.swapped) {                      // its K/V comes back from the host: no prefill
+      const int64_t need = (ctx + s->pool->block_size - 1) / s->pool->block_size;
+      if (s->admission_check && need > int64_t(s->pool->free_list.size())) break;
+      s->waiting.pop_front();
+      if (!pool_reserve(s->pool, r.id, ctx))
+        return fail(PKV_ERR_OUT_OF_BLOCKS, "sched_schedule: step %lld, request %lld does not fit and admission "
+                    "does not check", (long long)s->step, (long long)r.id);
+      const std::vector<int32_t>& t = s->pool->tables.at(r.id);
+      for (size_t j = 0; j < r.host.size(); ++j) {
+        s->swap_in.push_back(r.host[j]);
+        s->swap_in.push_back(t[j]);
+        s->host_free.push_back(r.host[j]);
+      }
+      s->blocks_in += int64_t(r.host.size());
+      r.host.clear();
+      r.swapped = false;
+      r.stage = kDecode;
+      s->running.push_back(head);
+      continue;
+    }
     // longest cached prefix; a fresh request computes at least its last prompt token
     const int32_t hit = s->prefix_cache && !r.tokens.empty()
                             ? s->lookup(r, std::min<int64_t>(r.prompt, ctx - 1), pages)
@@ -275,6 +312,7 @@ int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_
 int pkv_sched_update(pkv_sched* s) {
   if (!s) return fail(PKV_ERR_INVALID, "sched_update: scheduler is NULL");
   if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_update: no step scheduled");
+  s->swap_out.clear();
   for (int32_t i : s->running) {
     Req& r = s->reqs[i];
     if (r.stage == kPrefill) r.done += r.q_step;
@@ -304,6 +342,19 @@ int pkv_sched_update(pkv_sched* s) {
     }
     const int64_t need = int64_t(r.prompt) + r.n_out;   // tokens the next row writes up to
     if (!pool_reserve(s->pool, r.id, need)) {  // no block for the next token: preempt
+      const std::vector<int32_t>& t = s->pool->tables.at(r.id);
+      if (s->swap && s->host_free.size() >= t.size()) {   // by swap
+        r.host.clear();
+        for (int32_t b : t) {
+          r.host.push_back(s->host_free.back());
+          s->host_free.pop_back();
+          s->swap_out.push_back(b);
+          s->swap_out.push_back(r.host.back());
+        }
+        r.swapped = true;
+        ++s->swapped_out;
+        s->blocks_out += int64_t(t.size());
+      }                                        // else by recompute
       pool_release(s->pool, r.id);
       ++s->preempted;
       s->waiting.push_front(i);
@@ -331,6 +382,35 @@ int pkv_sched_set_token_budget(pkv_sched* s, int32_t max_batched_tokens, int32_t
     return fail(PKV_ERR_INVALID, "sched_set_token_budget: call before the first step");
   s->max_batched_tokens = max_batched_tokens;
   s->chunk_tokens = chunk_tokens;
+  return PKV_OK;
+}
+
+int pkv_sched_enable_swap(pkv_sched* s, int32_t host_blocks) {
+  if (!s || host_blocks < 1) return fail(PKV_ERR_INVALID, "sched_enable_swap: bad arguments");
+  if (s->step > 0 || s->scheduled) return fail(PKV_ERR_INVALID, "sched_enable_swap: call before the first step");
+  s->swap = true;
+  s->host_blocks = host_blocks;
+  s->host_free.resize(size_t(host_blocks));
+  for (int32_t i = 0; i < host_blocks; ++i) s->host_free[size_t(i)] = i;
+  return PKV_OK;
+}
+
+int pkv_sched_swap_pairs(const pkv_sched* s, int32_t* num_out, int32_t* num_in, int32_t* out_pairs,
+                         int32_t* in_pairs) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_swap_pairs: scheduler is NULL");
+  if (num_out) *num_out = int32_t(s->swap_out.size() / 2);
+  if (num_in) *num_in = int32_t(s->swap_in.size() / 2);
+  if (out_pairs) std::copy(s->swap_out.begin(), s->swap_out.end(), out_pairs);
+  if (in_pairs) std::copy(s->swap_in.begin(), s->swap_in.end(), in_pairs);
+  return PKV_OK;
+}
+
+int pkv_sched_swap_counters(const pkv_sched* s, int64_t* out) {
+  if (!s || !out) return fail(PKV_ERR_INVALID, "sched_swap_counters: bad arguments");
+  out[0] = s->swapped_out;
+  out[1] = s->blocks_out;
+  out[2] = s->blocks_in;
+  out[3] = int64_t(s->host_free.size());
   return PKV_OK;
 }
 

@@ -295,3 +295,30 @@ def test_pool_share_reference_counts():
     assert pool.block_refs().tolist() == [0, 0, 1, 0, 1, 1] and pool.stats() == (3, 1)
     pool.seq_release(2)                         # 5, 4, 2 freed in table order
     assert pool.free_list() == [0, 1, 3, 5, 4, 2]
+
+
+def test_swap_copy_argument_errors_enqueue_nothing():
+    # every case is rejected by the host checks before any HIP call (the pointers are
+    # stand-ins that are never dereferenced)
+    lib = pkv.lib()
+    p = ctypes.c_void_p(1 << 20)                       # 16-byte aligned stand-in
+    ok_dev = np.array([0, 3], np.int32)
+    ok_host = np.array([1, 0], np.int32)
+    ws = pkv.swap_workspace_bytes(2, 2, 4096)
+    assert ws == 2 * 2 * 2 * 4096 and pkv.swap_workspace_bytes(0, 2, 4096) == 0
+
+    def call(fn, dev, host, n=2, bb=4096, wsb=ws, nb=4, cap=2):
+        a, b = (dev, host) if fn == "out" else (host, dev)
+        f = lib.pkv_swap_out if fn == "out" else lib.pkv_swap_in
+        return f(p, p, 2, nb, bb, a.ctypes.data_as(ctypes.c_void_p), b.ctypes.data_as(ctypes.c_void_p), n, p, cap,
+                 p, wsb, None)
+
+    for fn in ("out", "in"):
+        assert call(fn, np.array([0, 4], np.int32), ok_host) == _lib.PKV_ERR_INVALID     # device id range
+        assert call(fn, ok_dev, np.array([2, 0], np.int32)) == _lib.PKV_ERR_INVALID      # host id range
+        assert call(fn, np.array([3, 3], np.int32), ok_host) == _lib.PKV_ERR_INVALID     # device id twice
+        assert call(fn, ok_dev, np.array([1, 1], np.int32)) == _lib.PKV_ERR_INVALID      # host id twice
+        assert call(fn, ok_dev, ok_host, wsb=ws - 16) == _lib.PKV_ERR_INVALID            # workspace short
+        assert call(fn, ok_dev, ok_host, bb=4100) == _lib.PKV_ERR_INVALID                # not a multiple of 16
+        assert call(fn, ok_dev, ok_host, n=-1) == _lib.PKV_ERR_INVALID
+        assert call(fn, ok_dev, ok_host, n=0) == _lib.PKV_OK                             # no-op

@@ -24,15 +24,17 @@ def _dense(tr, which, layer, req, L):
     return x
 
 
-def _check_step(tr, rec, rng, max_rows=8, tokens_per_row=3):
+def _check_step(tr, rec, rng, max_rows=8, tokens_per_row=3, prefer=()):
     plan = rec.plan
     cu = plan.cu_seqlens_q
     rows = list(range(len(plan.ids)))
+    first = [r for r in rows if int(plan.ids[r]) in set(prefer)][:max_rows // 2]   # rows that must be checked
     # prefill rows, later chunks of a cut prefill (or rows after a cached prefix) first
     pre = sorted((r for r in rows if plan.stages[r] == 0), key=lambda r: plan.q_lens[r] == plan.seq_lens[r])
     dec = [r for r in rows if plan.stages[r] == 1]
     pick = pre[:max_rows // 2] + list(rng.choice(dec, size=min(len(dec), max_rows - min(len(pre), max_rows // 2)),
                                                  replace=False))
+    pick = first + [r for r in pick if r not in first][:max_rows - len(first)]
     checked = 0
     for layer, out in rec.kept.items():
         o = out_f64(out)

@@ -9,7 +9,7 @@ import workloads
 from oracle import scheduler as osch
 
 
-def _pair(tr, prefix=False, budget=0, chunk=0):
+def _pair(tr, prefix=False, budget=0, chunk=0, swap=0):
     pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
                     free_order=tr.free_order)
     ours = pkv.Scheduler(pool, tr.max_running)
@@ -20,19 +20,31 @@ def _pair(tr, prefix=False, budget=0, chunk=0):
         ours.enable_prefix_cache(toks)
     if budget or chunk:
         ours.set_token_budget(budget, chunk)
+    if swap:
+        ours.enable_swap(swap)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
-                         tr.max_running, prompt_tokens=toks, max_batched_tokens=budget, chunk_tokens=chunk)
+                         tr.max_running, prompt_tokens=toks, max_batched_tokens=budget, chunk_tokens=chunk,
+                         swap_blocks=swap)
     return pool, ours, ref
 
 
-def _replay_both(tr, width, prefix=False, budget=0, chunk=0):
-    pool, ours, ref = _pair(tr, prefix, budget, chunk)
+def _counters(ours, swap):
+    c = ours.counters()
+    if swap:
+        c.update(ours.swap_counters())
+    return c
+
+
+def _replay_both(tr, width, prefix=False, budget=0, chunk=0, swap=0):
+    pool, ours, ref = _pair(tr, prefix, budget, chunk, swap)
     steps = 0
     for rp, rafter in osch.run(ref, width):
         n, q, mb = ours.schedule()
         assert (n, q) == (len(rp.ids), int(rp.q_lens.sum())), f"step {rp.step}"
         assert mb <= width
-        c = ours.counters()
+        if swap:
+            assert ours.swap_pairs()[1].tolist() == [list(x) for x in rp.swap_in], f"step {rp.step}: swap-ins"
+        c = _counters(ours, swap)
         assert {k: c[k] for k in rp.counters} == rp.counters, f"step {rp.step} after admission"
         p = ours.plan(n, q, width)
         for name in ("ids", "stages", "q_lens", "seq_lens", "block_tables", "cu_seqlens_q", "slot_mapping"):
@@ -41,7 +53,10 @@ def _replay_both(tr, width, prefix=False, budget=0, chunk=0):
         ours.update()
         if prefix:                             # shared blocks: the same reference counts
             assert (pool.block_refs() == np.asarray(ref.tables.ref)).all(), f"step {rp.step}: refs"
-        c = ours.counters()
+        if swap:
+            assert ours.swap_pairs()[0].tolist() == [list(x) for x in ref.swap_out], f"step {rp.step}: swap-outs"
+            assert ours.swap_counters()["host_free"] == ref.host.num_free
+        c = _counters(ours, swap)
         assert {k: c[k] for k in rafter} == rafter, f"step {rp.step} after update"
         steps += 1
     assert ours.counters()["finished"] == tr.num_requests
@@ -191,3 +206,41 @@ def test_token_budget_api_errors():
     s.update()
     with pytest.raises(pkv.PkvError):
         s.set_token_budget(8, 0)                           # after the first step
+
+
+def test_swap_config5_full_trace_bit_exact_every_step():
+    tr = workloads.config5()
+    steps, ref = _replay_both(tr, 512, swap=4096)
+    assert ref.swapped_out == ref.preemptions > 0 and ref.blocks_in == ref.blocks_out
+
+
+def test_swap_short_host_space_config5_bit_exact():
+    # 256 host blocks: some victims swap, the longer ones fall back to recompute
+    tr = workloads.config5()
+    steps, ref = _replay_both(tr, 512, swap=256)
+    assert 0 < ref.swapped_out < ref.preemptions
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(0, 10_000), st.integers(18, 60), st.integers(1, 8), st.sampled_from([1, 4, 16, 200]),
+       st.sampled_from([(0, 0), (8, 4)]), st.booleans())
+def test_swap_random_small_traces_bit_exact(seed, pool, max_running, swap, budget, prefix):
+    tr = workloads.small_trace(seed, 30, pool, block_size=4, max_running=max_running, prompt_max=24 if prefix else 40,
+                               out_max=16 if prefix else 30, rate=2.0, groups=3 if prefix else 0)
+    _replay_both(tr, 20, prefix=prefix, budget=budget[0], chunk=budget[1], swap=swap)
+
+
+def test_swap_api_errors():
+    pool = pkv.Pool(16, 4, 1, 64, "bf16")
+    s = pkv.Scheduler(pool, 2)
+    s.add_requests([1], [0], [5], [2])
+    with pytest.raises(pkv.PkvError):
+        s.enable_swap(0)
+    s.enable_swap(8)
+    assert s.swap_counters() == {"swapped_out": 0, "blocks_out": 0, "blocks_in": 0, "host_free": 8}
+    s.schedule()
+    out, inn = s.swap_pairs()
+    assert out.shape == (0, 2) and inn.shape == (0, 2)
+    s.update()
+    with pytest.raises(pkv.PkvError):
+        s.enable_swap(8)                                   # after the first step

@@ -33,11 +33,13 @@ class StepRecord:
     plan: Optional[object] = None
     first_outputs: Sequence[int] = ()   # requests whose first output token this step made
     host_s: float = 0.0          # host time to enqueue the step's layers (between the events)
+    swap_ev: tuple = ()          # (swap-in end event, swap-out start, swap-out end) or None entries
+    swap_blocks: tuple = (0, 0)  # (blocks swapped in before the layers, swapped out after the update)
 
 
 class Replay:
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
-                 prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0):
+                 prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0):
         import torch
         self.torch = torch
         self.tr = tr
@@ -64,6 +66,12 @@ class Replay:
         if token_budget or chunk_tokens:                       # chunked prefill
             self.sched.set_token_budget(token_budget, chunk_tokens)
         self.n_out = np.zeros(tr.num_requests, np.int64)        # outputs per request so far
+        self.host_space = self.swap_ws = None
+        if swap_blocks:                                        # preemption by swap
+            self.sched.enable_swap(swap_blocks)
+            block_bytes = self.k_cache[0, 0].numel() * self.k_cache.element_size()
+            self.pair_bytes = tr.num_layers * 2 * block_bytes
+            self.host_space = torch.empty(swap_blocks * self.pair_bytes, dtype=torch.uint8, pin_memory=True)
         self.heads = np.array([tr.num_q_heads, tr.num_kv_heads, tr.num_kv_heads], np.int64)
         self.buf = None
         self.e_kv = 1 if tr.cache_dtype == "fp8" else 2
@@ -147,10 +155,18 @@ class Replay:
         msl = int(seq_lens.max())
         out = torch.empty((T, tr.num_q_heads, tr.head_dim), dtype=torch.bfloat16, device="cuda")
         kept = {}
+        swap_in = self.sched.swap_pairs()[1] if self.host_space is not None else np.zeros((0, 2), np.int32)
+        if len(swap_in):
+            self._swap_workspace(len(swap_in))
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         h0 = time.perf_counter()
+        ei = None
+        if len(swap_in):                       # swapped requests' K/V back before the layers
+            pkv.swap_in(self.k_cache, self.v_cache, swap_in, self.host_space, self.swap_ws)
+            ei = torch.cuda.Event(enable_timing=True)
+            ei.record()
         for l in range(tr.num_layers):
             q, k, v = vals[l]
             pkv.kv_cache_write(k, v, self.k_cache[l], self.v_cache[l], slots, tr.block_size, tr.k_scale, tr.v_scale)
@@ -168,6 +184,15 @@ class Replay:
         e1.record()
         host_s = time.perf_counter() - h0
         self.sched.update()
+        es0 = es1 = None
+        swap_out = self.sched.swap_pairs()[0] if self.host_space is not None else np.zeros((0, 2), np.int32)
+        if len(swap_out):                      # victims' K/V to the host before the next step
+            self._swap_workspace(len(swap_out))
+            es0 = torch.cuda.Event(enable_timing=True)
+            es1 = torch.cuda.Event(enable_timing=True)
+            es0.record()
+            pkv.swap_out(self.k_cache, self.v_cache, swap_out, self.host_space, self.swap_ws)
+            es1.record()
         # a row makes an output token when it decodes or completes its context
         ids = plan.ids
         made = (plan.stages == 1) | (seq_lens == self.tr.prompt[ids] + self.n_out[ids])
@@ -179,7 +204,13 @@ class Replay:
                      + T * row_bytes * (2 + self.e_kv)                        # write: bf16 in, cache out
                      + T * tr.num_q_heads * tr.head_dim * 2 * 2)              # queries in, outputs out
         return StepRecord(step_no, n, T, ctx, int((plan.stages == 0).sum()), per_layer * tr.num_layers,
-                          (e0, e1), kept, plan if keep_plan else None, first.tolist(), host_s)
+                          (e0, e1), kept, plan if keep_plan else None, first.tolist(), host_s, (ei, es0, es1),
+                          (len(swap_in), len(swap_out)))
+
+    def _swap_workspace(self, n):
+        nb = pkv.swap_workspace_bytes(n, self.tr.num_layers, self.pair_bytes // (2 * self.tr.num_layers))
+        if self.swap_ws is None or self.swap_ws.numel() < nb:
+            self.swap_ws = self.torch.empty(max(nb, 64 << 20), dtype=self.torch.uint8, device="cuda")
 
 
 def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progress=None, **replay_args):
@@ -215,7 +246,11 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
             gc.enable()
     wall = time.perf_counter() - t0
     c = rp.sched.counters()
-    t = np.array([r.ev[0].elapsed_time(r.ev[1]) * 1e-3 for r in recs])
+    t_layers = np.array([r.ev[0].elapsed_time(r.ev[1]) * 1e-3 for r in recs])
+    t_in = np.array([r.ev[0].elapsed_time(r.swap_ev[0]) * 1e-3 if r.swap_ev and r.swap_ev[0] else 0.0 for r in recs])
+    t_out = np.array([r.swap_ev[1].elapsed_time(r.swap_ev[2]) * 1e-3 if r.swap_ev and r.swap_ev[1] else 0.0
+                      for r in recs])
+    t = t_layers + t_out                   # a step: swap-ins, the layers, then its swap-outs
     qtok = np.array([r.q_tokens for r in recs], np.float64)
     byts = np.array([r.attention_bytes for r in recs], np.float64)
     rows = np.array([r.rows for r in recs], np.float64)
@@ -258,4 +293,12 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
         "ttft_ms": pct(ttft), "tbt_ms": pct(tbt),
         "wall_s": round(wall, 2),
     }
+    if rp.host_space is not None:
+        sc = rp.sched.swap_counters()
+        b_in = sum(r.swap_blocks[0] for r in recs) * rp.pair_bytes
+        b_out = sum(r.swap_blocks[1] for r in recs) * rp.pair_bytes
+        summary["swap"] = {**sc, "swap_in_s": round(float(t_in.sum()), 4), "swap_out_s": round(float(t_out.sum()), 4),
+                           "GB_in": round(b_in / 1e9, 3), "GB_out": round(b_out / 1e9, 3),
+                           "GBps_in": round(b_in / max(float(t_in.sum()), 1e-12) / 1e9, 1),
+                           "GBps_out": round(b_out / max(float(t_out.sum()), 1e-12) / 1e9, 1)}
     return recs, summary
