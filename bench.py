@@ -50,6 +50,7 @@ def parse_args():
                     help="skip the continuous-batching trace replay (2000 requests, scheduler step + 16 layers of "
                          "cache write and mixed attention per step, bf16 and E4M3 caches)")
     ap.add_argument("--replay-steps", type=int, default=None, help="replay only the first N scheduler steps")
+    ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy measurement (1 GiB each way)")
     ap.add_argument("--replay-budget-sweep", action="store_true",
                     help="also replay the bf16 trace under several token budgets / chunk sizes (chunked prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
@@ -295,6 +296,54 @@ def mixed_step(steps: int, warmup: int):
     return res
 
 
+def swap_bench(reps: int = 5):
+    """Preemption by swap at the trace geometry (16 layers, 4,096 blocks of 16 tokens, 8 KV
+    heads x 64, bf16): 2,048 blocks = 1 GiB of K/V out to pinned host memory and back,
+    with the host blocks in one run and scattered; a plain DMA copy of 1 GiB each way
+    (contiguous device buffer <-> pinned host buffer) as the link's ceiling."""
+    import torch
+    import numpy as np
+    import paged_kv_cache_42_amd as pkv
+    import workloads
+    tr = workloads.config5("bf16")
+    L, nb = tr.num_layers, tr.num_blocks
+    k = torch.zeros((L, nb, tr.block_size, tr.num_kv_heads, tr.head_dim), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    block_bytes = k[0, 0].numel() * 2
+    n = 2048
+    nbytes = n * L * 2 * block_bytes
+    hs = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    ws = torch.empty(pkv.swap_workspace_bytes(n, L, block_bytes), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(31)
+    dev = rng.permutation(nb)[:n].astype(np.int32)
+    res = {"bytes_each_way": nbytes, "pages_model": "2 x KV bytes / PCIe bandwidth; 1 GB round trip ~80 ms on Gen4"}
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts[1:]))
+
+    for name, host in (("one_run", np.arange(n, dtype=np.int32)), ("scattered", rng.permutation(n).astype(np.int32))):
+        t_out = timed(lambda: pkv.swap_out(k, v, np.stack([dev, host], 1), hs, ws))
+        t_in = timed(lambda: pkv.swap_in(k, v, np.stack([host, dev], 1), hs, ws))
+        res[name] = {"swap_out_ms": round(t_out * 1e3, 3), "swap_in_ms": round(t_in * 1e3, 3),
+                     "round_trip_ms": round((t_out + t_in) * 1e3, 3),
+                     "GBps_out": round(nbytes / t_out / 1e9, 1), "GBps_in": round(nbytes / t_in / 1e9, 1)}
+    d2h = timed(lambda: hs.copy_(ws[:nbytes], non_blocking=True))
+    h2d = timed(lambda: ws[:nbytes].copy_(hs, non_blocking=True))
+    res["dma_only"] = {"d2h_ms": round(d2h * 1e3, 3), "h2d_ms": round(h2d * 1e3, 3),
+                       "GBps_d2h": round(nbytes / d2h / 1e9, 1), "GBps_h2d": round(nbytes / h2d / 1e9, 1)}
+    del k, v, hs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 BUDGET_SWEEP = ((1024, 512), (2048, 512), (4096, 1024), (8192, 2048))
 
 
@@ -325,6 +374,9 @@ def sched_replay(max_steps):
             # chunked prefill: at most 2048 new tokens per step, prefills in chunks of 512
             ("bf16_chunked_2048_512", workloads.config5("bf16"),
              {"token_budget": 2048, "chunk_tokens": 512, "chunk_cut": True}),
+            # preemption by swap into a host space of 4096 blocks (instead of recompute)
+            ("bf16_swap", workloads.config5("bf16"), {"swap_blocks": 4096}),
+            ("bf16_swap_overlap", workloads.config5("bf16"), {"swap_blocks": 4096, "swap_overlap": True}),
             # shared system prompts (16 groups), with and without the prefix cache
             ("bf16_prefix_cache", workloads.config5_prefix("bf16"), {}),
             ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), {"prefix_cache": False})]
@@ -601,6 +653,9 @@ def main():
     if not args.no_mixed:
         print("[bench] mixed prefill+decode step", file=sys.stderr, flush=True)
         res["mixed_step"] = mixed_step(args.steps, args.warmup)
+    if not args.no_swap:
+        print("[bench] swap copies", file=sys.stderr, flush=True)
+        res["swap_copy"] = swap_bench()
     if not args.no_replay:
         res["sched_replay"] = sched_replay(args.replay_steps)
     if args.replay_budget_sweep:

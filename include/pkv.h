@@ -443,12 +443,17 @@ int pkv_sched_enable_swap(pkv_sched* sched, int32_t host_blocks);
  * scatters them into the device blocks. Both are asynchronous on `stream` (hipStream_t,
  * NULL = default): the host space must not be read (after a swap-out) or rewritten
  * (before a swap-in completes) until the stream has reached that point; n = 0 is a
- * no-op. Errors: INVALID (sizes, pointers, ids), HIP (launch or copy failure). */
+ * no-op. pkv_swap_out's copy_stream (NULL: `stream`) takes the DMA copies, ordered after
+ * the gather by an event, so the transfer overlaps later work on `stream` (whose writes
+ * into the freed blocks come after the gather); the workspace and the host blocks are
+ * then busy until copy_stream reaches that point, which the caller must wait for before
+ * reusing the workspace or reading those host blocks (a later pkv_swap_in included).
+ * Errors: INVALID (sizes, pointers, ids), HIP (launch, ordering or copy failure). */
 int64_t pkv_swap_workspace_bytes(int32_t n, int32_t num_layers, int64_t block_bytes);
 int pkv_swap_out(const void* k_cache, const void* v_cache, int32_t num_layers, int32_t num_blocks,
                  int64_t block_bytes, const int32_t* dev_blocks, const int32_t* host_blocks, int32_t n,
                  void* host_space, int32_t host_capacity, void* workspace, int64_t workspace_bytes,
-                 void* stream);
+                 void* stream, void* copy_stream);
 int pkv_swap_in(void* k_cache, void* v_cache, int32_t num_layers, int32_t num_blocks, int64_t block_bytes,
                 const int32_t* host_blocks, const int32_t* dev_blocks, int32_t n, const void* host_space,
                 int32_t host_capacity, void* workspace, int64_t workspace_bytes, void* stream);

@@ -66,7 +66,7 @@ _SIGS = {
     "pkv_chunk_slots": (C.c_int, [i32, i32, i32, P_i32]),
     "pkv_chunk_workspace_bytes": (i64, [i32, i32]),
     "pkv_swap_workspace_bytes": (i64, [i32, i32, i64]),
-    "pkv_swap_out": (C.c_int, [vp, vp, i32, i32, i64, vp, vp, i32, vp, i32, vp, i64, vp]),
+    "pkv_swap_out": (C.c_int, [vp, vp, i32, i32, i64, vp, vp, i32, vp, i32, vp, i64, vp, vp]),
     "pkv_swap_in": (C.c_int, [vp, vp, i32, i32, i64, vp, vp, i32, vp, i32, vp, i64, vp]),
     "pkv_sched_create": (C.c_int, [vp, i32, C.POINTER(vp)]),
     "pkv_sched_destroy": (None, [vp]),
@@ -377,14 +377,17 @@ def _swap_args(k_cache, v_cache, pairs, host_space, workspace):
     return pairs, L, nb, block_bytes, cap, ws, torch
 
 
-def swap_out(k_cache, v_cache, pairs, host_space, workspace, stream=None) -> None:
+def swap_out(k_cache, v_cache, pairs, host_space, workspace, stream=None, copy_stream=None) -> None:
     """Copy device blocks to host blocks: pairs int32 [n][2] = (device block, host block);
     caches [layers][num_blocks][bs][Hkv][d]; host_space pinned, [host_blocks][layers][2][block]
-    bytes; workspace device, >= swap_workspace_bytes(n, layers, block bytes)."""
+    bytes; workspace device, >= swap_workspace_bytes(n, layers, block bytes). copy_stream:
+    the DMA leg runs there (after the gather on stream); the workspace and host blocks stay
+    busy until it is done."""
     pairs, L, nb, bb, cap, ws, _ = _swap_args(k_cache, v_cache, pairs, host_space, workspace)
     dev, host = np.ascontiguousarray(pairs[:, 0]), np.ascontiguousarray(pairs[:, 1])
     check(lib().pkv_swap_out(_dptr(k_cache), _dptr(v_cache), L, nb, bb, _np_ptr(dev), _np_ptr(host), len(pairs),
-                             vp(host_space.data_ptr()), cap, _dptr(workspace), ws, _stream(stream)))
+                             vp(host_space.data_ptr()), cap, _dptr(workspace), ws, _stream(stream),
+                             None if copy_stream is None else vp(copy_stream.cuda_stream)))
 
 
 def swap_in(k_cache, v_cache, pairs, host_space, workspace, stream=None) -> None:

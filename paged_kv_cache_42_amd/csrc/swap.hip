@@ -165,7 +165,8 @@ int64_t pkv_swap_workspace_bytes(int32_t n, int32_t num_layers, int64_t block_by
 
 int pkv_swap_out(const void* k_cache, const void* v_cache, int32_t num_layers, int32_t num_blocks,
                  int64_t block_bytes, const int32_t* dev_blocks, const int32_t* host_blocks, int32_t n,
-                 void* host_space, int32_t host_capacity, void* workspace, int64_t workspace_bytes, void* stream) {
+                 void* host_space, int32_t host_capacity, void* workspace, int64_t workspace_bytes, void* stream,
+                 void* copy_stream) {
   const char* who = "swap_out";
   int rc = check_common(who, k_cache, v_cache, num_layers, num_blocks, block_bytes, n, dev_blocks, host_blocks,
                         host_space, host_capacity, workspace, workspace_bytes);
@@ -178,8 +179,20 @@ int pkv_swap_out(const void* k_cache, const void* v_cache, int32_t num_layers, i
   rc = launch<true>(who, const_cast<void*>(k_cache), const_cast<void*>(v_cache), staging, num_layers, num_blocks,
                     block_bytes, dev_blocks, p, st);
   if (rc != PKV_OK) return rc;
+  // the device blocks are free for reuse on `stream` once the gather is done; the PCIe leg
+  // may run on a copy stream that waits for the gather only
+  hipStream_t cs = copy_stream ? reinterpret_cast<hipStream_t>(copy_stream) : st;
+  if (cs != st) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: event creation failed: %s", who, hipGetErrorString(e));
+    e = hipEventRecord(ev, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev, 0);
+    hipEventDestroy(ev);                   // released once the recorded work completes
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: stream ordering failed: %s", who, hipGetErrorString(e));
+  }
   return copy_runs<true>(who, static_cast<char*>(host_space), staging, int64_t(num_layers) * 2 * block_bytes,
-                         host_blocks, p, st);
+                         host_blocks, p, cs);
 }
 
 int pkv_swap_in(void* k_cache, void* v_cache, int32_t num_layers, int32_t num_blocks, int64_t block_bytes,

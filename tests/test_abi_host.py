@@ -309,9 +309,9 @@ def test_swap_copy_argument_errors_enqueue_nothing():
 
     def call(fn, dev, host, n=2, bb=4096, wsb=ws, nb=4, cap=2):
         a, b = (dev, host) if fn == "out" else (host, dev)
-        f = lib.pkv_swap_out if fn == "out" else lib.pkv_swap_in
-        return f(p, p, 2, nb, bb, a.ctypes.data_as(ctypes.c_void_p), b.ctypes.data_as(ctypes.c_void_p), n, p, cap,
-                 p, wsb, None)
+        args = (p, p, 2, nb, bb, a.ctypes.data_as(ctypes.c_void_p), b.ctypes.data_as(ctypes.c_void_p), n, p, cap,
+                p, wsb, None)
+        return lib.pkv_swap_out(*args, None) if fn == "out" else lib.pkv_swap_in(*args)
 
     for fn in ("out", "in"):
         assert call(fn, np.array([0, 4], np.int32), ok_host) == _lib.PKV_ERR_INVALID     # device id range

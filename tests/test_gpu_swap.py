@@ -28,8 +28,8 @@ def _pinned(nbytes, fill):
     return h
 
 
-@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
-def test_swap_out_and_in_match_the_oracle_bytes(cache_dtype):
+@pytest.mark.parametrize("cache_dtype,copy_stream", [("bf16", False), ("fp8", False), ("bf16", True)])
+def test_swap_out_and_in_match_the_oracle_bytes(cache_dtype, copy_stream):
     L, nb, bs, hkv, d, H = 3, 600, 16, 2, 64, 512
     rng = np.random.default_rng(17)
     if cache_dtype == "bf16":
@@ -50,7 +50,10 @@ def test_swap_out_and_in_match_the_oracle_bytes(cache_dtype):
     out_pairs = np.stack([dev, host], 1)
     hs = _pinned(H * L * 2 * block_bytes, 0xA5)
     ws = torch.empty(pkv.swap_workspace_bytes(300, L, block_bytes), dtype=torch.uint8, device="cuda")
-    pkv.swap_out(k, v, out_pairs, hs, ws)
+    cs = torch.cuda.Stream() if copy_stream else None
+    pkv.swap_out(k, v, out_pairs, hs, ws, copy_stream=cs)
+    if cs is not None:                         # the DMA leg runs on cs: the swap-in waits for it
+        torch.cuda.current_stream().wait_stream(cs)
     torch.cuda.synchronize()
     want = np.full((H, L, 2, block_bytes), 0xA5, np.uint8)
     osw.swap_out(kb, vb, out_pairs.tolist(), want)
@@ -124,7 +127,8 @@ def test_full_trace_geometry_one_gib_each_way_sampled():
     assert not k[:, torch.from_numpy(untouched).long().cuda()].view(torch.int16).any()
 
 
-def test_replay_with_swap_sampled_parity():
+@pytest.mark.parametrize("overlap", [False, True])
+def test_replay_with_swap_sampled_parity(overlap):
     # the trace replay with a host space of 4096 blocks: preempted requests are swapped out
     # and come back without a prefill; their decode rows after the swap-in must attend to
     # the K/V they had
@@ -139,7 +143,7 @@ def test_replay_with_swap_sampled_parity():
     assert len(back) >= 2
     keep_steps = sorted(back)[:3]
     keep = {s: (0, tr.num_layers - 1) for s in keep_steps}
-    recs, summary = replay.run(tr, max_steps=max(keep_steps) + 1, keep=keep, swap_blocks=4096)
+    recs, summary = replay.run(tr, max_steps=max(keep_steps) + 1, keep=keep, swap_blocks=4096, swap_overlap=overlap)
     assert summary["swap"]["swapped_out"] > 0 and summary["swap"]["blocks_in"] > 0
     by_step = {r.step: r for r in recs}
     rng = np.random.default_rng(13)

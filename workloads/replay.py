@@ -39,7 +39,8 @@ class StepRecord:
 
 class Replay:
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
-                 prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0):
+                 prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0,
+                 swap_overlap: bool = False):
         import torch
         self.torch = torch
         self.tr = tr
@@ -72,6 +73,9 @@ class Replay:
             block_bytes = self.k_cache[0, 0].numel() * self.k_cache.element_size()
             self.pair_bytes = tr.num_layers * 2 * block_bytes
             self.host_space = torch.empty(swap_blocks * self.pair_bytes, dtype=torch.uint8, pin_memory=True)
+        # swap-outs' DMA leg on a copy stream, overlapping the next steps; any later swap
+        # call waits for it (it reuses the workspace and may read those host blocks)
+        self.copy_stream = torch.cuda.Stream() if swap_overlap else None
         self.heads = np.array([tr.num_q_heads, tr.num_kv_heads, tr.num_kv_heads], np.int64)
         self.buf = None
         self.e_kv = 1 if tr.cache_dtype == "fp8" else 2
@@ -161,6 +165,8 @@ class Replay:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
+        if len(swap_in) and self.copy_stream is not None:
+            torch.cuda.current_stream().wait_stream(self.copy_stream)
         h0 = time.perf_counter()
         ei = None
         if len(swap_in):                       # swapped requests' K/V back before the layers
@@ -191,7 +197,12 @@ class Replay:
             es0 = torch.cuda.Event(enable_timing=True)
             es1 = torch.cuda.Event(enable_timing=True)
             es0.record()
-            pkv.swap_out(self.k_cache, self.v_cache, swap_out, self.host_space, self.swap_ws)
+            if self.copy_stream is not None:
+                torch.cuda.current_stream().wait_stream(self.copy_stream)
+            pkv.swap_out(self.k_cache, self.v_cache, swap_out, self.host_space, self.swap_ws,
+                         copy_stream=self.copy_stream)
+            if self.copy_stream is not None:   # the allocator must not hand it out before the DMA ends
+                self.swap_ws.record_stream(self.copy_stream)
             es1.record()
         # a row makes an output token when it decodes or completes its context
         ids = plan.ids
