@@ -42,10 +42,26 @@ Readings taken where the page leaves a step open (each listed with the others):
     space lacks blocks for the whole table the request is preempted by recompute instead.
     A swapped request is admitted like any other (blocks for prompt + outputs, strict
     FCFS, no prefix lookup); its host blocks are copied back into the first blocks of
-    its new table and returned to the host free list in table order, and it resumes with
-    a decode row (no prefill). The copies are listed per step: swap-outs by the update
+    its new table and returned to the host free list in table order, and it resumes where
+    it stopped (no prefill of what it had: its decode row, or with victim policies below
+    possibly its next prefill chunk). The copies are listed per step: swap-outs by the update
     (to run before the next step's kernels), swap-ins by the schedule (before the step's
-    attention).
+    attention);
+  * victim policies (the victim selection of "5. Technical explanation": LIFO keeps the
+    progress of long-running requests; the pure-Python engine's preemption takes the
+    running request with the fewest generated tokens): with victim "lifo" or "fewest"
+    the update first appends every row's output and frees finished requests (running
+    order), then walks the running requests in order; one that needs a block for its
+    next token and finds none preempts victims until it gets one: "lifo" takes the
+    running request admitted last, "fewest" the one with the fewest outputs (the earliest
+    admitted on ties), each among the least important priority class present; when the
+    victim is the request itself it stops there. The default "self" is the Go loop's
+    one-pass update, where the request that cannot grow preempts itself;
+  * priority admission (the Priority admission policy of "5. Technical explanation";
+    the priority classes of the serving project's extensions): given a class per
+    request (0 most important), the waiting queue is kept in (class, arrival step, id)
+    order, preempted requests included (they take their place by that key rather than
+    the front); admission still stops at the first head that does not fit.
 
 Parity unpinned beyond invariants and hand-worked traces: the pages print no trace of
 this loop, so the tests pin it with small traces worked out by hand from the page's
@@ -77,6 +93,7 @@ class Req:
     stage: int = PREFILL
     preempted: int = 0
     finished_step: int = -1
+    prio: int = 0                              # priority class (0: most important)
     host: Optional[List[int]] = None           # host blocks holding its swapped-out K/V
     tokens: Optional[Tuple[int, ...]] = None   # prompt token ids (prefix caching)
     cached: int = 0                            # prompt tokens of this prefill found in the cache
@@ -103,7 +120,8 @@ class Scheduler:
     def __init__(self, arrival, prompt, max_tokens, num_blocks: int, free_order, block_size: int,
                  max_running: int, admission_check: bool = True,
                  prompt_tokens: Optional[Sequence[Sequence[int]]] = None, max_batched_tokens: int = 0,
-                 chunk_tokens: int = 0, swap_blocks: int = 0):
+                 chunk_tokens: int = 0, swap_blocks: int = 0, victim: str = "self",
+                 priority: Optional[Sequence[int]] = None):
         self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
         # prompt_tokens given: prefix caching over shared blocks (oracle/prefix.py)
         self.pcache = None
@@ -141,6 +159,15 @@ class Scheduler:
         self.host = oa.BlockPool(swap_blocks) if swap_blocks > 0 else None
         self.swap_out: List[Tuple[int, int]] = []   # (device block, host block) of the last update
         self.swapped_out = self.blocks_out = self.blocks_in = 0
+        if victim not in ("self", "lifo", "fewest"):
+            raise ValueError(f"unknown victim policy {victim!r}")
+        self.victim = victim
+        self.by_priority = priority is not None
+        if priority is not None:
+            if len(priority) != len(self.reqs) or min(priority, default=0) < 0:
+                raise ValueError("one priority class >= 0 per request")
+            for r, c in zip(self.reqs, priority):
+                r.prio = int(c)
         self.waiting: collections.deque = collections.deque()
         self.running: List[Req] = []
         self.step_no = 0
@@ -167,7 +194,7 @@ class Scheduler:
             r = self.reqs[self.arrival_order[self.next_arrival]]
             if r.arrival > s:
                 break
-            self.waiting.append(r)
+            self._enqueue(r, front=False)
             self.next_arrival += 1
         swap_in = []
         while self.waiting and len(self.running) < self.max_running:
@@ -181,8 +208,7 @@ class Scheduler:
                 swap_in += list(zip(r.host, self.tables.tables[r.rid]))
                 self.blocks_in += len(r.host)
                 self.host.release(r.host)
-                r.host = None
-                r.stage = DECODE
+                r.host = None                                       # resumes in its stage
                 self.running.append(r)
                 continue
             n_hit, pages = 0, []
@@ -231,6 +257,36 @@ class Scheduler:
         return StepPlan(s, np.asarray(ids, np.int64), np.asarray(stages, np.int32), np.asarray(q, np.int32),
                         np.asarray(L, np.int32), bt, cu, slots, self.counters(), swap_in)
 
+    # -- queue and preemption helpers ---------------------------------------------------
+    def _enqueue(self, r: Req, front: bool) -> None:
+        if not self.by_priority:
+            (self.waiting.appendleft if front else self.waiting.append)(r)
+            return
+        key = (r.prio, r.arrival, r.rid)
+        k = 0
+        while k < len(self.waiting) and (self.waiting[k].prio, self.waiting[k].arrival, self.waiting[k].rid) < key:
+            k += 1
+        self.waiting.insert(k, r)
+
+    def _preempt(self, r: Req) -> None:
+        table = self.tables.tables[r.rid]
+        if self.host is not None and self.host.num_free >= len(table):
+            r.host = self.host.alloc(len(table))                    # by swap
+            self.swap_out += list(zip(table, r.host))
+            self.swapped_out += 1
+            self.blocks_out += len(table)
+        self.tables.release(r.rid)                                  # (else by recompute)
+        r.preempted += 1
+        self.preemptions += 1
+        self._enqueue(r, front=True)
+
+    def _pick_victim(self, alive: List[Req]) -> Req:
+        worst = max(c.prio for c in alive)
+        pool = [c for c in alive if c.prio == worst]
+        if self.victim == "lifo":
+            return pool[-1]
+        return min(pool, key=lambda c: c.n_out)                     # first minimum: earliest admitted
+
     # -- second half: one output token per row, retire, grow or preempt --------------
     def update(self) -> None:
         self.swap_out = []
@@ -241,6 +297,9 @@ class Scheduler:
             for r in self.running:
                 if r.stage == PREFILL and r.done == r.prompt + r.n_out:
                     self.pcache.insert(r.tokens, self.tables.tables[r.rid], r.prompt)
+        if self.victim != "self":
+            self._update_with_victims()
+            return
         still = []
         for r in self.running:
             had_row = r.q_step > 0
@@ -261,19 +320,53 @@ class Scheduler:
                 try:
                     self.tables.reserve(r.rid, need)                # one more block
                 except oa.OutOfBlocks:
-                    table = self.tables.tables[r.rid]
-                    if self.host is not None and self.host.num_free >= len(table):
-                        r.host = self.host.alloc(len(table))        # preempt by swap
-                        self.swap_out += list(zip(table, r.host))
-                        self.swapped_out += 1
-                        self.blocks_out += len(table)
-                    self.tables.release(r.rid)                      # (else by recompute)
-                    r.preempted += 1
-                    self.preemptions += 1
-                    self.waiting.appendleft(r)
+                    self._preempt(r)                                # the request preempts itself
                     continue
             still.append(r)
         self.running = still
+        self.step_no += 1
+
+    def _update_with_victims(self) -> None:
+        # outputs and retirements first, in running order
+        alive, grew = [], set()
+        for r in self.running:
+            had_row = r.q_step > 0
+            r.q_step = 0
+            if not had_row or (r.stage == PREFILL and r.done < r.prompt + r.n_out):
+                alive.append(r)
+                continue
+            r.cached = 0
+            r.n_out += 1
+            r.stage = DECODE
+            if r.n_out >= r.max_tokens:
+                self.tables.release(r.rid)
+                r.finished_step = self.step_no
+                self.finished += 1
+                continue
+            alive.append(r)
+            grew.add(r.rid)
+        # then the blocks for the next tokens, victims chosen by the policy
+        k = 0
+        while k < len(alive):
+            r = alive[k]
+            need = r.prompt + r.n_out
+            if r.rid in grew and need > len(self.tables.tables[r.rid]) * self.bs:
+                while True:
+                    try:
+                        self.tables.reserve(r.rid, need)
+                        break
+                    except oa.OutOfBlocks:
+                        v = self._pick_victim(alive)
+                        if alive.index(v) < k:
+                            k -= 1
+                        alive.remove(v)
+                        self._preempt(v)
+                        if v is r:
+                            break
+                if r not in alive:
+                    continue
+            k += 1
+        self.running = alive
         self.step_no += 1
 
 
