@@ -427,6 +427,27 @@ int pkv_sched_set_token_budget(pkv_sched* sched, int32_t max_batched_tokens, int
  * pkv_sched_swap_counters: out int64 [4] = requests swapped out so far, blocks swapped
  * out, blocks swapped in, free host blocks. */
 int pkv_sched_enable_swap(pkv_sched* sched, int32_t host_blocks);
+
+/* Victim policies ([CB] "5. Technical explanation", Preemption: victim selection; the
+ * pure-Python engine's preemption of the request with the fewest generated tokens),
+ * set before the first step. PKV_VICTIM_SELF (default): the one-pass update above, where
+ * a request that cannot grow preempts itself. PKV_VICTIM_LIFO / PKV_VICTIM_FEWEST:
+ * pkv_sched_update first appends every row's output and retires finished requests (in
+ * running order), then walks the running requests in order; one that produced an output
+ * and needs a block for its next token preempts victims until it gets one: the running
+ * request admitted last (LIFO) or with the fewest outputs (FEWEST; the earliest admitted
+ * on ties), among those of the least important priority class present, itself included
+ * (then it stops). Victims are preempted by swap or recompute as above and requeued as
+ * above; a swapped victim in the middle of a chunked prefill resumes with its next chunk.
+ * Priority admission ([CB] "5. Technical explanation", admission policies):
+ * pkv_sched_set_priorities gives requests (by id; host arrays [n]) a class >= 0, 0 the
+ * most important, others keep 0, before the first step; the waiting queue is then kept in
+ * (class, arrival step, id) order, preempted requests included (they take their place by
+ * that key instead of the front), and admission still stops at the first head that does
+ * not fit. INVALID: unknown ids, negative classes, calls after the first step. */
+enum { PKV_VICTIM_SELF = 0, PKV_VICTIM_LIFO = 1, PKV_VICTIM_FEWEST = 2 };
+int pkv_sched_set_victim_policy(pkv_sched* sched, int32_t policy);
+int pkv_sched_set_priorities(pkv_sched* sched, int32_t n, const int64_t* ids, const int32_t* classes);
 /* The copies of preemption by swap ([CB] "5. Technical explanation", Preemption: SWAP):
  * a pair moves every layer's K and V block, as the cache's bytes. Layouts: k_cache and
  * v_cache are device planes [num_layers][num_blocks][block_bytes] (block_bytes =

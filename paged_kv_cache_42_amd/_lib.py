@@ -80,6 +80,8 @@ _SIGS = {
     "pkv_sched_set_prompt_tokens": (C.c_int, [vp, i64, vp, i32]),
     "pkv_sched_set_token_budget": (C.c_int, [vp, i32, i32]),
     "pkv_sched_enable_swap": (C.c_int, [vp, i32]),
+    "pkv_sched_set_victim_policy": (C.c_int, [vp, i32]),
+    "pkv_sched_set_priorities": (C.c_int, [vp, i32, vp, vp]),
     "pkv_sched_swap_pairs": (C.c_int, [vp, P_i32, P_i32, vp, vp]),
     "pkv_sched_swap_counters": (C.c_int, [vp, vp]),
     "pkv_seq_share": (C.c_int, [vp, i64, vp, i32]),
@@ -162,6 +164,22 @@ class Scheduler:
         """Chunked prefill: at most max_batched_tokens new tokens per step, prefills cut into
         chunks of at most chunk_tokens (0: no limit); before the first step."""
         check(lib().pkv_sched_set_token_budget(self._h, int(max_batched_tokens), int(chunk_tokens)))
+
+    VICTIMS = {"self": 0, "lifo": 1, "fewest": 2}
+
+    def set_victim_policy(self, policy: str) -> None:
+        """"self" (default), "lifo" or "fewest" (before the first step)."""
+        if policy not in self.VICTIMS:
+            raise ValueError(f"unknown victim policy {policy!r}")
+        check(lib().pkv_sched_set_victim_policy(self._h, self.VICTIMS[policy]))
+
+    def set_priorities(self, ids, classes) -> None:
+        """Priority classes (0 most important) of the given request ids (before the first step)."""
+        i = np.ascontiguousarray(ids, dtype=np.int64)
+        c = np.ascontiguousarray(classes, dtype=np.int32)
+        if i.shape != c.shape:
+            raise ValueError("one class per id")
+        check(lib().pkv_sched_set_priorities(self._h, len(i), _np_ptr(i), _np_ptr(c)))
 
     def enable_swap(self, host_blocks: int) -> None:
         """Preemption by swap into a host space of host_blocks blocks (before the first step)."""

@@ -25,9 +25,18 @@
 // outputs, its host blocks are copied back into the first of them and freed in table
 // order, and it resumes with a decode row. The copies are listed per call: swap-outs by
 // the update, swap-ins by the schedule.
+//
+// Policy variants ("5. Technical explanation": victim selection and admission policies):
+// with the LIFO or fewest-generated victim policy the update first appends every row's
+// output and retires finished requests, then gives each running request (in order) the
+// block its next token needs, preempting victims until it gets one: the last admitted,
+// or the one with the fewest outputs (earliest admitted on ties), among the least
+// important priority class present, the request itself included. With priority classes
+// the waiting queue is ordered by (class, arrival, id), preempted requests included.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
+#include <tuple>
 #include <vector>
 
 #include "pkv.h"
@@ -48,6 +57,7 @@ struct Req {
   int32_t cached = 0;                  // prompt tokens of this prefill found in the cache
   int32_t done = 0;                    // context tokens of the current prefill computed so far
   int32_t q_step = 0;                  // new tokens of its row in the scheduled step (0: no row)
+  int32_t prio = 0;                    // priority class, 0 most important
   bool swapped = false;                // its K/V waits in `host`
   std::vector<int32_t> host;           // host blocks holding its swapped-out K/V, in table order
   std::vector<int32_t> tokens;         // prompt token ids (prefix caching), else empty
@@ -102,6 +112,55 @@ struct pkv_sched {
   std::vector<int32_t> swap_out;        // (device, host) pairs of the last update
   std::vector<int32_t> swap_in;         // (host, device) pairs of the last schedule
   int64_t swapped_out = 0, blocks_out = 0, blocks_in = 0;
+  int32_t victim = PKV_VICTIM_SELF;
+  bool by_priority = false;
+
+  // waiting queue insertion: the back (arrivals) or front (preempted), or by
+  // (class, arrival, id) with priority classes
+  void enqueue(int32_t i, bool front) {
+    if (!by_priority) {
+      if (front) waiting.push_front(i);
+      else waiting.push_back(i);
+      return;
+    }
+    auto key = [&](int32_t j) { const Req& r = reqs[size_t(j)]; return std::make_tuple(r.prio, r.arrival, r.id); };
+    auto it = waiting.begin();
+    while (it != waiting.end() && key(*it) < key(i)) ++it;
+    waiting.insert(it, i);
+  }
+  // preempt by swap when the host space holds the whole table, else by recompute
+  void preempt(int32_t i) {
+    Req& r = reqs[size_t(i)];
+    const std::vector<int32_t>& t = pool->tables.at(r.id);
+    if (swap && host_free.size() >= t.size()) {
+      r.host.clear();
+      for (int32_t b : t) {
+        r.host.push_back(host_free.back());
+        host_free.pop_back();
+        swap_out.push_back(b);
+        swap_out.push_back(r.host.back());
+      }
+      r.swapped = true;
+      ++swapped_out;
+      blocks_out += int64_t(t.size());
+    }
+    pool_release(pool, r.id);
+    ++preempted;
+    enqueue(i, true);
+  }
+  // victim among `alive` (running order) by the policy
+  size_t pick_victim(const std::vector<int32_t>& alive) const {
+    int32_t worst = 0;
+    for (int32_t j : alive) worst = std::max(worst, reqs[size_t(j)].prio);
+    size_t best = alive.size();
+    for (size_t k = 0; k < alive.size(); ++k) {
+      const Req& c = reqs[size_t(alive[k])];
+      if (c.prio != worst) continue;
+      if (victim == PKV_VICTIM_LIFO) best = k;                       // the last one
+      else if (best == alive.size() || c.n_out < reqs[size_t(alive[best])].n_out) best = k;   // first minimum
+    }
+    return best;
+  }
 
   // page-chained keys of tokens[0 : k * bs] for k = 1..pages
   std::vector<uint64_t> page_keys(const std::vector<int32_t>& tok, int64_t pages) const {
@@ -210,7 +269,7 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
   while (s->next_arrival < s->arrival_order.size()) {
     const int32_t i = s->arrival_order[s->next_arrival];
     if (s->reqs[i].arrival > s->step) break;
-    s->waiting.push_back(i);
+    s->enqueue(i, false);
     ++s->next_arrival;
   }
   // strict first-come-first-served admission
@@ -235,8 +294,7 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
       }
       s->blocks_in += int64_t(r.host.size());
       r.host.clear();
-      r.swapped = false;
-      r.stage = kDecode;
+      r.swapped = false;                  // resumes in its stage
       s->running.push_back(head);
       continue;
     }
@@ -309,6 +367,65 @@ int pkv_sched_plan(const pkv_sched* s, int32_t table_width, int64_t* ids, int32_
                                slot_mapping);
 }
 
+namespace {
+
+// the update of the LIFO / fewest-generated victim policies: outputs and retirements
+// first, then the blocks for the next tokens in running order
+int update_with_victims(pkv_sched* s) {
+  std::vector<int32_t> alive;
+  std::vector<uint8_t> grew;
+  alive.reserve(s->running.size());
+  for (int32_t i : s->running) {
+    Req& r = s->reqs[i];
+    const bool had_row = r.q_step > 0;
+    r.q_step = 0;
+    if (!had_row || (r.stage == kPrefill && r.done < r.prompt + r.n_out)) {
+      alive.push_back(i);
+      grew.push_back(0);
+      continue;
+    }
+    r.cached = 0;
+    r.n_out += 1;
+    r.stage = kDecode;
+    if (r.n_out >= r.max_tokens) {
+      pool_release(s->pool, r.id);
+      ++s->finished;
+      continue;
+    }
+    alive.push_back(i);
+    grew.push_back(1);
+  }
+  size_t k = 0;
+  while (k < alive.size()) {
+    const int32_t i = alive[k];
+    const Req& r = s->reqs[size_t(i)];
+    const int64_t need = int64_t(r.prompt) + r.n_out;
+    bool self_preempted = false;
+    if (grew[k]) {
+      while (!pool_reserve(s->pool, r.id, need)) {
+        const size_t v = s->pick_victim(alive);
+        const int32_t vi = alive[v];
+        alive.erase(alive.begin() + std::ptrdiff_t(v));
+        grew.erase(grew.begin() + std::ptrdiff_t(v));
+        if (v < k) --k;
+        s->preempt(vi);
+        if (vi == i) {
+          self_preempted = true;
+          break;
+        }
+      }
+    }
+    if (!self_preempted) ++k;
+  }
+  s->running.swap(alive);
+  s->rows.clear();
+  s->scheduled = false;
+  ++s->step;
+  return PKV_OK;
+}
+
+}  // namespace
+
 int pkv_sched_update(pkv_sched* s) {
   if (!s) return fail(PKV_ERR_INVALID, "sched_update: scheduler is NULL");
   if (!s->scheduled) return fail(PKV_ERR_INVALID, "sched_update: no step scheduled");
@@ -322,6 +439,7 @@ int pkv_sched_update(pkv_sched* s) {
       const Req& r = s->reqs[i];
       if (r.stage == kPrefill && r.done == r.prompt + r.n_out && !r.tokens.empty()) s->insert(i);
     }
+  if (s->victim != PKV_VICTIM_SELF) return update_with_victims(s);
   std::vector<int32_t> still;
   still.reserve(s->running.size());
   for (int32_t i : s->running) {
@@ -341,23 +459,8 @@ int pkv_sched_update(pkv_sched* s) {
       continue;
     }
     const int64_t need = int64_t(r.prompt) + r.n_out;   // tokens the next row writes up to
-    if (!pool_reserve(s->pool, r.id, need)) {  // no block for the next token: preempt
-      const std::vector<int32_t>& t = s->pool->tables.at(r.id);
-      if (s->swap && s->host_free.size() >= t.size()) {   // by swap
-        r.host.clear();
-        for (int32_t b : t) {
-          r.host.push_back(s->host_free.back());
-          s->host_free.pop_back();
-          s->swap_out.push_back(b);
-          s->swap_out.push_back(r.host.back());
-        }
-        r.swapped = true;
-        ++s->swapped_out;
-        s->blocks_out += int64_t(t.size());
-      }                                        // else by recompute
-      pool_release(s->pool, r.id);
-      ++s->preempted;
-      s->waiting.push_front(i);
+    if (!pool_reserve(s->pool, r.id, need)) {  // no block for the next token: it preempts itself
+      s->preempt(i);
       continue;
     }
     still.push_back(i);
@@ -382,6 +485,29 @@ int pkv_sched_set_token_budget(pkv_sched* s, int32_t max_batched_tokens, int32_t
     return fail(PKV_ERR_INVALID, "sched_set_token_budget: call before the first step");
   s->max_batched_tokens = max_batched_tokens;
   s->chunk_tokens = chunk_tokens;
+  return PKV_OK;
+}
+
+int pkv_sched_set_victim_policy(pkv_sched* s, int32_t policy) {
+  if (!s || policy < PKV_VICTIM_SELF || policy > PKV_VICTIM_FEWEST)
+    return fail(PKV_ERR_INVALID, "sched_set_victim_policy: bad arguments");
+  if (s->step > 0 || s->scheduled)
+    return fail(PKV_ERR_INVALID, "sched_set_victim_policy: call before the first step");
+  s->victim = policy;
+  return PKV_OK;
+}
+
+int pkv_sched_set_priorities(pkv_sched* s, int32_t n, const int64_t* ids, const int32_t* classes) {
+  if (!s || n < 0 || (n > 0 && (!ids || !classes))) return fail(PKV_ERR_INVALID, "sched_set_priorities: bad arguments");
+  if (s->step > 0 || s->scheduled)
+    return fail(PKV_ERR_INVALID, "sched_set_priorities: call before the first step");
+  for (int32_t k = 0; k < n; ++k) {
+    if (classes[k] < 0) return fail(PKV_ERR_INVALID, "sched_set_priorities: class %d < 0", classes[k]);
+    if (!s->index.count(ids[k]))
+      return fail(PKV_ERR_INVALID, "sched_set_priorities: unknown request %lld", (long long)ids[k]);
+  }
+  for (int32_t k = 0; k < n; ++k) s->reqs[size_t(s->index.at(ids[k]))].prio = classes[k];
+  s->by_priority = true;
   return PKV_OK;
 }
 

@@ -9,7 +9,7 @@ import workloads
 from oracle import scheduler as osch
 
 
-def _pair(tr, prefix=False, budget=0, chunk=0, swap=0):
+def _pair(tr, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None):
     pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
                     free_order=tr.free_order)
     ours = pkv.Scheduler(pool, tr.max_running)
@@ -22,9 +22,13 @@ def _pair(tr, prefix=False, budget=0, chunk=0, swap=0):
         ours.set_token_budget(budget, chunk)
     if swap:
         ours.enable_swap(swap)
+    if victim != "self":
+        ours.set_victim_policy(victim)
+    if prio is not None:
+        ours.set_priorities(np.arange(tr.num_requests), prio)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
                          tr.max_running, prompt_tokens=toks, max_batched_tokens=budget, chunk_tokens=chunk,
-                         swap_blocks=swap)
+                         swap_blocks=swap, victim=victim, priority=prio)
     return pool, ours, ref
 
 
@@ -35,8 +39,8 @@ def _counters(ours, swap):
     return c
 
 
-def _replay_both(tr, width, prefix=False, budget=0, chunk=0, swap=0):
-    pool, ours, ref = _pair(tr, prefix, budget, chunk, swap)
+def _replay_both(tr, width, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None):
+    pool, ours, ref = _pair(tr, prefix, budget, chunk, swap, victim, prio)
     steps = 0
     for rp, rafter in osch.run(ref, width):
         n, q, mb = ours.schedule()
@@ -244,3 +248,48 @@ def test_swap_api_errors():
     s.update()
     with pytest.raises(pkv.PkvError):
         s.enable_swap(8)                                   # after the first step
+
+
+@pytest.mark.parametrize("victim", ["lifo", "fewest"])
+def test_victim_policy_config5_full_trace_bit_exact(victim):
+    tr = workloads.config5()
+    steps, ref = _replay_both(tr, 512, victim=victim)
+    assert ref.preemptions > 0
+
+
+def test_priority_lifo_swap_chunked_config5_bit_exact():
+    tr = workloads.config5()
+    prio = workloads.priority_classes(tr)
+    steps, ref = _replay_both(tr, 512, victim="lifo", prio=prio, swap=1024, budget=2048, chunk=512)
+    assert ref.preemptions > 0 and ref.swapped_out > 0
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10_000), st.integers(18, 60), st.integers(1, 8), st.sampled_from(["self", "lifo", "fewest"]),
+       st.sampled_from([0, 16]), st.sampled_from([(0, 0), (8, 4)]), st.booleans(), st.booleans())
+def test_policies_random_small_traces_bit_exact(seed, pool, max_running, victim, swap, budget, prio, prefix):
+    tr = workloads.small_trace(seed, 30, pool, block_size=4, max_running=max_running, prompt_max=24 if prefix else 40,
+                               out_max=16 if prefix else 30, rate=2.0, groups=3 if prefix else 0)
+    classes = np.random.default_rng(seed).integers(0, 3, 30).astype(np.int32) if prio else None
+    _replay_both(tr, 20, prefix=prefix, budget=budget[0], chunk=budget[1], swap=swap, victim=victim, prio=classes)
+
+
+def test_policy_api_errors():
+    pool = pkv.Pool(16, 4, 1, 64, "bf16")
+    s = pkv.Scheduler(pool, 2)
+    s.add_requests([1, 2], [0, 0], [5, 6], [2, 2])
+    assert pkv.lib().pkv_sched_set_victim_policy(s._h, 3) != 0    # no such policy
+    with pytest.raises(ValueError):
+        s.set_victim_policy("oldest")
+    with pytest.raises(pkv.PkvError):
+        s.set_priorities([1, 7], [0, 1])                   # unknown id
+    with pytest.raises(pkv.PkvError):
+        s.set_priorities([1], [-1])
+    s.set_victim_policy("lifo")
+    s.set_priorities([2], [1])
+    s.schedule()
+    s.update()
+    with pytest.raises(pkv.PkvError):
+        s.set_victim_policy("fewest")                      # after the first step
+    with pytest.raises(pkv.PkvError):
+        s.set_priorities([1], [0])

@@ -47,6 +47,7 @@ _STREAM_GROUPS = 34         # prefix traces: group of each request
 _STREAM_SHARED = 35         #   lengths of the groups' shared prompts
 _STREAM_UNIQUE = 36         #   lengths of the requests' own prompt parts
 _STREAM_TOKENS = 37         #   token ids
+_STREAM_PRIORITY = 38       # priority class of each request
 GROUP_OWNER = 1 << 23       # value/token streams of group g are owned by GROUP_OWNER + g
 
 
@@ -534,6 +535,13 @@ def config5_prefix(cache_dtype: str = "bf16") -> Trace:
     prompt = np.minimum(plen + own.astype(np.int32), 4096).astype(np.int32)
     return dataclasses.replace(base, name=f"cfg5p_prefix_trace_{cache_dtype}", prompt=prompt, prefix_group=group,
                                prefix_len=np.minimum(plen, prompt - 1).astype(np.int32))
+
+
+def priority_classes(tr: Trace, premium: float = 0.25) -> np.ndarray:
+    """Priority class per request for the priority-admission variant: 0 (premium) with
+    probability `premium`, else 1 (bulk); a seeded draw of its own."""
+    u = rng_for(tr.seed, _STREAM_PRIORITY).random(tr.num_requests)
+    return np.where(u < premium, 0, 1).astype(np.int32)
 
 
 def small_trace(seed: int, n: int, num_blocks: int, block_size: int = 4, max_running: int = 8,
