@@ -377,12 +377,22 @@ def sched_replay(max_steps):
             # preemption by swap into a host space of 4096 blocks (instead of recompute)
             ("bf16_swap", workloads.config5("bf16"), {"swap_blocks": 4096}),
             ("bf16_swap_overlap", workloads.config5("bf16"), {"swap_blocks": 4096, "swap_overlap": True}),
+            # victim policies (LIFO; fewest generated) and priority admission (25% premium)
+            ("bf16_victim_lifo", workloads.config5("bf16"), {"victim": "lifo"}),
+            ("bf16_victim_fewest", workloads.config5("bf16"), {"victim": "fewest"}),
+            ("bf16_fcfs_classes", workloads.config5("bf16"), {"classes": True}),
+            ("bf16_priority", workloads.config5("bf16"), {"priority": True}),
+            ("bf16_priority_lifo", workloads.config5("bf16"), {"priority": True, "victim": "lifo"}),
             # shared system prompts (16 groups), with and without the prefix cache
             ("bf16_prefix_cache", workloads.config5_prefix("bf16"), {}),
             ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), {"prefix_cache": False})]
     for name, tr, kw in runs:
         print(f"[bench] replay {name}: {tr.name} {kw}", file=sys.stderr, flush=True)
-        _, summ = replay.run(tr, max_steps=max_steps, **kw,
+        args = dict(kw)
+        for key in ("priority", "classes"):    # 25% premium (class 0), 75% bulk (class 1)
+            if args.get(key):
+                args[key] = workloads.priority_classes(tr)
+        _, summ = replay.run(tr, max_steps=max_steps, **args,
                              progress=lambda n: print(f"[bench] replay {name}: {n} steps", file=sys.stderr, flush=True))
         summ.update({k: v for k, v in kw.items() if k != "prefix_cache"})
         out[name] = summ

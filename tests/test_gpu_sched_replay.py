@@ -126,3 +126,38 @@ def test_chunked_prefill_replay_sampled_parity():
     for s in keep_steps:
         checked += _check_step(tr, by_step[s], rng)
     assert checked >= 12
+
+
+def test_policy_variants_replay_sampled_parity():
+    # LIFO victims among the bulk class, priority admission, a short host space (swap and
+    # recompute both happen): rows of re-admitted victims attend to the right K/V
+    from oracle import scheduler as osch
+    tr = workloads.config5("bf16")
+    prio = workloads.priority_classes(tr)
+    ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
+                         tr.max_running, swap_blocks=64, victim="lifo", priority=prio)
+    plans, back, again = {}, [], []
+    for plan, _ in osch.run(ref, 512, 300):
+        plans[plan.step] = plan
+        if plan.swap_in:
+            back.append(plan.step)
+        if any(st_ == 0 and q > tr.prompt[i] for i, st_, q in zip(plan.ids, plan.stages, plan.q_lens)):
+            again.append(plan.step)
+    assert back and again
+    keep_steps = sorted(set(back[:2] + again[:2]))
+    keep = {s: (0, tr.num_layers - 1) for s in keep_steps}
+    recs, summary = replay.run(tr, max_steps=max(keep_steps) + 1, keep=keep, swap_blocks=64, victim="lifo",
+                               priority=prio)
+    assert summary["preemptions"] > 0 and summary["swap"]["swapped_out"] > 0
+    by_step = {r.step: r for r in recs}
+    rng = np.random.default_rng(19)
+    checked = 0
+    for s in keep_steps:
+        p = by_step[s].plan
+        assert (p.ids == plans[s].ids).all() and (p.seq_lens == plans[s].seq_lens).all()
+        swapped_blocks = {int(b) for _, b in plans[s].swap_in}
+        prefer = [int(i) for k, (i, st_, q) in enumerate(zip(p.ids, p.stages, p.q_lens))
+                  if (st_ == 0 and q > tr.prompt[i]) or swapped_blocks & set(p.block_tables[k].tolist())]
+        assert prefer
+        checked += _check_step(tr, by_step[s], rng, prefer=prefer)
+    assert checked >= 8

@@ -35,12 +35,13 @@ class StepRecord:
     host_s: float = 0.0          # host time to enqueue the step's layers (between the events)
     swap_ev: tuple = ()          # (swap-in end event, swap-out start, swap-out end) or None entries
     swap_blocks: tuple = (0, 0)  # (blocks swapped in before the layers, swapped out after the update)
+    decode_by_class: tuple = ()  # decode rows per priority class (priority replays)
 
 
 class Replay:
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
                  prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0,
-                 swap_overlap: bool = False):
+                 swap_overlap: bool = False, victim: str = "self", priority=None, classes=None):
         import torch
         self.torch = torch
         self.tr = tr
@@ -67,6 +68,13 @@ class Replay:
         if token_budget or chunk_tokens:                       # chunked prefill
             self.sched.set_token_budget(token_budget, chunk_tokens)
         self.n_out = np.zeros(tr.num_requests, np.int64)        # outputs per request so far
+        if victim != "self":
+            self.sched.set_victim_policy(victim)
+        self.priority = None if priority is None else np.asarray(priority, np.int32)
+        if self.priority is not None:                          # priority admission
+            self.sched.set_priorities(np.arange(tr.num_requests), self.priority)
+        # classes to report latencies by (the priority classes, or labels only)
+        self.classes = self.priority if classes is None else np.asarray(classes, np.int32)
         self.host_space = self.swap_ws = None
         if swap_blocks:                                        # preemption by swap
             self.sched.enable_swap(swap_blocks)
@@ -216,7 +224,13 @@ class Replay:
                      + T * tr.num_q_heads * tr.head_dim * 2 * 2)              # queries in, outputs out
         return StepRecord(step_no, n, T, ctx, int((plan.stages == 0).sum()), per_layer * tr.num_layers,
                           (e0, e1), kept, plan if keep_plan else None, first.tolist(), host_s, (ei, es0, es1),
-                          (len(swap_in), len(swap_out)))
+                          (len(swap_in), len(swap_out)), self._decode_by_class(plan))
+
+    def _decode_by_class(self, plan):
+        if self.classes is None:
+            return ()
+        cls = self.classes[plan.ids[plan.stages == 1]]
+        return tuple(np.bincount(cls, minlength=int(self.classes.max()) + 1).tolist())
 
     def _swap_workspace(self, n):
         nb = pkv.swap_workspace_bytes(n, self.tr.num_layers, self.pair_bytes // (2 * self.tr.num_layers))
@@ -304,6 +318,13 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
         "ttft_ms": pct(ttft), "tbt_ms": pct(tbt),
         "wall_s": round(wall, 2),
     }
+    if rp.classes is not None:                 # latencies per priority class
+        by = {}
+        for c in range(int(rp.classes.max()) + 1):
+            sel = rp.classes[got] == c
+            tb = np.repeat(t, [r.decode_by_class[c] for r in recs])
+            by[str(c)] = {"requests": int((rp.classes == c).sum()), "ttft_ms": pct(ttft[sel]), "tbt_ms": pct(tb)}
+        summary["by_priority_class"] = by
     if rp.host_space is not None:
         sc = rp.sched.swap_counters()
         b_in = sum(r.swap_blocks[0] for r in recs) * rp.pair_bytes
