@@ -10,6 +10,9 @@ Write ("Step 4: Implement the paged KV cache", append): for every new token i
 and KV head h, plane[slot_i // bs][slot_i % bs][h][:] = enc(x[i][h][:]); nothing
 else changes. enc is a bit copy for f32 and bf16, the E4M3 encoder of fp8.py
 for an fp8 cache. A negative slot skips the token (padding rows).
+
+An fp8 scale may be per KV head (an array [Hkv], see fp8.py): it then applies along the
+head axis of the rows and planes.
 """
 from __future__ import annotations
 
@@ -36,14 +39,19 @@ def _bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _along_heads(scale):
+    """A per-head scale array [Hkv] as [Hkv][1], to broadcast over [..., Hkv, d]."""
+    return np.asarray(scale, dtype=np.float64)[:, None] if np.ndim(scale) == 1 else scale
+
+
 def write(plane: np.ndarray, x: np.ndarray, in_dtype: str, cache_dtype: str,
-          slot_mapping, scale: float = 1.0) -> None:
+          slot_mapping, scale=1.0) -> None:
     """Scatter new rows x [T][Hkv][d] (float32 array or bf16 bits) into plane."""
     nb, bs = plane.shape[0], plane.shape[1]
     src = _bits_in(x, in_dtype)
     if cache_dtype == "fp8":
         xf = src.view(np.float32) if in_dtype == "f32" else _bf16_bits_to_f32(src)
-        enc = fp8.encode(xf, scale)
+        enc = fp8.encode(xf, _along_heads(scale))
     elif cache_dtype == in_dtype:
         enc = src
     else:
@@ -61,14 +69,14 @@ def write(plane: np.ndarray, x: np.ndarray, in_dtype: str, cache_dtype: str,
         plane[slot // bs, slot % bs] = enc[i]
 
 
-def decode_plane(plane: np.ndarray, cache_dtype: str, scale: float = 1.0) -> np.ndarray:
+def decode_plane(plane: np.ndarray, cache_dtype: str, scale=1.0) -> np.ndarray:
     """Exact float64 values of a cache plane (fp8 codes times scale)."""
     if cache_dtype == "f32":
         return plane.view(np.float32).astype(np.float64)
     if cache_dtype == "bf16":
         return _bf16_bits_to_f32(plane).astype(np.float64)
     if cache_dtype == "fp8":
-        return fp8.decode(plane, scale)
+        return fp8.decode(plane, _along_heads(scale))
     raise ValueError(cache_dtype)
 
 

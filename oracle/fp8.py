@@ -11,6 +11,11 @@ inv_scale = fl32(1 / scale); NaN encodes as 0x7F with the sign of y; |y| >= 448
 value, ties to the code with an even mantissa. The sign bit of y is kept, also
 when the magnitude rounds to zero. The encoder is brute force over all codes.
 
+Per-head scales (an extension the pages do not cover: they fix no 8-bit format at all):
+KV head h has its own scale, the per-tensor scale times a head factor (both float32
+values, the product taken in float64); encode and decode then use that head's scale for
+the head's elements. `scale` may be such an array, broadcast against the codes.
+
 Pinned by: values fixed by the format definition, the round trip of every finite
 code, and agreement with torch's independent float8_e4m3fn cast wherever that
 cast does not overflow (tests/test_oracle_fp8.py).
@@ -45,8 +50,16 @@ _POS_CODES = np.arange(0x7F, dtype=np.int64)
 _POS_VALUES = DECODE_TABLE[:0x7F]
 
 
-def inv_scale_f32(scale: float) -> np.float32:
-    return np.float32(1.0 / float(scale))
+def inv_scale_f32(scale):
+    """fl32(1 / scale), elementwise for an array of scales."""
+    if np.ndim(scale) == 0:
+        return np.float32(1.0 / float(scale))
+    return (1.0 / np.asarray(scale, dtype=np.float64)).astype(np.float32)
+
+
+def head_scales(scale: float, head_factors) -> np.ndarray:
+    """Per-head scales: the per-tensor scale times each head's factor, in float64."""
+    return np.float64(np.float32(scale)) * np.asarray(head_factors, dtype=np.float32).astype(np.float64)
 
 
 def encode_one(y: float) -> int:
@@ -86,6 +99,7 @@ def encode(x, scale: float = 1.0) -> np.ndarray:
     return out.reshape(y.shape)
 
 
-def decode(codes, scale: float = 1.0) -> np.ndarray:
-    """Exact float64 values of codes, times the per-tensor scale."""
-    return DECODE_TABLE[np.asarray(codes, dtype=np.uint8)] * float(scale)
+def decode(codes, scale=1.0) -> np.ndarray:
+    """Exact float64 values of codes, times the scale (per tensor, or an array broadcast
+    against the codes)."""
+    return DECODE_TABLE[np.asarray(codes, dtype=np.uint8)] * np.asarray(scale, dtype=np.float64)

@@ -75,3 +75,44 @@ def test_random_float32_inputs_against_torch_cast():
     x = (rng.standard_normal(200_000) * np.exp(rng.uniform(-12, 6, 200_000))).astype(np.float32)
     x = x[np.abs(x) < 464]
     np.testing.assert_array_equal(fp8.encode(x), _torch_codes(x))
+
+
+def test_per_head_scales_reduce_to_per_tensor_and_follow_the_head_axis():
+    # per-head scale = per-tensor scale x head factor (float64 product of float32 values)
+    hs = fp8.head_scales(0.5, np.array([1.0, 3.0, 0.25], np.float32))
+    assert hs.tolist() == [0.5, 1.5, 0.125]
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 2, (7, 3, 16)).astype(np.float32)          # [T][Hkv][d]
+    # all factors 1: identical codes to the per-tensor encoder
+    ones = fp8.head_scales(0.5, np.ones(3, np.float32))
+    assert (fp8.encode(x, ones[:, None]) == fp8.encode(x, 0.5)).all()
+    # each head's slice is the per-tensor encoding with that head's scale
+    codes = fp8.encode(x, hs[:, None])
+    for h in range(3):
+        assert (codes[:, h] == fp8.encode(x[:, h], float(hs[h]))).all()
+    # decode by hand: code 0x38 is 1.0, so head h decodes it to its scale
+    c = np.full((2, 3, 4), 0x38, np.uint8)
+    assert (fp8.decode(c, hs[:, None]) == np.broadcast_to(hs[:, None], (2, 3, 4))).all()
+
+
+def test_paged_attention_with_per_head_scales_equals_hand_dequantised_dense():
+    from oracle import attention as oatt
+    from oracle import cache as ocache
+    rng = np.random.default_rng(9)
+    T, Hkv, d, G, bs = 11, 2, 8, 2, 4
+    ks = fp8.head_scales(0.5, np.array([0.25, 4.0], np.float32))
+    vs = fp8.head_scales(2.0, np.array([1.5, 0.125], np.float32))
+    k = rng.normal(0, 1, (T, Hkv, d)).astype(np.float32)
+    v = rng.normal(0, 1, (T, Hkv, d)).astype(np.float32)
+    kp = ocache.empty_plane(3, bs, Hkv, d, "fp8")
+    vp = ocache.empty_plane(3, bs, Hkv, d, "fp8")
+    slots = np.array([8, 9, 10, 11, 0, 1, 2, 3, 4, 5, 6])        # blocks 2, 0, 1
+    ocache.write(kp, k, "f32", "fp8", slots, ks)
+    ocache.write(vp, v, "f32", "fp8", slots, vs)
+    q = rng.normal(0, 1, (1, Hkv * G, d))
+    out, _ = oatt.paged_attention(q, kp, vp, "fp8", np.array([[2, 0, 1]], np.int32), [T], [0, 1], 0.3, G, ks, vs)
+    # by hand: codes of each head times that head's scale, then plain attention
+    K = np.stack([fp8.decode(fp8.encode(k[:, h], float(ks[h])), float(ks[h])) for h in range(Hkv)], 1)
+    V = np.stack([fp8.decode(fp8.encode(v[:, h], float(vs[h])), float(vs[h])) for h in range(Hkv)], 1)
+    ref, _ = oatt.attend(q, K, V, [T - 1], 0.3, G)
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
