@@ -135,11 +135,18 @@ int pkv_build_block_table(const pkv_pool* pool, int32_t num_seqs, const int64_t*
  * E4M3 cache, y = fl32(x * fl32(1/scale)) rounded to nearest-even E4M3, |y| >= 448
  * saturating to 448 with y's sign, NaN -> 0x7F with y's sign. Supported
  * (in, cache): (f32,f32), (bf16,bf16), (bf16,fp8), (f32,fp8); else UNSUPPORTED.
- * Two tokens mapped to one slot race (the result is one of them). */
+ * Two tokens mapped to one slot race (the result is one of them).
+ * Per-head E4M3 scales (all attention calls take the same pair): k_head_scales /
+ * v_head_scales are host float [num_kv_heads] or NULL (factors of 1); head h's scale is
+ * k_scale * k_head_scales[h] (the product in double), so scale above is that product
+ * for head h's elements. Each factor must be finite and > 0; with per-head factors
+ * num_kv_heads is at most 16 and head_dim a multiple of 8 (INVALID otherwise). They are
+ * read during the call only. */
 int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
                        int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
                        int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
-                       const int64_t* slot_mapping, float k_scale, float v_scale, void* stream);
+                       const int64_t* slot_mapping, float k_scale, float v_scale,
+                       const float* k_head_scales, const float* v_head_scales, void* stream);
 
 /* Decode work list (host): one item per non-empty (sequence, context partition), so the
  * decode launch has no idle workgroups. seq_lens: host int32 [num_seqs] (the values the
@@ -165,8 +172,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * seq_lens: device int32 [num_seqs], each in 0..min(max_seq_len, table_width*bs)
  * (a sequence with seq_len 0 gets zeros and log-sum-exp -inf; larger values are
  * clamped to that bound); table entries outside 0..num_blocks-1 are skipped.
- * Keys are decoded as code * k_scale (values * v_scale) for an E4M3 cache; pass 1.0
- * otherwise. Supported: (q, cache) in {(f32,f32), (bf16,bf16), (bf16,fp8)};
+ * Keys are decoded as code * k_scale (values * v_scale) for an E4M3 cache, times
+ * k_head_scales[h] (v_head_scales[h]) for KV head h when those host arrays
+ * [num_kv_heads] are given (NULL: 1; at most 16 KV heads with them; as in
+ * pkv_kv_cache_write); pass 1.0 and NULL otherwise. The same scale arguments, with the
+ * same meaning, are taken by the split decode, the varlen and the chunk launches. Supported: (q, cache) in {(f32,f32), (bf16,bf16), (bf16,fp8)};
  * head_dim 64 or 128; block_size 16 or 32; num_q_heads/num_kv_heads in {1,2,4,8}.
  * partition_size 0 processes each sequence in one pass; otherwise (a multiple of
  * block_size) the context is split into partitions of that many tokens whose partial
@@ -183,7 +193,8 @@ int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const 
                                int32_t table_width, int32_t num_seqs, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_seq_len, float scale,
-                               float k_scale, float v_scale, int32_t partition_size,
+                               float k_scale, float v_scale, const float* k_head_scales,
+                               const float* v_head_scales, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, float* lse_out,
                                const int32_t* work_items, int32_t num_work, void* stream);
 
@@ -243,7 +254,8 @@ int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,
                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                      int32_t max_seq_len, float scale, float k_scale,
-                                     float v_scale, const int32_t* rows, int32_t num_rows,
+                                     float v_scale, const float* k_head_scales,
+                                     const float* v_head_scales, const int32_t* rows, int32_t num_rows,
                                      const int32_t* cu_seqlens_q, int32_t total_q,
                                      const int32_t* plan, int32_t num_slots,
                                      int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
@@ -280,6 +292,7 @@ int pkv_paged_attention_prefill_varlen(void* out, const void* q, int32_t q_dtype
                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
                                        float scale, float k_scale, float v_scale,
+                                       const float* k_head_scales, const float* v_head_scales,
                                        const int32_t* work_items, int32_t num_work, float* lse_out,
                                        void* stream);
 
@@ -335,6 +348,7 @@ int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype
                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
                                        float scale, float k_scale, float v_scale,
+                                       const float* k_head_scales, const float* v_head_scales,
                                        const int32_t* work_items, int32_t num_work,
                                        const int32_t* merges, int32_t num_merges, int32_t num_partials,
                                        void* workspace, int64_t workspace_bytes, float* lse_out,

@@ -51,17 +51,17 @@ _SIGS = {
     "pkv_seq_release": (C.c_int, [vp, i64]),
     "pkv_seq_table": (C.c_int, [vp, i64, vp, i32, P_i32]),
     "pkv_build_block_table": (C.c_int, [vp, i32, vp, vp, vp, i32, vp, vp, vp]),
-    "pkv_kv_cache_write": (C.c_int, [vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, f32, f32, vp]),
+    "pkv_kv_cache_write": (C.c_int, [vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, f32, f32, vp, vp, vp]),
     "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
     "pkv_decode_set_profile_event": (None, [vp]),
     "pkv_paged_attention_decode": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
-                                             i32, i32, f32, f32, f32, i32, vp, sz, vp, vp, i32, vp]),
+                                             i32, i32, f32, f32, f32, vp, vp, i32, vp, sz, vp, vp, i32, vp]),
     "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
     "pkv_build_varlen_work": (C.c_int, [i32, vp, vp, i32, i32, vp, i32, P_i32]),
     "pkv_build_decode_split": (C.c_int, [i32, vp, i32, i32, vp, i32, P_i32, P_i32]),
     "pkv_paged_attention_prefill_chunks": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
-                                                     i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, i32, i32, vp,
-                                                     i64, vp, vp]),
+                                                     i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32,
+                                                     i32, vp, i64, vp, vp]),
     "pkv_build_chunk_work": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, vp, i32, P_i32, vp, i32, P_i32, P_i32]),
     "pkv_chunk_slots": (C.c_int, [i32, i32, i32, P_i32]),
     "pkv_chunk_workspace_bytes": (i64, [i32, i32]),
@@ -89,10 +89,10 @@ _SIGS = {
     "pkv_decode_split_slots": (C.c_int, [i32, i32, i32, i32, P_i32]),
     "pkv_decode_split_workspace_bytes": (sz, [i32, i32, i32, i32]),
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                   i32, i32, f32, f32, f32, vp, i32, vp, i32, vp, i32, i32, i32, vp,
-                                                   sz, vp, vp]),
+                                                   i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+                                                   i32, vp, sz, vp, vp]),
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
-                                                     i32, i32, i32, i32, f32, f32, f32, vp, i32, vp, vp]),
+                                                     i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, vp]),
 }
 
 
@@ -417,9 +417,22 @@ def swap_in(k_cache, v_cache, pairs, host_space, workspace, stream=None) -> None
                             vp(host_space.data_ptr()), cap, _dptr(workspace), ws, _stream(stream)))
 
 
+def _heads(k_head_scales, v_head_scales, num_kv_heads: int):
+    """float32 arrays [num_kv_heads] (or None) of the per-head scale factors."""
+    out = []
+    for h in (k_head_scales, v_head_scales):
+        if h is not None:
+            h = np.ascontiguousarray(h, dtype=np.float32)
+            if h.shape != (num_kv_heads,):
+                raise ValueError(f"per-head scales must be [{num_kv_heads}]")
+        out.append(h)
+    return out
+
+
 def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scale: float = 1.0,
-                   v_scale: float = 1.0, stream=None) -> None:
-    """k, v: [T][Hkv][d]; caches: [num_blocks][block_size][Hkv][d]; slot_mapping int64 [T]."""
+                   v_scale: float = 1.0, stream=None, k_head_scales=None, v_head_scales=None) -> None:
+    """k, v: [T][Hkv][d]; caches: [num_blocks][block_size][Hkv][d]; slot_mapping int64 [T];
+    k_head_scales / v_head_scales: optional per-KV-head factors of the E4M3 scales."""
     torch = _torch()
     _require_cuda_contig(k, v, k_cache, v_cache, slot_mapping)
     if k.dim() != 3 or v.shape != k.shape or v.dtype != k.dtype:
@@ -428,9 +441,11 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scal
     _check_plane(k_cache, v_cache, block_size, Hkv, d)
     if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be int64 [T]")
+    kh, vh = _heads(k_head_scales, v_head_scales, Hkv)
     check(lib().pkv_kv_cache_write(_dptr(k), _dptr(v), tensor_dtype_code(k), T, Hkv, d, _dptr(k_cache),
                                    _dptr(v_cache), tensor_dtype_code(k_cache), k_cache.shape[0], block_size,
-                                   _dptr(slot_mapping), k_scale, v_scale, _stream(stream)))
+                                   _dptr(slot_mapping), k_scale, v_scale, _np_ptr(kh), _np_ptr(vh),
+                                   _stream(stream)))
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
@@ -451,7 +466,7 @@ def build_decode_work(seq_lens, partition_size: int) -> np.ndarray:
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int,
                            block_size: int, max_seq_len: int, scale: float, k_scale: float = 1.0,
                            v_scale: float = 1.0, partition_size: int = 0, workspace=None, lse=None,
-                           work=None, stream=None) -> None:
+                           work=None, stream=None, k_head_scales=None, v_head_scales=None) -> None:
     """q/out: [B][Hq][d]; block_tables int32 [B][W]; seq_lens int32 [B]."""
     torch = _torch()
     _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, workspace, lse)
@@ -473,7 +488,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num
     check(lib().pkv_paged_attention_decode(
         _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
         _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
-        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, partition_size, _dptr(workspace), ws_bytes,
+        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, *map(_np_ptr, _heads(k_head_scales, v_head_scales,
+                                                                                   num_kv_heads)),
+        partition_size, _dptr(workspace), ws_bytes,
         _dptr(lse), _dptr(work), 0 if work is None else work.shape[0], _stream(stream)))
 
 
@@ -509,7 +526,8 @@ def decode_split_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
 def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split: SplitPlan,
                                  num_kv_heads: int, block_size: int, max_seq_len: int, scale: float,
                                  k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, lse=None,
-                                 rows=None, cu_seqlens_q=None, stream=None) -> None:
+                                 rows=None, cu_seqlens_q=None, stream=None, k_head_scales=None,
+                                 v_head_scales=None) -> None:
     """Balanced-split decode. Without rows / cu_seqlens_q: q/out [B][Hq][d], one plan row per
     sequence. rows (device int32 [n]): the batch sequences the plan covers; cu_seqlens_q
     (device int32 [B + 1]): q/out are [total_q][Hq][d] and a sequence's row is its last
@@ -541,7 +559,8 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
     check(lib().pkv_paged_attention_decode_split(
         _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
         _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
-        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(rows), n, _dptr(cu_seqlens_q), T,
+        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
+        *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(rows), n, _dptr(cu_seqlens_q), T,
         _dptr(plan_dev), split.num_slots, split.tiles_per_slot, split.max_pieces, _dptr(workspace), ws_bytes,
         _dptr(lse), _stream(stream)))
 
@@ -641,7 +660,8 @@ def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots:
 
 def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,
                                    num_kv_heads: int, block_size: int, max_seq_len: int, scale: float,
-                                   k_scale: float = 1.0, v_scale: float = 1.0, lse=None, stream=None) -> None:
+                                   k_scale: float = 1.0, v_scale: float = 1.0, lse=None, stream=None,
+                                   k_head_scales=None, v_head_scales=None) -> None:
     """q/out: [total_q][Hq][d] bf16; cu_seqlens_q int32 [B+1]; work int32 [n][4] (device)."""
     torch = _torch()
     _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work, lse)
@@ -661,14 +681,15 @@ def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_l
     check(lib().pkv_paged_attention_prefill_varlen(
         _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
         _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads, d,
-        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(work), work.shape[0], _dptr(lse),
+        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
+        *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(work), work.shape[0], _dptr(lse),
         _stream(stream)))
 
 
 def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,
                                    merges, num_partials: int, workspace, num_kv_heads: int, block_size: int,
                                    max_seq_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-                                   lse=None, stream=None) -> None:
+                                   lse=None, stream=None, k_head_scales=None, v_head_scales=None) -> None:
     """Rows of the sequences with two or more new tokens. work: device int32 [n][8] and
     merges: device int32 [m][4] (or None) from build_chunk_work, num_partials its slots,
     workspace: device tensor of at least chunk_workspace_bytes (None when no slots); the
@@ -697,5 +718,6 @@ def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_l
     check(lib().pkv_paged_attention_prefill_chunks(
         _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
         _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads, d,
-        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale, _dptr(work), work.shape[0],
+        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
+        *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(work), work.shape[0],
         _dptr(merges), nm, num_partials, _dptr(workspace), wsb, _dptr(lse), _stream(stream)))

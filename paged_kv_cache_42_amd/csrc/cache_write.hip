@@ -8,6 +8,8 @@
 // and in the cache, so each lane moves 16 contiguous bytes of input.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -34,13 +36,20 @@ __global__ void __launch_bounds__(256) write_copy16(const uint4* __restrict__ k,
   }
 }
 
-// To E4M3: 8 input elements (16 B of bf16 or 32 B of f32) -> 8 code bytes per lane.
+// Inverse scales per KV head (every slot equal without per-head factors).
+struct InvScales {
+  float k[pkv::kHeadScales];
+  float v[pkv::kHeadScales];
+};
+
+// To E4M3: 8 input elements (16 B of bf16 or 32 B of f32) -> 8 code bytes per lane;
+// chunk c of a token row belongs to KV head c / chunks_per_head.
 template <bool IN_BF16>
 __global__ void __launch_bounds__(256) write_fp8(const void* __restrict__ k_, const void* __restrict__ v_,
                                                  uint2* __restrict__ kc, uint2* __restrict__ vc,
                                                  const int64_t* __restrict__ slots, int64_t num_tokens,
                                                  int64_t chunks_per_row, int64_t num_slots,
-                                                 float k_inv, float v_inv) {
+                                                 int64_t chunks_per_head, InvScales inv) {
   const int64_t total = num_tokens * chunks_per_row;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
@@ -73,6 +82,10 @@ __global__ void __launch_bounds__(256) write_fp8(const void* __restrict__ k_, co
         vx[j] = va[j];
       }
     }
+    const int64_t hh = c / chunks_per_head;
+    const int h = hh < pkv::kHeadScales ? int(hh) : pkv::kHeadScales - 1;
+    const float k_inv = inv.k[h];
+    const float v_inv = inv.v[h];
     uint32_t kw[2] = {0, 0}, vw[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -99,7 +112,7 @@ extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype
                                   int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
                                   int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
                                   const int64_t* slot_mapping, float k_scale, float v_scale,
-                                  void* stream) {
+                                  const float* k_head_scales, const float* v_head_scales, void* stream) {
   using pkv::fail;
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
     return fail(PKV_ERR_INVALID, "kv_cache_write: bad sizes");
@@ -122,17 +135,22 @@ extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype
     if (!(k_scale > 0.f) || !(v_scale > 0.f)) return fail(PKV_ERR_INVALID, "kv_cache_write: scales must be > 0");
     if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 8) || !aligned(v_cache, 8))
       return fail(PKV_ERR_INVALID, "kv_cache_write: input pointers must be 16-byte, cache 8-byte aligned");
-    const float k_inv = float(1.0 / double(k_scale));
-    const float v_inv = float(1.0 / double(v_scale));
+    if ((k_head_scales || v_head_scales) && head_dim % 8 != 0)
+      return fail(PKV_ERR_INVALID, "kv_cache_write: per-head scales need head_dim a multiple of 8");
+    InvScales inv;
+    const int rc = pkv::head_inverse_scales("kv_cache_write", num_kv_heads, k_scale, v_scale, k_head_scales,
+                                            v_head_scales, inv.k, inv.v);
+    if (rc != PKV_OK) return rc;
     const int64_t chunks = row / 8;
+    const int64_t per_head = head_dim % 8 == 0 ? head_dim / 8 : INT64_MAX;
     if (in_dtype == PKV_BF16)
       hipLaunchKernelGGL(write_fp8<true>, dim3(grid_for(num_tokens * chunks)), dim3(256), 0, st, k, v,
                          static_cast<uint2*>(k_cache), static_cast<uint2*>(v_cache), slot_mapping,
-                         int64_t(num_tokens), chunks, num_slots, k_inv, v_inv);
+                         int64_t(num_tokens), chunks, num_slots, per_head, inv);
     else
       hipLaunchKernelGGL(write_fp8<false>, dim3(grid_for(num_tokens * chunks)), dim3(256), 0, st, k, v,
                          static_cast<uint2*>(k_cache), static_cast<uint2*>(v_cache), slot_mapping,
-                         int64_t(num_tokens), chunks, num_slots, k_inv, v_inv);
+                         int64_t(num_tokens), chunks, num_slots, per_head, inv);
   } else {
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: input dtype %d -> cache dtype %d not supported", in_dtype,
                 cache_dtype);

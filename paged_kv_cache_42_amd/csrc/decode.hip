@@ -109,8 +109,8 @@ struct DecodeArgs {
   int len_clamp;     // min(max_seq_len, table_width * block_size)
   int part_tokens;   // 0 = whole context in one item
   int pmax;
-  float zscale;      // softmax scale * k_scale * log2(e)
-  float v_scale;
+  float zscale_h[pkv::kHeadScales];   // per KV head: softmax scale * k_scale * log2(e)
+  float vscale_h[pkv::kHeadScales];   // per KV head: v_scale
   int group;         // query heads per KV head
   int num_seqs;
   int num_work;      // items in `work`
@@ -181,6 +181,8 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
   static_assert(NLT >= 1 && TILE % TPL == 0, "tile too small for this row width");
 
   const int g = blockIdx.x;
+  const float zscale_g = a.zscale_h[g & (pkv::kHeadScales - 1)];
+  const float vscale_g = a.vscale_h[g & (pkv::kHeadScales - 1)];
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * G;
   const int lane = threadIdx.x & 63;
@@ -297,7 +299,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float zz = pkv::group_sum<LPT>(part[h]) * a.zscale;
+        const float zz = pkv::group_sum<LPT>(part[h]) * zscale_g;
         z[i][h] = valid[i] ? zz : -INFINITY;
       }
     }
@@ -403,7 +405,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs a) {
       S += sm_l[x][h] * wx;
       A += sm_acc[x][h][e] * wx;
     }
-    const float o = S > 0.f ? A / S * a.v_scale : 0.f;
+    const float o = S > 0.f ? A / S * vscale_g : 0.f;
     const float lse2 = S > 0.f ? M + log2f(S) : -INFINITY;
     const int hq = g * G + h;
     if (single) {
@@ -582,7 +584,7 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
   in.num_blocks = a.num_blocks;
   in.tok_begin = tok_begin;
   in.tok_end = tok_end;
-  in.zscale = a.zscale;
+  in.zscale = a.zscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)];
   float m, lsum;
   f32x4_t o[MT];
   pkv::decode_wave<CDT, D, BS>(in, vt_lds[w], m, lsum, o);
@@ -590,7 +592,7 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
 
   if (hl < G) {
     const int hq = g * G + hl;
-    const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+    const float inv = lsum > 0.f ? a.vscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)] / lsum : 0.f;
     const float lse2 = lsum > 0.f ? m + log2f(lsum) : -INFINITY;
     if (nparts == 1) {
       uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(s) * Hq + hq) * D + 4 * grp;
@@ -642,6 +644,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = blockIdx.x * HPW + w;
+  const float zscale_g = a.zscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)];
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * G;
@@ -848,7 +851,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * grp + r;
-      z[r] = (ok && t < tok_end) ? sc[r] * a.zscale : -INFINITY;
+      z[r] = (ok && t < tok_end) ? sc[r] * zscale_g : -INFINITY;
     }
     float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
@@ -885,7 +888,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     if (!sl_valid[k] || hl >= G) return;
     const int s = sl_s[k];
     const int hq = g * G + hl;
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    const float inv = l > 0.f ? a.vscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)] / l : 0.f;
     const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
     if (sl_np[k] == 1) {
       const int row = sl_row[k];
@@ -1087,8 +1090,9 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
                                           const int32_t* seq_lens, int32_t table_width, int32_t num_seqs,
                                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                           int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
-                                          float scale, float k_scale, float v_scale, int32_t partition_size,
-                                          void* workspace, size_t workspace_bytes, float* lse_out,
+                                          float scale, float k_scale, float v_scale,
+                                          const float* k_head_scales, const float* v_head_scales,
+                                          int32_t partition_size, void* workspace, size_t workspace_bytes, float* lse_out,
                                           const int32_t* work_items, int32_t num_work, void* stream) {
   using pkv::fail;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
@@ -1142,8 +1146,11 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + size_t(num_seqs) * num_q_heads * pmax * head_dim;
   }
-  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
-  a.v_scale = v_scale;
+  {
+    const int rc = pkv::head_scales("attention", num_kv_heads, scale, k_scale, v_scale, k_head_scales,
+                                    v_head_scales, a.zscale_h, a.vscale_h);
+    if (rc != PKV_OK) return rc;
+  }
   a.group = G;
   a.num_seqs = num_seqs;
   const bool mfma = q_dtype == PKV_BF16;
@@ -1202,7 +1209,8 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
                                                 int32_t table_width, int32_t num_seqs, int32_t num_q_heads,
                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                                 int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale,
-                                                float v_scale, const int32_t* rows, int32_t num_rows,
+                                                float v_scale, const float* k_head_scales,
+                                                const float* v_head_scales, const int32_t* rows, int32_t num_rows,
                                                 const int32_t* cu_seqlens_q, int32_t total_q,
                                                 const int32_t* plan, int32_t num_slots,
                                                 int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
@@ -1264,8 +1272,11 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + size_t(num_rows) * num_q_heads * max_pieces * head_dim;
   }
-  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
-  a.v_scale = v_scale;
+  {
+    const int rc = pkv::head_scales("attention", num_kv_heads, scale, k_scale, v_scale, k_head_scales,
+                                    v_head_scales, a.zscale_h, a.vscale_h);
+    if (rc != PKV_OK) return rc;
+  }
   a.group = G;
   a.num_seqs = num_rows;                      // the plan's rows
   a.plan = plan;

@@ -8,6 +8,7 @@
 // (a multi-block request is all-or-nothing and fails when too few blocks are free).
 #include <algorithm>
 #include <cstdint>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -39,6 +40,53 @@ int dtype_bytes(int32_t dt) {
     case PKV_FP8_E4M3: return 1;
     default: return 0;
   }
+}
+
+namespace {
+
+bool positive_finite(double x) { return x > 0.0 && x < 1e300; }
+
+// the product of the per-tensor scale and each head's factor (1 when NULL), checked
+int head_products(const char* who, int32_t hkv, float base, const float* head, double* out) {
+  if (head && hkv > kHeadScales)
+    return fail(PKV_ERR_INVALID, "%s: per-head scales need at most %d KV heads, got %d", who, kHeadScales, hkv);
+  if (!positive_finite(base) || !std::isfinite(base)) return fail(PKV_ERR_INVALID, "%s: scales must be finite and > 0", who);
+  for (int h = 0; h < kHeadScales; ++h) {
+    const double f = head && h < hkv ? double(head[h]) : 1.0;
+    if (head && h < hkv && (!std::isfinite(head[h]) || !(head[h] > 0.f)))
+      return fail(PKV_ERR_INVALID, "%s: per-head scale %d must be finite and > 0", who, h);
+    out[h] = double(base) * f;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+int head_scales(const char* who, int32_t num_kv_heads, float scale, float k_scale, float v_scale,
+                const float* k_head, const float* v_head, float* zs, float* vs) {
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PKV_ERR_INVALID, "%s: scales must be finite and > 0", who);
+  double kp[kHeadScales], vp[kHeadScales];
+  int rc = head_products(who, num_kv_heads, k_scale, k_head, kp);
+  if (rc == PKV_OK) rc = head_products(who, num_kv_heads, v_scale, v_head, vp);
+  if (rc != PKV_OK) return rc;
+  for (int h = 0; h < kHeadScales; ++h) {
+    zs[h] = float(double(scale) * kp[h] * 1.4426950408889634);
+    vs[h] = float(vp[h]);
+  }
+  return PKV_OK;
+}
+
+int head_inverse_scales(const char* who, int32_t num_kv_heads, float k_scale, float v_scale,
+                        const float* k_head, const float* v_head, float* ki, float* vi) {
+  double kp[kHeadScales], vp[kHeadScales];
+  int rc = head_products(who, num_kv_heads, k_scale, k_head, kp);
+  if (rc == PKV_OK) rc = head_products(who, num_kv_heads, v_scale, v_head, vp);
+  if (rc != PKV_OK) return rc;
+  for (int h = 0; h < kHeadScales; ++h) {
+    ki[h] = float(1.0 / kp[h]);
+    vi[h] = float(1.0 / vp[h]);
+  }
+  return PKV_OK;
 }
 
 }  // namespace pkv

@@ -10,6 +10,21 @@ int fail(int code, const char* fmt, ...);
 // Bytes per element of a PKV_* dtype code (0 if unknown).
 int dtype_bytes(int32_t dt);
 
+// Per-KV-head scale slots carried in kernel arguments: a kernel reads the slot of its
+// KV head (h & (kHeadScales - 1)); without per-head factors every slot holds the same
+// value, so any number of heads works, with them at most kHeadScales heads.
+constexpr int kHeadScales = 16;
+
+// Attention constants per KV head: zs[h] = scale * k_scale * k_head[h] * log2(e) and
+// vs[h] = v_scale * v_head[h] (a NULL array means factors of 1), products in double.
+// Checks that every scale is finite and > 0 and that per-head factors come with at most
+// kHeadScales heads; returns PKV_OK or the error (message recorded under `who`).
+int head_scales(const char* who, int32_t num_kv_heads, float scale, float k_scale, float v_scale,
+                const float* k_head, const float* v_head, float* zs, float* vs);
+// Cache-write inverses per KV head: ki[h] = fl32(1 / (k_scale * k_head[h])), likewise vi.
+int head_inverse_scales(const char* who, int32_t num_kv_heads, float k_scale, float v_scale,
+                        const float* k_head, const float* v_head, float* ki, float* vi);
+
 }  // namespace pkv
 
 #ifdef __HIPCC__

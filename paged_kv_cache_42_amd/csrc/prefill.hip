@@ -72,8 +72,8 @@ struct ChunkArgs {
   int group;
   int num_blocks;
   int len_clamp;
-  float zscale;           // softmax scale * k_scale * log2(e)
-  float v_scale;
+  float zscale_h[pkv::kHeadScales];   // per KV head: softmax scale * k_scale * log2(e)
+  float vscale_h[pkv::kHeadScales];   // per KV head: v_scale
 };
 
 template <int D>
@@ -108,6 +108,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   const int q0 = it.z;
   const int slot = it2.y;
   if (s < 0 || s >= a.num_seqs || g < 0 || g >= a.num_kv_heads || slot >= a.num_slots) return;
+  const float zscale_g = a.zscale_h[g & (pkv::kHeadScales - 1)];
   const int row0 = a.cu_q[s];
   const int qs = a.cu_q[s + 1] - row0;
   if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q || q0 < 0 || q0 >= qs) return;
@@ -304,7 +305,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
       float mx = sc[rb][0][0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[rb][e / 4][e % 4]);
-      lm[rb] = mx * a.zscale;
+      lm[rb] = mx * zscale_g;
     }
     if (__any((lm[0] > m[0] + kLazy) | (lm[1] > m[1] + kLazy))) {
 #pragma unroll
@@ -333,10 +334,10 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t p01 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][0], a.zscale, -mref)),
-                                             pkv::fast_exp2(fmaf(sc[rb][kb][1], a.zscale, -mref)));
-        const uint32_t p23 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][2], a.zscale, -mref)),
-                                             pkv::fast_exp2(fmaf(sc[rb][kb][3], a.zscale, -mref)));
+        const uint32_t p01 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][0], zscale_g, -mref)),
+                                             pkv::fast_exp2(fmaf(sc[rb][kb][1], zscale_g, -mref)));
+        const uint32_t p23 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][2], zscale_g, -mref)),
+                                             pkv::fast_exp2(fmaf(sc[rb][kb][3], zscale_g, -mref)));
         // the sum uses the same bf16-rounded weights that enter P.V (two per dot2)
         ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), kOnes, ps, false);
         ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), kOnes, ps, false);
@@ -405,7 +406,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
     l += __shfl_xor(l, 32);
     if (!row_ok[rb]) continue;
     const int r = 32 * w + 16 * rb + hl;
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    const float inv = l > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / l : 0.f;
     if (slot >= 0) {                                       // partial of a split item
       float* prow = a.ws_o + (int64_t(slot) * kRows + r) * D + 4 * grp;
 #pragma unroll
@@ -640,6 +641,7 @@ extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int3
                                                   int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
                                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                                   int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                                  const float* k_head_scales, const float* v_head_scales,
                                                   const int32_t* work_items, int32_t num_work,
                                                   const int32_t* merges, int32_t num_merges, int32_t num_partials,
                                                   void* workspace, int64_t workspace_bytes, float* lse_out,
@@ -700,8 +702,11 @@ extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int3
   a.num_blocks = num_blocks;
   const int64_t tcap = int64_t(table_width) * block_size;
   a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
-  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
-  a.v_scale = v_scale;
+  {
+    const int rc = pkv::head_scales("attention", num_kv_heads, scale, k_scale, v_scale, k_head_scales,
+                                    v_head_scales, a.zscale_h, a.vscale_h);
+    if (rc != PKV_OK) return rc;
+  }
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(fn, dim3(num_work), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();

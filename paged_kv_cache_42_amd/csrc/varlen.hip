@@ -67,8 +67,8 @@ struct VarlenArgs {
   int group;
   int num_blocks;
   int len_clamp;
-  float zscale;
-  float v_scale;
+  float zscale_h[pkv::kHeadScales];   // per KV head: softmax scale * k_scale * log2(e)
+  float vscale_h[pkv::kHeadScales];   // per KV head: v_scale
 };
 
 template <int CDT, int D>
@@ -113,7 +113,7 @@ __device__ __forceinline__ void run_decode_item(const VarlenArgs& a, uint8_t* sm
   in.num_blocks = a.num_blocks;
   in.tok_begin = b0 * BS;
   in.tok_end = min(key_end, b1 * BS);
-  in.zscale = a.zscale;
+  in.zscale = a.zscale_h[g & (pkv::kHeadScales - 1)];
   float m, lsum;
   f32x4_t o[MT];
   pkv::decode_wave<CDT, D, BS>(in, smem + w * 16 * RS, m, lsum, o);
@@ -152,7 +152,7 @@ __device__ __forceinline__ void run_decode_item(const VarlenArgs& a, uint8_t* sm
   }
   if (w != 0 || hl >= G) return;
   const int hq = g * G + hl;
-  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+  const float inv = lsum > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / lsum : 0.f;
   uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -287,7 +287,7 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = key0 + 16 * sb + 4 * grp + r;
-        z[4 * sb + r] = (row_ok && key <= pos && key < key_end) ? sc[r] * a.zscale : -INFINITY;
+        z[4 * sb + r] = (row_ok && key <= pos && key < key_end) ? sc[r] * a.zscale_h[g & (pkv::kHeadScales - 1)] : -INFINITY;
       }
     }
     float mt_ = z[0];
@@ -350,7 +350,7 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
   if (!row_ok) return;
   const int row = row0 + q0 + tok;
   const int hq = g * G + r_row % G;
-  const float inv = l > 0.f ? a.v_scale / l : 0.f;
+  const float inv = l > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / l : 0.f;
   uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -456,6 +456,7 @@ extern "C" int pkv_paged_attention_prefill_varlen(void* out, const void* q, int3
                                                   int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
                                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                                   int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                                  const float* k_head_scales, const float* v_head_scales,
                                                   const int32_t* work_items, int32_t num_work, float* lse_out,
                                                   void* stream) {
   using pkv::fail;
@@ -501,8 +502,11 @@ extern "C" int pkv_paged_attention_prefill_varlen(void* out, const void* q, int3
   a.num_blocks = num_blocks;
   const int64_t tcap = int64_t(table_width) * block_size;
   a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
-  a.zscale = float(double(scale) * double(k_scale) * 1.4426950408889634);
-  a.v_scale = v_scale;
+  {
+    const int rc = pkv::head_scales("attention", num_kv_heads, scale, k_scale, v_scale, k_head_scales,
+                                    v_head_scales, a.zscale_h, a.vscale_h);
+    if (rc != PKV_OK) return rc;
+  }
   hipLaunchKernelGGL(fn, dim3(num_work), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_varlen: launch failed: %s", hipGetErrorString(e));

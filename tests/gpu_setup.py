@@ -17,6 +17,7 @@ import workloads.gpu as wgen
 from oracle import allocator as oa
 from oracle import attention as oatt
 from oracle import cache as ocache
+from oracle import fp8 as ofp8
 from oracle.metadata import build_block_table as oracle_build
 
 DUMMY = 1 << 40
@@ -127,14 +128,26 @@ def build_step(w: workloads.Workload, width: Optional[int] = None, fill_nan: boo
         on += L - p
     if n_ctx:
         pkv.kv_cache_write(ctx_k, ctx_v, k_cache, v_cache, torch.from_numpy(ctx_slots).cuda(), w.block_size,
-                           w.k_scale, w.v_scale)
+                           w.k_scale, w.v_scale, **heads(w))
     if n_new:
         pkv.kv_cache_write(new_k, new_v, k_cache, v_cache, torch.from_numpy(slots).cuda(), w.block_size,
-                           w.k_scale, w.v_scale)
+                           w.k_scale, w.v_scale, **heads(w))
     del ctx_k, ctx_v
     return Step(w, pool, W, bt, cu, slots, k_cache, v_cache, q,
                 torch.from_numpy(bt).cuda(), torch.from_numpy(w.seq_lens.astype(np.int32)).cuda(),
                 torch.from_numpy(cu).cuda(), ctx_slots, (new_k, new_v))
+
+
+def heads(w: workloads.Workload) -> dict:
+    """The per-head scale factors as keyword arguments of the libpkv calls."""
+    return {"k_head_scales": w.k_head_scales, "v_head_scales": w.v_head_scales}
+
+
+def oracle_scales(w: workloads.Workload):
+    """(K, V) scales for the oracle: per tensor, or per head (the product of the two)."""
+    ks = w.k_scale if w.k_head_scales is None else ofp8.head_scales(w.k_scale, w.k_head_scales)
+    vs = w.v_scale if w.v_head_scales is None else ofp8.head_scales(w.v_scale, w.v_head_scales)
+    return ks, vs
 
 
 def oracle_planes(st: Step):
@@ -156,18 +169,19 @@ def oracle_planes(st: Step):
     ctx_v = np.concatenate([v[: prior[s]] for s, v in enumerate(vs)])
     new_k = np.concatenate([k[prior[s]:] for s, k in enumerate(ks)])
     new_v = np.concatenate([v[prior[s]:] for s, v in enumerate(vs)])
-    ocache.write(kp, ctx_k, w.dtype, w.cache_dtype, ctx_slots, w.k_scale)
-    ocache.write(vp, ctx_v, w.dtype, w.cache_dtype, ctx_slots, w.v_scale)
-    ocache.write(kp, new_k, w.dtype, w.cache_dtype, slots, w.k_scale)
-    ocache.write(vp, new_v, w.dtype, w.cache_dtype, slots, w.v_scale)
+    ks, vs = oracle_scales(w)
+    ocache.write(kp, ctx_k, w.dtype, w.cache_dtype, ctx_slots, ks)
+    ocache.write(vp, ctx_v, w.dtype, w.cache_dtype, ctx_slots, vs)
+    ocache.write(kp, new_k, w.dtype, w.cache_dtype, slots, ks)
+    ocache.write(vp, new_v, w.dtype, w.cache_dtype, slots, vs)
     return tabs, bt, cu, slots, kp, vp
 
 
 def oracle_attention_full(st: Step, kp, vp, bt, cu):
     w = st.w
     q = workloads.storage_to_f64(w.q_all(), w.dtype)
-    return oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, w.seq_lens, cu, w.softmax_scale, w.group,
-                                w.k_scale, w.v_scale)
+    ks, vs = oracle_scales(w)
+    return oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, w.seq_lens, cu, w.softmax_scale, w.group, ks, vs)
 
 
 def oracle_decode_sampled(w: workloads.Workload, pairs):
@@ -198,7 +212,8 @@ def run_decode(st: Step, partition_size: Optional[int] = None, lse: bool = True,
     lse_t = torch.empty((B, Hq), dtype=torch.float32, device="cuda") if lse else None
     work = torch.from_numpy(pkv.build_decode_work(w.seq_lens, P)).cuda() if use_work else None
     pkv.paged_attention_decode(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, w.num_kv_heads,
-                               w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, P, ws, lse_t, work=work)
+                               w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, P, ws, lse_t, work=work,
+                               **heads(w))
     torch.cuda.synchronize()
     return out, lse_t
 
@@ -221,7 +236,7 @@ def run_decode_split(st: Step, num_slots: Optional[int] = None, min_piece_tokens
     lse_t = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
     pkv.paged_attention_decode_split(out, st.q if q is None else q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, plan_d, split,
                                      w.num_kv_heads, w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale,
-                                     ws, lse_t)
+                                     ws, lse_t, **heads(w))
     torch.cuda.synchronize()
     return out, lse_t, split
 
@@ -248,7 +263,7 @@ def run_varlen(st: Step, lse: bool = True, max_seq_len=None):
     work = torch.from_numpy(pkv.build_varlen_work(w.q_lens, w.seq_lens, w.num_kv_heads, w.group)).cuda()
     pkv.paged_attention_prefill_varlen(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d, work,
                                        w.num_kv_heads, w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale,
-                                       lse=lse_t)
+                                       lse=lse_t, **heads(w))
     torch.cuda.synchronize()
     return out, lse_t
 
@@ -276,12 +291,13 @@ def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_to
         pkv.paged_attention_decode_split(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d,
                                          torch.from_numpy(mp.split.plan).cuda(), mp.split, w.num_kv_heads,
                                          w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, ws, lse_t,
-                                         rows=torch.from_numpy(mp.decode_rows).cuda(), cu_seqlens_q=st.cu_d)
+                                         rows=torch.from_numpy(mp.decode_rows).cuda(), cu_seqlens_q=st.cu_d,
+                                         **heads(w))
     dev = mp.chunks.to_device(d)
     if dev is not None:
         work, merges, cws = dev
         pkv.paged_attention_prefill_chunks(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d, work,
                                            merges, mp.chunks.num_partials, cws, w.num_kv_heads, w.block_size, msl,
-                                           w.softmax_scale, w.k_scale, w.v_scale, lse=lse_t)
+                                           w.softmax_scale, w.k_scale, w.v_scale, lse=lse_t, **heads(w))
     torch.cuda.synchronize()
     return out, lse_t

@@ -13,6 +13,14 @@ from gpu_setup import build_step, oracle_planes, plane_bits, to_device
 pytestmark = pytest.mark.gpu
 
 
+def _per_head(w):
+    """Distinct per-KV-head factors of the E4M3 scales (exact binary fractions and not)."""
+    h = w.num_kv_heads
+    w.k_head_scales = np.array([0.25, 3.0, 1.0, 0.7, 5.5, 0.125, 1.3, 2.0][:h], np.float32)
+    w.v_head_scales = np.array([2.0, 0.3, 0.5, 4.0, 1.0, 0.9, 8.0, 0.0625][:h], np.float32)
+    return w
+
+
 @pytest.mark.parametrize("make", [
     lambda: workloads.config1(),
     lambda: workloads.small_decode(21, [1, 16, 17, 33, 100], num_q_heads=8, num_kv_heads=2, head_dim=128,
@@ -21,7 +29,11 @@ pytestmark = pytest.mark.gpu
                                    block_size=32, dtype="bf16", cache_dtype="fp8"),
     lambda: workloads.small_decode(23, [5, 70], num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
                                    dtype="f32", cache_dtype="fp8"),
-], ids=["cfg1_f32", "bf16_d128", "bf16_to_fp8_bs32", "f32_to_fp8"])
+    lambda: _per_head(workloads.small_varlen(24, [40, 64, 7], [40, 10, 1], num_q_heads=16, num_kv_heads=8,
+                                             head_dim=64, block_size=16, dtype="bf16", cache_dtype="fp8")),
+    lambda: _per_head(workloads.small_decode(25, [5, 70], num_q_heads=4, num_kv_heads=2, head_dim=128,
+                                             block_size=32, dtype="f32", cache_dtype="fp8")),
+], ids=["cfg1_f32", "bf16_d128", "bf16_to_fp8_bs32", "f32_to_fp8", "bf16_to_fp8_per_head", "f32_to_fp8_per_head"])
 def test_cache_bytes_and_tables_bit_exact(make):
     w = make()
     if w.cache_dtype == "fp8":

@@ -225,6 +225,9 @@ class Workload:
     scale: Optional[float] = None  # softmax scale; None = 1/sqrt(head_dim)
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # per-KV-head factors of the E4M3 scales (float32 [num_kv_heads]) or None
+    k_head_scales: Optional[np.ndarray] = None
+    v_head_scales: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
