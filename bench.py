@@ -51,6 +51,8 @@ def parse_args():
                          "cache write and mixed attention per step, bf16 and E4M3 caches)")
     ap.add_argument("--replay-steps", type=int, default=None, help="replay only the first N scheduler steps")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy measurement (1 GiB each way)")
+    ap.add_argument("--replays", default=None,
+                    help="comma-separated names of the trace replays to run (default: all of them)")
     ap.add_argument("--replay-budget-sweep", action="store_true",
                     help="also replay the bf16 trace under several token budgets / chunk sizes (chunked prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
@@ -362,7 +364,7 @@ def replay_budget_sweep(max_steps):
     return out
 
 
-def sched_replay(max_steps):
+def sched_replay(max_steps, only=None):
     """Continuous-batching trace replay (the 2000-request trace): per step the host
     scheduler admits/plans/updates and 16 layers run the cache write and the mixed
     attention launch; per-step attention time from HIP events (inputs generated on the
@@ -386,6 +388,11 @@ def sched_replay(max_steps):
             # shared system prompts (16 groups), with and without the prefix cache
             ("bf16_prefix_cache", workloads.config5_prefix("bf16"), {}),
             ("bf16_prefix_trace_no_cache", workloads.config5_prefix("bf16"), {"prefix_cache": False})]
+    if only:
+        unknown = set(only) - {r[0] for r in runs}
+        if unknown:
+            raise SystemExit(f"unknown replay names: {sorted(unknown)}")
+        runs = [r for r in runs if r[0] in only]
     for name, tr, kw in runs:
         print(f"[bench] replay {name}: {tr.name} {kw}", file=sys.stderr, flush=True)
         args = dict(kw)
@@ -667,7 +674,7 @@ def main():
         print("[bench] swap copies", file=sys.stderr, flush=True)
         res["swap_copy"] = swap_bench()
     if not args.no_replay:
-        res["sched_replay"] = sched_replay(args.replay_steps)
+        res["sched_replay"] = sched_replay(args.replay_steps, args.replays.split(",") if args.replays else None)
     if args.replay_budget_sweep:
         res["replay_budget_sweep"] = replay_budget_sweep(args.replay_steps)
     if not args.no_cpu_baseline:
