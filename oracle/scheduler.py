@@ -61,7 +61,11 @@ Readings taken where the page leaves a step open (each listed with the others):
     the priority classes of the serving project's extensions): given a class per
     request (0 most important), the waiting queue is kept in (class, arrival step, id)
     order, preempted requests included (they take their place by that key rather than
-    the front); admission still stops at the first head that does not fit.
+    the front); admission still stops at the first head that does not fit;
+  * static batching (the baseline of "1. What is it?" and "2. Why does it exist?": a batch
+    is decided, run to completion, then the next one is decided): admission happens
+    only at steps that start with nothing running; finished requests still free their
+    blocks at once, but their slots stay empty until the whole batch is done.
 
 Parity unpinned beyond invariants and hand-worked traces: the pages print no trace of
 this loop, so the tests pin it with small traces worked out by hand from the page's
@@ -121,7 +125,7 @@ class Scheduler:
                  max_running: int, admission_check: bool = True,
                  prompt_tokens: Optional[Sequence[Sequence[int]]] = None, max_batched_tokens: int = 0,
                  chunk_tokens: int = 0, swap_blocks: int = 0, victim: str = "self",
-                 priority: Optional[Sequence[int]] = None):
+                 priority: Optional[Sequence[int]] = None, static: bool = False):
         self.reqs = [Req(i, int(a), int(p), int(m)) for i, (a, p, m) in enumerate(zip(arrival, prompt, max_tokens))]
         # prompt_tokens given: prefix caching over shared blocks (oracle/prefix.py)
         self.pcache = None
@@ -162,6 +166,7 @@ class Scheduler:
         if victim not in ("self", "lifo", "fewest"):
             raise ValueError(f"unknown victim policy {victim!r}")
         self.victim = victim
+        self.static = bool(static)                # admit only when the batch has drained
         self.by_priority = priority is not None
         if priority is not None:
             if len(priority) != len(self.reqs) or min(priority, default=0) < 0:
@@ -197,7 +202,8 @@ class Scheduler:
             self._enqueue(r, front=False)
             self.next_arrival += 1
         swap_in = []
-        while self.waiting and len(self.running) < self.max_running:
+        admit = not (self.static and self.running)
+        while admit and self.waiting and len(self.running) < self.max_running:
             r = self.waiting[0]
             ctx = r.prompt + r.n_out
             if r.host is not None:                                  # swapped out: copy back
