@@ -373,6 +373,8 @@ def sched_replay(max_steps, only=None):
     from workloads import replay
     out = {}
     runs = [("bf16", workloads.config5("bf16"), {}), ("fp8", workloads.config5("fp8"), {}),
+            # the static-batching baseline continuous batching is measured against
+            ("bf16_static_batching", workloads.config5("bf16"), {"static_batching": True}),
             # chunked prefill: at most 2048 new tokens per step, prefills in chunks of 512
             ("bf16_chunked_2048_512", workloads.config5("bf16"),
              {"token_budget": 2048, "chunk_tokens": 512, "chunk_cut": True}),

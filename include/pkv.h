@@ -460,6 +460,12 @@ int pkv_sched_enable_swap(pkv_sched* sched, int32_t host_blocks);
  * that key instead of the front), and admission still stops at the first head that does
  * not fit. INVALID: unknown ids, negative classes, calls after the first step. */
 enum { PKV_VICTIM_SELF = 0, PKV_VICTIM_LIFO = 1, PKV_VICTIM_FEWEST = 2 };
+/* Static batching (enabled != 0, before the first step), the baseline continuous
+ * batching is measured against ([CB] "1. What is it?", "2. Why does it exist?": a batch
+ * is decided and run to completion): pkv_sched_schedule admits only when nothing is
+ * running, so finished requests leave their slots empty (their blocks are still freed at
+ * once) and arrivals wait for the whole batch. Everything else is unchanged. */
+int pkv_sched_set_static_batching(pkv_sched* sched, int32_t enabled);
 int pkv_sched_set_victim_policy(pkv_sched* sched, int32_t policy);
 int pkv_sched_set_priorities(pkv_sched* sched, int32_t n, const int64_t* ids, const int32_t* classes);
 /* The copies of preemption by swap ([CB] "5. Technical explanation", Preemption: SWAP):

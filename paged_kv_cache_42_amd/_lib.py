@@ -81,6 +81,7 @@ _SIGS = {
     "pkv_sched_set_token_budget": (C.c_int, [vp, i32, i32]),
     "pkv_sched_enable_swap": (C.c_int, [vp, i32]),
     "pkv_sched_set_victim_policy": (C.c_int, [vp, i32]),
+    "pkv_sched_set_static_batching": (C.c_int, [vp, i32]),
     "pkv_sched_set_priorities": (C.c_int, [vp, i32, vp, vp]),
     "pkv_sched_swap_pairs": (C.c_int, [vp, P_i32, P_i32, vp, vp]),
     "pkv_sched_swap_counters": (C.c_int, [vp, vp]),
@@ -172,6 +173,10 @@ class Scheduler:
         if policy not in self.VICTIMS:
             raise ValueError(f"unknown victim policy {policy!r}")
         check(lib().pkv_sched_set_victim_policy(self._h, self.VICTIMS[policy]))
+
+    def set_static_batching(self, enabled: bool = True) -> None:
+        """Admit only when nothing runs (static batching, the baseline); before the first step."""
+        check(lib().pkv_sched_set_static_batching(self._h, int(bool(enabled))))
 
     def set_priorities(self, ids, classes) -> None:
         """Priority classes (0 most important) of the given request ids (before the first step)."""

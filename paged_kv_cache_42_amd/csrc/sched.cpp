@@ -33,6 +33,9 @@
 // or the one with the fewest outputs (earliest admitted on ties), among the least
 // important priority class present, the request itself included. With priority classes
 // the waiting queue is ordered by (class, arrival, id), preempted requests included.
+//
+// Static batching (the baseline of "1. What is it?": decide a batch, run it to
+// completion): admission only at a step that starts with nothing running.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
@@ -114,6 +117,7 @@ struct pkv_sched {
   int64_t swapped_out = 0, blocks_out = 0, blocks_in = 0;
   int32_t victim = PKV_VICTIM_SELF;
   bool by_priority = false;
+  bool static_batching = false;
 
   // waiting queue insertion: the back (arrivals) or front (preempted), or by
   // (class, arrival, id) with priority classes
@@ -275,7 +279,8 @@ int pkv_sched_schedule(pkv_sched* s, int32_t* num_rows, int32_t* total_q, int32_
   // strict first-come-first-served admission
   std::vector<int32_t> pages;
   s->swap_in.clear();
-  while (!s->waiting.empty() && int32_t(s->running.size()) < s->max_running) {
+  const bool admit = !(s->static_batching && !s->running.empty());
+  while (admit && !s->waiting.empty() && int32_t(s->running.size()) < s->max_running) {
     const int32_t head = s->waiting.front();
     Req& r = s->reqs[head];
     const int64_t ctx = int64_t(r.prompt) + r.n_out;
@@ -485,6 +490,14 @@ int pkv_sched_set_token_budget(pkv_sched* s, int32_t max_batched_tokens, int32_t
     return fail(PKV_ERR_INVALID, "sched_set_token_budget: call before the first step");
   s->max_batched_tokens = max_batched_tokens;
   s->chunk_tokens = chunk_tokens;
+  return PKV_OK;
+}
+
+int pkv_sched_set_static_batching(pkv_sched* s, int32_t enabled) {
+  if (!s) return fail(PKV_ERR_INVALID, "sched_set_static_batching: scheduler is NULL");
+  if (s->step > 0 || s->scheduled)
+    return fail(PKV_ERR_INVALID, "sched_set_static_batching: call before the first step");
+  s->static_batching = enabled != 0;
   return PKV_OK;
 }
 

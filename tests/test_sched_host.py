@@ -9,7 +9,7 @@ import workloads
 from oracle import scheduler as osch
 
 
-def _pair(tr, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None):
+def _pair(tr, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None, static=False):
     pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
                     free_order=tr.free_order)
     ours = pkv.Scheduler(pool, tr.max_running)
@@ -26,9 +26,11 @@ def _pair(tr, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None)
         ours.set_victim_policy(victim)
     if prio is not None:
         ours.set_priorities(np.arange(tr.num_requests), prio)
+    if static:
+        ours.set_static_batching(True)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
                          tr.max_running, prompt_tokens=toks, max_batched_tokens=budget, chunk_tokens=chunk,
-                         swap_blocks=swap, victim=victim, priority=prio)
+                         swap_blocks=swap, victim=victim, priority=prio, static=static)
     return pool, ours, ref
 
 
@@ -39,8 +41,8 @@ def _counters(ours, swap):
     return c
 
 
-def _replay_both(tr, width, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None):
-    pool, ours, ref = _pair(tr, prefix, budget, chunk, swap, victim, prio)
+def _replay_both(tr, width, prefix=False, budget=0, chunk=0, swap=0, victim="self", prio=None, static=False):
+    pool, ours, ref = _pair(tr, prefix, budget, chunk, swap, victim, prio, static)
     steps = 0
     for rp, rafter in osch.run(ref, width):
         n, q, mb = ours.schedule()
@@ -293,3 +295,17 @@ def test_policy_api_errors():
         s.set_victim_policy("fewest")                      # after the first step
     with pytest.raises(pkv.PkvError):
         s.set_priorities([1], [0])
+
+
+def test_static_batching_config5_bit_exact():
+    tr = workloads.config5()
+    steps, ref = _replay_both(tr, 512, static=True)
+    assert ref.finished == 2000
+
+
+@settings(max_examples=30, deadline=None)
+@given(st.integers(0, 10_000), st.integers(18, 60), st.integers(1, 8), st.booleans(), st.booleans())
+def test_static_batching_random_small_traces_bit_exact(seed, pool, max_running, swap, prefix):
+    tr = workloads.small_trace(seed, 30, pool, block_size=4, max_running=max_running, prompt_max=24 if prefix else 40,
+                               out_max=16 if prefix else 30, rate=2.0, groups=3 if prefix else 0)
+    _replay_both(tr, 20, prefix=prefix, swap=16 if swap else 0, static=True)

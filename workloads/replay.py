@@ -41,7 +41,8 @@ class StepRecord:
 class Replay:
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
                  prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0,
-                 swap_overlap: bool = False, victim: str = "self", priority=None, classes=None):
+                 swap_overlap: bool = False, victim: str = "self", priority=None, classes=None,
+                 static_batching: bool = False):
         import torch
         self.torch = torch
         self.tr = tr
@@ -70,6 +71,8 @@ class Replay:
         self.n_out = np.zeros(tr.num_requests, np.int64)        # outputs per request so far
         if victim != "self":
             self.sched.set_victim_policy(victim)
+        if static_batching:                                    # the static-batching baseline
+            self.sched.set_static_batching(True)
         self.priority = None if priority is None else np.asarray(priority, np.int32)
         if self.priority is not None:                          # priority admission
             self.sched.set_priorities(np.arange(tr.num_requests), self.priority)
