@@ -20,6 +20,12 @@ launch stream around the decode call. A second run of the same steps has the lib
 record an event between the partition pass and the merge; `roofline` reports that
 partition pass alone against the 8 TB/s HBM peak. `cpu_baseline` times the CPU oracle
 on a bounded prefix of the same batch.
+
+Sub-measurements in the same line: `mixed_step` (48 decode rows + 4 prefill chunks of
+512), `swap_copy` (1 GiB of K/V to pinned host memory and back) and `sched_replay` (the
+2000-request continuous-batching trace, 16 layers, with bf16 and E4M3 caches by default;
+`--replays all` adds static batching, chunked prefill, swap, victim policies, priority
+classes and prefix caching), each switchable off.
 """
 from __future__ import annotations
 
@@ -51,8 +57,10 @@ def parse_args():
                          "cache write and mixed attention per step, bf16 and E4M3 caches)")
     ap.add_argument("--replay-steps", type=int, default=None, help="replay only the first N scheduler steps")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy measurement (1 GiB each way)")
-    ap.add_argument("--replays", default=None,
-                    help="comma-separated names of the trace replays to run (default: all of them)")
+    ap.add_argument("--replays", default="bf16,fp8",
+                    help="comma-separated names of the trace replays to run (default: the trace with bf16 and "
+                         "E4M3 caches; 'all' for every variant: static batching, chunked prefill, swap, victim "
+                         "policies, priorities, prefix caching)")
     ap.add_argument("--replay-budget-sweep", action="store_true",
                     help="also replay the bf16 trace under several token budgets / chunk sizes (chunked prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
@@ -676,7 +684,8 @@ def main():
         print("[bench] swap copies", file=sys.stderr, flush=True)
         res["swap_copy"] = swap_bench()
     if not args.no_replay:
-        res["sched_replay"] = sched_replay(args.replay_steps, args.replays.split(",") if args.replays else None)
+        res["sched_replay"] = sched_replay(args.replay_steps,
+                                           None if args.replays == "all" else args.replays.split(","))
     if args.replay_budget_sweep:
         res["replay_budget_sweep"] = replay_budget_sweep(args.replay_steps)
     if not args.no_cpu_baseline:
