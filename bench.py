@@ -509,6 +509,54 @@ def setup_device(w, partition):
                 split=split, plan=torch.from_numpy(split.plan).cuda())
 
 
+def scheduler_host():
+    """libpkv's scheduler step on the host over the whole 2000-request trace (schedule,
+    plan with block tables / cu_seqlens / slot mapping, update), driven through the
+    Python binding: microseconds per step, no GPU work."""
+    import numpy as np
+    import paged_kv_cache_42_amd as pkv
+    import workloads
+    tr = workloads.config5("bf16")
+    pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
+                    free_order=tr.free_order)
+    sched = pkv.Scheduler(pool, tr.max_running)
+    sched.add_requests(np.arange(tr.num_requests), tr.arrival, tr.prompt, tr.max_tokens)
+    width = -(-int((tr.prompt + tr.max_tokens - 1).max()) // tr.block_size)
+    steps = rows = 0
+    t0 = time.perf_counter()
+    while sched.counters()["finished"] < tr.num_requests:
+        n, q, _ = sched.schedule()
+        if n:
+            sched.plan(n, q, width)
+        sched.update()
+        steps += 1
+        rows += n
+    dt = time.perf_counter() - t0
+    return {"steps": steps, "avg_rows": round(rows / steps, 1), "us_per_step": round(dt / steps * 1e6, 1),
+            "note": "C++ step through the ctypes binding (plan arrays allocated per step)"}
+
+
+def scheduler_oracle(budget_s: float):
+    """The scheduler oracle (plain Python) on the same trace, for at most budget_s seconds."""
+    import workloads
+    from oracle import scheduler as osch
+    tr = workloads.config5("bf16")
+    ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
+                         tr.max_running)
+    width = -(-int((tr.prompt + tr.max_tokens - 1).max()) // tr.block_size)
+    steps = rows = 0
+    t0 = time.perf_counter()
+    for plan, _ in osch.run(ref, width):
+        steps += 1
+        rows += len(plan.ids)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / steps * 1e6, 1), "unit": "us per scheduler step", "cores": 1, "kind": "oracle",
+            "sample": f"first {steps} steps of the 2000-request trace ({rows / steps:.1f} rows per step on "
+                      f"average), pure Python, one thread, {dt:.1f} s"}
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (float64 NumPy, as it stands) on a prefix of the batch, sequence by
     sequence, until `budget_s` seconds of oracle time; inputs prepared untimed."""
@@ -688,9 +736,13 @@ def main():
                                            None if args.replays == "all" else args.replays.split(","))
     if args.replay_budget_sweep:
         res["replay_budget_sweep"] = replay_budget_sweep(args.replay_steps)
+    if not args.no_replay:
+        res["scheduler_host"] = scheduler_host()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if not args.no_replay:
+            res["cpu_baseline"]["scheduler"] = scheduler_oracle(args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
