@@ -611,7 +611,7 @@ def cpu_baseline(w, budget_s: float):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     if args.probe_copy_mib:
