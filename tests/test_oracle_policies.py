@@ -136,5 +136,5 @@ def test_tag_simulation_with_policies(seed, pool, max_running, victim, swap_bloc
 @pytest.mark.parametrize("victim", ["lifo", "fewest"])
 def test_config5_trace_with_victim_policy(victim):
     tr = workloads.config5()
-    s, pre = _simulate(tr, victim=victim)
+    s, pre = _simulate(tr, victim=victim, check_every=16)
     assert s.preemptions > 0 and s.finished == 2000
