@@ -101,11 +101,12 @@ def test_prefix_trace_replay_sampled_parity():
     assert checked >= 12
 
 
-def test_chunked_prefill_replay_sampled_parity():
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+def test_chunked_prefill_replay_sampled_parity(cache_dtype):
     # token budget 2048, chunks of 512: long prompts are computed over several steps; a
     # later chunk attends over the K/V its request's earlier chunks wrote in earlier steps
     from oracle import scheduler as osch
-    tr = workloads.config5("bf16")
+    tr = workloads.config5(cache_dtype)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
                          tr.max_running, max_batched_tokens=2048, chunk_tokens=512)
     chunk_steps = []

@@ -127,13 +127,13 @@ def test_full_trace_geometry_one_gib_each_way_sampled():
     assert not k[:, torch.from_numpy(untouched).long().cuda()].view(torch.int16).any()
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_replay_with_swap_sampled_parity(overlap):
+@pytest.mark.parametrize("overlap,cache_dtype", [(False, "bf16"), (True, "bf16"), (True, "fp8")])
+def test_replay_with_swap_sampled_parity(overlap, cache_dtype):
     # the trace replay with a host space of 4096 blocks: preempted requests are swapped out
     # and come back without a prefill; their decode rows after the swap-in must attend to
     # the K/V they had
     from test_gpu_sched_replay import _check_step
-    tr = workloads.config5("bf16")
+    tr = workloads.config5(cache_dtype)
     ref = osch.Scheduler(tr.arrival, tr.prompt, tr.max_tokens, tr.num_blocks, tr.free_order, tr.block_size,
                          tr.max_running, swap_blocks=4096)
     back = {}
