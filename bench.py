@@ -354,7 +354,9 @@ def swap_bench(reps: int = 5):
     return res
 
 
-BUDGET_SWEEP = ((1024, 512), (2048, 512), (4096, 1024), (8192, 2048))
+# the budgets of the continuous-batching page's tuning exercise (the budget alone bounds
+# the chunks), then budget / chunk pairs with a 512-token chunk cap
+BUDGET_SWEEP = ((512, 0), (2048, 0), (8192, 0), (32768, 0), (1024, 512), (2048, 512), (4096, 1024))
 
 
 def replay_budget_sweep(max_steps):

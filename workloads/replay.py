@@ -298,7 +298,7 @@ def run(tr: workloads.Trace, max_steps: Optional[int] = None, keep=None, progres
     dec = np.array([r.rows - r.prefill_rows for r in recs], np.int64)
     tbt = np.repeat(t, dec)
 
-    def pct(x, qs=(50, 99)):
+    def pct(x, qs=(50, 95, 99)):
         return {f"p{q}": round(float(np.percentile(x, q)) * 1e3, 3) for q in qs} if len(x) else {}
 
     summary = {
