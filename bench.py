@@ -61,6 +61,8 @@ def parse_args():
                     help="comma-separated names of the trace replays to run (default: the trace with bf16 and "
                          "E4M3 caches; 'all' for every variant: static batching, chunked prefill, swap, victim "
                          "policies, priorities, prefix caching)")
+    ap.add_argument("--replay-batching-sweep", action="store_true",
+                    help="also replay continuous vs static batching for three output-length distributions")
     ap.add_argument("--replay-budget-sweep", action="store_true",
                     help="also replay the bf16 trace under several token budgets / chunk sizes (chunked prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
@@ -356,6 +358,29 @@ def swap_bench(reps: int = 5):
 
 # the budgets of the continuous-batching page's tuning exercise (the budget alone bounds
 # the chunks), then budget / chunk pairs with a 512-token chunk cap
+def replay_batching_sweep(max_steps):
+    """Continuous vs static batching on the trace with three output-length distributions
+    (constant, geometric, lognormal with a long tail): the gain's dependence on the
+    spread of output lengths."""
+    import workloads
+    from workloads import replay
+    out = {}
+    for kind in ("constant", "geometric", "lognormal"):
+        res = {}
+        for mode in ("continuous", "static"):
+            print(f"[bench] batching sweep {kind} {mode}", file=sys.stderr, flush=True)
+            _, summ = replay.run(workloads.config5_outputs(kind), max_steps=max_steps,
+                                 static_batching=mode == "static")
+            res[mode] = {k: summ[k] for k in ("steps", "attention_s_total", "requests_per_s", "avg_running_batch",
+                                              "ttft_ms", "tbt_ms", "preemptions")}
+        c, st = res["continuous"], res["static"]
+        res["gain_requests_per_s"] = round(c["requests_per_s"] / st["requests_per_s"], 2)
+        res["batch_ratio"] = round(c["avg_running_batch"] / st["avg_running_batch"], 2)
+        res["ttft_p50_ratio"] = round(st["ttft_ms"]["p50"] / c["ttft_ms"]["p50"], 2)
+        out[kind] = res
+    return out
+
+
 BUDGET_SWEEP = ((512, 0), (2048, 0), (8192, 0), (32768, 0), (1024, 512), (2048, 512), (4096, 1024))
 
 
@@ -738,6 +763,8 @@ def main():
                                            None if args.replays == "all" else args.replays.split(","))
     if args.replay_budget_sweep:
         res["replay_budget_sweep"] = replay_budget_sweep(args.replay_steps)
+    if args.replay_batching_sweep:
+        res["replay_batching_sweep"] = replay_batching_sweep(args.replay_steps)
     if not args.no_replay:
         res["scheduler_host"] = scheduler_host()
     if not args.no_cpu_baseline:

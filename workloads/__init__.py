@@ -48,6 +48,7 @@ _STREAM_SHARED = 35         #   lengths of the groups' shared prompts
 _STREAM_UNIQUE = 36         #   lengths of the requests' own prompt parts
 _STREAM_TOKENS = 37         #   token ids
 _STREAM_PRIORITY = 38       # priority class of each request
+_STREAM_OUT_LOGN = 39       # lognormal output lengths (output-length variants)
 GROUP_OWNER = 1 << 23       # value/token streams of group g are owned by GROUP_OWNER + g
 
 
@@ -522,6 +523,24 @@ def config5(cache_dtype: str = "bf16") -> Trace:
     max_tokens = np.minimum(rng_for(seed, _STREAM_OUTPUTS).geometric(1.0 / 256.0, size=n), 4096).astype(np.int32)
     return Trace(f"cfg5_trace_{cache_dtype}", seed, arrival, prompt, max_tokens, 4096, _permutation(seed, 4096),
                  cache_dtype=cache_dtype)
+
+
+def config5_outputs(kind: str, cache_dtype: str = "bf16") -> Trace:
+    """Config 5 with another output-length distribution (same arrivals, prompts, pool):
+    "constant" (every request 256 outputs), "geometric" (config 5: Geometric(1/256)),
+    "lognormal" (median 128, sigma 1.5, capped at 4096: a long tail)."""
+    base = config5(cache_dtype)
+    n = base.num_requests
+    if kind == "geometric":
+        return base
+    if kind == "constant":
+        out = np.full(n, 256, np.int32)
+    elif kind == "lognormal":
+        out = np.clip(np.rint(rng_for(base.seed, _STREAM_OUT_LOGN).lognormal(np.log(128.0), 1.5, size=n)),
+                      1, 4096).astype(np.int32)
+    else:
+        raise ValueError(kind)
+    return dataclasses.replace(base, name=f"cfg5_{kind}_outputs_{cache_dtype}", max_tokens=out)
 
 
 def config5_prefix(cache_dtype: str = "bf16") -> Trace:
