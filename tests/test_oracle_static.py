@@ -65,3 +65,4 @@ def test_config5_static_runs_longer_with_a_smaller_batch():
     rows_s = [len(p.ids) for p, _ in osch.run(stat, 512)]
     assert stat.finished == cont.finished == 2000
     assert len(rows_s) > len(rows_c) and np.mean(rows_s) < np.mean(rows_c)
+

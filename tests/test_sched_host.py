@@ -309,3 +309,27 @@ def test_static_batching_random_small_traces_bit_exact(seed, pool, max_running, 
     tr = workloads.small_trace(seed, 30, pool, block_size=4, max_running=max_running, prompt_max=24 if prefix else 40,
                                out_max=16 if prefix else 30, rate=2.0, groups=3 if prefix else 0)
     _replay_both(tr, 20, prefix=prefix, swap=16 if swap else 0, static=True)
+
+
+def test_static_batching_gain_grows_with_the_spread_of_output_lengths():
+    # the same arrivals and prompts with constant, geometric and long-tailed outputs (the
+    # static loop is bit-exact against its oracle above): static batching needs about as
+    # many steps as the continuous loop when every request finishes together, and ever
+    # more as the tail of the output lengths grows
+    ratios = {}
+    for kind in ("constant", "geometric", "lognormal"):
+        tr = workloads.config5_outputs(kind)
+        assert (tr.arrival == workloads.config5().arrival).all() and (tr.prompt == workloads.config5().prompt).all()
+        steps = []
+        for static in (False, True):
+            pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
+                            free_order=tr.free_order)
+            s = pkv.Scheduler(pool, tr.max_running)
+            s.add_requests(np.arange(tr.num_requests), tr.arrival, tr.prompt, tr.max_tokens)
+            s.set_static_batching(static)
+            while s.counters()["finished"] < tr.num_requests:
+                s.schedule()
+                s.update()
+            steps.append(s.counters()["step"])
+        ratios[kind] = steps[1] / steps[0]
+    assert ratios["constant"] < 1.1 < 2.5 < ratios["geometric"] < ratios["lognormal"]
