@@ -539,11 +539,23 @@ def setup_device(w, partition):
 def scheduler_host():
     """libpkv's scheduler step on the host over the whole 2000-request trace (schedule,
     plan with block tables / cu_seqlens / slot mapping, update), driven through the
-    Python binding: microseconds per step, no GPU work."""
+    Python binding: microseconds per step, no GPU work; at the trace's 128-request cap
+    and at caps of 8 and 256 (the batch sizes of the page's scheduler-cost exercise)."""
+    out = _scheduler_host_run(128)
+    # cap 256 with a 4x pool, so that the cap (not the memory) bounds the batch
+    out["by_max_running"] = {"8": _scheduler_host_run(8), "256 (16384-block pool)": _scheduler_host_run(256, 16384)}
+    return out
+
+
+def _scheduler_host_run(max_running, num_blocks=None):
+    import dataclasses
     import numpy as np
     import paged_kv_cache_42_amd as pkv
     import workloads
-    tr = workloads.config5("bf16")
+    tr = dataclasses.replace(workloads.config5("bf16"), max_running=max_running)
+    if num_blocks:
+        tr = dataclasses.replace(tr, num_blocks=num_blocks,
+                                 free_order=np.random.default_rng(5).permutation(num_blocks).astype(np.int32))
     pool = pkv.Pool(tr.num_blocks, tr.block_size, tr.num_kv_heads, tr.head_dim, tr.cache_dtype,
                     free_order=tr.free_order)
     sched = pkv.Scheduler(pool, tr.max_running)
