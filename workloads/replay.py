@@ -39,6 +39,17 @@ class StepRecord:
 
 
 class Replay:
+    """One trace replay: libpkv's scheduler over a pool, 16 layers of K/V planes on the
+    device, and the options of the scheduler and the launches:
+      chunk_cut / min_piece_tiles: cut long chunk blocks along the keys (chunk kernel);
+      prefix_cache: prefix caching for traces with shared system prompts;
+      token_budget / chunk_tokens: chunked prefill under a per-step token budget;
+      swap_blocks / swap_overlap: preemption by swap into pinned host memory (the DMA
+        leg of swap-outs on a copy stream when overlapped);
+      victim, priority, classes: victim policy, priority classes for admission, or
+        classes used only to report latencies by;
+      static_batching: the static-batching baseline."""
+
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
                  prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0,
                  swap_overlap: bool = False, victim: str = "self", priority=None, classes=None,
