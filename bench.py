@@ -244,7 +244,7 @@ def mixed_step(steps: int, warmup: int):
     mp = plans["cut"][0]
     rows_d = torch.from_numpy(mp.decode_rows).cuda()
     plan_d = torch.from_numpy(mp.split.plan).cuda()
-    ws = torch.empty(max(1, pkv.decode_split_workspace_bytes(len(mp.decode_rows), Hq, d, mp.split.max_pieces)),
+    ws = torch.empty(max(1, pkv.decode_split_workspace_bytes(mp.split.num_slots, Hq, d, mp.split.max_pieces)),
                      dtype=torch.uint8, device="cuda")
 
     def attention(mode, emid=None):
@@ -527,7 +527,7 @@ def setup_device(w, partition):
     # balanced split: the plan for the slots that fill this device
     cdt = pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16
     split = pkv.build_decode_split(w.seq_lens, pkv.decode_split_slots(cdt, Hkv, d, w.block_size), partition)
-    ws_bytes = max(ws_bytes, pkv.decode_split_workspace_bytes(w.num_seqs, Hq, d, split.max_pieces))
+    ws_bytes = max(ws_bytes, pkv.decode_split_workspace_bytes(split.num_slots, Hq, d, split.max_pieces))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     return dict(pool=pool, k_cache=k_cache, v_cache=v_cache, new_k=new_k, new_v=new_v, q=q,

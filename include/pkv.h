@@ -220,9 +220,12 @@ int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t mi
 int pkv_decode_split_slots(int32_t cache_dtype, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t* slots);
 
-/* Bytes of device workspace pkv_paged_attention_decode_split needs: partial outputs and
- * log-sum-exps of num_seqs * num_q_heads * max_pieces pieces (0 when max_pieces <= 1). */
-size_t pkv_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+/* Bytes of device workspace pkv_paged_attention_decode_split needs for a plan over
+ * num_slots slots: float32 partial outputs [num_slots][2][num_q_heads][head_dim] and
+ * log-sum-exps [num_slots][2][num_q_heads] (a slot holds at most two pieces of sequences
+ * that span several slots: its first and its last), so the size does not depend on the
+ * batch; 0 when max_pieces <= 1 (no sequence spans two slots). */
+size_t pkv_decode_split_workspace_bytes(int32_t num_slots, int32_t num_q_heads, int32_t head_dim,
                                         int32_t max_pieces);
 
 /* Decode attention with a balanced split of the context over a fixed number of slots
@@ -243,8 +246,9 @@ size_t pkv_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
  * has num_slots workgroups per group of KV heads. A plan row inside one slot's range is
  * written directly; the pieces of one spanning several slots are merged by log-sum-exp
  * in a second kernel, which also writes zeros (log-sum-exp -inf) for rows without
- * context. workspace: device, >= pkv_decode_split_workspace_bytes(num_rows,
- * num_q_heads, head_dim, max_pieces). A plan or row map that does not match the batch
+ * context. workspace: device, >= pkv_decode_split_workspace_bytes(num_slots,
+ * num_q_heads, head_dim, max_pieces); nothing in it needs to start at zero, and calls
+ * that share one workspace must not overlap. A plan or row map that does not match the batch
  * reads no memory out of bounds: a piece whose row falls outside the batch or that does
  * not fit is masked and not written. */
 int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,

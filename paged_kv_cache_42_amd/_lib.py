@@ -524,8 +524,9 @@ def decode_split_slots(cache_dtype: int, num_kv_heads: int, head_dim: int, block
     return n.value
 
 
-def decode_split_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_pieces: int) -> int:
-    return int(lib().pkv_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim, max_pieces))
+def decode_split_workspace_bytes(num_slots: int, num_q_heads: int, head_dim: int, max_pieces: int) -> int:
+    """Workspace bytes of a balanced-split launch over num_slots slots (from its SplitPlan)."""
+    return int(lib().pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces))
 
 
 def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split: SplitPlan,
@@ -537,6 +538,17 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
     sequence. rows (device int32 [n]): the batch sequences the plan covers; cu_seqlens_q
     (device int32 [B + 1]): q/out are [total_q][Hq][d] and a sequence's row is its last
     new token. plan_dev: device int32 copy of split.plan."""
+    args = _split_args(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split, num_kv_heads, block_size,
+                       max_seq_len, scale, k_scale, v_scale, workspace, lse, rows, cu_seqlens_q, k_head_scales,
+                       v_head_scales)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().pkv_paged_attention_decode_split(*args, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
+
+
+def _split_args(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split, num_kv_heads, block_size,
+                max_seq_len, scale, k_scale, v_scale, workspace, lse, rows, cu_seqlens_q, k_head_scales,
+                v_head_scales):
+    """Checks and the leading arguments (out .. max_pieces) of the balanced-split calls."""
     torch = _torch()
     _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, workspace, lse, rows,
                          cu_seqlens_q)
@@ -560,14 +572,12 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
         raise ValueError("plan must be int32 [rows + 1 + num_slots] (from build_decode_split)")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
         raise ValueError("lse must be float32 [rows][Hq]")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().pkv_paged_attention_decode_split(
-        _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
-        _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
-        k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
-        *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(rows), n, _dptr(cu_seqlens_q), T,
-        _dptr(plan_dev), split.num_slots, split.tiles_per_slot, split.max_pieces, _dptr(workspace), ws_bytes,
-        _dptr(lse), _stream(stream)))
+    return (_dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+            _dptr(block_tables), _dptr(seq_lens), block_tables.shape[1], B, Hq, num_kv_heads, d, block_size,
+            k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
+            *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(rows), n,
+            _dptr(cu_seqlens_q), T, _dptr(plan_dev), split.num_slots, split.tiles_per_slot, split.max_pieces)
+
 
 def decode_set_profile_event(event) -> None:
     """Record torch.cuda.Event `event` after the decode partition pass (None: off)."""

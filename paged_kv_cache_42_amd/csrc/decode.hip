@@ -100,8 +100,10 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_o;       // [B][Hq][pmax][D]
-  float* ws_lse;     // [B][Hq][pmax] (log2 domain)
+  // partials: fixed partitions [B][Hq][pmax][D] and [B][Hq][pmax] (log2 domain);
+  // balanced split [num_slots][2][Hq][D] and [num_slots][2][Hq] (see decode_split_kernel)
+  float* ws_o;
+  float* ws_lse;
   float* lse_out;    // [B][Hq] natural log, nullable
   int table_width;
   int num_kv_heads;
@@ -121,7 +123,18 @@ struct DecodeArgs {
   const int32_t* cu_q;   // balanced split: the batch's cu_seqlens_q (null: one query row per sequence)
   int num_batch;         // batch sequences (rows of block_tables / seq_lens)
   int total_q;           // query / output rows
+  int num_slots;         // balanced split: workgroup slots of the launch
 };
+
+// Partial of one piece of the balanced split, as an index into [num_slots][2][Hq]: a
+// sequence spanning slots first..first+np-1 leaves its piece p in slot first + p. Only the
+// first and the last piece of a slot can belong to such a sequence, and when both do they
+// are the same piece, so the slot keeps two entries: [1] for piece 0 (a sequence that
+// starts in the slot and runs past its end) and [0] for the others (a sequence that
+// began in an earlier slot). The bound is 2 * slots * heads, whatever the batch.
+__device__ __forceinline__ int64_t split_partial(int slot, int piece, int num_q_heads, int hq) {
+  return (int64_t(2 * slot + (piece == 0 ? 1 : 0))) * num_q_heads + hq;
+}
 
 // Batch sequence and query/output row of plan row s of a balanced split (the decode row
 // of a sequence is its last new token); -1 in *row for an index outside the batch.
@@ -438,6 +451,7 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   if (hq >= num_q_heads) return;
   int nparts;
   int orow_idx = s;
+  int first_slot = 0;
   if (a.plan) {
     // balanced split: pieces = slots that the sequence's tiles touch. The output row
     // (a row map lookup) is resolved after the partials' loads are issued, so the two
@@ -445,8 +459,11 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
     typedef __attribute__((address_space(4))) const int32_t* cptr;
     const cptr plan = (cptr)(uintptr_t)(a.plan);
     const int c0 = plan[s], c1 = plan[s + 1];
-    nparts = c1 > c0 && c0 >= 0 ? (c1 - 1) / a.tiles_per_slot - c0 / a.tiles_per_slot + 1 : 0;
+    first_slot = c0 >= 0 ? c0 / a.tiles_per_slot : 0;
+    nparts = c1 > c0 && c0 >= 0 ? (c1 - 1) / a.tiles_per_slot - first_slot + 1 : 0;
     if (nparts == 1) return;                  // written directly by the split pass
+    // a plan that does not fit this launch (more slots, or split without a workspace)
+    if (nparts > 1 && (first_slot + nparts > a.num_slots || !a.ws_o)) return;
     if (nparts == 0) {                        // no context: zero output (no piece wrote it)
       int b;
       split_row(a, s, b, orow_idx);
@@ -460,7 +477,6 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
       if (a.lse_out && e == 0) a.lse_out[int64_t(orow_idx) * num_q_heads + hq] = -INFINITY;
       return;
     }
-    nparts = nparts < a.pmax ? nparts : a.pmax;
   } else {
     int L = a.seq_lens[s];
     L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
@@ -468,6 +484,10 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   }
   if (nparts <= 1) return;                    // written directly by the partition pass
   const int64_t base = (int64_t(s) * num_q_heads + hq) * a.pmax;
+  // index of piece k's partial
+  auto piece = [&](int k) -> int64_t {
+    return a.plan ? split_partial(first_slot + k, k, num_q_heads, hq) : base + k;
+  };
   float M = -INFINITY, S = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   if (nparts <= kMergeFast) {
@@ -477,7 +497,7 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
     float4 ov[kMergeFast];
 #pragma unroll
     for (int k = 0; k < kMergeFast; ++k) {
-      const int64_t pi = base + (k < nparts ? k : 0);
+      const int64_t pi = piece(k < nparts ? k : 0);
       lse[k] = a.ws_lse[pi];
       ov[k] = *reinterpret_cast<const float4*>(a.ws_o + pi * D + e);
     }
@@ -496,12 +516,13 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   } else {
     // pass 1: the maximum log-sum-exp; pass 2: independent weighted loads (unrolled)
 #pragma unroll 8
-    for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_lse[base + k]);
+    for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_lse[piece(k)]);
     const float mref = M == -INFINITY ? 0.f : M;
 #pragma unroll 4
     for (int k = 0; k < nparts; ++k) {
-      const float wk = pkv::fast_exp2(a.ws_lse[base + k] - mref);   // 0 for an empty partition
-      const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + (base + k) * D + e);
+      const int64_t pi = piece(k);
+      const float wk = pkv::fast_exp2(a.ws_lse[pi] - mref);   // 0 for an empty partition
+      const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + pi * D + e);
       S += wk;
       A.x = fmaf(wk, ok.x, A.x);
       A.y = fmaf(wk, ok.y, A.y);
@@ -675,7 +696,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   cs = cs < 0 ? 0 : (cs > B ? B : cs);
   int cu_cur = plan[cs];
   int cu_next = cs < B ? plan[cs + 1] : 0x7fffffff;
-  int i_s = 0, i_row = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
+  int i_row = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
   bool i_valid = false;
   cptr_i32 i_bt = nullptr;
   // Queries: a piece's rows are loaded into qtmp when the piece is entered and moved
@@ -712,8 +733,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const int p = slot - first;
     // a piece of an inconsistent plan is streamed masked and not written
     const bool valid = row >= 0 && tb >= 0 && cu_cur >= 0 && p >= 0 && p < np &&
-                       (np == 1 || (a.ws_o != nullptr && p < a.pmax));
-    i_s = cs;
+                       (np == 1 || a.ws_o != nullptr);
     i_row = row;
     i_p = p;
     i_np = np;
@@ -738,7 +758,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   // per-slot tile state (NS slots: the tile being consumed and those in flight)
   static_assert(NS == 2 || NS == 3, "ring of 2 or 3 tiles");
   uint4 kb[NS][NV], vb[NS][NV];
-  int sl_t0[NS], sl_s[NS], sl_row[NS], sl_p[NS], sl_np[NS], sl_te[NS], sl_par[NS];
+  int sl_t0[NS], sl_row[NS], sl_p[NS], sl_np[NS], sl_te[NS], sl_par[NS];
   bool sl_ok[NS], sl_first[NS], sl_last[NS], sl_valid[NS];
 
   bool more = enter();
@@ -770,7 +790,6 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const int64_t off = (int64_t(ok ? blk : 0) * BS + (ti % SUB) * 16 + hl) * row_bytes + lane_off;
     sl_t0[k] = tok_lo;
     sl_ok[k] = ok;
-    sl_s[k] = i_s;
     sl_row[k] = i_row;
     sl_p[k] = i_p;
     sl_np[k] = i_np;
@@ -886,7 +905,6 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (!sl_valid[k] || hl >= G) return;
-    const int s = sl_s[k];
     const int hq = g * G + hl;
     const float inv = l > 0.f ? a.vscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)] / l : 0.f;
     const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
@@ -902,7 +920,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
       if (a.lse_out && grp == 0)
         pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + hq, __float_as_uint(lse2 * kLn2));
     } else {
-      const int64_t pi = (int64_t(s) * Hq + hq) * a.pmax + sl_p[k];
+      const int64_t pi = split_partial(slot, sl_p[k], Hq, hq);
       float* orow = a.ws_o + pi * D + 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -1197,10 +1215,10 @@ extern "C" int pkv_decode_split_slots(int32_t cache_dtype, int32_t num_kv_heads,
   return PKV_OK;
 }
 
-extern "C" size_t pkv_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+extern "C" size_t pkv_decode_split_workspace_bytes(int32_t num_slots, int32_t num_q_heads, int32_t head_dim,
                                                    int32_t max_pieces) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_pieces <= 1) return 0;
-  return size_t(num_seqs) * num_q_heads * max_pieces * (head_dim + 1) * sizeof(float);
+  if (num_slots <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_pieces <= 1) return 0;
+  return size_t(2) * num_slots * num_q_heads * (head_dim + 1) * sizeof(float);
 }
 
 extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache,
@@ -1250,7 +1268,7 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
   if (num_blocks < 1) return fail(PKV_ERR_INVALID, "decode_split: the cache has no blocks");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID, "decode_split: q, out and cache planes must be 16-byte aligned");
-  const size_t need = pkv_decode_split_workspace_bytes(num_rows, num_q_heads, head_dim, max_pieces);
+  const size_t need = pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_INVALID, "decode_split: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
 
@@ -1267,10 +1285,11 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
   a.num_blocks = num_blocks;
   const int64_t tcap = int64_t(table_width) * block_size;
   a.len_clamp = int(tcap < max_seq_len ? tcap : max_seq_len);
-  a.pmax = need > 0 ? max_pieces : 1;
+  a.pmax = 1;
+  a.num_slots = num_slots;
   if (need > 0) {
     a.ws_o = static_cast<float*>(workspace);
-    a.ws_lse = a.ws_o + size_t(num_rows) * num_q_heads * max_pieces * head_dim;
+    a.ws_lse = a.ws_o + size_t(2) * num_slots * num_q_heads * head_dim;
   }
   {
     const int rc = pkv::head_scales("attention", num_kv_heads, scale, k_scale, v_scale, k_head_scales,

@@ -144,7 +144,7 @@ def test_repeated_calls_on_one_workspace_agree():
     split = pkv.build_decode_split(w.seq_lens, 9)
     assert split.max_pieces > 1
     plan_d = torch.from_numpy(split.plan).cuda()
-    nb = pkv.decode_split_workspace_bytes(B, Hq, d, split.max_pieces)
+    nb = pkv.decode_split_workspace_bytes(split.num_slots, Hq, d, split.max_pieces)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     first = None
     for i in range(4):

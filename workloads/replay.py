@@ -175,7 +175,7 @@ class Replay:
         if len(mp.decode_rows):
             rows = torch.from_numpy(mp.decode_rows).cuda()
             plan_d = torch.from_numpy(mp.split.plan).cuda()
-            nb = pkv.decode_split_workspace_bytes(len(mp.decode_rows), tr.num_q_heads, tr.head_dim,
+            nb = pkv.decode_split_workspace_bytes(mp.split.num_slots, tr.num_q_heads, tr.head_dim,
                                                   mp.split.max_pieces)
             ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
         msl = int(seq_lens.max())
