@@ -265,6 +265,33 @@ int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,
                                      int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
                                      size_t workspace_bytes, float* lse_out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): pkv_paged_attention_decode_split
+ * with its partials in a fixed device array of the library (pkv_decode_split_noalloc_
+ * max_bytes() bytes, one per device, held until the process ends) instead of a
+ * workspace argument. Arguments and results as for pkv_paged_attention_decode_split
+ * without workspace / workspace_bytes; the current device must be the stream's. The
+ * call allocates nothing (the array's device address is looked up once per device, on
+ * the first call there). INVALID, with nothing launched, when
+ * pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces) exceeds
+ * the array. Every call on one device shares its array: calls that overlap on a device
+ * (other streams, other threads) race and must be serialised by the caller. */
+size_t pkv_decode_split_noalloc_max_bytes(void);
+int pkv_paged_attention_decode_split_noalloc(void* out, const void* q, int32_t q_dtype,
+                                             const void* k_cache, const void* v_cache,
+                                             int32_t cache_dtype, const int32_t* block_tables,
+                                             const int32_t* seq_lens, int32_t table_width,
+                                             int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t num_blocks,
+                                             int32_t max_seq_len, float scale, float k_scale,
+                                             float v_scale, const float* k_head_scales,
+                                             const float* v_head_scales, const int32_t* rows,
+                                             int32_t num_rows, const int32_t* cu_seqlens_q,
+                                             int32_t total_q, const int32_t* plan,
+                                             int32_t num_slots, int32_t tiles_per_slot,
+                                             int32_t max_pieces, float* lse_out, void* stream);
+
 /* Varlen work list (host) for pkv_paged_attention_prefill_varlen. For each sequence s
  * with q = q_lens[s] new tokens and seq_len L = seq_lens[s] (host int32 arrays):
  * q == 1 gives one decode item per KV head; q > 1 gives one prefill item

@@ -9,5 +9,6 @@ from ._lib import (  # noqa: F401
     paged_attention_decode, build_varlen_work, paged_attention_prefill_varlen, SplitPlan, build_decode_split,
     decode_split_slots, decode_split_workspace_bytes, paged_attention_decode_split, Scheduler, StepPlan,
     MixedPlan, build_mixed_step, paged_attention_prefill_chunks, ChunkPlan, build_chunk_work, chunk_slots,
-    chunk_workspace_bytes, swap_workspace_bytes, swap_out, swap_in,
+    chunk_workspace_bytes, swap_workspace_bytes, swap_out, swap_in, decode_split_noalloc_max_bytes,
+    paged_attention_decode_split_noalloc,
 )

@@ -92,6 +92,10 @@ _SIGS = {
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                                    i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, vp, i32, i32,
                                                    i32, vp, sz, vp, vp]),
+    "pkv_decode_split_noalloc_max_bytes": (sz, []),
+    "pkv_paged_attention_decode_split_noalloc": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                           i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, vp,
+                                                           i32, i32, i32, vp, vp]),
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, vp]),
 }
@@ -543,6 +547,24 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
                        v_head_scales)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().pkv_paged_attention_decode_split(*args, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
+
+
+def decode_split_noalloc_max_bytes() -> int:
+    """Size of the library's per-device partials array used by paged_attention_decode_split_noalloc."""
+    return int(lib().pkv_decode_split_noalloc_max_bytes())
+
+
+def paged_attention_decode_split_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev,
+                                         split: SplitPlan, num_kv_heads: int, block_size: int, max_seq_len: int,
+                                         scale: float, k_scale: float = 1.0, v_scale: float = 1.0, lse=None,
+                                         rows=None, cu_seqlens_q=None, stream=None, k_head_scales=None,
+                                         v_head_scales=None) -> None:
+    """paged_attention_decode_split without a workspace: the partials go to the library's
+    per-device array (calls on one device must not overlap)."""
+    args = _split_args(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split, num_kv_heads, block_size,
+                       max_seq_len, scale, k_scale, v_scale, None, lse, rows, cu_seqlens_q, k_head_scales,
+                       v_head_scales)
+    check(lib().pkv_paged_attention_decode_split_noalloc(*args, _dptr(lse), _stream(stream)))
 
 
 def _split_args(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split, num_kv_heads, block_size,
