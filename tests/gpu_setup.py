@@ -6,6 +6,12 @@ reads anything produced by the GPU path except to compare against it."""
 from __future__ import annotations
 
 import dataclasses
+import functools
+import json
+import os
+import subprocess
+import sys
+import tempfile
 from typing import Optional
 
 import numpy as np
@@ -184,22 +190,6 @@ def oracle_attention_full(st: Step, kp, vp, bt, cu):
     return oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, w.seq_lens, cu, w.softmax_scale, w.group, ks, vs)
 
 
-def oracle_decode_sampled(w: workloads.Workload, pairs):
-    """Oracle decode rows for sampled (sequence, KV head) pairs, from the dense
-    (gathered) K/V of that head; returns {(s, g): (out [G][d], lse [G])}."""
-    outs = {}
-    G = w.group
-    for s, g in pairs:
-        kh, vh = w.kv_head_f32(s, g)
-        K = kh.astype(np.float64)[:, None, :]
-        V = vh.astype(np.float64)[:, None, :]
-        q = workloads.storage_to_f64(w.q(s), w.dtype)[:, g * G:(g + 1) * G, :]
-        L = int(w.seq_lens[s])
-        o, lse = oatt.attend(q, K, V, [L - 1], w.softmax_scale, G)
-        outs[(s, g)] = (o[0], lse[0])
-    return outs
-
-
 def run_decode(st: Step, partition_size: Optional[int] = None, lse: bool = True, max_seq_len=None,
                use_work: bool = True):
     w = st.w
@@ -301,3 +291,34 @@ def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_to
                                            w.softmax_scale, w.k_scale, w.v_scale, lse=lse_t, **heads(w))
     torch.cuda.synchronize()
     return out, lse_t
+
+
+ORACLE_JOBS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_jobs.py")
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle_job(job_json: str, timeout: float):
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    print(f"[oracle] {job_json} on {workers} worker processes", flush=True)
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "oracle.npz")
+        subprocess.run([sys.executable, ORACLE_JOBS, job_json, path, str(workers)], check=True, timeout=timeout)
+        with np.load(path) as z:
+            return {k: z[k] for k in z.files}
+
+
+def oracle_job(job: dict, timeout: float = 900) -> dict:
+    """The oracle's results for `job` (see oracle_jobs.py), computed by a child program
+    with a pool of worker processes (this process holds the GPU and must not fork);
+    cached for the rest of the test session."""
+    return _oracle_job(json.dumps(job, sort_keys=True), timeout)
+
+
+def report_error(what: str, got: np.ndarray, ref: np.ndarray, got_lse=None, ref_lse=None) -> None:
+    """Print the worst absolute errors of a comparison (collected into the design notes)."""
+    msg = f"[parity] {what}: max |out err| {np.nanmax(np.abs(got - ref)):.3e}"
+    if got_lse is not None:
+        fin = np.isfinite(ref_lse)
+        e = np.abs(got_lse[fin] - ref_lse[fin])
+        msg += f", max |lse err| {e.max() if e.size else 0.0:.3e}"
+    print(msg, flush=True)

@@ -10,8 +10,8 @@ import paged_kv_cache_42_amd as pkv
 import workloads
 from oracle import fp8 as ofp8
 
-from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_decode_sampled, oracle_planes,
-                       out_f64, run_decode, torch_dtype)
+from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_job, oracle_planes, out_f64,
+                       report_error, run_decode, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -159,39 +159,23 @@ def test_split_matches_unsplit_closely():
         np.testing.assert_allclose(l.cpu().numpy(), l0.cpu().numpy(), rtol=0, atol=2 * LSE_ATOL["bf16"])
 
 
-def _pairs(w, n_samples):
-    rng = np.random.default_rng(w.seed)
-    order = np.argsort(w.seq_lens)
-    seqs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
-    seqs += rng.choice(w.num_seqs, size=min(n_samples, w.num_seqs), replace=False).tolist()
-    pairs = sorted(set((int(s), int(rng.integers(w.num_kv_heads))) for s in seqs))
-    return pairs + [(int(order[-1]), w.num_kv_heads - 1)]
-
-
-def _check_sampled(w, o, l, pairs, what):
-    ref = oracle_decode_sampled(w, pairs)
-    G = w.group
-    for (s, g), (ro, rl) in ref.items():
-        assert_close(o[s, g * G:(g + 1) * G], ro, w.dtype, f"{what} seq {s} head {g} (L={w.seq_lens[s]})")
-        np.testing.assert_allclose(l[s, g * G:(g + 1) * G], rl, rtol=0, atol=LSE_ATOL[w.dtype])
-
-
-def _sampled(w, partitions, n_samples=24):
+def _full_size(cfg, partitions):
+    """Every sequence and query head of a full-size decode batch against the oracle, for
+    each partition size (0: the whole context in one work item)."""
+    w = workloads.config(cfg)
+    ref = oracle_job({"kind": "decode", "config": cfg})
     st = build_step(w, fill_nan=False)
-    pairs = _pairs(w, n_samples)
     for P in partitions:
         out, lse = run_decode(st, partition_size=P)
-        o = out_f64(out)
-        assert np.isfinite(o).all()
-        _check_sampled(w, o, lse.cpu().numpy(), pairs, f"{w.name} P={P}")
-    return st
+        o, l_ = out_f64(out), lse.cpu().numpy().astype(np.float64)
+        report_error(f"{w.name} partitioned decode P={P}", o, ref["out"], l_, ref["lse"])
+        assert_close(o, ref["out"], w.dtype, f"{w.name} P={P}")
+        np.testing.assert_allclose(l_, ref["lse"], rtol=0, atol=LSE_ATOL[w.dtype])
 
 
-def test_config3_full_size_sampled():
-    w = workloads.config3()
-    _sampled(w, (w.partition_size, 0, 512), n_samples=24)
+def test_config3_full_size():
+    _full_size(3, (512, 0, 128))
 
 
-def test_config4_full_size_sampled():
-    w = workloads.config4()
-    _sampled(w, (w.partition_size,), n_samples=5)
+def test_config4_full_size():
+    _full_size(4, (512,))

@@ -1,6 +1,7 @@
 """Balanced-split decode on the GPU vs the oracle (element by element): every slot count
 from one workgroup to more slots than tiles, empty sequences, the full-size decode
-batches (sampled), and a plan built for longer contexts than the device lengths."""
+batches (every sequence and head, against the oracle run in a child program), and a
+plan built for longer contexts than the device lengths."""
 import zlib
 
 import numpy as np
@@ -10,8 +11,8 @@ import torch
 import paged_kv_cache_42_amd as pkv
 import workloads
 
-from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_decode_sampled, oracle_planes,
-                       out_f64, run_decode, run_decode_split)
+from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_job, oracle_planes, out_f64,
+                       report_error, run_decode, run_decode_split)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,29 +110,27 @@ def test_split_close_to_unsplit_partitioned_decode():
         np.testing.assert_allclose(l.cpu().numpy(), l0.cpu().numpy(), rtol=0, atol=2 * LSE_ATOL)
 
 
-def _sampled(w, n_samples):
+def _full_size(cfg, slot_counts=(None,)):
+    """Every sequence and query head of a full-size decode batch against the oracle, for
+    the device's slot count and the other counts given."""
+    w = workloads.config(cfg)
+    ref = oracle_job({"kind": "decode", "config": cfg})
     st = build_step(w, fill_nan=False)
-    rng = np.random.default_rng(w.seed)
-    order = np.argsort(w.seq_lens)
-    seqs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
-    seqs += rng.choice(w.num_seqs, size=min(n_samples, w.num_seqs), replace=False).tolist()
-    pairs = sorted(set((int(s), int(rng.integers(w.num_kv_heads))) for s in seqs))
-    out, lse, split = run_decode_split(st)
-    o = out_f64(out)
-    assert np.isfinite(o).all()
-    l = lse.cpu().numpy()
-    G = w.group
-    for (s, g), (ro, rl) in oracle_decode_sampled(w, pairs).items():
-        assert_close(o[s, g * G:(g + 1) * G], ro, w.dtype, f"{w.name} seq {s} head {g} (L={w.seq_lens[s]})")
-        np.testing.assert_allclose(l[s, g * G:(g + 1) * G], rl, rtol=0, atol=LSE_ATOL)
+    for n in slot_counts:
+        out, lse, split = run_decode_split(st, num_slots=n)
+        o, l_ = out_f64(out), lse.cpu().numpy().astype(np.float64)
+        report_error(f"{w.name} split decode, {split.num_slots} slots (max pieces {split.max_pieces})", o,
+                     ref["out"], l_, ref["lse"])
+        assert_close(o, ref["out"], w.dtype, f"{w.name} split over {split.num_slots} slots")
+        np.testing.assert_allclose(l_, ref["lse"], rtol=0, atol=LSE_ATOL)
 
 
-def test_config3_full_size_sampled_split():
-    _sampled(workloads.config3(), 24)
+def test_config3_full_size_split():
+    _full_size(3, (None, 97, 1000))
 
 
-def test_config4_full_size_sampled_split():
-    _sampled(workloads.config4(), 5)
+def test_config4_full_size_split():
+    _full_size(4, (None, 61))
 
 
 def test_repeated_calls_on_one_workspace_agree():

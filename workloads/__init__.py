@@ -121,12 +121,15 @@ def hash_values(key: int, e0: int, e1: int, sigma: float = 1.0) -> np.ndarray:
     t = np.empty(_CHUNK, np.uint64)
     f = np.empty((_CHUNK, 3), np.uint32)
     acc = np.empty((_CHUNK, 3), np.uint32)
+    tmp = np.empty((_CHUNK, 3), np.uint32)
+    ones = np.arange(1, _CHUNK + 1, dtype=np.uint64)
     k = np.uint64(key)
     sig = np.float32(sigma)
+    # every buffer is reused across chunks (a fresh temporary per chunk costs page faults)
     for c0 in range(n0, n1, _CHUNK):
         m = min(_CHUNK, n1 - c0)
         zz, tt = z[:m], t[:m]
-        zz[:] = np.arange(c0 + 1, c0 + 1 + m, dtype=np.uint64)
+        np.add(ones[:m], np.uint64(c0), out=zz)
         np.multiply(zz, _GAMMA, out=zz)
         np.add(zz, k, out=zz)
         np.right_shift(zz, np.uint64(30), out=tt)
@@ -137,14 +140,15 @@ def hash_values(key: int, e0: int, e1: int, sigma: float = 1.0) -> np.ndarray:
         np.multiply(zz, _MIX2, out=zz)
         np.right_shift(zz, np.uint64(31), out=tt)
         np.bitwise_xor(zz, tt, out=zz)
-        ff, aa = f[:m], acc[:m]
+        ff, aa, tm = f[:m], acc[:m], tmp[:m]
         for j in range(3):
             np.right_shift(zz, np.uint64(18 * j), out=tt)
             np.bitwise_and(tt, np.uint64(0x3FFFF), out=tt)
             ff[:, j] = tt
         np.bitwise_and(ff, np.uint32(63), out=aa)
         np.right_shift(ff, np.uint32(6), out=ff)
-        aa += ff & np.uint32(63)
+        np.bitwise_and(ff, np.uint32(63), out=tm)
+        aa += tm
         np.right_shift(ff, np.uint32(6), out=ff)
         aa += ff
         o = res[3 * (c0 - n0): 3 * (c0 - n0 + m)].reshape(m, 3)
