@@ -16,13 +16,16 @@ of 16 tokens, bf16, a pool 1.2x the need with shuffled block ids.
 Prints one JSON line. `value` is decode HBM GB/s: algorithmic bytes of the decode
 launch (K/V of every context token, queries, outputs, block-table entries, lengths)
 divided by the decode time (partition pass + merge), timed with HIP events on the
-launch stream around the decode call. A second run of the same steps has the library
-record an event between the partition pass and the merge; `roofline` reports that
-partition pass alone against the 8 TB/s HBM peak. `cpu_baseline` times the CPU oracle
-on a bounded prefix of the same batch.
+launch stream around the decode call; `roofline` reports that same decode (pass +
+merge) against the 8 TB/s HBM peak, and under `pass_only` the partition pass alone,
+from a second run of the steps in which the library records an event between the pass
+and the merge. `cpu_baseline` times the CPU oracle on a bounded prefix of the same batch
+with all BLAS threads and with one, and names the host CPU.
 
-Sub-measurements in the same line: `mixed_step` (48 decode rows + 4 prefill chunks of
-512), `swap_copy` (1 GiB of K/V to pinned host memory and back) and `sched_replay` (the
+Sub-measurements in the same line: `decode_variants` (the config-3 batch with an E4M3
+cache, and config 4: 16 sequences of 32k-128k tokens, each with GB/s, fraction of peak
+and the merge's share), `mixed_step` (48 decode rows + 4 prefill chunks of 512),
+`swap_copy` (1 GiB of K/V to pinned host memory and back) and `sched_replay` (the
 2000-request continuous-batching trace, 16 layers, with bf16 and E4M3 caches by default;
 `--replays all` adds static batching, chunked prefill, swap, victim policies, priority
 classes and prefix caching), each switchable off.
@@ -67,6 +70,8 @@ def parse_args():
                     help="also replay the bf16 trace under several token budgets / chunk sizes (chunked prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-variants", action="store_true",
+                    help="skip the config-3 E4M3-cache and config-4 (long context) decode sub-measurements")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="instead of the step, time a plain device copy of this many MiB (stream bandwidth and "
                          "the known-size kernel that calibrates HBM byte counters)")
@@ -244,8 +249,7 @@ def mixed_step(steps: int, warmup: int):
     mp = plans["cut"][0]
     rows_d = torch.from_numpy(mp.decode_rows).cuda()
     plan_d = torch.from_numpy(mp.split.plan).cuda()
-    ws = torch.empty(max(1, pkv.decode_split_workspace_bytes(mp.split.num_slots, Hq, d, mp.split.max_pieces)),
-                     dtype=torch.uint8, device="cuda")
+    ws = pkv.decode_split_workspace(mp.split, Hq, d)
 
     def attention(mode, emid=None):
         if mode == "one_launch":
@@ -467,7 +471,8 @@ def measured_traffic(partition: int, workload: str, decode: str):
 
 def setup_device(w, partition):
     """Pool + tables (libpkv host), K/V generated on the GPU, context written by the
-    cache-write kernel; returns the tensors of one decode step."""
+    cache-write kernel (E4M3-encoded for an fp8 cache); returns the tensors of one
+    decode step."""
     import numpy as np
     import torch
     import paged_kv_cache_42_amd as pkv
@@ -482,9 +487,10 @@ def setup_device(w, partition):
     _, _, ctx_slots = pool.build_block_table(ids, prior, prior, W)
     bt, cu, slots = pool.build_block_table(ids, w.q_lens, w.seq_lens, W)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[w.cache_dtype]
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-    k_cache = torch.empty(shape, dtype=dt, device="cuda")
-    v_cache = torch.empty(shape, dtype=dt, device="cuda")
+    k_cache = torch.empty(shape, dtype=cdt, device="cuda")
+    v_cache = torch.empty(shape, dtype=cdt, device="cuda")
     Hkv, Hq, d = w.num_kv_heads, w.num_q_heads, w.head_dim
     n_new = int(w.q_lens.sum())
     new_k = torch.empty((n_new, Hkv, d), dtype=dt, device="cuda")
@@ -511,7 +517,7 @@ def setup_device(w, partition):
             o += p
         if tok:
             sl = torch.from_numpy(ctx_slots[slot_off:slot_off + tok].copy()).cuda()
-            pkv.kv_cache_write(ck, cv, k_cache, v_cache, sl, w.block_size)
+            pkv.kv_cache_write(ck, cv, k_cache, v_cache, sl, w.block_size, w.k_scale, w.v_scale)
         slot_off += tok
         s0 = s1
         del ck, cv
@@ -525,15 +531,108 @@ def setup_device(w, partition):
     work = torch.from_numpy(pkv.build_decode_work(w.seq_lens, partition)).cuda()
     ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, Hq, d, msl, partition)
     # balanced split: the plan for the slots that fill this device
-    cdt = pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16
-    split = pkv.build_decode_split(w.seq_lens, pkv.decode_split_slots(cdt, Hkv, d, w.block_size), partition)
-    ws_bytes = max(ws_bytes, pkv.decode_split_workspace_bytes(split.num_slots, Hq, d, split.max_pieces))
+    split = pkv.build_decode_split(w.seq_lens, pkv.decode_split_slots({"bf16": pkv.BF16, "fp8": pkv.FP8}.get(w.cache_dtype, pkv.BF16), Hkv,
+                                                                      d, w.block_size), partition)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws_split = pkv.decode_split_workspace(split, Hq, d)
     torch.cuda.synchronize()
     return dict(pool=pool, k_cache=k_cache, v_cache=v_cache, new_k=new_k, new_v=new_v, q=q,
                 out=torch.empty_like(q), slots=torch.from_numpy(slots).cuda(), bt=torch.from_numpy(bt).cuda(),
-                lens=torch.from_numpy(w.seq_lens.astype(np.int32)).cuda(), ws=ws, max_seq_len=msl, work=work,
+                lens=torch.from_numpy(w.seq_lens.astype(np.int32)).cuda(), ws=ws, ws_split=ws_split,
+                max_seq_len=msl, work=work,
                 split=split, plan=torch.from_numpy(split.plan).cuda())
+
+
+def time_decode_step(w, P, decode_kind, steps, warmup):
+    """The decode step of workload w (cache write of its new tokens, then decode attention)
+    timed with HIP events on the launch stream: K steps as a caller runs them, then K more
+    with the library recording an event between the pass and the merge. Returns the
+    per-step event times (seconds, numpy arrays), the wall time of the first run and the
+    device tensors."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_42_amd as pkv
+
+    dev = setup_device(w, P)
+    stream = torch.cuda.current_stream()
+    scale = w.softmax_scale
+
+    def write():
+        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size,
+                           w.k_scale, w.v_scale)
+
+    def decode():
+        if decode_kind == "split":
+            pkv.paged_attention_decode_split(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"],
+                                             dev["lens"], dev["plan"], dev["split"], w.num_kv_heads, w.block_size,
+                                             dev["max_seq_len"], scale, w.k_scale, w.v_scale, dev["ws_split"])
+        else:
+            pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
+                                       w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, w.k_scale,
+                                       w.v_scale, P, dev["ws"], work=dev["work"])
+
+    for _ in range(warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+
+    def timed(profile: bool):
+        """K steps bracketed by events (write | decode); with profile=True the library also
+        records an event between the partition pass and the merge (which adds its own gap)."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for e in ev:        # materialise the event handles before use by the library hook
+            for x in e:
+                x.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            e0, e1, e2, e3 = ev[i]
+            e0.record(stream)
+            write()
+            e1.record(stream)
+            if profile:
+                pkv.decode_set_profile_event(e2)
+            decode()
+            if profile:
+                pkv.decode_set_profile_event(None)
+            e3.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in ev]) * 1e-3
+        return wall, ms(0, 1), ms(1, 3), ms(0, 3), (ms(1, 2) if profile else None), (ms(2, 3) if profile else None)
+
+    # the step as a caller runs it, then again with the pass/merge split point
+    wall, t_write, t_decode, t_step, _, _ = timed(False)
+    _, _, _, _, t_part, t_merge = timed(True)
+    return dict(wall=wall, write=t_write, decode=t_decode, step=t_step, part=t_part, merge=t_merge, dev=dev)
+
+
+def decode_record(w, P, decode_kind, steps, warmup):
+    """A decode sub-measurement: GB/s of the decode (pass + merge), its fraction of the
+    8 TB/s peak, the pass alone, and the merge's share of the decode time."""
+    import numpy as np
+    import torch
+    r = time_decode_step(w, P, decode_kind, steps, warmup)
+    dbytes = decode_bytes(w)
+    t_dec, t_part, t_merge = float(r["decode"].mean()), float(r["part"].mean()), float(r["merge"].mean())
+    split = r["dev"]["split"]
+    out = {"workload": w.name, "cache_dtype": w.cache_dtype, "num_seqs": w.num_seqs,
+           "context_tokens": int(w.seq_lens.sum()), "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+           "head_dim": w.head_dim, "block_size": w.block_size, "decode": decode_kind,
+           "algorithmic_bytes": dbytes,
+           "decode_us": round(t_dec * 1e6, 2), "decode_GBps": round(dbytes / t_dec / 1e9, 1),
+           "decode_frac_of_peak": round(dbytes / t_dec / 1e9 / PEAK_HBM_GBS, 4),
+           "pass_us_profiled": round(t_part * 1e6, 2), "merge_us_profiled": round(t_merge * 1e6, 2),
+           "pass_GBps": round(dbytes / t_part / 1e9, 1),
+           "pass_frac_of_peak": round(dbytes / t_part / 1e9 / PEAK_HBM_GBS, 4),
+           "merge_share_of_decode": round(t_merge / (t_part + t_merge), 4),
+           "tokens_per_s": round(w.num_seqs / float(r["step"].mean()), 1)}
+    if decode_kind == "split":
+        out.update(split_slots=split.num_slots, split_tiles_per_slot=split.tiles_per_slot,
+                   split_max_pieces=split.max_pieces)
+    del r
+    torch.cuda.empty_cache()
+    return out
 
 
 def scheduler_host():
@@ -596,9 +695,25 @@ def scheduler_oracle(budget_s: float):
                       f"average), pure Python, one thread, {dt:.1f} s"}
 
 
+def cpu_info() -> dict:
+    """The host the oracle runs on: CPU model, logical CPUs, the CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (float64 NumPy, as it stands) on a prefix of the batch, sequence by
-    sequence, until `budget_s` seconds of oracle time; inputs prepared untimed."""
+    sequence, until `budget_s` seconds of oracle time; inputs prepared untimed. Timed twice:
+    with NumPy's BLAS on all the threads it starts with (the headline value), and with one
+    BLAS thread."""
     import numpy as np
     import workloads
     from oracle import attention as oatt
@@ -606,9 +721,10 @@ def cpu_baseline(w, budget_s: float):
     from oracle.allocator import BlockPool, SeqTables
     from oracle.metadata import build_block_table
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = 1
 
     tabs = SeqTables(BlockPool(w.num_blocks, w.free_order), w.block_size)
@@ -630,21 +746,41 @@ def cpu_baseline(w, budget_s: float):
         prep.append((L, bt, cu, workloads.storage_to_f64(w.q(s), w.dtype)))
         if time.perf_counter() - t_prep > 4 * budget_s:
             break
-    # time whole passes of the oracle over the prepared sequences until the budget is spent
-    spent, passes = 0.0, 0
-    while spent < budget_s and passes < 100:
-        t0 = time.perf_counter()
-        for L, bt, cu, q in prep:
-            oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, [L], cu, w.softmax_scale, w.group)
-        spent += time.perf_counter() - t0
-        passes += 1
-    tokens = sum(p[0] for p in prep)
     e_kv = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
-    nbytes = tokens * 2 * w.num_kv_heads * w.head_dim * e_kv
-    return {"value": round(nbytes * passes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"first {len(prep)} of {w.num_seqs} sequences ({tokens} context tokens, {nbytes / 1e9:.3f} GB "
-                      f"of K/V), {passes} pass(es) of the float64 NumPy oracle in {spent:.1f} s; cores = BLAS threads"}
+
+    def timed(items, budget):
+        """Whole passes of the oracle over `items` until `budget` seconds are spent."""
+        spent, passes = 0.0, 0
+        while spent < budget and passes < 100:
+            t0 = time.perf_counter()
+            for L, bt, cu, q in items:
+                oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, [L], cu, w.softmax_scale, w.group)
+            spent += time.perf_counter() - t0
+            passes += 1
+        tokens = sum(p[0] for p in items)
+        nbytes = tokens * 2 * w.num_kv_heads * w.head_dim * e_kv
+        return nbytes * passes / spent / 1e9, tokens, nbytes, passes, spent
+
+    gbs, tokens, nbytes, passes, spent = timed(prep, budget_s)
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"first {len(prep)} of {w.num_seqs} sequences ({tokens} context tokens, {nbytes / 1e9:.3f} GB "
+                     f"of K/V), {passes} pass(es) of the float64 NumPy oracle in {spent:.1f} s; cores = BLAS threads",
+           **cpu_info(), "blas_threads": int(threads)}
+    if threadpool_limits is not None:
+        # one thread: the longest prefix of the prepared sequences one pass of which fits
+        # in the budget (the rate is per byte, so a prefix measures it)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            n = 0
+            while n < len(prep) and time.perf_counter() - t0 < budget_s / 2:
+                L, bt, cu, q = prep[n]
+                oatt.paged_attention(q, kp, vp, w.cache_dtype, bt, [L], cu, w.softmax_scale, w.group)
+                n += 1
+            g1, tok1, nb1, p1, sp1 = timed(prep[:max(n, 1)], budget_s / 2)
+        res["single_thread"] = {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
+                                "sample": f"first {max(n, 1)} sequences ({tok1} context tokens, {nb1 / 1e9:.3f} GB of "
+                                          f"K/V), {p1} pass(es) in {sp1:.1f} s with one BLAS thread"}
+    return res
 
 
 def main():
@@ -659,71 +795,23 @@ def main():
     if args.probe_read_mib:
         probe_read(args.probe_read_mib, args.steps)
         return
+    import dataclasses
     import numpy as np
     import torch
-    import paged_kv_cache_42_amd as pkv
     import workloads
 
     w = workloads.config3() if args.workload == "cfg3" else workloads.config4()
     P = w.partition_size if args.partition is None else args.partition
     print(f"[bench] {w.name}: B={w.num_seqs} sumL={int(w.seq_lens.sum())} P={P}; setting up", file=sys.stderr,
           flush=True)
-    dev = setup_device(w, P)
-    stream = torch.cuda.current_stream()
-    scale = w.softmax_scale
-
-    def decode():
-        if args.decode == "split":
-            pkv.paged_attention_decode_split(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"],
-                                             dev["lens"], dev["plan"], dev["split"], w.num_kv_heads, w.block_size,
-                                             dev["max_seq_len"], scale, 1.0, 1.0, dev["ws"])
-        else:
-            pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
-                                       w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, 1.0, 1.0, P,
-                                       dev["ws"], work=dev["work"])
-
-    for _ in range(args.warmup):
-        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size)
-        decode()
-    torch.cuda.synchronize()
-
     K = args.steps
-
-    def timed(profile: bool):
-        """K steps bracketed by events (write | decode); with profile=True the library also
-        records an event between the partition pass and the merge (which adds its own gap)."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-        for e in ev:        # materialise the event handles before use by the library hook
-            for x in e:
-                x.record(stream)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            e0, e1, e2, e3 = ev[i]
-            e0.record(stream)
-            pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"],
-                               w.block_size)
-            e1.record(stream)
-            if profile:
-                pkv.decode_set_profile_event(e2)
-            decode()
-            if profile:
-                pkv.decode_set_profile_event(None)
-            e3.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in ev]) * 1e-3
-        return wall, ms(0, 1), ms(1, 3), ms(0, 3), (ms(1, 2) if profile else None), (ms(2, 3) if profile else None)
-
-    # the step as a caller runs it (value), then again with the pass/merge split point (roofline)
-    wall, t_write, t_decode, t_step, _, _ = timed(False)
-    _, _, _, _, t_part, t_merge = timed(True)
-
+    r = time_decode_step(w, P, args.decode, K, args.warmup)
+    dev = r["dev"]
     dbytes = decode_bytes(w)
-    t_dec = float(t_decode.mean())
+    t_dec = float(r["decode"].mean())
     gbs = dbytes / t_dec / 1e9
-    part_gbs = dbytes / float(t_part.mean()) / 1e9
-    ms_step = wall / K * 1e3
+    part_gbs = dbytes / float(r["part"].mean()) / 1e9
+    ms_step = r["wall"] / K * 1e3
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -749,21 +837,35 @@ def main():
         "pct_of_measured_read_peak": None,
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
-        "kernel_us": {"kv_cache_write": round(float(t_write.mean()) * 1e6, 2),
+        "kernel_us": {"kv_cache_write": round(float(r["write"].mean()) * 1e6, 2),
                       "decode": round(t_dec * 1e6, 2),
-                      "decode_median": round(float(np.median(t_decode)) * 1e6, 2),
-                      "decode_min": round(float(t_decode.min()) * 1e6, 2),
-                      "step_events": round(float(t_step.mean()) * 1e6, 2),
-                      "profiled_partition_pass": round(float(t_part.mean()) * 1e6, 2),
-                      "profiled_merge": round(float(t_merge.mean()) * 1e6, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(part_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(part_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(P, args.workload, args.decode),
-                     "kernel": "decode partition pass", "algorithmic_bytes": dbytes},
+                      "decode_median": round(float(np.median(r["decode"])) * 1e6, 2),
+                      "decode_min": round(float(r["decode"].min()) * 1e6, 2),
+                      "step_events": round(float(r["step"].mean()) * 1e6, 2),
+                      "profiled_partition_pass": round(float(r["part"].mean()) * 1e6, 2),
+                      "profiled_merge": round(float(r["merge"].mean()) * 1e6, 2)},
+        # the decode as a caller runs it: the partition pass and the log-sum-exp merge
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(P, args.workload, args.decode),
+                     "kernel": "decode: partition pass + log-sum-exp merge (HIP events around both launches)",
+                     "algorithmic_bytes": dbytes,
+                     "pass_only": {"achieved": round(part_gbs, 2), "frac": round(part_gbs / PEAK_HBM_GBS, 4),
+                                   "us": round(float(r["part"].mean()) * 1e6, 2)}},
         "cpu_baseline": None,
     }
+    del r, dev
+    torch.cuda.empty_cache()
     rp = measured_read_peak()
     res["measured_read_peak_GBps"] = round(rp, 1)
     res["pct_of_measured_read_peak"] = round(100 * gbs / rp, 2)
+    if not args.no_decode_variants:
+        # the other decode shapes the workloads name: config 3 with an E4M3 cache (half the
+        # bytes) and config 4 (long contexts, split context merged by log-sum-exp)
+        res["decode_variants"] = {}
+        for name, wv in (("cfg3_e4m3_cache", dataclasses.replace(workloads.config3(), cache_dtype="fp8")),
+                         ("cfg4_long_context_bf16", workloads.config4())):
+            print(f"[bench] decode variant {name}", file=sys.stderr, flush=True)
+            res["decode_variants"][name] = decode_record(wv, wv.partition_size, "split", K, args.warmup)
     if not args.no_mixed:
         print("[bench] mixed prefill+decode step", file=sys.stderr, flush=True)
         res["mixed_step"] = mixed_step(args.steps, args.warmup)

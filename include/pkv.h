@@ -200,18 +200,26 @@ int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype, const 
 
 /* Balanced split plan (host) for pkv_paged_attention_decode_split. The context of each
  * sequence is cut into 16-token tiles (the last one partial) and the tiles of all
- * sequences are laid end to end; slot j of the launch streams tiles [j*C, (j+1)*C) with
- * C = max(ceil(total tiles / num_slots), ceil(min_piece_tokens / 16), 1), so every slot
- * moves the same bytes whatever the length mix. seq_lens: host int32 [num_seqs] (the
+ * sequences are laid end to end; slot j of the launch streams tiles
+ * [slot_lo[j], slot_lo[j + 1]). The boundaries make every slot take the same time under
+ * a cost model: a slot costs its tiles plus piece_cost_tokens / 16 tiles for each piece
+ * (a sequence, or part of one, that it streams: entering it and writing its output or
+ * partial), so a slot that crosses many short sequences gets fewer tiles. Slots are
+ * filled in order, each to the remaining cost over the remaining slots; at most
+ * min(num_slots, total tiles / ceil(min_piece_tokens / 16)) slots are used (at least one
+ * when there is any context; fewer when a slot would cost more in pieces than it saves),
+ * the rest are empty. seq_lens: host int32 [num_seqs] (the
  * values the device copy holds). plan: host int32 [capacity], capacity >=
- * num_seqs + 1 + num_slots, receiving the tile offsets [num_seqs + 1] (offset of sequence
- * s = tiles of sequences 0..s-1) followed by the first sequence with a tile in each slot's
- * range [num_slots]. *tiles_per_slot = C; *max_pieces = the most slots one sequence
- * spans (<= ceil(max_seq_len / (16 C)) + 1). INVALID on a bad argument, a short
- * capacity or more than 2^31 - 2 tiles (nothing useful written). */
+ * 3 * num_seqs + 2 * num_slots + 2, receiving in order: the tile offsets [num_seqs + 1]
+ * (offset of sequence s = tiles of sequences 0..s-1); the first sequence with a tile at
+ * or past each slot's start [num_slots]; slot_lo [num_slots + 1] (non-decreasing, the
+ * last entry the total); and for each sequence its first slot and number of pieces
+ * [num_seqs][2] (pieces 0 for an empty sequence). *tiles_per_slot = the most tiles in
+ * one slot; *max_pieces = the most slots one sequence spans. INVALID on a bad argument, a
+ * short capacity or more than 2^31 - 2 tiles (nothing useful written). */
 int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t min_piece_tokens,
-                           int32_t num_slots, int32_t* plan, int32_t capacity,
-                           int32_t* tiles_per_slot, int32_t* max_pieces);
+                           int32_t piece_cost_tokens, int32_t num_slots, int32_t* plan,
+                           int32_t capacity, int32_t* tiles_per_slot, int32_t* max_pieces);
 
 /* Slots that fill the current device with resident workgroups of the balanced-split
  * decode kernel for this cache dtype and shape (any value >= 1 is correct; this one
@@ -244,11 +252,13 @@ size_t pkv_decode_split_workspace_bytes(int32_t num_slots, int32_t num_q_heads, 
  * device int32, the array pkv_build_decode_split returned for the plan rows' seq_lens
  * (in plan-row order) and num_slots (tiles_per_slot and max_pieces likewise); the launch
  * has num_slots workgroups per group of KV heads. A plan row inside one slot's range is
- * written directly; the pieces of one spanning several slots are merged by log-sum-exp
- * in a second kernel, which also writes zeros (log-sum-exp -inf) for rows without
- * context. workspace: device, >= pkv_decode_split_workspace_bytes(num_slots,
- * num_q_heads, head_dim, max_pieces); nothing in it needs to start at zero, and calls
- * that share one workspace must not overlap. A plan or row map that does not match the batch
+ * written directly, as are zeros (log-sum-exp -inf) for rows without context; the
+ * pieces of one spanning several slots leave partials in the workspace, merged by
+ * log-sum-exp in a second kernel (one workgroup per such sequence, found from its first
+ * slot; not launched when max_pieces <= 1). workspace: device, >=
+ * pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces);
+ * nothing in it needs to start at zero, and calls that share one workspace must not
+ * overlap. A plan or row map that does not match the batch
  * reads no memory out of bounds: a piece whose row falls outside the batch or that does
  * not fit is masked and not written. */
 int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,

@@ -10,5 +10,6 @@ from ._lib import (  # noqa: F401
     decode_split_slots, decode_split_workspace_bytes, paged_attention_decode_split, Scheduler, StepPlan,
     MixedPlan, build_mixed_step, paged_attention_prefill_chunks, ChunkPlan, build_chunk_work, chunk_slots,
     chunk_workspace_bytes, swap_workspace_bytes, swap_out, swap_in, decode_split_noalloc_max_bytes,
+    decode_split_workspace, split_plan_len,
     paged_attention_decode_split_noalloc,
 )

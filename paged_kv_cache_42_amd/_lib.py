@@ -58,7 +58,7 @@ _SIGS = {
                                              i32, i32, f32, f32, f32, vp, vp, i32, vp, sz, vp, vp, i32, vp]),
     "pkv_build_decode_work": (C.c_int, [i32, vp, i32, vp, i32, P_i32]),
     "pkv_build_varlen_work": (C.c_int, [i32, vp, vp, i32, i32, vp, i32, P_i32]),
-    "pkv_build_decode_split": (C.c_int, [i32, vp, i32, i32, vp, i32, P_i32, P_i32]),
+    "pkv_build_decode_split": (C.c_int, [i32, vp, i32, i32, i32, vp, i32, P_i32, P_i32]),
     "pkv_paged_attention_prefill_chunks": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32,
                                                      i32, vp, i64, vp, vp]),
@@ -510,14 +510,24 @@ class SplitPlan:
         self.plan, self.num_slots, self.tiles_per_slot, self.max_pieces = plan, num_slots, tiles_per_slot, max_pieces
 
 
-def build_decode_split(seq_lens, num_slots: int, min_piece_tokens: int = 0) -> SplitPlan:
-    """Balanced split of the 16-token tiles of all sequences over num_slots workgroup slots."""
+SPLIT_PIECE_COST_TOKENS = 22
+
+
+def split_plan_len(num_seqs: int, num_slots: int) -> int:
+    """Entries of a balanced split plan (int32)."""
+    return 3 * int(num_seqs) + 2 * int(num_slots) + 2
+
+
+def build_decode_split(seq_lens, num_slots: int, min_piece_tokens: int = 0,
+                       piece_cost_tokens: int = SPLIT_PIECE_COST_TOKENS) -> SplitPlan:
+    """Balanced split of the 16-token tiles of all sequences over num_slots workgroup slots
+    (each slot's tiles plus piece_cost_tokens / 16 per piece equalised)."""
     L = np.ascontiguousarray(seq_lens, dtype=np.int32)
-    cap = len(L) + 1 + int(num_slots)
+    cap = split_plan_len(len(L), num_slots)
     plan = np.zeros(cap, np.int32)
     c, mp = i32(), i32()
-    check(lib().pkv_build_decode_split(len(L), _np_ptr(L), min_piece_tokens, num_slots, _np_ptr(plan), cap,
-                                       C.byref(c), C.byref(mp)))
+    check(lib().pkv_build_decode_split(len(L), _np_ptr(L), min_piece_tokens, piece_cost_tokens, num_slots,
+                                       _np_ptr(plan), cap, C.byref(c), C.byref(mp)))
     return SplitPlan(plan, int(num_slots), c.value, mp.value)
 
 
@@ -531,6 +541,14 @@ def decode_split_slots(cache_dtype: int, num_kv_heads: int, head_dim: int, block
 def decode_split_workspace_bytes(num_slots: int, num_q_heads: int, head_dim: int, max_pieces: int) -> int:
     """Workspace bytes of a balanced-split launch over num_slots slots (from its SplitPlan)."""
     return int(lib().pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces))
+
+
+def decode_split_workspace(split: SplitPlan, num_q_heads: int, head_dim: int, device="cuda"):
+    """A device workspace for a balanced-split launch of this plan (None when the plan
+    needs none)."""
+    torch = _torch()
+    nb = decode_split_workspace_bytes(split.num_slots, num_q_heads, head_dim, split.max_pieces)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
 
 
 def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split: SplitPlan,
@@ -590,8 +608,8 @@ def _split_args(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, spli
         raise ValueError("q must be [B][Hq][d] without cu_seqlens_q")
     if cu_seqlens_q is not None and (cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (B + 1,)):
         raise ValueError("cu_seqlens_q must be int32 [B + 1]")
-    if plan_dev.dtype != torch.int32 or tuple(plan_dev.shape) != (n + 1 + split.num_slots,):
-        raise ValueError("plan must be int32 [rows + 1 + num_slots] (from build_decode_split)")
+    if plan_dev.dtype != torch.int32 or tuple(plan_dev.shape) != (split_plan_len(n, split.num_slots),):
+        raise ValueError("plan must be int32 [3 rows + 2 num_slots + 2] (from build_decode_split)")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
         raise ValueError("lse must be float32 [rows][Hq]")
     return (_dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),

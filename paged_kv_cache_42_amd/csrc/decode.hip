@@ -118,7 +118,6 @@ struct DecodeArgs {
   int num_work;      // items in `work`
   const int4* work;  // (seq, partition, partitions, end token) per item, or null: grid over all
   const int32_t* plan;   // balanced split: tile offsets [B + 1], then first sequence per slot
-  int tiles_per_slot;    // balanced split: 16-token tiles per workgroup slot
   const int32_t* rows;   // balanced split: batch sequence of each plan row (null: row = sequence)
   const int32_t* cu_q;   // balanced split: the batch's cu_seqlens_q (null: one query row per sequence)
   int num_batch;         // batch sequences (rows of block_tables / seq_lens)
@@ -449,45 +448,13 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   const int hq = blockIdx.x * HW + threadIdx.x / LPH;
   const int e = 4 * (threadIdx.x % LPH);
   if (hq >= num_q_heads) return;
-  int nparts;
-  int orow_idx = s;
-  int first_slot = 0;
-  if (a.plan) {
-    // balanced split: pieces = slots that the sequence's tiles touch. The output row
-    // (a row map lookup) is resolved after the partials' loads are issued, so the two
-    // memory round trips overlap.
-    typedef __attribute__((address_space(4))) const int32_t* cptr;
-    const cptr plan = (cptr)(uintptr_t)(a.plan);
-    const int c0 = plan[s], c1 = plan[s + 1];
-    first_slot = c0 >= 0 ? c0 / a.tiles_per_slot : 0;
-    nparts = c1 > c0 && c0 >= 0 ? (c1 - 1) / a.tiles_per_slot - first_slot + 1 : 0;
-    if (nparts == 1) return;                  // written directly by the split pass
-    // a plan that does not fit this launch (more slots, or split without a workspace)
-    if (nparts > 1 && (first_slot + nparts > a.num_slots || !a.ws_o)) return;
-    if (nparts == 0) {                        // no context: zero output (no piece wrote it)
-      int b;
-      split_row(a, s, b, orow_idx);
-      if (orow_idx < 0) return;
-      const int64_t oi = (int64_t(orow_idx) * num_q_heads + hq) * D + e;
-      if constexpr (QDT == PKV_F32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(0u, 0u);
-      }
-      if (a.lse_out && e == 0) a.lse_out[int64_t(orow_idx) * num_q_heads + hq] = -INFINITY;
-      return;
-    }
-  } else {
-    int L = a.seq_lens[s];
-    L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
-    nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  }
+  const int orow_idx = s;
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;                    // written directly by the partition pass
   const int64_t base = (int64_t(s) * num_q_heads + hq) * a.pmax;
-  // index of piece k's partial
-  auto piece = [&](int k) -> int64_t {
-    return a.plan ? split_partial(first_slot + k, k, num_q_heads, hq) : base + k;
-  };
+  auto piece = [&](int k) -> int64_t { return base + k; };
   float M = -INFINITY, S = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   if (nparts <= kMergeFast) {
@@ -530,11 +497,6 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
       A.w = fmaf(wk, ok.w, A.w);
     }
   }
-  if (a.plan) {
-    int b;
-    split_row(a, s, b, orow_idx);
-    if (orow_idx < 0) return;
-  }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const float r[4] = {A.x * inv, A.y * inv, A.z * inv, A.w * inv};
   const int64_t oi = (int64_t(orow_idx) * num_q_heads + hq) * D + e;
@@ -547,6 +509,74 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
   }
   if (a.lse_out && e == 0)
     a.lse_out[int64_t(orow_idx) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
+}
+
+// Log-sum-exp merge of the sequences a balanced split cut across slots. Each such
+// sequence has a unique first slot j: the one holding its first tile, which it runs past.
+// Workgroup (j, y) takes the sequence that slot j starts and hands on (the sequence holding
+// the first tile of slot j + 1, when it began in slot j), and 256 of its Hq x D / 4 float4
+// output chunks, one per thread: M = max_k lse_k, out = sum_k 2^(lse_k - M) o_k /
+// sum_k 2^(lse_k - M) over its pieces k in slots j .. j + np - 1 (the partials o_k are
+// normalised). Pieces are loaded KB at a time (8, or 32 when some sequence spans more
+// than 8 slots), so a sequence's pieces usually take one memory round trip.
+template <int D, int KB>
+__global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_q_heads) {
+  constexpr int CH = D / 4;
+  typedef __attribute__((address_space(4))) const int32_t* cptr;
+  const int j = blockIdx.x;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int B = a.num_seqs;
+  if (j + 1 >= a.num_slots || c >= num_q_heads * CH || !a.ws_o) return;
+  const cptr plan = (cptr)(uintptr_t)(a.plan);
+  const cptr seq_slots = plan + (B + 1) + 2 * a.num_slots + 1;
+  const int s = plan[B + 1 + j + 1];
+  if (s < 0 || s >= B) return;
+  const int f = seq_slots[2 * s], np = seq_slots[2 * s + 1];
+  if (f != j || np < 2 || f + np > a.num_slots) return;
+  const int hq = c / CH, d0 = 4 * (c % CH);
+  float M = -INFINITY, S = 0.f;
+  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < np; k0 += KB) {
+    float lse[KB];
+    float4 ov[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int kk = k0 + k < np ? k0 + k : k0;
+      const int64_t pi = split_partial(f + kk, kk, num_q_heads, hq);
+      lse[k] = a.ws_lse[pi];
+      ov[k] = *reinterpret_cast<const float4*>(a.ws_o + pi * D + d0);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) Mb = k0 + k < np ? fmaxf(Mb, lse[k]) : Mb;
+    const float mref = Mb == -INFINITY ? 0.f : Mb;
+    const float r = M == -INFINITY ? 0.f : pkv::fast_exp2(M - mref);
+    S *= r;
+    A.x *= r;
+    A.y *= r;
+    A.z *= r;
+    A.w *= r;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const float wk = k0 + k < np ? pkv::fast_exp2(lse[k] - mref) : 0.f;
+      S += wk;
+      A.x = fmaf(wk, ov[k].x, A.x);
+      A.y = fmaf(wk, ov[k].y, A.y);
+      A.z = fmaf(wk, ov[k].z, A.z);
+      A.w = fmaf(wk, ov[k].w, A.w);
+    }
+    M = Mb;
+  }
+  int b, row;
+  split_row(a, s, b, row);
+  if (row < 0) return;
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  const uint32_t lo = pkv::f32_to_bf16(A.x * inv) | (pkv::f32_to_bf16(A.y * inv) << 16);
+  const uint32_t hi = pkv::f32_to_bf16(A.z * inv) | (pkv::f32_to_bf16(A.w * inv) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (int64_t(row) * num_q_heads + hq) * D + d0) =
+      make_uint2(lo, hi);
+  if (a.lse_out && d0 == 0)
+    a.lse_out[int64_t(row) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
 }
 
 // ---------------------------------------------------------------------------------
@@ -682,16 +712,17 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   uint8_t* my_vt = vt_lds[w];
 
   // ---- issue cursor: the piece whose tiles are being loaded. Slot j owns global tiles
-  // [j*C, (j+1)*C) of the sequences' tiles laid end to end; a piece is the part of
-  // one sequence inside that range.
+  // [slot_lo[j], slot_lo[j + 1]) of the sequences' tiles laid end to end; a piece is the
+  // part of one sequence inside that range.
   const int B = a.num_seqs;
   const cptr_i32 plan = (cptr_i32)(uintptr_t)(a.plan);
   const cptr_i32 lens = (cptr_i32)(uintptr_t)(a.seq_lens);
-  const int C = a.tiles_per_slot;
+  const cptr_i32 slot_lo = plan + B + 1 + a.num_slots;
+  const cptr_i32 seq_slots = slot_lo + a.num_slots + 1;          // [B][2]: first slot, pieces
   const int total = plan[B];
-  const int64_t lo64 = int64_t(slot) * C;
-  int t = lo64 < total ? int(lo64) : total;                      // global tile cursor
-  const int hi = lo64 + C < total ? int(lo64 + C) : total;
+  const int lo0 = min(max(slot_lo[slot], 0), total);
+  int t = lo0;                                                   // global tile cursor
+  const int hi = min(max(slot_lo[slot + 1], lo0), total);
   int cs = plan[B + 1 + slot];                                   // current sequence
   cs = cs < 0 ? 0 : (cs > B ? B : cs);
   int cu_cur = plan[cs];
@@ -728,8 +759,8 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     if (row < 0) b = 0;
     int L = lens[b];
     L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
-    const int first = cu_cur / C;
-    const int np = (cu_next - 1) / C - first + 1;
+    const int first = seq_slots[2 * cs];
+    const int np = seq_slots[2 * cs + 1];
     const int p = slot - first;
     // a piece of an inconsistent plan is streamed masked and not written
     const bool valid = row >= 0 && tb >= 0 && cu_cur >= 0 && p >= 0 && p < np &&
@@ -929,6 +960,19 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     }
   };
 
+  // rows without context (no piece anywhere): zero output, log-sum-exp -inf; plan row s
+  // belongs to slot s mod num_slots
+  for (int s0 = slot; s0 < B; s0 += a.num_slots) {
+    if (seq_slots[2 * s0 + 1] != 0) continue;
+    int b, row;
+    split_row(a, s0, b, row);
+    if (row < 0 || hl >= G) continue;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(row) * Hq + g * G + hl) * D + 4 * grp;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) pkv::store_b64_untracked(orow + 16 * mt, 0u, 0u);
+    if (a.lse_out && grp == 0)
+      pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + g * G + hl, __float_as_uint(-INFINITY));
+  }
   if (!more) return;
   // One exit, at the bottom: a tile issued after the stream ran out is masked to nothing
   // (no row is valid, so it changes neither the running sums nor the outputs). An exit
@@ -947,6 +991,11 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
       if (k == 1) live = l;
       consume(k, kb[k], vb[k]);
     }
+    // The waves of the workgroup stream the same tiles (one KV head each) and stay in
+    // step here. Left alone, the older wave on each SIMD wins issue and runs ahead: the
+    // waves of one slot ended up to a quarter of the pass apart, and the last stretch ran
+    // with half of the loads in flight. No memory wait is attached to the barrier.
+    __builtin_amdgcn_s_barrier();
   } while (live);
 }
 
@@ -1218,6 +1267,7 @@ extern "C" int pkv_decode_split_slots(int32_t cache_dtype, int32_t num_kv_heads,
 extern "C" size_t pkv_decode_split_workspace_bytes(int32_t num_slots, int32_t num_q_heads, int32_t head_dim,
                                                    int32_t max_pieces) {
   if (num_slots <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_pieces <= 1) return 0;
+  // partials [S][2][Hq][D] and their log-sum-exps [S][2][Hq], float
   return size_t(2) * num_slots * num_q_heads * (head_dim + 1) * sizeof(float);
 }
 
@@ -1233,6 +1283,20 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
                                                 const int32_t* plan, int32_t num_slots,
                                                 int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
                                                 size_t workspace_bytes, float* lse_out, void* stream) {
+  return pkv::decode_split(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, table_width,
+                           num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                           k_scale, v_scale, k_head_scales, v_head_scales, rows, num_rows, cu_seqlens_q, total_q,
+                           plan, num_slots, tiles_per_slot, max_pieces, workspace, workspace_bytes, lse_out, stream);
+}
+
+int pkv::decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                      int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens, int32_t table_width,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale,
+                      float v_scale, const float* k_head_scales, const float* v_head_scales, const int32_t* rows,
+                      int32_t num_rows, const int32_t* cu_seqlens_q, int32_t total_q, const int32_t* plan,
+                      int32_t num_slots, int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
+                      size_t workspace_bytes, float* lse_out, void* stream) {
   using pkv::fail;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
       max_seq_len < 0)
@@ -1299,19 +1363,21 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
   a.group = G;
   a.num_seqs = num_rows;                      // the plan's rows
   a.plan = plan;
-  a.tiles_per_slot = tiles_per_slot;
   a.rows = rows;
   a.cu_q = cu_seqlens_q;
   a.num_batch = num_seqs;
   a.total_q = total_q;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the pass (which also writes zeros for rows without context), then the merge of the
+  // sequences it cut across slots (none when no sequence spans two slots)
   hipLaunchKernelGGL(fn, dim3(num_kv_heads / hpw, num_slots), dim3(hpw * 64), 0, st, a);
   if (g_profile_event) (void)hipEventRecord(g_profile_event, st);
-  // the merge also writes the zero output of sequences without context
-  MergeFn mf = pick_merge(q_dtype, head_dim);
-  const int heads_per_wg = 256 / (head_dim / 4);
-  hipLaunchKernelGGL(mf, dim3((num_q_heads + heads_per_wg - 1) / heads_per_wg, num_rows), dim3(256), 0, st, a,
-                     num_q_heads);
+  if (need > 0) {
+    const int chunks = num_q_heads * (head_dim / 4);
+    auto mk = max_pieces <= 8 ? (head_dim == 64 ? split_merge_kernel<64, 8> : split_merge_kernel<128, 8>)
+                              : (head_dim == 64 ? split_merge_kernel<64, 32> : split_merge_kernel<128, 32>);
+    hipLaunchKernelGGL(mk, dim3(num_slots, (chunks + 255) / 256), dim3(256), 0, st, a, num_q_heads);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_split: launch failed: %s", hipGetErrorString(e));
   return PKV_OK;

@@ -70,10 +70,9 @@ extern "C" int pkv_paged_attention_decode_split_noalloc(
     const int rc = scratch_on_current_device(&ws);
     if (rc != PKV_OK) return rc;
   }
-  return pkv_paged_attention_decode_split(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens,
-                                          table_width, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                          num_blocks, max_seq_len, scale, k_scale, v_scale, k_head_scales,
-                                          v_head_scales, rows, num_rows, cu_seqlens_q, total_q, plan, num_slots,
-                                          tiles_per_slot, max_pieces, ws, need > 0 ? kNoAllocScratchBytes : 0,
-                                          lse_out, stream);
+  return pkv::decode_split(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, table_width,
+                           num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                           k_scale, v_scale, k_head_scales, v_head_scales, rows, num_rows, cu_seqlens_q, total_q,
+                           plan, num_slots, tiles_per_slot, max_pieces, ws, need > 0 ? kNoAllocScratchBytes : 0,
+                           lse_out, stream);
 }

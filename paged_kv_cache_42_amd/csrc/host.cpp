@@ -367,44 +367,92 @@ int pkv_build_decode_work(int32_t num_seqs, const int32_t* seq_lens, int32_t par
   return PKV_OK;
 }
 
-int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t min_piece_tokens, int32_t num_slots,
-                           int32_t* plan, int32_t capacity, int32_t* tiles_per_slot, int32_t* max_pieces) {
-  if (num_seqs < 0 || min_piece_tokens < 0 || num_slots < 1 || !tiles_per_slot || !max_pieces ||
-      (num_seqs > 0 && !seq_lens))
+int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t min_piece_tokens,
+                           int32_t piece_cost_tokens, int32_t num_slots, int32_t* plan, int32_t capacity,
+                           int32_t* tiles_per_slot, int32_t* max_pieces) {
+  if (num_seqs < 0 || min_piece_tokens < 0 || piece_cost_tokens < 0 || num_slots < 1 || !tiles_per_slot ||
+      !max_pieces || (num_seqs > 0 && !seq_lens))
     return fail(PKV_ERR_INVALID, "build_decode_split: bad arguments");
-  const int64_t need = int64_t(num_seqs) + 1 + num_slots;
+  const int64_t B = num_seqs, S = num_slots;
+  const int64_t need = 3 * B + 2 * S + 2;
   if (need > capacity || !plan)
     return fail(PKV_ERR_INVALID, "build_decode_split: plan needs %lld entries, capacity %d", (long long)need,
                 capacity);
+  int32_t* cu = plan;                      // [B + 1] tile offsets
+  int32_t* first_seq = plan + B + 1;       // [S] first sequence with a tile at or past the slot's start
+  int32_t* slot_lo = first_seq + S;        // [S + 1] first tile of each slot, then the total
+  int32_t* seq_slots = slot_lo + S + 1;    // [B][2] first slot and number of pieces of each sequence
   // tile offsets of the sequences laid end to end (16-token tiles, the last one partial)
-  int64_t total = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
+  int64_t total = 0, nonempty = 0;
+  cu[0] = 0;
+  for (int64_t s = 0; s < B; ++s) {
     const int64_t L = seq_lens[s] < 0 ? 0 : seq_lens[s];
     total += (L + 15) / 16;
+    nonempty += L > 0;
     if (total > INT32_MAX - 1) return fail(PKV_ERR_INVALID, "build_decode_split: context too long");
+    cu[s + 1] = int32_t(total);
   }
-  int64_t C = (total + num_slots - 1) / num_slots;
-  C = std::max<int64_t>(C, (int64_t(min_piece_tokens) + 15) / 16);
-  C = std::max<int64_t>(C, 1);
-  int32_t* cu = plan;
-  int32_t* first_seq = plan + num_seqs + 1;
-  int64_t acc = 0;
+  // Slot boundaries. A slot's time is modelled as its tiles plus `alpha` tiles for each
+  // piece (a sequence, or part of one, it enters: queries, table row, softmax state and
+  // the output or partial at the end). Slots are filled in stream order, each up to the
+  // remaining cost divided by the remaining slots, so every slot ends near the same time
+  // whatever the length mix. Slots past the active count (the context split into pieces
+  // of at least min_piece_tokens) stay empty.
+  const double alpha = piece_cost_tokens / 16.0;
+  const int64_t min_tiles = std::max<int64_t>(1, (int64_t(min_piece_tokens) + 15) / 16);
+  const int64_t active = total > 0 ? std::max<int64_t>(1, std::min<int64_t>(S, total / min_tiles)) : 0;
+  int64_t j = 0;                           // slot being filled
+  double cost = 0.0;                       // its cost so far
+  int64_t seqs_left = nonempty;            // sequences not yet started
+  slot_lo[0] = 0;
+  for (int64_t s = 0; s < B && active > 0; ++s) {
+    int64_t t = cu[s], end = cu[s + 1];
+    if (t == end) continue;
+    --seqs_left;
+    while (t < end) {
+      if (j == active - 1) {               // the last active slot takes the rest
+        t = end;
+        break;
+      }
+      const double rem = cost + double(total - t) + alpha * double(1 + seqs_left + (active - 1 - j));
+      const double room = rem / double(active - j) - cost - alpha;
+      if (room < 0.5 && cost > 0.0) {      // full: the sequence starts in the next slot
+        slot_lo[++j] = int32_t(t);
+        cost = 0.0;
+        continue;
+      }
+      const int64_t take = std::min<int64_t>(end - t, std::max<int64_t>(1, std::llround(room)));
+      cost += alpha + double(take);
+      t += take;
+      if (t < end) {                       // the sequence continues in the next slot
+        slot_lo[++j] = int32_t(t);
+        cost = 0.0;
+      }
+    }
+  }
+  for (int64_t k = j + 1; k <= S; ++k) slot_lo[k] = int32_t(total);
+  // first sequence of each slot, and each sequence's slots
+  int64_t s = 0, widest = 0;
+  for (int64_t k = 0; k < S; ++k) {
+    while (s < B && cu[s + 1] <= slot_lo[k]) ++s;
+    first_seq[k] = int32_t(s);
+    widest = std::max<int64_t>(widest, slot_lo[k + 1] - slot_lo[k]);
+  }
   int32_t pieces_max = 0;
-  int32_t s = 0;
-  cu[0] = 0;
-  for (int32_t i = 0; i < num_seqs; ++i) {
-    const int64_t L = seq_lens[i] < 0 ? 0 : seq_lens[i];
-    const int64_t nt = (L + 15) / 16;
-    if (nt > 0) pieces_max = std::max<int32_t>(pieces_max, int32_t((acc + nt - 1) / C - acc / C + 1));
-    acc += nt;
-    cu[i + 1] = int32_t(acc);
+  int64_t k = 0;                           // slot holding tile cu[s]
+  for (s = 0; s < B; ++s) {
+    while (k + 1 < S && slot_lo[k + 1] <= cu[s]) ++k;
+    int64_t np = 0;
+    if (cu[s + 1] > cu[s]) {
+      int64_t last = k;
+      while (last + 1 < S && slot_lo[last + 1] < cu[s + 1]) ++last;
+      np = last - k + 1;
+    }
+    seq_slots[2 * s] = int32_t(k);
+    seq_slots[2 * s + 1] = int32_t(np);
+    pieces_max = std::max<int32_t>(pieces_max, int32_t(np));
   }
-  for (int32_t j = 0; j < num_slots; ++j) {
-    const int64_t lo = int64_t(j) * C;
-    while (s < num_seqs && cu[s + 1] <= lo) ++s;     // first sequence with a tile at or past lo
-    first_seq[j] = s;
-  }
-  *tiles_per_slot = int32_t(C);
+  *tiles_per_slot = int32_t(std::max<int64_t>(widest, 1));
   *max_pieces = pieces_max;
   return PKV_OK;
 }

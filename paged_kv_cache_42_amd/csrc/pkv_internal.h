@@ -1,6 +1,7 @@
 // Internal helpers shared by libpkv's host code and HIP kernels (not part of the ABI).
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pkv {
@@ -24,6 +25,16 @@ int head_scales(const char* who, int32_t num_kv_heads, float scale, float k_scal
 // Cache-write inverses per KV head: ki[h] = fl32(1 / (k_scale * k_head[h])), likewise vi.
 int head_inverse_scales(const char* who, int32_t num_kv_heads, float k_scale, float v_scale,
                         const float* k_head, const float* v_head, float* ki, float* vi);
+
+// pkv_paged_attention_decode_split (the no-allocation entry point reuses it).
+int decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                 int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens, int32_t table_width,
+                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                 const float* k_head_scales, const float* v_head_scales, const int32_t* rows, int32_t num_rows,
+                 const int32_t* cu_seqlens_q, int32_t total_q, const int32_t* plan, int32_t num_slots,
+                 int32_t tiles_per_slot, int32_t max_pieces, void* workspace, size_t workspace_bytes,
+                 float* lse_out, void* stream);
 
 }  // namespace pkv
 

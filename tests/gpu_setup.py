@@ -221,8 +221,7 @@ def run_decode_split(st: Step, num_slots: Optional[int] = None, min_piece_tokens
     split = pkv.build_decode_split(w.seq_lens if plan_lens is None else plan_lens, num_slots, min_piece_tokens)
     plan_d = torch.from_numpy(split.plan).cuda()
     out = torch.full((B, Hq, d), float("nan"), dtype=torch_dtype(w.dtype), device="cuda")
-    nb = pkv.decode_split_workspace_bytes(split.num_slots, Hq, d, split.max_pieces)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+    ws = pkv.decode_split_workspace(split, Hq, d)
     lse_t = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
     pkv.paged_attention_decode_split(out, st.q if q is None else q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, plan_d, split,
                                      w.num_kv_heads, w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale,
@@ -276,8 +275,7 @@ def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_to
     out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse_t = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
     if len(mp.decode_rows):
-        nb = pkv.decode_split_workspace_bytes(mp.split.num_slots, Hq, d, mp.split.max_pieces)
-        ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+        ws = pkv.decode_split_workspace(mp.split, Hq, d)
         pkv.paged_attention_decode_split(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d,
                                          torch.from_numpy(mp.split.plan).cuda(), mp.split, w.num_kv_heads,
                                          w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, ws, lse_t,

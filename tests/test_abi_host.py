@@ -168,39 +168,70 @@ def test_decode_work_list_covers_every_partition_once(lens, P):
             raise pkv.PkvError(-1, "empty")
 
 
-@settings(max_examples=80, deadline=None)
-@given(st.lists(st.integers(0, 3000), max_size=30), st.integers(1, 300), st.sampled_from([0, 16, 100, 512]))
-def test_balanced_split_plan_covers_every_tile_once(lens, slots, min_piece):
-    sp = pkv.build_decode_split(lens, slots, min_piece)
-    B = len(lens)
-    cu, first = sp.plan[:B + 1], sp.plan[B + 1:]
+@settings(max_examples=120, deadline=None)
+@given(st.lists(st.integers(0, 3000), max_size=30), st.integers(1, 300), st.sampled_from([0, 16, 100, 512]),
+       st.sampled_from([0, 11, 22, 44, 88]))
+def test_balanced_split_plan_covers_every_tile_once(lens, slots, min_piece, piece_cost):
+    sp = pkv.build_decode_split(lens, slots, min_piece, piece_cost)
+    B, S = len(lens), slots
+    assert sp.plan.shape == (3 * B + 2 * S + 2,)
+    cu, first = sp.plan[:B + 1], sp.plan[B + 1:B + 1 + S]
+    lo, seq_slots = sp.plan[B + 1 + S:B + 2 + 2 * S], sp.plan[B + 2 + 2 * S:].reshape(B, 2)
     tiles = [-(-L // 16) for L in lens]
     assert cu.tolist() == np.concatenate([[0], np.cumsum(tiles, dtype=np.int64)]).astype(np.int64).tolist()
     total = int(cu[-1])
-    C = sp.tiles_per_slot
-    assert C >= max(1, -(-min_piece // 16)) and C >= -(-total // slots)
-    assert C == max(1, -(-min_piece // 16), -(-total // slots))
+    # boundaries: from 0 to the total, non-decreasing; the first `active` slots non-empty
+    min_tiles = max(1, -(-min_piece // 16))
+    active = max(1, min(S, total // min_tiles)) if total else 0
+    assert lo[0] == 0 and lo[S] == total and (np.diff(lo) >= 0).all()
+    used = int((np.diff(lo) > 0).sum())                     # non-empty slots come first
+    assert 1 <= used <= active if total else used == 0
+    assert (np.diff(lo)[:used] > 0).all() and (np.diff(lo)[used:] == 0).all()
+    assert sp.tiles_per_slot == max(1, int(np.diff(lo).max()) if S else 1)
     # walk the slots as the kernel does; every tile of every sequence lands in exactly one piece
     seen = [np.zeros(t, np.int32) for t in tiles]
     pieces = [0] * B
-    for j in range(slots):
-        lo, hi = min(j * C, total), min((j + 1) * C, total)
+    first_slot = [-1] * B
+    cost = []
+    for j in range(S):
+        a, b = int(lo[j]), int(lo[j + 1])
         s = int(first[j])
-        assert all(cu[i + 1] <= lo for i in range(s)) and (s == B or cu[s + 1] > lo or lo >= total)
-        t = lo
-        while t < hi:
+        assert all(cu[i + 1] <= a for i in range(s)) and (s == B or cu[s + 1] > a or a >= total)
+        t, n = a, 0
+        while t < b:
             while s < B and cu[s + 1] <= t:
                 s += 1
-            pe = min(hi, int(cu[s + 1]))
+            pe = min(b, int(cu[s + 1]))
             seen[s][t - cu[s]:pe - cu[s]] += 1
+            if pieces[s] == 0:
+                first_slot[s] = j
             pieces[s] += 1
-            assert j - int(cu[s]) // C == pieces[s] - 1            # piece index = slot - first slot
+            assert j - first_slot[s] == pieces[s] - 1            # piece index = slot - first slot
+            n += 1
             t = pe
+        if b > a:
+            cost.append((b - a) + n * piece_cost / 16)
     assert all((x == 1).all() for x in seen)
     assert sp.max_pieces == max([p for p in pieces] + [0])
-    for s, p in enumerate(pieces):
+    for s in range(B):
+        assert seq_slots[s, 1] == pieces[s]
         if tiles[s]:
-            assert p == (int(cu[s + 1]) - 1) // C - int(cu[s]) // C + 1
+            assert seq_slots[s, 0] == first_slot[s]
+    # balance: no slot costs more than the mean plus one piece and one tile
+    if cost:
+        assert max(cost) <= np.mean(cost) + piece_cost / 16 + 1 + 1e-9
+
+
+def test_piece_cost_evens_out_slots_crossing_many_sequences():
+    # short sequences first, one long one after: with a piece cost the slots over the
+    # short ones take fewer tiles than those inside the long one
+    lens = [40] * 200 + [20000]
+    sp0 = pkv.build_decode_split(lens, 16, 0, 0)
+    sp1 = pkv.build_decode_split(lens, 16, 0, 44)
+    B, S = len(lens), 16
+    lo0, lo1 = sp0.plan[B + 1 + S:B + 2 + 2 * S], sp1.plan[B + 1 + S:B + 2 + 2 * S]
+    assert np.ptp(np.diff(lo0)) <= 1                       # no piece cost: equal tiles
+    assert np.diff(lo1)[0] < np.diff(lo1)[-1]              # with it: the crowded slot is shorter
 
 
 def test_balanced_split_plan_errors():
@@ -209,8 +240,8 @@ def test_balanced_split_plan_errors():
     out = np.zeros(3, np.int32)
     c, m = ctypes.c_int32(), ctypes.c_int32()
     L = np.array([10, 20], np.int32)
-    with pytest.raises(pkv.PkvError):     # capacity below num_seqs + 1 + num_slots
-        _lib.check(pkv.lib().pkv_build_decode_split(2, L.ctypes.data_as(ctypes.c_void_p), 0, 4,
+    with pytest.raises(pkv.PkvError):     # capacity below 3 num_seqs + 2 num_slots + 2
+        _lib.check(pkv.lib().pkv_build_decode_split(2, L.ctypes.data_as(ctypes.c_void_p), 0, 22, 4,
                                                     out.ctypes.data_as(ctypes.c_void_p), 3, ctypes.byref(c),
                                                     ctypes.byref(m)))
 

@@ -143,8 +143,7 @@ def test_repeated_calls_on_one_workspace_agree():
     split = pkv.build_decode_split(w.seq_lens, 9)
     assert split.max_pieces > 1
     plan_d = torch.from_numpy(split.plan).cuda()
-    nb = pkv.decode_split_workspace_bytes(split.num_slots, Hq, d, split.max_pieces)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws = pkv.decode_split_workspace(split, Hq, d)
     first = None
     for i in range(4):
         out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -158,3 +157,4 @@ def test_repeated_calls_on_one_workspace_agree():
         if first is None:
             first = o
         assert (o == first).all(), f"call {i} differs from call 0"
+        ws.fill_(0x7F)                         # stale partials never leak into the next call

@@ -104,6 +104,9 @@ class Replay:
         self.slots = pkv.decode_split_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.num_kv_heads,
                                             tr.head_dim, tr.block_size)
         self.min_piece = 256
+        # the split decode's workspace (its size depends only on the slots and the heads)
+        self.split_ws = torch.empty(pkv.decode_split_workspace_bytes(self.slots, tr.num_q_heads, tr.head_dim, 2),
+                                    dtype=torch.uint8, device="cuda")
         self.chunk_slots = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim,
                                            tr.block_size) if chunk_cut else 0
         self.min_piece_tiles = min_piece_tiles
@@ -175,9 +178,7 @@ class Replay:
         if len(mp.decode_rows):
             rows = torch.from_numpy(mp.decode_rows).cuda()
             plan_d = torch.from_numpy(mp.split.plan).cuda()
-            nb = pkv.decode_split_workspace_bytes(mp.split.num_slots, tr.num_q_heads, tr.head_dim,
-                                                  mp.split.max_pieces)
-            ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+            ws = self.split_ws if mp.split.max_pieces > 1 else None
         msl = int(seq_lens.max())
         out = torch.empty((T, tr.num_q_heads, tr.head_dim), dtype=torch.bfloat16, device="cuda")
         kept = {}
