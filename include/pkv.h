@@ -395,7 +395,7 @@ int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype
                                        void* workspace, int64_t workspace_bytes, float* lse_out,
                                        void* stream);
 
-/* Continuous-batching scheduler step (host) over a pool ([CB] "2. Why does it exist?",
+/* Continuous-batching scheduler step (host) over a pool ([CB] "4. Tiny example",
  * the engine loop: admit, one mixed forward pass, update; [CB] "5. Technical
  * explanation", preemption by recompute). Each request's id is its sequence id in the
  * pool (the scheduler reserves and releases its table). One step is:

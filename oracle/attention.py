@@ -20,7 +20,8 @@ where that sketch is garbled or silent:
 
 `attend` is the plain definition over contiguous (gathered) K/V; `paged_attention`
 gathers each sequence's rows through its block table and calls it;
-`paged_attention_literal` is the page-by-page loop for tiny shapes; and
+`paged_attention_literal` evaluates the same definition token by token through the
+page table, in pure Python, for tiny shapes; and
 `split_merge` evaluates fixed-length context partitions and merges them by
 log-sum-exp, which equals `attend` algebraically.
 """
@@ -96,37 +97,31 @@ def paged_attention(q: np.ndarray, k_plane: np.ndarray, v_plane: np.ndarray, cac
 def paged_attention_literal(query: np.ndarray, page_table, k_plane: np.ndarray,
                             v_plane: np.ndarray, cache_dtype: str, seq_len: int,
                             group: int, scale: Optional[float] = None):
-    """Decode attention of one query [Hq][d] by walking pages and slots, per head.
+    """Decode attention of one query [Hq][d] evaluated token by token from the
+    definition, reading each key and value through the page table: token t of the
+    sequence is row t % block_size of physical block page_table[t // block_size]. Per
+    query head h (KV head h // group): z_t = scale * q_h . K_t for every t < seq_len,
+    weights w_t = exp(z_t - max z) / sum exp(z - max z), out_h = sum_t w_t V_t.
 
-    Slow by design (pure Python loops); for tiny shapes only."""
+    Slow by design (pure Python arithmetic); for tiny shapes only."""
     Hq, d = query.shape
     bs = k_plane.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    where = [(int(page_table[t // bs]), t % bs) for t in range(int(seq_len))]
     out = np.zeros((Hq, d), np.float64)
     for h in range(Hq):
         g = h // group
-        scores = []
-        for logical, page in enumerate(page_table):
-            start = logical * bs
-            end = min(start + bs, seq_len)
-            for t in range(start, end):
-                k = cache.decode_plane(k_plane[page, t - start, g], cache_dtype)
-                scores.append(sum(float(a) * float(b) for a, b in zip(query[h], k)) * scale)
-        if not scores:
+        K = [cache.decode_plane(k_plane[blk, off, g], cache_dtype) for blk, off in where]
+        V = [cache.decode_plane(v_plane[blk, off, g], cache_dtype) for blk, off in where]
+        if not K:
             continue
-        m = max(scores)
-        ex = [math.exp(z - m) for z in scores]
-        tot = sum(ex)
-        w = [e / tot for e in ex]
-        t_idx = 0
-        for logical, page in enumerate(page_table):
-            start = logical * bs
-            end = min(start + bs, seq_len)
-            for t in range(start, end):
-                v = cache.decode_plane(v_plane[page, t - start, g], cache_dtype)
-                out[h] += w[t_idx] * v
-                t_idx += 1
+        z = [scale * math.fsum(float(a) * float(b) for a, b in zip(query[h], k)) for k in K]
+        zmax = max(z)
+        e = [math.exp(zt - zmax) for zt in z]
+        tot = math.fsum(e)
+        for j in range(d):
+            out[h, j] = math.fsum(et / tot * float(v[j]) for et, v in zip(e, V))
     return out
 
 

@@ -2,7 +2,7 @@
 the smoke check and the benchmark's CPU baseline may use it; the product never does).
 
 The policy is the engine loop of "Continuous Batching" (infra.pidoku inference
-notes), section "2. Why does it exist?" (the Go `Engine.Step` with `preempt`), with
+notes), section "4. Tiny example" (the Go `Engine.Step` with `preempt`), with
 the lifecycle of its section "1. What is it?" and the recompute preemption of
 "5. Technical explanation":
 

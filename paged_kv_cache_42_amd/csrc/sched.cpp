@@ -1,7 +1,7 @@
 // Host scheduler step of continuous batching, on top of the block pool.
 //
 // The loop is the engine step of "Continuous Batching" (infra.pidoku inference notes),
-// section "2. Why does it exist?" (admit from the head of the waiting queue while a slot
+// section "4. Tiny example" (admit from the head of the waiting queue while a slot
 // and the blocks are free, stopping at the first request that does not fit; run one
 // mixed forward pass over every running request; then, in running order, append one
 // output token, free a finished request's blocks at once, give a request that needs one

@@ -1,5 +1,5 @@
 """The scheduler oracle against traces worked out by hand from the engine loop of
-"Continuous Batching" ("2. Why does it exist?", the Go Engine.Step and preempt), and
+"Continuous Batching" ("4. Tiny example", the Go Engine.Step and preempt), and
 against invariants on random and full-size traces. Beyond these the scheduler is
 parity unpinned: the pages print no trace of the loop."""
 import numpy as np
