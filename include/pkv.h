@@ -359,6 +359,25 @@ int pkv_build_chunk_work(int32_t num_seqs, const int32_t* q_lens, const int32_t*
                          int32_t capacity, int32_t* count, int32_t* merges, int32_t merge_capacity,
                          int32_t* merge_count, int32_t* num_partials);
 
+/* Host plan of a mixed step ([CB] "5. Technical explanation", mixed batching): the
+ * sequences with exactly one new token (decode rows) are listed in batch order in
+ * decode_rows (host int32, capacity num_seqs; *num_decode = their count) and get a
+ * balanced split plan over num_slots as pkv_build_decode_split would build from their
+ * seq_lens (plan, plan_capacity >= 3 * num_seqs + 2 * num_slots + 2, *tiles_per_slot,
+ * *max_pieces; left untouched, with both outputs 0, when there is no decode row); the
+ * sequences with two or more get the chunk work of pkv_build_chunk_work (items ..
+ * num_partials, same meaning and capacities). The decode rows go to
+ * pkv_paged_attention_decode_split as its row map, the chunk work to
+ * pkv_paged_attention_prefill_chunks. Errors as for the two builders. */
+int pkv_build_mixed_step(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
+                         int32_t num_kv_heads, int32_t group, int32_t num_slots,
+                         int32_t min_piece_tokens, int32_t piece_cost_tokens, int32_t chunk_slots,
+                         int32_t min_piece_tiles, int32_t* decode_rows, int32_t* num_decode,
+                         int32_t* plan, int32_t plan_capacity, int32_t* tiles_per_slot,
+                         int32_t* max_pieces, int32_t* items, int32_t capacity, int32_t* count,
+                         int32_t* merges, int32_t merge_capacity, int32_t* merge_count,
+                         int32_t* num_partials);
+
 /* Slots to balance chunk work over on the current device (its compute units: a second
  * resident workgroup shares a unit's issue slots, so it adds little throughput): the
  * num_slots of pkv_build_chunk_work. UNSUPPORTED for a cache dtype / head_dim /

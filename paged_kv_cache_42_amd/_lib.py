@@ -64,6 +64,8 @@ _SIGS = {
                                                      i32, vp, i64, vp, vp]),
     "pkv_build_chunk_work": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, vp, i32, P_i32, vp, i32, P_i32, P_i32]),
     "pkv_chunk_slots": (C.c_int, [i32, i32, i32, P_i32]),
+    "pkv_build_mixed_step": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, P_i32, vp, i32, P_i32,
+                                       P_i32, vp, i32, P_i32, vp, i32, P_i32, P_i32]),
     "pkv_chunk_workspace_bytes": (i64, [i32, i32]),
     "pkv_swap_workspace_bytes": (i64, [i32, i32, i64]),
     "pkv_swap_out": (C.c_int, [vp, vp, i32, i32, i64, vp, vp, i32, vp, i32, vp, i64, vp, vp]),
@@ -701,16 +703,35 @@ class MixedPlan:
 
 
 def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots: int,
-                     min_piece_tokens: int = 0, chunk_slots: int = 0, min_piece_tiles: int = 0) -> MixedPlan:
-    """Split a mixed step's rows: sequences with exactly one new token go to a balanced
+                     min_piece_tokens: int = 0, chunk_slots: int = 0, min_piece_tiles: int = 0,
+                     piece_cost_tokens: int = SPLIT_PIECE_COST_TOKENS) -> MixedPlan:
+    """libpkv's mixed-step plan: sequences with exactly one new token go to a balanced
     split plan over num_slots (rows in batch order), those with more to the chunk work list
     (cut along the keys over chunk_slots resident workgroups, 0: uncut)."""
     q = np.ascontiguousarray(q_lens, dtype=np.int32)
     L = np.ascontiguousarray(seq_lens, dtype=np.int32)
-    dec = np.nonzero(q == 1)[0].astype(np.int32)
-    split = build_decode_split(L[dec], num_slots, min_piece_tokens) if len(dec) else None
-    chunks = build_chunk_work(q, L, num_kv_heads, group, chunk_slots, min_piece_tiles)
-    return MixedPlan(dec, split, chunks)
+    B = len(q)
+    dec = np.zeros(max(B, 1), np.int32)
+    plan = np.zeros(split_plan_len(B, num_slots), np.int32)
+    nd, c, mp = i32(), i32(), i32()
+    n, m, p = i32(), i32(), i32()
+    cap, mcap = 64, 16
+    while True:
+        items = np.zeros((cap, 8), np.int32)
+        merges = np.zeros((mcap, 4), np.int32)
+        st = lib().pkv_build_mixed_step(B, _np_ptr(q), _np_ptr(L), num_kv_heads, group, num_slots, min_piece_tokens,
+                                        piece_cost_tokens, chunk_slots, min_piece_tiles, _np_ptr(dec), C.byref(nd),
+                                        _np_ptr(plan), len(plan), C.byref(c), C.byref(mp), _np_ptr(items), cap,
+                                        C.byref(n), _np_ptr(merges), mcap, C.byref(m), C.byref(p))
+        if st == PKV_OK:
+            break
+        if st != PKV_ERR_INVALID or (n.value <= cap and m.value <= mcap):
+            check(st)
+        cap, mcap = max(cap, n.value), max(mcap, m.value)
+    k = nd.value
+    split = SplitPlan(plan[:split_plan_len(k, num_slots)].copy(), int(num_slots), c.value, mp.value) if k else None
+    chunks = ChunkPlan(items[:n.value].copy(), merges[:m.value].copy(), p.value)
+    return MixedPlan(dec[:k].copy(), split, chunks)
 
 
 def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,

@@ -29,6 +29,33 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# The kernels issue some global stores as inline assembly that the compiler's wait-count
+# and hazard passes do not see (mfma_common.h); that they stay correct was checked on
+# the output of this compiler release. Another release may schedule differently, so the
+# build refuses it unless PKV_ALLOW_UNCHECKED_COMPILER=1 (then rerun the GPU tests,
+# test_small_mixed_steps with 5000 chunk slots in particular, before trusting results).
+CHECKED_COMPILER = ("HIP version: 7.2.", "AMD clang version 22.")
+
+
+def compiler_version() -> str:
+    r = subprocess.run([HIPCC, "--version"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def check_compiler() -> str:
+    """The hipcc version text; raises unless it is the release the kernels were checked on."""
+    text = compiler_version()
+    lines = text.splitlines()
+    ok = all(any(line.startswith(p) for line in lines) for p in CHECKED_COMPILER)
+    if not ok and os.environ.get("PKV_ALLOW_UNCHECKED_COMPILER") != "1":
+        raise RuntimeError(
+            "libpkv's inline-assembly stores were checked with " + " / ".join(CHECKED_COMPILER) +
+            f"*, not with:\n{text}\nSet PKV_ALLOW_UNCHECKED_COMPILER=1 to build anyway, then rerun the GPU tests.")
+    if not ok:
+        print(f"warning: building libpkv with an unchecked compiler:\n{text}", file=sys.stderr)
+    return text
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
@@ -50,6 +77,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
+    version = check_compiler()
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
@@ -63,6 +91,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(LIB + ".buildinfo", "w") as f:      # which compiler made this library
+        f.write(version + "\n")
     return LIB
 
 

@@ -457,4 +457,34 @@ int pkv_build_decode_split(int32_t num_seqs, const int32_t* seq_lens, int32_t mi
   return PKV_OK;
 }
 
+int pkv_build_mixed_step(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens, int32_t num_kv_heads,
+                         int32_t group, int32_t num_slots, int32_t min_piece_tokens, int32_t piece_cost_tokens,
+                         int32_t chunk_slots, int32_t min_piece_tiles, int32_t* decode_rows, int32_t* num_decode,
+                         int32_t* plan, int32_t plan_capacity, int32_t* tiles_per_slot, int32_t* max_pieces,
+                         int32_t* items, int32_t capacity, int32_t* count, int32_t* merges, int32_t merge_capacity,
+                         int32_t* merge_count, int32_t* num_partials) {
+  if (num_seqs < 0 || (num_seqs > 0 && (!q_lens || !seq_lens || !decode_rows)) || !num_decode || !tiles_per_slot ||
+      !max_pieces)
+    return fail(PKV_ERR_INVALID, "build_mixed_step: bad arguments");
+  // decode rows: the sequences with exactly one new token, in batch order
+  std::vector<int32_t> lens;
+  int32_t n = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (q_lens[s] != 1) continue;
+    decode_rows[n++] = s;
+    lens.push_back(seq_lens[s]);
+  }
+  *num_decode = n;
+  *tiles_per_slot = 0;
+  *max_pieces = 0;
+  if (n > 0) {
+    const int rc = pkv_build_decode_split(n, lens.data(), min_piece_tokens, piece_cost_tokens, num_slots, plan,
+                                          plan_capacity, tiles_per_slot, max_pieces);
+    if (rc != PKV_OK) return rc;
+  }
+  // the rows of sequences with two or more new tokens
+  return pkv_build_chunk_work(num_seqs, q_lens, seq_lens, num_kv_heads, group, chunk_slots, min_piece_tiles, items,
+                              capacity, count, merges, merge_capacity, merge_count, num_partials);
+}
+
 }  // extern "C"

@@ -353,3 +353,23 @@ def test_swap_copy_argument_errors_enqueue_nothing():
         assert call(fn, ok_dev, ok_host, bb=4100) == _lib.PKV_ERR_INVALID                # not a multiple of 16
         assert call(fn, ok_dev, ok_host, n=-1) == _lib.PKV_ERR_INVALID
         assert call(fn, ok_dev, ok_host, n=0) == _lib.PKV_OK                             # no-op
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 3), st.integers(0, 2500)), max_size=24), st.integers(1, 300),
+       st.sampled_from([0, 5, 64]), st.sampled_from([1, 4, 8]))
+def test_mixed_step_plan_is_the_decode_split_plus_the_chunk_work(pairs, slots, chunk_slots, G):
+    q = np.array([a for a, _ in pairs], np.int32)
+    L = q + np.array([b for _, b in pairs], np.int32)
+    mp = pkv.build_mixed_step(q, L, 2, G, slots, 0, chunk_slots, 0)
+    dec = np.nonzero(q == 1)[0]
+    assert mp.decode_rows.tolist() == dec.tolist()            # batch order
+    if len(dec):
+        ref = pkv.build_decode_split(L[dec], slots, 0)
+        assert mp.split.plan.tolist() == ref.plan.tolist()
+        assert (mp.split.tiles_per_slot, mp.split.max_pieces) == (ref.tiles_per_slot, ref.max_pieces)
+    else:
+        assert mp.split is None
+    cw = pkv.build_chunk_work(q, L, 2, G, chunk_slots, 0)
+    assert mp.chunks.items.tolist() == cw.items.tolist() and mp.chunks.merges.tolist() == cw.merges.tolist()
+    assert mp.chunks.num_partials == cw.num_partials
