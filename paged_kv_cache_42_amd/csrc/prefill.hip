@@ -49,8 +49,10 @@ constexpr bf16x2_t kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)
 constexpr float kLazy = 8.f;       // log2 headroom of the lazy softmax maximum
 constexpr int kRows = 128;         // query rows (token, head) of an item
 constexpr int kKeys = 64;          // keys per LDS tile
-constexpr int kWaves = 4;          // 32 rows each
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;          // waves of a group, 32 rows each
+constexpr int kGroups = 2;         // groups of a workgroup, each over half of the item's key tiles
+constexpr int kGroupThreads = 64 * kWaves;
+constexpr int kThreads = kGroupThreads * kGroups;
 
 struct ChunkArgs {
   const uint16_t* q;      // [total_q][Hq][D] bf16
@@ -80,20 +82,25 @@ template <int D>
 struct Lds {
   static constexpr int RS = D * 2 + 32;          // bytes per bf16 key row (padded)
   static constexpr int kTile = kKeys * RS;       // one K or V tile
-  static constexpr int kBytes = 4 * kTile;       // K, V x double buffer
+  static constexpr int kGroupBytes = 4 * kTile;  // K, V x double buffer, per group
+  static constexpr int kBytes = kGroups * kGroupBytes;
+  // the hand-over of a group's row states at the end: o [waves][2][D/16][64] float4, then
+  // m and the lane sums [waves][2][64] float each
+  static constexpr int kXchg = kWaves * 2 * (D / 16) * 64 * 16 + 2 * kWaves * 2 * 64 * 4;
+  static_assert(kXchg <= kBytes, "exchange fits in the tile buffers");
 };
 
 template <int CDT, int D, int BS>
-__global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
+__global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
   constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
   constexpr int RS = Lds<D>::RS;
   constexpr int TILE = Lds<D>::kTile;
   constexpr int CPK = D * EB / 16;                       // 16-byte chunks per key head row
-  constexpr int LPT = kKeys * CPK / kThreads;            // chunk loads per thread per plane
+  constexpr int LPT = kKeys * CPK / kGroupThreads;       // chunk loads per thread per plane
   constexpr int NB = kKeys / BS;                         // blocks per tile
-  static_assert(kKeys * CPK % kThreads == 0 && LPT >= 1, "tile / workgroup shape");
+  static_assert(kKeys * CPK % kGroupThreads == 0 && LPT >= 1, "tile / workgroup shape");
   static_assert(LPT <= 32, "mask word");
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D>::kBytes];
   typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
@@ -119,9 +126,14 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   const int key_lo = it.w;
   if (key_lo < 0 || key_lo % kKeys != 0) return;
 
-  const int tid = threadIdx.x;
+  // the two groups take the first and the second half of the item's key tiles; each
+  // has its own LDS buffers, and group 1 hands its row states to group 0 at the end
+  // (group and wave indices go through readfirstlane so that the compiler sees them, and
+  // everything derived from them, as wave-uniform: scalar loads and branches)
+  const int gi = __builtin_amdgcn_readfirstlane(threadIdx.x / kGroupThreads);
+  const int tid = threadIdx.x % kGroupThreads;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave within the group
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int G = a.group;
@@ -164,8 +176,12 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   const cptr_i32 btc = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(s) * a.table_width);
   const int64_t row_bytes = int64_t(Hkv) * D * EB;
   const int64_t head_off = int64_t(g) * D * EB;
-  const int t_lo = key_lo / kKeys;                      // tiles [t_lo, t_hi)
+  const int t_lo = key_lo / kKeys;                      // the item's tiles [t_lo, t_hi)
   const int t_hi = (key_end + kKeys - 1) / kKeys;
+  const int n_half = (max(t_hi - t_lo, 0) + 1) / 2;     // group 0: the first n_half tiles
+  const int my_t0 = gi == 0 ? t_lo : t_lo + n_half;
+  const int my_n = gi == 0 ? n_half : max(t_hi - t_lo - n_half, 0);
+  const int my_key_end = gi == 0 ? min(key_end, (t_lo + n_half) * kKeys) : key_end;
 
   // Per-thread parts of the chunk addresses (the same in every tile): chunk i of this
   // thread is 16 bytes of key kti[i] of the tile. The 64 chunks of one wave's load i cover
@@ -177,7 +193,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   uint32_t voff[LPT], loff[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int c = tid + kThreads * i;
+    const int c = tid + kGroupThreads * i;
     kti[i] = c / CPK;
     jw[i] = __builtin_amdgcn_readfirstlane(kti[i] / BS);
     voff[i] = uint32_t((kti[i] % BS) * row_bytes + head_off + 16 * (c % CPK));
@@ -192,10 +208,10 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   auto stage = [&](int t, uint4 (&ks)[LPT], uint4 (&vs)[LPT], uint32_t& keep) {
     const int key0 = t * kKeys;
     int blk[NB];
-    bool all_ok = key0 + kKeys <= key_end;
+    bool all_ok = key0 + kKeys <= my_key_end;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      blk[j] = key0 + j * BS < key_end ? btc[(key0 + j * BS) / BS] : -1;
+      blk[j] = key0 + j * BS < my_key_end ? btc[(key0 + j * BS) / BS] : -1;
       all_ok = all_ok && blk[j] >= 0 && blk[j] < a.num_blocks;
     }
     keep = all_ok ? 0xffffffffu : 0u;
@@ -207,7 +223,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
       const bool bok = b >= 0 && b < a.num_blocks;
       const int64_t base = int64_t(bok ? b : 0) * block_bytes;
       if (!all_ok) {                                      // uniform: the tail tile, or a bad block id
-        const bool ok = (key0 + kti[i] < key_end) & bok;
+        const bool ok = (key0 + kti[i] < my_key_end) & bok;
         keep |= ok ? (1u << i) : 0u;
       }
       const uint8_t* kb = a.kc + base;                     // scalar block bases
@@ -216,8 +232,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
       vs[i] = *reinterpret_cast<const uint4*>(vb + voff[i]);
     }
   };
+  uint8_t* const gsmem = smem + gi * Lds<D>::kGroupBytes;
   auto commit = [&](int buf, const uint4 (&ks)[LPT], const uint4 (&vs)[LPT], uint32_t keep) {
-    uint8_t* kt = smem + buf * 2 * TILE;
+    uint8_t* kt = gsmem + buf * 2 * TILE;
     uint8_t* vt = kt + TILE;
     const bool plain = keep == 0xffffffffu;                // uniform
 #pragma unroll
@@ -244,7 +261,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
   auto compute = [&](int t, int buf) {
     const int key0 = t * kKeys;
     if (key0 > wave_last) return;                          // uniform: every key is past every row
-    const uint8_t* kt = smem + buf * 2 * TILE;
+    const uint8_t* kt = gsmem + buf * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     // S^T blocks: sc[rb][kb] -> keys key0 + 16kb + 4grp + r of row block rb
     // the K fragments of 16-key group kb + 1 are read while group kb is on the MFMAs
@@ -377,25 +394,62 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(ChunkArgs a) {
     }
   };
 
-  if (t_lo < t_hi) {
-    // Two LDS buffers, one register stage: tile t + 1 is loaded into registers while tile
-    // t is computed, then written to the buffer tile t - 1 used (free once every wave has
-    // passed the barrier after t - 1). Tiles past the end are staged clamped and masked.
+  if (n_half > 0) {
+    // Per group: two LDS buffers, one register stage: tile i + 1 is loaded into registers
+    // while tile i is computed, then written to the buffer tile i - 1 used (free once every
+    // wave has passed the barrier after i - 1). Tiles past the group's end are staged
+    // clamped and masked. Both groups run n_half steps (group 1 may have one tile fewer),
+    // so they meet at the same workgroup barriers.
     uint4 kr[LPT], vr[LPT];
     uint32_t keep;
-    stage(t_lo, kr, vr, keep);
+    stage(my_t0, kr, vr, keep);
     commit(0, kr, vr, keep);
-    stage(t_lo + 1, kr, vr, keep);
+    stage(my_t0 + 1, kr, vr, keep);
     __syncthreads();
-    for (int t = t_lo; t < t_hi; t += 2) {
-      compute(t, 0);
+    for (int i = 0; i < n_half; i += 2) {
+      if (i < my_n) compute(my_t0 + i, 0);
       commit(1, kr, vr, keep);
-      stage(t + 2, kr, vr, keep);
+      stage(my_t0 + i + 2, kr, vr, keep);
       __syncthreads();
-      if (t + 1 < t_hi) compute(t + 1, 1);
+      if (i + 1 < my_n) compute(my_t0 + i + 1, 1);
       commit(0, kr, vr, keep);
-      stage(t + 3, kr, vr, keep);
+      stage(my_t0 + i + 3, kr, vr, keep);
       __syncthreads();
+    }
+  }
+  // ---- group 1 hands its row states (reference maximum, lane sums, accumulators) to
+  // group 0 through LDS, which merges them by log-sum-exp: with M = max(m0, m1),
+  // o = o0 2^(m0 - M) + o1 2^(m1 - M), l likewise. Either group may have had no key.
+  {
+    f32x4_t* xo = reinterpret_cast<f32x4_t*>(smem);
+    float* xm = reinterpret_cast<float*>(smem + kWaves * 2 * MT * 64 * 16);
+    float* xl = xm + kWaves * 2 * 64;
+    if (gi == 1) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xo[((w * 2 + rb) * MT + mt) * 64 + lane] = o[rb][mt];
+        xm[(w * 2 + rb) * 64 + lane] = m[rb];
+        xl[(w * 2 + rb) * 64 + lane] = lsum[rb];
+      }
+    }
+    __syncthreads();
+    if (gi == 1) return;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float m1 = xm[(w * 2 + rb) * 64 + lane];
+      const float l1 = xl[(w * 2 + rb) * 64 + lane];
+      const float M = fmaxf(m[rb], m1);
+      const float mref = M == -INFINITY ? 0.f : M;
+      const float c0 = pkv::fast_exp2(m[rb] - mref), c1 = pkv::fast_exp2(m1 - mref);
+      lsum[rb] = lsum[rb] * c0 + l1 * c1;
+      m[rb] = M;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4_t o1 = xo[((w * 2 + rb) * MT + mt) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[rb][mt][e] = fmaf(o[rb][mt][e], c0, o1[e] * c1);
+      }
     }
   }
 
