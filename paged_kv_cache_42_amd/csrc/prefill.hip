@@ -99,7 +99,6 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   constexpr int TILE = Lds<D>::kTile;
   constexpr int CPK = D * EB / 16;                       // 16-byte chunks per key head row
   constexpr int LPT = kKeys * CPK / kGroupThreads;       // chunk loads per thread per plane
-  constexpr int NB = kKeys / BS;                         // blocks per tile
   static_assert(kKeys * CPK % kGroupThreads == 0 && LPT >= 1, "tile / workgroup shape");
   static_assert(LPT <= 32, "mask word");
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D>::kBytes];
@@ -184,52 +183,45 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   const int my_key_end = gi == 0 ? min(key_end, (t_lo + n_half) * kKeys) : key_end;
 
   // Per-thread parts of the chunk addresses (the same in every tile): chunk i of this
-  // thread is 16 bytes of key kti[i] of the tile. The 64 chunks of one wave's load i cover
-  // 64 / CPK consecutive keys, aligned, so they never straddle a block: the block (jw[i])
-  // is wave-uniform, and the address is a scalar block base plus a fixed 32-bit lane
-  // offset (no per-lane 64-bit address arithmetic per tile).
+  // thread is 16 bytes of key kti0 + KPL i of the tile. The 64 chunks of one wave's load
+  // cover 64 / CPK consecutive keys, aligned, so they never straddle a block: the block is
+  // wave-uniform, and the address is a scalar block base (plus the key's compile-time
+  // offset in the block) and one 32-bit lane offset; the LDS offset of load i is loff0
+  // plus a constant.
+  constexpr int KPL = kGroupThreads / CPK;               // keys per load of the group
   static_assert(BS % (64 / CPK) == 0, "a wave's chunks of one load stay in one block");
-  int kti[LPT], jw[LPT];
-  uint32_t voff[LPT], loff[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int c = tid + kGroupThreads * i;
-    kti[i] = c / CPK;
-    jw[i] = __builtin_amdgcn_readfirstlane(kti[i] / BS);
-    voff[i] = uint32_t((kti[i] % BS) * row_bytes + head_off + 16 * (c % CPK));
-    loff[i] = uint32_t(kti[i] * RS + (CDT == PKV_BF16 ? 16 : 32) * (c % CPK));
-  }
+  static_assert(KPL % BS == 0 || BS % KPL == 0, "loads and blocks nest");
+  const int kti0 = tid / CPK;
+  const int jw0 = KPL % BS == 0 ? __builtin_amdgcn_readfirstlane(kti0 / BS) : 0;
+  const uint32_t voff0 = uint32_t((kti0 % BS) * row_bytes + head_off + 16 * (tid % CPK));
+  const uint32_t loff0 = uint32_t(kti0 * RS + (CDT == PKV_BF16 ? 16 : 32) * (tid % CPK));
   const int64_t block_bytes = int64_t(BS) * row_bytes;
 
-  // Stage tile t into registers: every load is issued (from block 0 when the tile's block
-  // is past the end or invalid), so the loads stay unconditional. `keep` marks the real
-  // rows; all-ones (uniform) when every row of the tile is in the context and its blocks
-  // are valid.
+  // Stage tile t into registers: every load is issued (from block 0 when the block is
+  // past the end or invalid), so the loads stay unconditional. The blocks are those that
+  // hold this wave's chunks, one scalar load each. `keep` marks the real rows; all-ones
+  // (uniform) when every row the wave loads is in the context and its blocks are valid.
   auto stage = [&](int t, uint4 (&ks)[LPT], uint4 (&vs)[LPT], uint32_t& keep) {
     const int key0 = t * kKeys;
-    int blk[NB];
+    int blk[LPT];
     bool all_ok = key0 + kKeys <= my_key_end;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      blk[j] = key0 + j * BS < my_key_end ? btc[(key0 + j * BS) / BS] : -1;
-      all_ok = all_ok && blk[j] >= 0 && blk[j] < a.num_blocks;
+    for (int i = 0; i < LPT; ++i) {
+      const int bi = key0 / BS + jw0 + KPL * i / BS;
+      blk[i] = bi * BS < my_key_end ? btc[bi] : -1;
+      all_ok = all_ok && blk[i] >= 0 && blk[i] < a.num_blocks;
     }
     keep = all_ok ? 0xffffffffu : 0u;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      int b = blk[0];
-#pragma unroll
-      for (int j = 1; j < NB; ++j) b = jw[i] == j ? blk[j] : b;      // wave-uniform
-      const bool bok = b >= 0 && b < a.num_blocks;
-      const int64_t base = int64_t(bok ? b : 0) * block_bytes;
+      const bool bok = blk[i] >= 0 && blk[i] < a.num_blocks;
       if (!all_ok) {                                      // uniform: the tail tile, or a bad block id
-        const bool ok = (key0 + kti[i] < my_key_end) & bok;
+        const bool ok = (key0 + kti0 + KPL * i < my_key_end) & bok;
         keep |= ok ? (1u << i) : 0u;
       }
-      const uint8_t* kb = a.kc + base;                     // scalar block bases
-      const uint8_t* vb = a.vc + base;
-      ks[i] = *reinterpret_cast<const uint4*>(kb + voff[i]);
-      vs[i] = *reinterpret_cast<const uint4*>(vb + voff[i]);
+      const int64_t base = int64_t(bok ? blk[i] : 0) * block_bytes + int64_t((KPL * i) % BS) * row_bytes;
+      ks[i] = *reinterpret_cast<const uint4*>(a.kc + base + voff0);
+      vs[i] = *reinterpret_cast<const uint4*>(a.vc + base + voff0);
     }
   };
   uint8_t* const gsmem = smem + gi * Lds<D>::kGroupBytes;
@@ -245,14 +237,15 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
         k = make_uint4(k.x & mk, k.y & mk, k.z & mk, k.w & mk);
         v = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
       }
+      const uint32_t lo = loff0 + KPL * i * RS;
       if constexpr (CDT == PKV_BF16) {
-        *reinterpret_cast<uint4*>(kt + loff[i]) = k;
-        *reinterpret_cast<uint4*>(vt + loff[i]) = v;
+        *reinterpret_cast<uint4*>(kt + lo) = k;
+        *reinterpret_cast<uint4*>(vt + lo) = v;
       } else {
-        *reinterpret_cast<uint4*>(kt + loff[i]) = pkv::fp8x8_to_bf16x8(k.x, k.y);
-        *reinterpret_cast<uint4*>(kt + loff[i] + 16) = pkv::fp8x8_to_bf16x8(k.z, k.w);
-        *reinterpret_cast<uint4*>(vt + loff[i]) = pkv::fp8x8_to_bf16x8(v.x, v.y);
-        *reinterpret_cast<uint4*>(vt + loff[i] + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+        *reinterpret_cast<uint4*>(kt + lo) = pkv::fp8x8_to_bf16x8(k.x, k.y);
+        *reinterpret_cast<uint4*>(kt + lo + 16) = pkv::fp8x8_to_bf16x8(k.z, k.w);
+        *reinterpret_cast<uint4*>(vt + lo) = pkv::fp8x8_to_bf16x8(v.x, v.y);
+        *reinterpret_cast<uint4*>(vt + lo + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
       }
     }
   };
