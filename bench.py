@@ -60,10 +60,11 @@ def parse_args():
                          "cache write and mixed attention per step, bf16 and E4M3 caches)")
     ap.add_argument("--replay-steps", type=int, default=None, help="replay only the first N scheduler steps")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy measurement (1 GiB each way)")
-    ap.add_argument("--replays", default="bf16,fp8",
+    ap.add_argument("--replays", default="bf16,fp8,bf16_per_layer",
                     help="comma-separated names of the trace replays to run (default: the trace with bf16 and "
-                         "E4M3 caches; 'all' for every variant: static batching, chunked prefill, swap, victim "
-                         "policies, priorities, prefix caching)")
+                         "E4M3 caches, layer-batched launches, and bf16 with one launch per layer; 'all' for every "
+                         "variant: static batching, chunked prefill, swap, victim policies, priorities, prefix "
+                         "caching)")
     ap.add_argument("--replay-batching-sweep", action="store_true",
                     help="also replay continuous vs static batching for three output-length distributions")
     ap.add_argument("--replay-budget-sweep", action="store_true",
@@ -412,6 +413,10 @@ def sched_replay(max_steps, only=None):
     from workloads import replay
     out = {}
     runs = [("bf16", workloads.config5("bf16"), {}), ("fp8", workloads.config5("fp8"), {}),
+            # one launch per kernel and layer, as a model running its layers in turn issues
+            # them (the runs above launch each kernel once per step for all 16 layers)
+            ("bf16_per_layer", workloads.config5("bf16"), {"layer_batched": False}),
+            ("fp8_per_layer", workloads.config5("fp8"), {"layer_batched": False}),
             # the static-batching baseline continuous batching is measured against
             ("bf16_static_batching", workloads.config5("bf16"), {"static_batching": True}),
             # chunked prefill: at most 2048 new tokens per step, prefills in chunks of 512

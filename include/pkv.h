@@ -49,6 +49,20 @@ extern "C" {
 
 typedef struct pkv_pool pkv_pool;
 
+/* Layer batching. The layers of a model run the same step over the same metadata (block
+ * tables, lengths, plans, work lists) with planes, queries and outputs of their own; a
+ * *_layers entry point covers num_layers of them in one launch per kernel (the layer is
+ * a grid dimension). The call's pointers are layer 0's; layer l's tensors sit l strides
+ * further. Strides may be 0 only when num_layers is 1 (layers must not alias their
+ * outputs). Read during the call only. */
+typedef struct pkv_layers {
+  int32_t num_layers;   /* >= 1 */
+  int64_t in_bytes;     /* between layers of the inputs: q (attention), k and v (cache write) */
+  int64_t out_bytes;    /* between layers of out (attention; unused by the cache write) */
+  int64_t cache_bytes;  /* between layers of k_cache and of v_cache */
+  int64_t lse_floats;   /* between layers of lse_out (unused when lse_out is NULL) */
+} pkv_layers;
+
 /* Library version string (static storage). */
 const char* pkv_version(void);
 /* Message of the last error returned on this thread (static per-thread storage). */
@@ -147,6 +161,16 @@ int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype, int32_t n
                        int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
                        const int64_t* slot_mapping, float k_scale, float v_scale,
                        const float* k_head_scales, const float* v_head_scales, void* stream);
+/* pkv_kv_cache_write for layers->num_layers layers in one launch (pkv_layers above): layer
+ * l writes its k and v (in_bytes apart) into its planes (cache_bytes apart) at the same
+ * slots. Errors as for pkv_kv_cache_write, and INVALID for a NULL layers, num_layers < 1,
+ * or strides that are negative, not multiples of 16, or 0 with num_layers > 1. */
+int pkv_kv_cache_write_layers(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
+                              int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
+                              const int64_t* slot_mapping, float k_scale, float v_scale,
+                              const float* k_head_scales, const float* v_head_scales,
+                              const pkv_layers* layers, void* stream);
 
 /* Decode work list (host): one item per non-empty (sequence, context partition), so the
  * decode launch has no idle workgroups. seq_lens: host int32 [num_seqs] (the values the
@@ -274,6 +298,28 @@ int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype,
                                      const int32_t* plan, int32_t num_slots,
                                      int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
                                      size_t workspace_bytes, float* lse_out, void* stream);
+/* pkv_paged_attention_decode_split for layers->num_layers layers in one launch of each
+ * kernel (pkv_layers above): the plan, rows and tables are shared; layer l reads its q
+ * and planes and writes its out and lse_out. workspace_bytes must cover num_layers
+ * times pkv_decode_split_workspace_bytes (layer l's partials at l times that size).
+ * Errors as for pkv_paged_attention_decode_split, and INVALID for a NULL layers,
+ * num_layers < 1, or strides that are negative, not multiples of 16 bytes (4 floats for
+ * lse_floats), or 0 with num_layers > 1. */
+int pkv_paged_attention_decode_split_layers(void* out, const void* q, int32_t q_dtype,
+                                            const void* k_cache, const void* v_cache,
+                                            int32_t cache_dtype, const int32_t* block_tables,
+                                            const int32_t* seq_lens, int32_t table_width,
+                                            int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t num_blocks,
+                                            int32_t max_seq_len, float scale, float k_scale,
+                                            float v_scale, const float* k_head_scales,
+                                            const float* v_head_scales, const int32_t* rows,
+                                            int32_t num_rows, const int32_t* cu_seqlens_q,
+                                            int32_t total_q, const int32_t* plan, int32_t num_slots,
+                                            int32_t tiles_per_slot, int32_t max_pieces,
+                                            void* workspace, size_t workspace_bytes, float* lse_out,
+                                            const pkv_layers* layers, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): pkv_paged_attention_decode_split
@@ -413,6 +459,27 @@ int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype
                                        const int32_t* merges, int32_t num_merges, int32_t num_partials,
                                        void* workspace, int64_t workspace_bytes, float* lse_out,
                                        void* stream);
+/* pkv_paged_attention_prefill_chunks for layers->num_layers layers in one launch of each
+ * kernel (pkv_layers above): the work items and merges are shared; layer l reads its q
+ * and planes and writes its out and lse_out. workspace_bytes must cover num_layers
+ * times pkv_chunk_workspace_bytes (layer l's partials at l times that size). Errors as
+ * for pkv_paged_attention_prefill_chunks, and INVALID for a NULL layers, num_layers < 1,
+ * or strides that are negative, not multiples of 16 bytes (4 floats for lse_floats), or
+ * 0 with num_layers > 1. */
+int pkv_paged_attention_prefill_chunks_layers(void* out, const void* q, int32_t q_dtype,
+                                              const void* k_cache, const void* v_cache,
+                                              int32_t cache_dtype, const int32_t* block_tables,
+                                              const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                              int32_t table_width, int32_t num_seqs, int32_t total_q,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                              int32_t max_seq_len, float scale, float k_scale,
+                                              float v_scale, const float* k_head_scales,
+                                              const float* v_head_scales, const int32_t* work_items,
+                                              int32_t num_work, const int32_t* merges, int32_t num_merges,
+                                              int32_t num_partials, void* workspace,
+                                              int64_t workspace_bytes, float* lse_out,
+                                              const pkv_layers* layers, void* stream);
 
 /* Continuous-batching scheduler step (host) over a pool ([CB] "4. Tiny example",
  * the engine loop: admit, one mixed forward pass, update; [CB] "5. Technical

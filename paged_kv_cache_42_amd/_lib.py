@@ -38,6 +38,13 @@ i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 P_i32 = C.POINTER(C.c_int32)
 P_i64 = C.POINTER(C.c_int64)
 
+
+class PkvLayers(C.Structure):
+    """struct pkv_layers: layer count and the strides between layers (bytes; lse in floats)."""
+    _fields_ = [("num_layers", C.c_int32), ("in_bytes", C.c_int64), ("out_bytes", C.c_int64),
+                ("cache_bytes", C.c_int64), ("lse_floats", C.c_int64)]
+
+
 _SIGS = {
     "pkv_version": (C.c_char_p, []),
     "pkv_last_error": (C.c_char_p, []),
@@ -52,6 +59,8 @@ _SIGS = {
     "pkv_seq_table": (C.c_int, [vp, i64, vp, i32, P_i32]),
     "pkv_build_block_table": (C.c_int, [vp, i32, vp, vp, vp, i32, vp, vp, vp]),
     "pkv_kv_cache_write": (C.c_int, [vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, f32, f32, vp, vp, vp]),
+    "pkv_kv_cache_write_layers": (C.c_int, [vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, f32, f32, vp,
+                                            vp, vp, vp]),
     "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
     "pkv_decode_set_profile_event": (None, [vp]),
     "pkv_paged_attention_decode": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -62,6 +71,9 @@ _SIGS = {
     "pkv_paged_attention_prefill_chunks": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32,
                                                      i32, vp, i64, vp, vp]),
+    "pkv_paged_attention_prefill_chunks_layers": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                                            i32, i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32,
+                                                            vp, i32, i32, vp, i64, vp, vp, vp]),
     "pkv_build_chunk_work": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, vp, i32, P_i32, vp, i32, P_i32, P_i32]),
     "pkv_chunk_slots": (C.c_int, [i32, i32, i32, P_i32]),
     "pkv_build_mixed_step": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, P_i32, vp, i32, P_i32,
@@ -94,6 +106,9 @@ _SIGS = {
     "pkv_paged_attention_decode_split": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                                    i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, vp, i32, i32,
                                                    i32, vp, sz, vp, vp]),
+    "pkv_paged_attention_decode_split_layers": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                          i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, vp,
+                                                          i32, i32, i32, vp, sz, vp, vp, vp]),
     "pkv_decode_split_noalloc_max_bytes": (sz, []),
     "pkv_paged_attention_decode_split_noalloc": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                                            i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, vp,
@@ -387,6 +402,23 @@ def _check_plane(k_cache, v_cache, block_size, Hkv, d):
         raise ValueError("K and V planes must have the same shape and dtype")
 
 
+def _layer_stride(t, num_layers: int, what: str) -> int:
+    """Byte stride between the layers of a layer-batched tensor t [L][...]: each layer
+    contiguous on the device, layers apart by a non-negative stride that does not overlap."""
+    if t.dim() < 2 or t.shape[0] != num_layers:
+        raise ValueError(f"{what} must have a leading layer axis of {num_layers}")
+    if not t.is_cuda or not t[0].is_contiguous():
+        raise ValueError(f"{what}: each layer must be a contiguous device tensor")
+    st = t.stride(0) if num_layers > 1 else t[0].numel()
+    if st < t[0].numel():
+        raise ValueError(f"{what}: layers overlap")
+    return st * t.element_size()
+
+
+def _layers_arg(num_layers: int, in_bytes: int = 0, out_bytes: int = 0, cache_bytes: int = 0, lse_floats: int = 0):
+    return C.byref(PkvLayers(num_layers, in_bytes, out_bytes, cache_bytes, lse_floats))
+
+
 def swap_workspace_bytes(n: int, num_layers: int, block_bytes: int) -> int:
     return int(lib().pkv_swap_workspace_bytes(int(n), int(num_layers), int(block_bytes)))
 
@@ -443,8 +475,22 @@ def _heads(k_head_scales, v_head_scales, num_kv_heads: int):
 def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scale: float = 1.0,
                    v_scale: float = 1.0, stream=None, k_head_scales=None, v_head_scales=None) -> None:
     """k, v: [T][Hkv][d]; caches: [num_blocks][block_size][Hkv][d]; slot_mapping int64 [T];
-    k_head_scales / v_head_scales: optional per-KV-head factors of the E4M3 scales."""
+    k_head_scales / v_head_scales: optional per-KV-head factors of the E4M3 scales. With a
+    leading layer axis on every tensor but slot_mapping (k, v [L][T][Hkv][d], each layer
+    contiguous, any layer stride; caches [L][num_blocks][...] contiguous) the L layers are
+    written in one launch (pkv_kv_cache_write_layers)."""
     torch = _torch()
+    layers = None
+    if k_cache.dim() == 5:
+        NL = k_cache.shape[0]
+        _require_cuda_contig(k_cache, v_cache)
+        ks, vs = _layer_stride(k, NL, "k"), _layer_stride(v, NL, "v")
+        if ks != vs:
+            raise ValueError("k and v must have the same layer stride")
+        if v_cache.shape != k_cache.shape:
+            raise ValueError("K and V planes must have the same shape")
+        layers = _layers_arg(NL, in_bytes=ks, cache_bytes=k_cache[0].numel() * k_cache.element_size())
+        k, v, k_cache, v_cache = k[0], v[0], k_cache[0], v_cache[0]
     _require_cuda_contig(k, v, k_cache, v_cache, slot_mapping)
     if k.dim() != 3 or v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v must both be [T][Hkv][d] of one dtype")
@@ -453,10 +499,13 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scal
     if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be int64 [T]")
     kh, vh = _heads(k_head_scales, v_head_scales, Hkv)
-    check(lib().pkv_kv_cache_write(_dptr(k), _dptr(v), tensor_dtype_code(k), T, Hkv, d, _dptr(k_cache),
-                                   _dptr(v_cache), tensor_dtype_code(k_cache), k_cache.shape[0], block_size,
-                                   _dptr(slot_mapping), k_scale, v_scale, _np_ptr(kh), _np_ptr(vh),
-                                   _stream(stream)))
+    args = (_dptr(k), _dptr(v), tensor_dtype_code(k), T, Hkv, d, _dptr(k_cache), _dptr(v_cache),
+            tensor_dtype_code(k_cache), k_cache.shape[0], block_size, _dptr(slot_mapping), k_scale, v_scale,
+            _np_ptr(kh), _np_ptr(vh))
+    if layers is None:
+        check(lib().pkv_kv_cache_write(*args, _stream(stream)))
+    else:
+        check(lib().pkv_kv_cache_write_layers(*args, layers, _stream(stream)))
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
@@ -545,11 +594,11 @@ def decode_split_workspace_bytes(num_slots: int, num_q_heads: int, head_dim: int
     return int(lib().pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces))
 
 
-def decode_split_workspace(split: SplitPlan, num_q_heads: int, head_dim: int, device="cuda"):
-    """A device workspace for a balanced-split launch of this plan (None when the plan
-    needs none)."""
+def decode_split_workspace(split: SplitPlan, num_q_heads: int, head_dim: int, device="cuda", num_layers: int = 1):
+    """A device workspace for a balanced-split launch of this plan over num_layers layers
+    (None when the plan needs none)."""
     torch = _torch()
-    nb = decode_split_workspace_bytes(split.num_slots, num_q_heads, head_dim, split.max_pieces)
+    nb = decode_split_workspace_bytes(split.num_slots, num_q_heads, head_dim, split.max_pieces) * num_layers
     return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
 
 
@@ -561,12 +610,36 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
     """Balanced-split decode. Without rows / cu_seqlens_q: q/out [B][Hq][d], one plan row per
     sequence. rows (device int32 [n]): the batch sequences the plan covers; cu_seqlens_q
     (device int32 [B + 1]): q/out are [total_q][Hq][d] and a sequence's row is its last
-    new token. plan_dev: device int32 copy of split.plan."""
+    new token. plan_dev: device int32 copy of split.plan. With a leading layer axis on q,
+    out, the caches and lse (each layer contiguous) the layers run in one launch of each
+    kernel (pkv_paged_attention_decode_split_layers); the workspace then holds one
+    plan's partials per layer."""
+    layers = None
+    if q.dim() == 4:
+        NL = q.shape[0]
+        layers, (out, q, k_cache, v_cache, lse) = _layered_attention(NL, out, q, k_cache, v_cache, lse)
     args = _split_args(out, q, k_cache, v_cache, block_tables, seq_lens, plan_dev, split, num_kv_heads, block_size,
                        max_seq_len, scale, k_scale, v_scale, workspace, lse, rows, cu_seqlens_q, k_head_scales,
                        v_head_scales)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().pkv_paged_attention_decode_split(*args, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
+    if layers is None:
+        check(lib().pkv_paged_attention_decode_split(*args, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
+    else:
+        check(lib().pkv_paged_attention_decode_split_layers(*args, _dptr(workspace), ws_bytes, _dptr(lse), layers,
+                                                            _stream(stream)))
+
+
+def _layered_attention(NL, out, q, k_cache, v_cache, lse):
+    """The layer descriptor of a layer-batched attention call and its layer-0 views."""
+    if k_cache.dim() != 5 or v_cache.shape != k_cache.shape or k_cache.shape[0] != NL:
+        raise ValueError(f"layer-batched caches must be [{NL}][num_blocks][block_size][Hkv][d]")
+    _require_cuda_contig(k_cache, v_cache)
+    lse_floats = 0
+    if lse is not None:
+        lse_floats = _layer_stride(lse, NL, "lse") // 4
+    layers = _layers_arg(NL, in_bytes=_layer_stride(q, NL, "q"), out_bytes=_layer_stride(out, NL, "out"),
+                         cache_bytes=k_cache[0].numel() * k_cache.element_size(), lse_floats=lse_floats)
+    return layers, (out[0], q[0], k_cache[0], v_cache[0], None if lse is None else lse[0])
 
 
 def decode_split_noalloc_max_bytes() -> int:
@@ -649,15 +722,16 @@ class ChunkPlan:
     def __init__(self, items: np.ndarray, merges: np.ndarray, num_partials: int):
         self.items, self.merges, self.num_partials = items, merges, num_partials
 
-    def to_device(self, head_dim: int, device="cuda"):
+    def to_device(self, head_dim: int, device="cuda", num_layers: int = 1):
         """(work, merges or None, workspace or None) as device tensors for
-        paged_attention_prefill_chunks; None when there are no items."""
+        paged_attention_prefill_chunks (the workspace sized for num_layers layers); None
+        when there are no items."""
         torch = _torch()
         if len(self.items) == 0:
             return None
         work = torch.from_numpy(self.items).to(device)
         merges = torch.from_numpy(self.merges).to(device) if len(self.merges) else None
-        nb = chunk_workspace_bytes(self.num_partials, head_dim)
+        nb = chunk_workspace_bytes(self.num_partials, head_dim) * num_layers
         ws = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
         return work, merges, ws
 
@@ -769,8 +843,14 @@ def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_l
     """Rows of the sequences with two or more new tokens. work: device int32 [n][8] and
     merges: device int32 [m][4] (or None) from build_chunk_work, num_partials its slots,
     workspace: device tensor of at least chunk_workspace_bytes (None when no slots); the
-    rest as for paged_attention_prefill_varlen."""
+    rest as for paged_attention_prefill_varlen. With a leading layer axis on q, out, the
+    caches and lse (each layer contiguous) the layers run in one launch of each kernel
+    (pkv_paged_attention_prefill_chunks_layers); the workspace then holds the partials of
+    every layer."""
     torch = _torch()
+    layers = None
+    if q.dim() == 4:
+        layers, (out, q, k_cache, v_cache, lse) = _layered_attention(q.shape[0], out, q, k_cache, v_cache, lse)
     _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work, merges, workspace, lse)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [total_q][Hq][d] of one dtype")
@@ -791,9 +871,12 @@ def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_l
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
         raise ValueError("lse must be float32 [total_q][Hq]")
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib().pkv_paged_attention_prefill_chunks(
-        _dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
-        _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads, d,
-        block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
-        *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(work), work.shape[0],
-        _dptr(merges), nm, num_partials, _dptr(workspace), wsb, _dptr(lse), _stream(stream)))
+    args = (_dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+            _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads,
+            d, block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
+            *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(work), work.shape[0],
+            _dptr(merges), nm, num_partials, _dptr(workspace), wsb, _dptr(lse))
+    if layers is None:
+        check(lib().pkv_paged_attention_prefill_chunks(*args, _stream(stream)))
+    else:
+        check(lib().pkv_paged_attention_prefill_chunks_layers(*args, layers, _stream(stream)))

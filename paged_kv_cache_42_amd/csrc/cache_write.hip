@@ -18,11 +18,22 @@ namespace {
 using pkv::f32_to_bf16;
 using pkv::f32_to_fp8;
 
+// Layer blockIdx.y of a layer-batched launch: inputs in_ls bytes apart, planes cache_ls.
+template <typename T>
+__device__ __forceinline__ T* at_layer(T* p, int64_t ls) {
+  return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + uintptr_t(int64_t(blockIdx.y) * ls));
+}
+
 // Same dtype: bit copy, one uint4 (16 B) per lane.
 __global__ void __launch_bounds__(256) write_copy16(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                     uint4* __restrict__ kc, uint4* __restrict__ vc,
                                                     const int64_t* __restrict__ slots, int64_t num_tokens,
-                                                    int64_t chunks_per_row, int64_t num_slots) {
+                                                    int64_t chunks_per_row, int64_t num_slots, int64_t in_ls,
+                                                    int64_t cache_ls) {
+  k = at_layer(k, in_ls);
+  v = at_layer(v, in_ls);
+  kc = at_layer(kc, cache_ls);
+  vc = at_layer(vc, cache_ls);
   const int64_t total = num_tokens * chunks_per_row;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
@@ -49,7 +60,12 @@ __global__ void __launch_bounds__(256) write_fp8(const void* __restrict__ k_, co
                                                  uint2* __restrict__ kc, uint2* __restrict__ vc,
                                                  const int64_t* __restrict__ slots, int64_t num_tokens,
                                                  int64_t chunks_per_row, int64_t num_slots,
-                                                 int64_t chunks_per_head, InvScales inv) {
+                                                 int64_t chunks_per_head, InvScales inv, int64_t in_ls,
+                                                 int64_t cache_ls) {
+  k_ = at_layer(k_, in_ls);
+  v_ = at_layer(v_, in_ls);
+  kc = at_layer(kc, cache_ls);
+  vc = at_layer(vc, cache_ls);
   const int64_t total = num_tokens * chunks_per_row;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
@@ -108,14 +124,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
-                                  int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
-                                  int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
-                                  const int64_t* slot_mapping, float k_scale, float v_scale,
-                                  const float* k_head_scales, const float* v_head_scales, void* stream) {
+namespace {
+int cache_write(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, void* k_cache, void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                int32_t block_size, const int64_t* slot_mapping, float k_scale, float v_scale,
+                const float* k_head_scales, const float* v_head_scales, const pkv::Layers& layers, void* stream) {
   using pkv::fail;
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
     return fail(PKV_ERR_INVALID, "kv_cache_write: bad sizes");
+  if (layers.n < 1 || layers.n > 65535) return fail(PKV_ERR_INVALID, "kv_cache_write: bad layer count %d", layers.n);
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping)
     return fail(PKV_ERR_INVALID, "kv_cache_write: NULL pointer");
@@ -128,9 +145,10 @@ extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype
     if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
       return fail(PKV_ERR_INVALID, "kv_cache_write: pointers must be 16-byte aligned");
     const int64_t chunks = row * eb / 16;
-    hipLaunchKernelGGL(write_copy16, dim3(grid_for(num_tokens * chunks)), dim3(256), 0, st,
+    hipLaunchKernelGGL(write_copy16, dim3(grid_for(num_tokens * chunks), layers.n), dim3(256), 0, st,
                        static_cast<const uint4*>(k), static_cast<const uint4*>(v), static_cast<uint4*>(k_cache),
-                       static_cast<uint4*>(v_cache), slot_mapping, int64_t(num_tokens), chunks, num_slots);
+                       static_cast<uint4*>(v_cache), slot_mapping, int64_t(num_tokens), chunks, num_slots, layers.in,
+                       layers.cache);
   } else if (cache_dtype == PKV_FP8_E4M3 && (in_dtype == PKV_BF16 || in_dtype == PKV_F32)) {
     if (!(k_scale > 0.f) || !(v_scale > 0.f)) return fail(PKV_ERR_INVALID, "kv_cache_write: scales must be > 0");
     if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 8) || !aligned(v_cache, 8))
@@ -144,13 +162,13 @@ extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype
     const int64_t chunks = row / 8;
     const int64_t per_head = head_dim % 8 == 0 ? head_dim / 8 : INT64_MAX;
     if (in_dtype == PKV_BF16)
-      hipLaunchKernelGGL(write_fp8<true>, dim3(grid_for(num_tokens * chunks)), dim3(256), 0, st, k, v,
+      hipLaunchKernelGGL(write_fp8<true>, dim3(grid_for(num_tokens * chunks), layers.n), dim3(256), 0, st, k, v,
                          static_cast<uint2*>(k_cache), static_cast<uint2*>(v_cache), slot_mapping,
-                         int64_t(num_tokens), chunks, num_slots, per_head, inv);
+                         int64_t(num_tokens), chunks, num_slots, per_head, inv, layers.in, layers.cache);
     else
-      hipLaunchKernelGGL(write_fp8<false>, dim3(grid_for(num_tokens * chunks)), dim3(256), 0, st, k, v,
+      hipLaunchKernelGGL(write_fp8<false>, dim3(grid_for(num_tokens * chunks), layers.n), dim3(256), 0, st, k, v,
                          static_cast<uint2*>(k_cache), static_cast<uint2*>(v_cache), slot_mapping,
-                         int64_t(num_tokens), chunks, num_slots, per_head, inv);
+                         int64_t(num_tokens), chunks, num_slots, per_head, inv, layers.in, layers.cache);
   } else {
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: input dtype %d -> cache dtype %d not supported", in_dtype,
                 cache_dtype);
@@ -158,4 +176,28 @@ extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_cache_write: launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+}  // namespace
+
+extern "C" int pkv_kv_cache_write(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
+                                  int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
+                                  const int64_t* slot_mapping, float k_scale, float v_scale,
+                                  const float* k_head_scales, const float* v_head_scales, void* stream) {
+  return cache_write(k, v, in_dtype, num_tokens, num_kv_heads, head_dim, k_cache, v_cache, cache_dtype, num_blocks,
+                     block_size, slot_mapping, k_scale, v_scale, k_head_scales, v_head_scales, pkv::Layers{},
+                     stream);
+}
+
+extern "C" int pkv_kv_cache_write_layers(const void* k, const void* v, int32_t in_dtype, int32_t num_tokens,
+                                         int32_t num_kv_heads, int32_t head_dim, void* k_cache, void* v_cache,
+                                         int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
+                                         const int64_t* slot_mapping, float k_scale, float v_scale,
+                                         const float* k_head_scales, const float* v_head_scales,
+                                         const pkv_layers* layers, void* stream) {
+  pkv::Layers ls;
+  const int rc = pkv::layers_from("kv_cache_write_layers", layers, true, pkv::kLayerIn | pkv::kLayerCache, &ls);
+  if (rc != PKV_OK) return rc;
+  return cache_write(k, v, in_dtype, num_tokens, num_kv_heads, head_dim, k_cache, v_cache, cache_dtype, num_blocks,
+                     block_size, slot_mapping, k_scale, v_scale, k_head_scales, v_head_scales, ls, stream);
 }

@@ -123,7 +123,33 @@ struct DecodeArgs {
   int num_batch;         // batch sequences (rows of block_tables / seq_lens)
   int total_q;           // query / output rows
   int num_slots;         // balanced split: workgroup slots of the launch
+  // balanced split over several layers (blockIdx.z): bytes between layers of q, out and
+  // the cache planes, floats between layers of lse_out and of the partials
+  int64_t ls_in, ls_out, ls_cache, ls_lse, ls_ws;
 };
+
+// The tensors of layer blockIdx.z of a layer-batched balanced-split launch.
+struct LayerPtrs {
+  const uint16_t* q;
+  uint16_t* out;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+};
+__device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeArgs& a) {
+  const int64_t l = blockIdx.z;
+  LayerPtrs p;
+  p.q = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.q) + l * a.ls_in);
+  p.out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + l * a.ls_out);
+  p.kc = static_cast<const uint8_t*>(a.k_cache) + l * a.ls_cache;
+  p.vc = static_cast<const uint8_t*>(a.v_cache) + l * a.ls_cache;
+  p.lse = a.lse_out ? a.lse_out + l * a.ls_lse : nullptr;
+  p.ws_o = a.ws_o ? a.ws_o + l * a.ls_ws : nullptr;
+  p.ws_lse = a.ws_lse ? a.ws_lse + l * a.ls_ws : nullptr;
+  return p;
+}
 
 // Partial of one piece of the balanced split, as an index into [num_slots][2][Hq]: a
 // sequence spanning slots first..first+np-1 leaves its piece p in slot first + p. Only the
@@ -527,6 +553,7 @@ __global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_
   const int c = blockIdx.y * 256 + threadIdx.x;
   const int B = a.num_seqs;
   if (j + 1 >= a.num_slots || c >= num_q_heads * CH || !a.ws_o) return;
+  const LayerPtrs lp = layer_ptrs(a);
   const cptr plan = (cptr)(uintptr_t)(a.plan);
   const cptr seq_slots = plan + (B + 1) + 2 * a.num_slots + 1;
   const int s = plan[B + 1 + j + 1];
@@ -543,8 +570,8 @@ __global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_
     for (int k = 0; k < KB; ++k) {
       const int kk = k0 + k < np ? k0 + k : k0;
       const int64_t pi = split_partial(f + kk, kk, num_q_heads, hq);
-      lse[k] = a.ws_lse[pi];
-      ov[k] = *reinterpret_cast<const float4*>(a.ws_o + pi * D + d0);
+      lse[k] = lp.ws_lse[pi];
+      ov[k] = *reinterpret_cast<const float4*>(lp.ws_o + pi * D + d0);
     }
     float Mb = M;
 #pragma unroll
@@ -573,10 +600,9 @@ __global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const uint32_t lo = pkv::f32_to_bf16(A.x * inv) | (pkv::f32_to_bf16(A.y * inv) << 16);
   const uint32_t hi = pkv::f32_to_bf16(A.z * inv) | (pkv::f32_to_bf16(A.w * inv) << 16);
-  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (int64_t(row) * num_q_heads + hq) * D + d0) =
-      make_uint2(lo, hi);
-  if (a.lse_out && d0 == 0)
-    a.lse_out[int64_t(row) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
+  *reinterpret_cast<uint2*>(lp.out + (int64_t(row) * num_q_heads + hq) * D + d0) = make_uint2(lo, hi);
+  if (lp.lse && d0 == 0)
+    lp.lse[int64_t(row) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
 }
 
 // ---------------------------------------------------------------------------------
@@ -703,8 +729,9 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   const int grp = lane >> 4;
   const int hl_q = hl < G ? hl : hl % G;
   const int slot = blockIdx.y;
-  const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache);
-  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache);
+  const LayerPtrs lp = layer_ptrs(a);
+  const uint8_t* kc = lp.kc;
+  const uint8_t* vc = lp.vc;
   const int64_t row_bytes = int64_t(Hkv) * D * EB;
   const int64_t lane_off = int64_t(g) * D * EB + 16 * grp;
 
@@ -775,8 +802,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     i_n = 0;
     i_bt = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(b) * a.table_width);
     // lanes past the group read a duplicate head of it: their columns are never written
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + (int64_t(row < 0 ? 0 : row) * Hq + int64_t(g) * G + hl_q) * D;
+    const uint16_t* qrow = lp.q + (int64_t(row < 0 ? 0 : row) * Hq + int64_t(g) * G + hl_q) * D;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int d0 = EB == 2 ? 32 * kk + 8 * grp : 64 * (kk / 2) + 16 * grp + 8 * (kk % 2);
@@ -941,22 +967,22 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
     if (sl_np[k] == 1) {
       const int row = sl_row[k];
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(row) * Hq + hq) * D + 4 * grp;
+      uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
         const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
         pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
       }
-      if (a.lse_out && grp == 0)
-        pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + hq, __float_as_uint(lse2 * kLn2));
+      if (lp.lse && grp == 0)
+        pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + hq, __float_as_uint(lse2 * kLn2));
     } else {
       const int64_t pi = split_partial(slot, sl_p[k], Hq, hq);
-      float* orow = a.ws_o + pi * D + 4 * grp;
+      float* orow = lp.ws_o + pi * D + 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         pkv::store_b128_untracked(orow + 16 * mt, o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv, o[mt][3] * inv);
-      if (grp == 0) pkv::store_b32_untracked(a.ws_lse + pi, __float_as_uint(lse2));
+      if (grp == 0) pkv::store_b32_untracked(lp.ws_lse + pi, __float_as_uint(lse2));
     }
   };
 
@@ -967,11 +993,11 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     int b, row;
     split_row(a, s0, b, row);
     if (row < 0 || hl >= G) continue;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(row) * Hq + g * G + hl) * D + 4 * grp;
+    uint16_t* orow = lp.out + (int64_t(row) * Hq + g * G + hl) * D + 4 * grp;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) pkv::store_b64_untracked(orow + 16 * mt, 0u, 0u);
-    if (a.lse_out && grp == 0)
-      pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + g * G + hl, __float_as_uint(-INFINITY));
+    if (lp.lse && grp == 0)
+      pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + g * G + hl, __float_as_uint(-INFINITY));
   }
   if (!more) return;
   // One exit, at the bottom: a tile issued after the stream ran out is masked to nothing
@@ -1267,8 +1293,10 @@ extern "C" int pkv_decode_split_slots(int32_t cache_dtype, int32_t num_kv_heads,
 extern "C" size_t pkv_decode_split_workspace_bytes(int32_t num_slots, int32_t num_q_heads, int32_t head_dim,
                                                    int32_t max_pieces) {
   if (num_slots <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_pieces <= 1) return 0;
-  // partials [S][2][Hq][D] and their log-sum-exps [S][2][Hq], float
-  return size_t(2) * num_slots * num_q_heads * (head_dim + 1) * sizeof(float);
+  // partials [S][2][Hq][D] and their log-sum-exps [S][2][Hq], float; rounded up to 256
+  // bytes so that the layers of a layer-batched call sit at multiples of it
+  const size_t b = size_t(2) * num_slots * num_q_heads * (head_dim + 1) * sizeof(float);
+  return (b + 255) / 256 * 256;
 }
 
 extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache,
@@ -1286,7 +1314,28 @@ extern "C" int pkv_paged_attention_decode_split(void* out, const void* q, int32_
   return pkv::decode_split(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, table_width,
                            num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                            k_scale, v_scale, k_head_scales, v_head_scales, rows, num_rows, cu_seqlens_q, total_q,
-                           plan, num_slots, tiles_per_slot, max_pieces, workspace, workspace_bytes, lse_out, stream);
+                           plan, num_slots, tiles_per_slot, max_pieces, workspace, workspace_bytes, lse_out,
+                           pkv::Layers{}, stream);
+}
+
+extern "C" int pkv_paged_attention_decode_split_layers(
+    void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache, int32_t cache_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, int32_t table_width, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_seq_len, float scale, float k_scale, float v_scale, const float* k_head_scales,
+    const float* v_head_scales, const int32_t* rows, int32_t num_rows, const int32_t* cu_seqlens_q, int32_t total_q,
+    const int32_t* plan, int32_t num_slots, int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
+    size_t workspace_bytes, float* lse_out, const pkv_layers* layers, void* stream) {
+  pkv::Layers ls;
+  const int rc = pkv::layers_from("decode_split_layers", layers, true,
+                                  pkv::kLayerIn | pkv::kLayerOut | pkv::kLayerCache | (lse_out ? pkv::kLayerLse : 0u),
+                                  &ls);
+  if (rc != PKV_OK) return rc;
+  return pkv::decode_split(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, table_width,
+                           num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                           k_scale, v_scale, k_head_scales, v_head_scales, rows, num_rows, cu_seqlens_q, total_q,
+                           plan, num_slots, tiles_per_slot, max_pieces, workspace, workspace_bytes, lse_out, ls,
+                           stream);
 }
 
 int pkv::decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
@@ -1296,11 +1345,12 @@ int pkv::decode_split(void* out, const void* q, int32_t q_dtype, const void* k_c
                       float v_scale, const float* k_head_scales, const float* v_head_scales, const int32_t* rows,
                       int32_t num_rows, const int32_t* cu_seqlens_q, int32_t total_q, const int32_t* plan,
                       int32_t num_slots, int32_t tiles_per_slot, int32_t max_pieces, void* workspace,
-                      size_t workspace_bytes, float* lse_out, void* stream) {
+                      size_t workspace_bytes, float* lse_out, const Layers& layers, void* stream) {
   using pkv::fail;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
       max_seq_len < 0)
     return fail(PKV_ERR_INVALID, "decode_split: bad sizes");
+  if (layers.n < 1 || layers.n > 65535) return fail(PKV_ERR_INVALID, "decode_split: bad layer count %d", layers.n);
   if (num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "decode_split: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
                 num_kv_heads);
@@ -1333,8 +1383,9 @@ int pkv::decode_split(void* out, const void* q, int32_t q_dtype, const void* k_c
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID, "decode_split: q, out and cache planes must be 16-byte aligned");
   const size_t need = pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_ERR_INVALID, "decode_split: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need > 0 && (!workspace || workspace_bytes / size_t(layers.n) < need))
+    return fail(PKV_ERR_INVALID, "decode_split: workspace of %d x %zu bytes needed, %zu given", layers.n, need,
+                workspace_bytes);
 
   DecodeArgs a{};
   a.q = q;
@@ -1367,16 +1418,22 @@ int pkv::decode_split(void* out, const void* q, int32_t q_dtype, const void* k_c
   a.cu_q = cu_seqlens_q;
   a.num_batch = num_seqs;
   a.total_q = total_q;
+  a.ls_in = layers.in;
+  a.ls_out = layers.out;
+  a.ls_cache = layers.cache;
+  a.ls_lse = layers.lse;
+  a.ls_ws = int64_t(need / sizeof(float));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // the pass (which also writes zeros for rows without context), then the merge of the
-  // sequences it cut across slots (none when no sequence spans two slots)
-  hipLaunchKernelGGL(fn, dim3(num_kv_heads / hpw, num_slots), dim3(hpw * 64), 0, st, a);
+  // sequences it cut across slots (none when no sequence spans two slots); the layers of
+  // a layer-batched call are the grid's third dimension
+  hipLaunchKernelGGL(fn, dim3(num_kv_heads / hpw, num_slots, layers.n), dim3(hpw * 64), 0, st, a);
   if (g_profile_event) (void)hipEventRecord(g_profile_event, st);
   if (need > 0) {
     const int chunks = num_q_heads * (head_dim / 4);
     auto mk = max_pieces <= 8 ? (head_dim == 64 ? split_merge_kernel<64, 8> : split_merge_kernel<128, 8>)
                               : (head_dim == 64 ? split_merge_kernel<64, 32> : split_merge_kernel<128, 32>);
-    hipLaunchKernelGGL(mk, dim3(num_slots, (chunks + 255) / 256), dim3(256), 0, st, a, num_q_heads);
+    hipLaunchKernelGGL(mk, dim3(num_slots, (chunks + 255) / 256, layers.n), dim3(256), 0, st, a, num_q_heads);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_split: launch failed: %s", hipGetErrorString(e));

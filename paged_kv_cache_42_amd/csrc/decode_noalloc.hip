@@ -74,5 +74,5 @@ extern "C" int pkv_paged_attention_decode_split_noalloc(
                            num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                            k_scale, v_scale, k_head_scales, v_head_scales, rows, num_rows, cu_seqlens_q, total_q,
                            plan, num_slots, tiles_per_slot, max_pieces, ws, need > 0 ? kNoAllocScratchBytes : 0,
-                           lse_out, stream);
+                           lse_out, pkv::Layers{}, stream);
 }

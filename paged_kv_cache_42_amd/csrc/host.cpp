@@ -62,6 +62,31 @@ int head_products(const char* who, int32_t hkv, float base, const float* head, d
 
 }  // namespace
 
+int layers_from(const char* who, const pkv_layers* desc, bool required, unsigned uses, Layers* out) {
+  *out = Layers{};
+  if (!desc) return required ? fail(PKV_ERR_INVALID, "%s: layers is NULL", who) : PKV_OK;
+  if (desc->num_layers < 1) return fail(PKV_ERR_INVALID, "%s: num_layers %d < 1", who, desc->num_layers);
+  const struct {
+    unsigned bit;
+    int64_t bytes;
+    const char* name;
+  } st[] = {{kLayerIn, desc->in_bytes, "in_bytes"},
+            {kLayerOut, desc->out_bytes, "out_bytes"},
+            {kLayerCache, desc->cache_bytes, "cache_bytes"},
+            {kLayerLse, desc->lse_floats * 4, "lse_floats"}};
+  for (const auto& x : st) {
+    if (!(uses & x.bit)) continue;
+    if (x.bytes < 0 || x.bytes % 16 != 0 || (desc->num_layers > 1 && x.bytes == 0))
+      return fail(PKV_ERR_INVALID, "%s: layer stride %s must be a positive multiple of 16 bytes", who, x.name);
+  }
+  out->n = desc->num_layers;
+  out->in = uses & kLayerIn ? desc->in_bytes : 0;
+  out->out = uses & kLayerOut ? desc->out_bytes : 0;
+  out->cache = uses & kLayerCache ? desc->cache_bytes : 0;
+  out->lse = uses & kLayerLse ? desc->lse_floats : 0;
+  return PKV_OK;
+}
+
 int head_scales(const char* who, int32_t num_kv_heads, float scale, float k_scale, float v_scale,
                 const float* k_head, const float* v_head, float* zs, float* vs) {
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PKV_ERR_INVALID, "%s: scales must be finite and > 0", who);

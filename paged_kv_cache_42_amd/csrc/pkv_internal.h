@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 // Record a message for pkv_last_error() and return `code`.
@@ -26,6 +28,17 @@ int head_scales(const char* who, int32_t num_kv_heads, float scale, float k_scal
 int head_inverse_scales(const char* who, int32_t num_kv_heads, float k_scale, float v_scale,
                         const float* k_head, const float* v_head, float* ki, float* vi);
 
+// Layer batching of a *_layers call, checked: n layers and the byte (lse: float)
+// strides between them. `uses` names the strides the call reads (kLayerIn | ...); each of
+// those must be >= 0, a multiple of 16 bytes (4 floats) and non-zero when n > 1. A NULL
+// descriptor is INVALID when `required`, else one layer.
+struct Layers {
+  int n = 1;
+  int64_t in = 0, out = 0, cache = 0, lse = 0;
+};
+constexpr unsigned kLayerIn = 1, kLayerOut = 2, kLayerCache = 4, kLayerLse = 8;
+int layers_from(const char* who, const pkv_layers* desc, bool required, unsigned uses, Layers* out);
+
 // pkv_paged_attention_decode_split (the no-allocation entry point reuses it).
 int decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
                  int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens, int32_t table_width,
@@ -34,7 +47,7 @@ int decode_split(void* out, const void* q, int32_t q_dtype, const void* k_cache,
                  const float* k_head_scales, const float* v_head_scales, const int32_t* rows, int32_t num_rows,
                  const int32_t* cu_seqlens_q, int32_t total_q, const int32_t* plan, int32_t num_slots,
                  int32_t tiles_per_slot, int32_t max_pieces, void* workspace, size_t workspace_bytes,
-                 float* lse_out, void* stream);
+                 float* lse_out, const Layers& layers, void* stream);
 
 }  // namespace pkv
 

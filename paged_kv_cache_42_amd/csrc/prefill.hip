@@ -76,7 +76,33 @@ struct ChunkArgs {
   int len_clamp;
   float zscale_h[pkv::kHeadScales];   // per KV head: softmax scale * k_scale * log2(e)
   float vscale_h[pkv::kHeadScales];   // per KV head: v_scale
+  // several layers (blockIdx.z): bytes between layers of q, out and the cache planes,
+  // floats between layers of lse_out and of the partials
+  int64_t ls_in, ls_out, ls_cache, ls_lse, ls_ws;
 };
+
+// The tensors of layer blockIdx.z of a layer-batched launch.
+struct ChunkLayer {
+  const uint16_t* q;
+  uint16_t* out;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+};
+__device__ __forceinline__ ChunkLayer chunk_layer(const ChunkArgs& a) {
+  const int64_t l = blockIdx.z;
+  ChunkLayer p;
+  p.q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.q) + l * a.ls_in);
+  p.out = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.out) + l * a.ls_out);
+  p.kc = a.kc + l * a.ls_cache;
+  p.vc = a.vc + l * a.ls_cache;
+  p.lse = a.lse_out ? a.lse_out + l * a.ls_lse : nullptr;
+  p.ws_o = a.ws_o ? a.ws_o + l * a.ls_ws : nullptr;
+  p.ws_lse = a.ws_lse ? a.ws_lse + l * a.ls_ws : nullptr;
+  return p;
+}
 
 template <int D>
 struct Lds {
@@ -124,6 +150,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   const int key_end = max(0, min(it2.x, L));
   const int key_lo = it.w;
   if (key_lo < 0 || key_lo % kKeys != 0) return;
+  const ChunkLayer lp = chunk_layer(a);
 
   // the two groups take the first and the second half of the item's key tiles; each
   // has its own LDS buffers, and group 1 hands its row states to group 0 at the end
@@ -151,7 +178,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
     const int tok = r / G;
     row_ok[rb] = tok < ntok;
     pos[rb] = pos0 + q0 + tok;
-    const uint16_t* qrow = a.q + (int64_t(row0 + q0 + min(tok, ntok - 1)) * Hq + int64_t(g) * G + r % G) * D + 8 * grp;
+    const uint16_t* qrow = lp.q + (int64_t(row0 + q0 + min(tok, ntok - 1)) * Hq + int64_t(g) * G + r % G) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
@@ -220,8 +247,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
         keep |= ok ? (1u << i) : 0u;
       }
       const int64_t base = int64_t(bok ? blk[i] : 0) * block_bytes + int64_t((KPL * i) % BS) * row_bytes;
-      ks[i] = *reinterpret_cast<const uint4*>(a.kc + base + voff0);
-      vs[i] = *reinterpret_cast<const uint4*>(a.vc + base + voff0);
+      ks[i] = *reinterpret_cast<const uint4*>(lp.kc + base + voff0);
+      vs[i] = *reinterpret_cast<const uint4*>(lp.vc + base + voff0);
     }
   };
   uint8_t* const gsmem = smem + gi * Lds<D>::kGroupBytes;
@@ -455,27 +482,27 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
     const int r = 32 * w + 16 * rb + hl;
     const float inv = l > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / l : 0.f;
     if (slot >= 0) {                                       // partial of a split item
-      float* prow = a.ws_o + (int64_t(slot) * kRows + r) * D + 4 * grp;
+      float* prow = lp.ws_o + (int64_t(slot) * kRows + r) * D + 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         pkv::store_b128_untracked(prow + 16 * mt, o[rb][mt][0] * inv, o[rb][mt][1] * inv, o[rb][mt][2] * inv,
                                   o[rb][mt][3] * inv);
       if (grp == 0)
-        pkv::store_b32_untracked(a.ws_lse + int64_t(slot) * kRows + r,
+        pkv::store_b32_untracked(lp.ws_lse + int64_t(slot) * kRows + r,
                                  __float_as_uint(l > 0.f ? m[rb] + log2f(l) : -INFINITY));
       continue;
     }
     const int row = row0 + q0 + r / G;
     const int hq = g * G + r % G;
-    uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+    uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t lo = pack_bf16x2_rne(o[rb][mt][0] * inv, o[rb][mt][1] * inv);
       const uint32_t hi = pack_bf16x2_rne(o[rb][mt][2] * inv, o[rb][mt][3] * inv);
       pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
     }
-    if (a.lse_out && grp == 0)
-      pkv::store_b32_untracked(a.lse_out + int64_t(row) * Hq + hq,
+    if (lp.lse && grp == 0)
+      pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + hq,
                                __float_as_uint(l > 0.f ? (m[rb] + log2f(l)) * kLn2 : -INFINITY));
   }
 }
@@ -493,6 +520,7 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
   const int first = mg.w & 0xfffff, np = mg.w >> 20;
   if (s < 0 || s >= a.num_seqs || g < 0 || g >= a.num_kv_heads || np < 1 || first < 0 || first + np > a.num_slots)
     return;
+  const ChunkLayer lp = chunk_layer(a);
   constexpr int LPR = D / 4;                               // threads per row
   const int task = blockIdx.y * 256 + threadIdx.x;
   const int r = task / LPR;
@@ -506,8 +534,8 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
 #pragma unroll
     for (int k = 0; k < kChunkMergeFast; ++k) {             // slots past np re-read piece 0
       const int64_t sl = first + (k < np ? k : 0);
-      lse[k] = a.ws_lse[sl * kRows + r];
-      ov[k] = *reinterpret_cast<const float4*>(a.ws_o + (sl * kRows + r) * D + e);
+      lse[k] = lp.ws_lse[sl * kRows + r];
+      ov[k] = *reinterpret_cast<const float4*>(lp.ws_o + (sl * kRows + r) * D + e);
     }
 #pragma unroll
     for (int k = 0; k < kChunkMergeFast; ++k) M = k < np ? fmaxf(M, lse[k]) : M;
@@ -522,11 +550,11 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
       A.w = fmaf(wk, ov[k].w, A.w);
     }
   } else {
-    for (int k = 0; k < np; ++k) M = fmaxf(M, a.ws_lse[int64_t(first + k) * kRows + r]);
+    for (int k = 0; k < np; ++k) M = fmaxf(M, lp.ws_lse[int64_t(first + k) * kRows + r]);
     const float mref = M == -INFINITY ? 0.f : M;
     for (int k = 0; k < np; ++k) {
-      const float wk = pkv::fast_exp2(a.ws_lse[int64_t(first + k) * kRows + r] - mref);
-      const float4 ok = *reinterpret_cast<const float4*>(a.ws_o + (int64_t(first + k) * kRows + r) * D + e);
+      const float wk = pkv::fast_exp2(lp.ws_lse[int64_t(first + k) * kRows + r] - mref);
+      const float4 ok = *reinterpret_cast<const float4*>(lp.ws_o + (int64_t(first + k) * kRows + r) * D + e);
       S += wk;
       A.x = fmaf(wk, ok.x, A.x);
       A.y = fmaf(wk, ok.y, A.y);
@@ -544,9 +572,9 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const int row = row0 + q0 + r / G;
   const int hq = g * G + r % G;
-  uint16_t* orow = a.out + (int64_t(row) * Hq + hq) * D + e;
+  uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + e;
   *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2_rne(A.x * inv, A.y * inv), pack_bf16x2_rne(A.z * inv, A.w * inv));
-  if (a.lse_out && e == 0) a.lse_out[int64_t(row) * Hq + hq] = S > 0.f ? (M + log2f(S)) * kLn2 : -INFINITY;
+  if (lp.lse && e == 0) lp.lse[int64_t(row) * Hq + hq] = S > 0.f ? (M + log2f(S)) * kLn2 : -INFINITY;
 }
 
 using ChunkFn = void (*)(ChunkArgs);
@@ -681,22 +709,20 @@ extern "C" int64_t pkv_chunk_workspace_bytes(int32_t num_partials, int32_t head_
   return int64_t(num_partials) * kRows * (head_dim + 1) * 4;
 }
 
-extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cache,
-                                                  const void* v_cache, int32_t cache_dtype,
-                                                  const int32_t* block_tables, const int32_t* seq_lens,
-                                                  const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs,
-                                                  int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
-                                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                                  int32_t max_seq_len, float scale, float k_scale, float v_scale,
-                                                  const float* k_head_scales, const float* v_head_scales,
-                                                  const int32_t* work_items, int32_t num_work,
-                                                  const int32_t* merges, int32_t num_merges, int32_t num_partials,
-                                                  void* workspace, int64_t workspace_bytes, float* lse_out,
-                                                  void* stream) {
+namespace {
+int prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                   int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens,
+                   const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs, int32_t total_q,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t max_seq_len, float scale, float k_scale, float v_scale, const float* k_head_scales,
+                   const float* v_head_scales, const int32_t* work_items, int32_t num_work, const int32_t* merges,
+                   int32_t num_merges, int32_t num_partials, void* workspace, int64_t workspace_bytes,
+                   float* lse_out, const pkv::Layers& layers, void* stream) {
   using pkv::fail;
   if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
       max_seq_len < 0 || num_work < 0 || num_merges < 0 || num_partials < 0 || num_partials >= (1 << kSlotBits))
     return fail(PKV_ERR_INVALID, "prefill_chunks: bad sizes");
+  if (layers.n < 1 || layers.n > 65535) return fail(PKV_ERR_INVALID, "prefill_chunks: bad layer count %d", layers.n);
   if (num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "prefill_chunks: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
                 num_kv_heads);
@@ -722,9 +748,9 @@ extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int3
     if (!merges || !workspace || !aligned16(merges) || !aligned16(workspace))
       return fail(PKV_ERR_INVALID, "prefill_chunks: split items need 16-byte aligned merges and workspace");
     const int64_t need = pkv_chunk_workspace_bytes(num_partials, head_dim);
-    if (workspace_bytes < need)
-      return fail(PKV_ERR_INVALID, "prefill_chunks: workspace %lld bytes, %lld needed", (long long)workspace_bytes,
-                  (long long)need);
+    if (workspace_bytes / layers.n < need)
+      return fail(PKV_ERR_INVALID, "prefill_chunks: workspace %lld bytes, %d x %lld needed",
+                  (long long)workspace_bytes, layers.n, (long long)need);
   }
   ChunkArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -754,15 +780,58 @@ extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int3
                                     v_head_scales, a.zscale_h, a.vscale_h);
     if (rc != PKV_OK) return rc;
   }
+  a.ls_in = layers.in;
+  a.ls_out = layers.out;
+  a.ls_cache = layers.cache;
+  a.ls_lse = layers.lse;
+  a.ls_ws = pkv_chunk_workspace_bytes(num_partials, head_dim) / 4;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3(num_work), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(fn, dim3(num_work, 1, layers.n), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: launch failed: %s", hipGetErrorString(e));
   if (num_merges > 0) {
-    hipLaunchKernelGGL(pick_merge(head_dim), dim3(num_merges, kRows * (head_dim / 4) / 256), dim3(256), 0, st, a,
-                       reinterpret_cast<const int4*>(merges));
+    hipLaunchKernelGGL(pick_merge(head_dim), dim3(num_merges, kRows * (head_dim / 4) / 256, layers.n), dim3(256), 0,
+                       st, a, reinterpret_cast<const int4*>(merges));
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: merge launch failed: %s", hipGetErrorString(e));
   }
   return PKV_OK;
+}
+}  // namespace
+
+extern "C" int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                                  const void* v_cache, int32_t cache_dtype,
+                                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                                  const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs,
+                                                  int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                                  int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                                  const float* k_head_scales, const float* v_head_scales,
+                                                  const int32_t* work_items, int32_t num_work,
+                                                  const int32_t* merges, int32_t num_merges, int32_t num_partials,
+                                                  void* workspace, int64_t workspace_bytes, float* lse_out,
+                                                  void* stream) {
+  return prefill_chunks(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, cu_seqlens_q,
+                        table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_seq_len, scale, k_scale, v_scale, k_head_scales, v_head_scales, work_items, num_work,
+                        merges, num_merges, num_partials, workspace, workspace_bytes, lse_out, pkv::Layers{}, stream);
+}
+
+extern "C" int pkv_paged_attention_prefill_chunks_layers(
+    void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache, int32_t cache_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t table_width,
+    int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
+    const float* k_head_scales, const float* v_head_scales, const int32_t* work_items, int32_t num_work,
+    const int32_t* merges, int32_t num_merges, int32_t num_partials, void* workspace, int64_t workspace_bytes,
+    float* lse_out, const pkv_layers* layers, void* stream) {
+  pkv::Layers ls;
+  const int rc = pkv::layers_from("prefill_chunks_layers", layers, true,
+                                  pkv::kLayerIn | pkv::kLayerOut | pkv::kLayerCache | (lse_out ? pkv::kLayerLse : 0u),
+                                  &ls);
+  if (rc != PKV_OK) return rc;
+  return prefill_chunks(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, cu_seqlens_q,
+                        table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_seq_len, scale, k_scale, v_scale, k_head_scales, v_head_scales, work_items, num_work,
+                        merges, num_merges, num_partials, workspace, workspace_bytes, lse_out, ls, stream);
 }

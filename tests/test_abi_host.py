@@ -355,6 +355,38 @@ def test_swap_copy_argument_errors_enqueue_nothing():
         assert call(fn, ok_dev, ok_host, n=0) == _lib.PKV_OK                             # no-op
 
 
+def test_layer_descriptors_checked_before_any_launch():
+    # the *_layers entry points check their layer descriptor first; every case here is
+    # refused before any HIP call (the pointers are stand-ins that are never dereferenced)
+    lib = pkv.lib()
+    p = ctypes.c_void_p(1 << 20)
+    PL = _lib.PkvLayers
+    bad = [None, PL(0, 16, 16, 16, 4), PL(2, 8, 16, 16, 4), PL(2, 0, 16, 16, 4), PL(2, 16, 16, -16, 4),
+           PL(2, 16, 0, 16, 4), PL(2, 16, 16, 16, 2)]
+
+    def ref(d):
+        return None if d is None else ctypes.byref(d)
+
+    for i, d in enumerate(bad):
+        # the cache write reads neither out nor lse strides: only cases 0-4 are errors for it
+        st_w = lib.pkv_kv_cache_write_layers(p, p, _lib.BF16, 4, 2, 64, p, p, _lib.BF16, 8, 16, p, 1.0, 1.0, None,
+                                             None, ref(d), None)
+        assert (st_w == _lib.PKV_ERR_INVALID) == (i <= 4), (i, _lib.last_error())
+        st_d = lib.pkv_paged_attention_decode_split_layers(p, p, _lib.BF16, p, p, _lib.BF16, p, p, 4, 2, 8, 2, 64,
+                                                           16, 8, 64, 0.125, 1.0, 1.0, None, None, None, 2, None,
+                                                           2, p, 4, 1, 1, None, 0, p, ref(d), None)
+        assert st_d == _lib.PKV_ERR_INVALID and "layer" in _lib.last_error(), (i, _lib.last_error())
+        st_c = lib.pkv_paged_attention_prefill_chunks_layers(p, p, _lib.BF16, p, p, _lib.BF16, p, p, p, 4, 2, 8, 8,
+                                                             2, 64, 16, 8, 64, 0.125, 1.0, 1.0, None, None, p, 1,
+                                                             None, 0, 0, None, 0, p, ref(d), None)
+        assert st_c == _lib.PKV_ERR_INVALID and "layer" in _lib.last_error(), (i, _lib.last_error())
+    # without lse_out the lse stride is not read
+    st_d = lib.pkv_paged_attention_decode_split_layers(p, p, _lib.BF16, p, p, 99, p, p, 4, 2, 8, 2, 64, 16, 8, 64,
+                                                       0.125, 1.0, 1.0, None, None, None, 2, None, 2, p, 4, 1, 1, None,
+                                                       0, None, ctypes.byref(PL(2, 16, 16, 16, 2)), None)
+    assert st_d == _lib.PKV_ERR_UNSUPPORTED, _lib.last_error()      # past the layer check: the cache dtype
+
+
 @settings(max_examples=60, deadline=None)
 @given(st.lists(st.tuples(st.integers(0, 3), st.integers(0, 2500)), max_size=24), st.integers(1, 300),
        st.sampled_from([0, 5, 64]), st.sampled_from([1, 4, 8]))

@@ -49,17 +49,20 @@ def _check_full(tr, recs, job, what):
     return by_step
 
 
-@pytest.mark.parametrize("cache_dtype,steps,keep_steps", [
-    ("bf16", 160, (1, 3, 112, 115, 159)),
-    ("fp8", 120, (0, 2, 112, 119)),
+@pytest.mark.parametrize("cache_dtype,steps,keep_steps,layer_batched", [
+    ("bf16", 160, (1, 3, 112, 115, 159), True),
+    ("fp8", 120, (0, 2, 112, 119), True),
+    ("bf16", 160, (1, 3, 112, 115, 159), False),      # one launch per kernel and layer
 ])
-def test_config5_replay_full_rows(cache_dtype, steps, keep_steps):
+def test_config5_replay_full_rows(cache_dtype, steps, keep_steps, layer_batched):
     tr = workloads.config5(cache_dtype)
     job = {"kind": "replay", "trace": "config5", "cache_dtype": cache_dtype, "steps": list(keep_steps),
            "layers": list(ALL_LAYERS)}
-    recs, summary = replay.run(tr, max_steps=steps, keep={s: ALL_LAYERS for s in keep_steps})
+    recs, summary = replay.run(tr, max_steps=steps, keep={s: ALL_LAYERS for s in keep_steps},
+                               layer_batched=layer_batched)
     assert summary["steps"] == steps
-    by_step = _check_full(tr, recs, job, f"config 5 replay ({cache_dtype} cache)")
+    by_step = _check_full(tr, recs, job, f"config 5 replay ({cache_dtype} cache, "
+                                         f"{'layer-batched' if layer_batched else 'per-layer'} launches)")
     if steps > 112:
         assert summary["preemptions"] > 0
         # the step after the first preemption re-prefills a request with its outputs

@@ -4,9 +4,12 @@ mixed (prefill + decode) attention launch of every layer, step after step.
 Benchmark and test infrastructure. Per step: the host scheduler admits, plans and
 updates (C ABI); the step's metadata goes to the device once for all layers; the Q/K/V
 of every new token of every layer are generated on the device by the counter-hash
-generator (outside the timed region), then each layer runs pkv_kv_cache_write, the
-balanced-split decode over the step's decode rows and the chunk kernel over its prefill
-chunks, bracketed by HIP events per step."""
+generator (outside the timed region), then the cache write, the balanced-split decode
+over the step's decode rows and the chunk kernel over its prefill chunks run for every
+layer, bracketed by HIP events per step: by default each kernel once for all layers (the
+layer-batched entry points; the layers' inputs here are independent streams), or one
+launch per kernel and layer (layer_batched=False), as a model that runs its layers in
+turn would issue them."""
 from __future__ import annotations
 
 import dataclasses
@@ -48,12 +51,13 @@ class Replay:
         leg of swap-outs on a copy stream when overlapped);
       victim, priority, classes: victim policy, priority classes for admission, or
         classes used only to report latencies by;
-      static_batching: the static-batching baseline."""
+      static_batching: the static-batching baseline;
+      layer_batched: one launch per kernel for all layers (else one per layer)."""
 
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
                  prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0,
                  swap_overlap: bool = False, victim: str = "self", priority=None, classes=None,
-                 static_batching: bool = False):
+                 static_batching: bool = False, layer_batched: bool = True):
         import torch
         self.torch = torch
         self.tr = tr
@@ -104,8 +108,11 @@ class Replay:
         self.slots = pkv.decode_split_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.num_kv_heads,
                                             tr.head_dim, tr.block_size)
         self.min_piece = 256
-        # the split decode's workspace (its size depends only on the slots and the heads)
-        self.split_ws = torch.empty(pkv.decode_split_workspace_bytes(self.slots, tr.num_q_heads, tr.head_dim, 2),
+        # the split decode's workspace (its size depends only on the slots and the heads;
+        # one plan's partials per layer when the layers share a launch)
+        self.layer_batched = layer_batched
+        nl = tr.num_layers if layer_batched else 1
+        self.split_ws = torch.empty(pkv.decode_split_workspace_bytes(self.slots, tr.num_q_heads, tr.head_dim, 2) * nl,
                                     dtype=torch.uint8, device="cuda")
         self.chunk_slots = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim,
                                            tr.block_size) if chunk_cut else 0
@@ -140,6 +147,12 @@ class Replay:
         np.cumsum(np.concatenate(sizes), out=off[1:])
         seg = torch.from_numpy(np.concatenate([keys, e0, off])).cuda()
         wgen.fill_segments(self.buf, seg, len(e0), int(off[-1]), tr.sigma)
+        if self.layer_batched:                 # q, k, v as [NL][T][heads][d], per_layer apart
+            views, o = [], 0
+            for h in self.heads:
+                views.append(self.buf.as_strided((NL, T, int(h), d), (per_layer, int(h) * d, d, 1), o))
+                o += T * int(h) * d
+            return views
         views = []
         o = 0
         for l in range(NL):
@@ -174,13 +187,15 @@ class Replay:
         # decode rows by the balanced-split decode, prefill rows by the chunk kernel
         mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, self.slots, self.min_piece,
                                   self.chunk_slots, self.min_piece_tiles)
-        chunk_dev = mp.chunks.to_device(tr.head_dim)
+        NL = tr.num_layers
+        chunk_dev = mp.chunks.to_device(tr.head_dim, num_layers=NL if self.layer_batched else 1)
         if len(mp.decode_rows):
             rows = torch.from_numpy(mp.decode_rows).cuda()
             plan_d = torch.from_numpy(mp.split.plan).cuda()
             ws = self.split_ws if mp.split.max_pieces > 1 else None
         msl = int(seq_lens.max())
-        out = torch.empty((T, tr.num_q_heads, tr.head_dim), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(((NL,) if self.layer_batched else ()) + (T, tr.num_q_heads, tr.head_dim),
+                          dtype=torch.bfloat16, device="cuda")
         kept = {}
         swap_in = self.sched.swap_pairs()[1] if self.host_space is not None else np.zeros((0, 2), np.int32)
         if len(swap_in):
@@ -196,20 +211,25 @@ class Replay:
             pkv.swap_in(self.k_cache, self.v_cache, swap_in, self.host_space, self.swap_ws)
             ei = torch.cuda.Event(enable_timing=True)
             ei.record()
-        for l in range(tr.num_layers):
-            q, k, v = vals[l]
-            pkv.kv_cache_write(k, v, self.k_cache[l], self.v_cache[l], slots, tr.block_size, tr.k_scale, tr.v_scale)
+        # the layers in turn, or all of them in each launch (the same calls on [NL][...] tensors)
+        for l in ([None] if self.layer_batched else range(NL)):
+            q, k, v = vals if l is None else vals[l]
+            kc, vc = (self.k_cache, self.v_cache) if l is None else (self.k_cache[l], self.v_cache[l])
+            pkv.kv_cache_write(k, v, kc, vc, slots, tr.block_size, tr.k_scale, tr.v_scale)
             if len(mp.decode_rows):
-                pkv.paged_attention_decode_split(out, q, self.k_cache[l], self.v_cache[l], bt, lens, plan_d, mp.split,
-                                                 tr.num_kv_heads, tr.block_size, msl, tr.softmax_scale, tr.k_scale,
-                                                 tr.v_scale, ws, rows=rows, cu_seqlens_q=cu)
+                pkv.paged_attention_decode_split(out, q, kc, vc, bt, lens, plan_d, mp.split, tr.num_kv_heads,
+                                                 tr.block_size, msl, tr.softmax_scale, tr.k_scale, tr.v_scale, ws,
+                                                 rows=rows, cu_seqlens_q=cu)
             if chunk_dev is not None:
                 work, merges, cws = chunk_dev
-                pkv.paged_attention_prefill_chunks(out, q, self.k_cache[l], self.v_cache[l], bt, lens, cu, work,
-                                                   merges, mp.chunks.num_partials, cws, tr.num_kv_heads,
-                                                   tr.block_size, msl, tr.softmax_scale, tr.k_scale, tr.v_scale)
-            if l in keep_layers:
+                pkv.paged_attention_prefill_chunks(out, q, kc, vc, bt, lens, cu, work, merges,
+                                                   mp.chunks.num_partials, cws, tr.num_kv_heads, tr.block_size, msl,
+                                                   tr.softmax_scale, tr.k_scale, tr.v_scale)
+            if l is not None and l in keep_layers:
                 kept[l] = out.clone()
+        if self.layer_batched:
+            for l in keep_layers:
+                kept[l] = out[l].clone()
         e1.record()
         host_s = time.perf_counter() - h0
         self.sched.update()
