@@ -472,13 +472,23 @@ def _heads(k_head_scales, v_head_scales, num_kv_heads: int):
     return out
 
 
+def _launch(fn, args, defer: bool):
+    """Call fn(*args) now, or (defer) return a callable that makes the call: the checks and
+    the argument marshalling are done either way, so a deferred call only crosses the ABI."""
+    if defer:
+        return lambda: check(fn(*args))
+    check(fn(*args))
+    return None
+
+
 def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scale: float = 1.0,
-                   v_scale: float = 1.0, stream=None, k_head_scales=None, v_head_scales=None) -> None:
+                   v_scale: float = 1.0, stream=None, k_head_scales=None, v_head_scales=None, defer: bool = False):
     """k, v: [T][Hkv][d]; caches: [num_blocks][block_size][Hkv][d]; slot_mapping int64 [T];
     k_head_scales / v_head_scales: optional per-KV-head factors of the E4M3 scales. With a
     leading layer axis on every tensor but slot_mapping (k, v [L][T][Hkv][d], each layer
     contiguous, any layer stride; caches [L][num_blocks][...] contiguous) the L layers are
-    written in one launch (pkv_kv_cache_write_layers)."""
+    written in one launch (pkv_kv_cache_write_layers). defer: return the checked call
+    instead of making it."""
     torch = _torch()
     layers = None
     if k_cache.dim() == 5:
@@ -503,9 +513,8 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scal
             tensor_dtype_code(k_cache), k_cache.shape[0], block_size, _dptr(slot_mapping), k_scale, v_scale,
             _np_ptr(kh), _np_ptr(vh))
     if layers is None:
-        check(lib().pkv_kv_cache_write(*args, _stream(stream)))
-    else:
-        check(lib().pkv_kv_cache_write_layers(*args, layers, _stream(stream)))
+        return _launch(lib().pkv_kv_cache_write, (*args, _stream(stream)), defer)
+    return _launch(lib().pkv_kv_cache_write_layers, (*args, layers, _stream(stream)), defer)
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
@@ -606,14 +615,14 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
                                  num_kv_heads: int, block_size: int, max_seq_len: int, scale: float,
                                  k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, lse=None,
                                  rows=None, cu_seqlens_q=None, stream=None, k_head_scales=None,
-                                 v_head_scales=None) -> None:
+                                 v_head_scales=None, defer: bool = False):
     """Balanced-split decode. Without rows / cu_seqlens_q: q/out [B][Hq][d], one plan row per
     sequence. rows (device int32 [n]): the batch sequences the plan covers; cu_seqlens_q
     (device int32 [B + 1]): q/out are [total_q][Hq][d] and a sequence's row is its last
     new token. plan_dev: device int32 copy of split.plan. With a leading layer axis on q,
     out, the caches and lse (each layer contiguous) the layers run in one launch of each
     kernel (pkv_paged_attention_decode_split_layers); the workspace then holds one
-    plan's partials per layer."""
+    plan's partials per layer. defer: return the checked call instead of making it."""
     layers = None
     if q.dim() == 4:
         NL = q.shape[0]
@@ -623,10 +632,10 @@ def paged_attention_decode_split(out, q, k_cache, v_cache, block_tables, seq_len
                        v_head_scales)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if layers is None:
-        check(lib().pkv_paged_attention_decode_split(*args, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)))
-    else:
-        check(lib().pkv_paged_attention_decode_split_layers(*args, _dptr(workspace), ws_bytes, _dptr(lse), layers,
-                                                            _stream(stream)))
+        return _launch(lib().pkv_paged_attention_decode_split,
+                       (*args, _dptr(workspace), ws_bytes, _dptr(lse), _stream(stream)), defer)
+    return _launch(lib().pkv_paged_attention_decode_split_layers,
+                   (*args, _dptr(workspace), ws_bytes, _dptr(lse), layers, _stream(stream)), defer)
 
 
 def _layered_attention(NL, out, q, k_cache, v_cache, lse):
@@ -839,14 +848,15 @@ def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_l
 def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,
                                    merges, num_partials: int, workspace, num_kv_heads: int, block_size: int,
                                    max_seq_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-                                   lse=None, stream=None, k_head_scales=None, v_head_scales=None) -> None:
+                                   lse=None, stream=None, k_head_scales=None, v_head_scales=None,
+                                   defer: bool = False):
     """Rows of the sequences with two or more new tokens. work: device int32 [n][8] and
     merges: device int32 [m][4] (or None) from build_chunk_work, num_partials its slots,
     workspace: device tensor of at least chunk_workspace_bytes (None when no slots); the
     rest as for paged_attention_prefill_varlen. With a leading layer axis on q, out, the
     caches and lse (each layer contiguous) the layers run in one launch of each kernel
     (pkv_paged_attention_prefill_chunks_layers); the workspace then holds the partials of
-    every layer."""
+    every layer. defer: return the checked call instead of making it."""
     torch = _torch()
     layers = None
     if q.dim() == 4:
@@ -877,6 +887,5 @@ def paged_attention_prefill_chunks(out, q, k_cache, v_cache, block_tables, seq_l
             *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(work), work.shape[0],
             _dptr(merges), nm, num_partials, _dptr(workspace), wsb, _dptr(lse))
     if layers is None:
-        check(lib().pkv_paged_attention_prefill_chunks(*args, _stream(stream)))
-    else:
-        check(lib().pkv_paged_attention_prefill_chunks_layers(*args, layers, _stream(stream)))
+        return _launch(lib().pkv_paged_attention_prefill_chunks, (*args, _stream(stream)), defer)
+    return _launch(lib().pkv_paged_attention_prefill_chunks_layers, (*args, layers, _stream(stream)), defer)

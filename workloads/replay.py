@@ -105,17 +105,21 @@ class Replay:
         self.heads = np.array([tr.num_q_heads, tr.num_kv_heads, tr.num_kv_heads], np.int64)
         self.buf = None
         self.e_kv = 1 if tr.cache_dtype == "fp8" else 2
-        self.slots = pkv.decode_split_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.num_kv_heads,
-                                            tr.head_dim, tr.block_size)
+        resident = pkv.decode_split_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.num_kv_heads,
+                                          tr.head_dim, tr.block_size)
         self.min_piece = 256
-        # the split decode's workspace (its size depends only on the slots and the heads;
-        # one plan's partials per layer when the layers share a launch)
+        # The split decode's slots: the workgroups resident at once. When the layers share
+        # a launch, its grid holds every layer's slots, so each layer's plan takes its share
+        # of them (fewer, longer pieces per layer: fewer partials to merge).
         self.layer_batched = layer_batched
         nl = tr.num_layers if layer_batched else 1
+        self.slots = max(1, -(-resident // nl))
+        # the workspace (its size depends only on the slots and the heads; one plan's
+        # partials per layer when the layers share a launch)
         self.split_ws = torch.empty(pkv.decode_split_workspace_bytes(self.slots, tr.num_q_heads, tr.head_dim, 2) * nl,
                                     dtype=torch.uint8, device="cuda")
-        self.chunk_slots = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim,
-                                           tr.block_size) if chunk_cut else 0
+        cs = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim, tr.block_size)
+        self.chunk_slots = max(1, -(-cs // nl)) if chunk_cut else 0
         self.min_piece_tiles = min_piece_tiles
 
     def _values(self, ids, q_lens, seq_lens):
@@ -200,6 +204,25 @@ class Replay:
         swap_in = self.sched.swap_pairs()[1] if self.host_space is not None else np.zeros((0, 2), np.int32)
         if len(swap_in):
             self._swap_workspace(len(swap_in))
+        # the layers' launches, checked and marshalled ahead of the timed region: all
+        # layers in each launch (the same calls on [NL][...] tensors), or the layers in turn
+        launches = []
+        for l in ([None] if self.layer_batched else range(NL)):
+            q, k, v = vals if l is None else vals[l]
+            kc, vc = (self.k_cache, self.v_cache) if l is None else (self.k_cache[l], self.v_cache[l])
+            launches.append(pkv.kv_cache_write(k, v, kc, vc, slots, tr.block_size, tr.k_scale, tr.v_scale,
+                                               defer=True))
+            if len(mp.decode_rows):
+                launches.append(pkv.paged_attention_decode_split(
+                    out, q, kc, vc, bt, lens, plan_d, mp.split, tr.num_kv_heads, tr.block_size, msl,
+                    tr.softmax_scale, tr.k_scale, tr.v_scale, ws, rows=rows, cu_seqlens_q=cu, defer=True))
+            if chunk_dev is not None:
+                work, merges, cws = chunk_dev
+                launches.append(pkv.paged_attention_prefill_chunks(
+                    out, q, kc, vc, bt, lens, cu, work, merges, mp.chunks.num_partials, cws, tr.num_kv_heads,
+                    tr.block_size, msl, tr.softmax_scale, tr.k_scale, tr.v_scale, defer=True))
+            if l is not None and l in keep_layers:
+                launches.append(lambda l=l: kept.__setitem__(l, out.clone()))
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -211,22 +234,8 @@ class Replay:
             pkv.swap_in(self.k_cache, self.v_cache, swap_in, self.host_space, self.swap_ws)
             ei = torch.cuda.Event(enable_timing=True)
             ei.record()
-        # the layers in turn, or all of them in each launch (the same calls on [NL][...] tensors)
-        for l in ([None] if self.layer_batched else range(NL)):
-            q, k, v = vals if l is None else vals[l]
-            kc, vc = (self.k_cache, self.v_cache) if l is None else (self.k_cache[l], self.v_cache[l])
-            pkv.kv_cache_write(k, v, kc, vc, slots, tr.block_size, tr.k_scale, tr.v_scale)
-            if len(mp.decode_rows):
-                pkv.paged_attention_decode_split(out, q, kc, vc, bt, lens, plan_d, mp.split, tr.num_kv_heads,
-                                                 tr.block_size, msl, tr.softmax_scale, tr.k_scale, tr.v_scale, ws,
-                                                 rows=rows, cu_seqlens_q=cu)
-            if chunk_dev is not None:
-                work, merges, cws = chunk_dev
-                pkv.paged_attention_prefill_chunks(out, q, kc, vc, bt, lens, cu, work, merges,
-                                                   mp.chunks.num_partials, cws, tr.num_kv_heads, tr.block_size, msl,
-                                                   tr.softmax_scale, tr.k_scale, tr.v_scale)
-            if l is not None and l in keep_layers:
-                kept[l] = out.clone()
+        for launch in launches:
+            launch()
         if self.layer_batched:
             for l in keep_layers:
                 kept[l] = out[l].clone()
