@@ -442,8 +442,9 @@ int64_t pkv_chunk_workspace_bytes(int32_t num_partials, int32_t head_dim);
  * [num_merges][4], both from pkv_build_chunk_work for the same q_lens and seq_lens, with
  * num_partials its slot count; workspace: device, at least pkv_chunk_workspace_bytes
  * bytes, 16-byte aligned (not needed when num_partials is 0). The chunk kernel runs one
- * workgroup per item (4 waves of 32 GQA-packed query rows, 64-key tiles on MFMA), then a
- * merge kernel writes the rows of split blocks. Rows of sequences with q < 2 are not
+ * workgroup per item (128 GQA-packed query rows; two groups of 4 waves take the first and
+ * the second half of the item's 64-key tiles on MFMA and merge their softmax states), then
+ * a merge kernel writes the rows of split blocks. Rows of sequences with q < 2 are not
  * written. Supported: bf16 queries with a bf16 or E4M3 cache, head_dim 64/128,
  * block_size 16/32, group 1/2/4/8/16. Calls sharing a workspace must not overlap. */
 int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype,

@@ -10,13 +10,15 @@
 //
 // gfx950 design (the MFMA-bound part of a mixed step; decode rows go to the split decode):
 //  * item = (sequence, KV head g, block of 128/G new tokens): 128 GQA-packed query rows
-//    (token, head), all G heads of g sharing each K/V tile. A workgroup of 4 waves takes
-//    an item, 32 rows per wave as two 16-row MFMA blocks, so every K and V fragment read
-//    from LDS feeds two MFMAs; two workgroups share a compute unit.
-//  * K/V tiles of 64 keys are staged in two LDS buffers (rows padded by 32 bytes) by the
-//    workgroup with coalesced 16-byte loads, the next tile held in registers while the
-//    current one is computed; E4M3 rows are widened to bf16 on the way in. Block ids of a
-//    tile are scalar loads.
+//    (token, head), all G heads of g sharing each K/V tile. A workgroup of 8 waves takes
+//    an item (one workgroup per compute unit): its two groups of 4 waves take the first
+//    and the second half of the item's key tiles, 32 rows per wave as two 16-row MFMA
+//    blocks, so every K and V fragment read from LDS feeds two MFMAs; at the end group 1
+//    hands its softmax states to group 0 through LDS, which merges them.
+//  * K/V tiles of 64 keys are staged per group in two LDS buffers (rows padded by 32
+//    bytes) with coalesced 16-byte loads, the next tile held in registers while the
+//    current one is computed; E4M3 rows are widened to bf16 on the way in. Block ids are
+//    scalar loads.
 //  * S^T = K.Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the packed
 //    queries as B): lane l holds row l%16 of its block for keys 4(l/16)+r of each
 //    16-key group. Online softmax per row (two shuffles for the tile maximum); masks only
