@@ -537,29 +537,29 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
     a.lse_out[int64_t(orow_idx) * num_q_heads + hq] = (S > 0.f ? M + log2f(S) : -INFINITY) * kLn2;
 }
 
-// Log-sum-exp merge of the sequences a balanced split cut across slots. Each such
-// sequence has a unique first slot j: the one holding its first tile, which it runs past.
-// Workgroup (j, y) takes the sequence that slot j starts and hands on (the sequence holding
-// the first tile of slot j + 1, when it began in slot j), and 256 of its Hq x D / 4 float4
-// output chunks, one per thread: M = max_k lse_k, out = sum_k 2^(lse_k - M) o_k /
-// sum_k 2^(lse_k - M) over its pieces k in slots j .. j + np - 1 (the partials o_k are
-// normalised). Pieces are loaded KB at a time (8, or 32 when some sequence spans more
-// than 8 slots), so a sequence's pieces usually take one memory round trip.
+// Log-sum-exp merge of the sequences a balanced split cut across slots: workgroup (s, y)
+// takes plan row s when its pieces span np >= 2 slots f .. f + np - 1 (one scalar load of
+// the plan's (first slot, pieces) pair; the other rows leave at once), and 256 of its
+// Hq x D / 4 float4 output chunks, one per thread: M = max_k lse_k, out = sum_k
+// 2^(lse_k - M) o_k / sum_k 2^(lse_k - M) over its pieces (the partials o_k are
+// normalised). The output row's lookups are issued before the partial loads, and pieces
+// are loaded KB at a time (8, or 32 when some sequence spans more than 8 slots), so a
+// sequence's pieces usually take one memory round trip after the plan's.
 template <int D, int KB>
 __global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_q_heads) {
   constexpr int CH = D / 4;
   typedef __attribute__((address_space(4))) const int32_t* cptr;
-  const int j = blockIdx.x;
+  const int s = blockIdx.x;
   const int c = blockIdx.y * 256 + threadIdx.x;
   const int B = a.num_seqs;
-  if (j + 1 >= a.num_slots || c >= num_q_heads * CH || !a.ws_o) return;
+  if (s >= B || c >= num_q_heads * CH || !a.ws_o) return;
   const LayerPtrs lp = layer_ptrs(a);
   const cptr plan = (cptr)(uintptr_t)(a.plan);
   const cptr seq_slots = plan + (B + 1) + 2 * a.num_slots + 1;
-  const int s = plan[B + 1 + j + 1];
-  if (s < 0 || s >= B) return;
   const int f = seq_slots[2 * s], np = seq_slots[2 * s + 1];
-  if (f != j || np < 2 || f + np > a.num_slots) return;
+  if (np < 2 || f < 0 || f + np > a.num_slots) return;
+  int b, row;
+  split_row(a, s, b, row);
   const int hq = c / CH, d0 = 4 * (c % CH);
   float M = -INFINITY, S = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -573,6 +573,9 @@ __global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_
       lse[k] = lp.ws_lse[pi];
       ov[k] = *reinterpret_cast<const float4*>(lp.ws_o + pi * D + d0);
     }
+    // every load above is issued before any use below (left alone, the scheduler folds
+    // each value into the maximum as it arrives: one memory round trip per piece)
+    __builtin_amdgcn_sched_barrier(0);
     float Mb = M;
 #pragma unroll
     for (int k = 0; k < KB; ++k) Mb = k0 + k < np ? fmaxf(Mb, lse[k]) : Mb;
@@ -594,8 +597,6 @@ __global__ void __launch_bounds__(256) split_merge_kernel(DecodeArgs a, int num_
     }
     M = Mb;
   }
-  int b, row;
-  split_row(a, s, b, row);
   if (row < 0) return;
   const float inv = S > 0.f ? 1.f / S : 0.f;
   const uint32_t lo = pkv::f32_to_bf16(A.x * inv) | (pkv::f32_to_bf16(A.y * inv) << 16);
@@ -1433,7 +1434,7 @@ int pkv::decode_split(void* out, const void* q, int32_t q_dtype, const void* k_c
     const int chunks = num_q_heads * (head_dim / 4);
     auto mk = max_pieces <= 8 ? (head_dim == 64 ? split_merge_kernel<64, 8> : split_merge_kernel<128, 8>)
                               : (head_dim == 64 ? split_merge_kernel<64, 32> : split_merge_kernel<128, 32>);
-    hipLaunchKernelGGL(mk, dim3(num_slots, (chunks + 255) / 256, layers.n), dim3(256), 0, st, a, num_q_heads);
+    hipLaunchKernelGGL(mk, dim3(num_rows, (chunks + 255) / 256, layers.n), dim3(256), 0, st, a, num_q_heads);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode_split: launch failed: %s", hipGetErrorString(e));

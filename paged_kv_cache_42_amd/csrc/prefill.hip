@@ -539,6 +539,7 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(ChunkArgs a, const int
       lse[k] = lp.ws_lse[sl * kRows + r];
       ov[k] = *reinterpret_cast<const float4*>(lp.ws_o + (sl * kRows + r) * D + e);
     }
+    __builtin_amdgcn_sched_barrier(0);                    // all loads issued before any use
 #pragma unroll
     for (int k = 0; k < kChunkMergeFast; ++k) M = k < np ? fmaxf(M, lse[k]) : M;
     const float mref = M == -INFINITY ? 0.f : M;
