@@ -278,8 +278,8 @@ size_t pkv_decode_split_workspace_bytes(int32_t num_slots, int32_t num_q_heads, 
  * has num_slots workgroups per group of KV heads. A plan row inside one slot's range is
  * written directly, as are zeros (log-sum-exp -inf) for rows without context; the
  * pieces of one spanning several slots leave partials in the workspace, merged by
- * log-sum-exp in a second kernel (one workgroup per such sequence, found from its first
- * slot; not launched when max_pieces <= 1). workspace: device, >=
+ * log-sum-exp in a second kernel (one workgroup per plan row and 256 output chunks;
+ * rows held by one slot leave at once; not launched when max_pieces <= 1). workspace: device, >=
  * pkv_decode_split_workspace_bytes(num_slots, num_q_heads, head_dim, max_pieces);
  * nothing in it needs to start at zero, and calls that share one workspace must not
  * overlap. A plan or row map that does not match the batch
