@@ -494,6 +494,7 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a, int num_q_head
       lse[k] = a.ws_lse[pi];
       ov[k] = *reinterpret_cast<const float4*>(a.ws_o + pi * D + e);
     }
+    __builtin_amdgcn_sched_barrier(0);                    // all loads issued before any use
 #pragma unroll
     for (int k = 0; k < kMergeFast; ++k) M = k < nparts ? fmaxf(M, lse[k]) : M;
     const float mref = M == -INFINITY ? 0.f : M;
