@@ -5,6 +5,7 @@ per-layer call on that layer's own tensors. The layers' planes differ (blocks ro
 signs flipped on odd layers), their queries sit in one buffer with a gap between layers,
 and the decode and chunk plans split sequences, so each layer also has partials of its
 own in the shared workspace."""
+import numpy as np
 import pytest
 import torch
 
@@ -24,10 +25,24 @@ def _flip(x):
     return (x.view(torch.int16) ^ -32768).view(x.dtype)
 
 
+def _finite(x):
+    """The plane with its NaN codes (the fill of unused blocks) made finite, so that blocks
+    rotated into use read numbers: E4M3 0x7f / 0xff -> 0x7e / 0xfe, bf16 NaN -> 0."""
+    if x.dtype == torch.uint8:
+        return torch.where((x & 0x7F) == 0x7F, x - 1, x)
+    return torch.where(torch.isnan(x), torch.zeros_like(x), x)
+
+
 def _layer_planes(plane):
-    """[NL][...] contiguous: layer l = plane with its blocks rotated by l, signs flipped on odd l."""
-    return torch.stack([_flip(torch.roll(plane, l, 0)) if l % 2 else torch.roll(plane, l, 0)
+    """[NL][...] contiguous: layer l = plane with its blocks rotated by l, signs flipped on
+    odd l, NaN codes made finite."""
+    return torch.stack([_finite(_flip(torch.roll(plane, l, 0)) if l % 2 else torch.roll(plane, l, 0))
                         for l in range(NL)]).contiguous()
+
+
+def _all_written(out, what):
+    bad = torch.isnan(out.float()).flatten(2).any(dim=2).nonzero().tolist()
+    assert not bad, f"{what}: (layer, row) pairs never written or NaN: {bad[:20]}"
 
 
 def _strided(xs, gap_rows=5):
@@ -106,6 +121,7 @@ def test_decode_split_layers(cdt, d):
         _same(out[l], ref[l][0], f"layer {l} output")
         _same(lse[l], ref[l][1], f"layer {l} log-sum-exp")
     assert not torch.equal(ref[0][0].view(torch.int16), ref[1][0].view(torch.int16)), "layers must differ"
+    _all_written(out, "split decode")
 
 
 @pytest.mark.parametrize("cdt,d,G", [("bf16", 128, 4), ("fp8", 128, 4), ("bf16", 64, 8)])
@@ -148,6 +164,72 @@ def test_chunks_and_mixed_step_layers(cdt, d, G):
     for l in range(NL):
         _same(out[l], ref[l][0], f"layer {l} output")
         _same(lse[l], ref[l][1], f"layer {l} log-sum-exp")
+    _all_written(out, "mixed step")
+
+
+K_HEAD = np.array([0.25, 3.0, 1.0, 0.7], np.float32)
+V_HEAD = np.array([2.0, 0.3, 0.5, 4.0], np.float32)
+
+
+def test_layers_with_per_head_e4m3_scales():
+    """The layer-batched cache write, split decode and chunk kernel with per-KV-head E4M3
+    scales (shared by the layers, as the entry points define them): every layer's cache
+    codes, outputs and log-sum-exps bit-identical to the per-layer calls with the same
+    head scales."""
+    Hkv, G, d = 4, 4, 128
+    w = workloads.small_varlen(75, [700, 1200, 40, 1500, 300], [1, 260, 3, 1, 300], num_q_heads=Hkv * G,
+                               num_kv_heads=Hkv, head_dim=d, block_size=16, dtype="bf16", cache_dtype="fp8")
+    w.k_scale, w.v_scale = 0.5, 0.25
+    kh = K_HEAD.copy()
+    vh = V_HEAD.copy()
+    st = build_step(w)
+    T, Hq = w.total_q, w.num_q_heads
+    slots = torch.from_numpy(st.slots).cuda()
+    g = torch.Generator(device="cuda").manual_seed(9)
+    ks = [torch.randn((T, Hkv, d), device="cuda", generator=g).bfloat16() for _ in range(NL)]
+    vs = [torch.randn((T, Hkv, d), device="cuda", generator=g).bfloat16() for _ in range(NL)]
+    kc, vc = _layer_planes(st.k_cache), _layer_planes(st.v_cache)
+    kc_ref, vc_ref = kc.clone(), vc.clone()
+    for l in range(NL):
+        pkv.kv_cache_write(ks[l], vs[l], kc_ref[l], vc_ref[l], slots, w.block_size, w.k_scale, w.v_scale,
+                           k_head_scales=kh, v_head_scales=vh)
+    pkv.kv_cache_write(_strided(ks), _strided(vs), kc, vc, slots, w.block_size, w.k_scale, w.v_scale,
+                       k_head_scales=kh, v_head_scales=vh)
+    torch.cuda.synchronize()
+    _same(kc, kc_ref, "K codes")
+    _same(vc, vc_ref, "V codes")
+
+    msl = int(w.seq_lens.max())
+    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, Hkv, G, 7, 0, 64)
+    assert mp.chunks.num_partials > 0 and mp.split.max_pieces > 1, "both plans must leave partials"
+    plan_d = torch.from_numpy(mp.split.plan).cuda()
+    rows = torch.from_numpy(mp.decode_rows).cuda()
+    qs = _queries(st.q)
+
+    def step(out, q, k, v, lse, nl):
+        pkv.paged_attention_decode_split(out, q, k, v, st.bt_d, st.lens_d, plan_d, mp.split, Hkv, w.block_size, msl,
+                                         w.softmax_scale, w.k_scale, w.v_scale,
+                                         pkv.decode_split_workspace(mp.split, Hq, d, num_layers=nl), lse, rows=rows,
+                                         cu_seqlens_q=st.cu_d, k_head_scales=kh, v_head_scales=vh)
+        work, merges, cws = mp.chunks.to_device(d, num_layers=nl)
+        pkv.paged_attention_prefill_chunks(out, q, k, v, st.bt_d, st.lens_d, st.cu_d, work, merges,
+                                           mp.chunks.num_partials, cws, Hkv, w.block_size, msl, w.softmax_scale,
+                                           w.k_scale, w.v_scale, lse=lse, k_head_scales=kh, v_head_scales=vh)
+
+    ref = []
+    for l in range(NL):
+        out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        step(out, qs[l], kc[l], vc[l], lse, 1)
+        ref.append((out, lse))
+    out = torch.full((NL, T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((NL, T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    step(out, _strided(qs), kc, vc, lse, NL)
+    torch.cuda.synchronize()
+    for l in range(NL):
+        _same(out[l], ref[l][0], f"layer {l} output")
+        _same(lse[l], ref[l][1], f"layer {l} log-sum-exp")
+    _all_written(out, "mixed step with per-head scales")
 
 
 def test_layer_descriptor_errors():
