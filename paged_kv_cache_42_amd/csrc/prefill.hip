@@ -15,10 +15,6 @@
 //    and the second half of the item's key tiles, 32 rows per wave as two 16-row MFMA
 //    blocks, so every K and V fragment read from LDS feeds two MFMAs; at the end group 1
 //    hands its softmax states to group 0 through LDS, which merges them.
-//  * K/V tiles of 64 keys are staged per group in two LDS buffers (rows padded by 32
-//    bytes) with coalesced 16-byte loads, the next tile held in registers while the
-//    current one is computed; E4M3 rows are widened to bf16 on the way in. Block ids are
-//    scalar loads.
 //  * S^T = K.Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the packed
 //    queries as B): lane l holds row l%16 of its block for keys 4(l/16)+r of each
 //    16-key group. Online softmax per row (two shuffles for the tile maximum); masks only
@@ -27,6 +23,13 @@
 //    weights (two 16-key groups) are its B fragment, V^T comes straight from two
 //    ds_read_b64_tr_b16 at the same keys. The softmax reference maximum is lazy: it moves
 //    (and the accumulators are rescaled) only when a row's maximum grows by more than 2^8.
+//  * Two kernels share that arithmetic. chunk_pp_kernel (bf16 cache, head_dim 128):
+//    the groups run in opposite phases (matrix / softmax), tiles reach LDS by direct
+//    global-to-LDS loads into swizzled, unpadded rows. chunk_kernel (E4M3 caches, head_dim
+//    64): both groups compute each tile in step, tiles of 64 keys staged per group in two
+//    LDS buffers (rows padded by 32 bytes) with coalesced 16-byte loads, the next tile held
+//    in registers while the current one is computed; E4M3 rows are widened to bf16 on the
+//    way in. Block ids are scalar loads.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -118,6 +121,185 @@ struct Lds {
   static_assert(kXchg <= kBytes, "exchange fits in the tile buffers");
 };
 
+// This wave's 32 query rows of an item (block rb holds rows 32w + 16rb + l % 16 -> token
+// r / G, head r % G) as the B operands of S^T = K.Q^T, zero past the item's tokens, and
+// their positions in the sequence.
+template <int D>
+__device__ __forceinline__ void load_rows(const uint16_t* q, int row0, int q0, int ntok, int Hq, int g, int G,
+                                          int pos0, int w, int hl, int grp, int (&pos)[2], bool (&row_ok)[2],
+                                          bf16x8_t (&qf)[2][D / 32]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 32 * w + 16 * rb + hl;
+    const int tok = r / G;
+    row_ok[rb] = tok < ntok;
+    pos[rb] = pos0 + q0 + tok;
+    const uint16_t* qrow = q + (int64_t(row0 + q0 + min(tok, ntok - 1)) * Hq + int64_t(g) * G + r % G) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      if (!row_ok[rb]) v = make_uint4(0, 0, 0, 0);
+      qf[rb][kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+}
+
+// The weights of one 64-key tile for a wave's 32 rows (two 16-row blocks; lane l holds
+// row 16rb + l % 16 for keys key0 + 16kb + 4(l / 16) + r in sc[rb][kb][r]): masks where
+// the tile reaches a row's diagonal or the end of the keys (`full` false; the mask is
+// added to the raw score, 0 or -inf, since a select around the scaled score was compiled
+// into per-lane branches), the lazy reference maximum, the exponentials rounded to bf16
+// (two per word, the P^T fragments of P.V) and the row sums of those same rounded values.
+// Lazy maximum: a row's reference moves only when the tile holds a score above it by
+// more than kLazy (log2 units), so weights stay below 2^kLazy; the sum and the output
+// share the reference, so the result is the same. Each lane first checks its own 16
+// scores per row block; only when some lane of the wave sees such a score (the first
+// tile, then rarely) is the row maximum reduced across lanes and the state rescaled.
+template <int MT>
+__device__ __forceinline__ void tile_weights(f32x4_t (&sc)[2][4], int key0, bool full, const int (&pos)[2],
+                                             int key_end, int grp, float zscale, float (&m)[2], float (&lsum)[2],
+                                             f32x4_t (&o)[2][MT], uint32_t (&pw)[2][4][2]) {
+  if (!full) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * kb + 4 * grp + r;
+          sc[rb][kb][r] += ((key <= pos[rb]) & (key < key_end)) ? 0.f : -INFINITY;
+        }
+  }
+  float lm[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    // the scale is positive: the maximum of the raw scores, scaled once; a linear chain,
+    // so pairs fold into three-operand v_max3 (a tree did not)
+    float mx = sc[rb][0][0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[rb][e / 4][e % 4]);
+    lm[rb] = mx * zscale;
+  }
+  if (__any((lm[0] > m[0] + kLazy) | (lm[1] > m[1] + kLazy))) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float mx = lm[rb];
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool up = mx > m[rb] + kLazy;                  // false while the row has no key
+      const float mn = up ? mx : m[rb];
+      const float alpha = up ? pkv::fast_exp2(m[rb] - mn) : 1.f;
+      m[rb] = mn;
+      lsum[rb] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        o[rb][mt][0] *= alpha;
+        o[rb][mt][1] *= alpha;
+        o[rb][mt][2] *= alpha;
+        o[rb][mt][3] *= alpha;
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t p01 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][0], zscale, -mref)),
+                                           pkv::fast_exp2(fmaf(sc[rb][kb][1], zscale, -mref)));
+      const uint32_t p23 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][2], zscale, -mref)),
+                                           pkv::fast_exp2(fmaf(sc[rb][kb][3], zscale, -mref)));
+      // the sum uses the same bf16-rounded weights that enter P.V (two per dot2)
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), kOnes, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), kOnes, ps, false);
+      pw[rb][kb][0] = p01;
+      pw[rb][kb][1] = p23;
+    }
+    lsum[rb] += ps;
+  }
+}
+
+// End of an item: group 1 hands its row states (reference maximum, lane sums,
+// accumulators) to group 0 through LDS (`smem`, free of tiles by then), which merges them
+// by log-sum-exp: with M = max(m0, m1), o = o0 2^(m0 - M) + o1 2^(m1 - M), l likewise
+// (either group may have had no key). Group 0 then writes its rows: the bf16 output and
+// natural-log LSE, or for a split item the normalised partial and its log2-sum-exp.
+template <int D>
+__device__ __forceinline__ void chunk_finish(const ChunkArgs& a, const ChunkLayer& lp, uint8_t* smem, int gi, int w,
+                                             int lane, int g, int G, int Hq, int row0, int q0, int slot,
+                                             const bool (&row_ok)[2], float (&m)[2], float (&lsum)[2],
+                                             f32x4_t (&o)[2][D / 16]) {
+  constexpr int MT = D / 16;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  {
+    f32x4_t* xo = reinterpret_cast<f32x4_t*>(smem);
+    float* xm = reinterpret_cast<float*>(smem + kWaves * 2 * MT * 64 * 16);
+    float* xl = xm + kWaves * 2 * 64;
+    if (gi == 1) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xo[((w * 2 + rb) * MT + mt) * 64 + lane] = o[rb][mt];
+        xm[(w * 2 + rb) * 64 + lane] = m[rb];
+        xl[(w * 2 + rb) * 64 + lane] = lsum[rb];
+      }
+    }
+    __syncthreads();
+    if (gi == 1) return;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float m1 = xm[(w * 2 + rb) * 64 + lane];
+      const float l1 = xl[(w * 2 + rb) * 64 + lane];
+      const float M = fmaxf(m[rb], m1);
+      const float mref = M == -INFINITY ? 0.f : M;
+      const float c0 = pkv::fast_exp2(m[rb] - mref), c1 = pkv::fast_exp2(m1 - mref);
+      lsum[rb] = lsum[rb] * c0 + l1 * c1;
+      m[rb] = M;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4_t o1 = xo[((w * 2 + rb) * MT + mt) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[rb][mt][e] = fmaf(o[rb][mt][e], c0, o1[e] * c1);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float l = lsum[rb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!row_ok[rb]) continue;
+    const int r = 32 * w + 16 * rb + hl;
+    const float inv = l > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / l : 0.f;
+    if (slot >= 0) {                                       // partial of a split item
+      float* prow = lp.ws_o + (int64_t(slot) * kRows + r) * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        pkv::store_b128_untracked(prow + 16 * mt, o[rb][mt][0] * inv, o[rb][mt][1] * inv, o[rb][mt][2] * inv,
+                                  o[rb][mt][3] * inv);
+      if (grp == 0)
+        pkv::store_b32_untracked(lp.ws_lse + int64_t(slot) * kRows + r,
+                                 __float_as_uint(l > 0.f ? m[rb] + log2f(l) : -INFINITY));
+      continue;
+    }
+    const int row = row0 + q0 + r / G;
+    const int hq = g * G + r % G;
+    uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t lo = pack_bf16x2_rne(o[rb][mt][0] * inv, o[rb][mt][1] * inv);
+      const uint32_t hi = pack_bf16x2_rne(o[rb][mt][2] * inv, o[rb][mt][3] * inv);
+      pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
+    }
+    if (lp.lse && grp == 0)
+      pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + hq,
+                               __float_as_uint(l > 0.f ? (m[rb] + log2f(l)) * kLn2 : -INFINITY));
+  }
+}
+
 template <int CDT, int D, int BS>
 __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   constexpr int KS = D / 32;
@@ -174,20 +356,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   int pos[2];
   bool row_ok[2];
   bf16x8_t qf[2][KS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * w + 16 * rb + hl;
-    const int tok = r / G;
-    row_ok[rb] = tok < ntok;
-    pos[rb] = pos0 + q0 + tok;
-    const uint16_t* qrow = lp.q + (int64_t(row0 + q0 + min(tok, ntok - 1)) * Hq + int64_t(g) * G + r % G) * D + 8 * grp;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-      if (!row_ok[rb]) v = make_uint4(0, 0, 0, 0);
-      qf[rb][kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
+  load_rows<D>(lp.q, row0, q0, ntok, Hq, g, G, pos0, w, hl, grp, pos, row_ok, qf);
   // positions of the wave's first and last valid rows (uniform); -1: no valid row
   const int tok_first = (32 * w) / G;
   const int tok_last = min(ntok - 1, (32 * w + 31) / G);
@@ -316,75 +485,10 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
       if (kb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // reads of group kb + 1
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // MFMAs of group kb
     }
-    // masks only where the tile reaches a row's diagonal or the end of the keys (uniform
-    // branch); inside it the mask is added to the raw score (0 or -inf), since a select
-    // around the scaled score was compiled into per-lane branches
+    // masks only where the tile reaches a row's diagonal or the end of the keys (uniform)
     const bool full = key0 + kKeys - 1 <= wave_first && key0 + kKeys <= key_end;
-    if (!full) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 16 * kb + 4 * grp + r;
-            sc[rb][kb][r] += ((key <= pos[rb]) & (key < key_end)) ? 0.f : -INFINITY;
-          }
-    }
-    // Lazy maximum: a row's reference moves only when the tile holds a score above it by
-    // more than kLazy (log2 units), so weights stay below 2^kLazy; the sum and the output
-    // share the reference, so the result is the same. Each lane first checks its own 16
-    // scores per row block; only when some lane of the wave sees such a score (the first
-    // tile, then rarely) is the row maximum reduced across lanes and the state rescaled.
-    float lm[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      // the scale is positive: the maximum of the raw scores, scaled once; a linear chain,
-      // so pairs fold into three-operand v_max3 (a tree did not)
-      float mx = sc[rb][0][0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[rb][e / 4][e % 4]);
-      lm[rb] = mx * zscale_g;
-    }
-    if (__any((lm[0] > m[0] + kLazy) | (lm[1] > m[1] + kLazy))) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float mx = lm[rb];
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool up = mx > m[rb] + kLazy;                // false while the row has no key
-        const float mn = up ? mx : m[rb];
-        const float alpha = up ? pkv::fast_exp2(m[rb] - mn) : 1.f;
-        m[rb] = mn;
-        lsum[rb] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          o[rb][mt][0] *= alpha;
-          o[rb][mt][1] *= alpha;
-          o[rb][mt][2] *= alpha;
-          o[rb][mt][3] *= alpha;
-        }
-      }
-    }
     uint32_t pw[2][4][2];                                  // [rb][kb]: rounded weights, 2 per word
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t p01 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][0], zscale_g, -mref)),
-                                             pkv::fast_exp2(fmaf(sc[rb][kb][1], zscale_g, -mref)));
-        const uint32_t p23 = pack_bf16x2_rne(pkv::fast_exp2(fmaf(sc[rb][kb][2], zscale_g, -mref)),
-                                             pkv::fast_exp2(fmaf(sc[rb][kb][3], zscale_g, -mref)));
-        // the sum uses the same bf16-rounded weights that enter P.V (two per dot2)
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p01), kOnes, ps, false);
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p23), kOnes, ps, false);
-        pw[rb][kb][0] = p01;
-        pw[rb][kb][1] = p23;
-      }
-      lsum[rb] += ps;
-    }
+    tile_weights<MT>(sc, key0, full, pos, key_end, grp, zscale_g, m, lsum, o, pw);
     // O^T[d][row] += V^T[d][key] . P^T[key][row] per 32 keys on the 16x16x32 MFMA. The
     // contraction slots of lane l are 8(l/16) .. +7; they take keys 32j + 4(l/16) + r and
     // 32j + 16 + 4(l/16) + r (r < 4) - the lane's own weights of 16-key groups 2j and 2j+1 -
@@ -439,75 +543,315 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
       __syncthreads();
     }
   }
-  // ---- group 1 hands its row states (reference maximum, lane sums, accumulators) to
-  // group 0 through LDS, which merges them by log-sum-exp: with M = max(m0, m1),
-  // o = o0 2^(m0 - M) + o1 2^(m1 - M), l likewise. Either group may have had no key.
-  {
-    f32x4_t* xo = reinterpret_cast<f32x4_t*>(smem);
-    float* xm = reinterpret_cast<float*>(smem + kWaves * 2 * MT * 64 * 16);
-    float* xl = xm + kWaves * 2 * 64;
-    if (gi == 1) {
+  chunk_finish<D>(a, lp, smem, gi, w, lane, g, G, Hq, row0, q0, slot, row_ok, m, lsum, o);
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 cache, head_dim 128: the same items, rows and arithmetic as chunk_kernel, with
+// the two groups run in opposite phases. A group's step alternates a matrix phase
+// (P.V of tile t - 1 and S^T = K.Q^T of tile t on the MFMAs) and a softmax phase (the
+// weights of tile t on the vector ALUs); group 1 runs one phase behind group 0, so on
+// every SIMD one wave issues MFMAs while the other runs its softmax, and a workgroup
+// barrier ends each phase. Tiles reach LDS by direct loads (global_load_lds_dwordx4: a
+// wave's 64 lanes fill 1 KB of LDS, no registers in between), issued at the start of a
+// softmax phase into buffers the group has finished with, three phases before their
+// first use. LDS rows are 256 bytes, unpadded; 16-byte chunk c of key row r sits at
+// chunk position c ^ swz(r), so the K-fragment reads (16 rows, one chunk each) and the
+// transposing V reads (8 rows x 32 bytes per half wave) fall on distinct banks. Rows
+// past the item's keys or in blocks outside the pool are zeroed after their load lands.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(N), no other counter
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BS>
+__global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
+  constexpr int D = 128;
+  constexpr int KS = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int RW = 2 * D;                              // LDS bytes per key row
+  constexpr int TILE = kKeys * RW;
+  constexpr int GB = 4 * TILE;                           // per group: K0, K1, V0, V1
+  static_assert(Lds<D>::kXchg <= 2 * GB, "exchange fits in the tile buffers");
+  static_assert(BS == 16 || BS == 32, "a wave's 4 rows of one load stay in one block");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * GB];
+  typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
+  typedef __attribute__((address_space(3))) uint8_t* lds_u8;
+
+  const int4 it = a.work[2 * blockIdx.x];
+  const int4 it2 = a.work[2 * blockIdx.x + 1];
+  const int s = it.x;
+  const int g = it.y;
+  const int q0 = it.z;
+  const int slot = it2.y;
+  if (s < 0 || s >= a.num_seqs || g < 0 || g >= a.num_kv_heads || slot >= a.num_slots) return;
+  const float zscale_g = a.zscale_h[g & (pkv::kHeadScales - 1)];
+  const int row0 = a.cu_q[s];
+  const int qs = a.cu_q[s + 1] - row0;
+  if (qs <= 0 || row0 < 0 || row0 + qs > a.total_q || q0 < 0 || q0 >= qs) return;
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_clamp ? a.len_clamp : L);
+  if (qs > L) return;
+  const int key_end = max(0, min(it2.x, L));
+  const int key_lo = it.w;
+  if (key_lo < 0 || key_lo % kKeys != 0) return;
+  const ChunkLayer lp = chunk_layer(a);
+
+  const int gi = __builtin_amdgcn_readfirstlane(threadIdx.x / kGroupThreads);
+  const int tid = threadIdx.x % kGroupThreads;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * G;
+  const int pos0 = L - qs;
+  const int ntok = min(kRows / G, qs - q0);
+
+  int pos[2];
+  bool row_ok[2];
+  bf16x8_t qf[2][KS];
+  load_rows<D>(lp.q, row0, q0, ntok, Hq, g, G, pos0, w, hl, grp, pos, row_ok, qf);
+  const int tok_first = (32 * w) / G;
+  const int tok_last = min(ntok - 1, (32 * w + 31) / G);
+  const int wave_first = pos0 + q0 + tok_first;
+  const int wave_last = tok_first < ntok ? pos0 + q0 + tok_last : -1;
+
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4_t o[2][MT];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xo[((w * 2 + rb) * MT + mt) * 64 + lane] = o[rb][mt];
-        xm[(w * 2 + rb) * 64 + lane] = m[rb];
-        xl[(w * 2 + rb) * 64 + lane] = lsum[rb];
-      }
+    for (int mt = 0; mt < MT; ++mt) o[rb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const cptr_i32 btc = (cptr_i32)(uintptr_t)(a.block_tables + int64_t(s) * a.table_width);
+  const int64_t row_bytes = int64_t(Hkv) * D * 2;
+  const int64_t head_off = int64_t(g) * D * 2;
+  const int64_t block_bytes = int64_t(BS) * row_bytes;
+  const int t_lo = key_lo / kKeys;
+  const int t_hi = (key_end + kKeys - 1) / kKeys;
+  const int n_half = (max(t_hi - t_lo, 0) + 1) / 2;
+  const int my_t0 = gi == 0 ? t_lo : t_lo + n_half;
+  const int my_n = gi == 0 ? n_half : max(t_hi - t_lo - n_half, 0);
+  const int my_key_end = gi == 0 ? min(key_end, (t_lo + n_half) * kKeys) : key_end;
+
+  // ---- direct loads: load i of wave w fills rows 16i + 4w .. +3 of a tile; lane l
+  // writes row 16i + 4w + l/16, chunk position l % 16, so it loads data chunk
+  // (l % 16) ^ swz(row) of that key's head row
+  uint8_t* const gs = smem + gi * GB;
+  const uint32_t gs_lds = uint32_t(uintptr_t((lds_u8)gs));
+  const int drow = 4 * w + (lane >> 4);
+  const uint32_t dvoff = uint32_t(drow * row_bytes + head_off + 16 * ((lane & 15) ^ swz(drow)));
+  // The block ids of tile u's four loads (-1 past the keys; the table is read in bounds,
+  // clamped to the last block that holds a key).
+  const int last_bi = max(my_key_end - 1, 0) / BS;
+  auto ids = [&](int u, int (&b)[4]) {
+    int v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = btc[min((u * kKeys + 16 * i) / BS, last_bi)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (u * kKeys + 16 * i) / BS <= last_bi ? v[i] : -1;
+  };
+  // Issue one plane's four loads of a tile into LDS buffer `buf` (load i: the block of
+  // id blk[i], rows 16i + 4w .. +3; block 0 where the id is past the keys or outside the
+  // pool). M0 holds the LDS address; an SALU write of M0 needs one wait state before a
+  // load reads it. Returns the mask of loads whose block is in the pool.
+  auto dma = [&](const uint8_t* plane, const int (&blk)[4], uint32_t buf) -> int {
+    int vm = 0;
+    const uint8_t* base[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = uint32_t(blk[i]) < uint32_t(a.num_blocks);
+      vm |= ok ? (1 << i) : 0;
+      base[i] = plane + uint64_t(ok ? uint32_t(blk[i]) : 0u) * uint32_t(block_bytes) +
+                (BS == 32 && (i & 1) ? 16 * row_bytes : 0);
     }
-    __syncthreads();
-    if (gi == 1) return;
+    const uint32_t m0 = gs_lds + buf + 4 * w * RW;
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_add_u32 m0, m0, 0x1000\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %4\n\t"
+        "s_add_u32 m0, m0, 0x1000\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %5\n\t"
+        "s_add_u32 m0, m0, 0x1000\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(m0), "v"(dvoff), "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3])
+        : "memory");
+    return vm;
+  };
+  auto bad = [&](int u, int vm) { return vm != 15 || u * kKeys + kKeys > my_key_end; };
+  // zero this lane's rows of tile u that are past the keys or whose block was not loaded
+  auto fix = [&](int u, uint32_t buf, int vm) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float m1 = xm[(w * 2 + rb) * 64 + lane];
-      const float l1 = xl[(w * 2 + rb) * 64 + lane];
-      const float M = fmaxf(m[rb], m1);
-      const float mref = M == -INFINITY ? 0.f : M;
-      const float c0 = pkv::fast_exp2(m[rb] - mref), c1 = pkv::fast_exp2(m1 - mref);
-      lsum[rb] = lsum[rb] * c0 + l1 * c1;
-      m[rb] = M;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = ((vm >> i) & 1) && u * kKeys + 16 * i + drow < my_key_end;
+      if (!ok) *reinterpret_cast<uint4*>(gs + buf + (16 * i + 4 * w) * RW + 16 * lane) = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto kbuf = [&](int t) -> uint32_t { return uint32_t((t & 1) * TILE); };
+  auto vbuf = [&](int t) -> uint32_t { return uint32_t(2 * TILE + (t & 1) * TILE); };
+
+  // per-lane LDS offsets: K fragment kk of row 16kb + hl sits at chunk (4kk + grp) ^ swz(hl);
+  // V^T read of row 32j + 16h + 4grp + hl/4, data chunk 2mt + (hl/2)%2
+  const int kswz = grp ^ swz(hl);
+  const int vrow = 4 * grp + (hl >> 2);
+  const int vswz = ((hl >> 1) & 1) ^ swz(vrow);
+
+  f32x4_t sc[2][4];
+  uint32_t pw[2][4][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pw[rb][kb][0] = 0u;
+      pw[rb][kb][1] = 0u;
+    }
+
+  // matrix phase of step t: O^T += V^T(t - 1).P^T(t - 1) (weights of step t - 1, zero at
+  // t = 0 over the loaded V(0)), and S^T(t) = K(t).Q^T (discarded past the last tile)
+  auto gemm = [&](int t) {
+    const uint8_t* kt = gs + kbuf(t);
+    const uint8_t* vt = gs + vbuf(t > 0 ? t - 1 : 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0][2 * j][0], pw[0][2 * j][1],
+                                                                     pw[0][2 * j + 1][0], pw[0][2 * j + 1][1]));
+      const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, make_uint4(pw[1][2 * j][0], pw[1][2 * j][1],
+                                                                     pw[1][2 * j + 1][0], pw[1][2 * j + 1][1]));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const f32x4_t o1 = xo[((w * 2 + rb) * MT + mt) * 64 + lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[rb][mt][e] = fmaf(o[rb][mt][e], c0, o1[e] * c1);
+        const int coff = 16 * ((2 * mt) ^ vswz) + 8 * (hl & 1);
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + (32 * j + vrow) * RW + coff));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + (32 * j + 16 + vrow) * RW + coff));
+        const uint2 u0 = __builtin_bit_cast(uint2, v0), u1 = __builtin_bit_cast(uint2, v1);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+        o[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb0, o[0][mt], 0, 0, 0);
+        o[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb1, o[1][mt], 0, 0, 0);
       }
     }
-  }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8_t kf[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8_t*>(kt + (16 * kb + hl) * RW + 16 * ((4 * kk) ^ kswz));
+      sc[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sc[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        sc[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[0][kk], sc[0][kb], 0, 0, 0);
+        sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[1][kk], sc[1][kb], 0, 0, 0);
+      }
+    }
+    // order for the scheduler: V reads four fragments ahead of their MFMAs, the K reads
+    // of 16-key group 0 over the last P.V fragments, those of group kb + 1 before the
+    // MFMAs of group kb (left alone, it hoists every read and runs out of registers)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int f = 0; f < 2 * MT; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (f + 4 < 2 * MT)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
+    }
+  };
 
+  // softmax phase of step t: the rounded weights of tile t (zero when every key of the
+  // tile is past every row of the wave); lazy reference maximum as in chunk_kernel
+  auto softmax = [&](int t) {
+    const int key0 = t * kKeys;
+    if (key0 > wave_last) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float l = lsum[rb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (!row_ok[rb]) continue;
-    const int r = 32 * w + 16 * rb + hl;
-    const float inv = l > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / l : 0.f;
-    if (slot >= 0) {                                       // partial of a split item
-      float* prow = lp.ws_o + (int64_t(slot) * kRows + r) * D + 4 * grp;
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        pkv::store_b128_untracked(prow + 16 * mt, o[rb][mt][0] * inv, o[rb][mt][1] * inv, o[rb][mt][2] * inv,
-                                  o[rb][mt][3] * inv);
-      if (grp == 0)
-        pkv::store_b32_untracked(lp.ws_lse + int64_t(slot) * kRows + r,
-                                 __float_as_uint(l > 0.f ? m[rb] + log2f(l) : -INFINITY));
-      continue;
+        for (int kb = 0; kb < 4; ++kb) {
+          pw[rb][kb][0] = 0u;
+          pw[rb][kb][1] = 0u;
+        }
+      return;
     }
-    const int row = row0 + q0 + r / G;
-    const int hq = g * G + r % G;
-    uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t lo = pack_bf16x2_rne(o[rb][mt][0] * inv, o[rb][mt][1] * inv);
-      const uint32_t hi = pack_bf16x2_rne(o[rb][mt][2] * inv, o[rb][mt][3] * inv);
-      pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
+    const bool full = key0 + kKeys - 1 <= wave_first && key0 + kKeys <= key_end;
+    tile_weights<MT>(sc, key0, full, pos, key_end, grp, zscale_g, m, lsum, o, pw);
+  };
+
+  // ---- the loop: step t = matrix phase t, barrier, softmax phase t, barrier, the same
+  // code in both groups; group 1 takes one extra barrier before it and group 0 one
+  // after, so each phase of one group meets the opposite phase of the other. Loads: K(0),
+  // V(0), K(1) before the loop; softmax phase t issues K(t + 2) and V(t + 1), then waits
+  // for K(t + 1) and V(t) (the next matrix phase's) and zeroes their bad rows.
+  const uint8_t* const kpl = lp.kc;
+  const uint8_t* const vpl = lp.vc;
+  int vmk1 = 15;                 // block mask of K tile t + 1 (issued, not yet checked)
+  int vmv0 = 15;                 // of V tile t
+  int bk[4], bv[4];              // block ids of the next K and V loads (tiles t + 2, t + 1)
+  if (my_n > 0) {
+    int b[4];
+    ids(my_t0, b);
+    const int k0 = dma(kpl, b, kbuf(0));
+    vmv0 = dma(vpl, b, vbuf(0));
+    if (my_n > 1) {
+      ids(my_t0 + 1, b);
+      vmk1 = dma(kpl, b, kbuf(1));
+      wait_vmcnt<4>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (lp.lse && grp == 0)
-      pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + hq,
-                               __float_as_uint(l > 0.f ? (m[rb] + log2f(l)) * kLn2 : -INFINITY));
+    if (bad(my_t0, k0)) fix(my_t0, kbuf(0), k0);
+    if (bad(my_t0, vmv0)) fix(my_t0, vbuf(0), vmv0);
   }
+  __syncthreads();
+  if (gi == 1) __syncthreads();
+  for (int t = 0; t <= n_half; ++t) {
+    if (my_n > 0 && t <= my_n) gemm(t);
+    if (t + 2 < my_n) ids(my_t0 + t + 2, bk);
+    if (t + 1 < my_n) ids(my_t0 + t + 1, bv);
+    __syncthreads();
+    if (t < my_n) {
+      int vmk_new = 15, vmv_new = 15;
+      if (t + 2 < my_n) vmk_new = dma(kpl, bk, kbuf(t + 2));
+      if (t + 1 < my_n) vmv_new = dma(vpl, bv, vbuf(t + 1));
+      __builtin_amdgcn_sched_barrier(0);                   // every load issued before the softmax
+      softmax(my_t0 + t);
+      if (t + 2 < my_n)
+        wait_vmcnt<8>();
+      else if (t + 1 < my_n)
+        wait_vmcnt<4>();
+      else
+        wait_vmcnt<0>();
+      // K(t + 1) and V(t) are in LDS now (both issued one softmax phase earlier)
+      if (t + 1 < my_n && bad(my_t0 + t + 1, vmk1)) fix(my_t0 + t + 1, kbuf(t + 1), vmk1);
+      if (bad(my_t0 + t, vmv0)) fix(my_t0 + t, vbuf(t), vmv0);
+      vmk1 = vmk_new;
+      vmv0 = vmv_new;
+    }
+    __syncthreads();
+  }
+  if (gi == 0) __syncthreads();
+  chunk_finish<D>(a, lp, smem, gi, w, lane, g, G, Hq, row0, q0, slot, row_ok, m, lsum, o);
 }
+
 
 // Log-sum-exp merge of the partials of split items. Merge record: (seq, KV head,
 // first new token, first slot | pieces << 20). One thread per (row of the 128, four
@@ -738,6 +1082,7 @@ int prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cach
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED, "prefill_chunks: head_dim %d / block_size %d not supported", head_dim,
                 block_size);
+  if (cache_dtype == PKV_BF16 && head_dim == 128) fn = block_size == 16 ? chunk_pp_kernel<16> : chunk_pp_kernel<32>;
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return fail(PKV_ERR_INVALID, "prefill_chunks: scales must be > 0");
   if (num_work == 0 || num_seqs == 0 || total_q == 0) return PKV_OK;
