@@ -556,11 +556,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
 // wave's 64 lanes fill 1 KB of LDS, no registers in between), issued at the start of a
 // softmax phase into buffers the group has finished with, three phases before their
 // first use. LDS rows are 256 bytes, unpadded; 16-byte chunk c of key row r sits at
-// chunk position c ^ swz(r), so the K-fragment reads (16 rows, one chunk each) and the
-// transposing V reads (8 rows x 32 bytes per half wave) fall on distinct banks. Rows
+// chunk position c ^ swz_k(r) in K tiles and c ^ swz_v(r) in V tiles, so the K-fragment
+// reads and the transposing V reads fall on distinct banks. Rows
 // past the item's keys or in blocks outside the pool are zeroed after their load lands.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Chunk positions of the two planes: a K-fragment read takes one chunk of 16 rows, and
+// ds_read_b128 serves 8 lanes at a time, so 8 consecutive rows must land on 8 distinct
+// chunk positions of an aligned group of 8 (r mod 16 does; 2(r mod 8) + (r / 8) mod 2 cost
+// ~590 bank-conflict cycles per wave). A transposing V read takes 32 bytes (a chunk pair)
+// of 8 rows per half wave: 2(r mod 8) + (r / 8) mod 2 gives them distinct pairs.
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // s_waitcnt vmcnt(N), no other counter
 template <int N>
@@ -643,11 +649,12 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
 
   // ---- direct loads: load i of wave w fills rows 16i + 4w .. +3 of a tile; lane l
   // writes row 16i + 4w + l/16, chunk position l % 16, so it loads data chunk
-  // (l % 16) ^ swz(row) of that key's head row
+  // (l % 16) ^ swz(row) of that key's head row (swz_k or swz_v by plane)
   uint8_t* const gs = smem + gi * GB;
   const uint32_t gs_lds = uint32_t(uintptr_t((lds_u8)gs));
   const int drow = 4 * w + (lane >> 4);
-  const uint32_t dvoff = uint32_t(drow * row_bytes + head_off + 16 * ((lane & 15) ^ swz(drow)));
+  const uint32_t dvoff_k = uint32_t(drow * row_bytes + head_off + 16 * ((lane & 15) ^ swz_k(drow)));
+  const uint32_t dvoff_v = uint32_t(drow * row_bytes + head_off + 16 * ((lane & 15) ^ swz_v(drow)));
   // The block ids of tile u's four loads (-1 past the keys; the table is read in bounds,
   // clamped to the last block that holds a key).
   const int last_bi = max(my_key_end - 1, 0) / BS;
@@ -662,7 +669,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
   // id blk[i], rows 16i + 4w .. +3; block 0 where the id is past the keys or outside the
   // pool). M0 holds the LDS address; an SALU write of M0 needs one wait state before a
   // load reads it. Returns the mask of loads whose block is in the pool.
-  auto dma = [&](const uint8_t* plane, const int (&blk)[4], uint32_t buf) -> int {
+  auto dma = [&](const uint8_t* plane, const int (&blk)[4], uint32_t buf, uint32_t voff) -> int {
     int vm = 0;
     const uint8_t* base[4];
 #pragma unroll
@@ -690,7 +697,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
         "global_load_lds_dwordx4 %2, %6\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(save)
-        : "s"(m0), "v"(dvoff), "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3])
+        : "s"(m0), "v"(voff), "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3])
         : "memory");
     return vm;
   };
@@ -706,11 +713,11 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
   auto kbuf = [&](int t) -> uint32_t { return uint32_t((t & 1) * TILE); };
   auto vbuf = [&](int t) -> uint32_t { return uint32_t(2 * TILE + (t & 1) * TILE); };
 
-  // per-lane LDS offsets: K fragment kk of row 16kb + hl sits at chunk (4kk + grp) ^ swz(hl);
+  // per-lane LDS offsets: K fragment kk of row 16kb + hl sits at chunk (4kk + grp) ^ swz_k(hl);
   // V^T read of row 32j + 16h + 4grp + hl/4, data chunk 2mt + (hl/2)%2
-  const int kswz = grp ^ swz(hl);
+  const int kswz = grp ^ swz_k(hl);
   const int vrow = 4 * grp + (hl >> 2);
-  const int vswz = ((hl >> 1) & 1) ^ swz(vrow);
+  const int vswz = ((hl >> 1) & 1) ^ swz_v(vrow);
 
   f32x4_t sc[2][4];
   uint32_t pw[2][4][2];
@@ -809,11 +816,11 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
   if (my_n > 0) {
     int b[4];
     ids(my_t0, b);
-    const int k0 = dma(kpl, b, kbuf(0));
-    vmv0 = dma(vpl, b, vbuf(0));
+    const int k0 = dma(kpl, b, kbuf(0), dvoff_k);
+    vmv0 = dma(vpl, b, vbuf(0), dvoff_v);
     if (my_n > 1) {
       ids(my_t0 + 1, b);
-      vmk1 = dma(kpl, b, kbuf(1));
+      vmk1 = dma(kpl, b, kbuf(1), dvoff_k);
       wait_vmcnt<4>();
     } else {
       wait_vmcnt<0>();
@@ -830,8 +837,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
     __syncthreads();
     if (t < my_n) {
       int vmk_new = 15, vmv_new = 15;
-      if (t + 2 < my_n) vmk_new = dma(kpl, bk, kbuf(t + 2));
-      if (t + 1 < my_n) vmv_new = dma(vpl, bv, vbuf(t + 1));
+      if (t + 2 < my_n) vmk_new = dma(kpl, bk, kbuf(t + 2), dvoff_k);
+      if (t + 1 < my_n) vmv_new = dma(vpl, bv, vbuf(t + 1), dvoff_v);
       __builtin_amdgcn_sched_barrier(0);                   // every load issued before the softmax
       softmax(my_t0 + t);
       if (t + 2 < my_n)
