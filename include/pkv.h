@@ -366,7 +366,9 @@ int pkv_build_varlen_work(int32_t num_seqs, const int32_t* q_lens, const int32_t
  * (device int32 [num_seqs+1], total_q rows in all); its new row i sits at position
  * seq_lens[s] - q_s + i and sees keys 0 .. that position (bottom-right causal; the step's
  * K/V are already in the cache). q, out: device bf16 [total_q][num_q_heads][head_dim].
- * Cache, block_tables, seq_lens, scales, num_blocks, max_seq_len: as for decode.
+ * Cache, block_tables, seq_lens, scales, num_blocks, max_seq_len: as for decode, except
+ * that table entries outside 0..num_blocks-1 (never dereferenced) read as zero keys and
+ * values here, where decode skips their keys.
  * work_items: device int32 [num_work][4] from pkv_build_varlen_work for the same q_lens
  * and seq_lens (rows not covered by an item are not written). lse_out: device float
  * [total_q][num_q_heads], nullable (natural log). Supported: bf16 queries with a bf16
@@ -445,8 +447,10 @@ int64_t pkv_chunk_workspace_bytes(int32_t num_partials, int32_t head_dim);
  * workgroup per item (128 GQA-packed query rows; two groups of 4 waves take the first and
  * the second half of the item's 64-key tiles on MFMA and merge their softmax states), then
  * a merge kernel writes the rows of split blocks. Rows of sequences with q < 2 are not
- * written. Supported: bf16 queries with a bf16 or E4M3 cache, head_dim 64/128,
- * block_size 16/32, group 1/2/4/8/16. Calls sharing a workspace must not overlap. */
+ * written (with a bf16 cache at head_dim 128 the two groups run in opposite phases,
+ * one on the MFMAs while the other computes its softmax). Supported: bf16 queries with a
+ * bf16 or E4M3 cache, head_dim 64/128, block_size 16/32, group 1/2/4/8/16. Calls sharing a
+ * workspace must not overlap. */
 int pkv_paged_attention_prefill_chunks(void* out, const void* q, int32_t q_dtype,
                                        const void* k_cache, const void* v_cache,
                                        int32_t cache_dtype, const int32_t* block_tables,
