@@ -717,7 +717,18 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
   constexpr int NV = (D / 4) * EB / 16;
   constexpr int SUB = BS / 16;
-  constexpr int RS = D * 2 + 32;
+  constexpr int RS = D * 2 + 32;            // LDS row stride of the bf16 V tile
+  constexpr int RSK = D * 2 + 16;           // LDS row stride of the bf16 K tile
+  // Load shape: HB bytes of this KV head per token row. One load instruction covers LPR
+  // lanes x 16 bytes of each of RPI rows: whole 128-byte lines when HB >= 128, so the
+  // non-temporal hint never leaves the other half of a line to a later instruction (with
+  // half lines per instruction it made the stream slower, with whole lines faster).
+  constexpr int HB = D * EB;
+  constexpr int LPR = HB >= 128 ? 8 : HB / 16;
+  constexpr int RPI = 64 / LPR;
+  constexpr int HPR = HB / (16 * LPR);      // loads per group of RPI rows
+  constexpr bool kStream = LPR == 8;
+  static_assert(NV == (16 / RPI) * HPR, "load shape must cover the tile");
   typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
 
   const int lane = threadIdx.x & 63;
@@ -735,10 +746,15 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   const uint8_t* kc = lp.kc;
   const uint8_t* vc = lp.vc;
   const int64_t row_bytes = int64_t(Hkv) * D * EB;
-  const int64_t lane_off = int64_t(g) * D * EB + 16 * grp;
+  const int lrow = lane / LPR;               // row of this lane in each load
+  const int lchunk = lane % LPR;             // 16-byte chunk of the head slice
+  const int64_t lane_off = int64_t(lrow) * row_bytes + int64_t(g) * HB + 16 * lchunk;
+  const int64_t group_step = int64_t(RPI) * row_bytes;
 
-  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[HPW][16 * RS];
-  uint8_t* my_vt = vt_lds[w];
+  // per wave: the K tile (16 rows, stride RSK) then the V tile (16 rows, stride RS)
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[HPW][16 * (RSK + RS)];
+  uint8_t* my_kt = kv_lds[w];
+  uint8_t* my_vt = kv_lds[w] + 16 * RSK;
 
   // ---- issue cursor: the piece whose tiles are being loaded. Slot j owns global tiles
   // [slot_lo[j], slot_lo[j + 1]) of the sequences' tiles laid end to end; a piece is the
@@ -807,8 +823,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const uint16_t* qrow = lp.q + (int64_t(row < 0 ? 0 : row) * Hq + int64_t(g) * G + hl_q) * D;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const int d0 = EB == 2 ? 32 * kk + 8 * grp : 64 * (kk / 2) + 16 * grp + 8 * (kk % 2);
-      qtmp[kk] = *reinterpret_cast<const uint4*>(qrow + d0);
+      qtmp[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * grp);
     }
     q_pending = true;
     return true;
@@ -846,7 +861,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const bool any = live && tok_lo < i_te;
     const int blk = any ? i_bt[ti / SUB] : -1;
     const bool ok = any && blk >= 0 && blk < a.num_blocks;
-    const int64_t off = (int64_t(ok ? blk : 0) * BS + (ti % SUB) * 16 + hl) * row_bytes + lane_off;
+    const int64_t off = (int64_t(ok ? blk : 0) * BS + (ti % SUB) * 16) * row_bytes + lane_off;
     sl_t0[k] = tok_lo;
     sl_ok[k] = ok;
     sl_row[k] = i_row;
@@ -864,8 +879,14 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      kr[i] = *reinterpret_cast<const uint4*>(kc + off + 64 * i);
-      vr[i] = *reinterpret_cast<const uint4*>(vc + off + 64 * i);
+      const int64_t o = off + (i / HPR) * group_step + (i % HPR) * (16 * LPR);
+      if constexpr (kStream) {
+        kr[i] = pkv::load_b128_stream(kc + o);
+        vr[i] = pkv::load_b128_stream(vc + o);
+      } else {
+        kr[i] = *reinterpret_cast<const uint4*>(kc + o);
+        vr[i] = *reinterpret_cast<const uint4*>(vc + o);
+      }
     }
     return live;
   };
@@ -890,27 +911,18 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     const int t0 = sl_t0[k];
     const int tok_end = sl_te[k];
     const bool ok = sl_ok[k];
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (CDT == PKV_BF16) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[kk]), qf[kk], sc, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const uint4 lo = pkv::fp8x8_to_bf16x8(kr[i].x, kr[i].y);
-        const uint4 hi = pkv::fp8x8_to_bf16x8(kr[i].z, kr[i].w);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qf[2 * i], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qf[2 * i + 1], sc, 0, 0, 0);
-      }
-    }
     {
-      // Rows past the end are zeroed by masking, not by a branch: every lane waits for
-      // its rows on the main path, so no later wait is made conservative by a skipped one.
-      const uint32_t keep = (ok && (t0 + hl < tok_end)) ? 0xffffffffu : 0u;
-      uint8_t* dst = my_vt + hl * RS;
+      // K and V rows -> LDS as bf16 [token][head_dim] (E4M3 widened on the way). V rows
+      // past the end are zeroed by masking, not by a branch: every lane waits for its rows
+      // on the main path, so no later wait is made conservative by a skipped one (a stale
+      // slot may hold NaN, and 0 x NaN would reach the output). K rows past the end only
+      // give scores that are masked below.
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
+        const int r = (i / HPR) * RPI + lrow;
+        const int c = (i % HPR) * LPR + lchunk;
+        const uint32_t keep = (ok && (t0 + r < tok_end)) ? 0xffffffffu : 0u;
+        const uint4 kv = kr[i];
         uint4 v = vr[i];
         asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
         v.x &= keep;
@@ -918,12 +930,24 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
         v.z &= keep;
         v.w &= keep;
         if constexpr (CDT == PKV_BF16) {
-          *reinterpret_cast<uint4*>(dst + 2 * (32 * i + 8 * grp)) = v;
+          *reinterpret_cast<uint4*>(my_kt + r * RSK + 16 * c) = kv;
+          *reinterpret_cast<uint4*>(my_vt + r * RS + 16 * c) = v;
         } else {
-          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp)) = pkv::fp8x8_to_bf16x8(v.x, v.y);
-          *reinterpret_cast<uint4*>(dst + 2 * (64 * i + 16 * grp) + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+          *reinterpret_cast<uint4*>(my_kt + r * RSK + 32 * c) = pkv::fp8x8_to_bf16x8(kv.x, kv.y);
+          *reinterpret_cast<uint4*>(my_kt + r * RSK + 32 * c + 16) = pkv::fp8x8_to_bf16x8(kv.z, kv.w);
+          *reinterpret_cast<uint4*>(my_vt + r * RS + 32 * c) = pkv::fp8x8_to_bf16x8(v.x, v.y);
+          *reinterpret_cast<uint4*>(my_vt + r * RS + 32 * c + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
         }
       }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // S = K.Q^T: the A operand is K in its MFMA layout (token hl, head_dim 32kk + 8grp ..),
+    // read back from the K tile; the B operand is the packed queries in the same order
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 kf = *reinterpret_cast<const uint4*>(my_kt + hl * RSK + 64 * kk + 16 * grp);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], sc, 0, 0, 0);
     }
     float z[4];
 #pragma unroll
