@@ -867,10 +867,11 @@ def main():
     res["pct_of_measured_read_peak"] = round(100 * gbs / rp, 2)
     if not args.no_decode_variants:
         # the other decode shapes the workloads name: config 3 with an E4M3 cache (half the
-        # bytes) and config 4 (long contexts, split context merged by log-sum-exp)
+        # bytes) and config 4 (long contexts, split context merged by log-sum-exp), bf16 and E4M3
         res["decode_variants"] = {}
         for name, wv in (("cfg3_e4m3_cache", dataclasses.replace(workloads.config3(), cache_dtype="fp8")),
-                         ("cfg4_long_context_bf16", workloads.config4())):
+                         ("cfg4_long_context_bf16", workloads.config4()),
+                         ("cfg4_e4m3_cache", dataclasses.replace(workloads.config4(), cache_dtype="fp8"))):
             print(f"[bench] decode variant {name}", file=sys.stderr, flush=True)
             res["decode_variants"][name] = decode_record(wv, wv.partition_size, "split", K, args.warmup)
     if not args.no_mixed:

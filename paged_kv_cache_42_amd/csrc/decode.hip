@@ -956,8 +956,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
       z[r] = (ok && t < tok_end) ? sc[r] * zscale_g : -INFINITY;
     }
     float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
+    mt_ = pkv::lane_groups_max(mt_);
     const float mn = fmaxf(m, mt_);
     const float mref = mn == -INFINITY ? 0.f : mn;
     const float alpha = pkv::fast_exp2(m - mref);
@@ -985,8 +984,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     if (!sl_last[k]) return;
     // ---- the item's last tile: write its output (or partition partial)
     float l = lsum;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = pkv::lane_groups_sum(l);
     if (!sl_valid[k] || hl >= G) return;
     const int hq = g * G + hl;
     const float inv = l > 0.f ? a.vscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)] / l : 0.f;

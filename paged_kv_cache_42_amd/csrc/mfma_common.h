@@ -61,6 +61,25 @@ __device__ __forceinline__ void store_b128_untracked(void* p, float x, float y, 
   asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 
+// Maximum and sum over the four lane groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
+// with gfx950's row swaps: v_permlane16_swap exchanges 16-lane rows 1 <-> 0 and 3 <-> 2
+// between its two operands, v_permlane32_swap rows 2, 3 <-> 0, 1, so swapping a value
+// with itself and combining the two results pairs lane l with l ^ 16, then with l ^ 32
+// (the same pairs, in the same order, as two xor shuffles). They are ALU instructions,
+// where a shuffle through ds_bpermute is an LDS round trip. Every lane must be active.
+__device__ __forceinline__ float lane_groups_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_groups_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // One 16-byte load with the non-temporal hint (global_load_dwordx4 ... nt), for data a
 // launch reads exactly once: the K/V rows of the decode stream. On MI355X a streaming
 // read of a large buffer runs 12-15% faster with this hint than with the default policy.
@@ -203,8 +222,7 @@ __device__ __forceinline__ void decode_wave(const DecodeWaveIn& in, uint8_t* my_
       z[r] = (ok && t < tok_end) ? sc[r] * in.zscale : -INFINITY;
     }
     float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
+    mt_ = lane_groups_max(mt_);
     const float mn = fmaxf(m, mt_);
     const float mref = mn == -INFINITY ? 0.f : mn;
     const float alpha = pkv::fast_exp2(m - mref);
@@ -246,8 +264,7 @@ __device__ __forceinline__ void decode_wave(const DecodeWaveIn& in, uint8_t* my_
   }
 
   // lane-partial sums over the 4 lane groups (m is uniform per head across them)
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = lane_groups_sum(lsum);
 }
 
 }  // namespace pkv

@@ -184,8 +184,7 @@ __device__ __forceinline__ void tile_weights(f32x4_t (&sc)[2][4], int key0, bool
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float mx = lm[rb];
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pkv::lane_groups_max(mx);
       const bool up = mx > m[rb] + kLazy;                  // false while the row has no key
       const float mn = up ? mx : m[rb];
       const float alpha = up ? pkv::fast_exp2(m[rb] - mn) : 1.f;
@@ -269,8 +268,7 @@ __device__ __forceinline__ void chunk_finish(const ChunkArgs& a, const ChunkLaye
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float l = lsum[rb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = pkv::lane_groups_sum(l);
     if (!row_ok[rb]) continue;
     const int r = 32 * w + 16 * rb + hl;
     const float inv = l > 0.f ? a.vscale_h[g & (pkv::kHeadScales - 1)] / l : 0.f;

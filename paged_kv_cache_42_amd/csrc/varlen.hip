@@ -293,8 +293,7 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
     float mt_ = z[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt_ = fmaxf(mt_, z[j]);
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 16));
-    mt_ = fmaxf(mt_, __shfl_xor(mt_, 32));
+    mt_ = pkv::lane_groups_max(mt_);
     const float mn = fmaxf(m, mt_);
     const float mref = mn == -INFINITY ? 0.f : mn;
     const float alpha = pkv::fast_exp2(m - mref);
@@ -345,8 +344,7 @@ __device__ __forceinline__ void run_prefill_item(const VarlenArgs& a, uint8_t* s
   }
 
   float l = lsum;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = pkv::lane_groups_sum(l);
   if (!row_ok) return;
   const int row = row0 + q0 + tok;
   const int hq = g * G + r_row % G;
