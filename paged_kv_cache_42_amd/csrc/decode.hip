@@ -698,6 +698,9 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
 // Tiles in each wave's load ring of the balanced-split kernel: while one is consumed,
 // NS - 1 are in flight.
 constexpr int kSplitRing = 2;
+// Tiles folded per softmax step of the balanced-split kernel: two for E4M3 caches, whose
+// 16-token tiles carry half the bytes of bf16 ones through the same per-tile work.
+constexpr int split_tps(int cdt) { return cdt == PKV_FP8_E4M3 ? 2 : 1; }
 
 // Balanced split decode (bf16 queries; bf16 or E4M3 cache). The context of every
 // sequence is cut into 16-token tiles and the tiles of all sequences are laid end to
@@ -710,7 +713,7 @@ constexpr int kSplitRing = 2;
 // boundaries (the next piece's queries and first tile are in flight while the last
 // tile of the current one is consumed). Per-tile work is that of decode_wave.
 // ---------------------------------------------------------------------------------
-template <int CDT, int D, int BS, int HPW, int NS = kSplitRing>
+template <int CDT, int D, int BS, int HPW, int NS = kSplitRing, int TPS = 1>
 __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
@@ -729,6 +732,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   constexpr int HPR = HB / (16 * LPR);      // loads per group of RPI rows
   constexpr bool kStream = LPR == 8;
   static_assert(NV == (16 / RPI) * HPR, "load shape must cover the tile");
+  static_assert(TPS == 1 || TPS == 2, "one or two tiles per step");
   typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
 
   const int lane = threadIdx.x & 63;
@@ -751,10 +755,10 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   const int64_t lane_off = int64_t(lrow) * row_bytes + int64_t(g) * HB + 16 * lchunk;
   const int64_t group_step = int64_t(RPI) * row_bytes;
 
-  // per wave: the K tile (16 rows, stride RSK) then the V tile (16 rows, stride RS)
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[HPW][16 * (RSK + RS)];
+  // per wave: TPS K tiles (16 rows, stride RSK), then TPS V tiles (16 rows, stride RS)
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[HPW][TPS * 16 * (RSK + RS)];
   uint8_t* my_kt = kv_lds[w];
-  uint8_t* my_vt = kv_lds[w] + 16 * RSK;
+  uint8_t* my_vt = kv_lds[w] + TPS * 16 * RSK;
 
   // ---- issue cursor: the piece whose tiles are being loaded. Slot j owns global tiles
   // [slot_lo[j], slot_lo[j + 1]) of the sequences' tiles laid end to end; a piece is the
@@ -775,14 +779,14 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   int i_row = 0, i_p = 0, i_np = 1, i_te = 0, i_t0 = 0, i_nt = 0, i_n = 0;
   bool i_valid = false;
   cptr_i32 i_bt = nullptr;
-  // Queries: a piece's rows are loaded into qtmp when the piece is entered and moved
-  // into stage (ordinal mod NS) at the start of the next issue, by which time only the
-  // loads issued after them (one tile) are still in flight. NS stages suffice: the piece
-  // NS ordinals back has been fully consumed by then (at most NS - 1 tiles are issued
-  // and not consumed). Named register arrays, selected by bit tests: an indexed array
-  // would be placed in scratch memory.
+  // Queries: a piece's rows are loaded into qtmp when the piece is entered and moved into
+  // stage (ordinal mod 2) at the start of the next live issue step, by which time only the
+  // loads issued after them are still in flight. Two stages suffice: a step's tiles belong
+  // to one piece, and when a piece's queries move in only the other ring slot's step is
+  // issued and not consumed, so the piece two ordinals back has been fully consumed. Named
+  // register arrays, selected by bit tests: an indexed array would be placed in scratch.
   uint4 qtmp[KS];
-  bf16x8_t qs0[KS], qs1[KS], qs2[NS > 2 ? KS : 1];
+  bf16x8_t qs0[KS], qs1[KS];
   int q_stage = 0;                           // stage of the piece being issued
   bool q_pending = false;
 
@@ -829,52 +833,49 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     return true;
   };
 
-  // per-slot tile state (NS slots: the tile being consumed and those in flight)
-  static_assert(NS == 2 || NS == 3, "ring of 2 or 3 tiles");
-  uint4 kb[NS][NV], vb[NS][NV];
-  int sl_t0[NS], sl_row[NS], sl_p[NS], sl_np[NS], sl_te[NS], sl_par[NS];
-  bool sl_ok[NS], sl_first[NS], sl_last[NS], sl_valid[NS];
+  // Ring state: NS slots of TPS consecutive tiles of one piece each (the step being
+  // consumed and the one in flight); per-tile metadata at index slot * TPS + tile. A step
+  // never spans two pieces: when its first tile ends a piece, its second is issued dead.
+  static_assert(NS == 2, "ring of 2 steps");
+  uint4 kb[NS][TPS * NV], vb[NS][TPS * NV];
+  int sl_t0[NS * TPS], sl_row[NS * TPS], sl_p[NS * TPS], sl_np[NS * TPS], sl_te[NS * TPS], sl_par[NS * TPS];
+  bool sl_ok[NS * TPS], sl_first[NS * TPS], sl_last[NS * TPS], sl_valid[NS * TPS];
 
   bool more = enter();
-  // issue the next tile of the stream into slot k; false when the stream is exhausted
-  auto issue = [&](int k, uint4 (&kr)[NV], uint4 (&vr)[NV]) -> bool {
-    if (q_pending) {
+  // issue the next tile of the stream as tile e of the ring (a dead, masked tile when
+  // !take); false when the stream is exhausted
+  auto issue_tile = [&](int e, uint4* kr, uint4* vr, bool take) -> bool {
+    if (q_pending && take) {
       q_pending = false;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const bf16x8_t v = __builtin_bit_cast(bf16x8_t, qtmp[kk]);
-        if constexpr (NS > 2) {
-          if (q_stage & 2) qs2[kk] = v;
-          else if (q_stage & 1) qs1[kk] = v;
-          else qs0[kk] = v;
-        } else {
-          if (q_stage & 1) qs1[kk] = v;
-          else qs0[kk] = v;
-        }
+        if (q_stage & 1) qs1[kk] = v;
+        else qs0[kk] = v;
       }
     }
     // Every call issues the same loads (row 0 of block 0 once the stream is exhausted),
     // so each consume waits on a fixed count and never drains the tile behind it.
-    const bool live = more;
+    const bool live = more && take;
     const int ti = i_t0 + i_n;               // tile within the sequence
     const int tok_lo = 16 * ti;
     const bool any = live && tok_lo < i_te;
     const int blk = any ? i_bt[ti / SUB] : -1;
     const bool ok = any && blk >= 0 && blk < a.num_blocks;
     const int64_t off = (int64_t(ok ? blk : 0) * BS + (ti % SUB) * 16) * row_bytes + lane_off;
-    sl_t0[k] = tok_lo;
-    sl_ok[k] = ok;
-    sl_row[k] = i_row;
-    sl_p[k] = i_p;
-    sl_np[k] = i_np;
-    sl_te[k] = i_te;
-    sl_valid[k] = live && i_valid;
-    sl_first[k] = live && i_n == 0;
-    sl_last[k] = live && i_n == i_nt - 1;
-    sl_par[k] = q_stage;
+    sl_t0[e] = tok_lo;
+    sl_ok[e] = ok;
+    sl_row[e] = i_row;
+    sl_p[e] = i_p;
+    sl_np[e] = i_np;
+    sl_te[e] = i_te;
+    sl_valid[e] = live && i_valid;
+    sl_first[e] = live && i_n == 0;
+    sl_last[e] = live && i_n == i_nt - 1;
+    sl_par[e] = q_stage;
     // the next piece's queries go out before this tile's rows
     if (live && ++i_n == i_nt) {
-      q_stage = q_stage + 1 == NS ? 0 : q_stage + 1;
+      q_stage ^= 1;
       more = enter();
     }
 #pragma unroll
@@ -890,71 +891,118 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     }
     return live;
   };
+  // issue the next step (TPS tiles) into ring slot k; false when its first tile is past the stream
+  auto issue = [&](int k) -> bool {
+    const bool l0 = issue_tile(k * TPS, kb[k], vb[k], true);
+    if constexpr (TPS == 2) issue_tile(k * TPS + 1, kb[k] + NV, vb[k] + NV, !sl_last[k * TPS]);
+    return l0;
+  };
 
   float m = -INFINITY, lsum = 0.f;
   f32x4_t o[MT];
 
-  auto consume = [&](int k, const uint4 (&kr)[NV], const uint4 (&vr)[NV]) {
-    bf16x8_t qf[KS];
+  auto qsel = [&](int e, bf16x8_t (&qf)[KS]) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8_t lo = (sl_par[k] & 1) ? qs1[kk] : qs0[kk];
-      if constexpr (NS > 2) qf[kk] = (sl_par[k] & 2) ? qs2[kk] : lo;
-      else qf[kk] = lo;
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = (sl_par[e] & 1) ? qs1[kk] : qs0[kk];
+  };
+  // K and V rows of tile e -> LDS tile u as bf16 [token][head_dim] (E4M3 widened on the
+  // way). V rows past the end are zeroed by masking, not by a branch: every lane waits for
+  // its rows on the main path, so no later wait is made conservative by a skipped one (a
+  // stale slot may hold NaN, and 0 x NaN would reach the output). K rows past the end only
+  // give scores that are masked.
+  auto stage_tile = [&](int e, int u, const uint4* kr, const uint4* vr) {
+    uint8_t* kt = my_kt + u * (16 * RSK);
+    uint8_t* vt = my_vt + u * (16 * RS);
+    const int t0 = sl_t0[e];
+    const int tok_end = sl_te[e];
+    const bool ok = sl_ok[e];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = (i / HPR) * RPI + lrow;
+      const int c = (i % HPR) * LPR + lchunk;
+      const uint32_t keep = (ok && (t0 + r < tok_end)) ? 0xffffffffu : 0u;
+      const uint4 kv = kr[i];
+      uint4 v = vr[i];
+      asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+      v.x &= keep;
+      v.y &= keep;
+      v.z &= keep;
+      v.w &= keep;
+      if constexpr (CDT == PKV_BF16) {
+        *reinterpret_cast<uint4*>(kt + r * RSK + 16 * c) = kv;
+        *reinterpret_cast<uint4*>(vt + r * RS + 16 * c) = v;
+      } else {
+        *reinterpret_cast<uint4*>(kt + r * RSK + 32 * c) = pkv::fp8x8_to_bf16x8(kv.x, kv.y);
+        *reinterpret_cast<uint4*>(kt + r * RSK + 32 * c + 16) = pkv::fp8x8_to_bf16x8(kv.z, kv.w);
+        *reinterpret_cast<uint4*>(vt + r * RS + 32 * c) = pkv::fp8x8_to_bf16x8(v.x, v.y);
+        *reinterpret_cast<uint4*>(vt + r * RS + 32 * c + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+      }
     }
-    if (sl_first[k]) {
+  };
+  auto reset_if_first = [&](int e) {
+    if (sl_first[e]) {
       m = -INFINITY;
       lsum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int t0 = sl_t0[k];
-    const int tok_end = sl_te[k];
-    const bool ok = sl_ok[k];
-    {
-      // K and V rows -> LDS as bf16 [token][head_dim] (E4M3 widened on the way). V rows
-      // past the end are zeroed by masking, not by a branch: every lane waits for its rows
-      // on the main path, so no later wait is made conservative by a skipped one (a stale
-      // slot may hold NaN, and 0 x NaN would reach the output). K rows past the end only
-      // give scores that are masked below.
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int r = (i / HPR) * RPI + lrow;
-        const int c = (i % HPR) * LPR + lchunk;
-        const uint32_t keep = (ok && (t0 + r < tok_end)) ? 0xffffffffu : 0u;
-        const uint4 kv = kr[i];
-        uint4 v = vr[i];
-        asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-        v.x &= keep;
-        v.y &= keep;
-        v.z &= keep;
-        v.w &= keep;
-        if constexpr (CDT == PKV_BF16) {
-          *reinterpret_cast<uint4*>(my_kt + r * RSK + 16 * c) = kv;
-          *reinterpret_cast<uint4*>(my_vt + r * RS + 16 * c) = v;
-        } else {
-          *reinterpret_cast<uint4*>(my_kt + r * RSK + 32 * c) = pkv::fp8x8_to_bf16x8(kv.x, kv.y);
-          *reinterpret_cast<uint4*>(my_kt + r * RSK + 32 * c + 16) = pkv::fp8x8_to_bf16x8(kv.z, kv.w);
-          *reinterpret_cast<uint4*>(my_vt + r * RS + 32 * c) = pkv::fp8x8_to_bf16x8(v.x, v.y);
-          *reinterpret_cast<uint4*>(my_vt + r * RS + 32 * c + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    // S = K.Q^T: the A operand is K in its MFMA layout (token hl, head_dim 32kk + 8grp ..),
-    // read back from the K tile; the B operand is the packed queries in the same order
+  };
+  // S = K.Q^T of LDS tile u: the A operand is K in its MFMA layout (token hl, head_dim
+  // 32kk + 8grp ..), read back from the K tile; the B operand is the packed queries in the
+  // same order. Scores of tile e come out as lane l: head hl, tokens 4grp + r, masked.
+  auto scores = [&](int e, int u, const bf16x8_t (&qf)[KS], float (&z)[4]) {
+    const uint8_t* kt = my_kt + u * (16 * RSK);
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint4 kf = *reinterpret_cast<const uint4*>(my_kt + hl * RSK + 64 * kk + 16 * grp);
+      const uint4 kf = *reinterpret_cast<const uint4*>(kt + hl * RSK + 64 * kk + 16 * grp);
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], sc, 0, 0, 0);
     }
-    float z[4];
+    const int t0 = sl_t0[e];
+    const int tok_end = sl_te[e];
+    const bool ok = sl_ok[e];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * grp + r;
       z[r] = (ok && t < tok_end) ? sc[r] * zscale_g : -INFINITY;
     }
+  };
+  // the piece's last tile was folded in: write its output (or partial)
+  auto finish = [&](int e) {
+    if (!sl_last[e]) return;
+    float l = lsum;
+    l = pkv::lane_groups_sum(l);
+    if (!sl_valid[e] || hl >= G) return;
+    const int hq = g * G + hl;
+    const float inv = l > 0.f ? a.vscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)] / l : 0.f;
+    const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
+    if (sl_np[e] == 1) {
+      const int row = sl_row[e];
+      uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
+        const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
+        pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
+      }
+      if (lp.lse && grp == 0)
+        pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + hq, __float_as_uint(lse2 * kLn2));
+    } else {
+      const int64_t pi = split_partial(slot, sl_p[e], Hq, hq);
+      float* orow = lp.ws_o + pi * D + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        pkv::store_b128_untracked(orow + 16 * mt, o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv, o[mt][3] * inv);
+      if (grp == 0) pkv::store_b32_untracked(lp.ws_lse + pi, __float_as_uint(lse2));
+    }
+  };
+  // one 16-token tile (ring tile e, LDS tile u) folded into the running state
+  auto step1 = [&](int e, int u) {
+    bf16x8_t qf[KS];
+    qsel(e, qf);
+    reset_if_first(e);
+    float z[4];
+    scores(e, u, qf, z);
     float mt_ = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mt_ = pkv::lane_groups_max(mt_);
     const float mn = fmaxf(m, mt_);
@@ -969,7 +1017,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
     m = mn;
     const pkv::s16x4_t pf = __builtin_bit_cast(pkv::s16x4_t, make_uint2(p01, p23));
     __builtin_amdgcn_wave_barrier();
-    const uint8_t* src = my_vt + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+    const uint8_t* src = my_vt + u * (16 * RS) + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const pkv::s16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pkv::lds_s16x4_t*)(src + 32 * mt));
@@ -981,33 +1029,64 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
       o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, acc, 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
-    if (!sl_last[k]) return;
-    // ---- the item's last tile: write its output (or partition partial)
-    float l = lsum;
-    l = pkv::lane_groups_sum(l);
-    if (!sl_valid[k] || hl >= G) return;
-    const int hq = g * G + hl;
-    const float inv = l > 0.f ? a.vscale_h[__builtin_amdgcn_readfirstlane(g) & (pkv::kHeadScales - 1)] / l : 0.f;
-    const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
-    if (sl_np[k] == 1) {
-      const int row = sl_row[k];
-      uint16_t* orow = lp.out + (int64_t(row) * Hq + hq) * D + 4 * grp;
+    finish(e);
+  };
+  // two consecutive tiles of one piece (ring tiles e, e + 1 in LDS tiles 0, 1; the second
+  // may be dead) in one softmax step: one maximum and one rescale for 32 keys, and P.V on
+  // 16x16x32 MFMAs whose 32 contraction slots of a lane are its own 4 + 4 rounded weights
+  // (tokens 4grp + r of each tile) against the two tiles' transposed V reads at the same keys
+  auto step2 = [&](int e) {
+    bf16x8_t qf[KS];
+    qsel(e, qf);
+    reset_if_first(e);
+    float z0[4], z1[4];
+    scores(e, 0, qf, z0);
+    scores(e + 1, 1, qf, z1);
+    const float z[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+    float mt_ = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    mt_ = pkv::lane_groups_max(mt_);
+    const float mn = fmaxf(m, mt_);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = pkv::fast_exp2(m - mref);
+    float pr[8];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t lo = pack_bf16x2_rne(o[mt][0] * inv, o[mt][1] * inv);
-        const uint32_t hi = pack_bf16x2_rne(o[mt][2] * inv, o[mt][3] * inv);
-        pkv::store_b64_untracked(orow + 16 * mt, lo, hi);
-      }
-      if (lp.lse && grp == 0)
-        pkv::store_b32_untracked(lp.lse + int64_t(row) * Hq + hq, __float_as_uint(lse2 * kLn2));
-    } else {
-      const int64_t pi = split_partial(slot, sl_p[k], Hq, hq);
-      float* orow = lp.ws_o + pi * D + 4 * grp;
+    for (int r = 0; r < 8; ++r) pr[r] = pkv::fast_exp2(z[r] - mref);
+    uint32_t pw[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        pkv::store_b128_untracked(orow + 16 * mt, o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv, o[mt][3] * inv);
-      if (grp == 0) pkv::store_b32_untracked(lp.ws_lse + pi, __float_as_uint(lse2));
+    for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2_rne(pr[2 * j], pr[2 * j + 1]);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ps += pkv::bf16_lo(pw[j]) + pkv::bf16_hi(pw[j]);
+    lsum = lsum * alpha + ps;
+    m = mn;
+    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* src = my_vt + (4 * grp + (hl >> 2)) * RS + (4 * (hl & 3)) * 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const pkv::s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pkv::lds_s16x4_t*)(src + 32 * mt));
+      const pkv::s16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((pkv::lds_s16x4_t*)(src + 16 * RS + 32 * mt));
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      f32x4_t acc = o[mt];
+      acc[0] *= alpha;
+      acc[1] *= alpha;
+      acc[2] *= alpha;
+      acc[3] *= alpha;
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc, 0, 0, 0);
     }
+    __builtin_amdgcn_wave_barrier();
+    finish(e);
+    finish(e + 1);
+  };
+  // consume ring slot k: stage its tiles in LDS, then fold them in (a dead tile changes
+  // nothing: its scores are masked and its V rows zeroed)
+  auto consume = [&](int k) {
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) stage_tile(k * TPS + u, u, kb[k] + u * NV, vb[k] + u * NV);
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (TPS == 1) step1(k, 0);
+    else step2(2 * k);
   };
 
   // rows without context (no piece anywhere): zero output, log-sum-exp -inf; plan row s
@@ -1029,7 +1108,7 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
   // between the two halves would join the loop's back edge in the control-flow graph
   // with a slot still in flight, and every wait at the top would become a full drain.
 #pragma unroll
-  for (int k = 0; k + 1 < NS; ++k) issue(k, kb[k], vb[k]);
+  for (int k = 0; k + 1 < NS; ++k) issue(k);
   bool live = true;
   do {
     // issue into the slot consumed last, then consume the oldest; after the sweep the
@@ -1037,9 +1116,9 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int ik = (k + NS - 1) % NS;
-      const bool l = issue(ik, kb[ik], vb[ik]);
+      const bool l = issue(ik);
       if (k == 1) live = l;
-      consume(k, kb[k], vb[k]);
+      consume(k);
     }
     // The waves of the workgroup stream the same tiles (one KV head each) and stay in
     // step here. Left alone, the older wave on each SIMD wins issue and runs ahead: the
@@ -1106,8 +1185,8 @@ DecodeFn pick_mfma(int D, int BS) {
 template <int CDT, int D, int HPW>
 DecodeFn pick_split_bs(int BS) {
   switch (BS) {
-    case 16: return decode_split_kernel<CDT, D, 16, HPW>;
-    case 32: return decode_split_kernel<CDT, D, 32, HPW>;
+    case 16: return decode_split_kernel<CDT, D, 16, HPW, kSplitRing, split_tps(CDT)>;
+    case 32: return decode_split_kernel<CDT, D, 32, HPW, kSplitRing, split_tps(CDT)>;
     default: return nullptr;
   }
 }
