@@ -104,29 +104,50 @@ def probe_read(mib: int, steps: int) -> None:
                               "unroll": unroll, "us": round(t * 1e6, 2), "GBps": round(gbs, 1)}), flush=True)
             if best is None or gbs > best[0]:
                 best = (gbs, blocks, unroll)
+    for blocks in (256, 512, 1024, 2048):
+        out = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
+        wgen.read_probe_stream(buf, blocks, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            wgen.read_probe_stream(buf, blocks, out)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        gbs = buf.numel() / t / 1e9
+        print(json.dumps({"probe": "stream read, one share per workgroup, non-temporal", "bytes": buf.numel(),
+                          "blocks": blocks, "threads": 512, "us": round(t * 1e6, 2), "GBps": round(gbs, 1)}), flush=True)
+        if gbs > best[0]:
+            best = (gbs, blocks, "stream")
     print(json.dumps({"probe": "stream read best", "GBps": round(best[0], 1), "blocks": best[1],
                       "unroll": best[2]}), flush=True)
 
 
 def measured_read_peak() -> float:
-    """Best stream-read rate of a 1 GiB buffer over a few launch shapes (GB/s): the
-    achievable read bandwidth the decode rate is also compared with."""
+    """Best stream-read rate of a 2 GiB buffer (GB/s) over a few launch shapes of two
+    probes: a grid-stride read with plain loads, and one contiguous share per workgroup
+    with non-temporal loads (the faster on MI355X): the achievable read bandwidth the
+    decode rate is also compared with. The buffer is 8x the 256 MB last-level cache."""
     import torch
     import workloads.gpu as wgen
-    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    runs = [(lambda b=b, u=u, o=torch.empty(b * 256, dtype=torch.int32, device="cuda"): wgen.read_probe(buf, b, u, o))
+            for b in (1024, 4096, 8192) for u in (4, 8)]
+    runs += [(lambda b=b, o=torch.empty(b * 512, dtype=torch.int32, device="cuda"): wgen.read_probe_stream(buf, b, o))
+             for b in (256, 512, 1024, 2048)]
     best = 0.0
-    for blocks, unroll in [(b, u) for b in (256, 512, 1024, 2048, 4096, 8192) for u in (1, 2, 4, 8)]:
-        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
-        wgen.read_probe(buf, blocks, unroll, out)
+    for run in runs:
+        run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(10):
-            wgen.read_probe(buf, blocks, unroll, out)
+            run()
         e1.record()
         torch.cuda.synchronize()
         best = max(best, buf.numel() / (e0.elapsed_time(e1) * 1e-3 / 10) / 1e9)
-    del buf
+    del buf, runs
     torch.cuda.empty_cache()
     return best
 

@@ -932,10 +932,24 @@ __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a)
         *reinterpret_cast<uint4*>(kt + r * RSK + 16 * c) = kv;
         *reinterpret_cast<uint4*>(vt + r * RS + 16 * c) = v;
       } else {
-        *reinterpret_cast<uint4*>(kt + r * RSK + 32 * c) = pkv::fp8x8_to_bf16x8(kv.x, kv.y);
-        *reinterpret_cast<uint4*>(kt + r * RSK + 32 * c + 16) = pkv::fp8x8_to_bf16x8(kv.z, kv.w);
-        *reinterpret_cast<uint4*>(vt + r * RS + 32 * c) = pkv::fp8x8_to_bf16x8(v.x, v.y);
-        *reinterpret_cast<uint4*>(vt + r * RS + 32 * c + 16) = pkv::fp8x8_to_bf16x8(v.z, v.w);
+        // A lane's 16 codes widen to 32 bytes, two 16-byte stores. An LDS store serves 8
+        // lanes at a time over 8 bank groups of 16 bytes (16-byte position mod 8). With
+        // 8 lanes per row (head_dim 128) they hold one row's chunks, 32 bytes apart, so the
+        // lanes of the upper four chunks store their halves in the opposite order; with 4
+        // (head_dim 64) they hold two rows, which the K stride already puts on opposite
+        // parities and the V stride does not, so odd V rows swap. Each store then meets 8
+        // distinct groups instead of 4 twice.
+        const bool swap_k = LPR == 8 && (lchunk & 4) != 0;
+        const bool swap_v = LPR == 8 ? (lchunk & 4) != 0 : (lrow & 1) != 0;
+        const uint32_t k0 = swap_k ? 16u : 0u, v0 = swap_v ? 16u : 0u;
+        *reinterpret_cast<uint4*>(kt + r * RSK + 32 * c + k0) =
+            pkv::fp8x8_to_bf16x8(swap_k ? kv.z : kv.x, swap_k ? kv.w : kv.y);
+        *reinterpret_cast<uint4*>(kt + r * RSK + 32 * c + (16u - k0)) =
+            pkv::fp8x8_to_bf16x8(swap_k ? kv.x : kv.z, swap_k ? kv.y : kv.w);
+        *reinterpret_cast<uint4*>(vt + r * RS + 32 * c + v0) =
+            pkv::fp8x8_to_bf16x8(swap_v ? v.z : v.x, swap_v ? v.w : v.y);
+        *reinterpret_cast<uint4*>(vt + r * RS + 32 * c + (16u - v0)) =
+            pkv::fp8x8_to_bf16x8(swap_v ? v.x : v.z, swap_v ? v.y : v.w);
       }
     }
   };

@@ -118,6 +118,38 @@ __global__ void __launch_bounds__(256) read_probe(const uint4* __restrict__ buf,
 }
 }  // namespace
 
+namespace {
+// The same probe with each workgroup (512 threads) streaming one contiguous share of the
+// buffer, 8 loads in flight per lane, with the non-temporal hint: the shape and cache
+// policy under which MI355X reads fastest (the per-lane xor keeps the loads live).
+__global__ void __launch_bounds__(512) read_probe_stream(const uint4* __restrict__ buf, int64_t n16, int64_t per,
+                                                         uint32_t* out) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t lo = int64_t(blockIdx.x) * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  int64_t i = lo + threadIdx.x;
+  u32x4 acc = {0, 0, 0, 0};
+  for (; i + 7 * 512 < hi; i += 8 * 512) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + i + u * 512));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < hi; i += 512) acc ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + i));
+  out[int64_t(blockIdx.x) * 512 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+}  // namespace
+
+// buf: device, n16 chunks of 16 bytes; out: device uint32 [blocks * 512].
+extern "C" int pkvgen_read_probe_stream(const void* buf, int64_t n16, int blocks, void* out, void* stream) {
+  if (!buf || !out || n16 <= 0 || blocks <= 0) return -1;
+  const int64_t per = (n16 + blocks - 1) / blocks;
+  hipLaunchKernelGGL(read_probe_stream, dim3(blocks), dim3(512), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(buf), n16, per, static_cast<uint32_t*>(out));
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 // buf: device, n16 chunks of 16 bytes; out: device uint32 [blocks * 256].
 extern "C" int pkvgen_read_probe(const void* buf, int64_t n16, int blocks, int unroll, void* out, void* stream) {
   if (!buf || !out || n16 <= 0 || blocks <= 0) return -1;

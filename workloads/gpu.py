@@ -44,6 +44,8 @@ def lib():
                                            C.c_int64, C.c_float, C.c_void_p]
         L.pkvgen_read_probe.restype = C.c_int
         L.pkvgen_read_probe.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+        L.pkvgen_read_probe_stream.restype = C.c_int
+        L.pkvgen_read_probe_stream.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib
 
@@ -89,6 +91,20 @@ def read_probe(buf, blocks: int, unroll: int, out) -> None:
                                  C.c_void_p(out.data_ptr()), C.c_void_p(st))
     if rc != 0:
         raise RuntimeError(f"pkvgen_read_probe failed ({rc})")
+
+
+def read_probe_stream(buf, blocks: int, out) -> None:
+    """Stream-read device tensor `buf` with one contiguous share per workgroup and
+    non-temporal loads (out: int32 tensor of blocks*512)."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    if out.numel() < blocks * 512 or nbytes % 16:
+        raise ValueError("probe buffers mis-sized")
+    st = torch.cuda.current_stream().cuda_stream
+    rc = lib().pkvgen_read_probe_stream(C.c_void_p(buf.data_ptr()), nbytes // 16, blocks,
+                                        C.c_void_p(out.data_ptr()), C.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError(f"pkvgen_read_probe_stream failed ({rc})")
 
 
 if __name__ == "__main__":
