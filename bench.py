@@ -635,11 +635,20 @@ def time_decode_step(w, P, decode_kind, steps, warmup):
     return dict(wall=wall, write=t_write, decode=t_decode, step=t_step, part=t_part, merge=t_merge, dev=dev)
 
 
+# Warmup steps of the decode sub-measurements (not the headline, which takes --warmup as
+# given): after the idle setup of a workload the first few hundred microseconds of GPU
+# work run slow, and the E4M3 decode (less memory-bound than bf16) reads 5-20 us high
+# after 5 steps, steady after 50.
+SUB_WARMUP = 50
+
+
 def decode_record(w, P, decode_kind, steps, warmup):
     """A decode sub-measurement: GB/s of the decode (pass + merge), its fraction of the
-    8 TB/s peak, the pass alone, and the merge's share of the decode time."""
+    8 TB/s peak, the pass alone, and the merge's share of the decode time (at least
+    SUB_WARMUP warmup steps first)."""
     import numpy as np
     import torch
+    warmup = max(warmup, SUB_WARMUP)
     r = time_decode_step(w, P, decode_kind, steps, warmup)
     dbytes = decode_bytes(w)
     t_dec, t_part, t_merge = float(r["decode"].mean()), float(r["part"].mean()), float(r["merge"].mean())
@@ -647,7 +656,7 @@ def decode_record(w, P, decode_kind, steps, warmup):
     out = {"workload": w.name, "cache_dtype": w.cache_dtype, "num_seqs": w.num_seqs,
            "context_tokens": int(w.seq_lens.sum()), "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
            "head_dim": w.head_dim, "block_size": w.block_size, "decode": decode_kind,
-           "algorithmic_bytes": dbytes,
+           "steps": steps, "warmup": warmup, "algorithmic_bytes": dbytes,
            "decode_us": round(t_dec * 1e6, 2), "decode_GBps": round(dbytes / t_dec / 1e9, 1),
            "decode_frac_of_peak": round(dbytes / t_dec / 1e9 / PEAK_HBM_GBS, 4),
            "pass_us_profiled": round(t_part * 1e6, 2), "merge_us_profiled": round(t_merge * 1e6, 2),
