@@ -207,8 +207,9 @@ def mixed_bytes_flops(w):
 
 def mixed_step(steps: int, warmup: int):
     """Config-2 mixed continuous-batching step: cache write of the 2096 new tokens, then the
-    attention of 48 decode rows and 4 prefill chunks of 512 (causal), as one varlen launch
-    or as split decode rows + the chunk kernel. Each timed step follows a 512 MiB cache
+    attention of 48 decode rows and 4 prefill chunks of 512 (causal): one launch of the
+    mixed kernel (the product form: decode slots and chunk items side by side), one varlen
+    launch, or split decode rows + the chunk kernel. Each timed step follows a 512 MiB cache
     flush; times are HIP events (write + attention), tokens/s = query tokens / that time."""
     import numpy as np
     import torch
@@ -272,11 +273,21 @@ def mixed_step(steps: int, warmup: int):
     rows_d = torch.from_numpy(mp.decode_rows).cuda()
     plan_d = torch.from_numpy(mp.split.plan).cuda()
     ws = pkv.decode_split_workspace(mp.split, Hq, d)
+    # the product form: one launch of the mixed kernel, decode slots balanced against the
+    # chunk items (pkv_mixed_decode_slots), chunk blocks uncut
+    mslots = pkv.mixed_decode_slots(w.q_lens, w.seq_lens, pkv.BF16, Hkv, w.group, d, w.block_size)
+    mmp = pkv.build_mixed_step(w.q_lens, w.seq_lens, Hkv, w.group, mslots, 0, 0)
+    mdev = mmp.to_device(d, Hq)
+    mixed = pkv.paged_attention_mixed(out, q, kc, vc, bt_d, lens_d, cu_d, mmp, mdev, Hkv, w.block_size, msl,
+                                      w.softmax_scale, defer=True)
 
     def attention(mode, emid=None):
         if mode == "one_launch":
             pkv.paged_attention_prefill_varlen(out, q, kc, vc, bt_d, lens_d, cu_d, work, Hkv, w.block_size, msl,
                                                w.softmax_scale)
+            return
+        if mode == "mixed":
+            mixed()
             return
         pkv.paged_attention_decode_split(out, q, kc, vc, bt_d, lens_d, plan_d, mp.split, Hkv, w.block_size, msl,
                                          w.softmax_scale, 1.0, 1.0, ws, rows=rows_d, cu_seqlens_q=cu_d)
@@ -301,7 +312,7 @@ def mixed_step(steps: int, warmup: int):
                        f"after 0/512/1024/1536 cached, 32/8 heads, d 128, bs 16, bf16, fragmented pool",
            "query_tokens": n_new, "context_tokens": int(w.seq_lens.sum()),
            "attention_bytes": nbytes, "attention_flops": flops}
-    names = {"one_launch": "one_launch", "uncut": "split_decode_plus_chunks_uncut",
+    names = {"mixed": "one_launch_mixed", "one_launch": "one_launch", "uncut": "split_decode_plus_chunks_uncut",
              "cut": "split_decode_plus_chunks"}
     # the step's working set (~250 MB) fits in the last-level cache: evict it before every
     # timed step (outside the events) by streaming a 512 MiB buffer through the caches. A
@@ -331,6 +342,9 @@ def mixed_step(steps: int, warmup: int):
             "tokens_per_s": round(n_new / wall, 1),
             "hbm_GBps": round(nbytes / t_a / 1e9, 1), "hbm_frac": round(nbytes / t_a / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_TFLOPs": round(flops / t_a / 1e12, 1), "mfma_frac": round(flops / t_a / 1e12 / 2500.0, 4)}
+        if two == "mixed":
+            res[names[two]]["decode_slots"] = mslots
+    res["product_form"] = "one_launch_mixed"
     return res
 
 

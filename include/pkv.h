@@ -426,6 +426,55 @@ int pkv_build_mixed_step(int32_t num_seqs, const int32_t* q_lens, const int32_t*
                          int32_t* merges, int32_t merge_capacity, int32_t* merge_count,
                          int32_t* num_partials);
 
+/* Decode slots for the one launch of pkv_paged_attention_mixed: the number of balanced-split
+ * slots over which a mixed step's decode rows (q_lens[s] == 1) finish together with its
+ * chunk items (q_lens[s] >= 2, the pkv_build_chunk_work items) running on the other
+ * compute units. q_lens, seq_lens: host int32 [num_seqs]. For a bf16 cache at head_dim 128
+ * with num_kv_heads a multiple of 8 and rows of both kinds, *slots weighs the decode
+ * rows' K/V bytes against the items' 64-key tiles with per-unit rates measured on MI355X
+ * for these kernels, in [1, pkv_decode_split_slots]; otherwise (one kind of row, or a
+ * shape that runs as two launches) *slots = pkv_decode_split_slots. Pass it to
+ * pkv_build_mixed_step as num_slots. INVALID on a bad argument or q > L, and the errors
+ * of pkv_decode_split_slots. */
+int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
+                           int32_t cache_dtype, int32_t num_kv_heads, int32_t group, int32_t head_dim,
+                           int32_t block_size, int32_t* slots);
+
+/* The attention of a mixed continuous-batching step ([CB] "5. Technical explanation",
+ * mixed batching: decode rows and prefill chunks in one batch; every row's attention as
+ * in [P17] "Step 6") in one kernel launch plus the log-sum-exp merges. The arguments from
+ * out to v_head_scales and lse_out are those of pkv_paged_attention_prefill_chunks (q and
+ * out [total_q][num_q_heads][head_dim], rows delimited by cu_seqlens_q); the plan is
+ * pkv_build_mixed_step's for the same q_lens and seq_lens: decode_rows (device int32
+ * [num_decode_rows]), split_plan / split_slots / tiles_per_slot / max_pieces and
+ * split_workspace (>= pkv_decode_split_workspace_bytes; not needed when max_pieces <= 1) as
+ * for pkv_paged_attention_decode_split's row map, chunk_items / chunk_merges /
+ * num_chunk_partials and chunk_workspace as for pkv_paged_attention_prefill_chunks;
+ * num_decode_rows or num_chunk_items may be 0. With a bf16 cache at head_dim 128, block
+ * size 16 or 32 and num_kv_heads a multiple of 8, one kernel runs both kinds of
+ * workgroup: the first split_slots x num_kv_heads / 8 run the decode pass (one per compute
+ * unit, for the whole pass), the rest the chunk items, on the units the decode leaves
+ * free, so the memory-bound decode and the MFMA-bound chunks run at the same time (with
+ * split_slots from pkv_mixed_decode_slots they end together); then the merges of split
+ * decode rows and of cut chunk blocks. Other shapes run the two kernels one after the
+ * other (the same results). Every row with q_lens = 1 and every row of a sequence with
+ * q_lens >= 2 is written (with its log-sum-exp when lse_out is given). Errors: those of
+ * the two calls it combines. Calls sharing a workspace must not overlap. */
+int pkv_paged_attention_mixed(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                              const void* v_cache, int32_t cache_dtype, const int32_t* block_tables,
+                              const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t table_width,
+                              int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                              float scale, float k_scale, float v_scale, const float* k_head_scales,
+                              const float* v_head_scales, const int32_t* decode_rows,
+                              int32_t num_decode_rows, const int32_t* split_plan, int32_t split_slots,
+                              int32_t tiles_per_slot, int32_t max_pieces, void* split_workspace,
+                              size_t split_workspace_bytes, const int32_t* chunk_items,
+                              int32_t num_chunk_items, const int32_t* chunk_merges,
+                              int32_t num_chunk_merges, int32_t num_chunk_partials,
+                              void* chunk_workspace, int64_t chunk_workspace_bytes, float* lse_out,
+                              void* stream);
+
 /* Slots to balance chunk work over on the current device (its compute units: a second
  * resident workgroup shares a unit's issue slots, so it adds little throughput): the
  * num_slots of pkv_build_chunk_work. UNSUPPORTED for a cache dtype / head_dim /

@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     MixedPlan, build_mixed_step, paged_attention_prefill_chunks, ChunkPlan, build_chunk_work, chunk_slots,
     chunk_workspace_bytes, swap_workspace_bytes, swap_out, swap_in, decode_split_noalloc_max_bytes,
     decode_split_workspace, split_plan_len,
-    paged_attention_decode_split_noalloc,
+    paged_attention_decode_split_noalloc, mixed_decode_slots, paged_attention_mixed,
 )

@@ -115,6 +115,10 @@ _SIGS = {
                                                            i32, i32, i32, vp, vp]),
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, vp]),
+    "pkv_mixed_decode_slots": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, i32, P_i32]),
+    "pkv_paged_attention_mixed": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, i32, i32, vp, sz, vp,
+                                            i32, vp, i32, i32, vp, i64, vp, vp]),
 }
 
 
@@ -784,6 +788,16 @@ class MixedPlan:
     def __init__(self, decode_rows, split, chunks):
         self.decode_rows, self.split, self.chunks = decode_rows, split, chunks
 
+    def to_device(self, head_dim: int, num_q_heads: int, device="cuda"):
+        """The device arrays of paged_attention_mixed: (rows, split plan, split workspace)
+        (None when there is no decode row) and ChunkPlan.to_device (None when no chunk)."""
+        torch = _torch()
+        dec = None
+        if self.split is not None:
+            dec = (torch.from_numpy(self.decode_rows).to(device), torch.from_numpy(self.split.plan).to(device),
+                   decode_split_workspace(self.split, num_q_heads, head_dim, device))
+        return dec, self.chunks.to_device(head_dim, device)
+
 
 def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots: int,
                      min_piece_tokens: int = 0, chunk_slots: int = 0, min_piece_tiles: int = 0,
@@ -815,6 +829,70 @@ def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots:
     split = SplitPlan(plan[:split_plan_len(k, num_slots)].copy(), int(num_slots), c.value, mp.value) if k else None
     chunks = ChunkPlan(items[:n.value].copy(), merges[:m.value].copy(), p.value)
     return MixedPlan(dec[:k].copy(), split, chunks)
+
+
+def mixed_decode_slots(q_lens, seq_lens, cache_dtype: int, num_kv_heads: int, group: int, head_dim: int,
+                       block_size: int) -> int:
+    """Decode slots for paged_attention_mixed's one launch: the slots that let the decode
+    rows finish with the chunk items running beside them (the full device when the step
+    has one kind of row only, or when the shape runs as two launches)."""
+    q = np.ascontiguousarray(q_lens, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    n = i32()
+    check(lib().pkv_mixed_decode_slots(len(q), _np_ptr(q), _np_ptr(L), cache_dtype, num_kv_heads, group, head_dim,
+                                       block_size, C.byref(n)))
+    return n.value
+
+
+def paged_attention_mixed(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, plan: MixedPlan, dev,
+                          num_kv_heads: int, block_size: int, max_seq_len: int, scale: float, k_scale: float = 1.0,
+                          v_scale: float = 1.0, lse=None, stream=None, k_head_scales=None, v_head_scales=None,
+                          defer: bool = False):
+    """The attention of a mixed step (decode rows and prefill chunks) as one launch plus
+    the merges. plan: build_mixed_step's result (for one launch, over mixed_decode_slots
+    decode slots); dev: plan.to_device(head_dim, num_q_heads); q/out [total_q][Hq][d],
+    cu_seqlens_q int32 [B + 1]; the rest as for paged_attention_prefill_chunks."""
+    torch = _torch()
+    ddev, cdev = dev
+    _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, lse)
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [total_q][Hq][d] of one dtype")
+    T, Hq, d = q.shape
+    _check_plane(k_cache, v_cache, block_size, num_kv_heads, d)
+    B = seq_lens.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][W]")
+    if seq_lens.dtype != torch.int32 or cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (B + 1,):
+        raise ValueError("seq_lens int32 [B] and cu_seqlens_q int32 [B+1] expected")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq)):
+        raise ValueError("lse must be float32 [total_q][Hq]")
+    rows = plan_d = sws = None
+    n_rows, slots, tps, mp, sws_bytes = 0, 1, 0, 0, 0
+    if ddev is not None:
+        rows, plan_d, sws = ddev
+        _require_cuda_contig(rows, plan_d, sws)
+        if rows.dtype != torch.int32 or plan_d.dtype != torch.int32 or \
+                tuple(plan_d.shape) != (split_plan_len(rows.shape[0], plan.split.num_slots),):
+            raise ValueError("decode rows / split plan do not match the mixed plan")
+        n_rows, slots, tps, mp = rows.shape[0], plan.split.num_slots, plan.split.tiles_per_slot, plan.split.max_pieces
+        sws_bytes = 0 if sws is None else sws.numel() * sws.element_size()
+    work = merges = cws = None
+    n_work = n_merges = 0
+    if cdev is not None:
+        work, merges, cws = cdev
+        _require_cuda_contig(work, merges, cws)
+        if work.dtype != torch.int32 or work.dim() != 2 or work.shape[1] != 8:
+            raise ValueError("work must be int32 [n][8] (from build_mixed_step)")
+        n_work = work.shape[0]
+        n_merges = 0 if merges is None else merges.shape[0]
+    cws_bytes = 0 if cws is None else cws.numel() * cws.element_size()
+    args = (_dptr(out), _dptr(q), tensor_dtype_code(q), _dptr(k_cache), _dptr(v_cache), tensor_dtype_code(k_cache),
+            _dptr(block_tables), _dptr(seq_lens), _dptr(cu_seqlens_q), block_tables.shape[1], B, T, Hq, num_kv_heads,
+            d, block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
+            *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(rows), n_rows, _dptr(plan_d),
+            slots, tps, mp, _dptr(sws), sws_bytes, _dptr(work), n_work, _dptr(merges), n_merges,
+            plan.chunks.num_partials, _dptr(cws), cws_bytes, _dptr(lse), _stream(stream))
+    return _launch(lib().pkv_paged_attention_mixed, args, defer)
 
 
 def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,

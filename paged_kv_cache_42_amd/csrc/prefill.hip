@@ -36,6 +36,7 @@
 #include <cmath>
 #include <vector>
 
+#include "decode_split.h"
 #include "mfma_common.h"
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -573,8 +574,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// LDS of the opposite-phase chunk kernel: per group K0, K1, V0, V1 tiles of 64 keys x 256 B
+constexpr int kPpLds = 2 * 4 * kKeys * 2 * 128;
+
+// One item of the opposite-phase chunk kernel (bf16 cache, head_dim 128): work record
+// `item`, on layer blockIdx.z; smem: kPpLds bytes of LDS, 16-byte aligned. Called by the
+// chunk kernel and by the mixed-step kernel.
 template <int BS>
-__global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
+__device__ __forceinline__ void chunk_pp_body(const ChunkArgs& a, uint8_t* smem, int item) {
   constexpr int D = 128;
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
@@ -583,12 +590,12 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
   constexpr int GB = 4 * TILE;                           // per group: K0, K1, V0, V1
   static_assert(Lds<D>::kXchg <= 2 * GB, "exchange fits in the tile buffers");
   static_assert(BS == 16 || BS == 32, "a wave's 4 rows of one load stay in one block");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * GB];
+  static_assert(2 * GB == kPpLds, "LDS layout");
   typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
   typedef __attribute__((address_space(3))) uint8_t* lds_u8;
 
-  const int4 it = a.work[2 * blockIdx.x];
-  const int4 it2 = a.work[2 * blockIdx.x + 1];
+  const int4 it = a.work[2 * item];
+  const int4 it2 = a.work[2 * item + 1];
   const int s = it.x;
   const int g = it.y;
   const int q0 = it.z;
@@ -857,6 +864,30 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
   chunk_finish<D>(a, lp, smem, gi, w, lane, g, G, Hq, row0, q0, slot, row_ok, m, lsum, o);
 }
 
+template <int BS>
+__global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPpLds];
+  chunk_pp_body<BS>(a, smem, blockIdx.x);
+}
+
+// A mixed step in one launch (bf16 cache, head_dim 128): workgroups 0 .. n_dec - 1 run
+// the balanced-split decode pass over the step's decode rows (slot b / hgroups, KV-head
+// group b % hgroups, 8 KV heads per workgroup), the others run chunk items of its prefill
+// rows, one LDS array serving either. The decode workgroups come first, so they hold
+// their units for the whole pass while chunk items flow through the rest: the memory-bound
+// decode and the MFMA-bound chunks run side by side instead of one after the other.
+static_assert(pkv::split::split_lds_bytes<PKV_BF16, 128, 8, 1>() <= kPpLds, "decode fits the chunk LDS");
+template <int BS>
+__global__ void __launch_bounds__(kThreads, 1) mixed_pp_kernel(pkv::split::DecodeArgs da, ChunkArgs ca, int n_dec,
+                                                                int hgroups) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPpLds];
+  const int b = blockIdx.x;
+  if (b < n_dec)
+    pkv::split::decode_split_body<PKV_BF16, 128, BS, 8, pkv::split::kSplitRing, 1>(da, smem, b % hgroups, b / hgroups);
+  else
+    chunk_pp_body<BS>(ca, smem, b - n_dec);
+}
+
 
 // Log-sum-exp merge of the partials of split items. Merge record: (seq, KV head,
 // first new token, first slot | pieces << 20). One thread per (row of the 128, four
@@ -1062,14 +1093,25 @@ extern "C" int64_t pkv_chunk_workspace_bytes(int32_t num_partials, int32_t head_
 }
 
 namespace {
-int prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+// A checked chunk launch (the chunk kernel and, for split blocks, the merge), built by
+// chunk_prepare from the arguments of pkv_paged_attention_prefill_chunks; empty when there
+// is nothing to launch.
+struct ChunkLaunch {
+  ChunkArgs a;
+  ChunkFn fn;
+  int num_work, num_merges, layers, head_dim;
+  const int4* merges;
+  bool empty;
+};
+
+int chunk_prepare(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
                    int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens,
                    const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs, int32_t total_q,
                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                    int32_t max_seq_len, float scale, float k_scale, float v_scale, const float* k_head_scales,
                    const float* v_head_scales, const int32_t* work_items, int32_t num_work, const int32_t* merges,
                    int32_t num_merges, int32_t num_partials, void* workspace, int64_t workspace_bytes,
-                   float* lse_out, const pkv::Layers& layers, void* stream) {
+                   float* lse_out, const pkv::Layers& layers, ChunkLaunch* L) {
   using pkv::fail;
   if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || table_width < 0 || num_blocks < 0 ||
       max_seq_len < 0 || num_work < 0 || num_merges < 0 || num_partials < 0 || num_partials >= (1 << kSlotBits))
@@ -1090,6 +1132,7 @@ int prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cach
   if (cache_dtype == PKV_BF16 && head_dim == 128) fn = block_size == 16 ? chunk_pp_kernel<16> : chunk_pp_kernel<32>;
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return fail(PKV_ERR_INVALID, "prefill_chunks: scales must be > 0");
+  L->empty = true;
   if (num_work == 0 || num_seqs == 0 || total_q == 0) return PKV_OK;
   if (num_blocks < 1) return fail(PKV_ERR_INVALID, "prefill_chunks: the cache has no blocks");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seqlens_q || !work_items)
@@ -1138,17 +1181,46 @@ int prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cach
   a.ls_cache = layers.cache;
   a.ls_lse = layers.lse;
   a.ls_ws = pkv_chunk_workspace_bytes(num_partials, head_dim) / 4;
-  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3(num_work, 1, layers.n), dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: launch failed: %s", hipGetErrorString(e));
-  if (num_merges > 0) {
-    hipLaunchKernelGGL(pick_merge(head_dim), dim3(num_merges, kRows * (head_dim / 4) / 256, layers.n), dim3(256), 0,
-                       st, a, reinterpret_cast<const int4*>(merges));
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill_chunks: merge launch failed: %s", hipGetErrorString(e));
-  }
+  L->a = a;
+  L->fn = fn;
+  L->num_work = num_work;
+  L->num_merges = num_merges;
+  L->layers = layers.n;
+  L->head_dim = head_dim;
+  L->merges = reinterpret_cast<const int4*>(merges);
+  L->empty = false;
   return PKV_OK;
+}
+
+int chunk_launch_merge(const ChunkLaunch& L, hipStream_t st) {
+  if (L.empty || L.num_merges == 0) return PKV_OK;
+  hipLaunchKernelGGL(pick_merge(L.head_dim), dim3(L.num_merges, kRows * (L.head_dim / 4) / 256, L.layers), dim3(256),
+                     0, st, L.a, L.merges);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::fail(PKV_ERR_HIP, "prefill_chunks: merge launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int prefill_chunks(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                   int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens,
+                   const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs, int32_t total_q,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t max_seq_len, float scale, float k_scale, float v_scale, const float* k_head_scales,
+                   const float* v_head_scales, const int32_t* work_items, int32_t num_work, const int32_t* merges,
+                   int32_t num_merges, int32_t num_partials, void* workspace, int64_t workspace_bytes,
+                   float* lse_out, const pkv::Layers& layers, void* stream) {
+  ChunkLaunch L;
+  const int rc = chunk_prepare(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, cu_seqlens_q,
+                               table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, max_seq_len, scale, k_scale, v_scale, k_head_scales, v_head_scales,
+                               work_items, num_work, merges, num_merges, num_partials, workspace, workspace_bytes,
+                               lse_out, layers, &L);
+  if (rc != PKV_OK || L.empty) return rc;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(L.fn, dim3(L.num_work, 1, L.layers), dim3(kThreads), 0, st, L.a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::fail(PKV_ERR_HIP, "prefill_chunks: launch failed: %s", hipGetErrorString(e));
+  return chunk_launch_merge(L, st);
 }
 }  // namespace
 
@@ -1187,4 +1259,101 @@ extern "C" int pkv_paged_attention_prefill_chunks_layers(
                         table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                         max_seq_len, scale, k_scale, v_scale, k_head_scales, v_head_scales, work_items, num_work,
                         merges, num_merges, num_partials, workspace, workspace_bytes, lse_out, ls, stream);
+}
+
+namespace {
+// Per-workgroup costs that balance a one-launch mixed step (bf16 cache, head_dim 128, 8
+// KV heads per decode workgroup), measured on MI355X with these kernels: a decode slot
+// streams ~41 GB/s once fewer slots than units share the memory (64 slots moved a
+// 203 MB step in 78 us), and a chunk item takes ~1.8 us of a unit per 64-key tile of its
+// 128 rows (the 8,448 item-tiles of a 4 x 512-token step in 59 us on 256 units).
+constexpr double kMixedSlotBytesPerUs = 41.0e3;
+constexpr double kMixedChunkTileUs = 1.8;
+}  // namespace
+
+extern "C" int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
+                                      int32_t cache_dtype, int32_t num_kv_heads, int32_t group, int32_t head_dim,
+                                      int32_t block_size, int32_t* slots) {
+  using pkv::fail;
+  if (num_seqs < 0 || num_kv_heads <= 0 || group <= 0 || !slots || (num_seqs > 0 && (!q_lens || !seq_lens)))
+    return fail(PKV_ERR_INVALID, "mixed_decode_slots: bad arguments");
+  int full = 0;
+  int rc = pkv_decode_split_slots(cache_dtype, num_kv_heads, head_dim, block_size, &full);
+  if (rc != PKV_OK) return rc;
+  *slots = full;
+  if (cache_dtype != PKV_BF16 || head_dim != 128 || num_kv_heads % 8 != 0 || group > 16 || kRows % group != 0)
+    return PKV_OK;                                       // two launches: the decode takes the device
+  int64_t dec_tiles = 0, chunk_tiles = 0;
+  const int32_t QB = kRows / group;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t q = q_lens[s], L = seq_lens[s];
+    if (q < 0 || L < 0 || q > L) return fail(PKV_ERR_INVALID, "mixed_decode_slots: sequence %d q_len %d seq_len %d", s, q, L);
+    if (q == 1) dec_tiles += (L + 15) / 16;
+    if (q < 2) continue;
+    for (int32_t q0 = 0; q0 < q; q0 += QB)
+      chunk_tiles += (int64_t(std::min(L, L - q + std::min(q, q0 + QB))) + kKeys - 1) / kKeys * num_kv_heads;
+  }
+  if (dec_tiles == 0 || chunk_tiles == 0) return PKV_OK;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(PKV_ERR_HIP, "mixed_decode_slots: device query failed");
+  const int hgroups = num_kv_heads / 8;
+  const double dec = double(dec_tiles) * hgroups * (16.0 * 8 * head_dim * 2 * 2) / kMixedSlotBytesPerUs;
+  const double chk = double(chunk_tiles) * kMixedChunkTileUs;
+  const int wgs = int(std::lround(cus * dec / (dec + chk)));
+  *slots = std::max(1, std::min(full, std::max(1, wgs) / hgroups));
+  return PKV_OK;
+}
+
+extern "C" int pkv_paged_attention_mixed(
+    void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache, int32_t cache_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t table_width,
+    int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
+    const float* k_head_scales, const float* v_head_scales, const int32_t* decode_rows, int32_t num_decode_rows,
+    const int32_t* split_plan, int32_t split_slots, int32_t tiles_per_slot, int32_t max_pieces,
+    void* split_workspace, size_t split_workspace_bytes, const int32_t* chunk_items, int32_t num_chunk_items,
+    const int32_t* chunk_merges, int32_t num_chunk_merges, int32_t num_chunk_partials, void* chunk_workspace,
+    int64_t chunk_workspace_bytes, float* lse_out, void* stream) {
+  using pkv::fail;
+  if (num_decode_rows < 0 || num_chunk_items < 0) return fail(PKV_ERR_INVALID, "mixed: bad sizes");
+  pkv::split::SplitLaunch SL;
+  SL.empty = true;
+  if (num_decode_rows > 0) {
+    const int rc = pkv::split::split_prepare(
+        out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, table_width, num_seqs, num_q_heads,
+        num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, k_scale, v_scale, k_head_scales,
+        v_head_scales, decode_rows, num_decode_rows, cu_seqlens_q, total_q, split_plan, split_slots, tiles_per_slot,
+        max_pieces, split_workspace, split_workspace_bytes, lse_out, pkv::Layers{}, &SL);
+    if (rc != PKV_OK) return rc;
+  }
+  ChunkLaunch CL;
+  {
+    const int rc = chunk_prepare(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens,
+                                 cu_seqlens_q, table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, num_blocks, max_seq_len, scale, k_scale, v_scale, k_head_scales,
+                                 v_head_scales, chunk_items, num_chunk_items, chunk_merges, num_chunk_merges,
+                                 num_chunk_partials, chunk_workspace, chunk_workspace_bytes, lse_out, pkv::Layers{},
+                                 &CL);
+    if (rc != PKV_OK) return rc;
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool one = !SL.empty && !CL.empty && cache_dtype == PKV_BF16 && head_dim == 128 && SL.hpw == 8 &&
+                   SL.hpw * 64 == kThreads && (block_size == 16 || block_size == 32);
+  if (one) {
+    const int n_dec = SL.hgroups * SL.num_slots;
+    hipLaunchKernelGGL(block_size == 16 ? mixed_pp_kernel<16> : mixed_pp_kernel<32>, dim3(n_dec + CL.num_work, 1, 1),
+                       dim3(kThreads), 0, st, SL.args, CL.a, n_dec, SL.hgroups);
+  } else {
+    if (!SL.empty)
+      hipLaunchKernelGGL(reinterpret_cast<void (*)(pkv::split::DecodeArgs)>(const_cast<void*>(SL.pass)),
+                         dim3(SL.hgroups, SL.num_slots, SL.layers), dim3(SL.hpw * 64), 0, st, SL.args);
+    if (!CL.empty) hipLaunchKernelGGL(CL.fn, dim3(CL.num_work, 1, CL.layers), dim3(kThreads), 0, st, CL.a);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "mixed: launch failed: %s", hipGetErrorString(e));
+  int rc = pkv::split::split_launch_merge(SL, st);
+  if (rc != PKV_OK) return rc;
+  return chunk_launch_merge(CL, st);
 }

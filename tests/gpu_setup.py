@@ -291,6 +291,30 @@ def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_to
     return out, lse_t
 
 
+def run_mixed(st: Step, num_slots: Optional[int] = None, min_piece_tokens: int = 0, lse: bool = True,
+              chunk_slots: Optional[int] = None, min_piece_tiles: int = 0):
+    """A mixed step through pkv_paged_attention_mixed (one launch plus the merges for a
+    bf16 cache at head_dim 128 with 8k KV heads, else the two kernels in turn); decode
+    slots from mixed_decode_slots when num_slots is None."""
+    w = st.w
+    T, Hq, d = w.total_q, w.num_q_heads, w.head_dim
+    msl = int(w.seq_lens.max())
+    cdt = pkv.FP8 if w.cache_dtype == "fp8" else pkv.BF16
+    if num_slots is None:
+        num_slots = pkv.mixed_decode_slots(w.q_lens, w.seq_lens, cdt, w.num_kv_heads, w.group, d, w.block_size)
+    if chunk_slots is None:
+        chunk_slots = pkv.chunk_slots(cdt, d, w.block_size)
+    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, w.num_kv_heads, w.group, num_slots, min_piece_tokens,
+                              chunk_slots, min_piece_tiles)
+    out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_t = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    pkv.paged_attention_mixed(out, st.q, st.k_cache, st.v_cache, st.bt_d, st.lens_d, st.cu_d, mp,
+                              mp.to_device(d, Hq), w.num_kv_heads, w.block_size, msl, w.softmax_scale, w.k_scale,
+                              w.v_scale, lse=lse_t, **heads(w))
+    torch.cuda.synchronize()
+    return out, lse_t
+
+
 ORACLE_JOBS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_jobs.py")
 
 

@@ -21,7 +21,7 @@ import workloads
 from oracle import fp8 as ofp8
 
 from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_planes, oracle_scales, out_f64,
-                       report_error, run_decode, run_decode_split, run_mixed_two_launch, run_varlen)
+                       report_error, run_decode, run_decode_split, run_mixed, run_mixed_two_launch, run_varlen)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,16 +96,15 @@ def test_decode_paths_with_late_outlier_keys(cdt):
         np.testing.assert_allclose(l_, ref_lse, rtol=lse_rtol(w.head_dim), atol=LSE_ATOL)
 
 
-MIXED = [("bf16", 128, 4), ("bf16", 64, 8), ("fp8", 128, 4), ("bf16", 128, 1)]
+MIXED = [("bf16", 128, 4, 2), ("bf16", 64, 8, 2), ("fp8", 128, 4, 2), ("bf16", 128, 1, 2), ("bf16", 128, 4, 8)]
 
 
-@pytest.mark.parametrize("cdt,d,G", MIXED, ids=[f"{a}-d{b}-g{c}" for a, b, c in MIXED])
-def test_mixed_paths_with_late_outlier_keys(cdt, d, G):
-    seed = zlib.crc32(f"out{cdt}{d}{G}".encode()) % 10_000
+@pytest.mark.parametrize("cdt,d,G,Hkv", MIXED, ids=[f"{a}-d{b}-g{c}-kv{e}" for a, b, c, e in MIXED])
+def test_mixed_paths_with_late_outlier_keys(cdt, d, G, Hkv):
+    seed = zlib.crc32(f"out{cdt}{d}{G}{Hkv}".encode()) % 10_000
     # decode rows, a chunk after a long cached prefix, a full prefill, a short chunk
     L = [600, 1300, 400, 2000, 90]
     q = [1, 300, 400, 1, 37]
-    Hkv = 2
     w = workloads.small_varlen(seed, L, q, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, block_size=16,
                                dtype="bf16", cache_dtype=cdt)
     if cdt == "fp8":
@@ -131,6 +130,10 @@ def test_mixed_paths_with_late_outlier_keys(cdt, d, G):
     for n, cs, mpt in ((None, 0, 0), (None, None, 0), (3, 5000, 0), (None, 7, 2)):
         runs.append((f"two launches ({n} / {cs} / {mpt})", run_mixed_two_launch(st, num_slots=n, chunk_slots=cs,
                                                                                 min_piece_tiles=mpt)))
+    # the mixed entry point (one launch for bf16 at head_dim 128 with 8k KV heads)
+    for n, cs, mpt in ((None, None, 0), (1, 5000, 0), (3, 0, 0)):
+        runs.append((f"mixed entry ({n} / {cs} / {mpt})", run_mixed(st, num_slots=n, chunk_slots=cs,
+                                                                   min_piece_tiles=mpt)))
     for tag, (out, lse) in runs:
         o, l_ = out_f64(out), lse.cpu().numpy().astype(np.float64)
         assert not np.isnan(o).any(), f"{tag}: unwritten rows"

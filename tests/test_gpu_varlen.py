@@ -9,8 +9,8 @@ import torch
 import paged_kv_cache_42_amd as pkv
 import workloads
 
-from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_planes, out_f64, run_mixed_two_launch,
-                       run_varlen)
+from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_planes, out_f64, run_mixed,
+                       run_mixed_two_launch, run_varlen)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,9 +20,12 @@ LSE_ATOL = 2.0 ** -8   # weights enter P.V rounded to bf16 (see the decode tests
 # two-launch variants: (decode split slots, chunk slots, min piece tiles); None = the
 # device's resident count; 5000 chunk slots cut every block into single tiles
 TWO_LAUNCH = ((None, None, 0), (3, 5000, 0), (None, 7, 2), (None, 0, 0))
+# pkv_paged_attention_mixed variants: (decode slots, chunk slots, min piece tiles); None
+# decode slots = mixed_decode_slots
+ONE_LAUNCH = ((None, None, 0), (1, 5000, 0), (None, 0, 0), (64, 7, 2))
 
 
-def _check(w, two_launch=TWO_LAUNCH):
+def _check(w, two_launch=TWO_LAUNCH, one_launch=ONE_LAUNCH):
     st = build_step(w)
     tabs, bt, cu, slots, kp, vp = oracle_planes(st)
     assert (st.bt == bt).all() and (st.cu == cu).all() and (st.slots == slots).all()
@@ -39,6 +42,14 @@ def _check(w, two_launch=TWO_LAUNCH):
         assert not np.isnan(got).any(), f"{tag}: unwritten rows"
         assert_close(got, ref, dt, tag)
         np.testing.assert_allclose(l2.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
+    # and through the mixed entry point (one launch for bf16 at head_dim 128 with 8k KV heads)
+    for n, cs, mpt in one_launch:
+        o3, l3 = run_mixed(st, num_slots=n, chunk_slots=cs, min_piece_tiles=mpt)
+        got = out_f64(o3)
+        tag = f"{w.name} mixed entry ({n} / {cs} / {mpt})"
+        assert not np.isnan(got).any(), f"{tag}: unwritten rows"
+        assert_close(got, ref, dt, tag)
+        np.testing.assert_allclose(l3.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
     return st, out, lse
 
 
@@ -80,6 +91,25 @@ def test_small_mixed_steps(cdt, d, G, bs):
     if cdt == "fp8":
         w.k_scale, w.v_scale = 0.5, 0.25
     _check(w)
+
+
+# one-launch mixed kernel shapes: bf16 cache, head_dim 128, 8 KV heads; decode rows only,
+# chunks only, and both, with contexts crossing tiles, blocks and slots
+ONE_CASES = [(G, bs, kind) for G in (1, 4) for bs in (16, 32) for kind in ("both", "decode", "chunks")]
+
+
+@pytest.mark.parametrize("G,bs,kind", ONE_CASES, ids=[f"g{a}-bs{b}-{c}" for a, b, c in ONE_CASES])
+def test_one_launch_mixed_steps(G, bs, kind):
+    seed = zlib.crc32(f"m{G}{bs}{kind}".encode()) % 10_000
+    L = {"both": [1, 40, 300, 17, 150, 64, 513, 2000, 9, 700],
+         "decode": [1, 40, 300, 17, 1500, 64, 513],
+         "chunks": [300, 17, 150, 64, 513]}[kind]
+    q = {"both": [1, 1, 300, 17, 33, 1, 200, 1, 7, 1],
+         "decode": [1] * 7,
+         "chunks": [300, 17, 33, 2, 200]}[kind]
+    w = workloads.small_varlen(seed, L, q, num_q_heads=8 * G, num_kv_heads=8, head_dim=128, block_size=bs,
+                               dtype="bf16", cache_dtype="bf16")
+    _check(w, two_launch=(), one_launch=ONE_LAUNCH + ((3, 0, 0), (1000, 0, 0)))
 
 
 def test_physical_permutation_bitwise():
