@@ -682,8 +682,8 @@ DecodeFn pick_mfma(int D, int BS) {
 template <int CDT, int D, int HPW>
 DecodeFn pick_split_bs(int BS) {
   switch (BS) {
-    case 16: return decode_split_kernel<CDT, D, 16, HPW, kSplitRing, split_tps(CDT)>;
-    case 32: return decode_split_kernel<CDT, D, 32, HPW, kSplitRing, split_tps(CDT)>;
+    case 16: return decode_split_kernel<CDT, D, 16, HPW, kSplitRing, split_tps(CDT, D)>;
+    case 32: return decode_split_kernel<CDT, D, 32, HPW, kSplitRing, split_tps(CDT, D)>;
     default: return nullptr;
   }
 }

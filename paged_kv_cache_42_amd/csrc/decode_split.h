@@ -100,9 +100,10 @@ __device__ __forceinline__ void split_row(const DecodeArgs& a, int s, int& b, in
 // Tiles in each wave's load ring of the balanced-split kernel: while one is consumed,
 // NS - 1 are in flight.
 constexpr int kSplitRing = 2;
-// Tiles folded per softmax step of the balanced-split kernel: two for E4M3 caches, whose
-// 16-token tiles carry half the bytes of bf16 ones through the same per-tile work.
-constexpr int split_tps(int cdt) { return cdt == PKV_FP8_E4M3 ? 2 : 1; }
+// Tiles folded per softmax step of the balanced-split kernel: two where a 16-token tile of
+// a KV head carries 2 KB per plane or less (E4M3 caches, bf16 at head_dim 64), half the
+// bytes of a bf16 tile at head_dim 128 through the same per-tile work.
+constexpr int split_tps(int cdt, int d) { return cdt == PKV_FP8_E4M3 || d == 64 ? 2 : 1; }
 
 // Balanced split decode (bf16 queries; bf16 or E4M3 cache). The context of every
 // sequence is cut into 16-token tiles and the tiles of all sequences are laid end to
