@@ -448,6 +448,10 @@ def sched_replay(max_steps, only=None):
     from workloads import replay
     out = {}
     runs = [("bf16", workloads.config5("bf16"), {}), ("fp8", workloads.config5("fp8"), {}),
+            # steps with decode rows and prefill chunks as two launches (split decode, then
+            # the chunk kernel) instead of one launch of the mixed kernel
+            ("bf16_two_launches", workloads.config5("bf16"), {"one_launch": False}),
+            ("fp8_two_launches", workloads.config5("fp8"), {"one_launch": False}),
             # one launch per kernel and layer, as a model running its layers in turn issues
             # them (the runs above launch each kernel once per step for all 16 layers)
             ("bf16_per_layer", workloads.config5("bf16"), {"layer_batched": False}),

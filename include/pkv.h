@@ -426,19 +426,21 @@ int pkv_build_mixed_step(int32_t num_seqs, const int32_t* q_lens, const int32_t*
                          int32_t* merges, int32_t merge_capacity, int32_t* merge_count,
                          int32_t* num_partials);
 
-/* Decode slots for the one launch of pkv_paged_attention_mixed: the number of balanced-split
- * slots over which a mixed step's decode rows (q_lens[s] == 1) finish together with its
- * chunk items (q_lens[s] >= 2, the pkv_build_chunk_work items) running on the other
- * compute units. q_lens, seq_lens: host int32 [num_seqs]. For a bf16 cache at head_dim 128
- * with num_kv_heads a multiple of 8 and rows of both kinds, *slots weighs the decode
- * rows' K/V bytes against the items' 64-key tiles with per-unit rates measured on MI355X
- * for these kernels, in [1, pkv_decode_split_slots]; otherwise (one kind of row, or a
- * shape that runs as two launches) *slots = pkv_decode_split_slots. Pass it to
- * pkv_build_mixed_step as num_slots. INVALID on a bad argument or q > L, and the errors
- * of pkv_decode_split_slots. */
+/* Decode slots per layer for the one launch of pkv_paged_attention_mixed (num_layers 1) or
+ * pkv_paged_attention_mixed_layers: the number of balanced-split slots over which a mixed
+ * step's decode rows (q_lens[s] == 1) finish together with its chunk items (q_lens[s] >= 2,
+ * the pkv_build_chunk_work items) running on the other compute units. q_lens, seq_lens:
+ * host int32 [num_seqs]. With L = ceil(pkv_decode_split_slots / num_layers) (the layers
+ * share the units): for a bf16 cache at head_dim 128 (block_size 16/32, num_kv_heads a
+ * multiple of 8) and rows of both kinds, *slots weighs the decode rows' K/V bytes against
+ * the items' 64-key tiles with per-unit rates measured on MI355X for these kernels, in
+ * [1, L]; otherwise (one kind of row, or a shape whose rates were not measured, where the
+ * decode then runs first and the chunk items after it in the same launch) *slots = L.
+ * Pass it to pkv_build_mixed_step as num_slots.
+ * INVALID on a bad argument or q > L, and the errors of pkv_decode_split_slots. */
 int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
                            int32_t cache_dtype, int32_t num_kv_heads, int32_t group, int32_t head_dim,
-                           int32_t block_size, int32_t* slots);
+                           int32_t block_size, int32_t num_layers, int32_t* slots);
 
 /* The attention of a mixed continuous-batching step ([CB] "5. Technical explanation",
  * mixed batching: decode rows and prefill chunks in one batch; every row's attention as
@@ -450,8 +452,8 @@ int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, const int32_
  * split_workspace (>= pkv_decode_split_workspace_bytes; not needed when max_pieces <= 1) as
  * for pkv_paged_attention_decode_split's row map, chunk_items / chunk_merges /
  * num_chunk_partials and chunk_workspace as for pkv_paged_attention_prefill_chunks;
- * num_decode_rows or num_chunk_items may be 0. With a bf16 cache at head_dim 128, block
- * size 16 or 32 and num_kv_heads a multiple of 8, one kernel runs both kinds of
+ * num_decode_rows or num_chunk_items may be 0. With a bf16 or E4M3 cache at head_dim 64
+ * or 128, block size 16 or 32 and num_kv_heads a multiple of 8, one kernel runs both kinds of
  * workgroup: the first split_slots x num_kv_heads / 8 run the decode pass (one per compute
  * unit, for the whole pass), the rest the chunk items, on the units the decode leaves
  * free, so the memory-bound decode and the MFMA-bound chunks run at the same time (with
@@ -474,6 +476,29 @@ int pkv_paged_attention_mixed(void* out, const void* q, int32_t q_dtype, const v
                               int32_t num_chunk_merges, int32_t num_chunk_partials,
                               void* chunk_workspace, int64_t chunk_workspace_bytes, float* lse_out,
                               void* stream);
+
+/* pkv_paged_attention_mixed for layers->num_layers layers of one step in one launch (the
+ * decode workgroups of every layer first, then every layer's chunk items, longest first),
+ * with q, out, the cache planes and lse_out strided by layer as for
+ * pkv_paged_attention_decode_split_layers; the workspaces hold one plan's partials per layer
+ * (num_layers x the bytes of one). Errors as for pkv_paged_attention_mixed, and INVALID for
+ * a NULL layers, num_layers < 1 or a bad stride. */
+int pkv_paged_attention_mixed_layers(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                     const void* v_cache, int32_t cache_dtype,
+                                     const int32_t* block_tables, const int32_t* seq_lens,
+                                     const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs,
+                                     int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                     const float* k_head_scales, const float* v_head_scales,
+                                     const int32_t* decode_rows, int32_t num_decode_rows,
+                                     const int32_t* split_plan, int32_t split_slots,
+                                     int32_t tiles_per_slot, int32_t max_pieces, void* split_workspace,
+                                     size_t split_workspace_bytes, const int32_t* chunk_items,
+                                     int32_t num_chunk_items, const int32_t* chunk_merges,
+                                     int32_t num_chunk_merges, int32_t num_chunk_partials,
+                                     void* chunk_workspace, int64_t chunk_workspace_bytes,
+                                     float* lse_out, const pkv_layers* layers, void* stream);
 
 /* Slots to balance chunk work over on the current device (its compute units: a second
  * resident workgroup shares a unit's issue slots, so it adds little throughput): the

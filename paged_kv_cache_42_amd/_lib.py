@@ -115,10 +115,13 @@ _SIGS = {
                                                            i32, i32, i32, vp, vp]),
     "pkv_paged_attention_prefill_varlen": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
                                                      i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, vp]),
-    "pkv_mixed_decode_slots": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, i32, P_i32]),
+    "pkv_mixed_decode_slots": (C.c_int, [i32, vp, vp, i32, i32, i32, i32, i32, i32, P_i32]),
     "pkv_paged_attention_mixed": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                             i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, i32, i32, vp, sz, vp,
                                             i32, vp, i32, i32, vp, i64, vp, vp]),
+    "pkv_paged_attention_mixed_layers": (C.c_int, [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                   i32, i32, i32, f32, f32, f32, vp, vp, vp, i32, vp, i32, i32, i32,
+                                                   vp, sz, vp, i32, vp, i32, i32, vp, i64, vp, vp, vp]),
 }
 
 
@@ -788,15 +791,16 @@ class MixedPlan:
     def __init__(self, decode_rows, split, chunks):
         self.decode_rows, self.split, self.chunks = decode_rows, split, chunks
 
-    def to_device(self, head_dim: int, num_q_heads: int, device="cuda"):
+    def to_device(self, head_dim: int, num_q_heads: int, device="cuda", num_layers: int = 1):
         """The device arrays of paged_attention_mixed: (rows, split plan, split workspace)
-        (None when there is no decode row) and ChunkPlan.to_device (None when no chunk)."""
+        (None when there is no decode row) and ChunkPlan.to_device (None when no chunk),
+        workspaces sized for num_layers layers."""
         torch = _torch()
         dec = None
         if self.split is not None:
             dec = (torch.from_numpy(self.decode_rows).to(device), torch.from_numpy(self.split.plan).to(device),
-                   decode_split_workspace(self.split, num_q_heads, head_dim, device))
-        return dec, self.chunks.to_device(head_dim, device)
+                   decode_split_workspace(self.split, num_q_heads, head_dim, device, num_layers))
+        return dec, self.chunks.to_device(head_dim, device, num_layers)
 
 
 def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots: int,
@@ -832,15 +836,16 @@ def build_mixed_step(q_lens, seq_lens, num_kv_heads: int, group: int, num_slots:
 
 
 def mixed_decode_slots(q_lens, seq_lens, cache_dtype: int, num_kv_heads: int, group: int, head_dim: int,
-                       block_size: int) -> int:
-    """Decode slots for paged_attention_mixed's one launch: the slots that let the decode
-    rows finish with the chunk items running beside them (the full device when the step
-    has one kind of row only, or when the shape runs as two launches)."""
+                       block_size: int, num_layers: int = 1) -> int:
+    """Decode slots per layer for paged_attention_mixed's one launch: the slots that let
+    the decode rows finish with the chunk items running beside them (the layers' share of
+    the device when the step has one kind of row only, or when the shape runs as two
+    launches)."""
     q = np.ascontiguousarray(q_lens, dtype=np.int32)
     L = np.ascontiguousarray(seq_lens, dtype=np.int32)
     n = i32()
     check(lib().pkv_mixed_decode_slots(len(q), _np_ptr(q), _np_ptr(L), cache_dtype, num_kv_heads, group, head_dim,
-                                       block_size, C.byref(n)))
+                                       block_size, num_layers, C.byref(n)))
     return n.value
 
 
@@ -851,9 +856,15 @@ def paged_attention_mixed(out, q, k_cache, v_cache, block_tables, seq_lens, cu_s
     """The attention of a mixed step (decode rows and prefill chunks) as one launch plus
     the merges. plan: build_mixed_step's result (for one launch, over mixed_decode_slots
     decode slots); dev: plan.to_device(head_dim, num_q_heads); q/out [total_q][Hq][d],
-    cu_seqlens_q int32 [B + 1]; the rest as for paged_attention_prefill_chunks."""
+    cu_seqlens_q int32 [B + 1]; the rest as for paged_attention_prefill_chunks. With a
+    leading layer axis on q, out, the caches and lse (each layer contiguous) the layers run
+    in the same launch (pkv_paged_attention_mixed_layers; dev from
+    plan.to_device(..., num_layers=NL))."""
     torch = _torch()
     ddev, cdev = dev
+    layers = None
+    if q.dim() == 4:
+        layers, (out, q, k_cache, v_cache, lse) = _layered_attention(q.shape[0], out, q, k_cache, v_cache, lse)
     _require_cuda_contig(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, lse)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [total_q][Hq][d] of one dtype")
@@ -891,8 +902,10 @@ def paged_attention_mixed(out, q, k_cache, v_cache, block_tables, seq_lens, cu_s
             d, block_size, k_cache.shape[0], max_seq_len, scale, k_scale, v_scale,
             *map(_np_ptr, _heads(k_head_scales, v_head_scales, num_kv_heads)), _dptr(rows), n_rows, _dptr(plan_d),
             slots, tps, mp, _dptr(sws), sws_bytes, _dptr(work), n_work, _dptr(merges), n_merges,
-            plan.chunks.num_partials, _dptr(cws), cws_bytes, _dptr(lse), _stream(stream))
-    return _launch(lib().pkv_paged_attention_mixed, args, defer)
+            plan.chunks.num_partials, _dptr(cws), cws_bytes, _dptr(lse))
+    if layers is None:
+        return _launch(lib().pkv_paged_attention_mixed, (*args, _stream(stream)), defer)
+    return _launch(lib().pkv_paged_attention_mixed_layers, (*args, layers, _stream(stream)), defer)
 
 
 def paged_attention_prefill_varlen(out, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, work,

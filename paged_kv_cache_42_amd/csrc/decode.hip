@@ -622,7 +622,7 @@ __global__ void __launch_bounds__(HPW * 64, 3) decode_mfma_kernel(DecodeArgs a) 
 template <int CDT, int D, int BS, int HPW, int NS = kSplitRing, int TPS = 1>
 __global__ void __launch_bounds__(HPW * 64, 2) decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[split_lds_bytes<CDT, D, HPW, TPS>()];
-  decode_split_body<CDT, D, BS, HPW, NS, TPS>(a, lds, blockIdx.x, blockIdx.y);
+  decode_split_body<CDT, D, BS, HPW, NS, TPS>(a, lds, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 constexpr int kWaves = 4;

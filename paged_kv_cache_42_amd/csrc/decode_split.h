@@ -61,8 +61,7 @@ struct LayerPtrs {
   float* ws_o;
   float* ws_lse;
 };
-__device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeArgs& a) {
-  const int64_t l = blockIdx.z;
+__device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeArgs& a, int64_t l) {
   LayerPtrs p;
   p.q = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.q) + l * a.ls_in);
   p.out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + l * a.ls_out);
@@ -73,6 +72,7 @@ __device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeArgs& a) {
   p.ws_lse = a.ws_lse ? a.ws_lse + l * a.ls_ws : nullptr;
   return p;
 }
+__device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeArgs& a) { return layer_ptrs(a, blockIdx.z); }
 
 // Partial of one piece of the balanced split, as an index into [num_slots][2][Hq]: a
 // sequence spanning slots first..first+np-1 leaves its piece p in slot first + p. Only the
@@ -122,10 +122,11 @@ constexpr int split_lds_bytes() {
 }
 
 // The pass of one workgroup: KV-head group `hgroup` (waves take KV heads hgroup * HPW + w)
-// of slot `slot`, on layer blockIdx.z; lds: split_lds_bytes<CDT, D, HPW, TPS>() bytes of
-// LDS, 16-byte aligned. Called by the decode kernel and by the mixed-step kernel.
+// of slot `slot`, on layer `layer`; lds: split_lds_bytes<CDT, D, HPW, TPS>() bytes of LDS,
+// 16-byte aligned. Called by the decode kernel and by the mixed-step kernel.
 template <int CDT, int D, int BS, int HPW, int NS = kSplitRing, int TPS = 1>
-__device__ __forceinline__ void decode_split_body(const DecodeArgs& a, uint8_t* lds, int hgroup, int slot) {
+__device__ __forceinline__ void decode_split_body(const DecodeArgs& a, uint8_t* lds, int hgroup, int slot,
+                                                  int layer) {
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
   constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
@@ -156,7 +157,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, uint8_t* 
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int hl_q = hl < G ? hl : hl % G;
-  const LayerPtrs lp = layer_ptrs(a);
+  const LayerPtrs lp = layer_ptrs(a, layer);
   const uint8_t* kc = lp.kc;
   const uint8_t* vc = lp.vc;
   const int64_t row_bytes = int64_t(Hkv) * D * EB;

@@ -97,8 +97,7 @@ struct ChunkLayer {
   float* ws_o;
   float* ws_lse;
 };
-__device__ __forceinline__ ChunkLayer chunk_layer(const ChunkArgs& a) {
-  const int64_t l = blockIdx.z;
+__device__ __forceinline__ ChunkLayer chunk_layer(const ChunkArgs& a, int64_t l) {
   ChunkLayer p;
   p.q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.q) + l * a.ls_in);
   p.out = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(a.out) + l * a.ls_out);
@@ -109,6 +108,7 @@ __device__ __forceinline__ ChunkLayer chunk_layer(const ChunkArgs& a) {
   p.ws_lse = a.ws_lse ? a.ws_lse + l * a.ls_ws : nullptr;
   return p;
 }
+__device__ __forceinline__ ChunkLayer chunk_layer(const ChunkArgs& a) { return chunk_layer(a, blockIdx.z); }
 
 template <int D>
 struct Lds {
@@ -299,8 +299,11 @@ __device__ __forceinline__ void chunk_finish(const ChunkArgs& a, const ChunkLaye
   }
 }
 
+// One item of the chunk kernel: work record `item`, on layer `layer`; smem:
+// Lds<D>::kBytes bytes of LDS, 16-byte aligned. Called by the chunk kernel and by the
+// mixed-step kernel.
 template <int CDT, int D, int BS>
-__global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
+__device__ __forceinline__ void chunk_body(const ChunkArgs& a, uint8_t* smem, int item, int layer) {
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
   constexpr int EB = CDT == PKV_BF16 ? 2 : 1;
@@ -310,14 +313,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   constexpr int LPT = kKeys * CPK / kGroupThreads;       // chunk loads per thread per plane
   static_assert(kKeys * CPK % kGroupThreads == 0 && LPT >= 1, "tile / workgroup shape");
   static_assert(LPT <= 32, "mask word");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D>::kBytes];
   typedef __attribute__((address_space(4))) const int32_t* cptr_i32;
 
   // ---- item (uniform): rows of (seq, KV head, block of new tokens) over keys
   // [key_lo, key_end); slot >= 0: write a partial for the merge. A malformed item exits
   // before any barrier.
-  const int4 it = a.work[2 * blockIdx.x];
-  const int4 it2 = a.work[2 * blockIdx.x + 1];
+  const int4 it = a.work[2 * item];
+  const int4 it2 = a.work[2 * item + 1];
   const int s = it.x;
   const int g = it.y;
   const int q0 = it.z;
@@ -333,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
   const int key_end = max(0, min(it2.x, L));
   const int key_lo = it.w;
   if (key_lo < 0 || key_lo % kKeys != 0) return;
-  const ChunkLayer lp = chunk_layer(a);
+  const ChunkLayer lp = chunk_layer(a, layer);
 
   // the two groups take the first and the second half of the item's key tiles; each
   // has its own LDS buffers, and group 1 hands its row states to group 0 at the end
@@ -568,6 +570,12 @@ __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // s_waitcnt vmcnt(N), no other counter
+template <int CDT, int D, int BS>
+__global__ void __launch_bounds__(kThreads, 1) chunk_kernel(ChunkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D>::kBytes];
+  chunk_body<CDT, D, BS>(a, smem, blockIdx.x, blockIdx.z);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -581,7 +589,7 @@ constexpr int kPpLds = 2 * 4 * kKeys * 2 * 128;
 // `item`, on layer blockIdx.z; smem: kPpLds bytes of LDS, 16-byte aligned. Called by the
 // chunk kernel and by the mixed-step kernel.
 template <int BS>
-__device__ __forceinline__ void chunk_pp_body(const ChunkArgs& a, uint8_t* smem, int item) {
+__device__ __forceinline__ void chunk_pp_body(const ChunkArgs& a, uint8_t* smem, int item, int layer) {
   constexpr int D = 128;
   constexpr int KS = D / 32;
   constexpr int MT = D / 16;
@@ -611,7 +619,7 @@ __device__ __forceinline__ void chunk_pp_body(const ChunkArgs& a, uint8_t* smem,
   const int key_end = max(0, min(it2.x, L));
   const int key_lo = it.w;
   if (key_lo < 0 || key_lo % kKeys != 0) return;
-  const ChunkLayer lp = chunk_layer(a);
+  const ChunkLayer lp = chunk_layer(a, layer);
 
   const int gi = __builtin_amdgcn_readfirstlane(threadIdx.x / kGroupThreads);
   const int tid = threadIdx.x % kGroupThreads;
@@ -867,25 +875,39 @@ __device__ __forceinline__ void chunk_pp_body(const ChunkArgs& a, uint8_t* smem,
 template <int BS>
 __global__ void __launch_bounds__(kThreads, 1) chunk_pp_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPpLds];
-  chunk_pp_body<BS>(a, smem, blockIdx.x);
+  chunk_pp_body<BS>(a, smem, blockIdx.x, blockIdx.z);
 }
 
-// A mixed step in one launch (bf16 cache, head_dim 128): workgroups 0 .. n_dec - 1 run
-// the balanced-split decode pass over the step's decode rows (slot b / hgroups, KV-head
-// group b % hgroups, 8 KV heads per workgroup), the others run chunk items of its prefill
-// rows, one LDS array serving either. The decode workgroups come first, so they hold
-// their units for the whole pass while chunk items flow through the rest: the memory-bound
-// decode and the MFMA-bound chunks run side by side instead of one after the other.
-static_assert(pkv::split::split_lds_bytes<PKV_BF16, 128, 8, 1>() <= kPpLds, "decode fits the chunk LDS");
-template <int BS>
-__global__ void __launch_bounds__(kThreads, 1) mixed_pp_kernel(pkv::split::DecodeArgs da, ChunkArgs ca, int n_dec,
-                                                                int hgroups) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPpLds];
+// A mixed step in one launch: workgroups 0 .. layers x n_dec - 1 run the balanced-split
+// decode pass over the step's decode rows (layer b / n_dec; slot r / hgroups and KV-head
+// group r % hgroups of r = b mod n_dec, 8 KV heads per workgroup), the others chunk items
+// of its prefill rows (item c / layers of layer c % layers, c counting from the first chunk
+// workgroup: every layer's longest items first), one LDS array serving either. The decode
+// workgroups come first, so they hold their units for the whole pass while chunk items
+// flow through the rest: the memory-bound decode and the MFMA-bound chunks run side by
+// side instead of one after the other.
+template <int CDT, int D>
+constexpr int mixed_lds_bytes() {
+  constexpr int dec = pkv::split::split_lds_bytes<CDT, D, 8, pkv::split::split_tps(CDT, D)>();
+  constexpr int chk = CDT == PKV_BF16 && D == 128 ? kPpLds : Lds<D>::kBytes;
+  return dec > chk ? dec : chk;
+}
+template <int CDT, int D, int BS>
+__global__ void __launch_bounds__(kThreads, 1) mixed_kernel(pkv::split::DecodeArgs da, ChunkArgs ca, int n_dec,
+                                                             int hgroups, int layers) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[mixed_lds_bytes<CDT, D>()];
   const int b = blockIdx.x;
-  if (b < n_dec)
-    pkv::split::decode_split_body<PKV_BF16, 128, BS, 8, pkv::split::kSplitRing, 1>(da, smem, b % hgroups, b / hgroups);
-  else
-    chunk_pp_body<BS>(ca, smem, b - n_dec);
+  if (b < n_dec * layers) {
+    const int r = b % n_dec;
+    pkv::split::decode_split_body<CDT, D, BS, 8, pkv::split::kSplitRing, pkv::split::split_tps(CDT, D)>(
+        da, smem, r % hgroups, r / hgroups, b / n_dec);
+  } else {
+    const int c = b - n_dec * layers;
+    if constexpr (CDT == PKV_BF16 && D == 128)
+      chunk_pp_body<BS>(ca, smem, c / layers, c % layers);
+    else
+      chunk_body<CDT, D, BS>(ca, smem, c / layers, c % layers);
+  }
 }
 
 
@@ -1262,27 +1284,61 @@ extern "C" int pkv_paged_attention_prefill_chunks_layers(
 }
 
 namespace {
-// Per-workgroup costs that balance a one-launch mixed step (bf16 cache, head_dim 128, 8
-// KV heads per decode workgroup), measured on MI355X with these kernels: a decode slot
-// streams ~41 GB/s once fewer slots than units share the memory (64 slots moved a
-// 203 MB step in 78 us), and a chunk item takes ~1.8 us of a unit per 64-key tile of its
-// 128 rows (the 8,448 item-tiles of a 4 x 512-token step in 59 us on 256 units).
+// Per-workgroup costs that balance a one-launch mixed step (bf16 cache, head_dim 128),
+// measured on MI355X with these kernels: a decode slot streams ~41 GB/s once fewer slots
+// than units share the memory (64 slots moved a 203 MB step of bf16 rows in 78 us), and a
+// chunk item takes ~1.8 us of a unit per 64-key tile of its 128 rows (the 8,448
+// item-tiles of a 4 x 512-token step in 59 us on 256 units).
 constexpr double kMixedSlotBytesPerUs = 41.0e3;
 constexpr double kMixedChunkTileUs = 1.8;
+
+using MixedFn = void (*)(pkv::split::DecodeArgs, ChunkArgs, int, int, int);
+template <int CDT, int D>
+MixedFn pick_mixed_bs(int BS) {
+  switch (BS) {
+    case 16: return mixed_kernel<CDT, D, 16>;
+    case 32: return mixed_kernel<CDT, D, 32>;
+    default: return nullptr;
+  }
+}
+template <int CDT>
+MixedFn pick_mixed_d(int D, int BS) {
+  switch (D) {
+    case 64: return pick_mixed_bs<CDT, 64>(BS);
+    case 128: return pick_mixed_bs<CDT, 128>(BS);
+    default: return nullptr;
+  }
+}
+// The mixed kernel of a shape (null where the step runs as two launches): decode
+// workgroups of 8 KV heads, so num_kv_heads a multiple of 8.
+MixedFn pick_mixed(int cache_dtype, int head_dim, int block_size, int num_kv_heads) {
+  if (num_kv_heads % 8 != 0) return nullptr;
+  if (cache_dtype == PKV_BF16) return pick_mixed_d<PKV_BF16>(head_dim, block_size);
+  if (cache_dtype == PKV_FP8_E4M3) return pick_mixed_d<PKV_FP8_E4M3>(head_dim, block_size);
+  return nullptr;
+}
 }  // namespace
 
 extern "C" int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,
                                       int32_t cache_dtype, int32_t num_kv_heads, int32_t group, int32_t head_dim,
-                                      int32_t block_size, int32_t* slots) {
+                                      int32_t block_size, int32_t num_layers, int32_t* slots) {
   using pkv::fail;
-  if (num_seqs < 0 || num_kv_heads <= 0 || group <= 0 || !slots || (num_seqs > 0 && (!q_lens || !seq_lens)))
+  if (num_seqs < 0 || num_kv_heads <= 0 || group <= 0 || num_layers < 1 || !slots ||
+      (num_seqs > 0 && (!q_lens || !seq_lens)))
     return fail(PKV_ERR_INVALID, "mixed_decode_slots: bad arguments");
   int full = 0;
   int rc = pkv_decode_split_slots(cache_dtype, num_kv_heads, head_dim, block_size, &full);
   if (rc != PKV_OK) return rc;
-  *slots = full;
-  if (cache_dtype != PKV_BF16 || head_dim != 128 || num_kv_heads % 8 != 0 || group > 16 || kRows % group != 0)
-    return PKV_OK;                                       // two launches: the decode takes the device
+  const int per_layer = std::max(1, (full + num_layers - 1) / num_layers);   // the layers share the units
+  *slots = per_layer;
+  // Balanced slots where the rates below were measured (bf16 at head_dim 128). Elsewhere
+  // the decode keeps the layers' share of the units and runs first, the chunk items after
+  // it in the same launch: a byte rate misjudges an E4M3 or head_dim-64 slot (its tiles
+  // take about as long as a bf16 head_dim-128 tile for half the bytes or less), and too few
+  // slots made the decode the step's tail (E4M3 replay 12% slower than two launches).
+  if (!pick_mixed(cache_dtype, head_dim, block_size, num_kv_heads) || cache_dtype != PKV_BF16 || head_dim != 128 ||
+      group > 16 || kRows % group != 0)
+    return PKV_OK;
   int64_t dec_tiles = 0, chunk_tiles = 0;
   const int32_t QB = kRows / group;
   for (int32_t s = 0; s < num_seqs; ++s) {
@@ -1301,21 +1357,23 @@ extern "C" int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, c
   const int hgroups = num_kv_heads / 8;
   const double dec = double(dec_tiles) * hgroups * (16.0 * 8 * head_dim * 2 * 2) / kMixedSlotBytesPerUs;
   const double chk = double(chunk_tiles) * kMixedChunkTileUs;
-  const int wgs = int(std::lround(cus * dec / (dec + chk)));
-  *slots = std::max(1, std::min(full, std::max(1, wgs) / hgroups));
+  const int wgs = int(std::lround(cus * dec / (dec + chk)));         // decode units over all layers
+  *slots = std::max(1, std::min(per_layer, wgs / (hgroups * num_layers)));
   return PKV_OK;
 }
 
-extern "C" int pkv_paged_attention_mixed(
-    void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache, int32_t cache_dtype,
-    const int32_t* block_tables, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t table_width,
-    int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
-    const float* k_head_scales, const float* v_head_scales, const int32_t* decode_rows, int32_t num_decode_rows,
-    const int32_t* split_plan, int32_t split_slots, int32_t tiles_per_slot, int32_t max_pieces,
-    void* split_workspace, size_t split_workspace_bytes, const int32_t* chunk_items, int32_t num_chunk_items,
-    const int32_t* chunk_merges, int32_t num_chunk_merges, int32_t num_chunk_partials, void* chunk_workspace,
-    int64_t chunk_workspace_bytes, float* lse_out, void* stream) {
+namespace {
+int mixed_attention(void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                    int32_t cache_dtype, const int32_t* block_tables, const int32_t* seq_lens,
+                    const int32_t* cu_seqlens_q, int32_t table_width, int32_t num_seqs, int32_t total_q,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                    const float* k_head_scales, const float* v_head_scales, const int32_t* decode_rows,
+                    int32_t num_decode_rows, const int32_t* split_plan, int32_t split_slots, int32_t tiles_per_slot,
+                    int32_t max_pieces, void* split_workspace, size_t split_workspace_bytes,
+                    const int32_t* chunk_items, int32_t num_chunk_items, const int32_t* chunk_merges,
+                    int32_t num_chunk_merges, int32_t num_chunk_partials, void* chunk_workspace,
+                    int64_t chunk_workspace_bytes, float* lse_out, const pkv::Layers& layers, void* stream) {
   using pkv::fail;
   if (num_decode_rows < 0 || num_chunk_items < 0) return fail(PKV_ERR_INVALID, "mixed: bad sizes");
   pkv::split::SplitLaunch SL;
@@ -1325,7 +1383,7 @@ extern "C" int pkv_paged_attention_mixed(
         out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, table_width, num_seqs, num_q_heads,
         num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, k_scale, v_scale, k_head_scales,
         v_head_scales, decode_rows, num_decode_rows, cu_seqlens_q, total_q, split_plan, split_slots, tiles_per_slot,
-        max_pieces, split_workspace, split_workspace_bytes, lse_out, pkv::Layers{}, &SL);
+        max_pieces, split_workspace, split_workspace_bytes, lse_out, layers, &SL);
     if (rc != PKV_OK) return rc;
   }
   ChunkLaunch CL;
@@ -1334,17 +1392,17 @@ extern "C" int pkv_paged_attention_mixed(
                                  cu_seqlens_q, table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                                  block_size, num_blocks, max_seq_len, scale, k_scale, v_scale, k_head_scales,
                                  v_head_scales, chunk_items, num_chunk_items, chunk_merges, num_chunk_merges,
-                                 num_chunk_partials, chunk_workspace, chunk_workspace_bytes, lse_out, pkv::Layers{},
-                                 &CL);
+                                 num_chunk_partials, chunk_workspace, chunk_workspace_bytes, lse_out, layers, &CL);
     if (rc != PKV_OK) return rc;
   }
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool one = !SL.empty && !CL.empty && cache_dtype == PKV_BF16 && head_dim == 128 && SL.hpw == 8 &&
-                   SL.hpw * 64 == kThreads && (block_size == 16 || block_size == 32);
-  if (one) {
+  const MixedFn mfn = pick_mixed(cache_dtype, head_dim, block_size, num_kv_heads);
+  if (mfn && !SL.empty && !CL.empty && SL.hpw == 8 && SL.hpw * 64 == kThreads) {
     const int n_dec = SL.hgroups * SL.num_slots;
-    hipLaunchKernelGGL(block_size == 16 ? mixed_pp_kernel<16> : mixed_pp_kernel<32>, dim3(n_dec + CL.num_work, 1, 1),
-                       dim3(kThreads), 0, st, SL.args, CL.a, n_dec, SL.hgroups);
+    const int64_t grid = (int64_t(n_dec) + CL.num_work) * layers.n;
+    if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "mixed: grid of %lld workgroups", (long long)grid);
+    hipLaunchKernelGGL(mfn, dim3(uint32_t(grid), 1, 1), dim3(kThreads), 0, st, SL.args, CL.a, n_dec, SL.hgroups,
+                       layers.n);
   } else {
     if (!SL.empty)
       hipLaunchKernelGGL(reinterpret_cast<void (*)(pkv::split::DecodeArgs)>(const_cast<void*>(SL.pass)),
@@ -1356,4 +1414,46 @@ extern "C" int pkv_paged_attention_mixed(
   int rc = pkv::split::split_launch_merge(SL, st);
   if (rc != PKV_OK) return rc;
   return chunk_launch_merge(CL, st);
+}
+}  // namespace
+
+extern "C" int pkv_paged_attention_mixed(
+    void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache, int32_t cache_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t table_width,
+    int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
+    const float* k_head_scales, const float* v_head_scales, const int32_t* decode_rows, int32_t num_decode_rows,
+    const int32_t* split_plan, int32_t split_slots, int32_t tiles_per_slot, int32_t max_pieces,
+    void* split_workspace, size_t split_workspace_bytes, const int32_t* chunk_items, int32_t num_chunk_items,
+    const int32_t* chunk_merges, int32_t num_chunk_merges, int32_t num_chunk_partials, void* chunk_workspace,
+    int64_t chunk_workspace_bytes, float* lse_out, void* stream) {
+  return mixed_attention(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, cu_seqlens_q,
+                         table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_seq_len, scale, k_scale, v_scale, k_head_scales, v_head_scales, decode_rows,
+                         num_decode_rows, split_plan, split_slots, tiles_per_slot, max_pieces, split_workspace,
+                         split_workspace_bytes, chunk_items, num_chunk_items, chunk_merges, num_chunk_merges,
+                         num_chunk_partials, chunk_workspace, chunk_workspace_bytes, lse_out, pkv::Layers{}, stream);
+}
+
+extern "C" int pkv_paged_attention_mixed_layers(
+    void* out, const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache, int32_t cache_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t table_width,
+    int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, float k_scale, float v_scale,
+    const float* k_head_scales, const float* v_head_scales, const int32_t* decode_rows, int32_t num_decode_rows,
+    const int32_t* split_plan, int32_t split_slots, int32_t tiles_per_slot, int32_t max_pieces,
+    void* split_workspace, size_t split_workspace_bytes, const int32_t* chunk_items, int32_t num_chunk_items,
+    const int32_t* chunk_merges, int32_t num_chunk_merges, int32_t num_chunk_partials, void* chunk_workspace,
+    int64_t chunk_workspace_bytes, float* lse_out, const pkv_layers* layers, void* stream) {
+  pkv::Layers ls;
+  const int rc = pkv::layers_from("mixed_layers", layers, true,
+                                  pkv::kLayerIn | pkv::kLayerOut | pkv::kLayerCache | (lse_out ? pkv::kLayerLse : 0u),
+                                  &ls);
+  if (rc != PKV_OK) return rc;
+  return mixed_attention(out, q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, seq_lens, cu_seqlens_q,
+                         table_width, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_seq_len, scale, k_scale, v_scale, k_head_scales, v_head_scales, decode_rows,
+                         num_decode_rows, split_plan, split_slots, tiles_per_slot, max_pieces, split_workspace,
+                         split_workspace_bytes, chunk_items, num_chunk_items, chunk_merges, num_chunk_merges,
+                         num_chunk_partials, chunk_workspace, chunk_workspace_bytes, lse_out, ls, stream);
 }

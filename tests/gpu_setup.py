@@ -293,9 +293,9 @@ def run_mixed_two_launch(st: Step, num_slots: Optional[int] = None, min_piece_to
 
 def run_mixed(st: Step, num_slots: Optional[int] = None, min_piece_tokens: int = 0, lse: bool = True,
               chunk_slots: Optional[int] = None, min_piece_tiles: int = 0):
-    """A mixed step through pkv_paged_attention_mixed (one launch plus the merges for a
-    bf16 cache at head_dim 128 with 8k KV heads, else the two kernels in turn); decode
-    slots from mixed_decode_slots when num_slots is None."""
+    """A mixed step through pkv_paged_attention_mixed (one launch plus the merges with 8k
+    KV heads, else the two kernels in turn); decode slots from mixed_decode_slots when
+    num_slots is None."""
     w = st.w
     T, Hq, d = w.total_q, w.num_q_heads, w.head_dim
     msl = int(w.seq_lens.max())

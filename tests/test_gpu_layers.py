@@ -167,6 +167,58 @@ def test_chunks_and_mixed_step_layers(cdt, d, G):
     _all_written(out, "mixed step")
 
 
+@pytest.mark.parametrize("cdt,d,G", [("bf16", 128, 4), ("fp8", 128, 4), ("bf16", 64, 8), ("fp8", 64, 4)])
+def test_mixed_entry_one_launch_and_layers(cdt, d, G):
+    """pkv_paged_attention_mixed (one launch: decode slots and chunk items in one grid) and
+    its layer-batched form against the split decode + chunk kernel of the same plan, per
+    layer: the same device code on the same work, so bit-identical."""
+    Hkv = 8
+    w = workloads.small_varlen(79, [600, 1300, 400, 2000, 90, 3, 250], [1, 300, 400, 1, 37, 3, 1],
+                               num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, block_size=16, dtype="bf16",
+                               cache_dtype=cdt)
+    if cdt == "fp8":
+        w.k_scale, w.v_scale = 0.5, 0.25
+    st = build_step(w)
+    T, Hq = w.total_q, w.num_q_heads
+    msl = int(w.seq_lens.max())
+    mp = pkv.build_mixed_step(w.q_lens, w.seq_lens, Hkv, G, 5, 0, 256)
+    assert mp.chunks.num_partials > 0 and mp.split.max_pieces > 1, "both plans must leave partials"
+    plan_d = torch.from_numpy(mp.split.plan).cuda()
+    rows = torch.from_numpy(mp.decode_rows).cuda()
+    kc, vc = _layer_planes(st.k_cache), _layer_planes(st.v_cache)
+    qs = _queries(st.q)
+    ref = []
+    for l in range(NL):
+        out = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_decode_split(out, qs[l], kc[l], vc[l], st.bt_d, st.lens_d, plan_d, mp.split, Hkv,
+                                         w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale,
+                                         pkv.decode_split_workspace(mp.split, Hq, d), lse, rows=rows,
+                                         cu_seqlens_q=st.cu_d)
+        work, merges, cws = mp.chunks.to_device(d)
+        pkv.paged_attention_prefill_chunks(out, qs[l], kc[l], vc[l], st.bt_d, st.lens_d, st.cu_d, work, merges,
+                                           mp.chunks.num_partials, cws, Hkv, w.block_size, msl, w.softmax_scale,
+                                           w.k_scale, w.v_scale, lse=lse)
+        ref.append((out, lse))
+        one = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        one_lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_mixed(one, qs[l], kc[l], vc[l], st.bt_d, st.lens_d, st.cu_d, mp, mp.to_device(d, Hq),
+                                  Hkv, w.block_size, msl, w.softmax_scale, w.k_scale, w.v_scale, lse=one_lse)
+        torch.cuda.synchronize()
+        _same(one, out, f"layer {l} one-launch output")
+        _same(one_lse, lse, f"layer {l} one-launch log-sum-exp")
+    out = torch.full((NL, T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((NL, T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_mixed(out, _strided(qs), kc, vc, st.bt_d, st.lens_d, st.cu_d, mp,
+                              mp.to_device(d, Hq, num_layers=NL), Hkv, w.block_size, msl, w.softmax_scale,
+                              w.k_scale, w.v_scale, lse=lse)
+    torch.cuda.synchronize()
+    for l in range(NL):
+        _same(out[l], ref[l][0], f"layer {l} layer-batched one-launch output")
+        _same(lse[l], ref[l][1], f"layer {l} layer-batched one-launch log-sum-exp")
+    _all_written(out, "layer-batched mixed step")
+
+
 K_HEAD = np.array([0.25, 3.0, 1.0, 0.7], np.float32)
 V_HEAD = np.array([2.0, 0.3, 0.5, 4.0], np.float32)
 

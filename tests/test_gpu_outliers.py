@@ -96,7 +96,8 @@ def test_decode_paths_with_late_outlier_keys(cdt):
         np.testing.assert_allclose(l_, ref_lse, rtol=lse_rtol(w.head_dim), atol=LSE_ATOL)
 
 
-MIXED = [("bf16", 128, 4, 2), ("bf16", 64, 8, 2), ("fp8", 128, 4, 2), ("bf16", 128, 1, 2), ("bf16", 128, 4, 8)]
+MIXED = [("bf16", 128, 4, 2), ("bf16", 64, 8, 2), ("fp8", 128, 4, 2), ("bf16", 128, 1, 2), ("bf16", 128, 4, 8),
+         ("fp8", 64, 4, 8)]
 
 
 @pytest.mark.parametrize("cdt,d,G,Hkv", MIXED, ids=[f"{a}-d{b}-g{c}-kv{e}" for a, b, c, e in MIXED])
@@ -130,7 +131,7 @@ def test_mixed_paths_with_late_outlier_keys(cdt, d, G, Hkv):
     for n, cs, mpt in ((None, 0, 0), (None, None, 0), (3, 5000, 0), (None, 7, 2)):
         runs.append((f"two launches ({n} / {cs} / {mpt})", run_mixed_two_launch(st, num_slots=n, chunk_slots=cs,
                                                                                 min_piece_tiles=mpt)))
-    # the mixed entry point (one launch for bf16 at head_dim 128 with 8k KV heads)
+    # the mixed entry point (one launch with 8k KV heads)
     for n, cs, mpt in ((None, None, 0), (1, 5000, 0), (3, 0, 0)):
         runs.append((f"mixed entry ({n} / {cs} / {mpt})", run_mixed(st, num_slots=n, chunk_slots=cs,
                                                                    min_piece_tiles=mpt)))

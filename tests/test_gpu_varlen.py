@@ -42,7 +42,7 @@ def _check(w, two_launch=TWO_LAUNCH, one_launch=ONE_LAUNCH):
         assert not np.isnan(got).any(), f"{tag}: unwritten rows"
         assert_close(got, ref, dt, tag)
         np.testing.assert_allclose(l2.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
-    # and through the mixed entry point (one launch for bf16 at head_dim 128 with 8k KV heads)
+    # and through the mixed entry point (one launch with 8k KV heads)
     for n, cs, mpt in one_launch:
         o3, l3 = run_mixed(st, num_slots=n, chunk_slots=cs, min_piece_tiles=mpt)
         got = out_f64(o3)
@@ -93,22 +93,26 @@ def test_small_mixed_steps(cdt, d, G, bs):
     _check(w)
 
 
-# one-launch mixed kernel shapes: bf16 cache, head_dim 128, 8 KV heads; decode rows only,
-# chunks only, and both, with contexts crossing tiles, blocks and slots
-ONE_CASES = [(G, bs, kind) for G in (1, 4) for bs in (16, 32) for kind in ("both", "decode", "chunks")]
+# one-launch mixed kernel shapes (8 KV heads): bf16 at head_dim 128 with decode rows only,
+# chunks only, and both; E4M3 and head_dim 64 with both; contexts crossing tiles, blocks
+# and slots
+ONE_CASES = [("bf16", 128, G, bs, kind) for G in (1, 4) for bs in (16, 32) for kind in ("both", "decode", "chunks")]
+ONE_CASES += [(cdt, d, 4, bs, "both") for cdt, d in (("fp8", 128), ("bf16", 64), ("fp8", 64)) for bs in (16, 32)]
 
 
-@pytest.mark.parametrize("G,bs,kind", ONE_CASES, ids=[f"g{a}-bs{b}-{c}" for a, b, c in ONE_CASES])
-def test_one_launch_mixed_steps(G, bs, kind):
-    seed = zlib.crc32(f"m{G}{bs}{kind}".encode()) % 10_000
+@pytest.mark.parametrize("cdt,d,G,bs,kind", ONE_CASES, ids=[f"{a}-d{b}-g{c}-bs{e}-{f}" for a, b, c, e, f in ONE_CASES])
+def test_one_launch_mixed_steps(cdt, d, G, bs, kind):
+    seed = zlib.crc32(f"m{cdt}{d}{G}{bs}{kind}".encode()) % 10_000
     L = {"both": [1, 40, 300, 17, 150, 64, 513, 2000, 9, 700],
          "decode": [1, 40, 300, 17, 1500, 64, 513],
          "chunks": [300, 17, 150, 64, 513]}[kind]
     q = {"both": [1, 1, 300, 17, 33, 1, 200, 1, 7, 1],
          "decode": [1] * 7,
          "chunks": [300, 17, 33, 2, 200]}[kind]
-    w = workloads.small_varlen(seed, L, q, num_q_heads=8 * G, num_kv_heads=8, head_dim=128, block_size=bs,
-                               dtype="bf16", cache_dtype="bf16")
+    w = workloads.small_varlen(seed, L, q, num_q_heads=8 * G, num_kv_heads=8, head_dim=d, block_size=bs,
+                               dtype="bf16", cache_dtype=cdt)
+    if cdt == "fp8":
+        w.k_scale, w.v_scale = 0.5, 0.25
     _check(w, two_launch=(), one_launch=ONE_LAUNCH + ((3, 0, 0), (1000, 0, 0)))
 
 

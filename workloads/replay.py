@@ -9,7 +9,8 @@ over the step's decode rows and the chunk kernel over its prefill chunks run for
 layer, bracketed by HIP events per step: by default each kernel once for all layers (the
 layer-batched entry points; the layers' inputs here are independent streams), or one
 launch per kernel and layer (layer_batched=False), as a model that runs its layers in
-turn would issue them."""
+turn would issue them. A step with both decode rows and prefill chunks runs them in one
+launch of the mixed kernel (one_launch, the default), decode slots beside chunk items."""
 from __future__ import annotations
 
 import dataclasses
@@ -52,12 +53,14 @@ class Replay:
       victim, priority, classes: victim policy, priority classes for admission, or
         classes used only to report latencies by;
       static_batching: the static-batching baseline;
-      layer_batched: one launch per kernel for all layers (else one per layer)."""
+      layer_batched: one launch per kernel for all layers (else one per layer);
+      one_launch: a step with decode rows and prefill chunks runs both in one launch
+        (pkv_paged_attention_mixed) over pkv_mixed_decode_slots decode slots."""
 
     def __init__(self, tr: workloads.Trace, chunk_cut: bool = False, min_piece_tiles: int = 0,
                  prefix_cache: bool = True, token_budget: int = 0, chunk_tokens: int = 0, swap_blocks: int = 0,
                  swap_overlap: bool = False, victim: str = "self", priority=None, classes=None,
-                 static_batching: bool = False, layer_batched: bool = True):
+                 static_batching: bool = False, layer_batched: bool = True, one_launch: bool = True):
         import torch
         self.torch = torch
         self.tr = tr
@@ -121,6 +124,7 @@ class Replay:
         cs = pkv.chunk_slots(pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16, tr.head_dim, tr.block_size)
         self.chunk_slots = max(1, -(-cs // nl)) if chunk_cut else 0
         self.min_piece_tiles = min_piece_tiles
+        self.one_launch = one_launch
 
     def _values(self, ids, q_lens, seq_lens):
         """Generate Q/K/V of the step's new tokens for every layer into one buffer; return
@@ -188,10 +192,18 @@ class Replay:
         lens = torch.from_numpy(seq_lens).cuda()
         cu = torch.from_numpy(plan.cu_seqlens_q).cuda()
         slots = torch.from_numpy(plan.slot_mapping).cuda()
-        # decode rows by the balanced-split decode, prefill rows by the chunk kernel
-        mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, self.slots, self.min_piece,
-                                  self.chunk_slots, self.min_piece_tiles)
+        # decode rows by the balanced-split decode, prefill rows by the chunk kernel; with
+        # both kinds in the step, in one launch over fewer decode slots (never more than
+        # self.slots, so the split workspace fits)
         NL = tr.num_layers
+        mixed = self.one_launch and bool((q_lens == 1).any()) and bool((q_lens >= 2).any())
+        dslots = self.slots
+        if mixed:
+            cdt = pkv.FP8 if tr.cache_dtype == "fp8" else pkv.BF16
+            dslots = pkv.mixed_decode_slots(q_lens, seq_lens, cdt, tr.num_kv_heads, tr.group, tr.head_dim,
+                                            tr.block_size, NL if self.layer_batched else 1)
+        mp = pkv.build_mixed_step(q_lens, seq_lens, tr.num_kv_heads, tr.group, dslots, self.min_piece,
+                                  self.chunk_slots, self.min_piece_tiles)
         chunk_dev = mp.chunks.to_device(tr.head_dim, num_layers=NL if self.layer_batched else 1)
         if len(mp.decode_rows):
             rows = torch.from_numpy(mp.decode_rows).cuda()
@@ -212,11 +224,15 @@ class Replay:
             kc, vc = (self.k_cache, self.v_cache) if l is None else (self.k_cache[l], self.v_cache[l])
             launches.append(pkv.kv_cache_write(k, v, kc, vc, slots, tr.block_size, tr.k_scale, tr.v_scale,
                                                defer=True))
-            if len(mp.decode_rows):
+            if mixed:
+                launches.append(pkv.paged_attention_mixed(
+                    out, q, kc, vc, bt, lens, cu, mp, ((rows, plan_d, ws), chunk_dev), tr.num_kv_heads,
+                    tr.block_size, msl, tr.softmax_scale, tr.k_scale, tr.v_scale, defer=True))
+            elif len(mp.decode_rows):
                 launches.append(pkv.paged_attention_decode_split(
                     out, q, kc, vc, bt, lens, plan_d, mp.split, tr.num_kv_heads, tr.block_size, msl,
                     tr.softmax_scale, tr.k_scale, tr.v_scale, ws, rows=rows, cu_seqlens_q=cu, defer=True))
-            if chunk_dev is not None:
+            if chunk_dev is not None and not mixed:
                 work, merges, cws = chunk_dev
                 launches.append(pkv.paged_attention_prefill_chunks(
                     out, q, kc, vc, bt, lens, cu, work, merges, mp.chunks.num_partials, cws, tr.num_kv_heads,
