@@ -431,11 +431,11 @@ int pkv_build_mixed_step(int32_t num_seqs, const int32_t* q_lens, const int32_t*
  * step's decode rows (q_lens[s] == 1) finish together with its chunk items (q_lens[s] >= 2,
  * the pkv_build_chunk_work items) running on the other compute units. q_lens, seq_lens:
  * host int32 [num_seqs]. With L = ceil(pkv_decode_split_slots / num_layers) (the layers
- * share the units): for a bf16 cache at head_dim 128 (block_size 16/32, num_kv_heads a
- * multiple of 8) and rows of both kinds, *slots weighs the decode rows' K/V bytes against
- * the items' 64-key tiles with per-unit rates measured on MI355X for these kernels, in
- * [1, L]; otherwise (one kind of row, or a shape whose rates were not measured, where the
- * decode then runs first and the chunk items after it in the same launch) *slots = L.
+ * share the units): for a shape the mixed kernel covers (bf16 or E4M3 cache, head_dim
+ * 64/128, block_size 16/32, num_kv_heads a multiple of 8) and rows of both kinds, *slots
+ * is the slot count at which the decode rows' 16-token tiles and the items' 64-key tiles,
+ * at per-unit rates measured on MI355X for these kernels and shapes, end soonest, in
+ * [1, L]; otherwise (one kind of row, or a shape that runs as two launches) *slots = L.
  * Pass it to pkv_build_mixed_step as num_slots.
  * INVALID on a bad argument or q > L, and the errors of pkv_decode_split_slots. */
 int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, const int32_t* seq_lens,

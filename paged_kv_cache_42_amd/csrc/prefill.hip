@@ -1284,13 +1284,20 @@ extern "C" int pkv_paged_attention_prefill_chunks_layers(
 }
 
 namespace {
-// Per-workgroup costs that balance a one-launch mixed step (bf16 cache, head_dim 128),
-// measured on MI355X with these kernels: a decode slot streams ~41 GB/s once fewer slots
-// than units share the memory (64 slots moved a 203 MB step of bf16 rows in 78 us), and a
-// chunk item takes ~1.8 us of a unit per 64-key tile of its 128 rows (the 8,448
-// item-tiles of a 4 x 512-token step in 59 us on 256 units).
-constexpr double kMixedSlotBytesPerUs = 41.0e3;
-constexpr double kMixedChunkTileUs = 1.8;
+// Per-unit costs that balance a one-launch mixed step, measured on MI355X with these
+// kernels (a step of 64 decode rows with 256-3000 keys and 4 chunks of 512 new tokens, 8
+// KV heads, the split decode over 64 slots and the chunk kernel alone, caches flushed):
+// us per 16-token decode tile of one 8-KV-head workgroup, and us of a unit per 64-key tile
+// of a 128-row chunk item. An E4M3 tile takes 0.83x a bf16 one for half the bytes, so a
+// rate in bytes would misjudge it.
+struct MixedRates {
+  double tile_us, item_tile_us;
+};
+MixedRates mixed_rates(int cache_dtype, int head_dim) {
+  if (head_dim == 128) return cache_dtype == PKV_BF16 ? MixedRates{1.55, 1.96} : MixedRates{1.29, 2.02};
+  return cache_dtype == PKV_BF16 ? MixedRates{0.91, 1.31} : MixedRates{0.84, 1.35};
+}
+constexpr double kMixedReadBytesPerUs = 6.3e6;   // the decode's stream-read rate at full occupancy
 
 using MixedFn = void (*)(pkv::split::DecodeArgs, ChunkArgs, int, int, int);
 template <int CDT, int D>
@@ -1331,14 +1338,8 @@ extern "C" int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, c
   if (rc != PKV_OK) return rc;
   const int per_layer = std::max(1, (full + num_layers - 1) / num_layers);   // the layers share the units
   *slots = per_layer;
-  // Balanced slots where the rates below were measured (bf16 at head_dim 128). Elsewhere
-  // the decode keeps the layers' share of the units and runs first, the chunk items after
-  // it in the same launch: a byte rate misjudges an E4M3 or head_dim-64 slot (its tiles
-  // take about as long as a bf16 head_dim-128 tile for half the bytes or less), and too few
-  // slots made the decode the step's tail (E4M3 replay 12% slower than two launches).
-  if (!pick_mixed(cache_dtype, head_dim, block_size, num_kv_heads) || cache_dtype != PKV_BF16 || head_dim != 128 ||
-      group > 16 || kRows % group != 0)
-    return PKV_OK;
+  if (!pick_mixed(cache_dtype, head_dim, block_size, num_kv_heads) || group > 16 || kRows % group != 0)
+    return PKV_OK;                                       // two launches: the decode takes the device
   int64_t dec_tiles = 0, chunk_tiles = 0;
   const int32_t QB = kRows / group;
   for (int32_t s = 0; s < num_seqs; ++s) {
@@ -1354,11 +1355,32 @@ extern "C" int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, c
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(PKV_ERR_HIP, "mixed_decode_slots: device query failed");
+  // Decode workgroups n (slots x KV-head groups x layers, so in steps of one slot per
+  // layer) on n of the cus units: the decode ends after max(tiles x tile_us / n, bytes /
+  // read rate), the chunk items on the other units after item_tiles x item_tile_us /
+  // (cus - n). The best such n is kept only where it beats the decode at the layers' share
+  // of the units followed by the chunk items on all of them by 5%: a step of a few long
+  // prefills leaves the decode too little to hide, and slots come in whole steps per layer.
   const int hgroups = num_kv_heads / 8;
-  const double dec = double(dec_tiles) * hgroups * (16.0 * 8 * head_dim * 2 * 2) / kMixedSlotBytesPerUs;
-  const double chk = double(chunk_tiles) * kMixedChunkTileUs;
-  const int wgs = int(std::lround(cus * dec / (dec + chk)));         // decode units over all layers
-  *slots = std::max(1, std::min(per_layer, wgs / (hgroups * num_layers)));
+  const MixedRates r = mixed_rates(cache_dtype, head_dim);
+  const double dec_work = double(dec_tiles) * hgroups * num_layers * r.tile_us;
+  const double dec_bytes = double(dec_tiles) * num_layers * 16.0 * num_kv_heads * head_dim *
+                           (cache_dtype == PKV_BF16 ? 2 : 1) * 2;
+  const double chk_work = double(chunk_tiles) * num_layers * r.item_tile_us;
+  auto t_dec = [&](int n) { return std::max(dec_work / n, dec_bytes / kMixedReadBytesPerUs); };
+  const int step = hgroups * num_layers;
+  const int share = per_layer * step;
+  const double t_seq = t_dec(share) + chk_work / cus;
+  int best = share;
+  double best_t = 1e300;
+  for (int n = step; n < cus && n < share; n += step) {
+    const double t = std::max(t_dec(n), chk_work / (cus - n));
+    if (t < best_t) {
+      best_t = t;
+      best = n;
+    }
+  }
+  if (best_t <= 0.95 * t_seq) *slots = best / step;
   return PKV_OK;
 }
 
