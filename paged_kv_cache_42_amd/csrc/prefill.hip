@@ -1298,6 +1298,10 @@ MixedRates mixed_rates(int cache_dtype, int head_dim) {
   return cache_dtype == PKV_BF16 ? MixedRates{0.91, 1.31} : MixedRates{0.84, 1.35};
 }
 constexpr double kMixedReadBytesPerUs = 6.3e6;   // the decode's stream-read rate at full occupancy
+// Beside chunk items the decode runs ~15% slower than alone (they share the memory
+// system): on the config-2 step the rates alone pick 55 slots (98 us), while 60-128 slots
+// take 86-89 us and fewer than 56 climb steeply, so the decode's work is scaled by this.
+constexpr double kMixedDecodeContention = 1.15;
 
 using MixedFn = void (*)(pkv::split::DecodeArgs, ChunkArgs, int, int, int);
 template <int CDT, int D>
@@ -1363,7 +1367,7 @@ extern "C" int pkv_mixed_decode_slots(int32_t num_seqs, const int32_t* q_lens, c
   // prefills leaves the decode too little to hide, and slots come in whole steps per layer.
   const int hgroups = num_kv_heads / 8;
   const MixedRates r = mixed_rates(cache_dtype, head_dim);
-  const double dec_work = double(dec_tiles) * hgroups * num_layers * r.tile_us;
+  const double dec_work = double(dec_tiles) * hgroups * num_layers * r.tile_us * kMixedDecodeContention;
   const double dec_bytes = double(dec_tiles) * num_layers * 16.0 * num_kv_heads * head_dim *
                            (cache_dtype == PKV_BF16 ? 2 : 1) * 2;
   const double chk_work = double(chunk_tiles) * num_layers * r.item_tile_us;
