@@ -98,18 +98,21 @@ def test_small_mixed_steps(cdt, d, G, bs):
 # and slots
 ONE_CASES = [("bf16", 128, G, bs, kind) for G in (1, 4) for bs in (16, 32) for kind in ("both", "decode", "chunks")]
 ONE_CASES += [(cdt, d, 4, bs, "both") for cdt, d in (("fp8", 128), ("bf16", 64), ("fp8", 64)) for bs in (16, 32)]
+ONE_CASES += [("bf16", 128, 2, 16, "both-kv16"), ("fp8", 64, 2, 16, "both-kv16")]   # two KV-head groups per slot
 
 
 @pytest.mark.parametrize("cdt,d,G,bs,kind", ONE_CASES, ids=[f"{a}-d{b}-g{c}-bs{e}-{f}" for a, b, c, e, f in ONE_CASES])
 def test_one_launch_mixed_steps(cdt, d, G, bs, kind):
     seed = zlib.crc32(f"m{cdt}{d}{G}{bs}{kind}".encode()) % 10_000
+    Hkv = 16 if kind.endswith("kv16") else 8
+    kind = kind.split("-")[0]
     L = {"both": [1, 40, 300, 17, 150, 64, 513, 2000, 9, 700],
          "decode": [1, 40, 300, 17, 1500, 64, 513],
          "chunks": [300, 17, 150, 64, 513]}[kind]
     q = {"both": [1, 1, 300, 17, 33, 1, 200, 1, 7, 1],
          "decode": [1] * 7,
          "chunks": [300, 17, 33, 2, 200]}[kind]
-    w = workloads.small_varlen(seed, L, q, num_q_heads=8 * G, num_kv_heads=8, head_dim=d, block_size=bs,
+    w = workloads.small_varlen(seed, L, q, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, block_size=bs,
                                dtype="bf16", cache_dtype=cdt)
     if cdt == "fp8":
         w.k_scale, w.v_scale = 0.5, 0.25
