@@ -1,6 +1,6 @@
 """Per-KV-head E4M3 scales on the GPU: every attention launch (decode with and without
 context partitions, the balanced-split decode, the varlen kernel, and the mixed step as
-split decode + chunk kernel, cut and uncut) against the oracle on caches written with a
+split decode + chunk kernel, cut and uncut, and the mixed entry) against the oracle on caches written with a
 different scale per KV head. Distinct factors per head make a wrong head index show as a
 large error. The cache bytes themselves are checked in test_gpu_cache_write.py."""
 import numpy as np
@@ -10,7 +10,7 @@ import paged_kv_cache_42_amd as pkv
 import workloads
 
 from gpu_setup import (assert_close, build_step, oracle_attention_full, oracle_planes, out_f64, run_decode,
-                       run_decode_split, run_mixed_two_launch, run_varlen)
+                       run_decode_split, run_mixed, run_mixed_two_launch, run_varlen)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,10 @@ def test_mixed_step_paths_per_head(d, hkv, G):
     for chunk_slots in (0, None):
         out, _ = run_mixed_two_launch(st, chunk_slots=chunk_slots)
         assert_close(out_f64(out), ref, "fp8", f"two-launch chunk_slots={chunk_slots}")
+    # the mixed entry: one launch of decode slots beside chunk items at 8 KV heads
+    for num_slots, chunk_slots in ((None, None), (3, 0)):
+        out, _ = run_mixed(st, num_slots=num_slots, chunk_slots=chunk_slots)
+        assert_close(out_f64(out), ref, "fp8", f"mixed entry slots={num_slots} chunk_slots={chunk_slots}")
 
 
 def test_per_head_argument_errors():
